@@ -1,0 +1,251 @@
+"""Python handle on the fp64 CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc -O2 and OpenMP (host code only)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("n_layer", ctypes.c_int32), ("n_embd", ctypes.c_int32), ("n_head", ctypes.c_int32),
+        ("n_kv_head", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_ff", ctypes.c_int32),
+        ("n_vocab", ctypes.c_int32), ("n_expert", ctypes.c_int32),
+        ("n_expert_used", ctypes.c_int32), ("sliding_window", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double), ("rms_norm_eps", ctypes.c_double),
+        ("w_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        P = ctypes.POINTER
+        L.orc_layer_stride.argtypes = [P(Config)]
+        L.orc_layer_stride.restype = i32
+        L.orc_round_bf16.argtypes = [dbl]
+        L.orc_round_bf16.restype = dbl
+        L.orc_rmsnorm.argtypes = [vp, vp, i32, dbl, vp]
+        L.orc_rmsnorm.restype = None
+        L.orc_rope.argtypes = [vp, i32, i32, dbl]
+        L.orc_rope.restype = None
+        L.orc_attend.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.orc_attend.restype = None
+        L.orc_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        L.orc_attention.restype = None
+        L.orc_silu.argtypes = [dbl]
+        L.orc_silu.restype = dbl
+        L.orc_moe_route.argtypes = [vp, i32, i32, vp, vp]
+        L.orc_moe_route.restype = dbl
+        L.orc_argmax.argtypes = [vp, i32]
+        L.orc_argmax.restype = i32
+        L.orc_state_new.argtypes = [P(Config), i32]
+        L.orc_state_new.restype = vp
+        L.orc_state_free.argtypes = [vp]
+        L.orc_state_free.restype = None
+        L.orc_state_set_pos.argtypes = [vp, i32]
+        L.orc_state_set_pos.restype = None
+        L.orc_state_pos.argtypes = [vp]
+        L.orc_state_pos.restype = i32
+        L.orc_state_set_kv.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.orc_state_set_kv.restype = i32
+        L.orc_step.argtypes = [P(Config), vp, vp, i32, vp, i32, vp, vp]
+        L.orc_step.restype = i32
+        L.orc_full_recompute.argtypes = [P(Config), vp, vp, i32, vp, i32]
+        L.orc_full_recompute.restype = i32
+        L.orc_max_threads.argtypes = []
+        L.orc_max_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------- building blocks
+
+def rmsnorm(x, g, eps):
+    x = _f64(x)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    y = np.empty_like(x)
+    lib().orc_rmsnorm(_ptr(x), _ptr(g), x.size, eps, _ptr(y))
+    return y
+
+
+def rope(u, pos, theta):
+    """RoPE of one head vector u [d] at position pos."""
+    u = _f64(u).copy()
+    lib().orc_rope(_ptr(u), u.size, pos, theta)
+    return u
+
+
+def attend(q, K, V):
+    q, K, V = _f64(q), _f64(K), _f64(V)
+    o = np.empty(q.size)
+    lib().orc_attend(_ptr(q), _ptr(K), _ptr(V), K.shape[0], q.size, _ptr(o))
+    return o
+
+
+def attention(q, K, V, pos, window=0):
+    """q [H][d]; K, V [Hk][T][d]; keys max(0,pos-W+1)..pos. Returns o [H][d]."""
+    q, K, V = _f64(q), _f64(K), _f64(V)
+    H, d = q.shape
+    Hk, T, _ = K.shape
+    o = np.empty((H, d))
+    lib().orc_attention(_ptr(q), _ptr(K), _ptr(V), H, Hk, d, T, pos, window, _ptr(o))
+    return o
+
+
+def silu(z):
+    return lib().orc_silu(float(z))
+
+
+def moe_route(r, k):
+    r = _f64(r)
+    ids = np.empty(k, dtype=np.int32)
+    w = np.empty(k)
+    gap = lib().orc_moe_route(_ptr(r), r.size, k, _ptr(ids), _ptr(w))
+    return ids, w, gap
+
+
+def argmax(logits):
+    logits = _f64(logits)
+    return lib().orc_argmax(_ptr(logits), logits.size)
+
+
+def round_bf16(v):
+    return lib().orc_round_bf16(float(v))
+
+
+# ----------------------------------------------------------------- model
+
+
+def config_of(wl) -> Config:
+    return Config(wl.n_layer, wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim, wl.n_ff,
+                  wl.n_vocab, wl.n_expert, wl.n_expert_used, wl.sliding_window,
+                  float(wl.rope_theta), float(wl.rms_norm_eps), wl.w_dtype, wl.kv_dtype,
+                  wl.act_dtype)
+
+
+class Model:
+    """Oracle view of a weight set drawn by ``synth.make_weights``."""
+
+    def __init__(self, wl, weights):
+        self.wl = wl
+        self.cfg = config_of(wl)
+        self.w = weights
+        stride = lib().orc_layer_stride(ctypes.byref(self.cfg))
+        n = 4 + wl.n_layer * stride
+        tab = (ctypes.c_void_p * n)()
+        tab[0] = _ptr(weights["tok_embd"])
+        tab[1] = _ptr(weights["out_norm"])
+        tab[2] = _ptr(weights["w_out"])
+        tab[3] = _ptr(weights["s_out"])
+        for l, L in enumerate(weights["layers"]):
+            if L is None:
+                raise ValueError("oracle needs every layer's weights")
+            b = 4 + l * stride
+            tab[b + 0] = _ptr(L["attn_norm"])
+            tab[b + 1] = _ptr(L["ffn_norm"])
+            for i, name in enumerate(("wq", "wk", "wv", "wo")):
+                tab[b + 2 + i] = _ptr(L[name])
+                tab[b + 6 + i] = _ptr(L["s_" + name[1:]])
+            tab[b + 10] = _ptr(L["w_router"])
+            for e in range(len(L["w_gate"])):
+                eb = b + 16 + 6 * e
+                tab[eb + 0] = _ptr(L["w_gate"][e])
+                tab[eb + 1] = _ptr(L["w_up"][e])
+                tab[eb + 2] = _ptr(L["w_down"][e])
+                tab[eb + 3] = _ptr(L["s_gate"][e])
+                tab[eb + 4] = _ptr(L["s_up"][e])
+                tab[eb + 5] = _ptr(L["s_down"][e])
+        self.tab = tab
+
+    def new_state(self, max_ctx):
+        return State(self, max_ctx)
+
+    def full_recompute(self, tokens, threads=1):
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        logits = np.empty(self.wl.n_vocab)
+        am = lib().orc_full_recompute(ctypes.byref(self.cfg), self.tab, _ptr(tokens), tokens.size,
+                                      _ptr(logits), threads)
+        return logits, am
+
+
+class State:
+    def __init__(self, model: Model, max_ctx: int):
+        self.model = model
+        self.h = lib().orc_state_new(ctypes.byref(model.cfg), max_ctx)
+        if not self.h:
+            raise MemoryError("oracle state allocation failed")
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h and _lib is not None:
+            _lib.orc_state_free(h)
+            self.h = None
+
+    @property
+    def pos(self):
+        return lib().orc_state_pos(self.h)
+
+    @pos.setter
+    def pos(self, p):
+        lib().orc_state_set_pos(self.h, int(p))
+
+    def set_kv(self, layer, pos0, k, v):
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        rc = lib().orc_state_set_kv(self.h, layer, pos0, k.shape[0], _ptr(k), _ptr(v))
+        if rc != 0:
+            raise ValueError("set_kv out of range")
+
+    def step(self, token, threads=1, want_route=False):
+        """One decode step. Returns (logits float64 [V], argmax id[, route ids, route gap])."""
+        wl = self.model.wl
+        logits = np.empty(wl.n_vocab)
+        ids = None
+        gap = ctypes.c_double(0.0)
+        if want_route:
+            ids = np.zeros((wl.n_layer, max(1, wl.n_expert_used)), dtype=np.int32)
+        am = lib().orc_step(ctypes.byref(self.model.cfg), self.model.tab, self.h, int(token),
+                            _ptr(logits), threads, _ptr(ids), ctypes.byref(gap))
+        if am < -1:
+            raise ValueError("oracle step failed (%d)" % am)
+        if want_route:
+            return logits, am, ids, gap.value
+        return logits, am

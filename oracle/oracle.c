@@ -1,0 +1,512 @@
+/*
+ * oracle.c - plain, slow CPU reference of one decode step of a Llama-family
+ * transformer, computed in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code with the HIP library.
+ *
+ * What it computes follows the Pantheon engine pages ("Core Engine API" and
+ * "Engine Architecture"):
+ *   - the forward signature forward(model, token, state) -> logits and the
+ *     state {kv_cache, pos} (Core Engine API, sections "pn_model struct" and
+ *     "pn_state struct");
+ *   - the per-token intermediates listed by the scratch-arena sizing: per
+ *     layer 5*n_embd + 3*n_ff + 2*n_kv_head*head_dim values (x, normed x,
+ *     attention output, projections, FFN gate/up/hidden and the new k, v),
+ *     MoE adding router logits and the chosen ids and weights, and once per
+ *     token the normed output, the scores and the logits (Core Engine API,
+ *     section "Scratch (arena) estimation");
+ *   - the config keys and defaults: rope_theta 10000, rms_norm_eps 1e-5,
+ *     sliding_window 0 = off, n_kv_head defaulting to n_head (Engine
+ *     Architecture, section "Config Parsing");
+ *   - Llama, Mistral and Mixtral sharing one forward, MoE switched on by an
+ *     expert count > 0 and the window by a config flag (Engine Architecture,
+ *     section "Architecture Detection");
+ *   - greedy decoding = argmax of the logits (Engine Architecture, section
+ *     "Sampling", temperature 0);
+ *   - quantised weights dequantised inside the mat-vec, norms kept in F32
+ *     (Engine Architecture, section "Weight Loading Modes").
+ * Where the pages are silent the plain Llama reading is taken: RMSNorm with
+ * eps inside the root; RoPE on adjacent pairs (2i, 2i+1) with
+ * w_i = theta^(-2i/d), applied to q and k only, k cached after rotation;
+ * query head h reads kv head floor(h / (n_head / n_kv_head)); scores scaled by
+ * 1/sqrt(d); the window holds the keys t with pos - W < t <= pos; SwiGLU FFN
+ * down(silu(gate x) * up x); MoE softmax router, top-k with ties to the lower
+ * index, weights renormalised over the chosen experts; untied LM head behind
+ * a final RMSNorm.
+ *
+ * Precision.  Every stored value (fp32, bf16, or int8 times an fp32 row
+ * scale) is widened to double on read and all arithmetic is double.  The
+ * values that the decode step stores in a narrower type are rounded at the
+ * same points: the inputs of every mat-vec (normed x, attention output,
+ * FFN hidden, final normed x) to the activation type, and the appended k, v
+ * to the KV type.  Integer decisions taken from floating point (the argmax of
+ * the logits, the router's top-k) compare the values rounded to fp32, the
+ * precision the GPU decides in.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2 };
+
+typedef struct {
+    int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab;
+    int32_t n_expert, n_expert_used, sliding_window;
+    double rope_theta, rms_norm_eps;
+    int32_t w_dtype, kv_dtype, act_dtype;
+} orc_config;
+
+/* Weight table (array of pointers, all host memory, matrices row-major [out][in]):
+ *   [0] tok_embd [V][E]   (fp32 when w_dtype is fp32, else bf16)
+ *   [1] out_norm [E] fp32     [2] w_out [V][E]     [3] s_out [V] (int8 only)
+ *   per layer l, at 4 + l * orc_layer_stride(cfg):
+ *   +0 attn_norm  +1 ffn_norm  +2 wq [H*d][E]  +3 wk [Hk*d][E]  +4 wv [Hk*d][E]
+ *   +5 wo [E][H*d]  +6..+9 row scales of q, k, v, o (int8 only)
+ *   +10 router [n_expert][E] (fp32 when w_dtype is fp32, else bf16)
+ *   +16 + 6e: gate [F][E], up [F][E], down [E][F], then their row scales.  */
+int orc_layer_stride(const orc_config *c) { return 16 + 6 * (c->n_expert > 0 ? c->n_expert : 1); }
+
+enum { T_EMBD = 0, T_OUT_NORM = 1, T_OUT = 2, T_S_OUT = 3, T_LAYER0 = 4 };
+enum { L_ATTN_NORM = 0, L_FFN_NORM, L_WQ, L_WK, L_WV, L_WO, L_SQ, L_SK, L_SV, L_SO, L_ROUTER };
+
+/* ------------------------------------------------------------------ rounding */
+
+/* nearest bf16 value of v, ties to even (bf16 keeps 8 significant bits) */
+double orc_round_bf16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e;
+    double m = frexp(v, &e);
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
+static double round_to(double v, int dt) {
+    if (dt == ORC_BF16) return orc_round_bf16(v);
+    return (double)(float)v;
+}
+
+static uint16_t bf16_bits(double v) {
+    float f = (float)orc_round_bf16(v);
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    return (uint16_t)(b >> 16);
+}
+
+static double bf16_value(uint16_t h) {
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return (double)f;
+}
+
+/* element i of a stored tensor, widened to double (int8: the raw code) */
+static double rd(const void *p, int dt, size_t i) {
+    switch (dt) {
+        case ORC_F32: return (double)((const float *)p)[i];
+        case ORC_BF16: return bf16_value(((const uint16_t *)p)[i]);
+        default: return (double)((const int8_t *)p)[i];
+    }
+}
+
+/* ------------------------------------------------------------------ building blocks */
+
+static int g_threads = 1;
+
+/* y[r] = sum_c W[r][c] * x[c]; int8 rows are scaled by s[r] after the sum */
+static void matvec(const void *W, int dt, const float *s, int rows, int cols, const double *x,
+                   double *y) {
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
+    for (int r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        size_t base = (size_t)r * (size_t)cols;
+        for (int c = 0; c < cols; ++c) acc += rd(W, dt, base + (size_t)c) * x[c];
+        y[r] = (dt == ORC_I8) ? (double)s[r] * acc : acc;
+    }
+}
+
+/* y = x * (mean(x^2) + eps)^(-1/2) * g */
+void orc_rmsnorm(const double *x, const float *g, int n, double eps, double *y) {
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i) ss += x[i] * x[i];
+    double inv = 1.0 / sqrt(ss / (double)n + eps);
+    for (int i = 0; i < n; ++i) y[i] = x[i] * inv * (double)g[i];
+}
+
+/* rotate pairs (u[2i], u[2i+1]) of one head vector by pos * theta^(-2i/d) */
+void orc_rope(double *u, int d, int pos, double theta) {
+    for (int i = 0; i < d / 2; ++i) {
+        double w = pow(theta, -2.0 * (double)i / (double)d);
+        double phi = (double)pos * w;
+        double c = cos(phi), s = sin(phi);
+        double a = u[2 * i], b = u[2 * i + 1];
+        u[2 * i] = a * c - b * s;
+        u[2 * i + 1] = a * s + b * c;
+    }
+}
+
+/* one query against T keys/values [T][d]: o = sum_t softmax(q.K_t / sqrt(d)) V_t */
+void orc_attend(const double *q, const double *K, const double *V, int T, int d, double *o) {
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double mx = -INFINITY;
+    double scale = 1.0 / sqrt((double)d);
+    for (int t = 0; t < T; ++t) {
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i) dot += q[i] * K[(size_t)t * d + i];
+        sc[t] = dot * scale;
+        if (sc[t] > mx) mx = sc[t];
+    }
+    double den = 0.0;
+    for (int t = 0; t < T; ++t) {
+        sc[t] = exp(sc[t] - mx);
+        den += sc[t];
+    }
+    for (int i = 0; i < d; ++i) o[i] = 0.0;
+    for (int t = 0; t < T; ++t) {
+        double a = sc[t] / den;
+        for (int i = 0; i < d; ++i) o[i] += a * V[(size_t)t * d + i];
+    }
+    free(sc);
+}
+
+/* Grouped-query attention of all heads at position pos.
+ * q [H][d]; K, V [Hk][T][d] hold positions 0..T-1 (T > pos); W = window (0 = off).
+ * Query head h reads kv head h / (H / Hk); keys t with max(0, pos-W+1) <= t <= pos. */
+void orc_attention(const double *q, const double *K, const double *V, int H, int Hk, int d,
+                   int T, int pos, int W, double *o) {
+    int G = H / Hk;
+    int t0 = (W > 0 && pos - W + 1 > 0) ? pos - W + 1 : 0;
+    int n = pos - t0 + 1;
+#pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
+    for (int h = 0; h < H; ++h) {
+        int j = h / G;
+        const double *Kj = K + ((size_t)j * T + t0) * d;
+        const double *Vj = V + ((size_t)j * T + t0) * d;
+        orc_attend(q + (size_t)h * d, Kj, Vj, n, d, o + (size_t)h * d);
+    }
+}
+
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Top-k routing of one token: ids by descending router logit compared in fp32
+ * (ties -> lower index); weights = softmax over all experts, renormalised over
+ * the chosen ones (equal to a softmax over the chosen logits). Returns the
+ * fp32 gap between the k-th and (k+1)-th logits (inf if k == n). */
+double orc_moe_route(const double *r, int n, int k, int32_t *ids, double *w) {
+    int used[64] = {0};
+    for (int a = 0; a < k; ++a) {
+        int best = -1;
+        float bv = 0.0f;
+        for (int e = 0; e < n; ++e) {
+            if (used[e]) continue;
+            float v = (float)r[e];
+            if (best < 0 || v > bv) { best = e; bv = v; }
+        }
+        used[best] = 1;
+        ids[a] = best;
+    }
+    double mx = -INFINITY;
+    for (int e = 0; e < n; ++e) if (r[e] > mx) mx = r[e];
+    double den = 0.0;
+    for (int e = 0; e < n; ++e) den += exp(r[e] - mx);
+    double sel = 0.0;
+    for (int a = 0; a < k; ++a) {
+        w[a] = exp(r[ids[a]] - mx) / den;
+        sel += w[a];
+    }
+    for (int a = 0; a < k; ++a) w[a] /= sel;
+    double gap = INFINITY;
+    if (k < n) {
+        float kth = (float)r[ids[k - 1]], next = -INFINITY;
+        for (int e = 0; e < n; ++e)
+            if (!used[e] && (float)r[e] > next) next = (float)r[e];
+        gap = (double)kth - (double)next;
+    }
+    return gap;
+}
+
+/* index of the largest logit compared in fp32, lowest index among equal maxima;
+ * -1 if any logit is NaN */
+int orc_argmax(const double *logits, int n) {
+    int best = 0;
+    float bv = (float)logits[0];
+    for (int i = 0; i < n; ++i) {
+        float v = (float)logits[i];
+        if (v != v) return -1;
+        if (v > bv) { bv = v; best = i; }
+    }
+    return best;
+}
+
+/* ------------------------------------------------------------------ state */
+
+typedef struct {
+    orc_config cfg;
+    int max_ctx, pos;
+    void **k, **v; /* per layer [Hk][max_ctx][d] in kv dtype */
+} orc_state;
+
+static size_t kv_elem(const orc_config *c) { return c->kv_dtype == ORC_BF16 ? 2 : 4; }
+
+orc_state *orc_state_new(const orc_config *c, int max_ctx) {
+    orc_state *s = (orc_state *)calloc(1, sizeof(orc_state));
+    s->cfg = *c;
+    s->max_ctx = max_ctx;
+    s->k = (void **)calloc((size_t)c->n_layer, sizeof(void *));
+    s->v = (void **)calloc((size_t)c->n_layer, sizeof(void *));
+    size_t bytes = (size_t)c->n_kv_head * (size_t)max_ctx * (size_t)c->head_dim * kv_elem(c);
+    for (int l = 0; l < c->n_layer; ++l) {
+        s->k[l] = calloc(1, bytes);
+        s->v[l] = calloc(1, bytes);
+        if (!s->k[l] || !s->v[l]) return NULL;
+    }
+    return s;
+}
+
+void orc_state_free(orc_state *s) {
+    if (!s) return;
+    for (int l = 0; l < s->cfg.n_layer; ++l) {
+        free(s->k[l]);
+        free(s->v[l]);
+    }
+    free(s->k);
+    free(s->v);
+    free(s);
+}
+
+void orc_state_set_pos(orc_state *s, int pos) { s->pos = pos; }
+int orc_state_pos(const orc_state *s) { return s->pos; }
+
+/* copy stored K/V of positions pos0..pos0+n-1, given as [n][Hk][d] in kv dtype */
+int orc_state_set_kv(orc_state *s, int layer, int pos0, int n, const void *k, const void *v) {
+    const orc_config *c = &s->cfg;
+    if (layer < 0 || layer >= c->n_layer || pos0 < 0 || pos0 + n > s->max_ctx) return -2;
+    size_t es = kv_elem(c), d = (size_t)c->head_dim;
+    for (int t = 0; t < n; ++t)
+        for (int j = 0; j < c->n_kv_head; ++j) {
+            size_t src = ((size_t)t * c->n_kv_head + j) * d * es;
+            size_t dst = ((size_t)j * s->max_ctx + (size_t)(pos0 + t)) * d * es;
+            memcpy((char *)s->k[layer] + dst, (const char *)k + src, d * es);
+            memcpy((char *)s->v[layer] + dst, (const char *)v + src, d * es);
+        }
+    return 0;
+}
+
+static void store_kv(void *base, int dt, size_t i, double v) {
+    if (dt == ORC_BF16)
+        ((uint16_t *)base)[i] = bf16_bits(v);
+    else
+        ((float *)base)[i] = (float)v;
+}
+
+/* ------------------------------------------------------------------ one layer */
+
+typedef struct {
+    double *xn, *q, *k, *v, *o, *tmp, *g, *u, *h, *y, *acc, *r;
+} scratch;
+
+static void scratch_new(const orc_config *c, scratch *s) {
+    size_t E = c->n_embd, Hd = (size_t)c->n_head * c->head_dim, F = c->n_ff;
+    size_t Kd = (size_t)c->n_kv_head * c->head_dim;
+    s->xn = malloc(sizeof(double) * E);
+    s->q = malloc(sizeof(double) * Hd);
+    s->k = malloc(sizeof(double) * Kd);
+    s->v = malloc(sizeof(double) * Kd);
+    s->o = malloc(sizeof(double) * Hd);
+    s->tmp = malloc(sizeof(double) * E);
+    s->g = malloc(sizeof(double) * F);
+    s->u = malloc(sizeof(double) * F);
+    s->h = malloc(sizeof(double) * F);
+    s->y = malloc(sizeof(double) * E);
+    s->acc = malloc(sizeof(double) * E);
+    s->r = malloc(sizeof(double) * (size_t)(c->n_expert > 0 ? c->n_expert : 1));
+}
+
+static void scratch_free(scratch *s) {
+    free(s->xn); free(s->q); free(s->k); free(s->v); free(s->o); free(s->tmp);
+    free(s->g); free(s->u); free(s->h); free(s->y); free(s->acc); free(s->r);
+}
+
+static const void *T(const void *const *tab, int i) { return tab[i]; }
+
+static int wdt(const orc_config *c) { return c->w_dtype; }
+static int aux_dt(const orc_config *c) { return c->w_dtype == ORC_F32 ? ORC_F32 : ORC_BF16; }
+
+/* the FFN of one token: x += FFN(round_act(RMSNorm(x) * g_ffn)); returns the
+ * router's fp32 k-th/(k+1)-th gap for MoE layers, +inf otherwise */
+static double ffn(const orc_config *c, const void *const *tab, int lb, double *x, scratch *s,
+                  int32_t *ids_out) {
+    int E = c->n_embd, F = c->n_ff;
+    orc_rmsnorm(x, (const float *)T(tab, lb + L_FFN_NORM), E, c->rms_norm_eps, s->xn);
+    for (int i = 0; i < E; ++i) s->xn[i] = round_to(s->xn[i], c->act_dtype);
+    int n_used = c->n_expert > 0 ? c->n_expert_used : 1;
+    int32_t ids[64];
+    double w[64];
+    double gap = INFINITY;
+    if (c->n_expert > 0) {
+        matvec(T(tab, lb + L_ROUTER), aux_dt(c), NULL, c->n_expert, E, s->xn, s->r);
+        gap = orc_moe_route(s->r, c->n_expert, n_used, ids, w);
+    } else {
+        ids[0] = 0;
+        w[0] = 1.0;
+    }
+    for (int i = 0; i < E; ++i) s->acc[i] = 0.0;
+    for (int a = 0; a < n_used; ++a) {
+        int eb = lb + 16 + 6 * ids[a];
+        matvec(T(tab, eb + 0), wdt(c), (const float *)T(tab, eb + 3), F, E, s->xn, s->g);
+        matvec(T(tab, eb + 1), wdt(c), (const float *)T(tab, eb + 4), F, E, s->xn, s->u);
+        for (int i = 0; i < F; ++i) s->h[i] = round_to(orc_silu(s->g[i]) * s->u[i], c->act_dtype);
+        matvec(T(tab, eb + 2), wdt(c), (const float *)T(tab, eb + 5), E, F, s->h, s->y);
+        for (int i = 0; i < E; ++i) s->acc[i] += w[a] * s->y[i];
+        if (ids_out) ids_out[a] = ids[a];
+    }
+    for (int i = 0; i < E; ++i) x[i] += s->acc[i];
+    return gap;
+}
+
+/* q, k, v of one token at position pos: round_act(RMSNorm(x)*g), projections, RoPE */
+static void qkv(const orc_config *c, const void *const *tab, int lb, const double *x, int pos,
+                scratch *s) {
+    int E = c->n_embd, d = c->head_dim, H = c->n_head, Hk = c->n_kv_head;
+    orc_rmsnorm(x, (const float *)T(tab, lb + L_ATTN_NORM), E, c->rms_norm_eps, s->xn);
+    for (int i = 0; i < E; ++i) s->xn[i] = round_to(s->xn[i], c->act_dtype);
+    matvec(T(tab, lb + L_WQ), wdt(c), (const float *)T(tab, lb + L_SQ), H * d, E, s->xn, s->q);
+    matvec(T(tab, lb + L_WK), wdt(c), (const float *)T(tab, lb + L_SK), Hk * d, E, s->xn, s->k);
+    matvec(T(tab, lb + L_WV), wdt(c), (const float *)T(tab, lb + L_SV), Hk * d, E, s->xn, s->v);
+    for (int h = 0; h < H; ++h) orc_rope(s->q + (size_t)h * d, d, pos, c->rope_theta);
+    for (int j = 0; j < Hk; ++j) orc_rope(s->k + (size_t)j * d, d, pos, c->rope_theta);
+}
+
+/* x += W_o * round_act(o) */
+static void attn_out(const orc_config *c, const void *const *tab, int lb, double *x, scratch *s) {
+    int E = c->n_embd, Hd = c->n_head * c->head_dim;
+    for (int i = 0; i < Hd; ++i) s->o[i] = round_to(s->o[i], c->act_dtype);
+    matvec(T(tab, lb + L_WO), wdt(c), (const float *)T(tab, lb + L_SO), E, Hd, s->o, s->tmp);
+    for (int i = 0; i < E; ++i) x[i] += s->tmp[i];
+}
+
+/* logits = W_out * round_act(RMSNorm(x) * g_out) */
+static void head(const orc_config *c, const void *const *tab, const double *x, double *logits,
+                 scratch *s) {
+    int E = c->n_embd;
+    orc_rmsnorm(x, (const float *)T(tab, T_OUT_NORM), E, c->rms_norm_eps, s->xn);
+    for (int i = 0; i < E; ++i) s->xn[i] = round_to(s->xn[i], c->act_dtype);
+    matvec(T(tab, T_OUT), wdt(c), (const float *)T(tab, T_S_OUT), c->n_vocab, E, s->xn, logits);
+}
+
+static void embed(const orc_config *c, const void *const *tab, int token, double *x) {
+    for (int i = 0; i < c->n_embd; ++i)
+        x[i] = rd(T(tab, T_EMBD), aux_dt(c), (size_t)token * c->n_embd + (size_t)i);
+}
+
+/* ------------------------------------------------------------------ decode step */
+
+/* One decode step: append the token's k, v at state->pos, attend, write the
+ * logits [V] and return the greedy id (or a negative error).  `route_ids`
+ * (optional, [n_layer][n_expert_used]) receives the experts each layer chose
+ * and `route_gap` (optional) the smallest router k-th/(k+1)-th fp32 gap. */
+int orc_step(const orc_config *c, const void *const *tab, orc_state *st, int token,
+             double *logits, int nthreads, int32_t *route_ids, double *route_gap) {
+    int E = c->n_embd, d = c->head_dim, H = c->n_head, Hk = c->n_kv_head;
+    int p = st->pos;
+    if (token < 0 || token >= c->n_vocab) return -3;
+    if (p < 0 || p >= st->max_ctx) return -2;
+    g_threads = nthreads > 0 ? nthreads : 1;
+    scratch s;
+    scratch_new(c, &s);
+    double *x = malloc(sizeof(double) * E);
+    int t0 = (c->sliding_window > 0 && p - c->sliding_window + 1 > 0) ? p - c->sliding_window + 1 : 0;
+    int n = p - t0 + 1;
+    double *K = malloc(sizeof(double) * (size_t)Hk * n * d);
+    double *V = malloc(sizeof(double) * (size_t)Hk * n * d);
+    double gap = INFINITY;
+    embed(c, tab, token, x);
+    for (int l = 0; l < c->n_layer; ++l) {
+        int lb = T_LAYER0 + l * orc_layer_stride(c);
+        qkv(c, tab, lb, x, p, &s);
+        for (int j = 0; j < Hk; ++j)
+            for (int i = 0; i < d; ++i) {
+                size_t at = ((size_t)j * st->max_ctx + (size_t)p) * d + (size_t)i;
+                store_kv(st->k[l], c->kv_dtype, at, s.k[(size_t)j * d + i]);
+                store_kv(st->v[l], c->kv_dtype, at, s.v[(size_t)j * d + i]);
+            }
+        /* the window's cached keys and values, widened to double, [Hk][n][d] */
+        for (int j = 0; j < Hk; ++j)
+            for (int t = 0; t < n; ++t)
+                for (int i = 0; i < d; ++i) {
+                    size_t src = ((size_t)j * st->max_ctx + (size_t)(t0 + t)) * d + (size_t)i;
+                    size_t dst = ((size_t)j * n + (size_t)t) * d + (size_t)i;
+                    K[dst] = rd(st->k[l], c->kv_dtype, src);
+                    V[dst] = rd(st->v[l], c->kv_dtype, src);
+                }
+        /* keys are the window only, so position p sits at index n-1 and W is not re-applied */
+        orc_attention(s.q, K, V, H, Hk, d, n, n - 1, 0, s.o);
+        attn_out(c, tab, lb, x, &s);
+        double gl = ffn(c, tab, lb, x, &s,
+                        route_ids ? route_ids + (size_t)l * (c->n_expert > 0 ? c->n_expert_used : 1)
+                                  : NULL);
+        if (gl < gap) gap = gl;
+    }
+    head(c, tab, x, logits, &s);
+    st->pos = p + 1;
+    if (route_gap) *route_gap = gap;
+    free(K);
+    free(V);
+    free(x);
+    scratch_free(&s);
+    return orc_argmax(logits, c->n_vocab);
+}
+
+/* Causal forward over tokens[0..n-1] from scratch (no cache carried between
+ * calls): every position's k, v are recomputed and rounded to the KV type, and
+ * the logits of the last position are written.  Returns its greedy id. */
+int orc_full_recompute(const orc_config *c, const void *const *tab, const int32_t *tokens, int n,
+                       double *logits, int nthreads) {
+    int E = c->n_embd, d = c->head_dim, H = c->n_head, Hk = c->n_kv_head;
+    g_threads = nthreads > 0 ? nthreads : 1;
+    for (int t = 0; t < n; ++t)
+        if (tokens[t] < 0 || tokens[t] >= c->n_vocab) return -3;
+    scratch s;
+    scratch_new(c, &s);
+    double *X = malloc(sizeof(double) * (size_t)n * E);
+    double *Q = malloc(sizeof(double) * (size_t)n * H * d);
+    double *K = malloc(sizeof(double) * (size_t)Hk * n * d);
+    double *V = malloc(sizeof(double) * (size_t)Hk * n * d);
+    for (int t = 0; t < n; ++t) embed(c, tab, tokens[t], X + (size_t)t * E);
+    for (int l = 0; l < c->n_layer; ++l) {
+        int lb = T_LAYER0 + l * orc_layer_stride(c);
+        for (int t = 0; t < n; ++t) {
+            qkv(c, tab, lb, X + (size_t)t * E, t, &s);
+            memcpy(Q + (size_t)t * H * d, s.q, sizeof(double) * (size_t)H * d);
+            for (int j = 0; j < Hk; ++j)
+                for (int i = 0; i < d; ++i) {
+                    K[((size_t)j * n + t) * d + i] = round_to(s.k[(size_t)j * d + i], c->kv_dtype);
+                    V[((size_t)j * n + t) * d + i] = round_to(s.v[(size_t)j * d + i], c->kv_dtype);
+                }
+        }
+        for (int t = 0; t < n; ++t) {
+            orc_attention(Q + (size_t)t * H * d, K, V, H, Hk, d, n, t, c->sliding_window, s.o);
+            attn_out(c, tab, lb, X + (size_t)t * E, &s);
+            ffn(c, tab, lb, X + (size_t)t * E, &s, NULL);
+        }
+    }
+    head(c, tab, X + (size_t)(n - 1) * E, logits, &s);
+    free(X);
+    free(Q);
+    free(K);
+    free(V);
+    scratch_free(&s);
+    return orc_argmax(logits, c->n_vocab);
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,370 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test checks one building block (or the whole step) against a closed form,
+an invariant, a brute-force or library computation (torch CPU routines in
+float64), or a special case that reduces to the textbook form.  Each was chosen
+so that a plausible slip (a dropped term, a wrong sign or index, a transposed
+operand, an off-by-one window) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+rng = np.random.default_rng(1234)
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_constant_vector_closed_form():
+    E, c, eps = 96, 0.37, 1e-5
+    g = (1.0 + 0.1 * rng.standard_normal(E)).astype(np.float32)
+    y = oracle.rmsnorm(np.full(E, c), g, eps)
+    want = c / math.sqrt(c * c + eps) * g.astype(np.float64)
+    np.testing.assert_allclose(y, want, rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_unit_rms_and_scale_invariance():
+    E = 257
+    x = rng.standard_normal(E) * 3.0
+    ones = np.ones(E, dtype=np.float32)
+    y = oracle.rmsnorm(x, ones, 0.0)
+    assert abs(np.sum(y * y) - E) < 1e-9 * E
+    np.testing.assert_allclose(oracle.rmsnorm(x * 1000.0, ones, 0.0), y, rtol=1e-13)
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    E, eps = 512, 1e-5
+    x = rng.standard_normal(E)
+    g = (1.0 + 0.1 * rng.standard_normal(E)).astype(np.float32)
+    ref = F.rms_norm(torch.tensor(x), (E,), weight=torch.tensor(g.astype(np.float64)), eps=eps)
+    np.testing.assert_allclose(oracle.rmsnorm(x, g, eps), ref.numpy(), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def _rope_complex(u, pos, theta):
+    """RoPE written as a complex product of adjacent pairs (torch.polar)."""
+    d = u.size
+    freqs = 1.0 / (theta ** (torch.arange(0, d, 2, dtype=torch.float64) / d))
+    rot = torch.polar(torch.ones(d // 2, dtype=torch.float64), pos * freqs)
+    z = torch.view_as_complex(torch.tensor(u).reshape(d // 2, 2).contiguous())
+    return torch.view_as_real(z * rot).reshape(d).numpy()
+
+
+@pytest.mark.parametrize("d,theta", [(32, 1e4), (128, 5e5), (64, 1e4)])
+def test_rope_matches_complex_rotation(d, theta):
+    for pos in (0, 1, 7, 2048, 16511):
+        u = rng.standard_normal(d)
+        np.testing.assert_allclose(oracle.rope(u, pos, theta), _rope_complex(u, pos, theta),
+                                   rtol=0, atol=1e-12)
+
+
+def test_rope_identity_at_zero_and_pair_norms():
+    d = 64
+    u = rng.standard_normal(d)
+    np.testing.assert_array_equal(oracle.rope(u, 0, 1e4), u)
+    r = oracle.rope(u, 1234, 1e4)
+    np.testing.assert_allclose(np.hypot(r[0::2], r[1::2]), np.hypot(u[0::2], u[1::2]), rtol=1e-14)
+
+
+def test_rope_theta_dependence():
+    d, p = 128, 37
+    e0 = np.zeros(d)
+    e0[0::2] = 1.0  # every pair starts at angle 0
+    for theta in (1e4, 5e5):
+        r = oracle.rope(e0, p, theta)
+        ang = np.arctan2(r[1::2], r[0::2])
+        # pair 0 turns by exactly p radians whatever theta is
+        assert abs(math.remainder(ang[0] - p, 2 * math.pi)) < 1e-12
+        # the last pair turns by p * theta^(-(d-2)/d)
+        want = p * theta ** (-(d - 2) / d)
+        assert abs(math.remainder(ang[-1] - want, 2 * math.pi)) < 1e-12
+    # changing theta changes only pairs i > 0
+    a, b = oracle.rope(e0, p, 1e4), oracle.rope(e0, p, 5e5)
+    np.testing.assert_array_equal(a[:2], b[:2])
+    assert np.all(np.abs(a[2:] - b[2:]).reshape(-1, 2).max(axis=1) > 0)
+
+
+def test_rope_relative_position():
+    d = 32
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n, delta in ((5, 2, 11), (100, 0, 3), (7, 7, 1000)):
+        a = oracle.rope(q, m, 1e4) @ oracle.rope(k, n, 1e4)
+        b = oracle.rope(q, m + delta, 1e4) @ oracle.rope(k, n + delta, 1e4)
+        assert abs(a - b) < 1e-11 * (1 + abs(a))
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _sdpa(q, K, V, pos, window):
+    """torch scaled_dot_product_attention (float64) with GQA and an explicit boolean mask."""
+    H, d = q.shape
+    Hk, T, _ = K.shape
+    t = torch.arange(T)
+    lo = max(0, pos - window + 1) if window > 0 else 0
+    mask = (t >= lo) & (t <= pos)
+    out = F.scaled_dot_product_attention(
+        torch.tensor(q)[None, :, None, :], torch.tensor(K)[None], torch.tensor(V)[None],
+        attn_mask=mask[None, None, None, :], enable_gqa=True)
+    return out[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("H,Hk,d,T", [(8, 2, 32, 40), (4, 4, 16, 30), (6, 1, 8, 25), (32, 8, 128, 70)])
+def test_attention_matches_sdpa(H, Hk, d, T):
+    q = rng.standard_normal((H, d))
+    K = rng.standard_normal((Hk, T, d))
+    V = rng.standard_normal((Hk, T, d))
+    for pos in (0, 1, T // 2, T - 1):
+        for W in (0, 1, 3, 8, T + 5):
+            np.testing.assert_allclose(oracle.attention(q, K, V, pos, W), _sdpa(q, K, V, pos, W),
+                                       rtol=1e-12, atol=1e-12)
+
+
+def test_window_bruteforce_small_contexts():
+    H, Hk, d = 4, 2, 8
+    for p in range(0, 25):
+        T = p + 1
+        q = rng.standard_normal((H, d))
+        K = rng.standard_normal((Hk, T, d))
+        V = rng.standard_normal((Hk, T, d))
+        full = oracle.attention(q, K, V, p, 0)
+        for W in (1, 2, 3, 5, 8):
+            got = oracle.attention(q, K, V, p, W)
+            np.testing.assert_allclose(got, _sdpa(q, K, V, p, W), rtol=1e-12, atol=1e-13)
+            if W >= p + 1:
+                np.testing.assert_array_equal(got, full)
+            if W == 1:  # a one-key window returns the newest value exactly
+                np.testing.assert_array_equal(got, V[np.arange(H) // (H // Hk), p])
+
+
+def test_attention_special_cases():
+    d, T = 16, 9
+    q = rng.standard_normal(d)
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    # one key: the output is that value exactly
+    np.testing.assert_array_equal(oracle.attend(q, K[:1], V[:1]), V[0])
+    # equal scores: the mean of the values
+    np.testing.assert_allclose(oracle.attend(q, np.zeros((T, d)), V), V.mean(axis=0), rtol=1e-14)
+    # shifting every score by the same amount changes nothing
+    u = rng.standard_normal(d)
+    np.testing.assert_allclose(oracle.attend(q, K + u, V), oracle.attend(q, K, V), rtol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    H, Hk, d, T = 8, 2, 16, 12
+    q = rng.standard_normal((H, d))
+    K = rng.standard_normal((Hk, T, d))
+    V = rng.standard_normal((Hk, T, d))
+    rep = H // Hk
+    Kr, Vr = np.repeat(K, rep, axis=0), np.repeat(V, rep, axis=0)
+    for pos, W in ((11, 0), (6, 3)):
+        np.testing.assert_array_equal(oracle.attention(q, K, V, pos, W),
+                                      oracle.attention(q, Kr, Vr, pos, W))
+
+
+# ----------------------------------------------------------------------------- FFN pieces
+
+def test_silu_matches_torch():
+    for z in (-30.0, -2.5, -1e-3, 0.0, 0.7, 4.0, 50.0):
+        assert abs(oracle.silu(z) - F.silu(torch.tensor(z, dtype=torch.float64)).item()) < 1e-15
+
+
+def test_moe_route_weights():
+    for _ in range(20):
+        r = rng.standard_normal(8) * 2
+        ids, w, gap = oracle.moe_route(r, 2)
+        assert abs(w.sum() - 1.0) < 1e-14
+        want = torch.softmax(torch.tensor(r[ids]), 0).numpy()
+        np.testing.assert_allclose(w, want, rtol=1e-13)
+        order = np.argsort(-r.astype(np.float32), kind="stable")
+        np.testing.assert_array_equal(ids, order[:2])
+        assert gap >= 0
+    # ties go to the lower index
+    ids, w, gap = oracle.moe_route(np.array([0.5, 1.0, 1.0, 1.0, 0.2]), 2)
+    assert list(ids) == [1, 2] and gap == 0.0
+    np.testing.assert_allclose(w, [0.5, 0.5])
+
+
+def test_argmax_lowest_index_on_ties():
+    x = rng.standard_normal(1000)
+    x[[17, 400, 999]] = 9.0
+    assert oracle.argmax(x) == 17
+    y = rng.standard_normal(5000)
+    assert oracle.argmax(y) == int(np.argmax(y.astype(np.float32)))
+    # values equal in fp32 but not in fp64 are a tie
+    z = np.zeros(10)
+    z[3], z[6] = 1.0, 1.0 + 1e-12
+    assert oracle.argmax(z) == 3
+
+
+def test_round_bf16_matches_torch():
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    mine = np.array([oracle.round_bf16(float(a)) for a in v])
+    ref = torch.tensor(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(mine, ref)
+
+
+# ----------------------------------------------------------------------------- whole model
+
+def _torch_forward(wl, W, tokens):
+    """The same model built from torch library routines (float64), full causal recompute."""
+    E, H, Hk, d = wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim
+
+    def mat(m, s=None):
+        if m.dtype == np.uint16:
+            a = torch.tensor(synth.bf16_to_f32(m).astype(np.float64))
+        elif m.dtype == np.int8:
+            a = torch.tensor(m.astype(np.float64)) * torch.tensor(s.astype(np.float64))[:, None]
+        else:
+            a = torch.tensor(m.astype(np.float64))
+        return a
+
+    def act(t):
+        if wl.act_dtype == synth.BF16:
+            return t.to(torch.bfloat16).to(torch.float64)
+        return t.to(torch.float32).to(torch.float64)
+
+    def kvr(t):
+        if wl.kv_dtype == synth.BF16:
+            return t.to(torch.bfloat16).to(torch.float64)
+        return t.to(torch.float32).to(torch.float64)
+
+    n = len(tokens)
+    x = mat(W["tok_embd"])[torch.tensor(np.asarray(tokens, dtype=np.int64))]
+    pos = torch.arange(n, dtype=torch.float64)
+    freqs = 1.0 / (wl.rope_theta ** (torch.arange(0, d, 2, dtype=torch.float64) / d))
+    rot = torch.polar(torch.ones(n, d // 2, dtype=torch.float64), pos[:, None] * freqs[None])
+
+    def rope(t):  # t [n, heads, d]
+        z = torch.view_as_complex(t.reshape(n, t.shape[1], d // 2, 2).contiguous())
+        return torch.view_as_real(z * rot[:, None, :]).reshape(t.shape)
+
+    tpos = torch.arange(n)
+    mask = tpos[None, :] <= tpos[:, None]
+    if wl.sliding_window > 0:
+        mask &= tpos[None, :] > tpos[:, None] - wl.sliding_window
+    for L in W["layers"]:
+        g = torch.tensor(L["attn_norm"].astype(np.float64))
+        xn = act(F.rms_norm(x, (E,), weight=g, eps=wl.rms_norm_eps))
+        q = rope((xn @ mat(L["wq"], L["s_q"]).T).reshape(n, H, d))
+        k = kvr(rope((xn @ mat(L["wk"], L["s_k"]).T).reshape(n, Hk, d)))
+        v = kvr((xn @ mat(L["wv"], L["s_v"]).T).reshape(n, Hk, d))
+        o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
+                                           v.transpose(0, 1)[None], attn_mask=mask[None, None],
+                                           enable_gqa=True)[0].transpose(0, 1).reshape(n, H * d)
+        x = x + act(o) @ mat(L["wo"], L["s_o"]).T
+        g2 = torch.tensor(L["ffn_norm"].astype(np.float64))
+        xn2 = act(F.rms_norm(x, (E,), weight=g2, eps=wl.rms_norm_eps))
+        if wl.n_expert == 0:
+            h = act(F.silu(xn2 @ mat(L["w_gate"][0], L["s_gate"][0]).T)
+                    * (xn2 @ mat(L["w_up"][0], L["s_up"][0]).T))
+            x = x + h @ mat(L["w_down"][0], L["s_down"][0]).T
+        else:
+            r = xn2 @ mat(L["w_router"]).T
+            top = torch.topk(r, wl.n_expert_used, dim=-1)
+            wts = torch.softmax(top.values, dim=-1)
+            out = torch.zeros_like(x)
+            for t in range(n):
+                for a in range(wl.n_expert_used):
+                    e = int(top.indices[t, a])
+                    h = act(F.silu(xn2[t] @ mat(L["w_gate"][e], L["s_gate"][e]).T)
+                            * (xn2[t] @ mat(L["w_up"][e], L["s_up"][e]).T))
+                    out[t] += wts[t, a] * (h @ mat(L["w_down"][e], L["s_down"][e]).T)
+            x = x + out
+    xf = act(F.rms_norm(x[-1], (E,), weight=torch.tensor(W["out_norm"].astype(np.float64)),
+                        eps=wl.rms_norm_eps))
+    return (xf @ mat(W["w_out"], W["s_out"]).T).numpy()
+
+
+SMALL = [
+    synth.tiny_fp32().with_(name="small-dense-f32", n_layer=2),
+    synth.tiny_fp32().with_(name="small-window-bf16", w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                            act_dtype=synth.BF16, sliding_window=3, seed=11),
+    synth.tiny_fp32().with_(name="small-int8", w_dtype=synth.I8, kv_dtype=synth.BF16,
+                            act_dtype=synth.BF16, seed=12, n_head=4, n_kv_head=4, head_dim=64),
+    synth.tiny_fp32().with_(name="small-moe", n_expert=4, n_expert_used=2, seed=13, n_ff=96),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_whole_model_matches_torch_composition(wl):
+    W = synth.make_weights(wl)
+    m = oracle.Model(wl, W)
+    tokens = list(synth.uniform_int(wl.seed, 99, 9, 0, wl.n_vocab - 1))
+    ref = _torch_forward(wl, W, tokens)
+    lf, _ = m.full_recompute(tokens)
+    rel = np.linalg.norm(lf - ref) / np.linalg.norm(ref)
+    assert rel < 1e-12, rel
+    st = m.new_state(16)
+    for t in tokens:
+        li, _ = st.step(int(t))
+    np.testing.assert_array_equal(li, lf)
+
+
+def test_incremental_equals_full_recompute_tiny_fp32():
+    """The KV-cache bookkeeping: every cached step equals a from-scratch causal forward."""
+    wl = synth.tiny_fp32()
+    m = oracle.Model(wl, synth.make_weights(wl))
+    st = m.new_state(wl.prompt_len + wl.steps)
+    seq = [int(t) for t in wl.prompt_tokens()]
+    for i, t in enumerate(seq):
+        li, am = st.step(t)
+    for s in range(wl.steps):
+        seq.append(am)
+        li, am = st.step(am)
+        if s % 4 == 0 or s == wl.steps - 1:
+            lf, af = m.full_recompute(seq)
+            rel = np.linalg.norm(li - lf) / np.linalg.norm(lf)
+            assert rel <= 1e-12 and am == af, (s, rel)
+    assert st.pos == wl.prompt_len + wl.steps
+
+
+def test_single_expert_equals_dense():
+    dense = synth.tiny_fp32().with_(n_layer=1, seed=21)
+    moe = dense.with_(n_expert=1, n_expert_used=1)
+    Wd = synth.make_weights(dense)
+    Wm = synth.make_weights(moe)
+    # the router of a one-expert model changes nothing: the expert weight is 1
+    for k in ("w_gate", "w_up", "w_down"):
+        np.testing.assert_array_equal(Wd["layers"][0][k][0], Wm["layers"][0][k][0])
+    toks = [3, 99, 500, 7]
+    ld, _ = oracle.Model(dense, Wd).full_recompute(toks)
+    lm, _ = oracle.Model(moe, Wm).full_recompute(toks)
+    np.testing.assert_allclose(lm, ld, rtol=1e-14, atol=1e-15)
+
+
+def test_identical_experts_equal_dense():
+    dense = synth.tiny_fp32().with_(n_layer=1, seed=22)
+    moe = dense.with_(n_expert=4, n_expert_used=2)
+    Wd = synth.make_weights(dense)
+    Wm = synth.make_weights(moe)
+    for k in ("w_gate", "w_up", "w_down"):
+        Wm["layers"][0][k] = [Wd["layers"][0][k][0]] * 4
+    for k in ("tok_embd", "out_norm", "w_out"):
+        Wm[k] = Wd[k]
+    for k in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo"):
+        Wm["layers"][0][k] = Wd["layers"][0][k]
+    toks = [1, 2, 3]
+    ld, _ = oracle.Model(dense, Wd).full_recompute(toks)
+    lm, _ = oracle.Model(moe, Wm).full_recompute(toks)
+    np.testing.assert_allclose(lm, ld, rtol=1e-13, atol=1e-14)
+
+
+def test_state_errors():
+    wl = synth.tiny_fp32().with_(n_layer=1)
+    m = oracle.Model(wl, synth.make_weights(wl))
+    st = m.new_state(2)
+    st.step(1)
+    st.step(2)
+    with pytest.raises(ValueError):
+        st.step(3)  # pos 2 is past max_ctx
+    st2 = m.new_state(4)
+    with pytest.raises(ValueError):
+        st2.step(wl.n_vocab)  # token id out of range
