@@ -1,0 +1,219 @@
+/*
+ * pn.h - C ABI of the MI355X one-token decode library.
+ *
+ * The library computes the architecture forward step of a Llama-family
+ * transformer, forward(model, token, state) -> logits, one token per sequence
+ * ("Core Engine API", section "pn_model struct": the forward function pointer
+ * takes a model, one token and a state and returns the logits), for one
+ * sequence or for a batch of independent sequences that each advance one token
+ * at their own position ("Engine Architecture", section "Continuous-Batch VLM
+ * Decoder": one M=B decode over all slots, each slot finishing on its own).
+ *
+ * Conventions shared by every entry point:
+ *  - Plain C types only.  Pointers named *_dev are device pointers; every
+ *    other pointer is host memory.  `stream` is a hipStream_t passed as void*
+ *    (NULL = the default stream).
+ *  - The caller owns all device memory.  The library owns only the host
+ *    handles (pn_model, pn_state) and allocates no device memory, neither at
+ *    create time nor per token: a model and each state live in buffers the
+ *    caller passes in, sized by pn_model_bytes / pn_state_bytes.  This mirrors
+ *    the pages' pre-sized scratch arena with no allocation per token ("Core
+ *    Engine API", section "Scratch (arena) estimation"; "Engine
+ *    Architecture", section "Memory Model").
+ *  - Calls that take a stream only enqueue work on it and return; completion
+ *    is observed through the stream.  This is the device form of the pages'
+ *    non-blocking begin/poll step ("Core Engine API", section "Async
+ *    forward-step seam").  Calls that use one model must be ordered on one
+ *    stream (the pages keep one step in flight per model).  A state must not
+ *    be used by two calls at once.
+ *  - Return value: 0 on success, else a negative PN_E* code; every failure
+ *    sets a message readable through pn_last_error() (thread-local).  All
+ *    argument checks happen on the host before anything is enqueued, so a
+ *    failed call leaves the device untouched.
+ */
+#ifndef PN_H
+#define PN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PN_OK = 0,
+    PN_EINVAL = -1,       /* bad config, NULL pointer, duplicate state, bad token/layer index */
+    PN_ERANGE = -2,       /* buffer too small, position past the state's capacity */
+    PN_EUNSUPPORTED = -3, /* valid but unsupported shape or dtype combination */
+    PN_EHIP = -4          /* HIP runtime failure */
+};
+
+typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2 } pn_dtype;
+
+/* Model dimensions and storage types.  Field names and defaults follow the
+ * pages' config keys ("Engine Architecture", section "Config Parsing"):
+ * n_kv_head defaults to n_head, n_ctx to 2048, rope_theta to 10000,
+ * rms_norm_eps to 1e-5, sliding_window to 0 (off); here n_kv_head 0 stands
+ * for n_head.  n_expert > 0 selects the
+ * top-k MoE FFN ("Engine Architecture", section "Architecture Detection":
+ * Mixtral is llama with an expert count > 0).
+ *
+ *  w_dtype   matrices: PN_F32, PN_BF16, or PN_I8 (symmetric int8 with one fp32
+ *            scale per output row).  The token embedding and the MoE router are
+ *            fp32 when w_dtype is PN_F32 and bf16 otherwise; norm gains are fp32.
+ *  kv_dtype  cached K and V: PN_F32 or PN_BF16 (k is cached after RoPE).
+ *  act_dtype type that every mat-vec input (normed x, attention output, FFN
+ *            hidden, final normed x) is rounded to: PN_F32 or PN_BF16.  The
+ *            residual stream, q, softmax and all accumulators stay fp32.
+ *            PN_I8 weights need act_dtype PN_BF16.
+ *  max_batch largest n accepted by pn_forward_batch (1..16; with act_dtype
+ *            PN_F32 and bf16/int8 weights, 1..5). */
+typedef struct pn_config {
+    int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab;
+    int32_t n_ctx;          /* default state capacity when pn_state_* is given max_ctx 0 */
+    int32_t n_expert;       /* 0 = dense SwiGLU FFN */
+    int32_t n_expert_used;  /* top-k (1..8) when n_expert > 0 */
+    int32_t sliding_window; /* 0 = off; else the step at pos attends to pos-W+1..pos */
+    int32_t max_batch;
+    float rope_theta, rms_norm_eps;
+    int32_t w_dtype, kv_dtype, act_dtype; /* pn_dtype values */
+} pn_config;
+
+/* Device pointers of one layer's weights, logical row-major [out][in].  The
+ * expert matrices are stacked: X = max(1, n_expert) blocks of gate/up [F][E]
+ * and down [E][F].  Scales (s_*) are required iff w_dtype == PN_I8 (one fp32
+ * per output row, stacked like the matrices), else ignored. */
+typedef struct pn_layer_weights {
+    const float *attn_norm, *ffn_norm;   /* [E] */
+    const void *wq, *wk, *wv, *wo;       /* [H*d][E], [Hk*d][E], [Hk*d][E], [E][H*d] */
+    const void *w_gate, *w_up, *w_down;  /* [X][F][E], [X][F][E], [X][E][F] */
+    const void *w_router;                /* [n_expert][E]; NULL for dense */
+    const float *s_q, *s_k, *s_v, *s_o, *s_gate, *s_up, *s_down;
+} pn_layer_weights;
+
+typedef struct pn_weights {
+    const void *tok_embd;  /* [V][E] */
+    const float *out_norm; /* [E] */
+    const void *w_out;     /* [V][E] LM head (untied) */
+    const float *s_out;    /* [V] iff PN_I8 */
+    const pn_layer_weights *layers; /* host array of n_layer entries */
+} pn_weights;
+
+typedef struct pn_model pn_model;
+typedef struct pn_state pn_state;
+
+/* Fill *cfg with the pages' defaults; dimensions are left 0. */
+void pn_config_default(pn_config *cfg);
+
+/* Validate a config without touching the device.  0 or PN_EINVAL / PN_EUNSUPPORTED. */
+int pn_config_check(const pn_config *cfg);
+
+/* Bytes of device memory a model of this config needs (packed weights plus
+ * per-model scratch for max_batch sequences); 0 if the config is invalid. */
+size_t pn_model_bytes(const pn_config *cfg);
+
+/* Build a model in the caller's device buffer `dev_buf` (>= pn_model_bytes,
+ * 256-byte aligned): the weights are re-laid into the library's tiled format
+ * by kernels enqueued on `stream`.  The source weights may be freed once that
+ * stream work has completed.  On success *out holds a host handle. */
+int pn_model_create(const pn_config *cfg, const pn_weights *w, void *dev_buf, size_t bytes,
+                    void *stream, pn_model **out);
+
+/* The same in steps, for models whose source weights do not fit on the device
+ * next to the packed copy: pn_model_init lays the model out in dev_buf without
+ * touching the device; pn_model_load_globals packs the embedding, final norm
+ * and LM head; pn_model_load_layer packs one layer.  The model may be used
+ * once the globals and every layer have been loaded and that stream work has
+ * completed; each source buffer may be freed once its call's work has. */
+int pn_model_init(const pn_config *cfg, void *dev_buf, size_t bytes, pn_model **out);
+int pn_model_load_globals(pn_model *m, const void *tok_embd, const float *out_norm, const void *w_out,
+                          const float *s_out, void *stream);
+int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *w, void *stream);
+
+/* Release the host handle (the device buffer stays the caller's). */
+void pn_model_free(pn_model *m);
+
+/* Bytes of device memory one state of capacity max_ctx positions needs (paged
+ * K/V cache for every layer, page table, attention split scratch); 0 if invalid. */
+size_t pn_state_bytes(const pn_model *m, int32_t max_ctx);
+
+/* Create a state (pos = 0, K/V zeroed, identity page table) in `dev_buf`
+ * (>= pn_state_bytes, 256-byte aligned).  Zeroing is enqueued on `stream`. */
+int pn_state_new(pn_model *m, int32_t max_ctx, void *dev_buf, size_t bytes, void *stream,
+                 pn_state **out);
+
+/* Zero every cached K and V and set pos = 0 ("Core Engine API", section
+ * "State lifecycle": reset zeros the kv tensors and resets pos). */
+int pn_state_reset(pn_state *s, void *stream);
+
+/* Write cached K and V of positions pos0..pos0+n-1 of one layer from device
+ * arrays k_dev, v_dev laid out [n][n_kv_head][head_dim] in kv_dtype (k after
+ * RoPE).  Used to resume or to prefill a cache.  Does not change pos. */
+int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const void *k_dev,
+                    const void *v_dev, void *stream);
+
+/* Map logical page i (positions i*page_size .. i*page_size+page_size-1) to
+ * physical page pages[i] of the state's own pool.  `pages` is a host array
+ * holding a permutation of 0..n-1, n = pn_state_pages(s).  Cached contents are
+ * not moved: set the table before writing K/V. */
+int pn_state_set_page_table(pn_state *s, const int32_t *pages, int32_t n, void *stream);
+int32_t pn_state_pages(const pn_state *s);
+int32_t pn_page_size(void);
+
+/* Number of positions already cached (the position the next step writes). */
+int pn_state_set_pos(pn_state *s, int32_t pos);
+int32_t pn_state_pos(const pn_state *s);
+int32_t pn_state_max_ctx(const pn_state *s);
+
+/* Read (and clear) the state's sticky device error flags; synchronizes
+ * `stream`.  Bit 0: a token id outside [0, n_vocab) was fed (row 0 was used
+ * instead).  Bit 1: a NaN logit was seen by the argmax. */
+int pn_state_check(pn_state *s, void *stream, int32_t *flags_out);
+
+void pn_state_free(pn_state *s);
+
+/* One decode step of one sequence: embed token_dev[0], append its k and v at
+ * pos, attend over the window ending at pos, run the FFN, and write the
+ * logits (logits_dev [n_vocab] fp32, may be NULL) and the greedy id (argmax_dev
+ * [1] int32, lowest index among equal maxima; may be NULL).  pos is advanced
+ * on the host at enqueue.  token_dev may alias argmax_dev of the previous step
+ * (greedy feedback with no host round trip). */
+int pn_forward_step(pn_model *m, pn_state *s, const int32_t *token_dev, float *logits_dev,
+                    int32_t *argmax_dev, void *stream);
+
+/* One decode step of n distinct states (1 <= n <= max_batch), each at its own
+ * pos: row i of tokens_dev [n], logits_dev [n][n_vocab] and argmax_dev [n]
+ * belongs to states[i].  Same semantics as n independent pn_forward_step calls. */
+int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int32_t *tokens_dev,
+                     float *logits_dev, int32_t *argmax_dev, void *stream);
+
+/* ---- tuning and measurement ------------------------------------------------ */
+
+/* Kernel classes, for timing. */
+enum {
+    PN_K_EMBED = 0, PN_K_QKV, PN_K_ATTN, PN_K_O, PN_K_GATEUP, PN_K_DOWN, PN_K_LMHEAD,
+    PN_K_ARGMAX, PN_K_ROUTER, PN_K_MOE_GATEUP, PN_K_MOE_DOWN, PN_K_MOE_COMBINE, PN_K_COUNT
+};
+
+/* Options: PN_OPT_ATTN_KEYS_PER_SPLIT (0 = automatic, else a multiple of 256
+ * keys handled by one attention work-group; the result changes only by fp32
+ * rounding). */
+enum { PN_OPT_ATTN_KEYS_PER_SPLIT = 1 };
+int pn_model_set_option(pn_model *m, int32_t option, int64_t value);
+
+/* Time every launch of kernel class `kernel` with HIP events recorded on the
+ * launch stream, from pn_profile_begin until pn_profile_end (which
+ * synchronizes the stream and reports the summed milliseconds and the
+ * number of launches). */
+int pn_profile_begin(pn_model *m, int32_t kernel);
+int pn_profile_end(pn_model *m, void *stream, double *total_ms, int64_t *launches);
+
+/* Message of the last failure on this thread ("" if none). */
+const char *pn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PN_H */

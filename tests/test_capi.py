@@ -1,0 +1,123 @@
+"""The C ABI on the host: every declared symbol is exported, the config defaults
+are the pages', and invalid arguments are rejected before any device work."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import token_decode_amd as td
+from token_decode_amd import _capi as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pn_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = C.lib()
+    names = declared_functions()
+    assert len(names) >= 25
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(C.EXPORTS)
+
+
+def test_config_defaults_match_pages():
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "config_defaults.json")))
+    cfg = C.pn_config()
+    C.lib().pn_config_default(ctypes.byref(cfg))
+    d = gold["defaults"]
+    assert cfg.n_ctx == d["n_ctx"]
+    assert cfg.rope_theta == pytest.approx(d["rope_theta"])
+    assert cfg.rms_norm_eps == pytest.approx(d["rms_norm_eps"], rel=1e-6)
+    assert cfg.sliding_window == d["sliding_window"]
+
+
+def good_cfg(**kw):
+    from token_decode_amd import device as dv
+    base = dict(n_layer=2, n_embd=256, n_head=8, n_kv_head=2, head_dim=32, n_ff=688, n_vocab=1024,
+                w_dtype=C.PN_F32, kv_dtype=C.PN_F32, act_dtype=C.PN_F32)
+    base.update(kw)
+    return dv.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_head=6, n_kv_head=4), C.PN_EINVAL),
+    (dict(head_dim=48), C.PN_EUNSUPPORTED),
+    (dict(n_head=16, n_kv_head=1), C.PN_EUNSUPPORTED),
+    (dict(n_layer=0), C.PN_EINVAL),
+    (dict(w_dtype=C.PN_I8, act_dtype=C.PN_F32), C.PN_EUNSUPPORTED),
+    (dict(kv_dtype=C.PN_I8), C.PN_EINVAL),
+    (dict(max_batch=17), C.PN_EINVAL),
+    (dict(w_dtype=C.PN_BF16, act_dtype=C.PN_F32, max_batch=6), C.PN_EUNSUPPORTED),
+    (dict(n_expert=4, n_expert_used=5), C.PN_EINVAL),
+    (dict(sliding_window=-1), C.PN_EINVAL),
+    (dict(rope_theta=0.0), C.PN_EINVAL),
+])
+def test_bad_configs_rejected(kw, code):
+    cfg = good_cfg(**kw)
+    assert C.lib().pn_config_check(ctypes.byref(cfg)) == code
+    assert C.lib().pn_last_error()
+    assert C.lib().pn_model_bytes(ctypes.byref(cfg)) == 0
+
+
+def test_good_configs_and_sizes():
+    L = C.lib()
+    for kw in (dict(), dict(w_dtype=C.PN_BF16, kv_dtype=C.PN_BF16, act_dtype=C.PN_F32, max_batch=5),
+               dict(w_dtype=C.PN_I8, kv_dtype=C.PN_BF16, act_dtype=C.PN_BF16, max_batch=16),
+               dict(n_expert=8, n_expert_used=2, w_dtype=C.PN_BF16, act_dtype=C.PN_BF16),
+               dict(n_kv_head=0)):
+        cfg = good_cfg(**kw)
+        assert L.pn_config_check(ctypes.byref(cfg)) == 0, L.pn_last_error()
+        assert L.pn_model_bytes(ctypes.byref(cfg)) > 0
+
+
+def test_model_bytes_cover_packed_weights():
+    """Llama-3-8B shape in bf16: the packed weights alone are 16.06e9 bytes."""
+    cfg = good_cfg(n_layer=32, n_embd=4096, n_head=32, n_kv_head=8, head_dim=128, n_ff=14336,
+                   n_vocab=128256, w_dtype=C.PN_BF16, kv_dtype=C.PN_BF16)
+    n = C.lib().pn_model_bytes(ctypes.byref(cfg))
+    params = 32 * (4096 * 6144 + 4096 * 4096 + 3 * 4096 * 14336) + 2 * 128256 * 4096
+    assert 2 * params <= n < 2 * params * 1.01
+
+
+def test_init_rejects_bad_buffers_without_device_work():
+    L = C.lib()
+    cfg = good_cfg()
+    need = L.pn_model_bytes(ctypes.byref(cfg))
+    h = ctypes.c_void_p()
+    assert L.pn_model_init(ctypes.byref(cfg), None, need, ctypes.byref(h)) == C.PN_EINVAL
+    assert L.pn_model_init(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), need - 1, ctypes.byref(h)) == C.PN_ERANGE
+    assert L.pn_model_init(ctypes.byref(cfg), ctypes.c_void_p((1 << 20) + 8), need, ctypes.byref(h)) == C.PN_EINVAL
+    # a layout on a fake (never dereferenced) address: sizing queries need no device
+    assert L.pn_model_init(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), need, ctypes.byref(h)) == 0
+    try:
+        assert L.pn_state_bytes(h, 132) > 0
+        assert L.pn_state_bytes(h, -1) == 0
+        st = ctypes.c_void_p()
+        assert L.pn_state_new(h, 64, None, 1 << 20, None, ctypes.byref(st)) == C.PN_EINVAL
+        assert L.pn_state_new(h, 64, ctypes.c_void_p(1 << 21), 16, None, ctypes.byref(st)) == C.PN_ERANGE
+        arr = (ctypes.c_void_p * 1)(None)
+        assert L.pn_forward_batch(h, arr, 1, ctypes.c_void_p(1 << 22), None, None, None) == C.PN_EINVAL
+        assert L.pn_forward_batch(h, arr, 2, ctypes.c_void_p(1 << 22), None, None, None) == C.PN_EINVAL
+        assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KEYS_PER_SPLIT, 100) == C.PN_EINVAL
+        assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KEYS_PER_SPLIT, 512) == 0
+        assert L.pn_profile_begin(h, 99) == C.PN_EINVAL
+        lw = C.pn_layer_weights()
+        assert L.pn_model_load_layer(h, 0, ctypes.byref(lw), None) == C.PN_EINVAL
+        assert L.pn_model_load_layer(h, 5, ctypes.byref(lw), None) == C.PN_EINVAL
+    finally:
+        L.pn_model_free(h)
+
+
+def test_package_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(C, "_lib", None)
+    with pytest.raises(ImportError):
+        C.lib()

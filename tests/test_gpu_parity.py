@@ -1,0 +1,95 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Every case runs the GPU on the oracle's greedy trajectory (the GPU is fed the
+oracle's tokens) and compares every step's logits (relative L2 within 1e-4 for
+fp32 models, 2e-2 for bf16 / int8) and greedy ids (equal, or a near tie that
+the oracle's top-two gap cannot resolve).  Shapes are chosen to span several
+tiles with ragged tails: dimensions that are not multiples of the tile widths,
+several attention splits and partial KV pages.
+"""
+import pytest
+
+import synth
+
+from harness import Pair, log, run_batch, run_single
+
+pytestmark = pytest.mark.gpu
+
+
+def ragged(name, **kw):
+    base = dict(n_layer=2, n_embd=200, n_head=6, n_kv_head=2, head_dim=32, n_ff=300, n_vocab=1000,
+                rope_theta=10000.0, seed=31)
+    base.update(kw)
+    return synth.Workload(name, **base)
+
+
+def test_tiny_fp32_full_run():
+    """The tiny fp32 model: a 4-token prompt then 128 greedy steps (positions 0..131)."""
+    wl = synth.tiny_fp32()
+    p = Pair(wl)
+    worst, near, n = run_single(p, 0, wl.prompt_tokens(), wl.steps)
+    log("  tiny-fp32: %d steps, worst rel L2 %.2e, near ties %d" % (n, worst, near))
+    assert near == 0
+
+
+CASES = [
+    ragged("ragged-f32", w_dtype=synth.F32, kv_dtype=synth.F32, act_dtype=synth.F32),
+    ragged("ragged-bf16-actf32-window", w_dtype=synth.BF16, kv_dtype=synth.BF16,
+           act_dtype=synth.F32, sliding_window=300, seed=32),
+    ragged("ragged-bf16-d64-g8", n_head=8, n_kv_head=1, head_dim=64, w_dtype=synth.BF16,
+           kv_dtype=synth.BF16, act_dtype=synth.BF16, seed=33),
+    ragged("ragged-int8-d128", n_head=4, n_kv_head=2, head_dim=128, w_dtype=synth.I8,
+           kv_dtype=synth.BF16, act_dtype=synth.BF16, seed=34, n_ff=520),
+    ragged("ragged-f32-kvbf16-mha", n_head=4, n_kv_head=4, w_dtype=synth.F32, kv_dtype=synth.BF16,
+           act_dtype=synth.BF16, seed=35),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_ragged_single(wl):
+    """Batch 1 with 700 cached positions (several attention splits), then 6 steps."""
+    p = Pair(wl)
+    toks = synth.uniform_int(wl.seed, 1 << 20, 2, 0, wl.n_vocab - 1)
+    worst, near, n = run_single(p, 700, toks, 4)
+    log("  %s: worst rel L2 %.2e near %d" % (wl.name, worst, near))
+
+
+def test_tiny_from_position_zero_bf16():
+    wl = synth.tiny_fp32().with_(name="tiny-bf16", w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                                 act_dtype=synth.BF16, seed=41)
+    p = Pair(wl)
+    worst, near, n = run_single(p, 0, wl.prompt_tokens(), 20)
+    log("  tiny-bf16: worst rel L2 %.2e near %d" % (worst, near))
+
+
+def test_batched_slots_window():
+    """Five slots at different positions (one inside the first page) with a window."""
+    wl = ragged("batch-bf16-window", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.BF16,
+                sliding_window=200, seed=42)
+    p = Pair(wl, max_batch=5)
+    worst, near = run_batch(p, [3, 64, 129, 450, 1000], 3)
+    log("  batch: worst rel L2 %.2e near %d" % (worst, near))
+
+
+def test_batched_fp32_activations():
+    wl = ragged("batch-bf16-actf32", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.F32,
+                seed=43)
+    p = Pair(wl, max_batch=5)
+    worst, near = run_batch(p, [0, 17, 300, 301, 999], 3)
+    log("  batch f32 act: worst rel L2 %.2e near %d" % (worst, near))
+
+
+def test_moe_small_batched():
+    wl = ragged("moe-small", n_expert=6, n_expert_used=2, w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                act_dtype=synth.BF16, seed=44, n_ff=160)
+    p = Pair(wl, max_batch=7)
+    worst, near = run_batch(p, [5, 70, 200, 260, 511, 600, 10], 3)
+    log("  moe: worst rel L2 %.2e near %d" % (worst, near))
+
+
+def test_moe_single_fp32():
+    wl = ragged("moe-f32", n_expert=4, n_expert_used=2, w_dtype=synth.F32, kv_dtype=synth.F32,
+                act_dtype=synth.F32, seed=45, n_ff=96)
+    p = Pair(wl)
+    worst, near, n = run_single(p, 100, [7, 8], 6)
+    log("  moe f32: worst rel L2 %.2e near %d" % (worst, near))

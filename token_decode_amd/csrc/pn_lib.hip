@@ -1,0 +1,973 @@
+// pn_lib.hip - host engine behind the C ABI in include/pn.h.
+//
+// The engine validates arguments, lays a model and each state out in the
+// caller's device buffers, packs weights once, and enqueues one decode step as
+// a fixed sequence of kernels on the caller's stream.  It never allocates
+// device memory and never synchronizes except in pn_state_check and
+// pn_profile_end.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pn.h"
+#include "pn_kernels.hpp"
+
+using namespace pn;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+struct Bump {  // offset assignment inside one caller buffer
+    size_t off = 0;
+    size_t take(size_t n) {
+        size_t at = off;
+        off = align256(off + n);
+        return at;
+    }
+};
+
+struct Mat {  // one packed matrix (or a stack of experts' matrices)
+    int N = 0, K = 0, n_tiles = 0, KT = 0;
+    size_t bytes1 = 0;  // bytes of one packed matrix
+    size_t off = 0;     // offset of the packed tiles
+    size_t soff = 0;    // offset of row scales (int8 only)
+};
+
+struct LayerOff {
+    size_t attn_norm, ffn_norm, router;
+    Mat qkv, o, gate, up, down;
+};
+
+struct Plan {
+    int kc = 1, ktc = 1, gx = 1, gz = 1;
+    size_t lds = 0;
+};
+
+}  // namespace
+
+struct pn_model {
+    pn_config cfg;
+    char *base = nullptr;
+    size_t bytes = 0;
+    int E, H, Hk, D, F, V, G, X, n_used, wt, at, kvt, pieces, rows_max;
+    int Nqkv;
+    std::vector<LayerOff> L;
+    size_t embd, out_norm;
+    Mat out;
+    // scratch
+    size_t x, q, o, h, y, route_ids, route_w, part, cnt, am_val, am_idx;
+    size_t part_bytes = 0, cnt_count = 0, am_count = 0;
+    int attn_kps = 0;  // 0 = automatic
+    int prof_kernel = -1;
+    std::vector<hipEvent_t> ev;
+    size_t ev_used = 0;
+};
+
+struct pn_state {
+    pn_model *m;
+    char *base;
+    size_t bytes;
+    int max_ctx, n_pages, pos, s_cap;
+    size_t kpool, vpool, layer_bytes, pt, part, cnt, err;
+};
+
+namespace {
+
+int dtype_size(int dt) { return dt == PN_F32 ? 4 : (dt == PN_BF16 ? 2 : 1); }
+
+// n_kv_head 0 stands for n_head (the pages' default for the key)
+pn_config normalized(const pn_config &c) {
+    pn_config n = c;
+    if (n.n_kv_head == 0) n.n_kv_head = n.n_head;
+    return n;
+}
+
+int check_config_n(const pn_config *c);
+
+int check_config(const pn_config *c) {
+    if (!c) return fail(PN_EINVAL, "config is NULL");
+    pn_config n = normalized(*c);
+    return check_config_n(&n);
+}
+
+int check_config_n(const pn_config *c) {
+    if (c->n_layer < 1 || c->n_embd < 1 || c->n_head < 1 || c->n_kv_head < 1 || c->n_ff < 1 ||
+        c->n_vocab < 1)
+        return fail(PN_EINVAL, "dimensions must be positive");
+    if (c->n_head % c->n_kv_head != 0) return fail(PN_EINVAL, "n_head must be a multiple of n_kv_head");
+    if (c->n_head / c->n_kv_head > kMaxG)
+        return fail(PN_EUNSUPPORTED, "at most %d query heads per kv head", kMaxG);
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+        return fail(PN_EUNSUPPORTED, "head_dim must be 32, 64 or 128");
+    if (c->n_expert < 0 || c->n_expert > 64) return fail(PN_EINVAL, "n_expert must be in [0, 64]");
+    if (c->n_expert > 0 && (c->n_expert_used < 1 || c->n_expert_used > std::min(8, c->n_expert)))
+        return fail(PN_EINVAL, "n_expert_used must be in [1, min(8, n_expert)]");
+    if (c->sliding_window < 0) return fail(PN_EINVAL, "sliding_window must be >= 0");
+    if (c->n_ctx < 0) return fail(PN_EINVAL, "n_ctx must be >= 0");
+    if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(PN_EINVAL, "rope_theta must be > 0");
+    if (!(c->rms_norm_eps >= 0.f) || !std::isfinite(c->rms_norm_eps)) return fail(PN_EINVAL, "rms_norm_eps must be >= 0");
+    if (c->w_dtype < PN_F32 || c->w_dtype > PN_I8) return fail(PN_EINVAL, "bad w_dtype");
+    if (c->kv_dtype != PN_F32 && c->kv_dtype != PN_BF16) return fail(PN_EINVAL, "kv_dtype must be F32 or BF16");
+    if (c->act_dtype != PN_F32 && c->act_dtype != PN_BF16) return fail(PN_EINVAL, "act_dtype must be F32 or BF16");
+    if (c->w_dtype == PN_I8 && c->act_dtype != PN_BF16)
+        return fail(PN_EUNSUPPORTED, "int8 weights need bf16 activations");
+    if (c->max_batch < 1 || c->max_batch > kMaxSlots) return fail(PN_EINVAL, "max_batch must be in [1, 16]");
+    const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
+    if (c->max_batch * pieces > kMaxRows)
+        return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
+                    c->max_batch, kMaxRows / pieces);
+    return PN_OK;
+}
+
+Mat make_mat(int N, int K, int wt) {
+    Mat m;
+    m.N = N;
+    m.K = K;
+    m.n_tiles = cdiv(N, 16);
+    m.KT = cdiv(K, tile_k(wt));
+    m.bytes1 = (size_t)m.n_tiles * m.KT * 1024;
+    return m;
+}
+
+size_t lds_of(int ktc, int rows, int ntw, int fb) {
+    return align256((size_t)ktc * 4 * rows * fb) + (size_t)kNW * ntw * 1024 + (size_t)ntw * 1024;
+}
+
+Plan make_plan(int gx, int gz, int KT, int rows, int ntw, int fb) {
+    Plan p;
+    p.gx = gx;
+    p.gz = gz;
+    int kc = 1;
+    for (;;) {
+        int ktc = cdiv(KT, kc);
+        bool big = lds_of(ktc, rows, ntw, fb) > 64 * 1024;
+        bool more = (long long)gx * gz * kc * kNW < 4096 && cdiv(KT, (long long)kc * 2) >= kNW * 8;
+        if ((big || more) && kc < KT) kc *= 2;
+        else break;
+    }
+    p.ktc = cdiv(KT, kc);
+    p.kc = cdiv(KT, p.ktc);
+    p.lds = lds_of(p.ktc, rows, ntw, fb);
+    return p;
+}
+
+// Lay out the model buffer; returns its size. Works on a zero base for sizing.
+size_t layout_model(pn_model *m) {
+    const pn_config &c = m->cfg;
+    m->E = c.n_embd;
+    m->H = c.n_head;
+    m->Hk = c.n_kv_head;
+    m->D = c.head_dim;
+    m->F = c.n_ff;
+    m->V = c.n_vocab;
+    m->G = c.n_head / c.n_kv_head;
+    m->X = std::max(1, c.n_expert);
+    m->n_used = c.n_expert > 0 ? c.n_expert_used : 1;
+    m->wt = c.w_dtype;
+    m->at = c.act_dtype;
+    m->kvt = c.kv_dtype;
+    m->pieces = (c.w_dtype == PN_BF16 && c.act_dtype == PN_F32) ? 3 : 1;
+    m->rows_max = c.max_batch * m->pieces;
+    m->Nqkv = (m->H + 2 * m->Hk) * m->D;
+    const int wt = m->wt, es_aux = (wt == PN_F32) ? 4 : 2;
+    const bool i8 = wt == PN_I8;
+    Bump bp;
+    m->embd = bp.take((size_t)m->V * m->E * es_aux);
+    m->out_norm = bp.take((size_t)m->E * 4);
+    m->out = make_mat(m->V, m->E, wt);
+    m->out.off = bp.take(m->out.bytes1);
+    if (i8) m->out.soff = bp.take((size_t)m->out.n_tiles * 16 * 4);
+    m->L.assign(c.n_layer, LayerOff{});
+    for (int l = 0; l < c.n_layer; ++l) {
+        LayerOff &L = m->L[l];
+        L.attn_norm = bp.take((size_t)m->E * 4);
+        L.ffn_norm = bp.take((size_t)m->E * 4);
+        L.router = c.n_expert > 0 ? bp.take((size_t)c.n_expert * m->E * es_aux) : 0;
+        L.qkv = make_mat(m->Nqkv, m->E, wt);
+        L.o = make_mat(m->E, m->H * m->D, wt);
+        L.gate = make_mat(m->F, m->E, wt);
+        L.up = make_mat(m->F, m->E, wt);
+        L.down = make_mat(m->E, m->F, wt);
+        for (Mat *mt : {&L.qkv, &L.o}) {
+            mt->off = bp.take(mt->bytes1);
+            if (i8) mt->soff = bp.take((size_t)mt->n_tiles * 16 * 4);
+        }
+        for (Mat *mt : {&L.gate, &L.up, &L.down}) {
+            mt->off = bp.take(mt->bytes1 * m->X);
+            if (i8) mt->soff = bp.take((size_t)mt->n_tiles * 16 * 4 * m->X);
+        }
+    }
+    // scratch
+    const int MB = c.max_batch, HD = m->H * m->D;
+    const int as = m->at == PN_F32 ? 4 : 2;
+    m->x = bp.take((size_t)MB * m->E * 4);
+    m->q = bp.take((size_t)MB * HD * 4);
+    m->o = bp.take((size_t)MB * HD * as);
+    m->h = bp.take((size_t)MB * m->n_used * m->F * as);
+    m->y = bp.take((size_t)MB * m->n_used * m->E * 4);
+    m->route_ids = bp.take((size_t)MB * m->n_used * 4);
+    m->route_w = bp.take((size_t)MB * m->n_used * 4);
+    // split-K scratch: the largest need over every GEMM and batch size
+    const int fb = frag_bytes(wt);
+    size_t pbytes = 0, ccount = 1;
+    for (int B = 1; B <= MB; ++B) {
+        const int rows = B * m->pieces;
+        const LayerOff &L = m->L[0];
+        struct { int gx, gz, KT, ntw; } g[] = {
+            {L.qkv.n_tiles, 1, L.qkv.KT, 1},
+            {L.o.n_tiles, 1, L.o.KT, 1},
+            {L.gate.n_tiles, c.n_expert > 0 ? m->X : 1, L.gate.KT, 2},
+            {L.down.n_tiles, c.n_expert > 0 ? m->X : 1, L.down.KT, 1},
+            {cdiv(m->out.n_tiles, 2), 1, m->out.KT, 2},
+        };
+        for (auto &e : g) {
+            Plan p = make_plan(e.gx, e.gz, e.KT, rows, e.ntw, fb);
+            if (p.kc > 1) {
+                pbytes = std::max(pbytes, (size_t)e.gx * e.gz * p.kc * e.ntw * 1024);
+                ccount = std::max(ccount, (size_t)e.gx * e.gz);
+            }
+        }
+    }
+    m->part_bytes = pbytes;
+    m->cnt_count = ccount;
+    m->part = bp.take(std::max<size_t>(pbytes, 256));
+    m->cnt = bp.take(ccount * 4);
+    m->am_count = (size_t)cdiv(m->out.n_tiles, 2) * MB;
+    m->am_val = bp.take(m->am_count * 4);
+    m->am_idx = bp.take(m->am_count * 4);
+    return bp.off;
+}
+
+int attn_kps_min() { return kAttnWaves * 64; }
+
+size_t layout_state(pn_state *s) {
+    const pn_model *m = s->m;
+    s->n_pages = cdiv(s->max_ctx, kPage);
+    const int es = dtype_size(m->kvt);
+    s->layer_bytes = (size_t)s->n_pages * m->Hk * kPage * m->D * es;
+    int keys = s->max_ctx;
+    if (m->cfg.sliding_window > 0) keys = std::min(keys, m->cfg.sliding_window);
+    s->s_cap = cdiv(keys, attn_kps_min());
+    Bump bp;
+    s->kpool = bp.take(s->layer_bytes * m->cfg.n_layer);
+    s->vpool = bp.take(s->layer_bytes * m->cfg.n_layer);
+    s->pt = bp.take((size_t)s->n_pages * 4);
+    s->part = bp.take((size_t)m->Hk * s->s_cap * m->G * (m->D + 2) * 4);
+    s->cnt = bp.take((size_t)m->Hk * 4);
+    s->err = bp.take(4);
+    return bp.off;
+}
+
+hipStream_t S(void *stream) { return reinterpret_cast<hipStream_t>(stream); }
+
+void fill32(void *p, size_t words, uint32_t v, hipStream_t s) {
+    if (!words) return;
+    int blocks = (int)std::min<size_t>(cdiv(words, 256), 4096);
+    hipLaunchKernelGGL(k_fill32, dim3(blocks), dim3(256), 0, s, (uint32_t *)p, (long long)words, v);
+}
+
+void copy_bytes(void *dst, const void *src, size_t n, hipStream_t s) {
+    if (!n) return;
+    int blocks = (int)std::min<size_t>(cdiv(n, 256), 8192);
+    hipLaunchKernelGGL(k_copy_bytes, dim3(blocks), dim3(256), 0, s, (uint8_t *)dst, (const uint8_t *)src,
+                       (long long)n);
+}
+
+void pack(const void *src, int N, int K, int wt, const Mat &mt, int tile_row0, uint8_t *dst_base,
+          hipStream_t s) {
+    const int nt = cdiv(N, 16);
+    uint8_t *dst = dst_base + (size_t)tile_row0 * mt.KT * 1024;
+    long long lanes = (long long)nt * mt.KT * 64;
+    int blocks = cdiv(lanes, 256);
+    if (wt == PN_F32)
+        hipLaunchKernelGGL(k_pack<4>, dim3(blocks), dim3(256), 0, s, (const uint8_t *)src, N, K, mt.KT, nt, dst);
+    else if (wt == PN_BF16)
+        hipLaunchKernelGGL(k_pack<2>, dim3(blocks), dim3(256), 0, s, (const uint8_t *)src, N, K, mt.KT, nt, dst);
+    else
+        hipLaunchKernelGGL(k_pack<1>, dim3(blocks), dim3(256), 0, s, (const uint8_t *)src, N, K, mt.KT, nt, dst);
+}
+
+// ---------------------------------------------------------------- launch dispatch
+
+template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR>
+void launch_gemm_t(const GemmArgs &g, const Plan &p, hipStream_t s) {
+    hipLaunchKernelGGL((k_gemm<WT, AT, PRO, EPI, NTW, PAIR>), dim3(p.gx, p.kc, p.gz), dim3(256), p.lds, s, g);
+}
+
+template <int PRO, int EPI, int NTW, bool PAIR>
+void launch_gemm(int wt, int at, const GemmArgs &g, const Plan &p, hipStream_t s) {
+    if (wt == PN_BF16 && at == PN_F32) launch_gemm_t<WT_BF16, AT_F32, PRO, EPI, NTW, PAIR>(g, p, s);
+    else if (wt == PN_BF16) launch_gemm_t<WT_BF16, AT_BF16, PRO, EPI, NTW, PAIR>(g, p, s);
+    else if (wt == PN_F32 && at == PN_F32) launch_gemm_t<WT_F32, AT_F32, PRO, EPI, NTW, PAIR>(g, p, s);
+    else if (wt == PN_F32) launch_gemm_t<WT_F32, AT_BF16, PRO, EPI, NTW, PAIR>(g, p, s);
+    else launch_gemm_t<WT_I8, AT_BF16, PRO, EPI, NTW, PAIR>(g, p, s);
+}
+
+template <int D, int KV>
+void launch_attn_d(int at, const AttnArgs &a, dim3 grid, hipStream_t s) {
+    if (at == PN_BF16) hipLaunchKernelGGL((k_attn<D, KV, AT_BF16>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<D, KV, AT_F32>), grid, dim3(256), 0, s, a);
+}
+
+void launch_attn(int D, int kvt, int at, const AttnArgs &a, dim3 grid, hipStream_t s) {
+    if (kvt == PN_BF16) {
+        if (D == 32) launch_attn_d<32, 1>(at, a, grid, s);
+        else if (D == 64) launch_attn_d<64, 1>(at, a, grid, s);
+        else launch_attn_d<128, 1>(at, a, grid, s);
+    } else {
+        if (D == 32) launch_attn_d<32, 0>(at, a, grid, s);
+        else if (D == 64) launch_attn_d<64, 0>(at, a, grid, s);
+        else launch_attn_d<128, 0>(at, a, grid, s);
+    }
+}
+
+// event timing of one kernel class
+struct Timed {
+    pn_model *m;
+    bool on;
+    hipStream_t s;
+    Timed(pn_model *mm, int k, hipStream_t ss) : m(mm), on(mm->prof_kernel == k), s(ss) {
+        if (!on) return;
+        if (m->ev_used + 2 > m->ev.size()) {
+            for (int i = 0; i < 256; ++i) {
+                hipEvent_t e;
+                if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
+                m->ev.push_back(e);
+            }
+        }
+        (void)hipEventRecord(m->ev[m->ev_used], s);
+    }
+    ~Timed() {
+        if (!on) return;
+        (void)hipEventRecord(m->ev[m->ev_used + 1], s);
+        m->ev_used += 2;
+    }
+};
+
+int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, float *logits, int32_t *amax,
+                 hipStream_t s) {
+    const pn_config &c = m->cfg;
+    char *mb = m->base;
+    const int E = m->E, HD = m->H * m->D, F = m->F;
+    const int wt = m->wt, at = m->at;
+    const int rows = n * m->pieces;
+    const int fb = frag_bytes(wt);
+    const int kv_es = dtype_size(m->kvt);
+
+    SlotPtrs sp{};
+    GemmArgs base{};
+    base.B = n;
+    base.eps = c.rms_norm_eps;
+    base.part = (float *)(mb + m->part);
+    base.cnt = (int *)(mb + m->cnt);
+    base.Hq = m->H;
+    base.Hk = m->Hk;
+    base.D = m->D;
+    base.kv_es = kv_es;
+    base.theta = (double)c.rope_theta;
+    for (int b = 0; b < n; ++b) {
+        sp.err[b] = (int *)(st[b]->base + st[b]->err);
+        base.err[b] = sp.err[b];
+        base.pos[b] = st[b]->pos;
+        base.pt[b] = (const int *)(st[b]->base + st[b]->pt);
+    }
+
+    float *x = (float *)(mb + m->x);
+    {
+        Timed tm(m, PN_K_EMBED, s);
+        if (wt == PN_F32)
+            hipLaunchKernelGGL(k_embed<0>, dim3(n), dim3(256), 0, s, (const void *)(mb + m->embd), tok, x, E, m->V, sp);
+        else
+            hipLaunchKernelGGL(k_embed<1>, dim3(n), dim3(256), 0, s, (const void *)(mb + m->embd), tok, x, E, m->V, sp);
+    }
+
+    // attention geometry per slot
+    AttnArgs aa{};
+    aa.q = (const float *)(mb + m->q);
+    aa.o = mb + m->o;
+    aa.Hq = m->H;
+    aa.Hk = m->Hk;
+    aa.G = m->G;
+    aa.scale = (float)(1.0 / std::sqrt((double)m->D));
+    int nsplit_max = 1;
+    int kps = m->attn_kps > 0 ? m->attn_kps : attn_kps_min();
+    for (int b = 0; b < n; ++b) {
+        const int pos = st[b]->pos;
+        const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
+        aa.pos[b] = pos;
+        aa.t0[b] = t0;
+        aa.nsplit[b] = cdiv(pos - t0 + 1, kps);
+        nsplit_max = std::max(nsplit_max, aa.nsplit[b]);
+        aa.pt[b] = (const int *)(st[b]->base + st[b]->pt);
+        aa.part[b] = (float *)(st[b]->base + st[b]->part);
+        aa.cnt[b] = (int *)(st[b]->base + st[b]->cnt);
+    }
+    aa.kps = kps;
+    for (int b = 0; b < n; ++b) {
+        aa.s_cap[b] = st[b]->s_cap;
+        if (aa.nsplit[b] > st[b]->s_cap) return fail(PN_ERANGE, "attention splits exceed state scratch");
+    }
+
+    const LayerOff &L0 = m->L[0];
+    Plan p_qkv = make_plan(L0.qkv.n_tiles, 1, L0.qkv.KT, rows, 1, fb);
+    Plan p_o = make_plan(L0.o.n_tiles, 1, L0.o.KT, rows, 1, fb);
+    const bool moe = c.n_expert > 0;
+    const int rows_moe = std::min(n, kMaxSlots) * m->pieces;
+    Plan p_gu = make_plan(L0.gate.n_tiles, moe ? m->X : 1, L0.gate.KT, moe ? rows_moe : rows, 2, fb);
+    Plan p_dn = make_plan(L0.down.n_tiles, moe ? m->X : 1, L0.down.KT, moe ? rows_moe : rows, 1, fb);
+    Plan p_lm = make_plan(cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, 2, fb);
+
+    for (int l = 0; l < c.n_layer; ++l) {
+        const LayerOff &L = m->L[l];
+        // ---- QKV + RoPE + KV append
+        {
+            GemmArgs g = base;
+            g.w = (const uint8_t *)(mb + L.qkv.off);
+            g.sc = (const float *)(mb + L.qkv.soff);
+            g.N = L.qkv.N;
+            g.n_tiles = L.qkv.n_tiles;
+            g.KT = L.qkv.KT;
+            g.K = E;
+            g.kc = p_qkv.kc;
+            g.ktc = p_qkv.ktc;
+            g.x = x;
+            g.gain = (const float *)(mb + L.attn_norm);
+            g.q_out = (float *)(mb + m->q);
+            for (int b = 0; b < n; ++b) {
+                g.kvk[b] = st[b]->base + st[b]->kpool + (size_t)l * st[b]->layer_bytes;
+                g.kvv[b] = st[b]->base + st[b]->vpool + (size_t)l * st[b]->layer_bytes;
+            }
+            Timed tm(m, PN_K_QKV, s);
+            launch_gemm<PRO_NORM, EPI_QKV, 1, false>(wt, at, g, p_qkv, s);
+        }
+        // ---- attention
+        {
+            for (int b = 0; b < n; ++b) {
+                aa.kvk[b] = st[b]->base + st[b]->kpool + (size_t)l * st[b]->layer_bytes;
+                aa.kvv[b] = st[b]->base + st[b]->vpool + (size_t)l * st[b]->layer_bytes;
+            }
+            Timed tm(m, PN_K_ATTN, s);
+            launch_attn(m->D, m->kvt, at, aa, dim3(nsplit_max, m->Hk, n), s);
+        }
+        // ---- O projection + residual
+        {
+            GemmArgs g = base;
+            g.w = (const uint8_t *)(mb + L.o.off);
+            g.sc = (const float *)(mb + L.o.soff);
+            g.N = E;
+            g.n_tiles = L.o.n_tiles;
+            g.KT = L.o.KT;
+            g.K = HD;
+            g.kc = p_o.kc;
+            g.ktc = p_o.ktc;
+            g.a = mb + m->o;
+            g.lda = HD;
+            g.out_f32 = x;
+            g.ld_out = E;
+            Timed tm(m, PN_K_O, s);
+            launch_gemm<PRO_LOAD, EPI_RESID, 1, false>(wt, at, g, p_o, s);
+        }
+        // ---- FFN
+        if (!moe) {
+            {
+                GemmArgs g = base;
+                g.w = (const uint8_t *)(mb + L.gate.off);
+                g.w2 = (const uint8_t *)(mb + L.up.off);
+                g.sc = (const float *)(mb + L.gate.soff);
+                g.sc2 = (const float *)(mb + L.up.soff);
+                g.N = F;
+                g.n_tiles = L.gate.n_tiles;
+                g.KT = L.gate.KT;
+                g.K = E;
+                g.kc = p_gu.kc;
+                g.ktc = p_gu.ktc;
+                g.x = x;
+                g.gain = (const float *)(mb + L.ffn_norm);
+                g.out_act = mb + m->h;
+                g.ld_out = F;
+                Timed tm(m, PN_K_GATEUP, s);
+                launch_gemm<PRO_NORM, EPI_SWIGLU, 2, true>(wt, at, g, p_gu, s);
+            }
+            {
+                GemmArgs g = base;
+                g.w = (const uint8_t *)(mb + L.down.off);
+                g.sc = (const float *)(mb + L.down.soff);
+                g.N = E;
+                g.n_tiles = L.down.n_tiles;
+                g.KT = L.down.KT;
+                g.K = F;
+                g.kc = p_dn.kc;
+                g.ktc = p_dn.ktc;
+                g.a = mb + m->h;
+                g.lda = F;
+                g.out_f32 = x;
+                g.ld_out = E;
+                Timed tm(m, PN_K_DOWN, s);
+                launch_gemm<PRO_LOAD, EPI_RESID, 1, false>(wt, at, g, p_dn, s);
+            }
+        } else {
+            int *rid = (int *)(mb + m->route_ids);
+            float *rw = (float *)(mb + m->route_w);
+            {
+                Timed tm(m, PN_K_ROUTER, s);
+                const size_t sh = (size_t)E * 4;
+                const void *wr = mb + L.router;
+                const float *gn = (const float *)(mb + L.ffn_norm);
+                if (wt == PN_F32) {
+                    if (at == PN_F32)
+                        hipLaunchKernelGGL((k_router<0, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                    else
+                        hipLaunchKernelGGL((k_router<0, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                } else {
+                    if (at == PN_F32)
+                        hipLaunchKernelGGL((k_router<1, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                    else
+                        hipLaunchKernelGGL((k_router<1, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                }
+            }
+            {
+                GemmArgs g = base;
+                g.w = (const uint8_t *)(mb + L.gate.off);
+                g.w2 = (const uint8_t *)(mb + L.up.off);
+                g.sc = (const float *)(mb + L.gate.soff);
+                g.sc2 = (const float *)(mb + L.up.soff);
+                g.ew_stride = (long long)L.gate.bytes1;
+                g.es_stride = (long long)L.gate.n_tiles * 16;
+                g.N = F;
+                g.n_tiles = L.gate.n_tiles;
+                g.KT = L.gate.KT;
+                g.K = E;
+                g.kc = p_gu.kc;
+                g.ktc = p_gu.ktc;
+                g.x = x;
+                g.gain = (const float *)(mb + L.ffn_norm);
+                g.route_ids = rid;
+                g.n_slots = n;
+                g.n_used = m->n_used;
+                g.out_act = mb + m->h;
+                g.ld_out = F;
+                Timed tm(m, PN_K_MOE_GATEUP, s);
+                launch_gemm<PRO_NORM, EPI_MOE_SWIGLU, 2, true>(wt, at, g, p_gu, s);
+            }
+            {
+                GemmArgs g = base;
+                g.w = (const uint8_t *)(mb + L.down.off);
+                g.sc = (const float *)(mb + L.down.soff);
+                g.ew_stride = (long long)L.down.bytes1;
+                g.es_stride = (long long)L.down.n_tiles * 16;
+                g.N = E;
+                g.n_tiles = L.down.n_tiles;
+                g.KT = L.down.KT;
+                g.K = F;
+                g.kc = p_dn.kc;
+                g.ktc = p_dn.ktc;
+                g.a = mb + m->h;
+                g.lda = F;
+                g.route_ids = rid;
+                g.n_slots = n;
+                g.n_used = m->n_used;
+                g.out_f32 = (float *)(mb + m->y);
+                g.ld_out = E;
+                Timed tm(m, PN_K_MOE_DOWN, s);
+                launch_gemm<PRO_LOAD, EPI_MOE_DOWN, 1, false>(wt, at, g, p_dn, s);
+            }
+            {
+                Timed tm(m, PN_K_MOE_COMBINE, s);
+                hipLaunchKernelGGL(k_moe_combine, dim3(cdiv(E, 256), n), dim3(256), 0, s, x,
+                                   (const float *)(mb + m->y), (const float *)rw, E, m->n_used);
+            }
+        }
+    }
+    // ---- final norm + LM head + argmax
+    {
+        GemmArgs g = base;
+        g.w = (const uint8_t *)(mb + m->out.off);
+        g.sc = (const float *)(mb + m->out.soff);
+        g.N = m->V;
+        g.n_tiles = m->out.n_tiles;
+        g.KT = m->out.KT;
+        g.K = E;
+        g.kc = p_lm.kc;
+        g.ktc = p_lm.ktc;
+        g.x = x;
+        g.gain = (const float *)(mb + m->out_norm);
+        g.out_f32 = logits;
+        g.am_val = (float *)(mb + m->am_val);
+        g.am_idx = (int *)(mb + m->am_idx);
+        Timed tm(m, PN_K_LMHEAD, s);
+        launch_gemm<PRO_NORM, EPI_LOGITS, 2, false>(wt, at, g, p_lm, s);
+    }
+    {
+        Timed tm(m, PN_K_ARGMAX, s);
+        hipLaunchKernelGGL(k_argmax, dim3(n), dim3(256), 0, s, (const float *)(mb + m->am_val),
+                           (const int *)(mb + m->am_idx), p_lm.gx, n, (int *)amax);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    for (int b = 0; b < n; ++b) st[b]->pos += 1;
+    return PN_OK;
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+
+extern "C" {
+
+void pn_config_default(pn_config *cfg) {
+    if (!cfg) return;
+    std::memset(cfg, 0, sizeof *cfg);
+    cfg->n_ctx = 2048;
+    cfg->rope_theta = 10000.0f;
+    cfg->rms_norm_eps = 1e-5f;
+    cfg->sliding_window = 0;
+    cfg->max_batch = 1;
+    cfg->w_dtype = PN_BF16;
+    cfg->kv_dtype = PN_BF16;
+    cfg->act_dtype = PN_F32;
+}
+
+int pn_config_check(const pn_config *cfg) {
+    g_err.clear();
+    return check_config(cfg);
+}
+
+size_t pn_model_bytes(const pn_config *cfg) {
+    if (check_config(cfg) != PN_OK) return 0;
+    pn_model m;
+    m.cfg = normalized(*cfg);
+    return layout_model(&m);
+}
+
+int pn_model_init(const pn_config *cfg, void *dev_buf, size_t bytes, pn_model **out) {
+    g_err.clear();
+    if (!out) return fail(PN_EINVAL, "out is NULL");
+    *out = nullptr;
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!dev_buf) return fail(PN_EINVAL, "device buffer is NULL");
+    if (((uintptr_t)dev_buf & 255) != 0) return fail(PN_EINVAL, "device buffer must be 256-byte aligned");
+    pn_model *m = new pn_model();
+    m->cfg = normalized(*cfg);
+    size_t need = layout_model(m);
+    if (bytes < need) {
+        delete m;
+        return fail(PN_ERANGE, "model buffer too small: %zu < %zu", bytes, need);
+    }
+    m->base = (char *)dev_buf;
+    m->bytes = bytes;
+    *out = m;
+    return PN_OK;
+}
+
+int pn_model_load_globals(pn_model *m, const void *tok_embd, const float *out_norm, const void *w_out,
+                          const float *s_out, void *stream) {
+    g_err.clear();
+    if (!m) return fail(PN_EINVAL, "model is NULL");
+    const bool i8 = m->wt == PN_I8;
+    if (!tok_embd || !out_norm || !w_out || (i8 && !s_out)) return fail(PN_EINVAL, "missing global weight pointer");
+    hipStream_t s = S(stream);
+    char *mb = m->base;
+    const int es_aux = m->wt == PN_F32 ? 4 : 2;
+    copy_bytes(mb + m->embd, tok_embd, (size_t)m->V * m->E * es_aux, s);
+    copy_bytes(mb + m->out_norm, out_norm, (size_t)m->E * 4, s);
+    pack(w_out, m->V, m->E, m->wt, m->out, 0, (uint8_t *)(mb + m->out.off), s);
+    if (i8) {
+        fill32(mb + m->out.soff, (size_t)m->out.n_tiles * 16, 0u, s);
+        copy_bytes(mb + m->out.soff, s_out, (size_t)m->V * 4, s);
+    }
+    fill32(mb + m->cnt, m->cnt_count, 0u, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PN_EHIP, "weight packing failed: %s", hipGetErrorString(e));
+    return PN_OK;
+}
+
+int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *W, void *stream) {
+    g_err.clear();
+    if (!m || !W) return fail(PN_EINVAL, "NULL argument");
+    const pn_config *cfg = &m->cfg;
+    if (layer < 0 || layer >= cfg->n_layer) return fail(PN_EINVAL, "layer %d out of range", layer);
+    const bool i8 = m->wt == PN_I8;
+    if (!W->attn_norm || !W->ffn_norm || !W->wq || !W->wk || !W->wv || !W->wo || !W->w_gate || !W->w_up || !W->w_down)
+        return fail(PN_EINVAL, "missing weight pointer in layer %d", layer);
+    if (cfg->n_expert > 0 && !W->w_router) return fail(PN_EINVAL, "missing router in layer %d", layer);
+    if (i8 && (!W->s_q || !W->s_k || !W->s_v || !W->s_o || !W->s_gate || !W->s_up || !W->s_down))
+        return fail(PN_EINVAL, "missing int8 scales in layer %d", layer);
+    hipStream_t s = S(stream);
+    char *mb = m->base;
+    const int wt = m->wt, es_aux = wt == PN_F32 ? 4 : 2, esw = dtype_size(wt);
+    const int E = m->E, HD = m->H * m->D, F = m->F, X = m->X;
+    const LayerOff &L = m->L[layer];
+    copy_bytes(mb + L.attn_norm, W->attn_norm, (size_t)E * 4, s);
+    copy_bytes(mb + L.ffn_norm, W->ffn_norm, (size_t)E * 4, s);
+    if (cfg->n_expert > 0) copy_bytes(mb + L.router, W->w_router, (size_t)cfg->n_expert * E * es_aux, s);
+    // q, k and v blocks are tile aligned because head_dim is a multiple of 16
+    uint8_t *qkv = (uint8_t *)(mb + L.qkv.off);
+    pack(W->wq, m->H * m->D, E, wt, L.qkv, 0, qkv, s);
+    pack(W->wk, m->Hk * m->D, E, wt, L.qkv, m->H * m->D / 16, qkv, s);
+    pack(W->wv, m->Hk * m->D, E, wt, L.qkv, (m->H + m->Hk) * m->D / 16, qkv, s);
+    pack(W->wo, E, HD, wt, L.o, 0, (uint8_t *)(mb + L.o.off), s);
+    if (i8) {
+        char *sq = mb + L.qkv.soff;
+        fill32(sq, (size_t)L.qkv.n_tiles * 16, 0u, s);
+        copy_bytes(sq, W->s_q, (size_t)m->H * m->D * 4, s);
+        copy_bytes(sq + (size_t)m->H * m->D * 4, W->s_k, (size_t)m->Hk * m->D * 4, s);
+        copy_bytes(sq + (size_t)(m->H + m->Hk) * m->D * 4, W->s_v, (size_t)m->Hk * m->D * 4, s);
+        fill32(mb + L.o.soff, (size_t)L.o.n_tiles * 16, 0u, s);
+        copy_bytes(mb + L.o.soff, W->s_o, (size_t)E * 4, s);
+    }
+    for (int e = 0; e < X; ++e) {
+        const char *g = (const char *)W->w_gate + (size_t)e * F * E * esw;
+        const char *u = (const char *)W->w_up + (size_t)e * F * E * esw;
+        const char *d = (const char *)W->w_down + (size_t)e * E * F * esw;
+        pack(g, F, E, wt, L.gate, 0, (uint8_t *)(mb + L.gate.off + e * L.gate.bytes1), s);
+        pack(u, F, E, wt, L.up, 0, (uint8_t *)(mb + L.up.off + e * L.up.bytes1), s);
+        pack(d, E, F, wt, L.down, 0, (uint8_t *)(mb + L.down.off + e * L.down.bytes1), s);
+        if (i8) {
+            const size_t gs = (size_t)L.gate.n_tiles * 16 * 4, ds = (size_t)L.down.n_tiles * 16 * 4;
+            fill32(mb + L.gate.soff + e * gs, gs / 4, 0u, s);
+            fill32(mb + L.up.soff + e * gs, gs / 4, 0u, s);
+            fill32(mb + L.down.soff + e * ds, ds / 4, 0u, s);
+            copy_bytes(mb + L.gate.soff + e * gs, W->s_gate + (size_t)e * F, (size_t)F * 4, s);
+            copy_bytes(mb + L.up.soff + e * gs, W->s_up + (size_t)e * F, (size_t)F * 4, s);
+            copy_bytes(mb + L.down.soff + e * ds, W->s_down + (size_t)e * E, (size_t)E * 4, s);
+        }
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PN_EHIP, "weight packing failed: %s", hipGetErrorString(e));
+    return PN_OK;
+}
+
+int pn_model_create(const pn_config *cfg, const pn_weights *w, void *dev_buf, size_t bytes, void *stream,
+                    pn_model **out) {
+    g_err.clear();
+    if (!out) return fail(PN_EINVAL, "out is NULL");
+    *out = nullptr;
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!w || !w->layers) return fail(PN_EINVAL, "weights are NULL");
+    pn_model *m = nullptr;
+    rc = pn_model_init(cfg, dev_buf, bytes, &m);
+    if (rc) return rc;
+    rc = pn_model_load_globals(m, w->tok_embd, w->out_norm, w->w_out, w->s_out, stream);
+    for (int l = 0; rc == PN_OK && l < cfg->n_layer; ++l) rc = pn_model_load_layer(m, l, &w->layers[l], stream);
+    if (rc) {
+        std::string msg = g_err;
+        delete m;
+        g_err = msg;
+        return rc;
+    }
+    *out = m;
+    return PN_OK;
+}
+
+void pn_model_free(pn_model *m) {
+    if (!m) return;
+    for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
+    delete m;
+}
+
+size_t pn_state_bytes(const pn_model *m, int32_t max_ctx) {
+    if (!m) return 0;
+    if (max_ctx == 0) max_ctx = m->cfg.n_ctx;
+    if (max_ctx < 1) return 0;
+    pn_state s{};
+    s.m = const_cast<pn_model *>(m);
+    s.max_ctx = max_ctx;
+    return layout_state(&s);
+}
+
+int pn_state_reset(pn_state *s, void *stream) {
+    g_err.clear();
+    if (!s) return fail(PN_EINVAL, "state is NULL");
+    hipStream_t st = S(stream);
+    fill32(s->base + s->kpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
+    fill32(s->base + s->vpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
+    fill32(s->base + s->cnt, (size_t)s->m->Hk, 0u, st);
+    fill32(s->base + s->err, 1, 0u, st);
+    s->pos = 0;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PN_EHIP, "reset failed: %s", hipGetErrorString(e));
+    return PN_OK;
+}
+
+int pn_state_new(pn_model *m, int32_t max_ctx, void *dev_buf, size_t bytes, void *stream, pn_state **out) {
+    g_err.clear();
+    if (!out) return fail(PN_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!m || !dev_buf) return fail(PN_EINVAL, "model or device buffer is NULL");
+    if (((uintptr_t)dev_buf & 255) != 0) return fail(PN_EINVAL, "device buffer must be 256-byte aligned");
+    if (max_ctx == 0) max_ctx = m->cfg.n_ctx;
+    if (max_ctx < 1) return fail(PN_EINVAL, "max_ctx must be >= 1");
+    pn_state *s = new pn_state{};
+    s->m = m;
+    s->max_ctx = max_ctx;
+    size_t need = layout_state(s);
+    if (bytes < need) {
+        delete s;
+        return fail(PN_ERANGE, "state buffer too small: %zu < %zu", bytes, need);
+    }
+    s->base = (char *)dev_buf;
+    s->bytes = bytes;
+    hipLaunchKernelGGL(k_iota, dim3(cdiv(s->n_pages, 256)), dim3(256), 0, S(stream), (int *)(s->base + s->pt),
+                       s->n_pages);
+    int rc = pn_state_reset(s, stream);
+    if (rc) {
+        delete s;
+        return rc;
+    }
+    *out = s;
+    return PN_OK;
+}
+
+int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const void *k, const void *v,
+                    void *stream) {
+    g_err.clear();
+    if (!s || !k || !v) return fail(PN_EINVAL, "NULL argument");
+    const pn_model *m = s->m;
+    if (layer < 0 || layer >= m->cfg.n_layer) return fail(PN_EINVAL, "layer %d out of range", layer);
+    if (n < 0 || pos0 < 0 || (long long)pos0 + n > s->max_ctx) return fail(PN_ERANGE, "positions out of range");
+    if (n == 0) return PN_OK;
+    char *kp = s->base + s->kpool + (size_t)layer * s->layer_bytes;
+    char *vp = s->base + s->vpool + (size_t)layer * s->layer_bytes;
+    long long total = (long long)n * m->Hk * m->D;
+    dim3 grid(cdiv(total, 256));
+    if (m->kvt == PN_BF16)
+        hipLaunchKernelGGL(k_set_kv<2>, grid, dim3(256), 0, S(stream), kp, vp, (const int *)(s->base + s->pt),
+                           (const char *)k, (const char *)v, pos0, n, m->Hk, m->D);
+    else
+        hipLaunchKernelGGL(k_set_kv<4>, grid, dim3(256), 0, S(stream), kp, vp, (const int *)(s->base + s->pt),
+                           (const char *)k, (const char *)v, pos0, n, m->Hk, m->D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PN_EHIP, "set_kv failed: %s", hipGetErrorString(e));
+    return PN_OK;
+}
+
+int pn_state_set_page_table(pn_state *s, const int32_t *pages, int32_t n, void *stream) {
+    g_err.clear();
+    if (!s || !pages) return fail(PN_EINVAL, "NULL argument");
+    if (n != s->n_pages) return fail(PN_EINVAL, "page table must have %d entries", s->n_pages);
+    std::vector<char> seen(n, 0);
+    for (int i = 0; i < n; ++i) {
+        if (pages[i] < 0 || pages[i] >= n || seen[pages[i]]) return fail(PN_EINVAL, "page table is not a permutation");
+        seen[pages[i]] = 1;
+    }
+    hipError_t e = hipMemcpyAsync(s->base + s->pt, pages, (size_t)n * 4, hipMemcpyHostToDevice, S(stream));
+    if (e == hipSuccess) e = hipStreamSynchronize(S(stream));
+    if (e != hipSuccess) return fail(PN_EHIP, "page table copy failed: %s", hipGetErrorString(e));
+    return PN_OK;
+}
+
+int32_t pn_state_pages(const pn_state *s) { return s ? s->n_pages : 0; }
+int32_t pn_page_size(void) { return kPage; }
+
+int pn_state_set_pos(pn_state *s, int32_t pos) {
+    g_err.clear();
+    if (!s) return fail(PN_EINVAL, "state is NULL");
+    if (pos < 0 || pos > s->max_ctx) return fail(PN_ERANGE, "pos %d out of range", pos);
+    s->pos = pos;
+    return PN_OK;
+}
+
+int32_t pn_state_pos(const pn_state *s) { return s ? s->pos : -1; }
+int32_t pn_state_max_ctx(const pn_state *s) { return s ? s->max_ctx : 0; }
+
+int pn_state_check(pn_state *s, void *stream, int32_t *flags_out) {
+    g_err.clear();
+    if (!s || !flags_out) return fail(PN_EINVAL, "NULL argument");
+    int32_t f = 0;
+    hipError_t e = hipMemcpyAsync(&f, s->base + s->err, 4, hipMemcpyDeviceToHost, S(stream));
+    if (e == hipSuccess) e = hipStreamSynchronize(S(stream));
+    if (e != hipSuccess) return fail(PN_EHIP, "flag read failed: %s", hipGetErrorString(e));
+    fill32(s->base + s->err, 1, 0u, S(stream));
+    *flags_out = f;
+    return PN_OK;
+}
+
+void pn_state_free(pn_state *s) { delete s; }
+
+int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int32_t *tokens_dev,
+                     float *logits_dev, int32_t *argmax_dev, void *stream) {
+    g_err.clear();
+    if (!m || !states || !tokens_dev) return fail(PN_EINVAL, "NULL argument");
+    if (n < 1 || n > m->cfg.max_batch) return fail(PN_EINVAL, "n = %d outside [1, max_batch = %d]", n, m->cfg.max_batch);
+    for (int i = 0; i < n; ++i) {
+        if (!states[i]) return fail(PN_EINVAL, "state %d is NULL", i);
+        if (states[i]->m != m) return fail(PN_EINVAL, "state %d belongs to another model", i);
+        if (states[i]->pos < 0 || states[i]->pos >= states[i]->max_ctx)
+            return fail(PN_ERANGE, "state %d: pos %d leaves no room (max_ctx %d)", i, states[i]->pos, states[i]->max_ctx);
+        for (int j = 0; j < i; ++j)
+            if (states[j] == states[i]) return fail(PN_EINVAL, "state %d appears twice", i);
+    }
+    return forward_impl(m, states, n, tokens_dev, logits_dev, argmax_dev, S(stream));
+}
+
+int pn_forward_step(pn_model *m, pn_state *s, const int32_t *token_dev, float *logits_dev, int32_t *argmax_dev,
+                    void *stream) {
+    pn_state *one[1] = {s};
+    return pn_forward_batch(m, one, 1, token_dev, logits_dev, argmax_dev, stream);
+}
+
+int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
+    g_err.clear();
+    if (!m) return fail(PN_EINVAL, "model is NULL");
+    if (option == PN_OPT_ATTN_KEYS_PER_SPLIT) {
+        if (value < 0 || value % attn_kps_min() != 0 || value > (1 << 24))
+            return fail(PN_EINVAL, "keys per split must be 0 or a multiple of %d", attn_kps_min());
+        m->attn_kps = (int)value;
+        return PN_OK;
+    }
+    return fail(PN_EINVAL, "unknown option %d", option);
+}
+
+int pn_profile_begin(pn_model *m, int32_t kernel) {
+    g_err.clear();
+    if (!m) return fail(PN_EINVAL, "model is NULL");
+    if (kernel < 0 || kernel >= PN_K_COUNT) return fail(PN_EINVAL, "unknown kernel class %d", kernel);
+    m->prof_kernel = kernel;
+    m->ev_used = 0;
+    return PN_OK;
+}
+
+int pn_profile_end(pn_model *m, void *stream, double *total_ms, int64_t *launches) {
+    g_err.clear();
+    if (!m || !total_ms || !launches) return fail(PN_EINVAL, "NULL argument");
+    m->prof_kernel = -1;
+    hipError_t e = hipStreamSynchronize(S(stream));
+    if (e != hipSuccess) return fail(PN_EHIP, "synchronize failed: %s", hipGetErrorString(e));
+    double tot = 0.0;
+    for (size_t i = 0; i + 1 < m->ev_used; i += 2) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, m->ev[i], m->ev[i + 1]);
+        if (e != hipSuccess) return fail(PN_EHIP, "event timing failed: %s", hipGetErrorString(e));
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = (int64_t)(m->ev_used / 2);
+    m->ev_used = 0;
+    return PN_OK;
+}
+
+const char *pn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"
