@@ -98,7 +98,8 @@ def main():
 
     B = wl.slots
     starts = [int(p) for p in wl.start_positions()]
-    total_steps = args.warmup + 2 * args.steps
+    kinds_n = 6  # per-kernel timing passes below
+    total_steps = args.warmup + (1 + kinds_n) * args.steps
     states = []
     t0 = time.time()
     for b in range(B):

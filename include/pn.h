@@ -196,10 +196,15 @@ enum {
     PN_K_ARGMAX, PN_K_ROUTER, PN_K_MOE_GATEUP, PN_K_MOE_DOWN, PN_K_MOE_COMBINE, PN_K_COUNT
 };
 
-/* Options: PN_OPT_ATTN_KEYS_PER_SPLIT (0 = automatic, else a multiple of 256
- * keys handled by one attention work-group; the result changes only by fp32
- * rounding). */
-enum { PN_OPT_ATTN_KEYS_PER_SPLIT = 1 };
+/* Options (tuning only; results change at most by fp32 rounding):
+ *  PN_OPT_ATTN_KEYS_PER_SPLIT  0 = automatic, else a multiple of 256 keys
+ *                              handled by one attention work-group;
+ *  PN_OPT_WAVES_*              waves per work-group (4, 8 or 16) of the QKV,
+ *                              O, gate/up, down and LM-head projections. */
+enum {
+    PN_OPT_ATTN_KEYS_PER_SPLIT = 1,
+    PN_OPT_WAVES_QKV = 10, PN_OPT_WAVES_O, PN_OPT_WAVES_GATEUP, PN_OPT_WAVES_DOWN, PN_OPT_WAVES_LMHEAD
+};
 int pn_model_set_option(pn_model *m, int32_t option, int64_t value);
 
 /* Time every launch of kernel class `kernel` with HIP events recorded on the

@@ -59,6 +59,7 @@ def good_cfg(**kw):
     (dict(n_expert=4, n_expert_used=5), C.PN_EINVAL),
     (dict(sliding_window=-1), C.PN_EINVAL),
     (dict(rope_theta=0.0), C.PN_EINVAL),
+    (dict(n_embd=252), C.PN_EUNSUPPORTED),
 ])
 def test_bad_configs_rejected(kw, code):
     cfg = good_cfg(**kw)

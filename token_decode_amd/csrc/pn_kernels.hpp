@@ -28,14 +28,14 @@ namespace pn {
 constexpr int kPage = 64;      // tokens per KV page
 constexpr int kMaxRows = 16;   // A rows of one MFMA tile
 constexpr int kMaxSlots = 16;  // sequences in one batched step
-constexpr int kNW = 4;         // waves per GEMM work-group
+constexpr int kNW = 16;        // waves per GEMM work-group
 constexpr int kU = 8;          // tiles per wave per load round
 constexpr int kAttnWaves = 4;  // waves per attention work-group
 constexpr int kMaxG = 8;       // query heads per KV head
 
 enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2 };
 enum AType { AT_F32 = 0, AT_BF16 = 1 };
-enum Pro { PRO_NORM = 0, PRO_LOAD = 1 };
+enum Pro { PRO_NORM = 0, PRO_LOAD = 1, PRO_CONV = 2 };  // CONV: A = round_act(fp32 rows), no norm
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_MOE_SWIGLU = 4,
            EPI_MOE_DOWN = 5 };
 
@@ -59,15 +59,38 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 __device__ __forceinline__ float bf16_round(float f) { return __uint_as_float(bf16_rne_bits(f) << 16); }
 __device__ __forceinline__ float bf16_bits_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Wave-wide reductions over the 64 lanes with DPP moves (no LDS traffic); the
+// combining order is fixed and the result is read from lane 63, so every lane
+// gets the same value.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within a row
+constexpr int kDppBcast15 = 0x142;    // lane 15 of the previous row
+constexpr int kDppBcast31 = 0x143;    // lane 31 to rows 2 and 3
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float ident, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f<kDppXor1, 0xF>(0.f, v);
+    v += dpp_f<kDppXor2, 0xF>(0.f, v);
+    v += dpp_f<kDppHalfMirror, 0xF>(0.f, v);
+    v += dpp_f<kDppMirror, 0xF>(0.f, v);
+    v += dpp_f<kDppBcast15, 0xA>(0.f, v);
+    v += dpp_f<kDppBcast31, 0xC>(0.f, v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_f<kDppXor1, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppXor2, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppMirror, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(-INFINITY, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
@@ -78,6 +101,40 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 enum { ERR_TOKEN = 1, ERR_NAN = 2 };
 
 // ---------------------------------------------------------------- GEMM
+
+// "A-ready" activation buffers.  A producer (attention combine, SwiGLU) writes
+// the next GEMM's input already in the element type its MFMA consumes, so
+// the consuming waves load their fragments straight from memory:
+//   bf16 weights, fp32 act: 3 planes of bf16 pieces (sum = the fp32 value)
+//   bf16 weights, bf16 act: 1 plane of bf16
+//   int8 weights (bf16 act): 1 plane of f16
+//   fp32 weights:           1 plane of fp32 (bf16-rounded when act is bf16)
+// Plane p of row r starts at element p*plane + r*ld; rows are zero-padded to
+// a whole number of k tiles.
+template <int WT, int AT>
+struct AReady {
+    static constexpr int PIECES = (WT == WT_BF16 && AT == AT_F32) ? 3 : 1;
+    static constexpr int ES = WT == WT_F32 ? 4 : 2;
+    __device__ static void store(void *base, long long plane, long long idx, float v) {
+        if constexpr (AT == AT_BF16) v = bf16_round(v);
+        if constexpr (WT == WT_F32) {
+            reinterpret_cast<float *>(base)[idx] = v;
+        } else if constexpr (WT == WT_I8) {
+            reinterpret_cast<_Float16 *>(base)[idx] = (_Float16)v;
+        } else if constexpr (PIECES == 1) {
+            reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)bf16_rne_bits(v);
+        } else {
+            const float p0 = bf16_round(v);
+            const float r1 = v - p0;
+            const float p1 = bf16_round(r1);
+            const float p2 = bf16_round(r1 - p1);
+            uint16_t *b = reinterpret_cast<uint16_t *>(base);
+            b[idx] = (uint16_t)bf16_rne_bits(p0);
+            b[plane + idx] = (uint16_t)bf16_rne_bits(p1);
+            b[2 * plane + idx] = (uint16_t)bf16_rne_bits(p2);
+        }
+    }
+};
 
 struct GemmArgs {
     const uint8_t *w;       // packed tiles of matrix 0 (of expert 0)
@@ -90,26 +147,28 @@ struct GemmArgs {
     int n_tiles;            // 16-row tiles per matrix
     int KT;                 // k tiles
     int K;                  // logical K
-    int kc;                 // k chunks (grid.y)
-    int ktc;                // tiles per chunk
     int B;                  // dense: slots
+    int nblk;               // row blocks of NTW tiles (per expert)
+    int tpw;                // row blocks per work-group
     const float *x;         // PRO_NORM: residual [slot][K]
     const float *gain;      // PRO_NORM: [K]
     float eps;
-    const void *a;          // PRO_LOAD: activation rows [row][lda]
-    int lda;
+    float *ssp;             // sums of squares of x per 16-element tile [slot][ssp_ld]
+    int ssp_ld, ssp_n;      // (read by the norm prologue, written by the residual epilogue)
+    const void *a;          // PRO_LOAD: A-ready activation planes
+    long long a_plane;      // PRO_LOAD: elements per plane
+    int lda;                // PRO_LOAD: elements per row (padded K)
     const int *route_ids;   // MoE: [slot][n_used] expert ids
     int n_slots;            // MoE: slots in the step
     int n_used;
-    float *part;            // split-K partial tiles
-    int *cnt;               // split-K arrival counters (self-resetting)
     float *out_f32;         // RESID: x; LOGITS: logits (nullable); MOE_DOWN: y rows
-    void *out_act;          // SWIGLU / MOE_SWIGLU: hidden rows (act dtype)
+    void *out_act;          // SWIGLU / MOE_SWIGLU: A-ready hidden planes
+    long long out_plane;    // elements per output plane
     int ld_out;
     float *q_out;           // QKV: q [slot][Hq*D]
     int Hq, Hk, D;
     int kv_es;              // QKV: bytes per cached element (2 = bf16, 4 = fp32)
-    double theta;
+    const float2 *rope;     // QKV: (cos, sin) per slot and rotation index [slot][D/2]
     float *am_val;          // LOGITS: per-WG best value [wg][slot]
     int *am_idx;
     int *err[kMaxSlots];    // per slot error flags
@@ -119,31 +178,30 @@ struct GemmArgs {
     const int *pt[kMaxSlots];
 };
 
+// One weight tile times one A fragment.  a0 (and a1 for int8) hold this lane's
+// A values: 4 fp32, 8 bf16 or 16 f16 of row (lane & 15).
 template <int WT>
-__device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const uint8_t *afrag, bool live) {
+__device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32x4 &a0, const u32x4 &a1) {
     if constexpr (WT == WT_BF16) {
-        u32x4 av = live ? *reinterpret_cast<const u32x4 *>(afrag) : u32x4{0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
                                                       __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
     } else if constexpr (WT == WT_F32) {
-        f32x4 av = live ? *reinterpret_cast<const f32x4 *>(afrag) : f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 bw = __builtin_bit_cast(f32x4, wv);
+        const f32x4 av = __builtin_bit_cast(f32x4, a0);
+        const f32x4 bw = __builtin_bit_cast(f32x4, wv);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bw[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bw[1], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bw[2], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bw[3], acc, 0, 0, 0);
     } else {
-        u32x4 a0 = live ? *reinterpret_cast<const u32x4 *>(afrag) : u32x4{0, 0, 0, 0};
-        u32x4 a1 = live ? *reinterpret_cast<const u32x4 *>(afrag + 16) : u32x4{0, 0, 0, 0};
         const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
         u32x4 b0, b1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04010400u);
-            uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04030402u);
-            f16x2 flo = __builtin_bit_cast(f16x2, lo) - off;
-            f16x2 fhi = __builtin_bit_cast(f16x2, hi) - off;
-            uint32_t ulo = __builtin_bit_cast(uint32_t, flo), uhi = __builtin_bit_cast(uint32_t, fhi);
+            // byte u -> f16 (1024 + u); minus 1152 leaves the signed code exactly
+            const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04010400u);
+            const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04030402u);
+            const uint32_t ulo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
+            const uint32_t uhi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
             if (i < 2) { b0[2 * i] = ulo; b0[2 * i + 1] = uhi; }
             else { b1[2 * (i - 2)] = ulo; b1[2 * (i - 2) + 1] = uhi; }
         }
@@ -154,91 +212,186 @@ __device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const uin
     }
 }
 
-// Store activation value v of (slot b, chunk-local k index kk) into the LDS A fragments.
-template <int WT, int AT>
-__device__ __forceinline__ void put_a(uint8_t *sa, int rows, int nb, int b, int kk, float v) {
-    constexpr int TK = tile_k(WT);
-    constexpr int FB = frag_bytes(WT);
-    constexpr int EPG = TK / 4;  // elements per (k-group) per tile
-    const int tt = kk / TK, kin = kk % TK, gq = kin / EPG, el = kin % EPG;
-    if constexpr (WT == WT_F32) {
-        *reinterpret_cast<float *>(sa + ((tt * 4 + gq) * rows + b) * FB + el * 4) = v;
-    } else if constexpr (WT == WT_I8) {
-        *reinterpret_cast<_Float16 *>(sa + ((tt * 4 + gq) * rows + b) * FB + el * 2) = (_Float16)v;
-    } else if constexpr (AT == AT_BF16) {
-        *reinterpret_cast<uint16_t *>(sa + ((tt * 4 + gq) * rows + b) * FB + el * 2) =
-            (uint16_t)bf16_rne_bits(v);
-    } else {
-        // three bf16 pieces with p0 + p1 + p2 == v exactly
-        float p0 = bf16_round(v);
-        float r1 = v - p0;
-        float p1 = bf16_round(r1);
-        float p2 = bf16_round(r1 - p1);
-        *reinterpret_cast<uint16_t *>(sa + ((tt * 4 + gq) * rows + b) * FB + el * 2) = (uint16_t)bf16_rne_bits(p0);
-        *reinterpret_cast<uint16_t *>(sa + ((tt * 4 + gq) * rows + nb + b) * FB + el * 2) = (uint16_t)bf16_rne_bits(p1);
-        *reinterpret_cast<uint16_t *>(sa + ((tt * 4 + gq) * rows + 2 * nb + b) * FB + el * 2) = (uint16_t)bf16_rne_bits(p2);
-    }
-}
-
-// Block-wide deterministic sum of one float per thread (256 threads).
-__device__ __forceinline__ float block_sum256(float v, float *red4) {
+// Block-wide deterministic sum of one float per thread.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float *redw) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) red4[w] = v;
+    if ((threadIdx.x & 63) == 0) redw[w] = v;
     __syncthreads();
-    return (red4[0] + red4[1]) + (red4[2] + red4[3]);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) s += redw[i];
+    return s;
 }
 
-// RoPE of the pair (y0, y1) at rotation index i of a head of width D, position pos.
-__device__ __forceinline__ void rope_pair(float &y0, float &y1, int i, int D, int pos, double theta) {
-    double w = pow(theta, -2.0 * (double)i / (double)D);
-    double phi = (double)pos * w;
-    double s, c;
-    sincos(phi, &s, &c);
-    float cf = (float)c, sf = (float)s;
-    float a = y0, b = y1;
-    y0 = a * cf - b * sf;
-    y1 = a * sf + b * cf;
+// RoPE of the pair (y0, y1) by the angle whose (cos, sin) is cs.
+__device__ __forceinline__ void rope_pair(float &y0, float &y1, float2 cs) {
+    const float a = y0, b = y1;
+    y0 = a * cs.x - b * cs.y;
+    y1 = a * cs.y + b * cs.x;
 }
 
-template <int AT>
-__device__ __forceinline__ void store_act(void *base, long long idx, float v) {
-    if constexpr (AT == AT_BF16)
-        reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)bf16_rne_bits(v);
-    else
-        reinterpret_cast<float *>(base)[idx] = v;
+// Issue the weight loads of one round: KU tiles of each matrix, always the
+// same number of loads (tiles past `last` re-read tile `last`), so the
+// compiler can wait for exactly the rounds it needs.
+template <int NTW, int KU>
+__device__ __forceinline__ void issue_w(u32x4 (&wr)[NTW][KU], const uint8_t *const (&wbase)[NTW], int t_at,
+                                        int last) {
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+        const int t = min(t_at + i, last);
+#pragma unroll
+        for (int mt = 0; mt < NTW; ++mt)
+            wr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wbase[mt] + (long long)t * 1024));
+    }
 }
 
-template <int AT>
-__device__ __forceinline__ float load_act(const void *base, long long idx) {
-    if constexpr (AT == AT_BF16)
-        return bf16_bits_f32(reinterpret_cast<const uint16_t *>(base)[idx]);
-    else
-        return reinterpret_cast<const float *>(base)[idx];
+// Issue the direct A-fragment loads of one round (A-ready input not staged in
+// LDS), with the same clamping.  `arow` is a valid address on every lane; rows
+// past `rows` read row 0 and use zeros.
+template <int WT, int AT, int KU>
+__device__ __forceinline__ void issue_a(u32x4 (&ar0)[KU], u32x4 (&ar1)[KU], const uint8_t *arow, bool alive,
+                                        int t_at, int last) {
+    constexpr int TK = tile_k(WT);
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+        const int t = min(t_at + i, last);
+        const uint8_t *p = arow + (long long)t * TK * AReady<WT, AT>::ES;
+        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(p);
+        ar0[i] = alive ? v0 : u32x4{0, 0, 0, 0};
+        if constexpr (WT == WT_I8) {
+            const u32x4 v1 = *reinterpret_cast<const u32x4 *>(p + 16);
+            ar1[i] = alive ? v1 : u32x4{0, 0, 0, 0};
+        }
+    }
+}
+
+// MFMA over one round: tiles t_at..t_at+n-1 with A from LDS fragments or registers.
+template <int WT, int NTW, int KU, bool ALDS>
+__device__ __forceinline__ void compute_round(f32x4 (&acc)[NTW], const u32x4 (&wr)[NTW][KU],
+                                              const u32x4 (&ar0)[KU], const u32x4 (&ar1)[KU],
+                                              const uint8_t *sa, int rows, int am, int ag, bool alive,
+                                              const bool (&wlive)[NTW], int t_loc, int n) {
+    constexpr int FB = frag_bytes(WT);
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+        if (i < n) {
+            u32x4 a0, a1 = u32x4{0, 0, 0, 0};
+            if constexpr (ALDS) {
+                const uint8_t *af = sa + (((t_loc + i) * 4 + ag) * rows + am) * FB;
+                a0 = alive ? *reinterpret_cast<const u32x4 *>(af) : u32x4{0, 0, 0, 0};
+                if constexpr (WT == WT_I8)
+                    a1 = alive ? *reinterpret_cast<const u32x4 *>(af + 16) : u32x4{0, 0, 0, 0};
+            } else {
+                a0 = ar0[i];
+                if constexpr (WT == WT_I8) a1 = ar1[i];
+            }
+#pragma unroll
+            for (int mt = 0; mt < NTW; ++mt)
+                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], a0, a1);
+        }
+    }
+}
+
+// Write the A values of 8 consecutive k (k0..k0+7, k0 a multiple of 8) of slot
+// b into the LDS fragments [kt][k-group][row][FB bytes].
+template <int WT, int AT>
+__device__ __forceinline__ void put_a8(uint8_t *sa, int rows, int nb, int b, int k0, const float (&v)[8]) {
+    constexpr int TK = tile_k(WT);
+    constexpr int FB = frag_bytes(WT);
+    constexpr int EPG = TK / 4;
+    const int kt = k0 / TK, kin = k0 % TK;
+    if constexpr (WT == WT_F32) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int gq = kin / EPG + h;
+            *reinterpret_cast<f32x4 *>(sa + ((kt * 4 + gq) * rows + b) * FB) =
+                f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+        }
+    } else if constexpr (WT == WT_I8) {
+        const int gq = kin / EPG, el = kin % EPG;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[2 * q], (_Float16)v[2 * q + 1]});
+        *reinterpret_cast<u32x4 *>(sa + ((kt * 4 + gq) * rows + b) * FB + el * 2) = o;
+    } else {
+        const int gq = kin / EPG;
+        uint8_t *dst = sa + ((kt * 4 + gq) * rows + b) * FB;
+        if constexpr (AReady<WT, AT>::PIECES == 1) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = bf16_rne_bits(v[2 * q]) | (bf16_rne_bits(v[2 * q + 1]) << 16);
+            *reinterpret_cast<u32x4 *>(dst) = o;
+        } else {
+            u32x4 o0, o1, o2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t w0[2], w1[2], w2[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float x = v[2 * q + h];
+                    const float p0 = bf16_round(x);
+                    const float r1 = x - p0;
+                    const float p1 = bf16_round(r1);
+                    const float p2 = bf16_round(r1 - p1);
+                    w0[h] = bf16_rne_bits(p0);
+                    w1[h] = bf16_rne_bits(p1);
+                    w2[h] = bf16_rne_bits(p2);
+                }
+                o0[q] = w0[0] | (w0[1] << 16);
+                o1[q] = w1[0] | (w1[1] << 16);
+                o2[q] = w2[0] | (w2[1] << 16);
+            }
+            *reinterpret_cast<u32x4 *>(dst) = o0;
+            *reinterpret_cast<u32x4 *>(dst + nb * FB) = o1;
+            *reinterpret_cast<u32x4 *>(dst + 2 * nb * FB) = o2;
+        }
+    }
 }
 
 // Skinny GEMM Y[rows][N] = A[rows][K] * W[N][K]^T for rows <= 16, fused with a
-// prologue that builds A and an epilogue that consumes Y.
-// grid: x = row-block (NTW tiles), y = k chunk, z = expert (MoE) ; 256 threads.
-// NTW = 2 with PAIR: tile x of matrices w and w2 (gate/up).  NTW = 2 without
-// PAIR: tiles 2x and 2x+1 of w.
-template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR>
-__global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
+// prologue that supplies A and an epilogue that consumes Y.
+// A row block is NTW weight tiles: with PAIR, tile blk of matrices w and w2
+// (gate and up); without, tiles NTW*blk .. NTW*blk+NTW-1 of w.  Work-group x
+// owns the consecutive row blocks [x*tpw, x*tpw + tpw) (grid z = expert for
+// MoE); its NW waves split K and reduce through LDS, so every work-group owns
+// whole output tiles.
+// A comes from LDS (ALDS: the prologue builds it there once for all the
+// group's blocks) or, for large A-ready inputs, straight from memory.
+// Memory accesses are issued early: the prologue's loads first, then two
+// rounds of weight tiles and the epilogue's inputs, so one round trip covers
+// the prologue; weight rounds then ping-pong between two register buffers, and
+// the next block's first rounds are in flight during this block's reduction
+// and epilogue.
+template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS>
+__global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
+    static_assert(PRO == PRO_LOAD || ALDS, "the norm prologue stages A in LDS");
+    constexpr bool XPRO = PRO == PRO_NORM || PRO == PRO_CONV;  // A built from fp32 rows in g.x
+    constexpr int NT = NW * 64;
     constexpr int TK = tile_k(WT);
     constexpr int FB = frag_bytes(WT);
-    constexpr int PIECES = (WT == WT_BF16 && AT == AT_F32) ? 3 : 1;
+    // tiles per matrix per round: two rounds in flight keep 8 KiB per wave
+    // outstanding within a 128-register budget (16 waves per CU)
+    constexpr int KU = 4 / NTW;
+    constexpr int PIECES = AReady<WT, AT>::PIECES;
     constexpr bool MOE = (EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN);
+    constexpr int CH = NW == 4 ? 2 : 1;        // x-prologue: 8-element chunks per thread per batch
+    constexpr int CHA = NW >= 16 ? 2 : 4;      // A-ready staging: fragments per thread per batch
+    constexpr int ES = AReady<WT, AT>::ES;
     extern __shared__ __align__(16) uint8_t smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bx = blockIdx.x, chunk = blockIdx.y, ex = blockIdx.z;
+    const int ex = blockIdx.z;
+    const int blk0 = blockIdx.x * g.tpw;
+    const int blk1 = min(g.nblk, blk0 + g.tpw);
+    if (blk0 >= blk1) return;
 
     __shared__ int s_ent[kMaxSlots];   // MoE: entry (slot*n_used + k) of each gathered row
     __shared__ int s_nb;
     __shared__ float s_rinv[kMaxSlots];
-    __shared__ float s_red4[4];
-    __shared__ int s_last;
 
     if constexpr (MOE) {
         if (tid == 0) {
@@ -253,232 +406,391 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
     const int nb = MOE ? s_nb : g.B;
     if (nb == 0) return;
     const int rows = nb * PIECES;
-
-    const int c0 = chunk * g.ktc;
-    const int c1 = min(g.KT, c0 + g.ktc);
-    const int clen = c1 - c0;
-    const int per = (clen + kNW - 1) / kNW;
-    const int wt0 = c0 + min(clen, wave * per);
-    const int wt1 = c0 + min(clen, (wave + 1) * per);
-
-    // matrix tile bases
-    const uint8_t *wbase[NTW];
-    bool wlive[NTW];
-#pragma unroll
-    for (int mt = 0; mt < NTW; ++mt) {
-        int nt = PAIR ? bx : bx * NTW + mt;
-        wlive[mt] = nt < g.n_tiles;
-        const uint8_t *m = (PAIR && mt == 1) ? g.w2 : g.w;
-        wbase[mt] = m + (long long)ex * g.ew_stride + ((long long)nt * g.KT) * 1024 + lane * 16;
-    }
-
-    // first load round, issued before the prologue so it overlaps it
-    u32x4 wr[NTW][kU];
-    int t = wt0;
-    {
-        int n = min(kU, wt1 - t);
-#pragma unroll
-        for (int i = 0; i < kU; ++i)
-#pragma unroll
-            for (int mt = 0; mt < NTW; ++mt)
-                if (i < n && wlive[mt])
-                    wr[mt][i] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(wbase[mt] + (long long)(t + i) * 1024));
-    }
-
-    // ---- prologue: A fragments of this chunk into LDS
-    uint8_t *sa = smem;
-    const int klo = c0 * TK;
-    const int klen = clen * TK;
-    if constexpr (PRO == PRO_NORM) {
-        for (int b = 0; b < nb; ++b) {
-            const int sb = MOE ? s_ent[b] / g.n_used : b;
-            const float *xr = g.x + (long long)sb * g.K;
-            float ss = 0.f;
-            for (int k = tid; k < g.K; k += 256) ss += xr[k] * xr[k];
-            ss = block_sum256(ss, s_red4);
-            if (tid == 0) s_rinv[b] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
-        }
-        __syncthreads();
-        for (int idx = tid; idx < nb * klen; idx += 256) {
-            const int b = idx / klen, kk = idx - b * klen, k = klo + kk;
-            const int sb = MOE ? s_ent[b] / g.n_used : b;
-            float v = 0.f;
-            if (k < g.K) {
-                v = (g.x[(long long)sb * g.K + k] * s_rinv[b]) * g.gain[k];
-                if (AT == AT_BF16) v = bf16_round(v);
-            }
-            put_a<WT, AT>(sa, rows, nb, b, kk, v);
-        }
-    } else {
-        for (int idx = tid; idx < nb * klen; idx += 256) {
-            const int b = idx / klen, kk = idx - b * klen, k = klo + kk;
-            const long long ar = MOE ? s_ent[b] : b;
-            float v = (k < g.K) ? load_act<AT>(g.a, ar * g.lda + k) : 0.f;
-            put_a<WT, AT>(sa, rows, nb, b, kk, v);
-        }
-    }
-    __syncthreads();
-
-    // ---- main loop
-    f32x4 acc[NTW];
-#pragma unroll
-    for (int mt = 0; mt < NTW; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int am = lane & 15, ag = lane >> 4;
     const bool alive = am < rows;
-    while (t < wt1) {
-        const int n = min(kU, wt1 - t);
+    uint8_t *sa = smem;  // A fragments [kt][k-group][row][FB bytes]
+    const int abytes = ALDS ? (g.KT * 4 * rows * FB + 255) & ~255 : 0;
+    float *red = reinterpret_cast<float *>(smem + abytes);  // [wave][mt][m][n]
+    float *C = red + NW * NTW * 256;                          // [mt][m][n]
+
+    // ---- phase 1: the prologue's loads
+    const int n8 = g.KT * TK / 8;  // 8-element chunks per A row
+    float xv[CH][8], gv[CH][8];
+    float ssv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    u32x4 st0[CHA], st1[CHA];
+    if constexpr (XPRO) {
 #pragma unroll
-        for (int i = 0; i < kU; ++i) {
-            if (i < n) {
-                const uint8_t *af = sa + (((t - c0 + i) * 4 + ag) * rows + am) * FB;
+        for (int c = 0; c < CH; ++c) {
+            const int ch = tid + c * NT;
+            const int b = ch / n8, k0 = (ch - b * n8) * 8;
+            const bool in = b < nb && k0 < g.K;
+            const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
+            const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 x0 = in ? xp[0] : z, x1 = in ? xp[1] : z;
 #pragma unroll
-                for (int mt = 0; mt < NTW; ++mt)
-                    if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], af, alive);
+            for (int e = 0; e < 4; ++e) { xv[c][e] = x0[e]; xv[c][4 + e] = x1[e]; }
+            if constexpr (PRO == PRO_NORM) {
+                const f32x4 *gp = reinterpret_cast<const f32x4 *>(g.gain + (in ? k0 : 0));
+                const f32x4 g0 = in ? gp[0] : z, g1 = in ? gp[1] : z;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { gv[c][e] = g0[e]; gv[c][4 + e] = g1[e]; }
             }
         }
-        t += n;
-        if (t < wt1) {
-            const int n2 = min(kU, wt1 - t);
+    }
+    if constexpr (PRO == PRO_NORM) {
+        if (wave < nb) {
+            const int sb = MOE ? s_ent[wave] / g.n_used : wave;
+            const float *sp = g.ssp + (long long)sb * g.ssp_ld;
 #pragma unroll
-            for (int i = 0; i < kU; ++i)
+            for (int u = 0; u < 8; ++u) ssv[u] = (lane + 64 * u < g.ssp_n) ? sp[lane + 64 * u] : 0.f;
+        }
+    }
+    if constexpr (PRO == PRO_LOAD && ALDS) {
 #pragma unroll
-                for (int mt = 0; mt < NTW; ++mt)
-                    if (i < n2 && wlive[mt])
-                        wr[mt][i] = __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4 *>(wbase[mt] + (long long)(t + i) * 1024));
+        for (int c = 0; c < CHA; ++c) {
+            const int idx = tid + c * NT;
+            const int chunksA = g.KT * 4;
+            const int m = idx / chunksA, f = idx - m * chunksA;
+            const bool in = m < rows;
+            const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
+            const long long r = MOE ? s_ent[b] : b;
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
+                                 ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
+            st0[c] = in ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0, 0, 0, 0};
+            if constexpr (WT == WT_I8) st1[c] = in ? *reinterpret_cast<const u32x4 *>(src + 16) : u32x4{0, 0, 0, 0};
         }
     }
 
-    // ---- reduce the waves' tiles: red[wave][mt][m][n]
-    const int abytes = g.ktc * 4 * rows * FB;
-    float *red = reinterpret_cast<float *>(smem + ((abytes + 255) & ~255));
-    float *C = red + kNW * NTW * 256;
+    // ---- phase 2: the first block's first two weight rounds (and direct A fragments)
+    const int per = (g.KT + NW - 1) / NW;
+    const int wt0 = min(g.KT, wave * per);
+    const int wt1 = min(g.KT, wt0 + per);
+    const int last = max(wt1 - 1, 0);             // clamp target of every load of this wave
+    const int rounds = (wt1 - wt0 + KU - 1) / KU;  // rounds with at least one tile
+    const uint8_t *mbase[NTW];
 #pragma unroll
     for (int mt = 0; mt < NTW; ++mt)
+        mbase[mt] = ((PAIR && mt == 1) ? g.w2 : g.w) + (long long)ex * g.ew_stride + lane * 16;
+    auto block_ptrs = [&](int blk, const uint8_t *(&wbase)[NTW], bool (&wlive)[NTW]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[(wave * NTW + mt) * 256 + (4 * ag + i) * 16 + am] = acc[mt][i];
-    __syncthreads();
-    for (int idx = tid; idx < NTW * 256; idx += 256) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) s += red[w * NTW * 256 + idx];
-        C[idx] = s;
-    }
-
-    if (g.kc > 1) {
-        const long long tg = (long long)ex * gridDim.x + bx;
-        float *mine = g.part + (tg * g.kc + chunk) * (NTW * 256);
-        for (int idx = tid; idx < NTW * 256; idx += 256) mine[idx] = C[idx];
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_last = (atomicAdd(&g.cnt[tg], 1) == g.kc - 1);
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        for (int idx = tid; idx < NTW * 256; idx += 256) {
-            float s = 0.f;
-            for (int c = 0; c < g.kc; ++c)
-                s += __builtin_nontemporal_load(g.part + (tg * g.kc + c) * (NTW * 256) + idx);
-            C[idx] = s;
-        }
-        if (tid == 0) g.cnt[tg] = 0;
-    }
-    __syncthreads();
-
-    // ---- epilogue.  Y[mt][b][n] = sum over pieces of C[mt][piece*nb + b][n]
-    auto Y = [&](int mt, int b, int n) -> float {
-        float v = C[mt * 256 + b * 16 + n];
-        if constexpr (PIECES == 3) v += C[mt * 256 + (nb + b) * 16 + n] + C[mt * 256 + (2 * nb + b) * 16 + n];
-        return v;
-    };
-    auto scale_of = [&](int mt, int r) -> float {
-        if constexpr (WT == WT_I8) {
-            const float *s = (PAIR && mt == 1) ? g.sc2 : g.sc;
-            return s[(long long)ex * g.es_stride + r];
-        } else {
-            return 1.0f;
+        for (int mt = 0; mt < NTW; ++mt) {
+            const int nt = PAIR ? blk : blk * NTW + mt;
+            wlive[mt] = nt < g.n_tiles;
+            // a dead tile (past the matrix) re-reads the block's first tile
+            wbase[mt] = mbase[mt] + ((long long)(wlive[mt] ? nt : (PAIR ? blk : blk * NTW)) * g.KT) * 1024;
         }
     };
+    const uint8_t *arow = nullptr;
+    if constexpr (!ALDS) {
+        long long r = 0, sp = 0;
+        if (alive) {
+            const int s = am / nb, b = am - s * nb;
+            r = MOE ? s_ent[b] : b;
+            sp = s;
+        }
+        arow = reinterpret_cast<const uint8_t *>(g.a) + (sp * g.a_plane + r * g.lda + ag * (TK / 4)) * ES;
+    }
+    u32x4 wa[NTW][KU], wb[NTW][KU];
+    u32x4 aa0[KU], aa1[KU], ab0[KU], ab1[KU];
+    const uint8_t *wbase[NTW];
+    bool wlive[NTW];
+    block_ptrs(blk0, wbase, wlive);
+    auto issue_first = [&]() {
+        issue_w<NTW, KU>(wa, wbase, wt0, last);
+        if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, wt0, last);
+        issue_w<NTW, KU>(wb, wbase, wt0 + KU, last);
+        if constexpr (!ALDS) issue_a<WT, AT, KU>(ab0, ab1, arow, alive, wt0 + KU, last);
+    };
+    issue_first();
 
-    if constexpr (EPI == EPI_QKV) {
-        const int hd = g.Hq * g.D, kd = g.Hk * g.D;
-        for (int idx = tid; idx < nb * 8; idx += 256) {
-            const int b = idx >> 3, n0 = (idx & 7) * 2;
-            const int r0 = bx * 16 + n0;
-            if (r0 >= g.N) continue;
-            float y0 = Y(0, b, n0) * scale_of(0, r0);
-            float y1 = Y(0, b, n0 + 1) * scale_of(0, r0 + 1);
-            const int pos = g.pos[b];
-            if (r0 < hd) {
-                rope_pair(y0, y1, (r0 % g.D) >> 1, g.D, pos, g.theta);
-                g.q_out[(long long)b * hd + r0] = y0;
-                g.q_out[(long long)b * hd + r0 + 1] = y1;
-            } else {
-                const bool isk = r0 < hd + kd;
-                const int rr = isk ? r0 - hd : r0 - hd - kd;
-                const int j = rr / g.D, dd = rr % g.D;
-                if (isk) rope_pair(y0, y1, dd >> 1, g.D, pos, g.theta);
-                const int page = g.pt[b][pos / kPage];
-                const long long off = (((long long)page * g.Hk + j) * kPage + (pos % kPage)) * g.D + dd;
-                char *base = isk ? g.kvk[b] : g.kvv[b];
-                if (g.kv_es == 2) {
-                    uint32_t pk = bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
-                    *reinterpret_cast<uint32_t *>(base + off * 2) = pk;
-                } else {
-                    reinterpret_cast<float *>(base)[off] = y0;
-                    reinterpret_cast<float *>(base)[off + 1] = y1;
+    // epilogue inputs of one block, loaded early by the threads that use them
+    // (row r of slot b: the old x for the residual, the (cos, sin) for RoPE,
+    // the int8 row scales)
+    struct EpIn { float x, s0, s1; float2 cs; };
+    auto epi_load = [&](int blk) -> EpIn {
+        EpIn e{0.f, 1.f, 1.f, make_float2(1.f, 0.f)};
+        if constexpr (EPI == EPI_RESID) {
+            if (tid < nb * 16) {
+                const int b = tid >> 4, r = blk * 16 + (tid & 15);
+                if (r < g.N) e.x = g.out_f32[(long long)b * g.ld_out + r];
+                if constexpr (WT == WT_I8) e.s0 = r < g.N ? g.sc[r] : 0.f;
+            }
+        } else if constexpr (EPI == EPI_QKV) {
+            if (tid < nb * 8) {
+                const int b = tid >> 3, r0 = blk * 16 + (tid & 7) * 2;
+                if (r0 < g.N) {
+                    e.cs = g.rope[(long long)b * (g.D / 2) + ((r0 % g.D) >> 1)];
+                    if constexpr (WT == WT_I8) { e.s0 = g.sc[r0]; e.s1 = g.sc[r0 + 1]; }
+                }
+            }
+        } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN) {
+            if constexpr (WT == WT_I8) {
+                if (tid < nb * 16) {
+                    const int r = blk * 16 + (tid & 15);
+                    if (r < g.N) {
+                        e.s0 = g.sc[(long long)ex * g.es_stride + r];
+                        if constexpr (PAIR) e.s1 = g.sc2[(long long)ex * g.es_stride + r];
+                    }
+                }
+            }
+        } else if constexpr (EPI == EPI_LOGITS) {
+            if constexpr (WT == WT_I8) {
+                if (tid < nb * NTW * 16) {
+                    const int c = tid % (NTW * 16);
+                    const int r = blk * NTW * 16 + c;
+                    if (r < g.N) e.s0 = g.sc[r];
                 }
             }
         }
-    } else if constexpr (EPI == EPI_RESID) {
-        for (int idx = tid; idx < nb * 16; idx += 256) {
-            const int b = idx >> 4, n = idx & 15, r = bx * 16 + n;
-            if (r < g.N) g.out_f32[(long long)b * g.ld_out + r] += Y(0, b, n) * scale_of(0, r);
-        }
-    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOE_SWIGLU) {
-        for (int idx = tid; idx < nb * 16; idx += 256) {
-            const int b = idx >> 4, n = idx & 15, r = bx * 16 + n;
-            if (r >= g.N) continue;
-            const float gt = Y(0, b, n) * scale_of(0, r);
-            const float up = Y(1, b, n) * scale_of(1, r);
-            const float h = (gt / (1.0f + expf(-gt))) * up;
-            const long long row = MOE ? s_ent[b] : b;
-            store_act<AT>(g.out_act, row * g.ld_out + r, h);
-        }
-    } else if constexpr (EPI == EPI_MOE_DOWN) {
-        for (int idx = tid; idx < nb * 16; idx += 256) {
-            const int b = idx >> 4, n = idx & 15, r = bx * 16 + n;
-            if (r < g.N) g.out_f32[(long long)s_ent[b] * g.ld_out + r] = Y(0, b, n) * scale_of(0, r);
-        }
-    } else if constexpr (EPI == EPI_LOGITS) {
-        float *L = red;  // reuse: logits of this block [slot][NTW*16]
-        for (int idx = tid; idx < nb * NTW * 16; idx += 256) {
-            const int b = idx / (NTW * 16), c = idx % (NTW * 16), mt = c >> 4, n = c & 15;
-            const int r = (bx * NTW + mt) * 16 + n;
-            float v = 0.f;
-            if (r < g.N) {
-                v = Y(mt, b, n) * scale_of(mt, r);
-                if (g.out_f32) g.out_f32[(long long)b * g.N + r] = v;
+        return e;
+    };
+    EpIn epc = epi_load(blk0);
+
+    // ---- phase 3: the prologue's arithmetic
+    if constexpr (XPRO) {
+        if constexpr (PRO == PRO_NORM) {
+            if (wave < nb) {
+                // fixed summation order: per lane, then the wave reduction
+                float ss = ((ssv[0] + ssv[1]) + (ssv[2] + ssv[3])) + ((ssv[4] + ssv[5]) + (ssv[6] + ssv[7]));
+                const int sb = MOE ? s_ent[wave] / g.n_used : wave;
+                for (int i = lane + 512; i < g.ssp_n; i += 64) ss += g.ssp[(long long)sb * g.ssp_ld + i];
+                ss = wave_sum(ss);
+                if (lane == 0) s_rinv[wave] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
             }
-            L[idx] = v;
+            for (int b = NW + wave; b < nb; b += NW) {  // more slots than waves
+                const int sb = MOE ? s_ent[b] / g.n_used : b;
+                float ss = 0.f;
+                for (int i = lane; i < g.ssp_n; i += 64) ss += g.ssp[(long long)sb * g.ssp_ld + i];
+                ss = wave_sum(ss);
+                if (lane == 0) s_rinv[b] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
+            }
+            __syncthreads();
+        }
+        for (int base = 0; base < nb * n8; base += CH * NT) {
+            if (base > 0) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int ch = base + tid + c * NT;
+                    const int b = ch / n8, k0 = (ch - b * n8) * 8;
+                    const bool in = b < nb && k0 < g.K;
+                    const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
+                    const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 x0 = in ? xp[0] : z, x1 = in ? xp[1] : z;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { xv[c][e] = x0[e]; xv[c][4 + e] = x1[e]; }
+                    if constexpr (PRO == PRO_NORM) {
+                        const f32x4 *gp = reinterpret_cast<const f32x4 *>(g.gain + (in ? k0 : 0));
+                        const f32x4 g0 = in ? gp[0] : z, g1 = in ? gp[1] : z;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { gv[c][e] = g0[e]; gv[c][4 + e] = g1[e]; }
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int ch = base + tid + c * NT;
+                const int b = ch / n8, k0 = (ch - b * n8) * 8;
+                if (b >= nb) continue;
+                float v[8];
+                if constexpr (PRO == PRO_NORM) {
+                    const float ri = s_rinv[b];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? (xv[c][e] * ri) * gv[c][e] : 0.f;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? xv[c][e] : 0.f;
+                }
+                if constexpr (AT == AT_BF16) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = bf16_round(v[e]);
+                }
+                put_a8<WT, AT>(sa, rows, nb, b, k0, v);
+            }
         }
         __syncthreads();
-        for (int b = tid; b < nb; b += 256) {
-            float best = 0.f;
-            int bi = -1;
-            bool nan = false;
-            for (int c = 0; c < NTW * 16; ++c) {
-                const int r = bx * NTW * 16 + c;
-                if (r >= g.N) break;
-                const float v = L[b * NTW * 16 + c];
-                if (v != v) { nan = true; continue; }
-                if (bi < 0 || v > best) { best = v; bi = r; }
+    } else if constexpr (ALDS) {
+        const int chunksA = g.KT * 4;  // fragments per A row
+        for (int base = 0; base < rows * chunksA; base += CHA * NT) {
+            if (base > 0) {
+#pragma unroll
+                for (int c = 0; c < CHA; ++c) {
+                    const int idx = base + tid + c * NT;
+                    const int m = idx / chunksA, f = idx - m * chunksA;
+                    const bool in = m < rows;
+                    const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
+                    const long long r = MOE ? s_ent[b] : b;
+                    const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
+                                         ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
+                    st0[c] = in ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0, 0, 0, 0};
+                    if constexpr (WT == WT_I8) st1[c] = in ? *reinterpret_cast<const u32x4 *>(src + 16) : u32x4{0, 0, 0, 0};
+                }
             }
-            g.am_val[(long long)bx * nb + b] = best;
-            g.am_idx[(long long)bx * nb + b] = bi;
-            if (nan) atomicOr(g.err[b], ERR_NAN);
+#pragma unroll
+            for (int c = 0; c < CHA; ++c) {
+                const int idx = base + tid + c * NT;
+                const int m = idx / chunksA, f = idx - m * chunksA;
+                if (m >= rows) continue;
+                uint8_t *dst = sa + (f * rows + m) * FB;
+                *reinterpret_cast<u32x4 *>(dst) = st0[c];
+                if constexpr (WT == WT_I8) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
+            }
         }
+        __syncthreads();
+    }
+
+    for (int blk = blk0; blk < blk1; ++blk) {
+        // ---- main loop of this block: weight rounds ping-pong between wa and wb.
+        // Every round issues the same loads (clamped past the end), so the
+        // waits are exact and the round after next is always in flight.
+        f32x4 acc[NTW];
+#pragma unroll
+        for (int mt = 0; mt < NTW; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < rounds; r += 2) {
+            const int ta = wt0 + r * KU;
+            compute_round<WT, NTW, KU, ALDS>(acc, wa, aa0, aa1, sa, rows, am, ag, alive, wlive, ta,
+                                             min(KU, wt1 - ta));
+            if (r + 2 < rounds) {
+                issue_w<NTW, KU>(wa, wbase, ta + 2 * KU, last);
+                if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, ta + 2 * KU, last);
+            }
+            if (r + 1 < rounds) {
+                compute_round<WT, NTW, KU, ALDS>(acc, wb, ab0, ab1, sa, rows, am, ag, alive, wlive, ta + KU,
+                                                 min(KU, wt1 - ta - KU));
+                if (r + 3 < rounds) {
+                    issue_w<NTW, KU>(wb, wbase, ta + 3 * KU, last);
+                    if constexpr (!ALDS) issue_a<WT, AT, KU>(ab0, ab1, arow, alive, ta + 3 * KU, last);
+                }
+            }
+        }
+        const bool live0 = wlive[0];
+        const bool live1 = NTW > 1 ? wlive[NTW - 1] : false;
+        // the next block's first rounds and epilogue inputs go out before this block's epilogue
+        EpIn epn = epc;
+        if (blk + 1 < blk1) {
+            block_ptrs(blk + 1, wbase, wlive);
+            issue_first();
+            epn = epi_load(blk + 1);
+        }
+
+        // ---- reduce the waves' tiles: red[wave][mt][m][n], then C[mt][m][n]
+#pragma unroll
+        for (int mt = 0; mt < NTW; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[(wave * NTW + mt) * 256 + (4 * ag + i) * 16 + am] = acc[mt][i];
+        __syncthreads();
+        for (int idx = tid; idx < NTW * 256; idx += NT) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sum += red[w * NTW * 256 + idx];
+            C[idx] = sum;
+        }
+        __syncthreads();
+
+        // ---- epilogue.  Y[mt][b][n] = sum over pieces of C[mt][piece*nb + b][n]
+        auto Y = [&](int mt, int b, int n) -> float {
+            float v = C[mt * 256 + b * 16 + n];
+            if constexpr (PIECES == 3) v += C[mt * 256 + (nb + b) * 16 + n] + C[mt * 256 + (2 * nb + b) * 16 + n];
+            return v;
+        };
+        if constexpr (EPI == EPI_QKV) {
+            const int hd = g.Hq * g.D, kd = g.Hk * g.D;
+            if (tid < nb * 8) {
+                const int b = tid >> 3, n0 = (tid & 7) * 2;
+                const int r0 = blk * 16 + n0;
+                if (r0 < g.N) {
+                    float y0 = Y(0, b, n0) * epc.s0;
+                    float y1 = Y(0, b, n0 + 1) * epc.s1;
+                    const int pos = g.pos[b];
+                    if (r0 < hd) {
+                        rope_pair(y0, y1, epc.cs);
+                        g.q_out[(long long)b * hd + r0] = y0;
+                        g.q_out[(long long)b * hd + r0 + 1] = y1;
+                    } else {
+                        const bool isk = r0 < hd + kd;
+                        const int rr = isk ? r0 - hd : r0 - hd - kd;
+                        const int j = rr / g.D, dd = rr % g.D;
+                        if (isk) rope_pair(y0, y1, epc.cs);
+                        const int page = g.pt[b][pos / kPage];
+                        const long long off = (((long long)page * g.Hk + j) * kPage + (pos % kPage)) * g.D + dd;
+                        char *base = isk ? g.kvk[b] : g.kvv[b];
+                        if (g.kv_es == 2) {
+                            const uint32_t pk = bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
+                            *reinterpret_cast<uint32_t *>(base + off * 2) = pk;
+                        } else {
+                            reinterpret_cast<float *>(base)[off] = y0;
+                            reinterpret_cast<float *>(base)[off + 1] = y1;
+                        }
+                    }
+                }
+            }
+        } else if constexpr (EPI == EPI_RESID) {
+            // x += y; then this tile's sum of squares of the new x for the next norm
+            if (tid < nb * 16) {
+                const int b = tid >> 4, n = tid & 15, r = blk * 16 + n;
+                float xn = 0.f;
+                if (r < g.N) {
+                    xn = epc.x + Y(0, b, n) * epc.s0;
+                    g.out_f32[(long long)b * g.ld_out + r] = xn;
+                }
+                float sq = xn * xn;
+                sq += __shfl_xor(sq, 8, 64);
+                sq += __shfl_xor(sq, 4, 64);
+                sq += __shfl_xor(sq, 2, 64);
+                sq += __shfl_xor(sq, 1, 64);
+                if (n == 0) g.ssp[(long long)b * g.ssp_ld + blk] = sq;
+            }
+        } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOE_SWIGLU) {
+            if (tid < nb * 16) {
+                const int b = tid >> 4, n = tid & 15, r = blk * 16 + n;
+                if (r < g.N) {
+                    const float gt = Y(0, b, n) * epc.s0;
+                    const float up = Y(1, b, n) * epc.s1;
+                    const float h = (gt / (1.0f + expf(-gt))) * up;
+                    const long long row = MOE ? s_ent[b] : b;
+                    AReady<WT, AT>::store(g.out_act, g.out_plane, row * g.ld_out + r, h);
+                }
+            }
+        } else if constexpr (EPI == EPI_MOE_DOWN) {
+            if (tid < nb * 16) {
+                const int b = tid >> 4, n = tid & 15, r = blk * 16 + n;
+                if (r < g.N) g.out_f32[(long long)s_ent[b] * g.ld_out + r] = Y(0, b, n) * epc.s0;
+            }
+        } else if constexpr (EPI == EPI_LOGITS) {
+            float *L = red;  // logits of this block [slot][NTW*16]
+            if (tid < nb * NTW * 16) {
+                const int b = tid / (NTW * 16), c = tid % (NTW * 16), mt = c >> 4, n = c & 15;
+                const int r = (blk * NTW + mt) * 16 + n;
+                float v = 0.f;
+                if (r < g.N) {
+                    v = Y(mt, b, n) * epc.s0;
+                    if (g.out_f32) g.out_f32[(long long)b * g.N + r] = v;
+                }
+                L[tid] = v;
+            }
+            __syncthreads();
+            if (tid < nb) {
+                const int b = tid;
+                float best = 0.f;
+                int bi = -1;
+                bool nan = false;
+                for (int c = 0; c < NTW * 16; ++c) {
+                    const int r = blk * NTW * 16 + c;
+                    if (r >= g.N) break;
+                    const float v = L[b * NTW * 16 + c];
+                    if (v != v) { nan = true; continue; }
+                    if (bi < 0 || v > best) { best = v; bi = r; }
+                }
+                g.am_val[(long long)blk * nb + b] = best;
+                g.am_idx[(long long)blk * nb + b] = bi;
+                if (nan) atomicOr(g.err[b], ERR_NAN);
+            }
+        }
+        (void)live0;
+        (void)live1;
+        epc = epn;
+        __syncthreads();  // red and C are reused by the next block
     }
 }
 
@@ -486,30 +798,26 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g) {
 
 struct AttnArgs {
     const float *q;   // [slot][Hq*D]
-    void *o;          // [slot][Hq*D] act dtype
-    int Hq, Hk, G, kps;
+    float *o;         // attention output [slot][Hq*D] (fp32; the O projection rounds it)
+    int Hq, Hk, kps;
     float scale;
     int pos[kMaxSlots], t0[kMaxSlots], nsplit[kMaxSlots], s_cap[kMaxSlots];
     const char *kvk[kMaxSlots], *kvv[kMaxSlots];
     const int *pt[kMaxSlots];
-    float *part[kMaxSlots];  // [Hk][s_cap][G][D+2]
-    int *cnt[kMaxSlots];     // [Hk]
+    float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max, sum, 2 pad, unnormalised output
 };
 
-template <int KV>
-__device__ __forceinline__ float kv_at(const char *base, long long i) {
-    if constexpr (KV == 1) return bf16_bits_f32(reinterpret_cast<const uint16_t *>(base)[i]);
-    else return reinterpret_cast<const float *>(base)[i];
-}
-
-// Split-K flash decode.  grid: x = split, y = kv head, z = slot; 256 threads.
+// Split-K flash decode for G query heads per KV head.
+// grid: x = split, y = kv head, z = slot; 256 threads.
 // Each split covers kps keys of the slot's window; each wave takes 64-key
 // chunks with an online softmax.  For q.k a lane owns one key and reads its
 // whole K row; for p.v a lane owns D/64 (at least one) consecutive dimensions
 // and reads one value row per key.  All K and V loads of a chunk are issued
-// before any arithmetic, so a wave keeps a whole chunk in flight.  Waves, then
-// splits, are merged in a fixed order, so results do not depend on timing.
-template <int D, int KV, int AT>
+// before any arithmetic, so a wave keeps a whole chunk in flight.  The waves
+// merge in a fixed order; a single-split slot writes the output directly,
+// otherwise the split's (max, sum, output) goes to the state's scratch for
+// k_attn_combine.
+template <int D, int KV, int G>
 __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     constexpr int VE = D >= 64 ? D / 64 : 1;   // value elements per lane
     constexpr int VL = D / VE;                 // lanes holding values
@@ -522,28 +830,35 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     if (s >= a.nsplit[b]) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int G = a.G;
     const int pos = a.pos[b];
     const int kb = a.t0[b] + s * a.kps;
     const int ke = min(kb + a.kps, pos + 1);
 
-    __shared__ float qs[kMaxG][D];
-    __shared__ float wm[kAttnWaves][kMaxG], wl[kAttnWaves][kMaxG];
-    __shared__ float wacc[kAttnWaves][kMaxG][D];
-    __shared__ int s_last;
-
-    for (int idx = tid; idx < G * D; idx += 256)
-        qs[idx / D][idx % D] = a.q[(long long)b * a.Hq * D + (long long)(j * G) * D + idx] * a.scale;
-    __syncthreads();
+    __shared__ __align__(16) float qs[G][D];
+    __shared__ float wm[kAttnWaves][G], wl[kAttnWaves][G];
+    __shared__ float wacc[kAttnWaves][G][D];
 
     const char *Kb = a.kvk[b];
     const char *Vb = a.kvv[b];
     const int *pt = a.pt[b];
     const bool vlane = lane < VL;
-
-    float m[kMaxG], l[kMaxG], acc[kMaxG][VE];
+    // page of this lane's key in the wave's first chunk, fetched before the q barrier
+    int page_next = pt[min(kb + w * 64 + lane, ke - 1) / kPage];
+    {
+        // q of the group's G heads: G*D/4 <= 256 float4s, one load per thread
+        const f32x4 *q4 = reinterpret_cast<const f32x4 *>(a.q + (long long)b * a.Hq * D + (long long)(j * G) * D);
+        if (tid < G * D / 4) {
+            const f32x4 v = q4[tid];
+            const int g = (tid * 4) / D, d = (tid * 4) % D;
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) {
+            for (int e = 0; e < 4; ++e) qs[g][d + e] = v[e] * a.scale;
+        }
+    }
+    __syncthreads();
+
+    float m[G], l[G], acc[G][VE];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
         m[g] = -INFINITY;
         l[g] = 0.f;
 #pragma unroll
@@ -553,8 +868,9 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     for (int cs = kb + w * 64; cs < ke; cs += kAttnWaves * 64) {
         const int t = cs + lane;
         const bool valid = t < ke;
-        const int tt = valid ? t : cs;  // invalid lanes read a valid key and get weight 0
-        const int off = ((pt[tt / kPage] * a.Hk + j) * kPage + (tt % kPage)) * D;  // element offset
+        const int tt = valid ? t : ke - 1;  // invalid lanes read a valid key and get weight 0
+        const int off = ((page_next * a.Hk + j) * kPage + (tt % kPage)) * D;  // element offset
+        if (cs + kAttnWaves * 64 < ke) page_next = pt[min(cs + kAttnWaves * 64 + lane, ke - 1) / kPage];
         // issue the chunk's loads: this lane's K row, then the first V rows
         u32x4 kreg[NKL];
         const u32x4 *kp = reinterpret_cast<const u32x4 *>(Kb + (long long)off * ES);
@@ -565,12 +881,30 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < VCH; ++u)
             vreg[u] = vbase[__builtin_amdgcn_readlane(off, u) / VE];
-        // q.k for this lane's key
-        float sc[kMaxG];
+        // q.k for this lane's key; the q values of step c+1 are read from LDS
+        // while step c is multiplied (the barrier keeps the compiler from
+        // hoisting every read)
+        float sc[G];
 #pragma unroll
-        for (int g = 0; g < kMaxG; ++g) sc[g] = 0.f;
+        for (int g = 0; g < G; ++g) sc[g] = 0.f;
+        float qn[G][KVEC];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < KVEC; ++e) qn[g][e] = qs[g][e];
 #pragma unroll
         for (int c = 0; c < NKL; ++c) {
+            float qc[G][KVEC];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < KVEC; ++e) qc[g][e] = qn[g][e];
+            if (c + 1 < NKL) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int e = 0; e < KVEC; ++e) qn[g][e] = qs[g][(c + 1) * KVEC + e];
+            }
             float kf[KVEC];
             if constexpr (KV == 1) {
 #pragma unroll
@@ -583,28 +917,30 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
                 for (int e = 0; e < 4; ++e) kf[e] = __uint_as_float(kreg[c][e]);
             }
 #pragma unroll
-            for (int g = 0; g < kMaxG; ++g)
-                if (g < G)
+            for (int g = 0; g < G; ++g)
 #pragma unroll
-                    for (int e = 0; e < KVEC; ++e) sc[g] = fmaf(qs[g][c * KVEC + e], kf[e], sc[g]);
+                for (int e = 0; e < KVEC; ++e) sc[g] = fmaf(qc[g][e], kf[e], sc[g]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // online softmax update
-        float p[kMaxG];
+        float p[G], mx[G];
 #pragma unroll
-        for (int g = 0; g < kMaxG; ++g) {
-            p[g] = 0.f;
-            if (g < G) {
-                const float sv = valid ? sc[g] : -INFINITY;
-                const float mn = fmaxf(m[g], wave_max(sv));
-                const float alpha = expf(m[g] - mn);
-                p[g] = valid ? expf(sv - mn) : 0.f;
-                l[g] = l[g] * alpha + wave_sum(p[g]);
+        for (int g = 0; g < G; ++g) mx[g] = wave_max(valid ? sc[g] : -INFINITY);
+        float ps[G];
 #pragma unroll
-                for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
-                m[g] = mn;
-            }
+        for (int g = 0; g < G; ++g) {
+            const float mn = fmaxf(m[g], mx[g]);
+            const float alpha = expf(m[g] - mn);
+            p[g] = valid ? expf(sc[g] - mn) : 0.f;
+            l[g] *= alpha;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
+            m[g] = mn;
         }
+#pragma unroll
+        for (int g = 0; g < G; ++g) ps[g] = wave_sum(p[g]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) l[g] += ps[g];
         // p.v
 #pragma unroll
         for (int vb = 0; vb < 64; vb += VCH) {
@@ -632,12 +968,10 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
                     }
                 }
 #pragma unroll
-                for (int g = 0; g < kMaxG; ++g) {
-                    if (g < G) {
-                        const float pg = readlane_f(p[g], vb + u);
+                for (int g = 0; g < G; ++g) {
+                    const float pg = readlane_f(p[g], vb + u);
 #pragma unroll
-                        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pg, v[e], acc[g][e]);
-                    }
+                    for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pg, v[e], acc[g][e]);
                 }
             }
         }
@@ -645,10 +979,11 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
 
     // merge the waves
     if (lane == 0)
-        for (int g = 0; g < G; ++g) { wm[w][g] = m[g]; wl[w][g] = l[g]; }
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g)
-        if (g < G && vlane)
+        for (int g = 0; g < G; ++g) { wm[w][g] = m[g]; wl[w][g] = l[g]; }
+    if (vlane)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int e = 0; e < VE; ++e) wacc[w][g][lane * VE + e] = acc[g][e];
     __syncthreads();
@@ -658,243 +993,88 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, d = idx % D;
         float M = wm[0][g];
+#pragma unroll
         for (int x = 1; x < kAttnWaves; ++x) M = fmaxf(M, wm[x][g]);
         float L = 0.f, A = 0.f;
+#pragma unroll
         for (int x = 0; x < kAttnWaves; ++x) {
             const float f = expf(wm[x][g] - M);
             L += wl[x][g] * f;
             A += wacc[x][g][d] * f;
         }
         if (ns == 1) {
-            store_act<AT>(a.o, (long long)b * a.Hq * D + (long long)(j * G + g) * D + d, A / L);
+            a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A / L;
         } else {
-            float *pp = part + (((long long)j * a.s_cap[b] + s) * G + g) * (D + 2);
+            float *pp = part + (((long long)j * a.s_cap[b] + s) * G + g) * (D + 4);
             if (d == 0) { pp[0] = M; pp[1] = L; }
-            pp[2 + d] = A;
+            pp[4 + d] = A;
         }
-    }
-    if (ns == 1) return;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&a.cnt[b][j], 1) == ns - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int g = idx / D, d = idx % D;
-        const float *p0 = part + ((long long)j * a.s_cap[b] * G + g) * (D + 2);
-        const long long sstride = (long long)G * (D + 2);
-        float M = -INFINITY;
-        for (int x = 0; x < ns; ++x) M = fmaxf(M, __builtin_nontemporal_load(p0 + x * sstride));
-        float L = 0.f, A = 0.f;
-        for (int x = 0; x < ns; ++x) {
-            const float *px = p0 + x * sstride;
-            const float f = expf(__builtin_nontemporal_load(px) - M);
-            L += __builtin_nontemporal_load(px + 1) * f;
-            A += __builtin_nontemporal_load(px + 2 + d) * f;
-        }
-        store_act<AT>(a.o, (long long)b * a.Hq * D + (long long)(j * G + g) * D + d, A / L);
-    }
-    if (tid == 0) a.cnt[b][j] = 0;
-}
-
-// ---------------------------------------------------------------- small kernels
-
-struct SlotPtrs {
-    int *err[kMaxSlots];
-};
-
-// x[b] = tok_embd[token[b]] (fp32 or bf16 table); bad ids use row 0 and set a flag.
-template <int ET>
-__global__ void __launch_bounds__(256) k_embed(const void *embd, const int *tokens, float *x, int E,
-                                                 int V, SlotPtrs sp) {
-    const int b = blockIdx.x;
-    int tok = tokens[b];
-    if (tok < 0 || tok >= V) {
-        if (threadIdx.x == 0) atomicOr(sp.err[b], ERR_TOKEN);
-        tok = 0;
-    }
-    for (int k = threadIdx.x; k < E; k += 256) {
-        float v;
-        if constexpr (ET == 1)
-            v = bf16_bits_f32(reinterpret_cast<const uint16_t *>(embd)[(long long)tok * E + k]);
-        else
-            v = reinterpret_cast<const float *>(embd)[(long long)tok * E + k];
-        x[(long long)b * E + k] = v;
     }
 }
 
-// argmax[b] over the LM head's per-block partials (value, lowest index on ties).
-__global__ void __launch_bounds__(256) k_argmax(const float *val, const int *idx, int nwg, int nb,
-                                                 int *out) {
-    const int b = blockIdx.x, tid = threadIdx.x;
-    float best = 0.f;
-    int bi = -1;
-    for (int w = tid; w < nwg; w += 256) {
-        const int i = idx[(long long)w * nb + b];
-        const float v = val[(long long)w * nb + b];
-        if (i < 0) continue;
-        if (bi < 0 || v > best || (v == best && i < bi)) { best = v; bi = i; }
-    }
-    __shared__ float sv[256];
-    __shared__ int si[256];
-    sv[tid] = best;
-    si[tid] = bi;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (tid < o) {
-            const float v = sv[tid + o];
-            const int i = si[tid + o];
-            if (i >= 0 && (si[tid] < 0 || v > sv[tid] || (v == sv[tid] && i < si[tid]))) {
-                sv[tid] = v;
-                si[tid] = i;
-            }
+// Merge the splits of every (slot, kv head) whose window took more than one
+// split, in split order.  grid: x = kv head, y = slot; 256 threads.  Splits
+// are staged through LDS kSplitChunk at a time (one independent 16-byte load
+// per thread step) and folded into a running (max, sum, output).
+constexpr int kSplitChunk = 8;
+
+template <int D, int G>
+__global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int ns = a.nsplit[b];
+    if (ns <= 1) return;
+    constexpr int per = G * (D + 4);  // floats of one split, a multiple of 4
+    const f32x4 *part = reinterpret_cast<const f32x4 *>(a.part[b] + (long long)j * a.s_cap[b] * per);
+    __shared__ __align__(16) float sp[kSplitChunk * per];
+    constexpr int OPT = (G * D + 255) / 256;  // outputs per thread
+    constexpr int LPT = (kSplitChunk * per / 4 + 255) / 256;  // float4 loads per thread
+    float M[OPT], L[OPT], A[OPT];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) { M[u] = -INFINITY; L[u] = 0.f; A[u] = 0.f; }
+    for (int s0 = 0; s0 < ns; s0 += kSplitChunk) {
+        const int nc = min(kSplitChunk, ns - s0);
+        const int n4 = nc * per / 4;
+        f32x4 v[LPT];
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int i = threadIdx.x + u * 256;
+            if (i < n4) v[u] = part[(long long)s0 * per / 4 + i];
         }
         __syncthreads();
-    }
-    if (tid == 0 && out) out[b] = si[0];
-}
-
-// MoE router of one slot: xn = round_act(RMSNorm(x)*g); r = W_r xn; top-k (ties
-// to the lower index); weights = softmax over the chosen logits.
-template <int RT, int AT>
-__global__ void __launch_bounds__(256) k_router(const float *x, const float *gain, const void *wr,
-                                                 int E, int n_expert, int k_used, float eps,
-                                                 int *ids, float *wts) {
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    extern __shared__ float xs[];  // [E]
-    __shared__ float red4[4];
-    __shared__ float r[64];
-    const float *xr = x + (long long)b * E;
-    float ss = 0.f;
-    for (int k = tid; k < E; k += 256) ss += xr[k] * xr[k];
-    ss = block_sum256(ss, red4);
-    const float rinv = 1.0f / sqrtf(ss / (float)E + eps);
-    for (int k = tid; k < E; k += 256) {
-        float v = (xr[k] * rinv) * gain[k];
-        if (AT == AT_BF16) v = bf16_round(v);
-        xs[k] = v;
-    }
-    __syncthreads();
-    for (int e = w; e < n_expert; e += 4) {
-        float acc = 0.f;
-        for (int k = lane; k < E; k += 64) {
-            float wv;
-            if constexpr (RT == 1)
-                wv = bf16_bits_f32(reinterpret_cast<const uint16_t *>(wr)[(long long)e * E + k]);
-            else
-                wv = reinterpret_cast<const float *>(wr)[(long long)e * E + k];
-            acc = fmaf(wv, xs[k], acc);
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const int i = threadIdx.x + u * 256;
+            if (i < n4) reinterpret_cast<f32x4 *>(sp)[i] = v[u];
         }
-        acc = wave_sum(acc);
-        if (lane == 0) r[e] = acc;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        unsigned long long used = 0ull;
-        int sel[8];
-        for (int a2 = 0; a2 < k_used; ++a2) {
-            int best = -1;
-            for (int e = 0; e < n_expert; ++e) {
-                if ((used >> e) & 1ull) continue;
-                if (best < 0 || r[e] > r[best]) best = e;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < OPT; ++u) {
+            const int idx = threadIdx.x + u * 256;
+            if (idx < G * D) {
+                const int g = idx / D, d = idx % D;
+                float mm = M[u];
+                for (int x = 0; x < nc; ++x) mm = fmaxf(mm, sp[x * per + g * (D + 4)]);
+                const float f0 = expf(M[u] - mm);
+                float ll = L[u] * f0, aa = A[u] * f0;
+                for (int x = 0; x < nc; ++x) {
+                    const float *px = sp + x * per + g * (D + 4);
+                    const float f = expf(px[0] - mm);
+                    ll += px[1] * f;
+                    aa += px[4 + d] * f;
+                }
+                M[u] = mm;
+                L[u] = ll;
+                A[u] = aa;
             }
-            used |= 1ull << best;
-            sel[a2] = best;
-        }
-        const float mx = r[sel[0]];
-        float den = 0.f;
-        float pe[8];
-        for (int a2 = 0; a2 < k_used; ++a2) {
-            pe[a2] = expf(r[sel[a2]] - mx);
-            den += pe[a2];
-        }
-        for (int a2 = 0; a2 < k_used; ++a2) {
-            ids[b * k_used + a2] = sel[a2];
-            wts[b * k_used + a2] = pe[a2] / den;
         }
     }
-}
-
-// x[b][r] += sum_k w[b][k] * y[b*k_used + k][r]
-__global__ void __launch_bounds__(256) k_moe_combine(float *x, const float *y, const float *wts,
-                                                      int E, int k_used) {
-    const int b = blockIdx.y;
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= E) return;
-    float s = 0.f;
-    for (int k = 0; k < k_used; ++k)
-        s += wts[b * k_used + k] * y[((long long)b * k_used + k) * E + r];
-    x[(long long)b * E + r] += s;
-}
-
-// Re-lay a row-major matrix [N][K] (element size ES) into 1 KiB tiles.
-// Int8 codes are stored biased (u = q + 128); padding is the code of 0.
-template <int ES>
-__global__ void __launch_bounds__(256) k_pack(const uint8_t *src, int N, int K, int KT, int n_tiles,
-                                               uint8_t *dst) {
-    constexpr int EPL = 16 / ES;  // elements per lane chunk
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long total = (long long)n_tiles * KT * 64;
-    if (i >= total) return;
-    const int lane = (int)(i & 63);
-    const long long tileid = i >> 6;
-    const int nt = (int)(tileid / KT), kt = (int)(tileid % KT);
-    const int row = nt * 16 + (lane & 15);
-    const int k0 = kt * EPL * 4 + (lane >> 4) * EPL;
-    uint8_t out[16];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int k = k0 + e;
-        const bool in = row < N && k < K;
-#pragma unroll
-        for (int bb = 0; bb < ES; ++bb) {
-            uint8_t v = in ? src[((long long)row * K + k) * ES + bb] : 0;
-            if (ES == 1) v = (uint8_t)(v ^ 0x80u);
-            out[e * ES + bb] = v;
+    for (int u = 0; u < OPT; ++u) {
+        const int idx = threadIdx.x + u * 256;
+        if (idx < G * D) {
+            const int g = idx / D, d = idx % D;
+            a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A[u] / L[u];
         }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        o[q] = (uint32_t)out[4 * q] | ((uint32_t)out[4 * q + 1] << 8) | ((uint32_t)out[4 * q + 2] << 16) |
-               ((uint32_t)out[4 * q + 3] << 24);
-    reinterpret_cast<u32x4 *>(dst)[i] = o;
-}
-
-__global__ void __launch_bounds__(256) k_fill32(uint32_t *p, long long n, uint32_t v) {
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
-        p[i] = v;
-}
-
-__global__ void __launch_bounds__(256) k_iota(int *p, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = i;
-}
-
-__global__ void __launch_bounds__(256) k_copy_bytes(uint8_t *dst, const uint8_t *src, long long n) {
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
-        dst[i] = src[i];
-}
-
-// Scatter K and V of positions pos0..pos0+n-1 ([n][Hk][D]) into the pages of one layer.
-template <int ES>
-__global__ void __launch_bounds__(256) k_set_kv(char *kpool, char *vpool, const int *pt, const char *k,
-                                                 const char *v, int pos0, int n, int Hk, int D) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long total = (long long)n * Hk * D;
-    if (i >= total) return;
-    const int d = (int)(i % D);
-    const int j = (int)((i / D) % Hk);
-    const int t = (int)(i / ((long long)D * Hk));
-    const int p = pos0 + t;
-    const long long off = (((long long)pt[p / kPage] * Hk + j) * kPage + (p % kPage)) * D + d;
-    if constexpr (ES == 2) {
-        reinterpret_cast<uint16_t *>(kpool)[off] = reinterpret_cast<const uint16_t *>(k)[i];
-        reinterpret_cast<uint16_t *>(vpool)[off] = reinterpret_cast<const uint16_t *>(v)[i];
-    } else {
-        reinterpret_cast<float *>(kpool)[off] = reinterpret_cast<const float *>(k)[i];
-        reinterpret_cast<float *>(vpool)[off] = reinterpret_cast<const float *>(v)[i];
     }
 }
 

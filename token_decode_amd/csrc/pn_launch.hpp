@@ -1,0 +1,61 @@
+// pn_launch.hpp - launch entry points of the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "pn_kernels.hpp"
+
+namespace pn {
+
+// The GEMM variants of one decode step.
+enum GemmKind {
+    GK_QKV = 0,        // norm prologue, RoPE + KV-append epilogue
+    GK_RESID = 1,      // A-ready input, residual epilogue (O, down)
+    GK_SWIGLU = 2,     // norm prologue, gate/up pair, SwiGLU epilogue
+    GK_LOGITS = 3,     // norm prologue, two tiles per block, logits + argmax partials
+    GK_MOE_SWIGLU = 4, // gathered rows, per-expert gate/up pair
+    GK_MOE_DOWN = 5,   // gathered A-ready rows, per-expert down
+    GK_O = 6,          // fp32 rows rounded to the activation type, residual epilogue
+    GK_COUNT = 7
+};
+
+// LDS a launch may use, in bytes (the hardware limit of one work-group).
+constexpr size_t kMaxLds = 160 * 1024;
+
+// Defined once per (weight type, activation type) in pn_gemm.hip; nw = waves
+// per work-group (4, 8 or 16); alds = stage an A-ready input in LDS.  With occ
+// non-null nothing is launched: *occ receives the resident work-groups per CU.
+void launch_gemm_f32_f32(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+                         int *occ);
+void launch_gemm_f32_bf16(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+                         int *occ);
+void launch_gemm_bf16_f32(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+                         int *occ);
+void launch_gemm_bf16_bf16(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+                         int *occ);
+void launch_gemm_i8_bf16(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+                         int *occ);
+
+// Defined once per (head_dim, KV type) in pn_attn.hip: attention with G query
+// heads per KV head, and the split combine when `combine`.
+#define PN_ATTN_DECL(name) void name(int G, const AttnArgs &a, dim3 grid, bool combine, hipStream_t s);
+PN_ATTN_DECL(launch_attn_32_0)
+PN_ATTN_DECL(launch_attn_32_1)
+PN_ATTN_DECL(launch_attn_64_0)
+PN_ATTN_DECL(launch_attn_64_1)
+PN_ATTN_DECL(launch_attn_128_0)
+PN_ATTN_DECL(launch_attn_128_1)
+#undef PN_ATTN_DECL
+
+inline void launch_attn(int D, int kvt, int G, const AttnArgs &a, dim3 grid, bool combine, hipStream_t s) {
+    if (kvt == 1) {
+        if (D == 32) launch_attn_32_1(G, a, grid, combine, s);
+        else if (D == 64) launch_attn_64_1(G, a, grid, combine, s);
+        else launch_attn_128_1(G, a, grid, combine, s);
+    } else {
+        if (D == 32) launch_attn_32_0(G, a, grid, combine, s);
+        else if (D == 64) launch_attn_64_0(G, a, grid, combine, s);
+        else launch_attn_128_0(G, a, grid, combine, s);
+    }
+}
+
+}  // namespace pn

@@ -12,11 +12,14 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "pn.h"
-#include "pn_kernels.hpp"
+#include "pn_launch.hpp"
+#include "pn_small.hpp"
 
 using namespace pn;
 
@@ -59,7 +62,8 @@ struct LayerOff {
 };
 
 struct Plan {
-    int kc = 1, ktc = 1, gx = 1, gz = 1;
+    int gx = 1, gz = 1, nw = 8, nblk = 1, tpw = 1;
+    bool a_lds = false;
     size_t lds = 0;
 };
 
@@ -75,9 +79,17 @@ struct pn_model {
     size_t embd, out_norm;
     Mat out;
     // scratch
-    size_t x, q, o, h, y, route_ids, route_w, part, cnt, am_val, am_idx;
-    size_t part_bytes = 0, cnt_count = 0, am_count = 0;
+    size_t x, q, o, h, y, route_ids, route_w, am_val, am_idx;
+    size_t o_bytes = 0, h_bytes = 0, am_count = 0;
+    int a_es = 2;                      // bytes per A-ready element
+    long long h_plane = 0;
+    int h_ld = 0;
     int attn_kps = 0;  // 0 = automatic
+    int nw[GK_COUNT] = {8, 8, 8, 8, 8, 8, 16};  // waves per work-group of each GEMM kind
+    int nw_down = 16;                       // the down projection (K = n_ff) uses GK_RESID too
+    std::map<std::tuple<int, int, int, size_t>, int> occ;  // resident work-groups per CU of a GEMM variant
+    size_t rope = 0, omega = 0, ssp = 0;
+    int ssp_ld = 0;
     int prof_kernel = -1;
     std::vector<hipEvent_t> ev;
     size_t ev_used = 0;
@@ -88,12 +100,58 @@ struct pn_state {
     char *base;
     size_t bytes;
     int max_ctx, n_pages, pos, s_cap;
-    size_t kpool, vpool, layer_bytes, pt, part, cnt, err;
+    size_t kpool, vpool, layer_bytes, pt, part, err;
 };
 
 namespace {
 
 int dtype_size(int dt) { return dt == PN_F32 ? 4 : (dt == PN_BF16 ? 2 : 1); }
+
+// LDS of one GEMM launch with nw waves: the A fragments of every k tile (when
+// A is staged in LDS), the waves' partial tiles and the summed tile.
+size_t lds_of(bool a_in_lds, int KT, int rows, int ntw, int fb, int nw) {
+    size_t a = a_in_lds ? (((size_t)KT * 4 * rows * fb + 255) & ~(size_t)255) : 0;
+    return a + (size_t)nw * ntw * 1024 + (size_t)ntw * 1024;
+}
+
+// A-ready inputs are copied into LDS when they take at most this much.
+constexpr size_t kALdsMax = 96 * 1024;
+constexpr int kCUs = 256;
+
+bool norm_kind(int kind) {  // A built in LDS from fp32 rows
+    return kind == GK_QKV || kind == GK_SWIGLU || kind == GK_LOGITS || kind == GK_MOE_SWIGLU || kind == GK_O;
+}
+int ntw_of(int kind) { return (kind == GK_SWIGLU || kind == GK_LOGITS || kind == GK_MOE_SWIGLU) ? 2 : 1; }
+
+struct OccKey {
+    int kind, nw, alds;
+    size_t lds;
+};
+
+// nblk row blocks per expert, gz experts.  Each work-group takes tpw
+// consecutive blocks, so that all work-groups are resident at once (by the
+// runtime's occupancy of this kernel) and carry equal work.
+template <typename OccFn>
+Plan make_plan(int kind, int nblk, int gz, int KT, int rows, int fb, int nw, OccFn occ_of) {
+    Plan p;
+    p.nw = nw;
+    p.gz = gz;
+    p.nblk = nblk;
+    const bool norm = norm_kind(kind);
+    p.a_lds = !norm && (size_t)KT * 4 * rows * fb <= kALdsMax;
+    // direct A fragments need the larger register budget (int8 needs twice the fragment registers)
+    if (!norm && !p.a_lds) p.nw = fb == 32 ? 4 : std::min(nw, 8);
+    p.lds = lds_of(norm || p.a_lds, KT, rows, ntw_of(kind), fb, p.nw);
+    while (p.lds > kMaxLds && p.nw > 4) {  // many A rows: fewer waves leave room for them
+        p.nw /= 2;
+        p.lds = lds_of(norm || p.a_lds, KT, rows, ntw_of(kind), fb, p.nw);
+    }
+    const int wpc = std::max(1, occ_of(kind, p.nw, p.a_lds, p.lds));
+    const long long slots = (long long)kCUs * wpc;
+    p.tpw = std::max(1, cdiv((long long)nblk * gz, slots));
+    p.gx = cdiv(nblk, p.tpw);
+    return p;
+}
 
 // n_kv_head 0 stands for n_head (the pages' default for the key)
 pn_config normalized(const pn_config &c) {
@@ -115,14 +173,19 @@ int check_config_n(const pn_config *c) {
         c->n_vocab < 1)
         return fail(PN_EINVAL, "dimensions must be positive");
     if (c->n_head % c->n_kv_head != 0) return fail(PN_EINVAL, "n_head must be a multiple of n_kv_head");
-    if (c->n_head / c->n_kv_head > kMaxG)
-        return fail(PN_EUNSUPPORTED, "at most %d query heads per kv head", kMaxG);
+    {
+        const int G = c->n_head / c->n_kv_head;
+        if (G != 1 && G != 2 && G != 3 && G != 4 && G != 6 && G != 8)
+            return fail(PN_EUNSUPPORTED, "query heads per kv head must be 1, 2, 3, 4, 6 or 8");
+    }
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
         return fail(PN_EUNSUPPORTED, "head_dim must be 32, 64 or 128");
     if (c->n_expert < 0 || c->n_expert > 64) return fail(PN_EINVAL, "n_expert must be in [0, 64]");
     if (c->n_expert > 0 && (c->n_expert_used < 1 || c->n_expert_used > std::min(8, c->n_expert)))
         return fail(PN_EINVAL, "n_expert_used must be in [1, min(8, n_expert)]");
     if (c->sliding_window < 0) return fail(PN_EINVAL, "sliding_window must be >= 0");
+    if (c->n_embd % 8 != 0 || c->n_embd > 8192)
+        return fail(PN_EUNSUPPORTED, "n_embd must be a multiple of 8 and at most 8192");
     if (c->n_ctx < 0) return fail(PN_EINVAL, "n_ctx must be >= 0");
     if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(PN_EINVAL, "rope_theta must be > 0");
     if (!(c->rms_norm_eps >= 0.f) || !std::isfinite(c->rms_norm_eps)) return fail(PN_EINVAL, "rms_norm_eps must be >= 0");
@@ -136,6 +199,9 @@ int check_config_n(const pn_config *c) {
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
                     c->max_batch, kMaxRows / pieces);
+    const int kt = cdiv(c->n_embd, tile_k(c->w_dtype));
+    if (lds_of(true, kt, c->max_batch * pieces, 2, frag_bytes(c->w_dtype), 4) > kMaxLds)
+        return fail(PN_EUNSUPPORTED, "n_embd %d too large for max_batch %d", c->n_embd, c->max_batch);
     return PN_OK;
 }
 
@@ -149,27 +215,6 @@ Mat make_mat(int N, int K, int wt) {
     return m;
 }
 
-size_t lds_of(int ktc, int rows, int ntw, int fb) {
-    return align256((size_t)ktc * 4 * rows * fb) + (size_t)kNW * ntw * 1024 + (size_t)ntw * 1024;
-}
-
-Plan make_plan(int gx, int gz, int KT, int rows, int ntw, int fb) {
-    Plan p;
-    p.gx = gx;
-    p.gz = gz;
-    int kc = 1;
-    for (;;) {
-        int ktc = cdiv(KT, kc);
-        bool big = lds_of(ktc, rows, ntw, fb) > 64 * 1024;
-        bool more = (long long)gx * gz * kc * kNW < 4096 && cdiv(KT, (long long)kc * 2) >= kNW * 8;
-        if ((big || more) && kc < KT) kc *= 2;
-        else break;
-    }
-    p.ktc = cdiv(KT, kc);
-    p.kc = cdiv(KT, p.ktc);
-    p.lds = lds_of(p.ktc, rows, ntw, fb);
-    return p;
-}
 
 // Lay out the model buffer; returns its size. Works on a zero base for sizing.
 size_t layout_model(pn_model *m) {
@@ -219,39 +264,23 @@ size_t layout_model(pn_model *m) {
     }
     // scratch
     const int MB = c.max_batch, HD = m->H * m->D;
-    const int as = m->at == PN_F32 ? 4 : 2;
+    m->a_es = wt == PN_F32 ? 4 : 2;
+    const int tk = tile_k(wt);
+    m->h_ld = cdiv(m->F, tk) * tk;
+    m->h_plane = (long long)MB * m->n_used * m->h_ld;
+    m->o_bytes = (size_t)MB * HD * 4;
+    m->h_bytes = (size_t)m->pieces * m->h_plane * m->a_es;
     m->x = bp.take((size_t)MB * m->E * 4);
     m->q = bp.take((size_t)MB * HD * 4);
-    m->o = bp.take((size_t)MB * HD * as);
-    m->h = bp.take((size_t)MB * m->n_used * m->F * as);
+    m->o = bp.take(m->o_bytes);
+    m->h = bp.take(m->h_bytes);
     m->y = bp.take((size_t)MB * m->n_used * m->E * 4);
     m->route_ids = bp.take((size_t)MB * m->n_used * 4);
     m->route_w = bp.take((size_t)MB * m->n_used * 4);
-    // split-K scratch: the largest need over every GEMM and batch size
-    const int fb = frag_bytes(wt);
-    size_t pbytes = 0, ccount = 1;
-    for (int B = 1; B <= MB; ++B) {
-        const int rows = B * m->pieces;
-        const LayerOff &L = m->L[0];
-        struct { int gx, gz, KT, ntw; } g[] = {
-            {L.qkv.n_tiles, 1, L.qkv.KT, 1},
-            {L.o.n_tiles, 1, L.o.KT, 1},
-            {L.gate.n_tiles, c.n_expert > 0 ? m->X : 1, L.gate.KT, 2},
-            {L.down.n_tiles, c.n_expert > 0 ? m->X : 1, L.down.KT, 1},
-            {cdiv(m->out.n_tiles, 2), 1, m->out.KT, 2},
-        };
-        for (auto &e : g) {
-            Plan p = make_plan(e.gx, e.gz, e.KT, rows, e.ntw, fb);
-            if (p.kc > 1) {
-                pbytes = std::max(pbytes, (size_t)e.gx * e.gz * p.kc * e.ntw * 1024);
-                ccount = std::max(ccount, (size_t)e.gx * e.gz);
-            }
-        }
-    }
-    m->part_bytes = pbytes;
-    m->cnt_count = ccount;
-    m->part = bp.take(std::max<size_t>(pbytes, 256));
-    m->cnt = bp.take(ccount * 4);
+    m->rope = bp.take((size_t)MB * (m->D / 2) * 8);
+    m->omega = bp.take((size_t)(m->D / 2) * 8);
+    m->ssp_ld = cdiv(m->E, 16);
+    m->ssp = bp.take((size_t)MB * m->ssp_ld * 4);
     m->am_count = (size_t)cdiv(m->out.n_tiles, 2) * MB;
     m->am_val = bp.take(m->am_count * 4);
     m->am_idx = bp.take(m->am_count * 4);
@@ -272,8 +301,7 @@ size_t layout_state(pn_state *s) {
     s->kpool = bp.take(s->layer_bytes * m->cfg.n_layer);
     s->vpool = bp.take(s->layer_bytes * m->cfg.n_layer);
     s->pt = bp.take((size_t)s->n_pages * 4);
-    s->part = bp.take((size_t)m->Hk * s->s_cap * m->G * (m->D + 2) * 4);
-    s->cnt = bp.take((size_t)m->Hk * 4);
+    s->part = bp.take((size_t)m->Hk * s->s_cap * m->G * (m->D + 4) * 4);
     s->err = bp.take(4);
     return bp.off;
 }
@@ -309,36 +337,20 @@ void pack(const void *src, int N, int K, int wt, const Mat &mt, int tile_row0, u
 
 // ---------------------------------------------------------------- launch dispatch
 
-template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR>
-void launch_gemm_t(const GemmArgs &g, const Plan &p, hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm<WT, AT, PRO, EPI, NTW, PAIR>), dim3(p.gx, p.kc, p.gz), dim3(256), p.lds, s, g);
+void gemm_entry(int kind, int wt, int at, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds,
+                hipStream_t s, int *occ) {
+    if (wt == PN_BF16 && at == PN_F32) launch_gemm_bf16_f32(kind, nw, alds, g, grid, lds, s, occ);
+    else if (wt == PN_BF16) launch_gemm_bf16_bf16(kind, nw, alds, g, grid, lds, s, occ);
+    else if (wt == PN_F32 && at == PN_F32) launch_gemm_f32_f32(kind, nw, alds, g, grid, lds, s, occ);
+    else if (wt == PN_F32) launch_gemm_f32_bf16(kind, nw, alds, g, grid, lds, s, occ);
+    else launch_gemm_i8_bf16(kind, nw, alds, g, grid, lds, s, occ);
 }
 
-template <int PRO, int EPI, int NTW, bool PAIR>
-void launch_gemm(int wt, int at, const GemmArgs &g, const Plan &p, hipStream_t s) {
-    if (wt == PN_BF16 && at == PN_F32) launch_gemm_t<WT_BF16, AT_F32, PRO, EPI, NTW, PAIR>(g, p, s);
-    else if (wt == PN_BF16) launch_gemm_t<WT_BF16, AT_BF16, PRO, EPI, NTW, PAIR>(g, p, s);
-    else if (wt == PN_F32 && at == PN_F32) launch_gemm_t<WT_F32, AT_F32, PRO, EPI, NTW, PAIR>(g, p, s);
-    else if (wt == PN_F32) launch_gemm_t<WT_F32, AT_BF16, PRO, EPI, NTW, PAIR>(g, p, s);
-    else launch_gemm_t<WT_I8, AT_BF16, PRO, EPI, NTW, PAIR>(g, p, s);
-}
-
-template <int D, int KV>
-void launch_attn_d(int at, const AttnArgs &a, dim3 grid, hipStream_t s) {
-    if (at == PN_BF16) hipLaunchKernelGGL((k_attn<D, KV, AT_BF16>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn<D, KV, AT_F32>), grid, dim3(256), 0, s, a);
-}
-
-void launch_attn(int D, int kvt, int at, const AttnArgs &a, dim3 grid, hipStream_t s) {
-    if (kvt == PN_BF16) {
-        if (D == 32) launch_attn_d<32, 1>(at, a, grid, s);
-        else if (D == 64) launch_attn_d<64, 1>(at, a, grid, s);
-        else launch_attn_d<128, 1>(at, a, grid, s);
-    } else {
-        if (D == 32) launch_attn_d<32, 0>(at, a, grid, s);
-        else if (D == 64) launch_attn_d<64, 0>(at, a, grid, s);
-        else launch_attn_d<128, 0>(at, a, grid, s);
-    }
+void launch_gemm(int kind, int wt, int at, GemmArgs g, const Plan &p, hipStream_t s) {
+    const dim3 grid(p.gx, 1, p.gz);
+    g.nblk = p.nblk;
+    g.tpw = p.tpw;
+    gemm_entry(kind, wt, at, p.nw, p.a_lds, g, grid, p.lds, s, nullptr);
 }
 
 // event timing of one kernel class
@@ -373,20 +385,23 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     const int rows = n * m->pieces;
     const int fb = frag_bytes(wt);
     const int kv_es = dtype_size(m->kvt);
+    const bool moe = c.n_expert > 0;
 
     SlotPtrs sp{};
     GemmArgs base{};
     base.B = n;
     base.eps = c.rms_norm_eps;
-    base.part = (float *)(mb + m->part);
-    base.cnt = (int *)(mb + m->cnt);
     base.Hq = m->H;
     base.Hk = m->Hk;
     base.D = m->D;
     base.kv_es = kv_es;
-    base.theta = (double)c.rope_theta;
+    base.rope = (const float2 *)(mb + m->rope);
+    base.ssp = (float *)(mb + m->ssp);
+    base.ssp_ld = m->ssp_ld;
+    base.ssp_n = m->ssp_ld;
     for (int b = 0; b < n; ++b) {
         sp.err[b] = (int *)(st[b]->base + st[b]->err);
+        sp.pos[b] = st[b]->pos;
         base.err[b] = sp.err[b];
         base.pos[b] = st[b]->pos;
         base.pt[b] = (const int *)(st[b]->base + st[b]->pt);
@@ -395,47 +410,60 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     float *x = (float *)(mb + m->x);
     {
         Timed tm(m, PN_K_EMBED, s);
+        float2 *rope = (float2 *)(mb + m->rope);
+        const double *omega = (const double *)(mb + m->omega);
+        float *ssp = (float *)(mb + m->ssp);
         if (wt == PN_F32)
-            hipLaunchKernelGGL(k_embed<0>, dim3(n), dim3(256), 0, s, (const void *)(mb + m->embd), tok, x, E, m->V, sp);
+            hipLaunchKernelGGL(k_embed<0>, dim3(n), dim3(256), 0, s, (const void *)(mb + m->embd), tok, x, E, m->V, sp,
+                               rope, omega, m->D, ssp, m->ssp_ld);
         else
-            hipLaunchKernelGGL(k_embed<1>, dim3(n), dim3(256), 0, s, (const void *)(mb + m->embd), tok, x, E, m->V, sp);
+            hipLaunchKernelGGL(k_embed<1>, dim3(n), dim3(256), 0, s, (const void *)(mb + m->embd), tok, x, E, m->V, sp,
+                               rope, omega, m->D, ssp, m->ssp_ld);
     }
 
     // attention geometry per slot
     AttnArgs aa{};
     aa.q = (const float *)(mb + m->q);
-    aa.o = mb + m->o;
+    aa.o = (float *)(mb + m->o);
     aa.Hq = m->H;
     aa.Hk = m->Hk;
-    aa.G = m->G;
     aa.scale = (float)(1.0 / std::sqrt((double)m->D));
     int nsplit_max = 1;
-    int kps = m->attn_kps > 0 ? m->attn_kps : attn_kps_min();
+    const int kps = m->attn_kps > 0 ? m->attn_kps : attn_kps_min();
     for (int b = 0; b < n; ++b) {
         const int pos = st[b]->pos;
         const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
         aa.pos[b] = pos;
         aa.t0[b] = t0;
         aa.nsplit[b] = cdiv(pos - t0 + 1, kps);
+        aa.s_cap[b] = st[b]->s_cap;
+        if (aa.nsplit[b] > st[b]->s_cap) return fail(PN_ERANGE, "attention splits exceed state scratch");
         nsplit_max = std::max(nsplit_max, aa.nsplit[b]);
         aa.pt[b] = (const int *)(st[b]->base + st[b]->pt);
         aa.part[b] = (float *)(st[b]->base + st[b]->part);
-        aa.cnt[b] = (int *)(st[b]->base + st[b]->cnt);
     }
     aa.kps = kps;
-    for (int b = 0; b < n; ++b) {
-        aa.s_cap[b] = st[b]->s_cap;
-        if (aa.nsplit[b] > st[b]->s_cap) return fail(PN_ERANGE, "attention splits exceed state scratch");
-    }
 
     const LayerOff &L0 = m->L[0];
-    Plan p_qkv = make_plan(L0.qkv.n_tiles, 1, L0.qkv.KT, rows, 1, fb);
-    Plan p_o = make_plan(L0.o.n_tiles, 1, L0.o.KT, rows, 1, fb);
-    const bool moe = c.n_expert > 0;
-    const int rows_moe = std::min(n, kMaxSlots) * m->pieces;
-    Plan p_gu = make_plan(L0.gate.n_tiles, moe ? m->X : 1, L0.gate.KT, moe ? rows_moe : rows, 2, fb);
-    Plan p_dn = make_plan(L0.down.n_tiles, moe ? m->X : 1, L0.down.KT, moe ? rows_moe : rows, 1, fb);
-    Plan p_lm = make_plan(cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, 2, fb);
+    const int gz = moe ? m->X : 1;
+    auto occ_of = [&](int kind, int nw, bool alds, size_t lds) -> int {
+        const auto key = std::make_tuple(kind, nw, alds ? 1 : 0, lds);
+        auto it = m->occ.find(key);
+        if (it != m->occ.end()) return it->second;
+        int n = 1;
+        GemmArgs none{};
+        gemm_entry(kind, wt, at, nw, alds, none, dim3(1), lds, s, &n);
+        m->occ[key] = n;
+        return n;
+    };
+    const Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of);
+    const Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of);
+    const Plan p_gu = make_plan(moe ? GK_MOE_SWIGLU : GK_SWIGLU, L0.gate.n_tiles, gz, L0.gate.KT, rows, fb,
+                                m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of);
+    const Plan p_dn = make_plan(moe ? GK_MOE_DOWN : GK_RESID, L0.down.n_tiles, gz, L0.down.KT, rows, fb,
+                                moe ? m->nw[GK_MOE_DOWN] : m->nw_down, occ_of);
+    const Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of);
+    // (plans for the other kinds take one row block per tile)
 
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerOff &L = m->L[l];
@@ -448,8 +476,6 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.n_tiles = L.qkv.n_tiles;
             g.KT = L.qkv.KT;
             g.K = E;
-            g.kc = p_qkv.kc;
-            g.ktc = p_qkv.ktc;
             g.x = x;
             g.gain = (const float *)(mb + L.attn_norm);
             g.q_out = (float *)(mb + m->q);
@@ -458,16 +484,16 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.kvv[b] = st[b]->base + st[b]->vpool + (size_t)l * st[b]->layer_bytes;
             }
             Timed tm(m, PN_K_QKV, s);
-            launch_gemm<PRO_NORM, EPI_QKV, 1, false>(wt, at, g, p_qkv, s);
+            launch_gemm(GK_QKV, wt, at, g, p_qkv, s);
         }
-        // ---- attention
+        // ---- attention (+ split combine)
         {
             for (int b = 0; b < n; ++b) {
                 aa.kvk[b] = st[b]->base + st[b]->kpool + (size_t)l * st[b]->layer_bytes;
                 aa.kvv[b] = st[b]->base + st[b]->vpool + (size_t)l * st[b]->layer_bytes;
             }
             Timed tm(m, PN_K_ATTN, s);
-            launch_attn(m->D, m->kvt, at, aa, dim3(nsplit_max, m->Hk, n), s);
+            launch_attn(m->D, m->kvt, m->G, aa, dim3(nsplit_max, m->Hk, n), nsplit_max > 1, s);
         }
         // ---- O projection + residual
         {
@@ -478,14 +504,11 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.n_tiles = L.o.n_tiles;
             g.KT = L.o.KT;
             g.K = HD;
-            g.kc = p_o.kc;
-            g.ktc = p_o.ktc;
-            g.a = mb + m->o;
-            g.lda = HD;
+            g.x = (const float *)(mb + m->o);
             g.out_f32 = x;
             g.ld_out = E;
             Timed tm(m, PN_K_O, s);
-            launch_gemm<PRO_LOAD, EPI_RESID, 1, false>(wt, at, g, p_o, s);
+            launch_gemm(GK_O, wt, at, g, p_o, s);
         }
         // ---- FFN
         if (!moe) {
@@ -499,14 +522,13 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.n_tiles = L.gate.n_tiles;
                 g.KT = L.gate.KT;
                 g.K = E;
-                g.kc = p_gu.kc;
-                g.ktc = p_gu.ktc;
                 g.x = x;
                 g.gain = (const float *)(mb + L.ffn_norm);
                 g.out_act = mb + m->h;
-                g.ld_out = F;
+                g.out_plane = m->h_plane;
+                g.ld_out = m->h_ld;
                 Timed tm(m, PN_K_GATEUP, s);
-                launch_gemm<PRO_NORM, EPI_SWIGLU, 2, true>(wt, at, g, p_gu, s);
+                launch_gemm(GK_SWIGLU, wt, at, g, p_gu, s);
             }
             {
                 GemmArgs g = base;
@@ -516,14 +538,13 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.n_tiles = L.down.n_tiles;
                 g.KT = L.down.KT;
                 g.K = F;
-                g.kc = p_dn.kc;
-                g.ktc = p_dn.ktc;
                 g.a = mb + m->h;
-                g.lda = F;
+                g.a_plane = m->h_plane;
+                g.lda = m->h_ld;
                 g.out_f32 = x;
                 g.ld_out = E;
                 Timed tm(m, PN_K_DOWN, s);
-                launch_gemm<PRO_LOAD, EPI_RESID, 1, false>(wt, at, g, p_dn, s);
+                launch_gemm(GK_RESID, wt, at, g, p_dn, s);
             }
         } else {
             int *rid = (int *)(mb + m->route_ids);
@@ -535,14 +556,14 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 const float *gn = (const float *)(mb + L.ffn_norm);
                 if (wt == PN_F32) {
                     if (at == PN_F32)
-                        hipLaunchKernelGGL((k_router<0, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                        hipLaunchKernelGGL((k_router<0, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
                     else
-                        hipLaunchKernelGGL((k_router<0, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                        hipLaunchKernelGGL((k_router<0, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
                 } else {
                     if (at == PN_F32)
-                        hipLaunchKernelGGL((k_router<1, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                        hipLaunchKernelGGL((k_router<1, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
                     else
-                        hipLaunchKernelGGL((k_router<1, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, rid, rw);
+                        hipLaunchKernelGGL((k_router<1, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
                 }
             }
             {
@@ -557,17 +578,16 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.n_tiles = L.gate.n_tiles;
                 g.KT = L.gate.KT;
                 g.K = E;
-                g.kc = p_gu.kc;
-                g.ktc = p_gu.ktc;
                 g.x = x;
                 g.gain = (const float *)(mb + L.ffn_norm);
                 g.route_ids = rid;
                 g.n_slots = n;
                 g.n_used = m->n_used;
                 g.out_act = mb + m->h;
-                g.ld_out = F;
+                g.out_plane = m->h_plane;
+                g.ld_out = m->h_ld;
                 Timed tm(m, PN_K_MOE_GATEUP, s);
-                launch_gemm<PRO_NORM, EPI_MOE_SWIGLU, 2, true>(wt, at, g, p_gu, s);
+                launch_gemm(GK_MOE_SWIGLU, wt, at, g, p_gu, s);
             }
             {
                 GemmArgs g = base;
@@ -579,22 +599,22 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.n_tiles = L.down.n_tiles;
                 g.KT = L.down.KT;
                 g.K = F;
-                g.kc = p_dn.kc;
-                g.ktc = p_dn.ktc;
                 g.a = mb + m->h;
-                g.lda = F;
+                g.a_plane = m->h_plane;
+                g.lda = m->h_ld;
                 g.route_ids = rid;
                 g.n_slots = n;
                 g.n_used = m->n_used;
                 g.out_f32 = (float *)(mb + m->y);
                 g.ld_out = E;
                 Timed tm(m, PN_K_MOE_DOWN, s);
-                launch_gemm<PRO_LOAD, EPI_MOE_DOWN, 1, false>(wt, at, g, p_dn, s);
+                launch_gemm(GK_MOE_DOWN, wt, at, g, p_dn, s);
             }
             {
                 Timed tm(m, PN_K_MOE_COMBINE, s);
                 hipLaunchKernelGGL(k_moe_combine, dim3(cdiv(E, 256), n), dim3(256), 0, s, x,
-                                   (const float *)(mb + m->y), (const float *)rw, E, m->n_used);
+                                   (const float *)(mb + m->y), (const float *)rw, E, m->n_used,
+                                   (float *)(mb + m->ssp), m->ssp_ld);
             }
         }
     }
@@ -607,20 +627,18 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         g.n_tiles = m->out.n_tiles;
         g.KT = m->out.KT;
         g.K = E;
-        g.kc = p_lm.kc;
-        g.ktc = p_lm.ktc;
         g.x = x;
         g.gain = (const float *)(mb + m->out_norm);
         g.out_f32 = logits;
         g.am_val = (float *)(mb + m->am_val);
         g.am_idx = (int *)(mb + m->am_idx);
         Timed tm(m, PN_K_LMHEAD, s);
-        launch_gemm<PRO_NORM, EPI_LOGITS, 2, false>(wt, at, g, p_lm, s);
+        launch_gemm(GK_LOGITS, wt, at, g, p_lm, s);
     }
     {
         Timed tm(m, PN_K_ARGMAX, s);
         hipLaunchKernelGGL(k_argmax, dim3(n), dim3(256), 0, s, (const float *)(mb + m->am_val),
-                           (const int *)(mb + m->am_idx), p_lm.gx, n, (int *)amax);
+                           (const int *)(mb + m->am_idx), p_lm.nblk, n, (int *)amax);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -696,7 +714,9 @@ int pn_model_load_globals(pn_model *m, const void *tok_embd, const float *out_no
         fill32(mb + m->out.soff, (size_t)m->out.n_tiles * 16, 0u, s);
         copy_bytes(mb + m->out.soff, s_out, (size_t)m->V * 4, s);
     }
-    fill32(mb + m->cnt, m->cnt_count, 0u, s);
+    hipLaunchKernelGGL(k_omega, dim3(1), dim3(64), 0, s, (double *)(mb + m->omega), m->D, (double)m->cfg.rope_theta);
+    fill32(mb + m->o, m->o_bytes / 4, 0u, s);
+    fill32(mb + m->h, m->h_bytes / 4, 0u, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PN_EHIP, "weight packing failed: %s", hipGetErrorString(e));
     return PN_OK;
@@ -803,7 +823,6 @@ int pn_state_reset(pn_state *s, void *stream) {
     hipStream_t st = S(stream);
     fill32(s->base + s->kpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
     fill32(s->base + s->vpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
-    fill32(s->base + s->cnt, (size_t)s->m->Hk, 0u, st);
     fill32(s->base + s->err, 1, 0u, st);
     s->pos = 0;
     hipError_t e = hipGetLastError();
@@ -931,6 +950,17 @@ int pn_forward_step(pn_model *m, pn_state *s, const int32_t *token_dev, float *l
 int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
     g_err.clear();
     if (!m) return fail(PN_EINVAL, "model is NULL");
+    if (option >= PN_OPT_WAVES_QKV && option <= PN_OPT_WAVES_LMHEAD) {
+        if (value != 4 && value != 8 && value != 16) return fail(PN_EINVAL, "waves must be 4, 8 or 16");
+        switch (option) {
+            case PN_OPT_WAVES_QKV: m->nw[GK_QKV] = (int)value; break;
+            case PN_OPT_WAVES_O: m->nw[GK_O] = (int)value; break;
+            case PN_OPT_WAVES_GATEUP: m->nw[GK_SWIGLU] = (int)value; m->nw[GK_MOE_SWIGLU] = (int)value; break;
+            case PN_OPT_WAVES_DOWN: m->nw_down = (int)value; m->nw[GK_MOE_DOWN] = (int)value; break;
+            default: m->nw[GK_LOGITS] = (int)value; break;
+        }
+        return PN_OK;
+    }
     if (option == PN_OPT_ATTN_KEYS_PER_SPLIT) {
         if (value < 0 || value % attn_kps_min() != 0 || value > (1 << 24))
             return fail(PN_EINVAL, "keys per split must be 0 or a multiple of %d", attn_kps_min());

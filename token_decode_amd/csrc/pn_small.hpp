@@ -1,0 +1,333 @@
+// pn_small.hpp - the small kernels of the decode step (embedding, argmax,
+// MoE router and combine) and the one-time set-up kernels (weight packing,
+// fills, K/V scatter).  Included only by pn_lib.hip.
+#pragma once
+#include "pn_kernels.hpp"
+
+namespace pn {
+
+// ---------------------------------------------------------------- small kernels
+
+struct SlotPtrs {
+    int *err[kMaxSlots];
+    int pos[kMaxSlots];
+};
+
+// Sum of squares of the 16 values held by a group of 16 consecutive lanes.
+__device__ __forceinline__ float group16_sumsq(float v) {
+    float sq = v * v;
+    sq += __shfl_xor(sq, 8, 64);
+    sq += __shfl_xor(sq, 4, 64);
+    sq += __shfl_xor(sq, 2, 64);
+    sq += __shfl_xor(sq, 1, 64);
+    return sq;
+}
+
+// x[b] = tok_embd[token[b]] (fp32 or bf16 table); a bad id uses row 0 and sets
+// a flag.  Also writes the sums of squares of x per 16-element tile and the
+// step's RoPE table: for rotation index i of slot b, (cos, sin) of
+// pos_b * omega_i with the angle, its sine and cosine in fp64, rounded to fp32.
+// One work-group of 256 threads per slot; E <= 8192.
+template <int ET>
+__global__ void __launch_bounds__(256) k_embed(const void *embd, const int *tokens, float *x, int E,
+                                                 int V, SlotPtrs sp, float2 *rope, const double *omega,
+                                                 int D, float *ssp, int ssp_ld) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    int tok = tokens[b];
+    if (tok < 0 || tok >= V) {
+        if (tid == 0) atomicOr(sp.err[b], ERR_TOKEN);
+        tok = 0;
+    }
+    // 32 consecutive elements per thread, loaded before any store
+    constexpr int EPT = 32;
+    float v[EPT];
+    const int k0 = tid * EPT;
+    if (k0 < E) {
+        if constexpr (ET == 1) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(embd) +
+                                                               (long long)tok * E + k0);
+            u32x4 w[EPT / 8];
+#pragma unroll
+            for (int q = 0; q < EPT / 8; ++q) w[q] = (k0 + 8 * q < E) ? src[q] : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < EPT / 8; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[8 * q + 2 * e] = __uint_as_float(w[q][e] << 16);
+                    v[8 * q + 2 * e + 1] = __uint_as_float(w[q][e] & 0xFFFF0000u);
+                }
+        } else {
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(embd) +
+                                                               (long long)tok * E + k0);
+            f32x4 w[EPT / 4];
+#pragma unroll
+            for (int q = 0; q < EPT / 4; ++q) w[q] = (k0 + 4 * q < E) ? src[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < EPT / 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * q + e] = w[q][e];
+        }
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q)
+            if (k0 + 4 * q < E)
+                *reinterpret_cast<f32x4 *>(x + (long long)b * E + k0 + 4 * q) =
+                    f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        // two 16-element tiles per thread
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (k0 + 16 * h < E) {
+                float sq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sq += v[16 * h + e] * v[16 * h + e];
+                ssp[(long long)b * ssp_ld + (k0 >> 4) + h] = sq;
+            }
+        }
+    }
+    for (int i = tid; i < D / 2; i += 256) {
+        const double phi = (double)sp.pos[b] * omega[i];
+        double sn, cs;
+        sincos(phi, &sn, &cs);
+        rope[(long long)b * (D / 2) + i] = make_float2((float)cs, (float)sn);
+    }
+}
+
+// omega_i = theta^(-2i/D) in fp64, once per model.
+__global__ void __launch_bounds__(64) k_omega(double *omega, int D, double theta) {
+    for (int i = threadIdx.x; i < D / 2; i += 64) omega[i] = pow(theta, -2.0 * (double)i / (double)D);
+}
+
+// argmax[b] over the LM head's per-block partials (value, lowest index on ties).
+// Up to 16 partials per thread are loaded before any comparison.
+__global__ void __launch_bounds__(256) k_argmax(const float *val, const int *idx, int nwg, int nb, int *out) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    float best = 0.f;
+    int bi = -1;
+    for (int base = 0; base < nwg; base += 256 * 16) {
+        float vv[16];
+        int ii[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int w = base + tid + 256 * u;
+            ii[u] = w < nwg ? idx[(long long)w * nb + b] : -1;
+            vv[u] = w < nwg ? val[(long long)w * nb + b] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = ii[u];
+            const float v = vv[u];
+            if (i < 0) continue;
+            if (bi < 0 || v > best || (v == best && i < bi)) { best = v; bi = i; }
+        }
+    }
+    __shared__ float sv[256];
+    __shared__ int si[256];
+    sv[tid] = best;
+    si[tid] = bi;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) {
+            const float v = sv[tid + o];
+            const int i = si[tid + o];
+            if (i >= 0 && (si[tid] < 0 || v > sv[tid] || (v == sv[tid] && i < si[tid]))) {
+                sv[tid] = v;
+                si[tid] = i;
+            }
+        }
+        __syncthreads();
+    }
+    if (tid == 0 && out) out[b] = si[0];
+}
+
+// MoE router of one slot: xn = round_act(RMSNorm(x)*g) with the norm from the
+// per-tile sums of squares; r = W_r xn; top-k by fp32 logit (ties to the lower
+// index); weights = softmax over the chosen logits.  256 threads; E <= 8192,
+// E a multiple of 8.
+template <int RT, int AT>
+__global__ void __launch_bounds__(256) k_router(const float *x, const float *gain, const void *wr, int E,
+                                                 int n_expert, int k_used, float eps, const float *ssp, int ssp_ld,
+                                                 int ssp_n, int *ids, float *wts) {
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    extern __shared__ float xs[];  // [E]
+    __shared__ float red4[4];
+    __shared__ float r[64];
+    const float *xr = x + (long long)b * E;
+    // this thread's 32 elements of x and gain, and a share of the sums of squares
+    constexpr int EPT = 32;
+    const int k0 = tid * EPT;
+    f32x4 xv[EPT / 4], gv[EPT / 4];
+#pragma unroll
+    for (int q = 0; q < EPT / 4; ++q) {
+        const bool in = k0 + 4 * q < E;
+        xv[q] = in ? reinterpret_cast<const f32x4 *>(xr + k0)[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+        gv[q] = in ? reinterpret_cast<const f32x4 *>(gain + k0)[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float ss = 0.f;
+    for (int i = tid; i < ssp_n; i += 256) ss += ssp[(long long)b * ssp_ld + i];
+    ss = block_sum<4>(ss, red4);
+    const float rinv = 1.0f / sqrtf(ss / (float)E + eps);
+#pragma unroll
+    for (int q = 0; q < EPT / 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = k0 + 4 * q + e;
+            if (k < E) {
+                float v = (xv[q][e] * rinv) * gv[q][e];
+                if (AT == AT_BF16) v = bf16_round(v);
+                xs[k] = v;
+            }
+        }
+    __syncthreads();
+    // expert e on wave e % 4: lanes stride over E in 8-element groups
+    for (int e = w; e < n_expert; e += 4) {
+        float acc = 0.f;
+        for (int base = 0; base < E; base += 64 * 8 * 8) {
+            float wv[8][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = base + (lane + 64 * u) * 8;
+                if (k < E) {
+                    if constexpr (RT == 1) {
+                        const u32x4 q = *reinterpret_cast<const u32x4 *>(
+                            reinterpret_cast<const uint16_t *>(wr) + (long long)e * E + k);
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            wv[u][2 * h] = __uint_as_float(q[h] << 16);
+                            wv[u][2 * h + 1] = __uint_as_float(q[h] & 0xFFFF0000u);
+                        }
+                    } else {
+                        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(wr) +
+                                                                           (long long)e * E + k);
+                        const f32x4 q0 = p[0], q1 = p[1];
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) { wv[u][h] = q0[h]; wv[u][4 + h] = q1[h]; }
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) wv[u][h] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = base + (lane + 64 * u) * 8;
+                if (k < E)
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) acc = fmaf(wv[u][h], xs[k + h], acc);
+            }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) r[e] = acc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long used = 0ull;
+        int sel[8];
+        for (int a2 = 0; a2 < k_used; ++a2) {
+            int best = -1;
+            for (int e = 0; e < n_expert; ++e) {
+                if ((used >> e) & 1ull) continue;
+                if (best < 0 || r[e] > r[best]) best = e;
+            }
+            used |= 1ull << best;
+            sel[a2] = best;
+        }
+        const float mx = r[sel[0]];
+        float den = 0.f;
+        float pe[8];
+        for (int a2 = 0; a2 < k_used; ++a2) {
+            pe[a2] = expf(r[sel[a2]] - mx);
+            den += pe[a2];
+        }
+        for (int a2 = 0; a2 < k_used; ++a2) {
+            ids[b * k_used + a2] = sel[a2];
+            wts[b * k_used + a2] = pe[a2] / den;
+        }
+    }
+}
+
+// x[b][r] += sum_k w[b][k] * y[b*k_used + k][r], and the new per-tile sums of squares.
+__global__ void __launch_bounds__(256) k_moe_combine(float *x, const float *y, const float *wts, int E,
+                                                      int k_used, float *ssp, int ssp_ld) {
+    const int b = blockIdx.y;
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    float xn = 0.f;
+    if (r < E) {
+        float s = 0.f;
+        for (int k = 0; k < k_used; ++k) s += wts[b * k_used + k] * y[((long long)b * k_used + k) * E + r];
+        xn = x[(long long)b * E + r] + s;
+        x[(long long)b * E + r] = xn;
+    }
+    const float sq = group16_sumsq(xn);
+    if ((threadIdx.x & 15) == 0 && r < E) ssp[(long long)b * ssp_ld + (r >> 4)] = sq;
+}
+
+// Re-lay a row-major matrix [N][K] (element size ES) into 1 KiB tiles.
+// Int8 codes are stored biased (u = q + 128); padding is the code of 0.
+template <int ES>
+__global__ void __launch_bounds__(256) k_pack(const uint8_t *src, int N, int K, int KT, int n_tiles,
+                                               uint8_t *dst) {
+    constexpr int EPL = 16 / ES;  // elements per lane chunk
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)n_tiles * KT * 64;
+    if (i >= total) return;
+    const int lane = (int)(i & 63);
+    const long long tileid = i >> 6;
+    const int nt = (int)(tileid / KT), kt = (int)(tileid % KT);
+    const int row = nt * 16 + (lane & 15);
+    const int k0 = kt * EPL * 4 + (lane >> 4) * EPL;
+    uint8_t out[16];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int k = k0 + e;
+        const bool in = row < N && k < K;
+#pragma unroll
+        for (int bb = 0; bb < ES; ++bb) {
+            uint8_t v = in ? src[((long long)row * K + k) * ES + bb] : 0;
+            if (ES == 1) v = (uint8_t)(v ^ 0x80u);
+            out[e * ES + bb] = v;
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)out[4 * q] | ((uint32_t)out[4 * q + 1] << 8) | ((uint32_t)out[4 * q + 2] << 16) |
+               ((uint32_t)out[4 * q + 3] << 24);
+    reinterpret_cast<u32x4 *>(dst)[i] = o;
+}
+
+__global__ void __launch_bounds__(256) k_fill32(uint32_t *p, long long n, uint32_t v) {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+        p[i] = v;
+}
+
+__global__ void __launch_bounds__(256) k_iota(int *p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = i;
+}
+
+__global__ void __launch_bounds__(256) k_copy_bytes(uint8_t *dst, const uint8_t *src, long long n) {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+        dst[i] = src[i];
+}
+
+// Scatter K and V of positions pos0..pos0+n-1 ([n][Hk][D]) into the pages of one layer.
+template <int ES>
+__global__ void __launch_bounds__(256) k_set_kv(char *kpool, char *vpool, const int *pt, const char *k,
+                                                 const char *v, int pos0, int n, int Hk, int D) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)n * Hk * D;
+    if (i >= total) return;
+    const int d = (int)(i % D);
+    const int j = (int)((i / D) % Hk);
+    const int t = (int)(i / ((long long)D * Hk));
+    const int p = pos0 + t;
+    const long long off = (((long long)pt[p / kPage] * Hk + j) * kPage + (p % kPage)) * D + d;
+    if constexpr (ES == 2) {
+        reinterpret_cast<uint16_t *>(kpool)[off] = reinterpret_cast<const uint16_t *>(k)[i];
+        reinterpret_cast<uint16_t *>(vpool)[off] = reinterpret_cast<const uint16_t *>(v)[i];
+    } else {
+        reinterpret_cast<float *>(kpool)[off] = reinterpret_cast<const float *>(k)[i];
+        reinterpret_cast<float *>(vpool)[off] = reinterpret_cast<const float *>(v)[i];
+    }
+}
+
+}  // namespace pn
