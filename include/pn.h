@@ -197,8 +197,10 @@ enum {
 };
 
 /* Options (tuning only; results change at most by fp32 rounding):
- *  PN_OPT_ATTN_KEYS_PER_SPLIT  0 = automatic, else a multiple of 256 keys
- *                              handled by one attention work-group;
+ *  PN_OPT_ATTN_KEYS_PER_SPLIT  0 = automatic, else a multiple of 64 keys
+ *                              handled by one attention work-group (raised
+ *                              where a state's split scratch, at most 256
+ *                              splits, needs it);
  *  PN_OPT_WAVES_*              waves per work-group (4, 8 or 16) of the QKV,
  *                              O, gate/up, down and LM-head projections. */
 enum {

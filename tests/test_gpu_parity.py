@@ -93,3 +93,18 @@ def test_moe_single_fp32():
     p = Pair(wl)
     worst, near, n = run_single(p, 100, [7, 8], 6)
     log("  moe f32: worst rel L2 %.2e near %d" % (worst, near))
+
+
+@pytest.mark.parametrize("kps", [64, 192, 320, 1024])
+def test_attention_split_sizes(kps):
+    """Keys per attention split (one chunk, several chunks, the whole 1001-key
+    window in one split) change the result only by fp32 rounding: every split
+    size matches the oracle, with fp32 (at 1e-4) and bf16 caches."""
+    from token_decode_amd import _capi as C
+    for kv in (synth.F32, synth.BF16):
+        wl = ragged("split-%d-kv%d" % (kps, kv), w_dtype=synth.F32, kv_dtype=kv,
+                    act_dtype=synth.F32, seed=46)
+        p = Pair(wl)
+        p.dm.set_option(C.PN_OPT_ATTN_KEYS_PER_SPLIT, kps)
+        worst, near, n = run_single(p, 999, [11, 12], 2)
+        log("  kps %d kv %d: worst rel L2 %.2e near %d" % (kps, kv, worst, near))

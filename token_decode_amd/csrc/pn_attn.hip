@@ -1,4 +1,4 @@
-// pn_attn.hip - split-K flash-decode attention and its split combine for one
+// pn_attn.hip - split-K flash-decode attention and its split merge for one
 // (head_dim, KV type) pair.  Compiled once per pair with -DPN_D=<32|64|128>
 // -DPN_KV=<0|1> -DPN_NAME=<entry>.
 #include "pn_launch.hpp"
@@ -7,21 +7,21 @@ namespace pn {
 namespace {
 
 template <int G>
-void go(const AttnArgs &a, dim3 grid, bool combine, hipStream_t s) {
+void go(const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
     hipLaunchKernelGGL((k_attn<PN_D, PN_KV, G>), grid, dim3(256), 0, s, a);
-    if (combine) hipLaunchKernelGGL((k_attn_combine<PN_D, G>), dim3(grid.y, grid.z), dim3(256), 0, s, a);
+    if (merge) hipLaunchKernelGGL((k_attn_merge<PN_D, G>), dim3(a.Hq, grid.z), dim3(256), 0, s, a);
 }
 
 }  // namespace
 
-void PN_NAME(int G, const AttnArgs &a, dim3 grid, bool combine, hipStream_t s) {
+void PN_NAME(int G, const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
     switch (G) {
-        case 1: go<1>(a, grid, combine, s); break;
-        case 2: go<2>(a, grid, combine, s); break;
-        case 3: go<3>(a, grid, combine, s); break;
-        case 4: go<4>(a, grid, combine, s); break;
-        case 6: go<6>(a, grid, combine, s); break;
-        default: go<8>(a, grid, combine, s); break;
+        case 1: go<1>(a, grid, merge, s); break;
+        case 2: go<2>(a, grid, merge, s); break;
+        case 3: go<3>(a, grid, merge, s); break;
+        case 4: go<4>(a, grid, merge, s); break;
+        case 6: go<6>(a, grid, merge, s); break;
+        default: go<8>(a, grid, merge, s); break;
     }
 }
 

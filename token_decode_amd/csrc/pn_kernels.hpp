@@ -29,8 +29,6 @@ constexpr int kPage = 64;      // tokens per KV page
 constexpr int kMaxRows = 16;   // A rows of one MFMA tile
 constexpr int kMaxSlots = 16;  // sequences in one batched step
 constexpr int kNW = 16;        // waves per GEMM work-group
-constexpr int kU = 8;          // tiles per wave per load round
-constexpr int kAttnWaves = 4;  // waves per attention work-group
 constexpr int kMaxG = 8;       // query heads per KV head
 
 enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2 };
@@ -41,6 +39,7 @@ enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_MOE_S
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -807,197 +806,209 @@ struct AttnArgs {
     float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max, sum, 2 pad, unnormalised output
 };
 
-// Split-K flash decode for G query heads per KV head.
-// grid: x = split, y = kv head, z = slot; 256 threads.
-// Each split covers kps keys of the slot's window; each wave takes 64-key
-// chunks with an online softmax.  For q.k a lane owns one key and reads its
-// whole K row; for p.v a lane owns D/64 (at least one) consecutive dimensions
-// and reads one value row per key.  All K and V loads of a chunk are issued
-// before any arithmetic, so a wave keeps a whole chunk in flight.  The waves
-// merge in a fixed order; a single-split slot writes the output directly,
-// otherwise the split's (max, sum, output) goes to the state's scratch for
-// k_attn_combine.
-template <int D, int KV, int G>
-__global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
-    constexpr int VE = D >= 64 ? D / 64 : 1;   // value elements per lane
-    constexpr int VL = D / VE;                 // lanes holding values
-    constexpr int ES = KV == 1 ? 2 : 4;
-    constexpr int KVEC = 16 / ES;              // K elements per 16-byte load
-    constexpr int NKL = D / KVEC;              // 16-byte loads per K row
-    constexpr int VCH = (VE * ES > 4) ? 32 : 64;  // keys whose V is held at once
+// Split-K flash decode for G query heads per KV head.  Decode attention
+// moves few bytes per work-group, and one compute unit only pulls a small
+// share of HBM bandwidth, so the window is cut into many short splits (a
+// multiple of 64 keys each) spread over the whole chip; k_attn_merge then
+// folds the splits together.
+//
+// grid: x = split, y = kv head, z = slot; 256 threads (4 waves).  A split is
+// walked in chunks of 64 keys, 16 per wave.  For q.k four lanes share a key,
+// each taking the 16-byte pieces dq, dq+4, dq+8, ... of its row (so every load
+// instruction of the four lanes covers 64 contiguous bytes) and two DPP steps
+// finish the dot product; for p.v a lane owns D/64 (at least one) consecutive
+// dimensions and reads one value row per key.  All K and V loads of a chunk
+// are issued before any arithmetic; in multi-chunk splits the next chunk is in
+// flight while the current one is scored.  Each wave keeps a running (max,
+// sum, output); the waves merge in a fixed order.  A single-split slot writes
+// the output; otherwise the split's (max, sum, unnormalised output) goes to
+// the state's split scratch.
+constexpr int kAttnWaves = 4;
+constexpr int kAttnChunk = kAttnWaves * 16;  // keys per chunk, and the split granularity
+constexpr int kMaxSplits = 256;              // splits per (slot, kv head)
+
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp_f<kDppXor1, 0xF>(0.f, v);
+    v += dpp_f<kDppXor2, 0xF>(0.f, v);
+    return v;
+}
+
+template <int D, int KV>
+struct AttnShape {
+    static constexpr int ES = KV == 1 ? 2 : 4;       // bytes per cached element
+    static constexpr int VE = D >= 64 ? D / 64 : 1;  // value elements per lane
+    static constexpr int VL = D / VE;                // lanes holding values
+    static constexpr int NKL = D * ES / 64;          // 16-byte K loads per lane
+    static constexpr int KVEC = 16 / ES;             // K elements per load
     typedef typename std::conditional<VE * ES == 2, uint16_t,
             typename std::conditional<VE * ES == 4, uint32_t, unsigned long long>::type>::type vword;
+    // double-buffer a chunk's rows when both copies fit the register budget
+    static constexpr bool PREF = (NKL * 4 + 16 * (int)sizeof(vword) / 4) <= 40;
+};
+
+// Issue the K and V loads of one wave's 16 keys starting at k0 (positions
+// clamped to kl, the split's last key, so every load is in bounds).
+template <int D, int KV>
+__device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int k0, int kl, int kq, int dq,
+                                          int lane, u32x4 (&kr)[AttnShape<D, KV>::NKL],
+                                          typename AttnShape<D, KV>::vword (&vr)[16]) {
+    typedef AttnShape<D, KV> S;
+    const int *pt = a.pt[b];
+    const int tq = min(k0 + kq, kl);
+    const int offq = ((pt[tq / kPage] * a.Hk + j) * kPage + (tq % kPage)) * D + dq * S::KVEC;
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.kvk[b] + (long long)offq * S::ES);
+#pragma unroll
+    for (int c = 0; c < S::NKL; ++c) kr[c] = kp[4 * c];
+    const typename S::vword *vb =
+        reinterpret_cast<const typename S::vword *>(a.kvv[b]) + (lane < S::VL ? lane : 0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int t = min(k0 + u, kl);
+        vr[u] = vb[((pt[t / kPage] * a.Hk + j) * kPage + (t % kPage)) * (D / S::VE)];
+    }
+}
+
+// Score one wave's 16 keys (nv of them valid) and fold them into the running
+// (m, l, acc) of its G query heads.
+template <int D, int KV, int G>
+__device__ __forceinline__ void attn_chunk(const float (*qs)[D], const u32x4 (&kr)[AttnShape<D, KV>::NKL],
+                                           const typename AttnShape<D, KV>::vword (&vr)[16], int nv, int kq,
+                                           int dq, float (&m)[G], float (&l)[G],
+                                           float (&acc)[G][AttnShape<D, KV>::VE]) {
+    typedef AttnShape<D, KV> S;
+    float sc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sc[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < S::NKL; ++c) {
+        float kf[S::KVEC];
+        if constexpr (KV == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kf[2 * e] = __uint_as_float(kr[c][e] << 16);
+                kf[2 * e + 1] = __uint_as_float(kr[c][e] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kf[e] = __uint_as_float(kr[c][e]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < S::KVEC; ++e) sc[g] = fmaf(qs[g][(4 * c + dq) * S::KVEC + e], kf[e], sc[g]);
+    }
+    const bool valid = kq < nv;
+    float p[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        sc[g] = quad_sum(sc[g]);
+        const float mx = fmaxf(m[g], wave_max(valid ? sc[g] : -INFINITY));
+        const float f = expf(m[g] - mx);  // 0 on the wave's first chunk
+        p[g] = valid ? expf(sc[g] - mx) : 0.f;
+        l[g] = l[g] * f + wave_sum(dq == 0 ? p[g] : 0.f);
+#pragma unroll
+        for (int e = 0; e < S::VE; ++e) acc[g][e] *= f;
+        m[g] = mx;
+    }
+    // p.v: key u's weight sits in lane 4u
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        float v[S::VE];
+        if constexpr (KV == 1) {
+            v[0] = __uint_as_float((uint32_t)vr[u] << 16);
+            if constexpr (S::VE == 2) v[1] = __uint_as_float((uint32_t)vr[u] & 0xFFFF0000u);
+        } else {
+            v[0] = __uint_as_float((uint32_t)((unsigned long long)vr[u] & 0xFFFFFFFFull));
+            if constexpr (S::VE == 2) v[1] = __uint_as_float((uint32_t)((unsigned long long)vr[u] >> 32));
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float pg = readlane_f(p[g], 4 * u);
+#pragma unroll
+            for (int e = 0; e < S::VE; ++e) acc[g][e] = fmaf(pg, v[e], acc[g][e]);
+        }
+    }
+}
+
+template <int D, int KV, int G>
+__global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
+    typedef AttnShape<D, KV> S;
+    constexpr int NWV = kAttnWaves;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     if (s >= a.nsplit[b]) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int pos = a.pos[b];
     const int kb = a.t0[b] + s * a.kps;
-    const int ke = min(kb + a.kps, pos + 1);
+    const int ke = min(kb + a.kps, a.pos[b] + 1);
 
     __shared__ __align__(16) float qs[G][D];
-    __shared__ float wm[kAttnWaves][G], wl[kAttnWaves][G];
-    __shared__ float wacc[kAttnWaves][G][D];
+    __shared__ float wm[NWV][G], wl[NWV][G];
+    __shared__ float wacc[NWV][G][D];
 
-    const char *Kb = a.kvk[b];
-    const char *Vb = a.kvv[b];
-    const int *pt = a.pt[b];
-    const bool vlane = lane < VL;
-    // page of this lane's key in the wave's first chunk, fetched before the q barrier
-    int page_next = pt[min(kb + w * 64 + lane, ke - 1) / kPage];
+    const int kq = lane >> 2, dq = lane & 3;
+    u32x4 kc[S::NKL], kn[S::NKL];
+    typename S::vword vc[16], vn[16];
+    attn_load<D, KV>(a, b, j, kb + w * 16, ke - 1, kq, dq, lane, kc, vc);
     {
-        // q of the group's G heads: G*D/4 <= 256 float4s, one load per thread
         const f32x4 *q4 = reinterpret_cast<const f32x4 *>(a.q + (long long)b * a.Hq * D + (long long)(j * G) * D);
-        if (tid < G * D / 4) {
-            const f32x4 v = q4[tid];
-            const int g = (tid * 4) / D, d = (tid * 4) % D;
+        for (int i = tid; i < G * D / 4; i += 256) {
+            const f32x4 v = q4[i];
+            const int g = (i * 4) / D, d = (i * 4) % D;
 #pragma unroll
             for (int e = 0; e < 4; ++e) qs[g][d + e] = v[e] * a.scale;
         }
     }
     __syncthreads();
 
-    float m[G], l[G], acc[G][VE];
+    float m[G], l[G], acc[G][S::VE];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = -INFINITY;
         l[g] = 0.f;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[g][e] = 0.f;
+        for (int e = 0; e < S::VE; ++e) acc[g][e] = 0.f;
     }
-
-    for (int cs = kb + w * 64; cs < ke; cs += kAttnWaves * 64) {
-        const int t = cs + lane;
-        const bool valid = t < ke;
-        const int tt = valid ? t : ke - 1;  // invalid lanes read a valid key and get weight 0
-        const int off = ((page_next * a.Hk + j) * kPage + (tt % kPage)) * D;  // element offset
-        if (cs + kAttnWaves * 64 < ke) page_next = pt[min(cs + kAttnWaves * 64 + lane, ke - 1) / kPage];
-        // issue the chunk's loads: this lane's K row, then the first V rows
-        u32x4 kreg[NKL];
-        const u32x4 *kp = reinterpret_cast<const u32x4 *>(Kb + (long long)off * ES);
-#pragma unroll
-        for (int c = 0; c < NKL; ++c) kreg[c] = kp[c];
-        vword vreg[VCH];
-        const vword *vbase = reinterpret_cast<const vword *>(Vb) + (vlane ? lane : 0);
-#pragma unroll
-        for (int u = 0; u < VCH; ++u)
-            vreg[u] = vbase[__builtin_amdgcn_readlane(off, u) / VE];
-        // q.k for this lane's key; the q values of step c+1 are read from LDS
-        // while step c is multiplied (the barrier keeps the compiler from
-        // hoisting every read)
-        float sc[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) sc[g] = 0.f;
-        float qn[G][KVEC];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < KVEC; ++e) qn[g][e] = qs[g][e];
-#pragma unroll
-        for (int c = 0; c < NKL; ++c) {
-            float qc[G][KVEC];
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < KVEC; ++e) qc[g][e] = qn[g][e];
-            if (c + 1 < NKL) {
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int e = 0; e < KVEC; ++e) qn[g][e] = qs[g][(c + 1) * KVEC + e];
+    if (ke - kb <= kAttnChunk) {
+        const int k0 = kb + w * 16;
+        if (k0 < ke) attn_chunk<D, KV, G>(qs, kc, vc, ke - k0, kq, dq, m, l, acc);
+    } else {
+        for (int c0 = kb; c0 < ke; c0 += kAttnChunk) {
+            const int k0 = c0 + w * 16;
+            if constexpr (S::PREF) {
+                // next chunk in flight (clamped into the split past its end)
+                attn_load<D, KV>(a, b, j, k0 + kAttnChunk, ke - 1, kq, dq, lane, kn, vn);
+            } else if (c0 != kb) {
+                attn_load<D, KV>(a, b, j, k0, ke - 1, kq, dq, lane, kc, vc);
             }
-            float kf[KVEC];
-            if constexpr (KV == 1) {
+            if (k0 < ke) attn_chunk<D, KV, G>(qs, kc, vc, ke - k0, kq, dq, m, l, acc);
+            if constexpr (S::PREF) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kf[2 * e] = __uint_as_float(kreg[c][e] << 16);
-                    kf[2 * e + 1] = __uint_as_float(kreg[c][e] & 0xFFFF0000u);
-                }
-            } else {
+                for (int c = 0; c < S::NKL; ++c) kc[c] = kn[c];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kf[e] = __uint_as_float(kreg[c][e]);
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < KVEC; ++e) sc[g] = fmaf(qc[g][e], kf[e], sc[g]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // online softmax update
-        float p[G], mx[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) mx[g] = wave_max(valid ? sc[g] : -INFINITY);
-        float ps[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mn = fmaxf(m[g], mx[g]);
-            const float alpha = expf(m[g] - mn);
-            p[g] = valid ? expf(sc[g] - mn) : 0.f;
-            l[g] *= alpha;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
-            m[g] = mn;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) ps[g] = wave_sum(p[g]);
-#pragma unroll
-        for (int g = 0; g < G; ++g) l[g] += ps[g];
-        // p.v
-#pragma unroll
-        for (int vb = 0; vb < 64; vb += VCH) {
-            if (vb > 0) {
-#pragma unroll
-                for (int u = 0; u < VCH; ++u)
-                    vreg[u] = vbase[__builtin_amdgcn_readlane(off, vb + u) / VE];
-            }
-#pragma unroll
-            for (int u = 0; u < VCH; ++u) {
-                float v[VE];
-                if constexpr (KV == 1) {
-                    if constexpr (VE == 2) {
-                        v[0] = __uint_as_float((uint32_t)vreg[u] << 16);
-                        v[1] = __uint_as_float((uint32_t)vreg[u] & 0xFFFF0000u);
-                    } else {
-                        v[0] = __uint_as_float((uint32_t)vreg[u] << 16);
-                    }
-                } else {
-                    if constexpr (VE == 2) {
-                        v[0] = __uint_as_float((uint32_t)(vreg[u] & 0xFFFFFFFFull));
-                        v[1] = __uint_as_float((uint32_t)(vreg[u] >> 32));
-                    } else {
-                        v[0] = __uint_as_float((uint32_t)vreg[u]);
-                    }
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float pg = readlane_f(p[g], vb + u);
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pg, v[e], acc[g][e]);
-                }
+                for (int u = 0; u < 16; ++u) vc[u] = vn[u];
             }
         }
     }
 
-    // merge the waves
+    // merge the waves in wave order (a wave with no keys has m = -inf, l = 0)
     if (lane == 0)
 #pragma unroll
         for (int g = 0; g < G; ++g) { wm[w][g] = m[g]; wl[w][g] = l[g]; }
-    if (vlane)
+    if (lane < S::VL)
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int e = 0; e < VE; ++e) wacc[w][g][lane * VE + e] = acc[g][e];
+            for (int e = 0; e < S::VE; ++e) wacc[w][g][lane * S::VE + e] = acc[g][e];
     __syncthreads();
 
     const int ns = a.nsplit[b];
-    float *part = a.part[b];
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, d = idx % D;
         float M = wm[0][g];
 #pragma unroll
-        for (int x = 1; x < kAttnWaves; ++x) M = fmaxf(M, wm[x][g]);
+        for (int x = 1; x < NWV; ++x) M = fmaxf(M, wm[x][g]);
         float L = 0.f, A = 0.f;
 #pragma unroll
-        for (int x = 0; x < kAttnWaves; ++x) {
+        for (int x = 0; x < NWV; ++x) {
             const float f = expf(wm[x][g] - M);
             L += wl[x][g] * f;
             A += wacc[x][g][d] * f;
@@ -1005,77 +1016,88 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
         if (ns == 1) {
             a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A / L;
         } else {
-            float *pp = part + (((long long)j * a.s_cap[b] + s) * G + g) * (D + 4);
+            float *pp = a.part[b] + (((long long)j * a.s_cap[b] + s) * G + g) * (D + 4);
             if (d == 0) { pp[0] = M; pp[1] = L; }
             pp[4 + d] = A;
         }
     }
 }
 
-// Merge the splits of every (slot, kv head) whose window took more than one
-// split, in split order.  grid: x = kv head, y = slot; 256 threads.  Splits
-// are staged through LDS kSplitChunk at a time (one independent 16-byte load
-// per thread step) and folded into a running (max, sum, output).
-constexpr int kSplitChunk = 8;
-
+// Fold the splits of one (slot, query head) together.  grid: x = query head,
+// y = slot; 256 threads.  Every split's weight exp(M_s - M) / L is computed
+// once (thread s) and kept in LDS; wave w then sums the unnormalised outputs
+// of splits w, w+4, w+8, ... (loads batched 16 deep), and the four partial
+// sums are added in wave order.  Slots with one split were finished by k_attn.
 template <int D, int G>
-__global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
-    const int j = blockIdx.x, b = blockIdx.y;
+__global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
+    constexpr int VE = D >= 64 ? D / 64 : 1;
+    constexpr int VL = D / VE;
+    constexpr int NWV = 4;
+    constexpr int BATCH = 16;
+    const int h = blockIdx.x, b = blockIdx.y;
     const int ns = a.nsplit[b];
     if (ns <= 1) return;
-    constexpr int per = G * (D + 4);  // floats of one split, a multiple of 4
-    const f32x4 *part = reinterpret_cast<const f32x4 *>(a.part[b] + (long long)j * a.s_cap[b] * per);
-    __shared__ __align__(16) float sp[kSplitChunk * per];
-    constexpr int OPT = (G * D + 255) / 256;  // outputs per thread
-    constexpr int LPT = (kSplitChunk * per / 4 + 255) / 256;  // float4 loads per thread
-    float M[OPT], L[OPT], A[OPT];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int j = h / G, g = h % G;
+    const long long stride = (long long)G * (D + 4);  // floats between consecutive splits
+    const float *base = a.part[b] + ((long long)j * a.s_cap[b] * G + g) * (D + 4);
+
+    __shared__ float fs[kMaxSplits];
+    __shared__ float red[NWV][2];
+    __shared__ float pacc[NWV][D];
+
+    // split weights: thread s holds split s (ns <= kMaxSplits = blockDim)
+    float Ms = -INFINITY, Ls = 0.f;
+    if (tid < ns) {
+        const f32x2 ml = *reinterpret_cast<const f32x2 *>(base + tid * stride);
+        Ms = ml[0];
+        Ls = ml[1];
+    }
+    float mx = wave_max(Ms);
+    if (lane == 0) red[w][0] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+    const float f = tid < ns ? expf(Ms - mx) : 0.f;
+    const float ls = wave_sum(f * Ls);
+    if (lane == 0) red[w][1] = ls;
+    __syncthreads();
+    const float L = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
+    if (tid < ns) fs[tid] = f / L;
+    __syncthreads();
+
+    float acc[VE];
 #pragma unroll
-    for (int u = 0; u < OPT; ++u) { M[u] = -INFINITY; L[u] = 0.f; A[u] = 0.f; }
-    for (int s0 = 0; s0 < ns; s0 += kSplitChunk) {
-        const int nc = min(kSplitChunk, ns - s0);
-        const int n4 = nc * per / 4;
-        f32x4 v[LPT];
+    for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+    const int dl = (lane < VL ? lane : 0) * VE;
+    for (int s0 = w; s0 < ns; s0 += NWV * BATCH) {
+        float v[BATCH][VE];
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int i = threadIdx.x + u * 256;
-            if (i < n4) v[u] = part[(long long)s0 * per / 4 + i];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int i = threadIdx.x + u * 256;
-            if (i < n4) reinterpret_cast<f32x4 *>(sp)[i] = v[u];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < OPT; ++u) {
-            const int idx = threadIdx.x + u * 256;
-            if (idx < G * D) {
-                const int g = idx / D, d = idx % D;
-                float mm = M[u];
-                for (int x = 0; x < nc; ++x) mm = fmaxf(mm, sp[x * per + g * (D + 4)]);
-                const float f0 = expf(M[u] - mm);
-                float ll = L[u] * f0, aa = A[u] * f0;
-                for (int x = 0; x < nc; ++x) {
-                    const float *px = sp + x * per + g * (D + 4);
-                    const float f = expf(px[0] - mm);
-                    ll += px[1] * f;
-                    aa += px[4 + d] * f;
-                }
-                M[u] = mm;
-                L[u] = ll;
-                A[u] = aa;
+        for (int u = 0; u < BATCH; ++u) {
+            const int sx = min(s0 + u * NWV, ns - 1);
+            const float *px = base + sx * stride + 4 + dl;
+            if constexpr (VE == 2) {
+                const f32x2 t = *reinterpret_cast<const f32x2 *>(px);
+                v[u][0] = t[0];
+                v[u][1] = t[1];
+            } else {
+                v[u][0] = *px;
             }
         }
-    }
 #pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-        const int idx = threadIdx.x + u * 256;
-        if (idx < G * D) {
-            const int g = idx / D, d = idx % D;
-            a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A[u] / L[u];
+        for (int u = 0; u < BATCH; ++u) {
+            const int sx = s0 + u * NWV;
+            const float fw = sx < ns ? fs[sx] : 0.f;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] = fmaf(fw, v[u][e], acc[e]);
         }
     }
+    if (lane < VL)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) pacc[w][dl + e] = acc[e];
+    __syncthreads();
+    if (tid < D)
+        a.o[(long long)b * a.Hq * D + (long long)h * D + tid] =
+            (pacc[0][tid] + pacc[1][tid]) + (pacc[2][tid] + pacc[3][tid]);
 }
 
 }  // namespace pn

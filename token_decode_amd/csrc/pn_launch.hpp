@@ -37,7 +37,8 @@ void launch_gemm_i8_bf16(int kind, int nw, bool alds, const GemmArgs &g, dim3 gr
 
 // Defined once per (head_dim, KV type) in pn_attn.hip: attention with G query
 // heads per KV head, and the split combine when `combine`.
-#define PN_ATTN_DECL(name) void name(int G, const AttnArgs &a, dim3 grid, bool combine, hipStream_t s);
+#define PN_ATTN_DECL(name) \
+    void name(int G, const AttnArgs &a, dim3 grid, bool merge, hipStream_t s);
 PN_ATTN_DECL(launch_attn_32_0)
 PN_ATTN_DECL(launch_attn_32_1)
 PN_ATTN_DECL(launch_attn_64_0)
@@ -46,15 +47,15 @@ PN_ATTN_DECL(launch_attn_128_0)
 PN_ATTN_DECL(launch_attn_128_1)
 #undef PN_ATTN_DECL
 
-inline void launch_attn(int D, int kvt, int G, const AttnArgs &a, dim3 grid, bool combine, hipStream_t s) {
+inline void launch_attn(int D, int kvt, int G, const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
     if (kvt == 1) {
-        if (D == 32) launch_attn_32_1(G, a, grid, combine, s);
-        else if (D == 64) launch_attn_64_1(G, a, grid, combine, s);
-        else launch_attn_128_1(G, a, grid, combine, s);
+        if (D == 32) launch_attn_32_1(G, a, grid, merge, s);
+        else if (D == 64) launch_attn_64_1(G, a, grid, merge, s);
+        else launch_attn_128_1(G, a, grid, merge, s);
     } else {
-        if (D == 32) launch_attn_32_0(G, a, grid, combine, s);
-        else if (D == 64) launch_attn_64_0(G, a, grid, combine, s);
-        else launch_attn_128_0(G, a, grid, combine, s);
+        if (D == 32) launch_attn_32_0(G, a, grid, merge, s);
+        else if (D == 64) launch_attn_64_0(G, a, grid, merge, s);
+        else launch_attn_128_0(G, a, grid, merge, s);
     }
 }
 

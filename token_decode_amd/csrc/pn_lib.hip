@@ -287,7 +287,8 @@ size_t layout_model(pn_model *m) {
     return bp.off;
 }
 
-int attn_kps_min() { return kAttnWaves * 64; }
+// Automatic split size: aim for about this many attention work-groups per step.
+constexpr int kAttnTargetGroups = 512;
 
 size_t layout_state(pn_state *s) {
     const pn_model *m = s->m;
@@ -296,7 +297,7 @@ size_t layout_state(pn_state *s) {
     s->layer_bytes = (size_t)s->n_pages * m->Hk * kPage * m->D * es;
     int keys = s->max_ctx;
     if (m->cfg.sliding_window > 0) keys = std::min(keys, m->cfg.sliding_window);
-    s->s_cap = cdiv(keys, attn_kps_min());
+    s->s_cap = std::min(cdiv(keys, kAttnChunk), kMaxSplits);
     Bump bp;
     s->kpool = bp.take(s->layer_bytes * m->cfg.n_layer);
     s->vpool = bp.take(s->layer_bytes * m->cfg.n_layer);
@@ -428,8 +429,26 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     aa.Hq = m->H;
     aa.Hk = m->Hk;
     aa.scale = (float)(1.0 / std::sqrt((double)m->D));
+    // keys per split: a multiple of kAttnChunk, small enough to spread the window
+    // over about kAttnTargetGroups work-groups, large enough that every slot's
+    // splits fit its scratch
+    int span_max = 1;
+    for (int b = 0; b < n; ++b) {
+        const int pos = st[b]->pos;
+        const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
+        span_max = std::max(span_max, pos - t0 + 1);
+    }
+    int kps = m->attn_kps;
+    if (kps <= 0) {
+        const int want = std::max(1, kAttnTargetGroups / (m->Hk * n));
+        kps = kAttnChunk * cdiv(span_max, kAttnChunk * want);
+    }
     int nsplit_max = 1;
-    const int kps = m->attn_kps > 0 ? m->attn_kps : attn_kps_min();
+    for (int b = 0; b < n; ++b) {
+        const int pos = st[b]->pos;
+        const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
+        kps = std::max(kps, kAttnChunk * cdiv(pos - t0 + 1, kAttnChunk * st[b]->s_cap));
+    }
     for (int b = 0; b < n; ++b) {
         const int pos = st[b]->pos;
         const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
@@ -437,7 +456,8 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         aa.t0[b] = t0;
         aa.nsplit[b] = cdiv(pos - t0 + 1, kps);
         aa.s_cap[b] = st[b]->s_cap;
-        if (aa.nsplit[b] > st[b]->s_cap) return fail(PN_ERANGE, "attention splits exceed state scratch");
+        if (aa.nsplit[b] > st[b]->s_cap || aa.nsplit[b] > kMaxSplits)
+            return fail(PN_ERANGE, "attention splits exceed state scratch");
         nsplit_max = std::max(nsplit_max, aa.nsplit[b]);
         aa.pt[b] = (const int *)(st[b]->base + st[b]->pt);
         aa.part[b] = (float *)(st[b]->base + st[b]->part);
@@ -962,8 +982,8 @@ int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
         return PN_OK;
     }
     if (option == PN_OPT_ATTN_KEYS_PER_SPLIT) {
-        if (value < 0 || value % attn_kps_min() != 0 || value > (1 << 24))
-            return fail(PN_EINVAL, "keys per split must be 0 or a multiple of %d", attn_kps_min());
+        if (value < 0 || value % kAttnChunk != 0 || value > (1 << 24))
+            return fail(PN_EINVAL, "keys per split must be 0 or a multiple of %d", kAttnChunk);
         m->attn_kps = (int)value;
         return PN_OK;
     }
