@@ -1,11 +1,20 @@
 """Decode throughput of the HIP path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
 
-A step is one whole decode step (every layer, LM head and greedy argmax) for
-every sequence of the workload, with the previous step's argmax fed back on
-the device.  Inputs are seeded synthetic weights and K/V of the workload's
-shape, resident in HBM before the timed region starts.  Prints one JSON line.
+A step is one whole decode step (embedding, every layer, LM head and greedy
+argmax) for every sequence of the workload, with the previous step's argmax
+fed back on the device.  Inputs are seeded synthetic weights and K/V of the
+workload's shape, resident in HBM before the timed region starts.  Prints one
+JSON line with the throughput, the roofline of the dominant kernel (gate/up:
+algorithmic bytes over its average launch time, from HIP events around
+replays of the timed steps' launches; HBM traffic from the committed counter
+summary while the GEMM sources are unchanged) and the fp64 CPU oracle timed
+on a bounded sample of the same workload.
+
+--calibrate-copy runs only a 1 GiB device copy, the reference for scaling the
+HBM byte counters; --print-source-hash prints the hash the counter summary is
+tied to.
 """
 from __future__ import annotations
 
@@ -67,13 +76,24 @@ def main():
     ap.add_argument("--workload", default="llama3-8b-bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough budget of the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (the scale of the HBM byte counters)")
+    ap.add_argument("--print-source-hash", action="store_true",
+                    help="print the hash of the GEMM sources the counter summary is tied to")
     args = ap.parse_args()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import synth
     from token_decode_amd import _capi as C
@@ -98,8 +118,7 @@ def main():
 
     B = wl.slots
     starts = [int(p) for p in wl.start_positions()]
-    kinds_n = 6  # per-kernel timing passes below
-    total_steps = args.warmup + (1 + kinds_n) * args.steps
+    total_steps = args.warmup + args.steps
     states = []
     t0 = time.time()
     for b in range(B):
@@ -142,18 +161,21 @@ def main():
     log("step %.3f ms, %.1f tok/s, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms_step, tok_s, gbs,
                                                                    100 * gbs / HBM_PEAK_GBS))
 
-    # per-kernel-class timing over the same number of steps (HIP events around each
-    # launch of the class, on the launch stream), in a second pass
+    # per-kernel-class timing: HIP events on the launch stream around back-to-back
+    # replays of the class's launches in the last timed step (every layer's, in
+    # order, with the step's arguments)
     kinds = {"qkv": C.PN_K_QKV, "attn": C.PN_K_ATTN, "o": C.PN_K_O, "gateup": C.PN_K_GATEUP,
              "down": C.PN_K_DOWN, "lmhead": C.PN_K_LMHEAD}
     per_kernel = {}
     for name, k in kinds.items():
-        model.profile_begin(k)
-        for _ in range(args.steps):
-            step()
-        tot, n = model.profile_end(stream)
-        per_kernel[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n,
-                            "ms_per_step": tot / args.steps}
+        reps = 64 if name == "lmhead" else 8 * wl.n_layer
+        model.profile_replay(k, 2, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        model.profile_replay(k, reps, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_kernel[name] = {"avg_us": round(1e3 * e0.elapsed_time(e1) / reps, 3), "replays": reps}
     dom = "gateup"
     dom_bytes = gemm_bytes(wl, dom)
     dom_us = per_kernel[dom]["avg_us"]
@@ -162,6 +184,7 @@ def main():
         bb = gemm_bytes(wl, name)
         per_kernel[name]["GBps"] = round(bb / (per_kernel[name]["avg_us"] * 1e-6) / 1e9, 1)
     log("per kernel: " + json.dumps(per_kernel))
+    traffic = measured_traffic(wl.name)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -189,12 +212,54 @@ def main():
                 "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"kernel": "gate/up GEMM + SwiGLU", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)},
         "kernels": per_kernel,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+GEMM_SOURCES = ("token_decode_amd/csrc/pn_kernels.hpp", "token_decode_amd/csrc/pn_gemm.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "gateup_llama3-8b-bf16_counters.md")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary (FETCH_SIZE
+    + WRITE_SIZE, each scaled by the same counter on a copy of known size), or
+    None when the summary is missing, is for another workload, or was taken on
+    GEMM sources that have changed since."""
+    try:
+        with open(COUNTERS) as fh:
+            kv = dict(l.strip("- \n").split(": ", 1) for l in fh if l.startswith("- ") and ": " in l)
+    except OSError:
+        return None
+    if kv.get("workload") != workload or kv.get("kernel sources sha256/16") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["traffic bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(wl, W, starts, budget_s):

@@ -216,6 +216,18 @@ int pn_model_set_option(pn_model *m, int32_t option, int64_t value);
 int pn_profile_begin(pn_model *m, int32_t kernel);
 int pn_profile_end(pn_model *m, void *stream, double *total_ms, int64_t *launches);
 
+/* Enqueue `reps` launches of kernel class `kernel` (QKV, ATTN, O, GATEUP,
+ * DOWN or LMHEAD; ATTN includes the split merge) back to back, cycling
+ * through that class's launches of the most recent step (one per layer)
+ * with their arguments, so that a caller can time the class with events
+ * around the whole batch under the weight streams of a real step.  A QKV replay appends its
+ * k, v rows to a model-owned scratch page rather than to any state; the
+ * other classes rewrite only model scratch (activations, which the next
+ * step rebuilds) and, for LMHEAD, the logits buffer of the recorded step.
+ * PN_EINVAL when the class has no recorded launch (none since the model was
+ * created, or a state of the recorded step was freed since). */
+int pn_profile_replay(pn_model *m, int32_t kernel, int32_t reps, void *stream);
+
 /* Message of the last failure on this thread ("" if none). */
 const char *pn_last_error(void);
 

@@ -80,6 +80,7 @@ def lib():
             "pn_model_set_option": (ctypes.c_int, [vp, i32, ctypes.c_int64]),
             "pn_profile_begin": (ctypes.c_int, [vp, i32]),
             "pn_profile_end": (ctypes.c_int, [vp, vp, P(ctypes.c_double), P(ctypes.c_int64)]),
+            "pn_profile_replay": (ctypes.c_int, [vp, i32, i32, vp]),
             "pn_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -96,7 +97,7 @@ EXPORTS = ["pn_config_default", "pn_config_check", "pn_model_bytes", "pn_model_c
            "pn_state_set_page_table", "pn_state_pages", "pn_page_size", "pn_state_set_pos",
            "pn_state_pos", "pn_state_max_ctx", "pn_state_check", "pn_state_free",
            "pn_forward_step", "pn_forward_batch", "pn_model_set_option", "pn_profile_begin",
-           "pn_profile_end", "pn_last_error"]
+           "pn_profile_end", "pn_profile_replay", "pn_last_error"]
 
 
 def check(rc):

@@ -799,39 +799,55 @@ struct AttnArgs {
     const float *q;   // [slot][Hq*D]
     float *o;         // attention output [slot][Hq*D] (fp32; the O projection rounds it)
     int Hq, Hk, kps;
-    float scale;
-    int pos[kMaxSlots], t0[kMaxSlots], nsplit[kMaxSlots], s_cap[kMaxSlots];
+    float scale;      // 1/sqrt(D) * log2(e): scores are kept in the base-2 domain
+    int pos[kMaxSlots];     // the slot's current position (its last key)
+    int lo[kMaxSlots];      // first key inside the window
+    int origin[kMaxSlots];  // lo rounded down to a page: split s starts at origin + s*kps
+    int nsplit[kMaxSlots], s_cap[kMaxSlots];
     const char *kvk[kMaxSlots], *kvv[kMaxSlots];
     const int *pt[kMaxSlots];
-    float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max, sum, 2 pad, unnormalised output
+    float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max (base 2), sum, 2 pad, unnormalised output
 };
 
 // Split-K flash decode for G query heads per KV head.  Decode attention
 // moves few bytes per work-group, and one compute unit only pulls a small
 // share of HBM bandwidth, so the window is cut into many short splits (a
-// multiple of 64 keys each) spread over the whole chip; k_attn_merge then
-// folds the splits together.
+// multiple of 64 keys each, aligned to pages) spread over the whole chip;
+// k_attn_merge then folds the splits together.
 //
 // grid: x = split, y = kv head, z = slot; 256 threads (4 waves).  A split is
-// walked in chunks of 64 keys, 16 per wave.  For q.k four lanes share a key,
-// each taking the 16-byte pieces dq, dq+4, dq+8, ... of its row (so every load
-// instruction of the four lanes covers 64 contiguous bytes) and two DPP steps
-// finish the dot product; for p.v a lane owns D/64 (at least one) consecutive
-// dimensions and reads one value row per key.  All K and V loads of a chunk
-// are issued before any arithmetic; in multi-chunk splits the next chunk is in
-// flight while the current one is scored.  Each wave keeps a running (max,
-// sum, output); the waves merge in a fixed order.  A single-split slot writes
-// the output; otherwise the split's (max, sum, unnormalised output) goes to
-// the state's split scratch.
+// walked in page-aligned chunks of 64 keys, 16 per wave, so a wave's keys sit
+// in one page (one scalar page-table load).  For q.k four lanes share a key,
+// each taking the 16-byte pieces dq, dq+4, dq+8, ... of its row (so every
+// load instruction of the four lanes covers 64 contiguous bytes) and two DPP
+// steps finish the dot product; for p.v a lane owns D/64 (at least one)
+// consecutive dimensions and reads one value row per key, with the 16 key
+// weights broadcast through LDS.  All K and V loads of a chunk are issued
+// before any arithmetic; in multi-chunk splits the next chunk is in flight
+// while the current one is scored.  Keys outside [lo, pos] are masked (their
+// rows are clamped into the window, so masked lanes read valid data).  Each
+// wave keeps a running (max, sum, output); the waves merge in a fixed order.
+// A single-split slot writes the output; otherwise the split's (max, sum,
+// unnormalised output) goes to the state's split scratch.
 constexpr int kAttnWaves = 4;
 constexpr int kAttnChunk = kAttnWaves * 16;  // keys per chunk, and the split granularity
 constexpr int kMaxSplits = 256;              // splits per (slot, kv head)
+static_assert(kAttnChunk == kPage, "a chunk is one page of keys");
 
 __device__ __forceinline__ float quad_sum(float v) {
     v += dpp_f<kDppXor1, 0xF>(0.f, v);
     v += dpp_f<kDppXor2, 0xF>(0.f, v);
     return v;
 }
+// max over the 64 lanes of a value that is uniform within each quad of lanes
+__device__ __forceinline__ float wave_max_q(float v) {
+    v = fmaxf(v, dpp_f<kDppHalfMirror, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppMirror, 0xF>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(-INFINITY, v));
+    v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(-INFINITY, v));
+    return readlane_f(v, 63);
+}
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int D, int KV>
 struct AttnShape {
@@ -846,34 +862,39 @@ struct AttnShape {
     static constexpr bool PREF = (NKL * 4 + 16 * (int)sizeof(vword) / 4) <= 40;
 };
 
-// Issue the K and V loads of one wave's 16 keys starting at k0 (positions
-// clamped to kl, the split's last key, so every load is in bounds).
+// Issue the K and V loads of one wave's 16 keys k0..k0+15 (k0 a multiple of
+// 16, w-uniform).  Rows are clamped into [lo, kl], which keeps them inside
+// the page of clamp(k0, lo, kl) and inside the written window.
 template <int D, int KV>
-__device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int k0, int kl, int kq, int dq,
+__device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int k0, int lo, int kl, int kq, int dq,
                                           int lane, u32x4 (&kr)[AttnShape<D, KV>::NKL],
                                           typename AttnShape<D, KV>::vword (&vr)[16]) {
     typedef AttnShape<D, KV> S;
-    const int *pt = a.pt[b];
-    const int tq = min(k0 + kq, kl);
-    const int offq = ((pt[tq / kPage] * a.Hk + j) * kPage + (tq % kPage)) * D + dq * S::KVEC;
-    const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.kvk[b] + (long long)offq * S::ES);
+    const int tc = min(max(k0, lo), kl);
+    const int pg = a.pt[b][tc / kPage];
+    const long long row0 = ((long long)pg * a.Hk + j) * kPage;  // row of the page's first key
+    const int tq = min(max(k0 + kq, lo), kl);
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(
+        a.kvk[b] + ((row0 + tq % kPage) * D + dq * S::KVEC) * S::ES);
 #pragma unroll
     for (int c = 0; c < S::NKL; ++c) kr[c] = kp[4 * c];
     const typename S::vword *vb =
         reinterpret_cast<const typename S::vword *>(a.kvv[b]) + (lane < S::VL ? lane : 0);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-        const int t = min(k0 + u, kl);
-        vr[u] = vb[((pt[t / kPage] * a.Hk + j) * kPage + (t % kPage)) * (D / S::VE)];
+        const int t = min(max(k0 + u, lo), kl);
+        vr[u] = vb[(row0 + t % kPage) * (D / S::VE)];
     }
 }
 
-// Score one wave's 16 keys (nv of them valid) and fold them into the running
-// (m, l, acc) of its G query heads.
+// Score one wave's 16 keys k0..k0+15 (valid: lo <= key < ke, at least one)
+// and fold them into the running (m, l, acc) of its G query heads.  pw is the
+// wave's LDS slice for the key weights.
 template <int D, int KV, int G>
-__device__ __forceinline__ void attn_chunk(const float (*qs)[D], const u32x4 (&kr)[AttnShape<D, KV>::NKL],
-                                           const typename AttnShape<D, KV>::vword (&vr)[16], int nv, int kq,
-                                           int dq, float (&m)[G], float (&l)[G],
+__device__ __forceinline__ void attn_chunk(const float (*qs)[D], float (*pw)[16],
+                                           const u32x4 (&kr)[AttnShape<D, KV>::NKL],
+                                           const typename AttnShape<D, KV>::vword (&vr)[16], int k0, int lo,
+                                           int ke, int kq, int dq, float (&m)[G], float (&l)[G],
                                            float (&acc)[G][AttnShape<D, KV>::VE]) {
     typedef AttnShape<D, KV> S;
     float sc[G];
@@ -897,37 +918,54 @@ __device__ __forceinline__ void attn_chunk(const float (*qs)[D], const u32x4 (&k
 #pragma unroll
             for (int e = 0; e < S::KVEC; ++e) sc[g] = fmaf(qs[g][(4 * c + dq) * S::KVEC + e], kf[e], sc[g]);
     }
-    const bool valid = kq < nv;
+    const int key = k0 + kq;
+    const bool valid = key >= lo && key < ke;
     float p[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         sc[g] = quad_sum(sc[g]);
-        const float mx = fmaxf(m[g], wave_max(valid ? sc[g] : -INFINITY));
-        const float f = expf(m[g] - mx);  // 0 on the wave's first chunk
-        p[g] = valid ? expf(sc[g] - mx) : 0.f;
-        l[g] = l[g] * f + wave_sum(dq == 0 ? p[g] : 0.f);
+        const float mx = fmaxf(m[g], wave_max_q(valid ? sc[g] : -INFINITY));
+        const float f = exp2_fast(m[g] - mx);  // 0 on the wave's first chunk
+        p[g] = valid ? exp2_fast(sc[g] - mx) : 0.f;
+        m[g] = mx;
+        l[g] *= f;
 #pragma unroll
         for (int e = 0; e < S::VE; ++e) acc[g][e] *= f;
-        m[g] = mx;
     }
-    // p.v: key u's weight sits in lane 4u
+    // the 16 key weights of each head to every lane, through the wave's LDS slice
+    if (dq == 0)
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        float v[S::VE];
-        if constexpr (KV == 1) {
-            v[0] = __uint_as_float((uint32_t)vr[u] << 16);
-            if constexpr (S::VE == 2) v[1] = __uint_as_float((uint32_t)vr[u] & 0xFFFF0000u);
-        } else {
-            v[0] = __uint_as_float((uint32_t)((unsigned long long)vr[u] & 0xFFFFFFFFull));
-            if constexpr (S::VE == 2) v[1] = __uint_as_float((uint32_t)((unsigned long long)vr[u] >> 32));
+        for (int g = 0; g < G; ++g) pw[g][kq] = p[g];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float pg[16];
+#pragma unroll
+        for (int u = 0; u < 16; u += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(&pw[g][u]);
+            pg[u] = t[0]; pg[u + 1] = t[1]; pg[u + 2] = t[2]; pg[u + 3] = t[3];
         }
+        float ls = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float pg = readlane_f(p[g], 4 * u);
+        for (int u = 0; u < 16; ++u) ls += pg[u];
+        l[g] += ls;
 #pragma unroll
-            for (int e = 0; e < S::VE; ++e) acc[g][e] = fmaf(pg, v[e], acc[g][e]);
+        for (int u = 0; u < 16; ++u) {
+            float v[S::VE];
+            if constexpr (KV == 1) {
+                v[0] = __uint_as_float((uint32_t)vr[u] << 16);
+                if constexpr (S::VE == 2) v[1] = __uint_as_float((uint32_t)vr[u] & 0xFFFF0000u);
+            } else {
+                v[0] = __uint_as_float((uint32_t)((unsigned long long)vr[u] & 0xFFFFFFFFull));
+                if constexpr (S::VE == 2) v[1] = __uint_as_float((uint32_t)((unsigned long long)vr[u] >> 32));
+            }
+#pragma unroll
+            for (int e = 0; e < S::VE; ++e) acc[g][e] = fmaf(pg[u], v[e], acc[g][e]);
         }
     }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
 template <int D, int KV, int G>
@@ -936,18 +974,22 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     constexpr int NWV = kAttnWaves;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     if (s >= a.nsplit[b]) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int kb = a.t0[b] + s * a.kps;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lo = a.lo[b];
+    const int kb = a.origin[b] + s * a.kps;
     const int ke = min(kb + a.kps, a.pos[b] + 1);
+    const int kl = ke - 1;
 
     __shared__ __align__(16) float qs[G][D];
+    __shared__ __align__(16) float pws[NWV][G][16];
     __shared__ float wm[NWV][G], wl[NWV][G];
     __shared__ float wacc[NWV][G][D];
 
     const int kq = lane >> 2, dq = lane & 3;
     u32x4 kc[S::NKL], kn[S::NKL];
     typename S::vword vc[16], vn[16];
-    attn_load<D, KV>(a, b, j, kb + w * 16, ke - 1, kq, dq, lane, kc, vc);
+    attn_load<D, KV>(a, b, j, kb + w * 16, lo, kl, kq, dq, lane, kc, vc);
     {
         const f32x4 *q4 = reinterpret_cast<const f32x4 *>(a.q + (long long)b * a.Hq * D + (long long)(j * G) * D);
         for (int i = tid; i < G * D / 4; i += 256) {
@@ -967,19 +1009,20 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < S::VE; ++e) acc[g][e] = 0.f;
     }
+    // a wave's 16 keys take part when at least one lies in [lo, ke)
     if (ke - kb <= kAttnChunk) {
         const int k0 = kb + w * 16;
-        if (k0 < ke) attn_chunk<D, KV, G>(qs, kc, vc, ke - k0, kq, dq, m, l, acc);
+        if (k0 + 15 >= lo && k0 < ke) attn_chunk<D, KV, G>(qs, pws[w], kc, vc, k0, lo, ke, kq, dq, m, l, acc);
     } else {
         for (int c0 = kb; c0 < ke; c0 += kAttnChunk) {
             const int k0 = c0 + w * 16;
             if constexpr (S::PREF) {
                 // next chunk in flight (clamped into the split past its end)
-                attn_load<D, KV>(a, b, j, k0 + kAttnChunk, ke - 1, kq, dq, lane, kn, vn);
+                attn_load<D, KV>(a, b, j, k0 + kAttnChunk, lo, kl, kq, dq, lane, kn, vn);
             } else if (c0 != kb) {
-                attn_load<D, KV>(a, b, j, k0, ke - 1, kq, dq, lane, kc, vc);
+                attn_load<D, KV>(a, b, j, k0, lo, kl, kq, dq, lane, kc, vc);
             }
-            if (k0 < ke) attn_chunk<D, KV, G>(qs, kc, vc, ke - k0, kq, dq, m, l, acc);
+            if (k0 + 15 >= lo && k0 < ke) attn_chunk<D, KV, G>(qs, pws[w], kc, vc, k0, lo, ke, kq, dq, m, l, acc);
             if constexpr (S::PREF) {
 #pragma unroll
                 for (int c = 0; c < S::NKL; ++c) kc[c] = kn[c];
@@ -1009,7 +1052,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
         float L = 0.f, A = 0.f;
 #pragma unroll
         for (int x = 0; x < NWV; ++x) {
-            const float f = expf(wm[x][g] - M);
+            const float f = exp2_fast(wm[x][g] - M);
             L += wl[x][g] * f;
             A += wacc[x][g][d] * f;
         }
@@ -1024,20 +1067,19 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
 }
 
 // Fold the splits of one (slot, query head) together.  grid: x = query head,
-// y = slot; 256 threads.  Every split's weight exp(M_s - M) / L is computed
-// once (thread s) and kept in LDS; wave w then sums the unnormalised outputs
-// of splits w, w+4, w+8, ... (loads batched 16 deep), and the four partial
-// sums are added in wave order.  Slots with one split were finished by k_attn.
-template <int D, int G>
-__global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
+// y = slot; 256 threads.  Wave w owns splits w, w+4, w+8, ...: it issues the
+// loads of their unnormalised outputs together with the (max, sum) pairs, so
+// the kernel waits for memory once.  Every split's weight exp2(M_s - M) / L
+// is then formed from the pairs (thread s holds split s) and kept in LDS, each
+// wave sums its splits' weighted outputs, and the four partial sums are added
+// in wave order.  Slots with one split were finished by k_attn.
+template <int D, int G, int NB>
+__device__ __forceinline__ void attn_merge_body(const AttnArgs &a, int h, int b, int ns) {
     constexpr int VE = D >= 64 ? D / 64 : 1;
     constexpr int VL = D / VE;
     constexpr int NWV = 4;
-    constexpr int BATCH = 16;
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int ns = a.nsplit[b];
-    if (ns <= 1) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = h / G, g = h % G;
     const long long stride = (long long)G * (D + 4);  // floats between consecutive splits
     const float *base = a.part[b] + ((long long)j * a.s_cap[b] * G + g) * (D + 4);
@@ -1046,50 +1088,45 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
     __shared__ float red[NWV][2];
     __shared__ float pacc[NWV][D];
 
-    // split weights: thread s holds split s (ns <= kMaxSplits = blockDim)
-    float Ms = -INFINITY, Ls = 0.f;
-    if (tid < ns) {
-        const f32x2 ml = *reinterpret_cast<const f32x2 *>(base + tid * stride);
-        Ms = ml[0];
-        Ls = ml[1];
+    // issue everything: this thread's (max, sum) pair and the wave's outputs
+    // (split indices clamped to the last split, so every load is in bounds)
+    const int dl = (lane < VL ? lane : 0) * VE;
+    const f32x2 ml = *reinterpret_cast<const f32x2 *>(base + min(tid, ns - 1) * stride);
+    float v[NB][VE];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const float *px = base + min(w + u * NWV, ns - 1) * stride + 4 + dl;
+        if constexpr (VE == 2) {
+            const f32x2 t = *reinterpret_cast<const f32x2 *>(px);
+            v[u][0] = t[0];
+            v[u][1] = t[1];
+        } else {
+            v[u][0] = *px;
+        }
     }
+    const float Ms = tid < ns ? ml[0] : -INFINITY;
     float mx = wave_max(Ms);
     if (lane == 0) red[w][0] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
-    const float f = tid < ns ? expf(Ms - mx) : 0.f;
-    const float ls = wave_sum(f * Ls);
+    const float f = tid < ns ? exp2_fast(Ms - mx) : 0.f;
+    const float ls = wave_sum(tid < ns ? f * ml[1] : 0.f);
     if (lane == 0) red[w][1] = ls;
     __syncthreads();
     const float L = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
-    if (tid < ns) fs[tid] = f / L;
+    fs[tid] = f / L;  // 0 past the last split
     __syncthreads();
 
     float acc[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-    const int dl = (lane < VL ? lane : 0) * VE;
-    for (int s0 = w; s0 < ns; s0 += NWV * BATCH) {
-        float v[BATCH][VE];
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int sx = min(s0 + u * NWV, ns - 1);
-            const float *px = base + sx * stride + 4 + dl;
-            if constexpr (VE == 2) {
-                const f32x2 t = *reinterpret_cast<const f32x2 *>(px);
-                v[u][0] = t[0];
-                v[u][1] = t[1];
-            } else {
-                v[u][0] = *px;
-            }
-        }
+    for (int u = 0; u < NB; ++u) {
+        const int sx = w + u * NWV;
+        // a clamped (repeated) split has weight 0 here; fs is 0 past ns
+        const float fw = fs[min(sx, kMaxSplits - 1)];
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int sx = s0 + u * NWV;
-            const float fw = sx < ns ? fs[sx] : 0.f;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) acc[e] = fmaf(fw, v[u][e], acc[e]);
-        }
+        for (int e = 0; e < VE; ++e) acc[e] = sx < ns ? fmaf(fw, v[u][e], acc[e]) : acc[e];
     }
     if (lane < VL)
 #pragma unroll
@@ -1098,6 +1135,18 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
     if (tid < D)
         a.o[(long long)b * a.Hq * D + (long long)h * D + tid] =
             (pacc[0][tid] + pacc[1][tid]) + (pacc[2][tid] + pacc[3][tid]);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int ns = a.nsplit[b];
+    if (ns <= 1) return;
+    // per-wave split count, rounded up to one of three batch depths (block-uniform)
+    const int nbw = (ns + 3) / 4;
+    if (nbw <= 4) attn_merge_body<D, G, 4>(a, h, b, ns);
+    else if (nbw <= 16) attn_merge_body<D, G, 16>(a, h, b, ns);
+    else attn_merge_body<D, G, kMaxSplits / 4>(a, h, b, ns);
 }
 
 }  // namespace pn

@@ -93,6 +93,18 @@ struct pn_model {
     int prof_kernel = -1;
     std::vector<hipEvent_t> ev;
     size_t ev_used = 0;
+    // the launches of each kernel class in the most recent step (one per
+    // layer, or one), for pn_profile_replay
+    struct Replay {
+        int kind = -1;  // GEMM kind, or -1 for attention
+        GemmArgs g{};
+        Plan p{};
+        AttnArgs aa{};
+        dim3 grid{};
+        bool merge = false;
+    };
+    std::vector<Replay> last[PN_K_COUNT];
+    size_t replay_kv = 0, replay_pt = 0;
 };
 
 struct pn_state {
@@ -284,6 +296,10 @@ size_t layout_model(pn_model *m) {
     m->am_count = (size_t)cdiv(m->out.n_tiles, 2) * MB;
     m->am_val = bp.take(m->am_count * 4);
     m->am_idx = bp.take(m->am_count * 4);
+    // pn_profile_replay: a QKV replay appends its k, v rows here (page 0 of a
+    // one-entry page table) instead of into a state's cache
+    m->replay_kv = bp.take((size_t)2 * MB * m->Hk * kPage * m->D * dtype_size(m->kvt));
+    m->replay_pt = bp.take(256);
     return bp.off;
 }
 
@@ -297,7 +313,8 @@ size_t layout_state(pn_state *s) {
     s->layer_bytes = (size_t)s->n_pages * m->Hk * kPage * m->D * es;
     int keys = s->max_ctx;
     if (m->cfg.sliding_window > 0) keys = std::min(keys, m->cfg.sliding_window);
-    s->s_cap = std::min(cdiv(keys, kAttnChunk), kMaxSplits);
+    // splits start on page boundaries, so a window may touch one more chunk
+    s->s_cap = std::min(cdiv(keys + kPage - 1, kAttnChunk), kMaxSplits);
     Bump bp;
     s->kpool = bp.take(s->layer_bytes * m->cfg.n_layer);
     s->vpool = bp.take(s->layer_bytes * m->cfg.n_layer);
@@ -354,6 +371,23 @@ void launch_gemm(int kind, int wt, int at, GemmArgs g, const Plan &p, hipStream_
     gemm_entry(kind, wt, at, p.nw, p.a_lds, g, grid, p.lds, s, nullptr);
 }
 
+void record_gemm(pn_model *m, int cls, int kind, const GemmArgs &g, const Plan &p) {
+    pn_model::Replay r;
+    r.kind = kind;
+    r.g = g;
+    r.p = p;
+    if (kind == GK_QKV) {  // keep a replay away from the states' caches
+        const size_t slot = (size_t)m->Hk * kPage * m->D * dtype_size(m->kvt);
+        for (int b = 0; b < g.B; ++b) {
+            r.g.kvk[b] = m->base + m->replay_kv + (size_t)(2 * b) * slot;
+            r.g.kvv[b] = m->base + m->replay_kv + (size_t)(2 * b + 1) * slot;
+            r.g.pt[b] = (const int *)(m->base + m->replay_pt);
+            r.g.pos[b] = g.pos[b] % kPage;
+        }
+    }
+    m->last[cls].push_back(r);
+}
+
 // event timing of one kernel class
 struct Timed {
     pn_model *m;
@@ -381,6 +415,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                  hipStream_t s) {
     const pn_config &c = m->cfg;
     char *mb = m->base;
+    for (auto &r : m->last) r.clear();
     const int E = m->E, HD = m->H * m->D, F = m->F;
     const int wt = m->wt, at = m->at;
     const int rows = n * m->pieces;
@@ -428,33 +463,35 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     aa.o = (float *)(mb + m->o);
     aa.Hq = m->H;
     aa.Hk = m->Hk;
-    aa.scale = (float)(1.0 / std::sqrt((double)m->D));
+    aa.scale = (float)(1.4426950408889634 / std::sqrt((double)m->D));  // log2(e) / sqrt(D)
     // keys per split: a multiple of kAttnChunk, small enough to spread the window
     // over about kAttnTargetGroups work-groups, large enough that every slot's
-    // splits fit its scratch
+    // splits fit its scratch.  Splits start at the window start rounded down to
+    // a page.
+    auto window_lo = [&](int pos) { return c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0; };
     int span_max = 1;
     for (int b = 0; b < n; ++b) {
         const int pos = st[b]->pos;
-        const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
-        span_max = std::max(span_max, pos - t0 + 1);
+        span_max = std::max(span_max, pos + 1 - window_lo(pos) / kPage * kPage);
     }
     int kps = m->attn_kps;
     if (kps <= 0) {
         const int want = std::max(1, kAttnTargetGroups / (m->Hk * n));
         kps = kAttnChunk * cdiv(span_max, kAttnChunk * want);
     }
+    for (int b = 0; b < n; ++b) {
+        const int pos = st[b]->pos;
+        const int span = pos + 1 - window_lo(pos) / kPage * kPage;
+        kps = std::max(kps, kAttnChunk * cdiv(span, kAttnChunk * st[b]->s_cap));
+    }
     int nsplit_max = 1;
     for (int b = 0; b < n; ++b) {
         const int pos = st[b]->pos;
-        const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
-        kps = std::max(kps, kAttnChunk * cdiv(pos - t0 + 1, kAttnChunk * st[b]->s_cap));
-    }
-    for (int b = 0; b < n; ++b) {
-        const int pos = st[b]->pos;
-        const int t0 = c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0;
+        const int lo = window_lo(pos);
         aa.pos[b] = pos;
-        aa.t0[b] = t0;
-        aa.nsplit[b] = cdiv(pos - t0 + 1, kps);
+        aa.lo[b] = lo;
+        aa.origin[b] = lo / kPage * kPage;
+        aa.nsplit[b] = cdiv(pos + 1 - aa.origin[b], kps);
         aa.s_cap[b] = st[b]->s_cap;
         if (aa.nsplit[b] > st[b]->s_cap || aa.nsplit[b] > kMaxSplits)
             return fail(PN_ERANGE, "attention splits exceed state scratch");
@@ -505,6 +542,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             }
             Timed tm(m, PN_K_QKV, s);
             launch_gemm(GK_QKV, wt, at, g, p_qkv, s);
+            record_gemm(m, PN_K_QKV, GK_QKV, g, p_qkv);
         }
         // ---- attention (+ split combine)
         {
@@ -514,6 +552,11 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             }
             Timed tm(m, PN_K_ATTN, s);
             launch_attn(m->D, m->kvt, m->G, aa, dim3(nsplit_max, m->Hk, n), nsplit_max > 1, s);
+            pn_model::Replay r;
+            r.aa = aa;
+            r.grid = dim3(nsplit_max, m->Hk, n);
+            r.merge = nsplit_max > 1;
+            m->last[PN_K_ATTN].push_back(r);
         }
         // ---- O projection + residual
         {
@@ -529,6 +572,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.ld_out = E;
             Timed tm(m, PN_K_O, s);
             launch_gemm(GK_O, wt, at, g, p_o, s);
+            record_gemm(m, PN_K_O, GK_O, g, p_o);
         }
         // ---- FFN
         if (!moe) {
@@ -549,6 +593,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.ld_out = m->h_ld;
                 Timed tm(m, PN_K_GATEUP, s);
                 launch_gemm(GK_SWIGLU, wt, at, g, p_gu, s);
+                record_gemm(m, PN_K_GATEUP, GK_SWIGLU, g, p_gu);
             }
             {
                 GemmArgs g = base;
@@ -565,6 +610,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.ld_out = E;
                 Timed tm(m, PN_K_DOWN, s);
                 launch_gemm(GK_RESID, wt, at, g, p_dn, s);
+                record_gemm(m, PN_K_DOWN, GK_RESID, g, p_dn);
             }
         } else {
             int *rid = (int *)(mb + m->route_ids);
@@ -654,6 +700,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         g.am_idx = (int *)(mb + m->am_idx);
         Timed tm(m, PN_K_LMHEAD, s);
         launch_gemm(GK_LOGITS, wt, at, g, p_lm, s);
+        record_gemm(m, PN_K_LMHEAD, GK_LOGITS, g, p_lm);
     }
     {
         Timed tm(m, PN_K_ARGMAX, s);
@@ -737,6 +784,7 @@ int pn_model_load_globals(pn_model *m, const void *tok_embd, const float *out_no
     hipLaunchKernelGGL(k_omega, dim3(1), dim3(64), 0, s, (double *)(mb + m->omega), m->D, (double)m->cfg.rope_theta);
     fill32(mb + m->o, m->o_bytes / 4, 0u, s);
     fill32(mb + m->h, m->h_bytes / 4, 0u, s);
+    fill32(mb + m->replay_pt, 64, 0u, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PN_EHIP, "weight packing failed: %s", hipGetErrorString(e));
     return PN_OK;
@@ -943,7 +991,11 @@ int pn_state_check(pn_state *s, void *stream, int32_t *flags_out) {
     return PN_OK;
 }
 
-void pn_state_free(pn_state *s) { delete s; }
+void pn_state_free(pn_state *s) {
+    if (!s) return;
+    for (auto &r : s->m->last) r.clear();  // recorded launches may point into this state
+    delete s;
+}
 
 int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int32_t *tokens_dev,
                      float *logits_dev, int32_t *argmax_dev, void *stream) {
@@ -996,6 +1048,25 @@ int pn_profile_begin(pn_model *m, int32_t kernel) {
     if (kernel < 0 || kernel >= PN_K_COUNT) return fail(PN_EINVAL, "unknown kernel class %d", kernel);
     m->prof_kernel = kernel;
     m->ev_used = 0;
+    return PN_OK;
+}
+
+int pn_profile_replay(pn_model *m, int32_t kernel, int32_t reps, void *stream) {
+    g_err.clear();
+    if (!m) return fail(PN_EINVAL, "model is NULL");
+    if (kernel < 0 || kernel >= PN_K_COUNT) return fail(PN_EINVAL, "unknown kernel class %d", kernel);
+    if (reps < 1) return fail(PN_EINVAL, "reps must be positive");
+    const std::vector<pn_model::Replay> &rs = m->last[kernel];
+    if (rs.empty() || (kernel != PN_K_ATTN && rs[0].kind < 0))
+        return fail(PN_EINVAL, "no recorded launch of kernel class %d", kernel);
+    hipStream_t s = S(stream);
+    for (int i = 0; i < reps; ++i) {
+        const pn_model::Replay &r = rs[i % rs.size()];
+        if (kernel == PN_K_ATTN) launch_attn(m->D, m->kvt, m->G, r.aa, r.grid, r.merge, s);
+        else launch_gemm(r.kind, m->wt, m->at, r.g, r.p, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PN_EHIP, "replay launch failed: %s", hipGetErrorString(e));
     return PN_OK;
 }
 

@@ -72,6 +72,7 @@ class DeviceModel:
         C.check(L.pn_model_init(ctypes.byref(cfg), ctypes.c_void_p(_aligned(self.buf)), nbytes,
                                 ctypes.byref(h)))
         self.h = h
+        self._L = L
         s = stream if stream is not None else torch.cuda.current_stream()
         sp = _stream_ptr(s)
         g = [upload(weights["tok_embd"], device), upload(weights["out_norm"], device),
@@ -91,9 +92,11 @@ class DeviceModel:
             del t
 
     def __del__(self):
-        h = getattr(self, "h", None)
-        if h is not None and h.value and C._lib is not None:
-            C._lib.pn_model_free(h)
+        # the library handle is held by the object: module globals may already
+        # be gone when this runs at interpreter exit
+        h, L = getattr(self, "h", None), getattr(self, "_L", None)
+        if h is not None and h.value and L is not None:
+            L.pn_model_free(h)
             self.h = None
 
     def set_option(self, option, value):
@@ -101,6 +104,10 @@ class DeviceModel:
 
     def profile_begin(self, kernel):
         C.check(C.lib().pn_profile_begin(self.h, kernel))
+
+    def profile_replay(self, kernel, reps, stream=None):
+        """Enqueue reps copies of the last launch of a kernel class (for timing)."""
+        C.check(C.lib().pn_profile_replay(self.h, kernel, reps, _stream_ptr(stream)))
 
     def profile_end(self, stream=None):
         ms = ctypes.c_double()
@@ -123,11 +130,12 @@ class DeviceState:
         C.check(L.pn_state_new(model.h, max_ctx, ctypes.c_void_p(_aligned(self.buf)), nbytes,
                                _stream_ptr(stream), ctypes.byref(h)))
         self.h = h
+        self._L = L
 
     def __del__(self):
-        h = getattr(self, "h", None)
-        if h is not None and h.value and C._lib is not None:
-            C._lib.pn_state_free(h)
+        h, L = getattr(self, "h", None), getattr(self, "_L", None)
+        if h is not None and h.value and L is not None:
+            L.pn_state_free(h)
             self.h = None
 
     @property
