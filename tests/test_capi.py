@@ -110,6 +110,8 @@ def test_init_rejects_bad_buffers_without_device_work():
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KEYS_PER_SPLIT, 100) == C.PN_EINVAL
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KEYS_PER_SPLIT, 512) == 0
         assert L.pn_profile_begin(h, 99) == C.PN_EINVAL
+        assert L.pn_profile_replay(h, C.PN_K_GATEUP, 4, None) == C.PN_EINVAL  # nothing recorded yet
+        assert L.pn_profile_replay(h, 99, 4, None) == C.PN_EINVAL
         lw = C.pn_layer_weights()
         assert L.pn_model_load_layer(h, 0, ctypes.byref(lw), None) == C.PN_EINVAL
         assert L.pn_model_load_layer(h, 5, ctypes.byref(lw), None) == C.PN_EINVAL

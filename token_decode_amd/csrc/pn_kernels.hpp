@@ -92,6 +92,16 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Work-group barrier for LDS data only.  __syncthreads() also waits for every
+// outstanding global load of the wave (vmcnt(0)), which would drain the weight
+// rounds kept in flight across a block's reduction; these barriers only order
+// LDS accesses, so they wait for LDS operations alone.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float readlane_f(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -216,9 +226,9 @@ template <int NW>
 __device__ __forceinline__ float block_sum(float v, float *redw) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) redw[w] = v;
-    __syncthreads();
+    lds_barrier();
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < NW; ++i) s += redw[i];
@@ -378,7 +388,11 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     constexpr int PIECES = AReady<WT, AT>::PIECES;
     constexpr bool MOE = (EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN);
     constexpr int CH = NW == 4 ? 2 : 1;        // x-prologue: 8-element chunks per thread per batch
-    constexpr int CHA = NW >= 16 ? 2 : 4;      // A-ready staging: fragments per thread per batch
+    // A-ready staging: fragments per thread per batch, enough for A in one batch
+    // up to the LDS staging limit (96 KiB) where the registers allow
+    constexpr int CHA_FULL = (96 * 1024 / frag_bytes(WT) + NW * 64 - 1) / (NW * 64);
+    constexpr int CHA = CHA_FULL < 12 ? CHA_FULL : 12;
+    constexpr int SPW = (kMaxSlots + NW - 1) / NW;  // norm prologue: slots whose sums of squares a wave reads
     constexpr int ES = AReady<WT, AT>::ES;
     extern __shared__ __align__(16) uint8_t smem[];
 
@@ -400,7 +414,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                     if (g.route_ids[b * g.n_used + k] == ex) s_ent[n++] = b * g.n_used + k;
             s_nb = n;
         }
-        __syncthreads();
+        lds_barrier();
     }
     const int nb = MOE ? s_nb : g.B;
     if (nb == 0) return;
@@ -412,10 +426,12 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     float *red = reinterpret_cast<float *>(smem + abytes);  // [wave][mt][m][n]
     float *C = red + NW * NTW * 256;                          // [mt][m][n]
 
-    // ---- phase 1: the prologue's loads
+    // ---- phase 1: the prologue's loads, all issued before any weight load and
+    // with a fixed count (addresses clamped, values selected), so that waiting
+    // for them never waits for weights
     const int n8 = g.KT * TK / 8;  // 8-element chunks per A row
     float xv[CH][8], gv[CH][8];
-    float ssv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float ssv[SPW][8];
     u32x4 st0[CHA], st1[CHA];
     if constexpr (XPRO) {
 #pragma unroll
@@ -425,41 +441,95 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
             const bool in = b < nb && k0 < g.K;
             const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
             const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 x0 = in ? xp[0] : z, x1 = in ? xp[1] : z;
+            // (values of chunks past the rows or K are never used)
+            const f32x4 x0 = xp[0], x1 = xp[1];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { xv[c][e] = x0[e]; xv[c][4 + e] = x1[e]; }
+            for (int e = 0; e < 4; ++e) {
+                xv[c][e] = x0[e];
+                xv[c][4 + e] = x1[e];
+            }
             if constexpr (PRO == PRO_NORM) {
                 const f32x4 *gp = reinterpret_cast<const f32x4 *>(g.gain + (in ? k0 : 0));
-                const f32x4 g0 = in ? gp[0] : z, g1 = in ? gp[1] : z;
+                const f32x4 g0 = gp[0], g1 = gp[1];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { gv[c][e] = g0[e]; gv[c][4 + e] = g1[e]; }
+                for (int e = 0; e < 4; ++e) {
+                    gv[c][e] = g0[e];
+                    gv[c][4 + e] = g1[e];
+                }
             }
         }
     }
     if constexpr (PRO == PRO_NORM) {
-        if (wave < nb) {
-            const int sb = MOE ? s_ent[wave] / g.n_used : wave;
+        // the per-16-element sums of squares of slots wave, wave+NW, ... (at most
+        // 512 of them: K <= 8192)
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) {
+            const int b = wave + q * NW;
+            const int sb = b < nb ? (MOE ? s_ent[b] / g.n_used : b) : 0;
             const float *sp = g.ssp + (long long)sb * g.ssp_ld;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) ssv[u] = (lane + 64 * u < g.ssp_n) ? sp[lane + 64 * u] : 0.f;
+            for (int u = 0; u < 8; ++u) ssv[q][u] = sp[min(lane + 64 * u, g.ssp_n - 1)];  // masked in phase 3
         }
     }
     if constexpr (PRO == PRO_LOAD && ALDS) {
+        const int chunksA = g.KT * 4;
 #pragma unroll
         for (int c = 0; c < CHA; ++c) {
             const int idx = tid + c * NT;
-            const int chunksA = g.KT * 4;
             const int m = idx / chunksA, f = idx - m * chunksA;
             const bool in = m < rows;
             const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
             const long long r = MOE ? s_ent[b] : b;
             const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
                                  ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
-            st0[c] = in ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0, 0, 0, 0};
-            if constexpr (WT == WT_I8) st1[c] = in ? *reinterpret_cast<const u32x4 *>(src + 16) : u32x4{0, 0, 0, 0};
+            st0[c] = *reinterpret_cast<const u32x4 *>(src);  // (rows past A are never stored)
+            if constexpr (WT == WT_I8) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
         }
     }
+
+    // epilogue inputs of one block, loaded early by the threads that use them
+    // (row r of slot b: the old x for the residual, the (cos, sin) for RoPE,
+    // the int8 row scales)
+    struct EpIn { float x, s0, s1; float2 cs; int page; };
+    auto epi_load = [&](int blk) -> EpIn {
+        EpIn e{0.f, 1.f, 1.f, make_float2(1.f, 0.f), 0};
+        if constexpr (EPI == EPI_RESID) {
+            if (tid < nb * 16) {
+                const int b = tid >> 4, r = blk * 16 + (tid & 15);
+                if (r < g.N) e.x = g.out_f32[(long long)b * g.ld_out + r];
+                if constexpr (WT == WT_I8) e.s0 = r < g.N ? g.sc[r] : 0.f;
+            }
+        } else if constexpr (EPI == EPI_QKV) {
+            if (tid < nb * 8) {
+                const int b = tid >> 3, r0 = blk * 16 + (tid & 7) * 2;
+                e.page = g.pt[b][g.pos[b] / kPage];  // the page the k, v rows are appended to
+                if (r0 < g.N) {
+                    e.cs = g.rope[(long long)b * (g.D / 2) + ((r0 % g.D) >> 1)];
+                    if constexpr (WT == WT_I8) { e.s0 = g.sc[r0]; e.s1 = g.sc[r0 + 1]; }
+                }
+            }
+        } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN) {
+            if constexpr (WT == WT_I8) {
+                if (tid < nb * 16) {
+                    const int r = blk * 16 + (tid & 15);
+                    if (r < g.N) {
+                        e.s0 = g.sc[(long long)ex * g.es_stride + r];
+                        if constexpr (PAIR) e.s1 = g.sc2[(long long)ex * g.es_stride + r];
+                    }
+                }
+            }
+        } else if constexpr (EPI == EPI_LOGITS) {
+            if constexpr (WT == WT_I8) {
+                if (tid < nb * NTW * 16) {
+                    const int c = tid % (NTW * 16);
+                    const int r = blk * NTW * 16 + c;
+                    if (r < g.N) e.s0 = g.sc[r];
+                }
+            }
+        }
+        return e;
+    };
+    EpIn epc = epi_load(blk0);
 
     // ---- phase 2: the first block's first two weight rounds (and direct A fragments)
     const int per = (g.KT + NW - 1) / NW;
@@ -503,90 +573,28 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     };
     issue_first();
 
-    // epilogue inputs of one block, loaded early by the threads that use them
-    // (row r of slot b: the old x for the residual, the (cos, sin) for RoPE,
-    // the int8 row scales)
-    struct EpIn { float x, s0, s1; float2 cs; };
-    auto epi_load = [&](int blk) -> EpIn {
-        EpIn e{0.f, 1.f, 1.f, make_float2(1.f, 0.f)};
-        if constexpr (EPI == EPI_RESID) {
-            if (tid < nb * 16) {
-                const int b = tid >> 4, r = blk * 16 + (tid & 15);
-                if (r < g.N) e.x = g.out_f32[(long long)b * g.ld_out + r];
-                if constexpr (WT == WT_I8) e.s0 = r < g.N ? g.sc[r] : 0.f;
-            }
-        } else if constexpr (EPI == EPI_QKV) {
-            if (tid < nb * 8) {
-                const int b = tid >> 3, r0 = blk * 16 + (tid & 7) * 2;
-                if (r0 < g.N) {
-                    e.cs = g.rope[(long long)b * (g.D / 2) + ((r0 % g.D) >> 1)];
-                    if constexpr (WT == WT_I8) { e.s0 = g.sc[r0]; e.s1 = g.sc[r0 + 1]; }
-                }
-            }
-        } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN) {
-            if constexpr (WT == WT_I8) {
-                if (tid < nb * 16) {
-                    const int r = blk * 16 + (tid & 15);
-                    if (r < g.N) {
-                        e.s0 = g.sc[(long long)ex * g.es_stride + r];
-                        if constexpr (PAIR) e.s1 = g.sc2[(long long)ex * g.es_stride + r];
-                    }
-                }
-            }
-        } else if constexpr (EPI == EPI_LOGITS) {
-            if constexpr (WT == WT_I8) {
-                if (tid < nb * NTW * 16) {
-                    const int c = tid % (NTW * 16);
-                    const int r = blk * NTW * 16 + c;
-                    if (r < g.N) e.s0 = g.sc[r];
-                }
-            }
-        }
-        return e;
-    };
-    EpIn epc = epi_load(blk0);
 
     // ---- phase 3: the prologue's arithmetic
     if constexpr (XPRO) {
         if constexpr (PRO == PRO_NORM) {
-            if (wave < nb) {
-                // fixed summation order: per lane, then the wave reduction
-                float ss = ((ssv[0] + ssv[1]) + (ssv[2] + ssv[3])) + ((ssv[4] + ssv[5]) + (ssv[6] + ssv[7]));
-                const int sb = MOE ? s_ent[wave] / g.n_used : wave;
-                for (int i = lane + 512; i < g.ssp_n; i += 64) ss += g.ssp[(long long)sb * g.ssp_ld + i];
-                ss = wave_sum(ss);
-                if (lane == 0) s_rinv[wave] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
-            }
-            for (int b = NW + wave; b < nb; b += NW) {  // more slots than waves
-                const int sb = MOE ? s_ent[b] / g.n_used : b;
-                float ss = 0.f;
-                for (int i = lane; i < g.ssp_n; i += 64) ss += g.ssp[(long long)sb * g.ssp_ld + i];
-                ss = wave_sum(ss);
-                if (lane == 0) s_rinv[b] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
-            }
-            __syncthreads();
-        }
-        for (int base = 0; base < nb * n8; base += CH * NT) {
-            if (base > 0) {
 #pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    const int ch = base + tid + c * NT;
-                    const int b = ch / n8, k0 = (ch - b * n8) * 8;
-                    const bool in = b < nb && k0 < g.K;
-                    const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
-                    const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
-                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    const f32x4 x0 = in ? xp[0] : z, x1 = in ? xp[1] : z;
+            for (int q = 0; q < SPW; ++q) {
+                const int b = wave + q * NW;
+                if (b < nb) {
+                    // fixed summation order: per lane, then the wave reduction
+                    float v[8];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) { xv[c][e] = x0[e]; xv[c][4 + e] = x1[e]; }
-                    if constexpr (PRO == PRO_NORM) {
-                        const f32x4 *gp = reinterpret_cast<const f32x4 *>(g.gain + (in ? k0 : 0));
-                        const f32x4 g0 = in ? gp[0] : z, g1 = in ? gp[1] : z;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) { gv[c][e] = g0[e]; gv[c][4 + e] = g1[e]; }
-                    }
+                    for (int u = 0; u < 8; ++u) v[u] = lane + 64 * u < g.ssp_n ? ssv[q][u] : 0.f;
+                    float ss = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+                    ss = wave_sum(ss);
+                    if (lane == 0) s_rinv[b] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
                 }
             }
+            lds_barrier();
+        }
+        // batch 0 comes from the phase-1 registers; later batches (more rows
+        // than one batch covers) load their own, after the weights
+        auto stage_x = [&](int base) {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int ch = base + tid + c * NT;
@@ -607,25 +615,32 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 }
                 put_a8<WT, AT>(sa, rows, nb, b, k0, v);
             }
-        }
-        __syncthreads();
-    } else if constexpr (ALDS) {
-        const int chunksA = g.KT * 4;  // fragments per A row
-        for (int base = 0; base < rows * chunksA; base += CHA * NT) {
-            if (base > 0) {
+        };
+        stage_x(0);
+        for (int base = CH * NT; base < nb * n8; base += CH * NT) {
 #pragma unroll
-                for (int c = 0; c < CHA; ++c) {
-                    const int idx = base + tid + c * NT;
-                    const int m = idx / chunksA, f = idx - m * chunksA;
-                    const bool in = m < rows;
-                    const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
-                    const long long r = MOE ? s_ent[b] : b;
-                    const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
-                                         ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
-                    st0[c] = in ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0, 0, 0, 0};
-                    if constexpr (WT == WT_I8) st1[c] = in ? *reinterpret_cast<const u32x4 *>(src + 16) : u32x4{0, 0, 0, 0};
+            for (int c = 0; c < CH; ++c) {
+                const int ch = base + tid + c * NT;
+                const int b = ch / n8, k0 = (ch - b * n8) * 8;
+                const bool in = b < nb && k0 < g.K;
+                const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
+                const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
+                const f32x4 x0 = xp[0], x1 = xp[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { xv[c][e] = x0[e]; xv[c][4 + e] = x1[e]; }
+                if constexpr (PRO == PRO_NORM) {
+                    const f32x4 *gp = reinterpret_cast<const f32x4 *>(g.gain + (in ? k0 : 0));
+                    const f32x4 g0 = gp[0], g1 = gp[1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { gv[c][e] = g0[e]; gv[c][4 + e] = g1[e]; }
                 }
             }
+            stage_x(base);
+        }
+        lds_barrier();
+    } else if constexpr (ALDS) {
+        const int chunksA = g.KT * 4;  // fragments per A row
+        auto stage_a = [&](int base) {
 #pragma unroll
             for (int c = 0; c < CHA; ++c) {
                 const int idx = base + tid + c * NT;
@@ -635,8 +650,24 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 *reinterpret_cast<u32x4 *>(dst) = st0[c];
                 if constexpr (WT == WT_I8) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
             }
+        };
+        stage_a(0);  // from the phase-1 registers
+        for (int base = CHA * NT; base < rows * chunksA; base += CHA * NT) {
+#pragma unroll
+            for (int c = 0; c < CHA; ++c) {
+                const int idx = base + tid + c * NT;
+                const int m = idx / chunksA, f = idx - m * chunksA;
+                const bool in = m < rows;
+                const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
+                const long long r = MOE ? s_ent[b] : b;
+                const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
+                                     ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
+                st0[c] = *reinterpret_cast<const u32x4 *>(src);
+                if constexpr (WT == WT_I8) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
+            }
+            stage_a(base);
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     for (int blk = blk0; blk < blk1; ++blk) {
@@ -669,8 +700,8 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         EpIn epn = epc;
         if (blk + 1 < blk1) {
             block_ptrs(blk + 1, wbase, wlive);
-            issue_first();
             epn = epi_load(blk + 1);
+            issue_first();
         }
 
         // ---- reduce the waves' tiles: red[wave][mt][m][n], then C[mt][m][n]
@@ -678,14 +709,14 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         for (int mt = 0; mt < NTW; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[(wave * NTW + mt) * 256 + (4 * ag + i) * 16 + am] = acc[mt][i];
-        __syncthreads();
+        lds_barrier();
         for (int idx = tid; idx < NTW * 256; idx += NT) {
             float sum = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) sum += red[w * NTW * 256 + idx];
             C[idx] = sum;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- epilogue.  Y[mt][b][n] = sum over pieces of C[mt][piece*nb + b][n]
         auto Y = [&](int mt, int b, int n) -> float {
@@ -711,7 +742,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                         const int rr = isk ? r0 - hd : r0 - hd - kd;
                         const int j = rr / g.D, dd = rr % g.D;
                         if (isk) rope_pair(y0, y1, epc.cs);
-                        const int page = g.pt[b][pos / kPage];
+                        const int page = epc.page;
                         const long long off = (((long long)page * g.Hk + j) * kPage + (pos % kPage)) * g.D + dd;
                         char *base = isk ? g.kvk[b] : g.kvv[b];
                         if (g.kv_es == 2) {
@@ -757,39 +788,47 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 if (r < g.N) g.out_f32[(long long)s_ent[b] * g.ld_out + r] = Y(0, b, n) * epc.s0;
             }
         } else if constexpr (EPI == EPI_LOGITS) {
-            float *L = red;  // logits of this block [slot][NTW*16]
-            if (tid < nb * NTW * 16) {
-                const int b = tid / (NTW * 16), c = tid % (NTW * 16), mt = c >> 4, n = c & 15;
+            // the block's logits, and per slot the (value, lowest index) max over
+            // its 32 rows by a shuffle reduction within the slot's half-wave
+            // (NaN rows are skipped and flag the slot)
+            static_assert(NTW * 16 == 32, "one half-wave per slot");
+            if (tid < nb * 32) {
+                const int b = tid >> 5, c = tid & 31, mt = c >> 4, n = c & 15;
                 const int r = (blk * NTW + mt) * 16 + n;
                 float v = 0.f;
-                if (r < g.N) {
-                    v = Y(mt, b, n) * epc.s0;
-                    if (g.out_f32) g.out_f32[(long long)b * g.N + r] = v;
-                }
-                L[tid] = v;
-            }
-            __syncthreads();
-            if (tid < nb) {
-                const int b = tid;
-                float best = 0.f;
-                int bi = -1;
+                int vi = -1;
                 bool nan = false;
-                for (int c = 0; c < NTW * 16; ++c) {
-                    const int r = blk * NTW * 16 + c;
-                    if (r >= g.N) break;
-                    const float v = L[b * NTW * 16 + c];
-                    if (v != v) { nan = true; continue; }
-                    if (bi < 0 || v > best) { best = v; bi = r; }
+                if (r < g.N) {
+                    const float y = Y(mt, b, n) * epc.s0;
+                    if (g.out_f32) g.out_f32[(long long)b * g.N + r] = y;
+                    if (y != y) {
+                        nan = true;
+                    } else {
+                        v = y;
+                        vi = r;
+                    }
                 }
-                g.am_val[(long long)blk * nb + b] = best;
-                g.am_idx[(long long)blk * nb + b] = bi;
-                if (nan) atomicOr(g.err[b], ERR_NAN);
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) {
+                    const float ov = __shfl_xor(v, o, 64);
+                    const int oi = __shfl_xor(vi, o, 64);
+                    if (oi >= 0 && (vi < 0 || ov > v || (ov == v && oi < vi))) {
+                        v = ov;
+                        vi = oi;
+                    }
+                }
+                const unsigned long long bal = __ballot(nan);
+                if (c == 0) {
+                    g.am_val[(long long)blk * nb + b] = v;
+                    g.am_idx[(long long)blk * nb + b] = vi;
+                    if ((bal >> (lane & 32)) & 0xFFFFFFFFull) atomicOr(g.err[b], ERR_NAN);
+                }
             }
         }
         (void)live0;
         (void)live1;
         epc = epn;
-        __syncthreads();  // red and C are reused by the next block
+        lds_barrier();  // red and C are reused by the next block
     }
 }
 
@@ -999,7 +1038,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
             for (int e = 0; e < 4; ++e) qs[g][d + e] = v[e] * a.scale;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     float m[G], l[G], acc[G][S::VE];
 #pragma unroll
@@ -1041,7 +1080,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int e = 0; e < S::VE; ++e) wacc[w][g][lane * S::VE + e] = acc[g][e];
-    __syncthreads();
+    lds_barrier();
 
     const int ns = a.nsplit[b];
     for (int idx = tid; idx < G * D; idx += 256) {
@@ -1107,15 +1146,15 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs &a, int h, int b,
     const float Ms = tid < ns ? ml[0] : -INFINITY;
     float mx = wave_max(Ms);
     if (lane == 0) red[w][0] = mx;
-    __syncthreads();
+    lds_barrier();
     mx = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
     const float f = tid < ns ? exp2_fast(Ms - mx) : 0.f;
     const float ls = wave_sum(tid < ns ? f * ml[1] : 0.f);
     if (lane == 0) red[w][1] = ls;
-    __syncthreads();
+    lds_barrier();
     const float L = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
     fs[tid] = f / L;  // 0 past the last split
-    __syncthreads();
+    lds_barrier();
 
     float acc[VE];
 #pragma unroll
@@ -1131,7 +1170,7 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs &a, int h, int b,
     if (lane < VL)
 #pragma unroll
         for (int e = 0; e < VE; ++e) pacc[w][dl + e] = acc[e];
-    __syncthreads();
+    lds_barrier();
     if (tid < D)
         a.o[(long long)b * a.Hq * D + (long long)h * D + tid] =
             (pacc[0][tid] + pacc[1][tid]) + (pacc[2][tid] + pacc[3][tid]);

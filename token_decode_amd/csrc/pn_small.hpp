@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(256) k_argmax(const float *val, const int *idx
     __shared__ int si[256];
     sv[tid] = best;
     si[tid] = bi;
-    __syncthreads();
+    lds_barrier();
     for (int o = 128; o > 0; o >>= 1) {
         if (tid < o) {
             const float v = sv[tid + o];
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(256) k_argmax(const float *val, const int *idx
                 si[tid] = i;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (tid == 0 && out) out[b] = si[0];
 }
@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(256) k_router(const float *x, const float *gai
                 xs[k] = v;
             }
         }
-    __syncthreads();
+    lds_barrier();
     // expert e on wave e % 4: lanes stride over E in 8-element groups
     for (int e = w; e < n_expert; e += 4) {
         float acc = 0.f;
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(256) k_router(const float *x, const float *gai
         acc = wave_sum(acc);
         if (lane == 0) r[e] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         unsigned long long used = 0ull;
         int sel[8];
