@@ -41,9 +41,12 @@
  * values that the decode step stores in a narrower type are rounded at the
  * same points: the inputs of every mat-vec (normed x, attention output,
  * FFN hidden, final normed x) to the activation type, and the appended k, v
- * to the KV type.  Integer decisions taken from floating point (the argmax of
- * the logits, the router's top-k) compare the values rounded to fp32, the
- * precision the GPU decides in.
+ * to the KV type.  Decisions that floating point takes, and that pick a
+ * discrete result, are taken in fp32, the precision the GPU decides in: the
+ * argmax of the logits and the router's top-k compare values rounded to fp32,
+ * and a value stored as bf16 is first rounded to fp32, then to its bf16 code.
+ * (With bf16 activations a 32-layer model is chaotic enough that a difference
+ * of one fp32 ulp before a bf16 rounding moves its logits by about 1%.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -85,13 +88,14 @@ double orc_round_bf16(double v) {
     return ldexp(nearbyint(ldexp(m, 8)), e - 8);
 }
 
+/* v stored in type dt: fp32, or the bf16 code of its fp32 value */
 static double round_to(double v, int dt) {
-    if (dt == ORC_BF16) return orc_round_bf16(v);
+    if (dt == ORC_BF16) return orc_round_bf16((double)(float)v);
     return (double)(float)v;
 }
 
 static uint16_t bf16_bits(double v) {
-    float f = (float)orc_round_bf16(v);
+    float f = (float)orc_round_bf16((double)(float)v);
     uint32_t b;
     memcpy(&b, &f, 4);
     return (uint16_t)(b >> 16);
