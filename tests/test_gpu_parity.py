@@ -108,3 +108,14 @@ def test_attention_split_sizes(kps):
         p.dm.set_option(C.PN_OPT_ATTN_KEYS_PER_SPLIT, kps)
         worst, near, n = run_single(p, 999, [11, 12], 2)
         log("  kps %d kv %d: worst rel L2 %.2e near %d" % (kps, kv, worst, near))
+
+
+def test_batched_16_slots_large_lds():
+    """16 slots with n_embd 2048: several GEMM variants stage more than 64 KiB of
+    A in LDS in the same step (each needs its own launch attribute)."""
+    wl = ragged("batch16-e2048", n_embd=2048, n_head=16, n_kv_head=4, head_dim=128, n_ff=600,
+                w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.BF16, seed=48)
+    p = Pair(wl, max_batch=16)
+    starts = [int(s) for s in synth.uniform_int(48, 99, 16, 0, 400)]
+    worst, near = run_batch(p, starts, 2)
+    log("  batch 16: worst rel L2 %.2e near %d" % (worst, near))

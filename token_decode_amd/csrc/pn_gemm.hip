@@ -5,12 +5,13 @@
 namespace pn {
 namespace {
 
-template <typename F>
-void allow_lds(F *kernel, size_t lds) {
-    // dynamic LDS above 64 KiB has to be enabled per kernel; done once per kernel
+// Dynamic LDS above 64 KiB has to be enabled per kernel; done once for each
+// kernel (one flag per instantiation: the kernels all share one signature).
+template <auto *KERNEL>
+void allow_lds(size_t lds) {
     static bool done = false;
     if (lds > 64 * 1024 && !done) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(KERNEL),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
         done = true;
     }
@@ -20,7 +21,7 @@ void allow_lds(F *kernel, size_t lds) {
 template <int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS>
 void go_k(const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
     auto *k = &k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS>;
-    allow_lds(k, lds);
+    allow_lds<&k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS>>(lds);
     if (occ) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, NW * 64, lds) != hipSuccess) n = 1;

@@ -18,8 +18,9 @@ enum GemmKind {
     GK_COUNT = 7
 };
 
-// LDS a launch may use, in bytes (the hardware limit of one work-group).
-constexpr size_t kMaxLds = 160 * 1024;
+// Dynamic LDS a launch may use, in bytes: a work-group's 160 KiB less 1 KiB
+// for the kernels' static LDS (the two together may not exceed the limit).
+constexpr size_t kMaxLds = 159 * 1024;
 
 // Defined once per (weight type, activation type) in pn_gemm.hip; nw = waves
 // per work-group (4, 8 or 16); alds = stage an A-ready input in LDS.  With occ

@@ -388,6 +388,16 @@ void record_gemm(pn_model *m, int cls, int kind, const GemmArgs &g, const Plan &
     m->last[cls].push_back(r);
 }
 
+// the launch just enqueued, checked at once so that a failure names its kernel
+int launched(const char *what, const Plan *p = nullptr) {
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return PN_OK;
+    if (p)
+        return fail(PN_EHIP, "%s launch failed (grid %d x %d, %d waves, %zu B LDS): %s", what, p->gx, p->gz, p->nw,
+                    p->lds, hipGetErrorString(e));
+    return fail(PN_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
 // event timing of one kernel class
 struct Timed {
     pn_model *m;
@@ -542,6 +552,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             }
             Timed tm(m, PN_K_QKV, s);
             launch_gemm(GK_QKV, wt, at, g, p_qkv, s);
+            if (int rc = launched("QKV projection", &p_qkv)) return rc;
             record_gemm(m, PN_K_QKV, GK_QKV, g, p_qkv);
         }
         // ---- attention (+ split combine)
@@ -552,6 +563,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             }
             Timed tm(m, PN_K_ATTN, s);
             launch_attn(m->D, m->kvt, m->G, aa, dim3(nsplit_max, m->Hk, n), nsplit_max > 1, s);
+            if (int rc = launched("attention")) return rc;
             pn_model::Replay r;
             r.aa = aa;
             r.grid = dim3(nsplit_max, m->Hk, n);
@@ -572,6 +584,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.ld_out = E;
             Timed tm(m, PN_K_O, s);
             launch_gemm(GK_O, wt, at, g, p_o, s);
+            if (int rc = launched("O projection", &p_o)) return rc;
             record_gemm(m, PN_K_O, GK_O, g, p_o);
         }
         // ---- FFN
@@ -593,6 +606,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.ld_out = m->h_ld;
                 Timed tm(m, PN_K_GATEUP, s);
                 launch_gemm(GK_SWIGLU, wt, at, g, p_gu, s);
+                if (int rc = launched("gate/up projection", &p_gu)) return rc;
                 record_gemm(m, PN_K_GATEUP, GK_SWIGLU, g, p_gu);
             }
             {
@@ -610,6 +624,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.ld_out = E;
                 Timed tm(m, PN_K_DOWN, s);
                 launch_gemm(GK_RESID, wt, at, g, p_dn, s);
+                if (int rc = launched("down projection", &p_dn)) return rc;
                 record_gemm(m, PN_K_DOWN, GK_RESID, g, p_dn);
             }
         } else {
@@ -654,6 +669,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.ld_out = m->h_ld;
                 Timed tm(m, PN_K_MOE_GATEUP, s);
                 launch_gemm(GK_MOE_SWIGLU, wt, at, g, p_gu, s);
+                if (int rc = launched("expert gate/up projection", &p_gu)) return rc;
             }
             {
                 GemmArgs g = base;
@@ -675,6 +691,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.ld_out = E;
                 Timed tm(m, PN_K_MOE_DOWN, s);
                 launch_gemm(GK_MOE_DOWN, wt, at, g, p_dn, s);
+                if (int rc = launched("expert down projection", &p_dn)) return rc;
             }
             {
                 Timed tm(m, PN_K_MOE_COMBINE, s);
@@ -700,6 +717,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         g.am_idx = (int *)(mb + m->am_idx);
         Timed tm(m, PN_K_LMHEAD, s);
         launch_gemm(GK_LOGITS, wt, at, g, p_lm, s);
+        if (int rc = launched("LM head", &p_lm)) return rc;
         record_gemm(m, PN_K_LMHEAD, GK_LOGITS, g, p_lm);
     }
     {
