@@ -158,7 +158,8 @@ struct GemmArgs {
     int K;                  // logical K
     int B;                  // dense: slots
     int nblk;               // row blocks of NTW tiles (per expert)
-    int tpw;                // row blocks per work-group
+    int tpw;                // the most row blocks a work-group takes (work-group x takes
+                            // blocks [x*nblk/gx, (x+1)*nblk/gx) of its expert)
     const float *x;         // PRO_NORM: residual [slot][K]
     const float *gain;      // PRO_NORM: [K]
     float eps;
@@ -387,7 +388,11 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     constexpr int KU = 4 / NTW;
     constexpr int PIECES = AReady<WT, AT>::PIECES;
     constexpr bool MOE = (EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN);
-    constexpr int CH = NW == 4 ? 2 : 1;        // x-prologue: 8-element chunks per thread per batch
+    // x-prologue: 8-element chunks per thread per batch (its first batch's loads
+    // go out before any weight load): for the norm prologue four rows of 4096
+    // with 16 waves, one with 8 (more would cost the occupancy of 8-wave
+    // groups), two with 4
+    constexpr int CH = (NW == 8 || PRO == PRO_CONV) ? 1 : 2;
     // A-ready staging: fragments per thread per batch, enough for A in one batch
     // up to the LDS staging limit (96 KiB) where the registers allow
     constexpr int CHA_FULL = (96 * 1024 / frag_bytes(WT) + NW * 64 - 1) / (NW * 64);
@@ -398,8 +403,9 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ex = blockIdx.z;
-    const int blk0 = blockIdx.x * g.tpw;
-    const int blk1 = min(g.nblk, blk0 + g.tpw);
+    // an equal share (+-1) of the expert's blocks per work-group
+    const int blk0 = (int)((long long)blockIdx.x * g.nblk / gridDim.x);
+    const int blk1 = (int)((long long)(blockIdx.x + 1) * g.nblk / gridDim.x);
     if (blk0 >= blk1) return;
 
     __shared__ int s_ent[kMaxSlots];   // MoE: entry (slot*n_used + k) of each gathered row
@@ -902,15 +908,14 @@ struct AttnShape {
 };
 
 // Issue the K and V loads of one wave's 16 keys k0..k0+15 (k0 a multiple of
-// 16, w-uniform).  Rows are clamped into [lo, kl], which keeps them inside
-// the page of clamp(k0, lo, kl) and inside the written window.
+// 16, w-uniform), which lie in physical page pg.  Rows are clamped into
+// [lo, kl], which keeps them inside that page (the page of clamp(k0, lo, kl))
+// and inside the written window.
 template <int D, int KV>
-__device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int k0, int lo, int kl, int kq, int dq,
-                                          int lane, u32x4 (&kr)[AttnShape<D, KV>::NKL],
+__device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int pg, int k0, int lo, int kl, int kq,
+                                          int dq, int lane, u32x4 (&kr)[AttnShape<D, KV>::NKL],
                                           typename AttnShape<D, KV>::vword (&vr)[16]) {
     typedef AttnShape<D, KV> S;
-    const int tc = min(max(k0, lo), kl);
-    const int pg = a.pt[b][tc / kPage];
     const long long row0 = ((long long)pg * a.Hk + j) * kPage;  // row of the page's first key
     const int tq = min(max(k0 + kq, lo), kl);
     const u32x4 *kp = reinterpret_cast<const u32x4 *>(
@@ -1026,9 +1031,18 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     __shared__ float wacc[NWV][G][D];
 
     const int kq = lane >> 2, dq = lane & 3;
+    // the split's pages, one chunk (= page) per lane, looked up once; chunk ci
+    // past the split's last reads the last one (its loads are clamped there)
+    const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
+    const int *ptb = a.pt[b] + kb / kPage;
+    const int vpg = ptb[min(lane, nch - 1)];
+    auto page_of = [&](int ci) -> int {
+        ci = min(ci, nch - 1);
+        return ci < 64 ? __builtin_amdgcn_readlane(vpg, ci) : ptb[ci];
+    };
     u32x4 kc[S::NKL], kn[S::NKL];
     typename S::vword vc[16], vn[16];
-    attn_load<D, KV>(a, b, j, kb + w * 16, lo, kl, kq, dq, lane, kc, vc);
+    attn_load<D, KV>(a, b, j, page_of(0), kb + w * 16, lo, kl, kq, dq, lane, kc, vc);
     {
         const f32x4 *q4 = reinterpret_cast<const f32x4 *>(a.q + (long long)b * a.Hq * D + (long long)(j * G) * D);
         for (int i = tid; i < G * D / 4; i += 256) {
@@ -1053,13 +1067,13 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
         const int k0 = kb + w * 16;
         if (k0 + 15 >= lo && k0 < ke) attn_chunk<D, KV, G>(qs, pws[w], kc, vc, k0, lo, ke, kq, dq, m, l, acc);
     } else {
-        for (int c0 = kb; c0 < ke; c0 += kAttnChunk) {
+        for (int c0 = kb, ci = 0; c0 < ke; c0 += kAttnChunk, ++ci) {
             const int k0 = c0 + w * 16;
             if constexpr (S::PREF) {
                 // next chunk in flight (clamped into the split past its end)
-                attn_load<D, KV>(a, b, j, k0 + kAttnChunk, lo, kl, kq, dq, lane, kn, vn);
+                attn_load<D, KV>(a, b, j, page_of(ci + 1), k0 + kAttnChunk, lo, kl, kq, dq, lane, kn, vn);
             } else if (c0 != kb) {
-                attn_load<D, KV>(a, b, j, k0, lo, kl, kq, dq, lane, kc, vc);
+                attn_load<D, KV>(a, b, j, page_of(ci), k0, lo, kl, kq, dq, lane, kc, vc);
             }
             if (k0 + 15 >= lo && k0 < ke) attn_chunk<D, KV, G>(qs, pws[w], kc, vc, k0, lo, ke, kq, dq, m, l, acc);
             if constexpr (S::PREF) {

@@ -87,6 +87,7 @@ struct pn_model {
     int attn_kps = 0;  // 0 = automatic
     int nw[GK_COUNT] = {8, 8, 8, 8, 8, 8, 16};  // waves per work-group of each GEMM kind
     int nw_down = 16;                       // the down projection (K = n_ff) uses GK_RESID too
+    bool nw_set = false;                    // waves chosen by the caller (PN_OPT_WAVES_*): no auto choice
     std::map<std::tuple<int, int, int, size_t>, int> occ;  // resident work-groups per CU of a GEMM variant
     size_t rope = 0, omega = 0, ssp = 0;
     int ssp_ld = 0;
@@ -140,29 +141,50 @@ struct OccKey {
     size_t lds;
 };
 
-// nblk row blocks per expert, gz experts.  Each work-group takes tpw
-// consecutive blocks, so that all work-groups are resident at once (by the
-// runtime's occupancy of this kernel) and carry equal work.
+// nblk row blocks per expert, gz experts.  As many work-groups as the
+// runtime's occupancy keeps resident at once (but no more than blocks), each
+// taking an equal share (+-1) of consecutive blocks, so that every compute
+// unit streams.  With auto_nw the wave count is the one of {nw, 16} that puts
+// more waves on a compute unit (a large A in LDS may leave room for one
+// work-group only).
 template <typename OccFn>
-Plan make_plan(int kind, int nblk, int gz, int KT, int rows, int fb, int nw, OccFn occ_of) {
-    Plan p;
-    p.nw = nw;
-    p.gz = gz;
-    p.nblk = nblk;
-    const bool norm = norm_kind(kind);
-    p.a_lds = !norm && (size_t)KT * 4 * rows * fb <= kALdsMax;
-    // direct A fragments need the larger register budget (int8 needs twice the fragment registers)
-    if (!norm && !p.a_lds) p.nw = fb == 32 ? 4 : std::min(nw, 8);
-    p.lds = lds_of(norm || p.a_lds, KT, rows, ntw_of(kind), fb, p.nw);
-    while (p.lds > kMaxLds && p.nw > 4) {  // many A rows: fewer waves leave room for them
-        p.nw /= 2;
+Plan make_plan(int kind, int nblk, int gz, int KT, int rows, int fb, int nw, OccFn occ_of, bool auto_nw = true,
+               int slots_in = 1) {
+    auto plan_for = [&](int want) {
+        Plan p;
+        p.nw = want;
+        p.gz = gz;
+        p.nblk = nblk;
+        const bool norm = norm_kind(kind);
+        p.a_lds = !norm && (size_t)KT * 4 * rows * fb <= kALdsMax;
+        // direct A fragments need the larger register budget (int8 needs twice the fragment registers)
+        if (!norm && !p.a_lds) p.nw = fb == 32 ? 4 : std::min(want, 8);
         p.lds = lds_of(norm || p.a_lds, KT, rows, ntw_of(kind), fb, p.nw);
+        while (p.lds > kMaxLds && p.nw > 4) {  // many A rows: fewer waves leave room for them
+            p.nw /= 2;
+            p.lds = lds_of(norm || p.a_lds, KT, rows, ntw_of(kind), fb, p.nw);
+        }
+        const int wpc = std::max(1, occ_of(kind, p.nw, p.a_lds, p.lds));
+        const long long slots = (long long)kCUs * wpc;
+        // as few work-groups as keep every resident slot busy with whole shares;
+        // when that leaves compute units idle, one work-group per resident slot
+        p.tpw = std::max(1, (int)cdiv((long long)nblk * gz, slots));
+        p.gx = cdiv(nblk, p.tpw);
+        if ((long long)p.gx * gz < kCUs) {
+            p.gx = (int)std::max(1LL, std::min<long long>(nblk, slots / gz));
+            p.tpw = cdiv(nblk, p.gx);
+        }
+        return std::make_pair(p, p.nw * std::min<long long>(wpc, cdiv((long long)p.gx * gz, kCUs)));
+    };
+    auto best = plan_for(nw);
+    if (auto_nw && nw != 16) {
+        // 16-wave groups also stage four input rows per prologue batch (against one
+        // with 8 waves): with several slots they win ties
+        auto alt = plan_for(16);
+        if (alt.second > best.second || (alt.second == best.second && norm_kind(kind) && slots_in > 1))
+            best = alt;
     }
-    const int wpc = std::max(1, occ_of(kind, p.nw, p.a_lds, p.lds));
-    const long long slots = (long long)kCUs * wpc;
-    p.tpw = std::max(1, cdiv((long long)nblk * gz, slots));
-    p.gx = cdiv(nblk, p.tpw);
-    return p;
+    return best.first;
 }
 
 // n_kv_head 0 stands for n_head (the pages' default for the key)
@@ -304,7 +326,7 @@ size_t layout_model(pn_model *m) {
 }
 
 // Automatic split size: aim for about this many attention work-groups per step.
-constexpr int kAttnTargetGroups = 512;
+constexpr int kAttnTargetGroups = 2048;
 
 size_t layout_state(pn_state *s) {
     const pn_model *m = s->m;
@@ -523,13 +545,13 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         m->occ[key] = n;
         return n;
     };
-    const Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of);
-    const Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of);
+    const Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of, !m->nw_set, n);
+    const Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of, !m->nw_set, n);
     const Plan p_gu = make_plan(moe ? GK_MOE_SWIGLU : GK_SWIGLU, L0.gate.n_tiles, gz, L0.gate.KT, rows, fb,
-                                m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of);
+                                m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of, !m->nw_set, n);
     const Plan p_dn = make_plan(moe ? GK_MOE_DOWN : GK_RESID, L0.down.n_tiles, gz, L0.down.KT, rows, fb,
-                                moe ? m->nw[GK_MOE_DOWN] : m->nw_down, occ_of);
-    const Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of);
+                                moe ? m->nw[GK_MOE_DOWN] : m->nw_down, occ_of, !m->nw_set);
+    const Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of, !m->nw_set, n);
     // (plans for the other kinds take one row block per tile)
 
     for (int l = 0; l < c.n_layer; ++l) {
@@ -1049,6 +1071,7 @@ int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
             case PN_OPT_WAVES_DOWN: m->nw_down = (int)value; m->nw[GK_MOE_DOWN] = (int)value; break;
             default: m->nw[GK_LOGITS] = (int)value; break;
         }
+        m->nw_set = true;
         return PN_OK;
     }
     if (option == PN_OPT_ATTN_KEYS_PER_SPLIT) {
