@@ -325,8 +325,9 @@ size_t layout_model(pn_model *m) {
     return bp.off;
 }
 
-// Automatic split size: aim for about this many attention work-groups per step.
-constexpr int kAttnTargetGroups = 2048;
+// Automatic split size: aim for about this many attention work-groups per step
+// (two per compute unit: all resident at once, and evenly spread).
+constexpr int kAttnTargetGroups = 512;
 
 size_t layout_state(pn_state *s) {
     const pn_model *m = s->m;
