@@ -18,10 +18,10 @@ void allow_lds(size_t lds) {
 }
 
 // occ >= 0: report resident work-groups per CU in *occ instead of launching
-template <int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS>
+template <int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS, bool WL>
 void go_k(const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
-    auto *k = &k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS>;
-    allow_lds<&k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS>>(lds);
+    auto *k = &k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS, WL>;
+    allow_lds<&k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS, WL>>(lds);
     if (occ) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, NW * 64, lds) != hipSuccess) n = 1;
@@ -32,33 +32,40 @@ void go_k(const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
 }
 
 template <int PRO, int EPI, int NTW, bool PAIR, int NW>
-void go_nw(bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
+void go_nw(int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
+    constexpr bool MOE = EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN;
+    if constexpr (!MOE) {
+        if (amode == A_LDS_WAVE) {
+            go_k<PRO, EPI, NTW, PAIR, NW, true, true>(g, grid, lds, s, occ);
+            return;
+        }
+    }
     if constexpr (PRO != PRO_LOAD) {
-        go_k<PRO, EPI, NTW, PAIR, NW, true>(g, grid, lds, s, occ);
+        go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
     } else {
-        if (alds) go_k<PRO, EPI, NTW, PAIR, NW, true>(g, grid, lds, s, occ);
-        else go_k<PRO, EPI, NTW, PAIR, NW, false>(g, grid, lds, s, occ);
+        if (amode != A_DIRECT) go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
+        else go_k<PRO, EPI, NTW, PAIR, NW, false, false>(g, grid, lds, s, occ);
     }
 }
 
 template <int PRO, int EPI, int NTW, bool PAIR>
-void go(int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
-    if (nw == 4) go_nw<PRO, EPI, NTW, PAIR, 4>(alds, g, grid, lds, s, occ);
-    else if (nw == 8) go_nw<PRO, EPI, NTW, PAIR, 8>(alds, g, grid, lds, s, occ);
-    else go_nw<PRO, EPI, NTW, PAIR, 16>(alds, g, grid, lds, s, occ);
+void go(int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
+    if (nw == 4) go_nw<PRO, EPI, NTW, PAIR, 4>(amode, g, grid, lds, s, occ);
+    else if (nw == 8) go_nw<PRO, EPI, NTW, PAIR, 8>(amode, g, grid, lds, s, occ);
+    else go_nw<PRO, EPI, NTW, PAIR, 16>(amode, g, grid, lds, s, occ);
 }
 
 }  // namespace
 
-void PN_NAME(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
+void PN_NAME(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
     switch (kind) {
-        case GK_QKV: go<PRO_NORM, EPI_QKV, 1, false>(nw, alds, g, grid, lds, s, occ); break;
-        case GK_RESID: go<PRO_LOAD, EPI_RESID, 1, false>(nw, alds, g, grid, lds, s, occ); break;
-        case GK_SWIGLU: go<PRO_NORM, EPI_SWIGLU, 2, true>(nw, alds, g, grid, lds, s, occ); break;
-        case GK_LOGITS: go<PRO_NORM, EPI_LOGITS, 2, false>(nw, alds, g, grid, lds, s, occ); break;
-        case GK_MOE_SWIGLU: go<PRO_NORM, EPI_MOE_SWIGLU, 2, true>(nw, alds, g, grid, lds, s, occ); break;
-        case GK_MOE_DOWN: go<PRO_LOAD, EPI_MOE_DOWN, 1, false>(nw, alds, g, grid, lds, s, occ); break;
-        case GK_O: go<PRO_CONV, EPI_RESID, 1, false>(nw, alds, g, grid, lds, s, occ); break;
+        case GK_QKV: go<PRO_NORM, EPI_QKV, 1, false>(nw, amode, g, grid, lds, s, occ); break;
+        case GK_RESID: go<PRO_LOAD, EPI_RESID, 1, false>(nw, amode, g, grid, lds, s, occ); break;
+        case GK_SWIGLU: go<PRO_NORM, EPI_SWIGLU, 2, true>(nw, amode, g, grid, lds, s, occ); break;
+        case GK_LOGITS: go<PRO_NORM, EPI_LOGITS, 2, false>(nw, amode, g, grid, lds, s, occ); break;
+        case GK_MOE_SWIGLU: go<PRO_NORM, EPI_MOE_SWIGLU, 2, true>(nw, amode, g, grid, lds, s, occ); break;
+        case GK_MOE_DOWN: go<PRO_LOAD, EPI_MOE_DOWN, 1, false>(nw, amode, g, grid, lds, s, occ); break;
+        case GK_O: go<PRO_CONV, EPI_RESID, 1, false>(nw, amode, g, grid, lds, s, occ); break;
         default: break;
     }
 }

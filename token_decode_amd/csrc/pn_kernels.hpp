@@ -362,6 +362,33 @@ __device__ __forceinline__ void put_a8(uint8_t *sa, int rows, int nb, int b, int
     }
 }
 
+// Prologue register budgets of a GEMM variant.  x-prologue: 8-element chunks
+// per thread per batch (its first batch's loads go out before any weight
+// load): for the norm prologue four rows of 4096 with 16 waves, one with 8
+// (more would cost the occupancy of 8-wave groups), two with 4.  A-ready
+// staging: fragments per thread per batch, enough for A in one batch up to the
+// LDS staging limit (96 KiB) where the registers allow.
+__host__ __device__ constexpr int gemm_ch(int nw, int pro) { return (nw == 8 || pro == PRO_CONV) ? 1 : 2; }
+__host__ __device__ constexpr int gemm_cha(int wt, int nw) {
+    return (96 * 1024 / frag_bytes(wt) + nw * 64 - 1) / (nw * 64) < 12
+               ? (96 * 1024 / frag_bytes(wt) + nw * 64 - 1) / (nw * 64)
+               : 12;
+}
+__host__ __device__ constexpr int gemm_spw(int nw) { return (kMaxSlots + nw - 1) / nw; }
+
+// Whether the wave-local prologue fits: each wave loads the A slice of its own
+// k tiles (nb slots of x for the norm / conversion prologue, rows A-ready rows
+// otherwise) in one batch of the prologue registers.
+__host__ __device__ constexpr bool gemm_wave_local_fits(int wt, int pro, int nw, int nb, int rows, int KT) {
+    const int per = (KT + nw - 1) / nw;
+    if (pro == PRO_NORM || pro == PRO_CONV) {
+        const int cpr = (per * tile_k(wt) / 8 + 63) / 64 > 1 ? (per * tile_k(wt) / 8 + 63) / 64 : 1;
+        return nb <= gemm_spw(nw) && nb * cpr <= gemm_ch(nw, pro);
+    }
+    const int cpr = (per * 4 + 63) / 64 > 1 ? (per * 4 + 63) / 64 : 1;
+    return rows * cpr <= gemm_cha(wt, nw);
+}
+
 // Skinny GEMM Y[rows][N] = A[rows][K] * W[N][K]^T for rows <= 16, fused with a
 // prologue that supplies A and an epilogue that consumes Y.
 // A row block is NTW weight tiles: with PAIR, tile blk of matrices w and w2
@@ -376,9 +403,10 @@ __device__ __forceinline__ void put_a8(uint8_t *sa, int rows, int nb, int b, int
 // the prologue; weight rounds then ping-pong between two register buffers, and
 // the next block's first rounds are in flight during this block's reduction
 // and epilogue.
-template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS>
+template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS, bool WL>
 __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     static_assert(PRO == PRO_LOAD || ALDS, "the norm prologue stages A in LDS");
+    static_assert(!WL || ALDS, "the wave-local prologue stages A in LDS");
     constexpr bool XPRO = PRO == PRO_NORM || PRO == PRO_CONV;  // A built from fp32 rows in g.x
     constexpr int NT = NW * 64;
     constexpr int TK = tile_k(WT);
@@ -392,12 +420,9 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     // go out before any weight load): for the norm prologue four rows of 4096
     // with 16 waves, one with 8 (more would cost the occupancy of 8-wave
     // groups), two with 4
-    constexpr int CH = (NW == 8 || PRO == PRO_CONV) ? 1 : 2;
-    // A-ready staging: fragments per thread per batch, enough for A in one batch
-    // up to the LDS staging limit (96 KiB) where the registers allow
-    constexpr int CHA_FULL = (96 * 1024 / frag_bytes(WT) + NW * 64 - 1) / (NW * 64);
-    constexpr int CHA = CHA_FULL < 12 ? CHA_FULL : 12;
-    constexpr int SPW = (kMaxSlots + NW - 1) / NW;  // norm prologue: slots whose sums of squares a wave reads
+    constexpr int CH = gemm_ch(NW, PRO);
+    constexpr int CHA = gemm_cha(WT, NW);
+    constexpr int SPW = gemm_spw(NW);  // norm prologue: slots whose sums of squares a wave reads
     constexpr int ES = AReady<WT, AT>::ES;
     extern __shared__ __align__(16) uint8_t smem[];
 
@@ -436,14 +461,37 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     // with a fixed count (addresses clamped, values selected), so that waiting
     // for them never waits for weights
     const int n8 = g.KT * TK / 8;  // 8-element chunks per A row
+    // the k tiles of this wave (the waves split K evenly; the last ones may be short or empty)
+    const int per = (g.KT + NW - 1) / NW;
+    const int wt0 = min(g.KT, wave * per);
+    const int wt1 = min(g.KT, wt0 + per);
+    // Wave-local prologue: when the A slice of this wave's k tiles fits the
+    // registers below, each wave loads and stages only that slice (and works out
+    // the norm factors itself), so no wave waits at a work-group barrier for
+    // another wave's prologue loads.  The condition is uniform over the group.
+    // Load c of a lane covers A row c / cpr, items (c % cpr) * 64 + lane of the
+    // row's slice (8-element chunks of x, or A fragments); the divisions are
+    // scalar.
+    const int nchw = (wt1 - wt0) * TK / 8;  // 8-element chunks of this wave's tiles, per A row
+    const int nfw = (wt1 - wt0) * 4;        // A fragments of this wave's tiles, per A row
+    const int cpr = XPRO ? max(1, (per * TK / 8 + 63) / 64) : max(1, (per * 4 + 63) / 64);
+    constexpr bool wl = WL;
     float xv[CH][8], gv[CH][8];
     float ssv[SPW][8];
     u32x4 st0[CHA], st1[CHA];
     if constexpr (XPRO) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int ch = tid + c * NT;
-            const int b = ch / n8, k0 = (ch - b * n8) * 8;
+            int b, k0;
+            if constexpr (wl) {
+                const int j = (c % cpr) * 64 + lane;
+                b = j < nchw ? c / cpr : nb;
+                k0 = wt0 * TK + j * 8;
+            } else {
+                const int ch = tid + c * NT;
+                b = ch / n8;
+                k0 = (ch - b * n8) * 8;
+            }
             const bool in = b < nb && k0 < g.K;
             const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
             const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
@@ -467,10 +515,10 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     }
     if constexpr (PRO == PRO_NORM) {
         // the per-16-element sums of squares of slots wave, wave+NW, ... (at most
-        // 512 of them: K <= 8192)
+        // 512 of them: K <= 8192); wave-local: of every slot
 #pragma unroll
         for (int q = 0; q < SPW; ++q) {
-            const int b = wave + q * NW;
+            const int b = WL ? q : wave + q * NW;
             const int sb = b < nb ? (MOE ? s_ent[b] / g.n_used : b) : 0;
             const float *sp = g.ssp + (long long)sb * g.ssp_ld;
 #pragma unroll
@@ -481,8 +529,16 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         const int chunksA = g.KT * 4;
 #pragma unroll
         for (int c = 0; c < CHA; ++c) {
-            const int idx = tid + c * NT;
-            const int m = idx / chunksA, f = idx - m * chunksA;
+            int m, f;
+            if constexpr (wl) {
+                const int j = (c % cpr) * 64 + lane;
+                m = j < nfw ? c / cpr : rows;
+                f = wt0 * 4 + j;
+            } else {
+                const int idx = tid + c * NT;
+                m = idx / chunksA;
+                f = idx - m * chunksA;
+            }
             const bool in = m < rows;
             const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
             const long long r = MOE ? s_ent[b] : b;
@@ -538,9 +594,6 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     EpIn epc = epi_load(blk0);
 
     // ---- phase 2: the first block's first two weight rounds (and direct A fragments)
-    const int per = (g.KT + NW - 1) / NW;
-    const int wt0 = min(g.KT, wave * per);
-    const int wt1 = min(g.KT, wt0 + per);
     const int last = max(wt1 - 1, 0);             // clamp target of every load of this wave
     const int rounds = (wt1 - wt0 + KU - 1) / KU;  // rounds with at least one tile
     const uint8_t *mbase[NTW];
@@ -582,35 +635,36 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
 
     // ---- phase 3: the prologue's arithmetic
     if constexpr (XPRO) {
-        if constexpr (PRO == PRO_NORM) {
+        if constexpr (wl) {
+            // this wave's tiles of every slot: norm factors from all the slot's
+            // sums of squares (same order as below), then straight into LDS
+            float ri[SPW];
 #pragma unroll
             for (int q = 0; q < SPW; ++q) {
-                const int b = wave + q * NW;
-                if (b < nb) {
-                    // fixed summation order: per lane, then the wave reduction
-                    float v[8];
+                ri[q] = 1.f;
+                if constexpr (PRO == PRO_NORM) {
+                    if (q < nb) {
+                        float v[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) v[u] = lane + 64 * u < g.ssp_n ? ssv[q][u] : 0.f;
-                    float ss = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-                    ss = wave_sum(ss);
-                    if (lane == 0) s_rinv[b] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
+                        for (int u = 0; u < 8; ++u) v[u] = lane + 64 * u < g.ssp_n ? ssv[q][u] : 0.f;
+                        float ss = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+                        ss = wave_sum(ss);
+                        ri[q] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
+                    }
                 }
             }
-            lds_barrier();
-        }
-        // batch 0 comes from the phase-1 registers; later batches (more rows
-        // than one batch covers) load their own, after the weights
-        auto stage_x = [&](int base) {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int ch = base + tid + c * NT;
-                const int b = ch / n8, k0 = (ch - b * n8) * 8;
-                if (b >= nb) continue;
+                const int b = c / cpr, j = (c % cpr) * 64 + lane;
+                if (b >= nb || j >= nchw) continue;
+                const int k0 = wt0 * TK + j * 8;
+                float rb = ri[0];
+#pragma unroll
+                for (int q = 1; q < SPW; ++q) rb = b == q ? ri[q] : rb;
                 float v[8];
                 if constexpr (PRO == PRO_NORM) {
-                    const float ri = s_rinv[b];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? (xv[c][e] * ri) * gv[c][e] : 0.f;
+                    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? (xv[c][e] * rb) * gv[c][e] : 0.f;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? xv[c][e] : 0.f;
@@ -621,59 +675,113 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 }
                 put_a8<WT, AT>(sa, rows, nb, b, k0, v);
             }
-        };
-        stage_x(0);
-        for (int base = CH * NT; base < nb * n8; base += CH * NT) {
+        } else {
+            if constexpr (PRO == PRO_NORM) {
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int ch = base + tid + c * NT;
-                const int b = ch / n8, k0 = (ch - b * n8) * 8;
-                const bool in = b < nb && k0 < g.K;
-                const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
-                const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
-                const f32x4 x0 = xp[0], x1 = xp[1];
+                for (int q = 0; q < SPW; ++q) {
+                    const int b = wave + q * NW;
+                    if (b < nb) {
+                        // fixed summation order: per lane, then the wave reduction
+                        float v[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { xv[c][e] = x0[e]; xv[c][4 + e] = x1[e]; }
-                if constexpr (PRO == PRO_NORM) {
-                    const f32x4 *gp = reinterpret_cast<const f32x4 *>(g.gain + (in ? k0 : 0));
-                    const f32x4 g0 = gp[0], g1 = gp[1];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { gv[c][e] = g0[e]; gv[c][4 + e] = g1[e]; }
+                        for (int u = 0; u < 8; ++u) v[u] = lane + 64 * u < g.ssp_n ? ssv[q][u] : 0.f;
+                        float ss = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+                        ss = wave_sum(ss);
+                        if (lane == 0) s_rinv[b] = 1.0f / sqrtf(ss / (float)g.K + g.eps);
+                    }
                 }
+                lds_barrier();
             }
-            stage_x(base);
+            // batch 0 comes from the phase-1 registers; later batches (more rows
+            // than one batch covers) load their own, after the weights
+            auto stage_x = [&](int base) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int ch = base + tid + c * NT;
+                    const int b = ch / n8, k0 = (ch - b * n8) * 8;
+                    if (b >= nb) continue;
+                    float v[8];
+                    if constexpr (PRO == PRO_NORM) {
+                        const float ri = s_rinv[b];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? (xv[c][e] * ri) * gv[c][e] : 0.f;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? xv[c][e] : 0.f;
+                    }
+                    if constexpr (AT == AT_BF16) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = bf16_round(v[e]);
+                    }
+                    put_a8<WT, AT>(sa, rows, nb, b, k0, v);
+                }
+            };
+            stage_x(0);
+            for (int base = CH * NT; base < nb * n8; base += CH * NT) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int ch = base + tid + c * NT;
+                    const int b = ch / n8, k0 = (ch - b * n8) * 8;
+                    const bool in = b < nb && k0 < g.K;
+                    const int sb = in ? (MOE ? s_ent[b] / g.n_used : b) : 0;
+                    const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)sb * g.K + (in ? k0 : 0));
+                    const f32x4 x0 = xp[0], x1 = xp[1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { xv[c][e] = x0[e]; xv[c][4 + e] = x1[e]; }
+                    if constexpr (PRO == PRO_NORM) {
+                        const f32x4 *gp = reinterpret_cast<const f32x4 *>(g.gain + (in ? k0 : 0));
+                        const f32x4 g0 = gp[0], g1 = gp[1];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { gv[c][e] = g0[e]; gv[c][4 + e] = g1[e]; }
+                    }
+                }
+                stage_x(base);
+            }
+            lds_barrier();
         }
-        lds_barrier();
     } else if constexpr (ALDS) {
-        const int chunksA = g.KT * 4;  // fragments per A row
-        auto stage_a = [&](int base) {
+        if constexpr (wl) {
+            // this wave's fragments of every row, straight into LDS
 #pragma unroll
             for (int c = 0; c < CHA; ++c) {
-                const int idx = base + tid + c * NT;
-                const int m = idx / chunksA, f = idx - m * chunksA;
-                if (m >= rows) continue;
+                const int m = c / cpr, j = (c % cpr) * 64 + lane;
+                if (m >= rows || j >= nfw) continue;
+                const int f = wt0 * 4 + j;
                 uint8_t *dst = sa + (f * rows + m) * FB;
                 *reinterpret_cast<u32x4 *>(dst) = st0[c];
                 if constexpr (WT == WT_I8) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
             }
-        };
-        stage_a(0);  // from the phase-1 registers
-        for (int base = CHA * NT; base < rows * chunksA; base += CHA * NT) {
+        } else {
+            const int chunksA = g.KT * 4;  // fragments per A row
+            auto stage_a = [&](int base) {
 #pragma unroll
-            for (int c = 0; c < CHA; ++c) {
-                const int idx = base + tid + c * NT;
-                const int m = idx / chunksA, f = idx - m * chunksA;
-                const bool in = m < rows;
-                const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
-                const long long r = MOE ? s_ent[b] : b;
-                const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
-                                     ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
-                st0[c] = *reinterpret_cast<const u32x4 *>(src);
-                if constexpr (WT == WT_I8) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
+                for (int c = 0; c < CHA; ++c) {
+                    const int idx = base + tid + c * NT;
+                    const int m = idx / chunksA, f = idx - m * chunksA;
+                    if (m >= rows) continue;
+                    uint8_t *dst = sa + (f * rows + m) * FB;
+                    *reinterpret_cast<u32x4 *>(dst) = st0[c];
+                    if constexpr (WT == WT_I8) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
+                }
+            };
+            stage_a(0);  // from the phase-1 registers
+            for (int base = CHA * NT; base < rows * chunksA; base += CHA * NT) {
+#pragma unroll
+                for (int c = 0; c < CHA; ++c) {
+                    const int idx = base + tid + c * NT;
+                    const int m = idx / chunksA, f = idx - m * chunksA;
+                    const bool in = m < rows;
+                    const int s = in ? m / nb : 0, b = in ? m - s * nb : 0;
+                    const long long r = MOE ? s_ent[b] : b;
+                    const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
+                                         ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
+                    st0[c] = *reinterpret_cast<const u32x4 *>(src);
+                    if constexpr (WT == WT_I8) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
+                }
+                stage_a(base);
             }
-            stage_a(base);
+            lds_barrier();
         }
-        lds_barrier();
     }
 
     for (int blk = blk0; blk < blk1; ++blk) {

@@ -23,17 +23,20 @@ enum GemmKind {
 constexpr size_t kMaxLds = 159 * 1024;
 
 // Defined once per (weight type, activation type) in pn_gemm.hip; nw = waves
-// per work-group (4, 8 or 16); alds = stage an A-ready input in LDS.  With occ
-// non-null nothing is launched: *occ receives the resident work-groups per CU.
-void launch_gemm_f32_f32(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+// per work-group (4, 8 or 16); amode: A_DIRECT reads an A-ready input straight
+// from memory, A_LDS stages A in LDS, A_LDS_WAVE stages it per wave (the
+// wave-local prologue; not for MoE kinds).  With occ non-null nothing is
+// launched: *occ receives the resident work-groups per CU.
+enum AMode { A_DIRECT = 0, A_LDS = 1, A_LDS_WAVE = 2 };
+void launch_gemm_f32_f32(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
                          int *occ);
-void launch_gemm_f32_bf16(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+void launch_gemm_f32_bf16(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
                          int *occ);
-void launch_gemm_bf16_f32(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+void launch_gemm_bf16_f32(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
                          int *occ);
-void launch_gemm_bf16_bf16(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+void launch_gemm_bf16_bf16(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
                          int *occ);
-void launch_gemm_i8_bf16(int kind, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+void launch_gemm_i8_bf16(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
                          int *occ);
 
 // Defined once per (head_dim, KV type) in pn_attn.hip: attention with G query

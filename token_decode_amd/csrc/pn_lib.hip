@@ -378,20 +378,33 @@ void pack(const void *src, int N, int K, int wt, const Mat &mt, int tile_row0, u
 
 // ---------------------------------------------------------------- launch dispatch
 
-void gemm_entry(int kind, int wt, int at, int nw, bool alds, const GemmArgs &g, dim3 grid, size_t lds,
+void gemm_entry(int kind, int wt, int at, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds,
                 hipStream_t s, int *occ) {
-    if (wt == PN_BF16 && at == PN_F32) launch_gemm_bf16_f32(kind, nw, alds, g, grid, lds, s, occ);
-    else if (wt == PN_BF16) launch_gemm_bf16_bf16(kind, nw, alds, g, grid, lds, s, occ);
-    else if (wt == PN_F32 && at == PN_F32) launch_gemm_f32_f32(kind, nw, alds, g, grid, lds, s, occ);
-    else if (wt == PN_F32) launch_gemm_f32_bf16(kind, nw, alds, g, grid, lds, s, occ);
-    else launch_gemm_i8_bf16(kind, nw, alds, g, grid, lds, s, occ);
+    if (wt == PN_BF16 && at == PN_F32) launch_gemm_bf16_f32(kind, nw, amode, g, grid, lds, s, occ);
+    else if (wt == PN_BF16) launch_gemm_bf16_bf16(kind, nw, amode, g, grid, lds, s, occ);
+    else if (wt == PN_F32 && at == PN_F32) launch_gemm_f32_f32(kind, nw, amode, g, grid, lds, s, occ);
+    else if (wt == PN_F32) launch_gemm_f32_bf16(kind, nw, amode, g, grid, lds, s, occ);
+    else launch_gemm_i8_bf16(kind, nw, amode, g, grid, lds, s, occ);
+}
+
+int pro_of(int kind) {
+    if (kind == GK_RESID || kind == GK_MOE_DOWN) return PRO_LOAD;
+    return kind == GK_O ? PRO_CONV : PRO_NORM;
 }
 
 void launch_gemm(int kind, int wt, int at, GemmArgs g, const Plan &p, hipStream_t s) {
     const dim3 grid(p.gx, 1, p.gz);
     g.nblk = p.nblk;
     g.tpw = p.tpw;
-    gemm_entry(kind, wt, at, p.nw, p.a_lds, g, grid, p.lds, s, nullptr);
+    // the wave-local prologue where one batch of its registers holds a wave's
+    // A slice (few slots); MoE kinds gather their rows on the device
+    const bool moe = kind == GK_MOE_SWIGLU || kind == GK_MOE_DOWN;
+    const int pieces = (wt == PN_BF16 && at == PN_F32) ? 3 : 1;
+    const int pro = pro_of(kind);
+    int amode = p.a_lds || pro != PRO_LOAD ? A_LDS : A_DIRECT;
+    if (!moe && amode == A_LDS && gemm_wave_local_fits(wt, pro, p.nw, g.B, g.B * pieces, g.KT))
+        amode = A_LDS_WAVE;
+    gemm_entry(kind, wt, at, p.nw, amode, g, grid, p.lds, s, nullptr);
 }
 
 void record_gemm(pn_model *m, int cls, int kind, const GemmArgs &g, const Plan &p) {
@@ -542,7 +555,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         if (it != m->occ.end()) return it->second;
         int n = 1;
         GemmArgs none{};
-        gemm_entry(kind, wt, at, nw, alds, none, dim3(1), lds, s, &n);
+        gemm_entry(kind, wt, at, nw, alds ? A_LDS : A_DIRECT, none, dim3(1), lds, s, &n);
         m->occ[key] = n;
         return n;
     };
