@@ -201,10 +201,14 @@ enum {
  *                              handled by one attention work-group (raised
  *                              where a state's split scratch, at most 256
  *                              splits, needs it);
+ *  PN_OPT_ATTN_KERNEL          attention over a bf16 cache: 0 = automatic,
+ *                              1 = vector units, 2 = matrix cores (an fp32
+ *                              cache always uses the vector units);
  *  PN_OPT_WAVES_*              waves per work-group (4, 8 or 16) of the QKV,
  *                              O, gate/up, down and LM-head projections. */
 enum {
     PN_OPT_ATTN_KEYS_PER_SPLIT = 1,
+    PN_OPT_ATTN_KERNEL = 2,
     PN_OPT_WAVES_QKV = 10, PN_OPT_WAVES_O, PN_OPT_WAVES_GATEUP, PN_OPT_WAVES_DOWN, PN_OPT_WAVES_LMHEAD
 };
 int pn_model_set_option(pn_model *m, int32_t option, int64_t value);

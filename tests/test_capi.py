@@ -109,6 +109,8 @@ def test_init_rejects_bad_buffers_without_device_work():
         assert L.pn_forward_batch(h, arr, 2, ctypes.c_void_p(1 << 22), None, None, None) == C.PN_EINVAL
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KEYS_PER_SPLIT, 100) == C.PN_EINVAL
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KEYS_PER_SPLIT, 512) == 0
+        assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KERNEL, 3) == C.PN_EINVAL
+        assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KERNEL, 2) == 0
         assert L.pn_profile_begin(h, 99) == C.PN_EINVAL
         assert L.pn_profile_replay(h, C.PN_K_GATEUP, 4, None) == C.PN_EINVAL  # nothing recorded yet
         assert L.pn_profile_replay(h, 99, 4, None) == C.PN_EINVAL

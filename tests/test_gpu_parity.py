@@ -110,6 +110,29 @@ def test_attention_split_sizes(kps):
         log("  kps %d kv %d: worst rel L2 %.2e near %d" % (kps, kv, worst, near))
 
 
+@pytest.mark.parametrize("kind", [1, 2], ids=["vector", "matrix"])
+@pytest.mark.parametrize("kps", [0, 64, 256])
+def test_attention_kernels_bf16_cache(kind, kps):
+    """Both attention kernels over a bf16 cache (vector units, matrix cores),
+    automatic and fixed split sizes: batch 1 with a window and head_dim 64 /
+    128, and five batched slots, against the oracle."""
+    from token_decode_amd import _capi as C
+    wl = ragged("attn-kind%d-kps%d" % (kind, kps), n_head=8, n_kv_head=2, head_dim=64, w_dtype=synth.BF16,
+                kv_dtype=synth.BF16, act_dtype=synth.F32, sliding_window=333, seed=47)
+    p = Pair(wl)
+    p.dm.set_option(C.PN_OPT_ATTN_KERNEL, kind)
+    p.dm.set_option(C.PN_OPT_ATTN_KEYS_PER_SPLIT, kps)
+    worst, near, n = run_single(p, 700, [21, 22], 2)
+    log("  kind %d kps %d d64 window: worst rel L2 %.2e near %d" % (kind, kps, worst, near))
+    wl = ragged("attn-kind%d-kps%d-b" % (kind, kps), n_head=4, n_kv_head=2, head_dim=128, w_dtype=synth.BF16,
+                kv_dtype=synth.BF16, act_dtype=synth.BF16, seed=49)
+    p = Pair(wl, max_batch=5)
+    p.dm.set_option(C.PN_OPT_ATTN_KERNEL, kind)
+    p.dm.set_option(C.PN_OPT_ATTN_KEYS_PER_SPLIT, kps)
+    worst, near = run_batch(p, [0, 15, 63, 64, 900], 2)
+    log("  kind %d kps %d d128 batch: worst rel L2 %.2e near %d" % (kind, kps, worst, near))
+
+
 def test_batched_16_slots_large_lds():
     """16 slots with n_embd 2048: several GEMM variants stage more than 64 KiB of
     A in LDS in the same step (each needs its own launch attribute)."""

@@ -31,6 +31,24 @@ constexpr int kMaxSlots = 16;  // sequences in one batched step
 constexpr int kNW = 16;        // waves per GEMM work-group
 constexpr int kMaxG = 8;       // query heads per KV head
 
+// Layout of one KV head's block of a page (kPage keys x D dims).  An fp32
+// cache keeps K by rows [key][dim] and V by columns [dim][key].  A bf16 cache
+// keeps both in the operand order of the attention's matrix-core steps, so
+// that each load instruction of a wave reads one contiguous run:
+//   K: [key / 16][dim / 32][((dim % 32) / 8) * 16 + key % 16][dim % 8]
+//      (a 16x16x32 A fragment per 16 keys and 32 dims, 1 KiB),
+//   V: [key / 16][dim / 16][((key % 16) / 4) * 16 + dim % 16][key % 4]
+//      (a 16x16x16 A fragment per 16 keys and 16 dims, 512 B).
+// Offsets are in elements from the start of the head's block.
+__host__ __device__ constexpr long long kv_k_off(bool tiled, int key, int d, int D) {
+    return tiled ? ((long long)((key / 16) * (D / 32) + d / 32) * 64 + ((d % 32) / 8) * 16 + key % 16) * 8 + d % 8
+                 : (long long)key * D + d;
+}
+__host__ __device__ constexpr long long kv_v_off(bool tiled, int key, int d, int D) {
+    return tiled ? ((long long)((key / 16) * (D / 16) + d / 16) * 64 + ((key % 16) / 4) * 16 + d % 16) * 4 + key % 4
+                 : (long long)d * kPage + key;
+}
+
 enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2 };
 enum AType { AT_F32 = 0, AT_BF16 = 1 };
 enum Pro { PRO_NORM = 0, PRO_LOAD = 1, PRO_CONV = 2 };  // CONV: A = round_act(fp32 rows), no norm
@@ -38,6 +56,8 @@ enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_MOE_S
            EPI_MOE_DOWN = 5 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -856,15 +876,30 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                         const int rr = isk ? r0 - hd : r0 - hd - kd;
                         const int j = rr / g.D, dd = rr % g.D;
                         if (isk) rope_pair(y0, y1, epc.cs);
-                        const int page = epc.page;
-                        const long long off = (((long long)page * g.Hk + j) * kPage + (pos % kPage)) * g.D + dd;
-                        char *base = isk ? g.kvk[b] : g.kvv[b];
-                        if (g.kv_es == 2) {
-                            const uint32_t pk = bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
-                            *reinterpret_cast<uint32_t *>(base + off * 2) = pk;
+                        // the head's block of the page (layouts as kv_k_off / kv_v_off)
+                        const long long hb = ((long long)epc.page * g.Hk + j) * kPage * g.D;
+                        const int t = pos % kPage;
+                        const bool tiled = g.kv_es == 2;
+                        if (isk) {
+                            // dd, dd + 1 are adjacent in both K layouts
+                            const long long off = hb + kv_k_off(tiled, t, dd, g.D);
+                            if (tiled) {
+                                const uint32_t pk = bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
+                                *reinterpret_cast<uint32_t *>(g.kvk[b] + off * 2) = pk;
+                            } else {
+                                reinterpret_cast<float *>(g.kvk[b])[off] = y0;
+                                reinterpret_cast<float *>(g.kvk[b])[off + 1] = y1;
+                            }
                         } else {
-                            reinterpret_cast<float *>(base)[off] = y0;
-                            reinterpret_cast<float *>(base)[off + 1] = y1;
+                            const long long o0 = hb + kv_v_off(tiled, t, dd, g.D);
+                            const long long o1 = hb + kv_v_off(tiled, t, dd + 1, g.D);
+                            if (tiled) {
+                                reinterpret_cast<uint16_t *>(g.kvv[b])[o0] = (uint16_t)bf16_rne_bits(y0);
+                                reinterpret_cast<uint16_t *>(g.kvv[b])[o1] = (uint16_t)bf16_rne_bits(y1);
+                            } else {
+                                reinterpret_cast<float *>(g.kvv[b])[o0] = y0;
+                                reinterpret_cast<float *>(g.kvv[b])[o1] = y1;
+                            }
                         }
                     }
                 }
@@ -960,6 +995,7 @@ struct AttnArgs {
     const char *kvk[kMaxSlots], *kvv[kMaxSlots];
     const int *pt[kMaxSlots];
     float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max (base 2), sum, 2 pad, unnormalised output
+    int kind;                // bf16 cache: 0 = vector units (k_attn), 1 = matrix cores (k_attn_mfma)
 };
 
 // Split-K flash decode for G query heads per KV head.  Decode attention
@@ -1016,26 +1052,65 @@ struct AttnShape {
 };
 
 // Issue the K and V loads of one wave's 16 keys k0..k0+15 (k0 a multiple of
-// 16, w-uniform), which lie in physical page pg.  Rows are clamped into
-// [lo, kl], which keeps them inside that page (the page of clamp(k0, lo, kl))
-// and inside the written window.
+// 16, w-uniform), which lie in physical page pg.  K rows are clamped into
+// [lo, kl], which keeps them inside that page and inside the written window;
+// a lane gathers the 16 keys of each of its V dimensions (one run for an fp32
+// cache, four 8-byte pieces for a bf16 one), and keys outside [lo, kl] read
+// zeros (their weights are 0, and 0 * NaN would not be).
 template <int D, int KV>
 __device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int pg, int k0, int lo, int kl, int kq,
                                           int dq, int lane, u32x4 (&kr)[AttnShape<D, KV>::NKL],
                                           typename AttnShape<D, KV>::vword (&vr)[16]) {
     typedef AttnShape<D, KV> S;
-    const long long row0 = ((long long)pg * a.Hk + j) * kPage;  // row of the page's first key
+    const long long hb = ((long long)pg * a.Hk + j) * kPage * D;  // the head's block of the page
     const int tq = min(max(k0 + kq, lo), kl);
-    const u32x4 *kp = reinterpret_cast<const u32x4 *>(
-        a.kvk[b] + ((row0 + tq % kPage) * D + dq * S::KVEC) * S::ES);
+    const int dl = (lane < S::VL ? lane : 0) * S::VE;
+    uint32_t col[S::VE][16];
+    if constexpr (KV == 1) {
+        // tiled (kv_k_off / kv_v_off): piece dq + 4c of key row tq % 16 is 16 bytes of
+        // the group's 1 KiB step c; the 4 keys 4q..4q+3 of a dim are 8 contiguous bytes
+        const uint8_t *gk = reinterpret_cast<const uint8_t *>(a.kvk[b]) + (hb + (long long)(k0 % kPage) * D) * 2;
 #pragma unroll
-    for (int c = 0; c < S::NKL; ++c) kr[c] = kp[4 * c];
-    const typename S::vword *vb =
-        reinterpret_cast<const typename S::vword *>(a.kvv[b]) + (lane < S::VL ? lane : 0);
+        for (int c = 0; c < S::NKL; ++c)
+            kr[c] = *reinterpret_cast<const u32x4 *>(gk + c * 1024 + (dq * 16 + tq % 16) * 16);
+        const uint8_t *gv = reinterpret_cast<const uint8_t *>(a.kvv[b]) + (hb + (long long)(k0 % kPage) * D) * 2;
+#pragma unroll
+        for (int e = 0; e < S::VE; ++e) {
+            const int d = dl + e;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 t = *reinterpret_cast<const u32x2 *>(gv + (((d / 16) * 64 + q * 16 + d % 16) * 4) * 2);
+                col[e][4 * q] = t[0] & 0xFFFFu;
+                col[e][4 * q + 1] = t[0] >> 16;
+                col[e][4 * q + 2] = t[1] & 0xFFFFu;
+                col[e][4 * q + 3] = t[1] >> 16;
+            }
+        }
+    } else {
+        // rows for K, columns for V
+        const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.kvk[b] + (hb + (long long)(tq % kPage) * D + dq * S::KVEC) * S::ES);
+#pragma unroll
+        for (int c = 0; c < S::NKL; ++c) kr[c] = kp[4 * c];
+        constexpr int NV = 16 * S::ES / 16;  // 16-byte loads per column run
+#pragma unroll
+        for (int e = 0; e < S::VE; ++e) {
+            const u32x4 *vp = reinterpret_cast<const u32x4 *>(
+                a.kvv[b] + (hb + (long long)(dl + e) * kPage + k0 % kPage) * S::ES);
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                const u32x4 t = vp[c];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) col[e][4 * c + q] = t[q];
+            }
+        }
+    }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-        const int t = min(max(k0 + u, lo), kl);
-        vr[u] = vb[(row0 + t % kPage) * (D / S::VE)];
+        const bool in = k0 + u >= lo && k0 + u <= kl;
+        unsigned long long w = 0;
+#pragma unroll
+        for (int e = 0; e < S::VE; ++e) w |= (unsigned long long)(in ? col[e][u] : 0u) << (8 * S::ES * e);
+        vr[u] = (typename S::vword)w;
     }
 }
 
@@ -1202,6 +1277,226 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int e = 0; e < S::VE; ++e) wacc[w][g][lane * S::VE + e] = acc[g][e];
+    lds_barrier();
+
+    const int ns = a.nsplit[b];
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int g = idx / D, d = idx % D;
+        float M = wm[0][g];
+#pragma unroll
+        for (int x = 1; x < NWV; ++x) M = fmaxf(M, wm[x][g]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int x = 0; x < NWV; ++x) {
+            const float f = exp2_fast(wm[x][g] - M);
+            L += wl[x][g] * f;
+            A += wacc[x][g][d] * f;
+        }
+        if (ns == 1) {
+            a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A / L;
+        } else {
+            float *pp = a.part[b] + (((long long)j * a.s_cap[b] + s) * G + g) * (D + 4);
+            if (d == 0) { pp[0] = M; pp[1] = L; }
+            pp[4 + d] = A;
+        }
+    }
+}
+
+// The three bf16 pieces of x: x == p0 + p1 + p2 exactly (24 mantissa bits).
+__device__ __forceinline__ void bf16_pieces(float x, uint32_t &b0, uint32_t &b1, uint32_t &b2) {
+    const float p0 = bf16_round(x);
+    const float r1 = x - p0;
+    const float p1 = bf16_round(r1);
+    const float p2 = bf16_round(r1 - p1);
+    b0 = bf16_rne_bits(p0);
+    b1 = bf16_rne_bits(p1);
+    b2 = bf16_rne_bits(p2);
+}
+
+// The same split-K flash decode as k_attn for a bf16 cache, on the matrix
+// cores.  A wave's 16 keys form one 16x16 score tile per KV head:
+//   S^T[key][g] = sum_d K[key][d] * q[g][d]
+// with K fragments as the A operand (16x16x32 steps over d; the cache stores
+// them in that order, see kv_k_off, so each load reads 1 KiB) and the scaled fp32
+// query split into three exact bf16 pieces that the same accumulator adds
+// (the products are exact, the sums fp32).  The tile leaves lane l holding
+// head l%16 and keys 4*(l/16)..+3, which is the B-operand layout of a
+// 16x16x16 step over keys, so the softmax stays in the lane and the weights
+// (again three bf16 pieces) feed
+//   O^T[d][g] += sum_key V^T[d][key] * P^T[key][g]
+// with V fragments (stored in operand order too, see kv_v_off: 512 B per
+// load) as the A operand; keys of a fragment outside the window are zeroed
+// (their weight is 0, and 0 * NaN is not) and rows of K outside it are masked
+// after the scores.  The output tile's column is again the lane's head, the one whose
+// running max the lane keeps (its running sum covers the lane's own keys and
+// is added over the four lanes of a head at the end).  Query heads past G are
+// zero columns.  The query pieces sit in LDS; K and V rotate through three
+// register buffers, so two chunks are in flight while one is scored.
+template <int D, int G>
+__global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
+    static_assert(G <= 16, "one 16-column tile of query heads");
+    constexpr int NWV = kAttnWaves;
+    constexpr int KS = D / 32;  // 16x16x32 steps over d
+    constexpr int DT = D / 16;  // 16-row output tiles over d
+    const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    if (s >= a.nsplit[b]) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int lo = a.lo[b];
+    const int kb = a.origin[b] + s * a.kps;
+    const int ke = min(kb + a.kps, a.pos[b] + 1);
+    const int kl = ke - 1;
+
+    __shared__ __align__(16) u32x4 qsh[3][KS][64];  // B operands of the query pieces, by lane
+    __shared__ float wm[NWV][16], wl[NWV][16];
+    __shared__ float wacc[NWV][G][D];
+
+    // the split's pages, one chunk (= page) per lane, looked up once
+    const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
+    const int *ptb = a.pt[b] + kb / kPage;
+    const int vpg = ptb[min(lane, nch - 1)];
+    auto page_of = [&](int ci) -> int {
+        ci = min(ci, nch - 1);
+        return ci < 64 ? __builtin_amdgcn_readlane(vpg, ci) : ptb[ci];
+    };
+    // K fragments of wave chunk ci (keys k0..k0+15, rows clamped into [lo, kl],
+    // inside the chunk's page; chunks past the split's last re-read the last) and
+    // V column fragments (keys 4*q4..+3 of dims dt*16 + r16)
+    auto load = [&](int ci, u32x4 (&kr)[KS], u32x2 (&vr)[DT]) {
+        ci = min(ci, nch - 1);
+        // the wave's 16-key group of the page's head block (16 * D elements of K and of V)
+        const long long gb = (((long long)page_of(ci) * a.Hk + j) * kPage + w * 16) * D * 2;
+        const uint8_t *kp = reinterpret_cast<const uint8_t *>(a.kvk[b]) + gb + lane * 16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kr[ks] = *reinterpret_cast<const u32x4 *>(kp + ks * 1024);
+        const uint8_t *vp = reinterpret_cast<const uint8_t *>(a.kvv[b]) + gb + lane * 8;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vr[dt] = *reinterpret_cast<const u32x2 *>(vp + dt * 512);
+    };
+    u32x4 k0r[KS], k1r[KS], k2r[KS];
+    u32x2 v0r[DT], v1r[DT], v2r[DT];
+    load(0, k0r, v0r);
+    if (nch > 1) load(1, k1r, v1r);  // (split-uniform)
+
+    // the query pieces: wave w fills steps w, w+4, ... (lane l: head r16, d = ks*32 + 8*q4..+7)
+    for (int ks = w; ks < KS; ks += NWV) {
+        const float *qp = a.q + (long long)b * a.Hq * D + (long long)(j * G + min(r16, G - 1)) * D + ks * 32 + 8 * q4;
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(qp);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(qp + 4);
+        const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        u32x4 p0, p1, p2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t lo0, lo1, lo2, hi0, hi1, hi2;
+            bf16_pieces(r16 < G ? xv[2 * e] * a.scale : 0.f, lo0, lo1, lo2);
+            bf16_pieces(r16 < G ? xv[2 * e + 1] * a.scale : 0.f, hi0, hi1, hi2);
+            p0[e] = lo0 | (hi0 << 16);
+            p1[e] = lo1 | (hi1 << 16);
+            p2[e] = lo2 | (hi2 << 16);
+        }
+        qsh[0][ks][lane] = p0;
+        qsh[1][ks][lane] = p1;
+        qsh[2][ks][lane] = p2;
+    }
+    lds_barrier();
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // one wave chunk: keys k0..k0+15 with at least one in [lo, ke) (none past the split)
+    auto chunk = [&](int ci, const u32x4 (&kr)[KS], const u32x2 (&vr)[DT]) {
+        const int k0 = kb + ci * kAttnChunk + w * 16;
+        if (ci >= nch || k0 + 15 < lo || k0 >= ke) return;
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[ks]),
+                                                             __builtin_bit_cast(bf16x8, qsh[p][ks][lane]), sc, 0, 0,
+                                                             0);
+        const int key0 = k0 + 4 * q4;
+        float sv[4];
+        bool vin[4];
+        float cm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            vin[i] = key0 + i >= lo && key0 + i < ke;
+            sv[i] = vin[i] ? sc[i] : -INFINITY;
+            cm = fmaxf(cm, sv[i]);
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float mn = fmaxf(m, cm);
+        const float f = exp2_fast(m - mn);  // 0 on the wave's first chunk
+        float pv[4], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = vin[i] ? exp2_fast(sv[i] - mn) : 0.f;
+            ps += pv[i];
+        }
+        l = l * f + ps;
+        m = mn;
+        u32x2 pb[3];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t a0, a1, a2, c0, c1, c2;
+            bf16_pieces(pv[2 * h], a0, a1, a2);
+            bf16_pieces(pv[2 * h + 1], c0, c1, c2);
+            pb[0][h] = a0 | (c0 << 16);
+            pb[1][h] = a1 | (c1 << 16);
+            pb[2][h] = a2 | (c2 << 16);
+        }
+        // keys outside the window read zeros from V (their weight is 0, and 0 * NaN is not)
+        const bool all_in = vin[0] && vin[1] && vin[2] && vin[3];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            u32x2 v = vr[dt];
+            if (!all_in) {
+                v[0] = (vin[0] ? v[0] & 0xFFFFu : 0u) | (vin[1] ? v[0] & 0xFFFF0000u : 0u);
+                v[1] = (vin[2] ? v[1] & 0xFFFFu : 0u) | (vin[3] ? v[1] & 0xFFFF0000u : 0u);
+            }
+            f32x4 c = acc[dt] * f;
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v),
+                                                             __builtin_bit_cast(s16x4, pb[p]), c, 0, 0, 0);
+            acc[dt] = c;
+        }
+    };
+
+    if (nch == 1) {
+        chunk(0, k0r, v0r);
+    } else {
+        // chunk ci lives in buffer ci % 3; the loads of chunk ci + 2 go out before
+        // chunk ci is scored.  Every round issues the same loads (chunks past the
+        // split re-read its last), so the waits stay exact.
+        for (int ci = 0; ci < nch; ci += 3) {
+            load(ci + 2, k2r, v2r);
+            chunk(ci, k0r, v0r);
+            load(ci + 3, k0r, v0r);
+            chunk(ci + 1, k1r, v1r);
+            load(ci + 4, k1r, v1r);
+            chunk(ci + 2, k2r, v2r);
+        }
+    }
+    // the lane's sum covers its own keys: add the head's four lanes
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+
+    // merge the waves in wave order (a wave with no keys has m = -inf, l = 0)
+    if (q4 == 0) {
+        wm[w][r16] = m;
+        wl[w][r16] = l;
+    }
+    if (r16 < G)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wacc[w][r16][dt * 16 + 4 * q4 + i] = acc[dt][i];
     lds_barrier();
 
     const int ns = a.nsplit[b];

@@ -84,7 +84,8 @@ struct pn_model {
     int a_es = 2;                      // bytes per A-ready element
     long long h_plane = 0;
     int h_ld = 0;
-    int attn_kps = 0;  // 0 = automatic
+    int attn_kps = 0;   // 0 = automatic
+    int attn_kind = 0;  // bf16 cache: 0 = automatic, 1 = vector units, 2 = matrix cores
     int nw[GK_COUNT] = {8, 8, 8, 8, 8, 8, 16};  // waves per work-group of each GEMM kind
     int nw_down = 16;                       // the down projection (K = n_ff) uses GK_RESID too
     bool nw_set = false;                    // waves chosen by the caller (PN_OPT_WAVES_*): no auto choice
@@ -597,6 +598,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 aa.kvk[b] = st[b]->base + st[b]->kpool + (size_t)l * st[b]->layer_bytes;
                 aa.kvv[b] = st[b]->base + st[b]->vpool + (size_t)l * st[b]->layer_bytes;
             }
+            aa.kind = m->attn_kind == 1 ? 0 : 1;
             Timed tm(m, PN_K_ATTN, s);
             launch_attn(m->D, m->kvt, m->G, aa, dim3(nsplit_max, m->Hk, n), nsplit_max > 1, s);
             if (int rc = launched("attention")) return rc;
@@ -1086,6 +1088,11 @@ int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
             default: m->nw[GK_LOGITS] = (int)value; break;
         }
         m->nw_set = true;
+        return PN_OK;
+    }
+    if (option == PN_OPT_ATTN_KERNEL) {
+        if (value < 0 || value > 2) return fail(PN_EINVAL, "attention kernel must be 0, 1 or 2");
+        m->attn_kind = (int)value;
         return PN_OK;
     }
     if (option == PN_OPT_ATTN_KEYS_PER_SPLIT) {

@@ -309,7 +309,8 @@ __global__ void __launch_bounds__(256) k_copy_bytes(uint8_t *dst, const uint8_t 
         dst[i] = src[i];
 }
 
-// Scatter K and V of positions pos0..pos0+n-1 ([n][Hk][D]) into the pages of one layer.
+// Scatter K and V of positions pos0..pos0+n-1 ([n][Hk][D]) into the pages of one
+// layer (each head's block of a page laid out as kv_k_off / kv_v_off say).
 template <int ES>
 __global__ void __launch_bounds__(256) k_set_kv(char *kpool, char *vpool, const int *pt, const char *k,
                                                  const char *v, int pos0, int n, int Hk, int D) {
@@ -320,13 +321,15 @@ __global__ void __launch_bounds__(256) k_set_kv(char *kpool, char *vpool, const 
     const int j = (int)((i / D) % Hk);
     const int t = (int)(i / ((long long)D * Hk));
     const int p = pos0 + t;
-    const long long off = (((long long)pt[p / kPage] * Hk + j) * kPage + (p % kPage)) * D + d;
+    const long long hb = ((long long)pt[p / kPage] * Hk + j) * kPage * D;
+    const long long koff = hb + kv_k_off(ES == 2, p % kPage, d, D);
+    const long long voff = hb + kv_v_off(ES == 2, p % kPage, d, D);
     if constexpr (ES == 2) {
-        reinterpret_cast<uint16_t *>(kpool)[off] = reinterpret_cast<const uint16_t *>(k)[i];
-        reinterpret_cast<uint16_t *>(vpool)[off] = reinterpret_cast<const uint16_t *>(v)[i];
+        reinterpret_cast<uint16_t *>(kpool)[koff] = reinterpret_cast<const uint16_t *>(k)[i];
+        reinterpret_cast<uint16_t *>(vpool)[voff] = reinterpret_cast<const uint16_t *>(v)[i];
     } else {
-        reinterpret_cast<float *>(kpool)[off] = reinterpret_cast<const float *>(k)[i];
-        reinterpret_cast<float *>(vpool)[off] = reinterpret_cast<const float *>(v)[i];
+        reinterpret_cast<float *>(kpool)[koff] = reinterpret_cast<const float *>(k)[i];
+        reinterpret_cast<float *>(vpool)[voff] = reinterpret_cast<const float *>(v)[i];
     }
 }
 
