@@ -135,7 +135,9 @@ int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *w, v
 void pn_model_free(pn_model *m);
 
 /* Bytes of device memory one state of capacity max_ctx positions needs (paged
- * K/V cache for every layer, page table, attention split scratch); 0 if invalid. */
+ * K/V cache for every layer, page table, attention split scratch); 0 if invalid
+ * (max_ctx < 1, or one layer's K pool would reach 2 GiB: about a million
+ * positions of 8 bf16 KV heads of 128 dims). */
 size_t pn_state_bytes(const pn_model *m, int32_t max_ctx);
 
 /* Create a state (pos = 0, K/V zeroed, identity page table) in `dev_buf`
@@ -197,10 +199,13 @@ enum {
 };
 
 /* Options (tuning only; results change at most by fp32 rounding):
- *  PN_OPT_ATTN_KEYS_PER_SPLIT  0 = automatic, else a multiple of 64 keys
- *                              handled by one attention work-group (raised
- *                              where a state's split scratch, at most 256
- *                              splits, needs it);
+ *  PN_OPT_ATTN_KEYS_PER_SPLIT  0 = automatic (about 512 attention
+ *                              work-groups shared among the slots in
+ *                              proportion to their windows), else a multiple
+ *                              of 64: a slot's window of P pages of 64 keys is
+ *                              cut into ceil(P / (value / 64)) splits that
+ *                              share its pages evenly (at most the state's
+ *                              split scratch, 256 splits);
  *  PN_OPT_ATTN_KERNEL          attention over a bf16 cache: 0 = automatic,
  *                              1 = vector units, 2 = matrix cores (an fp32
  *                              cache always uses the vector units);

@@ -101,6 +101,7 @@ def test_init_rejects_bad_buffers_without_device_work():
     try:
         assert L.pn_state_bytes(h, 132) > 0
         assert L.pn_state_bytes(h, -1) == 0
+        assert L.pn_state_bytes(h, 2_000_000_000) == 0  # one layer's K pool past 2 GiB
         st = ctypes.c_void_p()
         assert L.pn_state_new(h, 64, None, 1 << 20, None, ctypes.byref(st)) == C.PN_EINVAL
         assert L.pn_state_new(h, 64, ctypes.c_void_p(1 << 21), 16, None, ctypes.byref(st)) == C.PN_ERANGE

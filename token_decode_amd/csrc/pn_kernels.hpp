@@ -986,15 +986,17 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
 struct AttnArgs {
     const float *q;   // [slot][Hq*D]
     float *o;         // attention output [slot][Hq*D] (fp32; the O projection rounds it)
-    int Hq, Hk, kps;
+    int Hq, Hk;
     float scale;      // 1/sqrt(D) * log2(e): scores are kept in the base-2 domain
     int pos[kMaxSlots];     // the slot's current position (its last key)
     int lo[kMaxSlots];      // first key inside the window
-    int origin[kMaxSlots];  // lo rounded down to a page: split s starts at origin + s*kps
+    int origin[kMaxSlots];  // lo rounded down to a page: the window's np pages start there
+    int np[kMaxSlots];      // split s of nsplit takes pages [s*np/nsplit, (s+1)*np/nsplit)
     int nsplit[kMaxSlots], s_cap[kMaxSlots];
     const char *kvk[kMaxSlots], *kvv[kMaxSlots];
     const int *pt[kMaxSlots];
     float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max (base 2), sum, 2 pad, unnormalised output
+    unsigned kv_bytes[kMaxSlots];  // bytes of one layer's K (and of its V) pool
     int kind;                // bf16 cache: 0 = vector units (k_attn), 1 = matrix cores (k_attn_mfma)
 };
 
@@ -1204,8 +1206,9 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lo = a.lo[b];
-    const int kb = a.origin[b] + s * a.kps;
-    const int ke = min(kb + a.kps, a.pos[b] + 1);
+    const int np = a.np[b], ns_b = a.nsplit[b];
+    const int kb = a.origin[b] + (int)((long long)s * np / ns_b) * kPage;
+    const int ke = min(a.origin[b] + (int)((long long)(s + 1) * np / ns_b) * kPage, a.pos[b] + 1);
     const int kl = ke - 1;
 
     __shared__ __align__(16) float qs[G][D];
@@ -1344,8 +1347,9 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
     const int lo = a.lo[b];
-    const int kb = a.origin[b] + s * a.kps;
-    const int ke = min(kb + a.kps, a.pos[b] + 1);
+    const int np = a.np[b], ns_b = a.nsplit[b];
+    const int kb = a.origin[b] + (int)((long long)s * np / ns_b) * kPage;
+    const int ke = min(a.origin[b] + (int)((long long)(s + 1) * np / ns_b) * kPage, a.pos[b] + 1);
     const int kl = ke - 1;
 
     __shared__ __align__(16) u32x4 qsh[3][KS][64];  // B operands of the query pieces, by lane
@@ -1360,19 +1364,22 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
         ci = min(ci, nch - 1);
         return ci < 64 ? __builtin_amdgcn_readlane(vpg, ci) : ptb[ci];
     };
-    // K fragments of wave chunk ci (keys k0..k0+15, rows clamped into [lo, kl],
-    // inside the chunk's page; chunks past the split's last re-read the last) and
-    // V column fragments (keys 4*q4..+3 of dims dt*16 + r16)
+    // buffer loads over the layer's pools: an offset past the pool reads zeros
+    // without a memory access, which is how chunks past the split are loaded
+    constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) access
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(a.kvk[b]), (short)0, (int)a.kv_bytes[b], kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(a.kvv[b]), (short)0, (int)a.kv_bytes[b], kRsrcWord3);
     auto load = [&](int ci, u32x4 (&kr)[KS], u32x2 (&vr)[DT]) {
-        ci = min(ci, nch - 1);
         // the wave's 16-key group of the page's head block (16 * D elements of K and of V)
-        const long long gb = (((long long)page_of(ci) * a.Hk + j) * kPage + w * 16) * D * 2;
-        const uint8_t *kp = reinterpret_cast<const uint8_t *>(a.kvk[b]) + gb + lane * 16;
+        const unsigned gb = (unsigned)((((long long)page_of(ci) * a.Hk + j) * kPage + w * 16) * D * 2);
+        const unsigned ko = ci < nch ? gb + lane * 16 : 0xFFFFFFF0u;
+        const unsigned vo = ci < nch ? gb + lane * 8 : 0xFFFFFFF0u;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[ks] = *reinterpret_cast<const u32x4 *>(kp + ks * 1024);
-        const uint8_t *vp = reinterpret_cast<const uint8_t *>(a.kvv[b]) + gb + lane * 8;
+        for (int ks = 0; ks < KS; ++ks) kr[ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(ko + ks * 1024), 0, 0);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vr[dt] = *reinterpret_cast<const u32x2 *>(vp + dt * 512);
+        for (int dt = 0; dt < DT; ++dt) vr[dt] = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(vo + dt * 512), 0, 0);
     };
     u32x4 k0r[KS], k1r[KS], k2r[KS];
     u32x2 v0r[DT], v1r[DT], v2r[DT];
@@ -1473,7 +1480,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     } else {
         // chunk ci lives in buffer ci % 3; the loads of chunk ci + 2 go out before
         // chunk ci is scored.  Every round issues the same loads (chunks past the
-        // split re-read its last), so the waits stay exact.
+        // split read zeros without touching memory), so the waits stay exact.
         for (int ci = 0; ci < nch; ci += 3) {
             load(ci + 2, k2r, v2r);
             chunk(ci, k0r, v0r);

@@ -329,6 +329,8 @@ size_t layout_model(pn_model *m) {
 // Automatic split size: aim for about this many attention work-groups per step
 // (two per compute unit: all resident at once, and evenly spread).
 constexpr int kAttnTargetGroups = 512;
+// The attention addresses a layer's K and V pools with 32-bit buffer offsets.
+constexpr size_t kMaxLayerBytes = (size_t)1 << 31;
 
 size_t layout_state(pn_state *s) {
     const pn_model *m = s->m;
@@ -511,25 +513,17 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     aa.Hq = m->H;
     aa.Hk = m->Hk;
     aa.scale = (float)(1.4426950408889634 / std::sqrt((double)m->D));  // log2(e) / sqrt(D)
-    // keys per split: a multiple of kAttnChunk, small enough to spread the window
-    // over about kAttnTargetGroups work-groups, large enough that every slot's
-    // splits fit its scratch.  Splits start at the window start rounded down to
-    // a page.
+    // Splits.  A slot's window, from its start rounded down to a page, is np
+    // pages; split s of nsplit takes pages [s*np/nsplit, (s+1)*np/nsplit), so a
+    // slot's splits differ by at most one page.  nsplit comes from the caller's
+    // keys per split (PN_OPT_ATTN_KEYS_PER_SPLIT), else from sharing about
+    // kAttnTargetGroups work-groups among the slots in proportion to their
+    // pages; it is at most the slot's pages and its scratch capacity.
     auto window_lo = [&](int pos) { return c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0; };
-    int span_max = 1;
+    long long np_sum = 0;
     for (int b = 0; b < n; ++b) {
         const int pos = st[b]->pos;
-        span_max = std::max(span_max, pos + 1 - window_lo(pos) / kPage * kPage);
-    }
-    int kps = m->attn_kps;
-    if (kps <= 0) {
-        const int want = std::max(1, kAttnTargetGroups / (m->Hk * n));
-        kps = kAttnChunk * cdiv(span_max, kAttnChunk * want);
-    }
-    for (int b = 0; b < n; ++b) {
-        const int pos = st[b]->pos;
-        const int span = pos + 1 - window_lo(pos) / kPage * kPage;
-        kps = std::max(kps, kAttnChunk * cdiv(span, kAttnChunk * st[b]->s_cap));
+        np_sum += cdiv(pos + 1 - window_lo(pos) / kPage * kPage, kPage);
     }
     int nsplit_max = 1;
     for (int b = 0; b < n; ++b) {
@@ -538,15 +532,18 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         aa.pos[b] = pos;
         aa.lo[b] = lo;
         aa.origin[b] = lo / kPage * kPage;
-        aa.nsplit[b] = cdiv(pos + 1 - aa.origin[b], kps);
+        const int np = cdiv(pos + 1 - aa.origin[b], kPage);
+        long long ns = m->attn_kps > 0 ? cdiv(np, m->attn_kps / kPage)
+                                       : (long long)kAttnTargetGroups * np / ((long long)m->Hk * np_sum);
+        ns = std::min<long long>(std::max<long long>(ns, 1), std::min(np, std::min(st[b]->s_cap, kMaxSplits)));
+        aa.np[b] = np;
+        aa.nsplit[b] = (int)ns;
         aa.s_cap[b] = st[b]->s_cap;
-        if (aa.nsplit[b] > st[b]->s_cap || aa.nsplit[b] > kMaxSplits)
-            return fail(PN_ERANGE, "attention splits exceed state scratch");
         nsplit_max = std::max(nsplit_max, aa.nsplit[b]);
         aa.pt[b] = (const int *)(st[b]->base + st[b]->pt);
         aa.part[b] = (float *)(st[b]->base + st[b]->part);
+        aa.kv_bytes[b] = (unsigned)st[b]->layer_bytes;
     }
-    aa.kps = kps;
 
     const LayerOff &L0 = m->L[0];
     const int gz = moe ? m->X : 1;
@@ -938,7 +935,8 @@ size_t pn_state_bytes(const pn_model *m, int32_t max_ctx) {
     pn_state s{};
     s.m = const_cast<pn_model *>(m);
     s.max_ctx = max_ctx;
-    return layout_state(&s);
+    const size_t need = layout_state(&s);
+    return s.layer_bytes < kMaxLayerBytes ? need : 0;
 }
 
 int pn_state_reset(pn_state *s, void *stream) {
@@ -966,6 +964,10 @@ int pn_state_new(pn_model *m, int32_t max_ctx, void *dev_buf, size_t bytes, void
     s->m = m;
     s->max_ctx = max_ctx;
     size_t need = layout_state(s);
+    if (s->layer_bytes >= kMaxLayerBytes) {
+        delete s;
+        return fail(PN_ERANGE, "max_ctx %d too large: one layer's K pool would reach 2 GiB", max_ctx);
+    }
     if (bytes < need) {
         delete s;
         return fail(PN_ERANGE, "state buffer too small: %zu < %zu", bytes, need);
