@@ -133,6 +133,21 @@ def test_attention_kernels_bf16_cache(kind, kps):
     log("  kind %d kps %d d128 batch: worst rel L2 %.2e near %d" % (kind, kps, worst, near))
 
 
+@pytest.mark.parametrize("heads", [(6, 2, 32), (6, 1, 64), (3, 1, 128)], ids=["g3-d32", "g6-d64", "g3-d128"])
+def test_attention_group_sizes(heads):
+    """Query heads per KV head of 3 and 6 (the matrix-core tile's unused
+    columns) and head_dim 32, over a bf16 cache with a window, batch 1 and
+    three batched slots."""
+    H, Hk, d = heads
+    wl = ragged("attn-g%d-d%d" % (H // Hk, d), n_head=H, n_kv_head=Hk, head_dim=d, w_dtype=synth.BF16,
+                kv_dtype=synth.BF16, act_dtype=synth.F32, sliding_window=250, seed=50 + H + d)
+    p = Pair(wl, max_batch=3)
+    worst, near, n = run_single(p, 600, [31, 32], 2)
+    log("  %s single: worst rel L2 %.2e near %d" % (wl.name, worst, near))
+    worst, near = run_batch(p, [1, 249, 777], 2)
+    log("  %s batch: worst rel L2 %.2e near %d" % (wl.name, worst, near))
+
+
 def test_batched_16_slots_large_lds():
     """16 slots with n_embd 2048: several GEMM variants stage more than 64 KiB of
     A in LDS in the same step (each needs its own launch attribute)."""
