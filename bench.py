@@ -12,6 +12,9 @@ replays of the timed steps' launches; HBM traffic from the committed counter
 summary while the GEMM sources are unchanged) and the fp64 CPU oracle timed
 on a bounded sample of the same workload.
 
+The line also reports the time of one on-device sampling call (pn_sample) over
+the step's logits, outside the timed steps.
+
 --calibrate-copy runs only a 1 GiB device copy, the reference for scaling the
 HBM byte counters; --print-source-hash prints the hash the counter summary is
 tied to.
@@ -176,6 +179,21 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         per_kernel[name] = {"avg_us": round(1e3 * e0.elapsed_time(e1) / reps, 3), "replays": reps}
+    # on-device sampling of the step's logits (pn_sample), for the record: one
+    # call per step over every slot's row
+    sp = [dict(temperature=0.8, top_k=40, top_p=0.95, repeat_penalty=1.1)] * B
+    u_dev = torch.full((B,), 0.5, dtype=torch.float32, device="cuda")
+    s_ids = torch.empty(B, dtype=torch.int32, device="cuda")
+    s_recent = torch.zeros((B, 64), dtype=torch.int32, device="cuda")
+    for _ in range(4):
+        dv.sample(model, logits, sp, u_dev, s_ids, s_recent, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(64):
+        dv.sample(model, logits, sp, u_dev, s_ids, s_recent, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sample_us = round(1e3 * e0.elapsed_time(e1) / 64, 2)
     dom = "gateup"
     dom_bytes = gemm_bytes(wl, dom)
     dom_us = per_kernel[dom]["avg_us"]
@@ -215,6 +233,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)},
         "kernels": per_kernel,
+        "sampling": {"us_per_call": sample_us, "rows": B, "vocab": wl.n_vocab,
+                     "params": "temperature 0.8, top_k 40, top_p 0.95, repeat_penalty 1.1 over 64 recent tokens"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

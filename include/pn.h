@@ -190,6 +190,37 @@ int pn_forward_step(pn_model *m, pn_state *s, const int32_t *token_dev, float *l
 int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int32_t *tokens_dev,
                      float *logits_dev, int32_t *argmax_dev, void *stream);
 
+/* ---- sampling ------------------------------------------------------------- */
+
+/* Sampling parameters of one row ("Engine Architecture", section "Sampling";
+ * the pages' sampler seam takes them per request: "Core Engine API", section
+ * "Sampler seam"). */
+typedef struct pn_sampling_params {
+    float temperature;     /* <= 0: greedy, the argmax of the raw logits (the rest unused) */
+    float repeat_penalty;  /* applied to the distinct tokens of the row's recent window; 1 = none */
+    int32_t top_k;         /* keep the top_k highest (1..4096) */
+    float top_p;           /* keep the shortest top-ranked prefix whose probability exceeds
+                              top_p; >= 1 = no cut */
+} pn_sampling_params;
+
+/* Sample one token per row of logits_dev [n][n_vocab] (fp32, device, not
+ * modified) into ids_dev [n] (int32, device), on `stream`, in the pages'
+ * order: divide by the temperature (fp32); penalise the row's recent tokens
+ * (z / r if z > 0, else z * r); rank tokens by value, equal values by lower
+ * index; keep the top_k; softmax over them (exp(z - z_max), fp64 sums); keep
+ * the shortest prefix whose cumulative probability exceeds top_p of the total;
+ * return the first token of the prefix whose cumulative probability exceeds
+ * u times the prefix total.  u_dev [n] holds the caller's uniform draws in
+ * [0, 1) (the random numbers are an input, so a seeded caller reproduces its
+ * tokens).  recent_dev [n][n_recent] (0 <= n_recent <= 1024) lists each row's
+ * recent tokens; entries < 0 or >= n_vocab are empty; it may be NULL when
+ * n_recent is 0.  params is a host array [n]; 1 <= n <= max_batch.  Uses the
+ * model's scratch (calls on one model must be stream-ordered).  Errors:
+ * PN_EINVAL (NULL pointer, bad n, n_recent, NaN or non-positive penalty),
+ * PN_EUNSUPPORTED (top_k outside 1..4096 with a positive temperature). */
+int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling_params *params,
+              const int32_t *recent_dev, int32_t n_recent, const float *u_dev, int32_t *ids_dev, void *stream);
+
 /* ---- tuning and measurement ------------------------------------------------ */
 
 /* Kernel classes, for timing. */

@@ -14,7 +14,8 @@ sampler):
   -0 counts as +0 and NaN as -inf;
 - the tokens are ranked by z, highest first, equal z by lower index (the
   canonical order); top-k keeps the first k of that order;
-- probabilities are exp(z - z_max) over the kept tokens, in fp64;
+- probabilities are exp(z - z_max) over the kept tokens, in fp64 (a token
+  whose z equals z_max weighs 1, so all -inf rows draw evenly);
 - top-p keeps the shortest prefix of the canonical order whose cumulative
   probability exceeds p times the kept total (p >= 1: all kept tokens);
 - the draw takes a uniform u in [0, 1) as an input and returns the first
@@ -57,7 +58,8 @@ def sample(logits, temperature, top_k, top_p=1.0, repeat_penalty=1.0, recent=(),
     z = transformed(logits, temperature, repeat_penalty, recent)
     order = canonical_order(z)[:max(1, int(top_k))]
     zk = z[order].astype(np.float64)
-    w = np.exp(zk - zk[0])
+    with np.errstate(invalid="ignore"):
+        w = np.where(zk == zk[0], 1.0, np.exp(zk - zk[0]))  # (all -inf: equal weights)
     cum = np.cumsum(w)
     if top_p < 1.0:
         n_p = int(np.argmax(cum > top_p * cum[-1])) + 1 if np.any(cum > top_p * cum[-1]) else len(cum)

@@ -113,6 +113,23 @@ def test_init_rejects_bad_buffers_without_device_work():
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KERNEL, 3) == C.PN_EINVAL
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KERNEL, 2) == 0
         assert L.pn_profile_begin(h, 99) == C.PN_EINVAL
+        # sampling: every argument is checked on the host before anything is enqueued
+        sp = (C.pn_sampling_params * 2)()
+        for i in range(2):
+            sp[i].temperature, sp[i].repeat_penalty, sp[i].top_k, sp[i].top_p = 1.0, 1.0, 40, 0.9
+        dv_ = ctypes.c_void_p(1 << 22)
+        assert L.pn_sample(h, dv_, 0, sp, None, 0, dv_, dv_, None) == C.PN_EINVAL
+        assert L.pn_sample(h, None, 1, sp, None, 0, dv_, dv_, None) == C.PN_EINVAL
+        assert L.pn_sample(h, dv_, 1, sp, None, 2000, dv_, dv_, None) == C.PN_EINVAL
+        assert L.pn_sample(h, dv_, 1, sp, None, 8, dv_, dv_, None) == C.PN_EINVAL  # recent NULL
+        sp[0].top_k = 0
+        assert L.pn_sample(h, dv_, 1, sp, None, 0, dv_, dv_, None) == C.PN_EUNSUPPORTED
+        sp[0].top_k = 5000
+        assert L.pn_sample(h, dv_, 1, sp, None, 0, dv_, dv_, None) == C.PN_EUNSUPPORTED
+        sp[0].top_k, sp[0].repeat_penalty = 40, 0.0
+        assert L.pn_sample(h, dv_, 1, sp, None, 0, dv_, dv_, None) == C.PN_EINVAL
+        sp[0].repeat_penalty, sp[0].temperature = 1.0, float("nan")
+        assert L.pn_sample(h, dv_, 1, sp, None, 0, dv_, dv_, None) == C.PN_EINVAL
         assert L.pn_profile_replay(h, C.PN_K_GATEUP, 4, None) == C.PN_EINVAL  # nothing recorded yet
         assert L.pn_profile_replay(h, 99, 4, None) == C.PN_EINVAL
         lw = C.pn_layer_weights()

@@ -33,6 +33,11 @@ class pn_layer_weights(ctypes.Structure):
                                    "s_up", "s_down")]
 
 
+class pn_sampling_params(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("repeat_penalty", ctypes.c_float), ("top_k", i32),
+                ("top_p", ctypes.c_float)]
+
+
 class pn_weights(ctypes.Structure):
     _fields_ = [("tok_embd", vp), ("out_norm", vp), ("w_out", vp), ("s_out", vp),
                 ("layers", ctypes.POINTER(pn_layer_weights))]
@@ -78,6 +83,7 @@ def lib():
             "pn_state_free": (None, [vp]),
             "pn_forward_step": (ctypes.c_int, [vp, vp, vp, vp, vp, vp]),
             "pn_forward_batch": (ctypes.c_int, [vp, P(vp), i32, vp, vp, vp, vp]),
+            "pn_sample": (ctypes.c_int, [vp, vp, i32, P(pn_sampling_params), vp, i32, vp, vp, vp]),
             "pn_model_set_option": (ctypes.c_int, [vp, i32, ctypes.c_int64]),
             "pn_profile_begin": (ctypes.c_int, [vp, i32]),
             "pn_profile_end": (ctypes.c_int, [vp, vp, P(ctypes.c_double), P(ctypes.c_int64)]),
@@ -97,7 +103,7 @@ EXPORTS = ["pn_config_default", "pn_config_check", "pn_model_bytes", "pn_model_c
            "pn_state_bytes", "pn_state_new", "pn_state_reset", "pn_state_set_kv",
            "pn_state_set_page_table", "pn_state_pages", "pn_page_size", "pn_state_set_pos",
            "pn_state_pos", "pn_state_max_ctx", "pn_state_check", "pn_state_free",
-           "pn_forward_step", "pn_forward_batch", "pn_model_set_option", "pn_profile_begin",
+           "pn_forward_step", "pn_forward_batch", "pn_sample", "pn_model_set_option", "pn_profile_begin",
            "pn_profile_end", "pn_profile_replay", "pn_last_error"]
 
 

@@ -20,6 +20,7 @@
 #include "pn.h"
 #include "pn_launch.hpp"
 #include "pn_small.hpp"
+#include "pn_sample.hpp"
 
 using namespace pn;
 
@@ -80,6 +81,7 @@ struct pn_model {
     Mat out;
     // scratch
     size_t x, q, o, h, y, route_ids, route_w, am_val, am_idx;
+    size_t samp_keys = 0, samp_hist = 0;  // pn_sample scratch
     size_t o_bytes = 0, h_bytes = 0, am_count = 0;
     int a_es = 2;                      // bytes per A-ready element
     long long h_plane = 0;
@@ -319,6 +321,8 @@ size_t layout_model(pn_model *m) {
     m->am_count = (size_t)cdiv(m->out.n_tiles, 2) * MB;
     m->am_val = bp.take(m->am_count * 4);
     m->am_idx = bp.take(m->am_count * 4);
+    m->samp_keys = bp.take((size_t)MB * m->V * 4);
+    m->samp_hist = bp.take((size_t)MB * kSampleBlocks * kSampleBins * 4);
     // pn_profile_replay: a QKV replay appends its k, v rows here (page 0 of a
     // one-entry page table) instead of into a state's cache
     m->replay_kv = bp.take((size_t)2 * MB * m->Hk * kPage * m->D * dtype_size(m->kvt));
@@ -1069,6 +1073,57 @@ int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int3
             if (states[j] == states[i]) return fail(PN_EINVAL, "state %d appears twice", i);
     }
     return forward_impl(m, states, n, tokens_dev, logits_dev, argmax_dev, S(stream));
+}
+
+int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling_params *params,
+              const int32_t *recent_dev, int32_t n_recent, const float *u_dev, int32_t *ids_dev, void *stream) {
+    g_err.clear();
+    if (!m || !logits_dev || !params || !u_dev || !ids_dev) return fail(PN_EINVAL, "NULL argument");
+    if (n < 1 || n > m->cfg.max_batch) return fail(PN_EINVAL, "n = %d outside [1, max_batch = %d]", n, m->cfg.max_batch);
+    if (n_recent < 0 || n_recent > kSampleMaxRecent)
+        return fail(PN_EINVAL, "n_recent = %d outside [0, %d]", n_recent, kSampleMaxRecent);
+    if (n_recent > 0 && !recent_dev) return fail(PN_EINVAL, "recent_dev is NULL");
+    SampleArgs a{};
+    a.logits = logits_dev;
+    a.V = m->V;
+    a.n_recent = n_recent;
+    a.recent = recent_dev;
+    a.u = u_dev;
+    a.ids = ids_dev;
+    a.keys = (unsigned *)(m->base + m->samp_keys);
+    a.hist = (unsigned *)(m->base + m->samp_hist);
+    for (int b = 0; b < n; ++b) {
+        const pn_sampling_params &p = params[b];
+        if (std::isnan(p.temperature)) return fail(PN_EINVAL, "row %d: temperature is NaN", b);
+        if (p.temperature > 0.f) {
+            if (!std::isfinite(p.temperature)) return fail(PN_EINVAL, "row %d: temperature must be finite", b);
+            if (p.top_k < 1 || p.top_k > kSampleMaxK)
+                return fail(PN_EUNSUPPORTED, "row %d: top_k = %d outside [1, %d]", b, p.top_k, kSampleMaxK);
+            if (!(p.repeat_penalty > 0.f) || !std::isfinite(p.repeat_penalty))
+                return fail(PN_EINVAL, "row %d: repeat_penalty must be finite and > 0", b);
+            if (std::isnan(p.top_p)) return fail(PN_EINVAL, "row %d: top_p is NaN", b);
+        }
+        a.temp[b] = p.temperature;
+        a.rp[b] = p.repeat_penalty;
+        a.top_p[b] = p.top_p;
+        a.top_k[b] = p.top_k;
+    }
+    hipStream_t st = S(stream);
+    hipLaunchKernelGGL(k_sample_keys, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
+    if (int rc = launched("sampling keys")) return rc;
+    // the candidate buffer is dynamic LDS; with the kernel's static LDS the
+    // total passes 64 KiB, which needs the attribute (the two within 160 KiB)
+    static bool lds_set = false;
+    const size_t lds = (size_t)kSampleCap * 8;
+    if (!lds_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_sample_pick),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return fail(PN_EHIP, "sampling LDS attribute: %s", hipGetErrorString(e));
+        lds_set = true;
+    }
+    hipLaunchKernelGGL(k_sample_pick, dim3(n), dim3(kSamplePick), lds, st, a);
+    if (int rc = launched("sampling pick")) return rc;
+    return PN_OK;
 }
 
 int pn_forward_step(pn_model *m, pn_state *s, const int32_t *token_dev, float *logits_dev, int32_t *argmax_dev,

@@ -180,3 +180,19 @@ def forward_batch(model, states, tokens_dev, logits_dev=None, argmax_dev=None, s
     arr = (ctypes.c_void_p * len(states))(*[s.h.value for s in states])
     C.check(C.lib().pn_forward_batch(model.h, arr, len(states), _ptr(tokens_dev), _ptr(logits_dev),
                                      _ptr(argmax_dev), _stream_ptr(stream)))
+
+
+def sample(model, logits_dev, params, u_dev, ids_dev, recent_dev=None, stream=None):
+    """Sample one token per row of logits_dev [n][n_vocab] into ids_dev [n].
+    params: a list of n dicts (temperature, repeat_penalty, top_k, top_p);
+    u_dev [n] fp32 uniform draws; recent_dev [n][n_recent] int32 or None."""
+    n = len(params)
+    arr = (C.pn_sampling_params * n)()
+    for i, p in enumerate(params):
+        arr[i].temperature = p.get("temperature", 1.0)
+        arr[i].repeat_penalty = p.get("repeat_penalty", 1.0)
+        arr[i].top_k = p.get("top_k", 40)
+        arr[i].top_p = p.get("top_p", 1.0)
+    n_recent = 0 if recent_dev is None else int(recent_dev.shape[-1])
+    C.check(C.lib().pn_sample(model.h, _ptr(logits_dev), n, arr, _ptr(recent_dev), n_recent, _ptr(u_dev),
+                              _ptr(ids_dev), _stream_ptr(stream)))
