@@ -190,6 +190,21 @@ int pn_forward_step(pn_model *m, pn_state *s, const int32_t *token_dev, float *l
 int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int32_t *tokens_dev,
                      float *logits_dev, int32_t *argmax_dev, void *stream);
 
+/* Prefill: feed the n prompt tokens tokens_dev [n] (device) to state s at
+ * positions pos..pos+n-1 and advance pos by n.  The result is that of n
+ * pn_forward_step calls, one per token ("Engine Architecture", section
+ * "Generation Loop": prefill runs the forward for each prompt token), up to
+ * fp32 summation order: row t of logits_dev [n][n_vocab] and argmax_dev [n]
+ * (either may be NULL) are the logits and greedy id after token t, and the
+ * cache holds every token's K/V.  The tokens go in chunks of max_batch, each
+ * chunk one batched step whose rows are consecutive positions of the state
+ * (the pages' chunked prefill: "Serve Layer Architecture", section "Batched
+ * Decode", "L2 - chunked prefill"), so every weight is read once per chunk
+ * instead of once per token.  Errors: PN_EINVAL (NULL pointer, n < 1, state
+ * of another model), PN_ERANGE (pos + n > max_ctx). */
+int pn_prefill(pn_model *m, pn_state *s, const int32_t *tokens_dev, int32_t n, float *logits_dev,
+               int32_t *argmax_dev, void *stream);
+
 /* ---- sampling ------------------------------------------------------------- */
 
 /* Sampling parameters of one row ("Engine Architecture", section "Sampling";

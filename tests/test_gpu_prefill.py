@@ -1,0 +1,97 @@
+"""GPU parity of chunked prefill (pn_prefill) against the oracle's one step per
+prompt token: every row's logits and greedy id, then ordinary decode steps on
+the resulting cache (which checks every appended K/V)."""
+import pytest
+
+import synth
+
+from harness import Pair, compare_step, log
+
+pytestmark = pytest.mark.gpu
+
+
+def ragged(name, **kw):
+    base = dict(n_layer=2, n_embd=200, n_head=6, n_kv_head=2, head_dim=32, n_ff=300, n_vocab=1000,
+                rope_theta=10000.0, seed=81)
+    base.update(kw)
+    return synth.Workload(name, **base)
+
+
+def run_prefill(p, start, prompt, n_decode, tol=None):
+    import torch
+    from token_decode_amd import device as dv
+    wl = p.wl
+    ds, os_ = p.states(0, start, start + len(prompt) + n_decode + 1)
+    toks = torch.tensor([int(t) for t in prompt], dtype=torch.int32, device="cuda")
+    logits = torch.empty(len(prompt), wl.n_vocab, dtype=torch.float32, device="cuda")
+    am = torch.empty(len(prompt), dtype=torch.int32, device="cuda")
+    dv.prefill(p.dm, ds, toks, logits, am)
+    assert ds.pos == start + len(prompt)
+    g, ga = logits.cpu().numpy(), am.cpu().numpy()
+    worst, near, nxt = 0.0, 0, None
+    for t, tok in enumerate(prompt):
+        ol, oa = os_.step(int(tok))
+        rel, nt = compare_step(wl, g[t], ol, int(ga[t]), oa, "prompt row %d:" % t, tol)
+        worst, near, nxt = max(worst, rel), near + int(nt), oa
+    # decode on from the prefilled cache
+    tok = torch.tensor([nxt], dtype=torch.int32, device="cuda")
+    lg1 = torch.empty(wl.n_vocab, dtype=torch.float32, device="cuda")
+    a1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    for i in range(n_decode):
+        dv.forward_step(p.dm, ds, tok, lg1, a1)
+        ol, oa = os_.step(int(tok.item()))
+        rel, nt = compare_step(wl, lg1.cpu().numpy(), ol, int(a1.item()), oa, "decode step %d:" % i, tol)
+        worst, near = max(worst, rel), near + int(nt)
+        tok.fill_(oa)
+    return worst, near
+
+
+def test_prefill_tiny_fp32_from_zero():
+    wl = synth.tiny_fp32()
+    p = Pair(wl, max_batch=16)
+    prompt = list(synth.uniform_int(wl.seed, 91, 37, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 0, prompt, 5)
+    log("  tiny fp32, 37 prompt tokens in chunks of 16: worst rel L2 %.2e, near %d" % (worst, near))
+    assert near == 0
+
+
+def test_prefill_window_on_existing_cache():
+    """Chunks of 16 over a 300-token cache with a 40-token window: rows of one
+    chunk see each other's keys and drop the ones that leave the window."""
+    wl = ragged("prefill-bf16-window", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.BF16,
+                sliding_window=40)
+    p = Pair(wl, max_batch=16)
+    prompt = list(synth.uniform_int(wl.seed, 92, 50, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 300, prompt, 3)
+    log("  bf16 window 40, 50 tokens from 300: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_prefill_fp32_activations_chunks_of_five():
+    wl = ragged("prefill-actf32", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.F32, seed=82)
+    p = Pair(wl, max_batch=5)
+    prompt = list(synth.uniform_int(wl.seed, 93, 12, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 63, prompt, 2)
+    log("  bf16 weights, fp32 activations, 12 tokens from 63: worst rel L2 %.2e" % worst)
+
+
+def test_prefill_moe():
+    wl = ragged("prefill-moe", n_expert=4, n_expert_used=2, w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                act_dtype=synth.BF16, seed=83, n_ff=128)
+    p = Pair(wl, max_batch=7)
+    prompt = list(synth.uniform_int(wl.seed, 94, 10, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 5, prompt, 2)
+    log("  MoE, 10 tokens from 5: worst rel L2 %.2e" % worst)
+
+
+def test_prefill_range_error():
+    import torch
+    from token_decode_amd import _capi as C
+    from token_decode_amd import device as dv
+    wl = synth.tiny_fp32()
+    p = Pair(wl, max_batch=4)
+    ds = dv.DeviceState(p.dm, 20)
+    ds.pos = 15
+    with pytest.raises(C.PNError) as e:
+        dv.prefill(p.dm, ds, torch.zeros(6, dtype=torch.int32, device="cuda"))
+    assert e.value.code == C.PN_ERANGE
+    assert ds.pos == 15

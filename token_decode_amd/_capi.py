@@ -84,6 +84,7 @@ def lib():
             "pn_forward_step": (ctypes.c_int, [vp, vp, vp, vp, vp, vp]),
             "pn_forward_batch": (ctypes.c_int, [vp, P(vp), i32, vp, vp, vp, vp]),
             "pn_sample": (ctypes.c_int, [vp, vp, i32, P(pn_sampling_params), vp, i32, vp, vp, vp]),
+            "pn_prefill": (ctypes.c_int, [vp, vp, vp, i32, vp, vp, vp]),
             "pn_model_set_option": (ctypes.c_int, [vp, i32, ctypes.c_int64]),
             "pn_profile_begin": (ctypes.c_int, [vp, i32]),
             "pn_profile_end": (ctypes.c_int, [vp, vp, P(ctypes.c_double), P(ctypes.c_int64)]),
@@ -103,7 +104,7 @@ EXPORTS = ["pn_config_default", "pn_config_check", "pn_model_bytes", "pn_model_c
            "pn_state_bytes", "pn_state_new", "pn_state_reset", "pn_state_set_kv",
            "pn_state_set_page_table", "pn_state_pages", "pn_page_size", "pn_state_set_pos",
            "pn_state_pos", "pn_state_max_ctx", "pn_state_check", "pn_state_free",
-           "pn_forward_step", "pn_forward_batch", "pn_sample", "pn_model_set_option", "pn_profile_begin",
+           "pn_forward_step", "pn_forward_batch", "pn_prefill", "pn_sample", "pn_model_set_option", "pn_profile_begin",
            "pn_profile_end", "pn_profile_replay", "pn_last_error"]
 
 

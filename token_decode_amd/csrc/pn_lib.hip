@@ -82,6 +82,7 @@ struct pn_model {
     // scratch
     size_t x, q, o, h, y, route_ids, route_w, am_val, am_idx;
     size_t samp_keys = 0, samp_hist = 0;  // pn_sample scratch
+    size_t attn_part = 0, attn_part_row = 0;  // pn_prefill: per-row attention split scratch
     size_t o_bytes = 0, h_bytes = 0, am_count = 0;
     int a_es = 2;                      // bytes per A-ready element
     long long h_plane = 0;
@@ -322,6 +323,8 @@ size_t layout_model(pn_model *m) {
     m->am_val = bp.take(m->am_count * 4);
     m->am_idx = bp.take(m->am_count * 4);
     m->samp_keys = bp.take((size_t)MB * m->V * 4);
+    m->attn_part_row = (size_t)m->Hk * kMaxSplits * m->G * (m->D + 4) * 4;
+    m->attn_part = bp.take((size_t)MB * m->attn_part_row);
     m->samp_hist = bp.take((size_t)MB * kSampleBlocks * kSampleBins * 4);
     // pn_profile_replay: a QKV replay appends its k, v rows here (page 0 of a
     // one-entry page table) instead of into a state's cache
@@ -464,8 +467,13 @@ struct Timed {
     }
 };
 
+// One step over n rows.  Row b belongs to st[b] at its pos, or, for a
+// prefill (row_pos given), every row to the one state st[0] at row_pos[b]:
+// the rows then share the state's cache and page table, and their attention
+// splits use the model's per-row scratch.
 int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, float *logits, int32_t *amax,
-                 hipStream_t s) {
+                 hipStream_t s, const int *row_pos = nullptr) {
+    auto posof = [&](int b) { return row_pos ? row_pos[b] : st[b]->pos; };
     const pn_config &c = m->cfg;
     char *mb = m->base;
     for (auto &r : m->last) r.clear();
@@ -490,9 +498,9 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     base.ssp_n = m->ssp_ld;
     for (int b = 0; b < n; ++b) {
         sp.err[b] = (int *)(st[b]->base + st[b]->err);
-        sp.pos[b] = st[b]->pos;
+        sp.pos[b] = posof(b);
         base.err[b] = sp.err[b];
-        base.pos[b] = st[b]->pos;
+        base.pos[b] = posof(b);
         base.pt[b] = (const int *)(st[b]->base + st[b]->pt);
     }
 
@@ -526,12 +534,12 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     auto window_lo = [&](int pos) { return c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0; };
     long long np_sum = 0;
     for (int b = 0; b < n; ++b) {
-        const int pos = st[b]->pos;
+        const int pos = posof(b);
         np_sum += cdiv(pos + 1 - window_lo(pos) / kPage * kPage, kPage);
     }
     int nsplit_max = 1;
     for (int b = 0; b < n; ++b) {
-        const int pos = st[b]->pos;
+        const int pos = posof(b);
         const int lo = window_lo(pos);
         aa.pos[b] = pos;
         aa.lo[b] = lo;
@@ -539,13 +547,15 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         const int np = cdiv(pos + 1 - aa.origin[b], kPage);
         long long ns = m->attn_kps > 0 ? cdiv(np, m->attn_kps / kPage)
                                        : (long long)kAttnTargetGroups * np / ((long long)m->Hk * np_sum);
-        ns = std::min<long long>(std::max<long long>(ns, 1), std::min(np, std::min(st[b]->s_cap, kMaxSplits)));
+        const int cap = row_pos ? kMaxSplits : st[b]->s_cap;
+        ns = std::min<long long>(std::max<long long>(ns, 1), std::min(np, std::min(cap, kMaxSplits)));
         aa.np[b] = np;
         aa.nsplit[b] = (int)ns;
-        aa.s_cap[b] = st[b]->s_cap;
+        aa.s_cap[b] = cap;
         nsplit_max = std::max(nsplit_max, aa.nsplit[b]);
         aa.pt[b] = (const int *)(st[b]->base + st[b]->pt);
-        aa.part[b] = (float *)(st[b]->base + st[b]->part);
+        aa.part[b] = row_pos ? (float *)(m->base + m->attn_part + (size_t)b * m->attn_part_row)
+                             : (float *)(st[b]->base + st[b]->part);
         aa.kv_bytes[b] = (unsigned)st[b]->layer_bytes;
     }
 
@@ -766,7 +776,8 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
-    for (int b = 0; b < n; ++b) st[b]->pos += 1;
+    if (row_pos) st[0]->pos += n;
+    else for (int b = 0; b < n; ++b) st[b]->pos += 1;
     return PN_OK;
 }
 
@@ -1073,6 +1084,28 @@ int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int3
             if (states[j] == states[i]) return fail(PN_EINVAL, "state %d appears twice", i);
     }
     return forward_impl(m, states, n, tokens_dev, logits_dev, argmax_dev, S(stream));
+}
+
+int pn_prefill(pn_model *m, pn_state *s, const int32_t *tokens_dev, int32_t n, float *logits_dev,
+               int32_t *argmax_dev, void *stream) {
+    g_err.clear();
+    if (!m || !s || !tokens_dev) return fail(PN_EINVAL, "NULL argument");
+    if (s->m != m) return fail(PN_EINVAL, "state belongs to another model");
+    if (n < 1) return fail(PN_EINVAL, "n = %d must be >= 1", n);
+    if (s->pos < 0 || (long long)s->pos + n > s->max_ctx)
+        return fail(PN_ERANGE, "positions %d..%lld exceed max_ctx %d", s->pos, (long long)s->pos + n - 1, s->max_ctx);
+    // chunks of max_batch tokens, each one batched step over consecutive positions
+    const int chunk = m->cfg.max_batch;
+    std::vector<pn_state *> rows(chunk, s);
+    int rp[kMaxSlots];
+    for (int t0 = 0; t0 < n; t0 += chunk) {
+        const int c = std::min(chunk, n - t0);
+        for (int b = 0; b < c; ++b) rp[b] = s->pos + b;
+        if (int rc = forward_impl(m, rows.data(), c, tokens_dev + t0, logits_dev ? logits_dev + (size_t)t0 * m->V : nullptr,
+                                  argmax_dev ? argmax_dev + t0 : nullptr, S(stream), rp))
+            return rc;
+    }
+    return PN_OK;
 }
 
 int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling_params *params,

@@ -182,6 +182,12 @@ def forward_batch(model, states, tokens_dev, logits_dev=None, argmax_dev=None, s
                                      _ptr(argmax_dev), _stream_ptr(stream)))
 
 
+def prefill(model, state, tokens_dev, logits_dev=None, argmax_dev=None, stream=None):
+    """Feed tokens_dev [n] to the state at consecutive positions (chunks of max_batch)."""
+    C.check(C.lib().pn_prefill(model.h, state.h, _ptr(tokens_dev), int(tokens_dev.numel()), _ptr(logits_dev),
+                               _ptr(argmax_dev), _stream_ptr(stream)))
+
+
 def sample(model, logits_dev, params, u_dev, ids_dev, recent_dev=None, stream=None):
     """Sample one token per row of logits_dev [n][n_vocab] into ids_dev [n].
     params: a list of n dicts (temperature, repeat_penalty, top_k, top_p);
