@@ -102,6 +102,7 @@ typedef struct pn_weights {
 
 typedef struct pn_model pn_model;
 typedef struct pn_state pn_state;
+typedef struct pn_pool pn_pool;
 
 /* Fill *cfg with the pages' defaults; dimensions are left 0. */
 void pn_config_default(pn_config *cfg);
@@ -146,12 +147,15 @@ int pn_state_new(pn_model *m, int32_t max_ctx, void *dev_buf, size_t bytes, void
                  pn_state **out);
 
 /* Zero every cached K and V and set pos = 0 ("Core Engine API", section
- * "State lifecycle": reset zeros the kv tensors and resets pos). */
+ * "State lifecycle": reset zeros the kv tensors and resets pos).  A pooled
+ * state gives its pages back instead (a page is zeroed when next taken). */
 int pn_state_reset(pn_state *s, void *stream);
 
 /* Write cached K and V of positions pos0..pos0+n-1 of one layer from device
  * arrays k_dev, v_dev laid out [n][n_kv_head][head_dim] in kv_dtype (k after
- * RoPE).  Used to resume or to prefill a cache.  Does not change pos. */
+ * RoPE).  Used to resume or to prefill a cache.  Does not change pos.  A
+ * pooled state takes pages for those positions (PN_ERANGE if the pool runs
+ * out or if pos0 lies below pages that went back to the pool). */
 int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const void *k_dev,
                     const void *v_dev, void *stream);
 
@@ -163,8 +167,12 @@ int pn_state_set_page_table(pn_state *s, const int32_t *pages, int32_t n, void *
 int32_t pn_state_pages(const pn_state *s);
 int32_t pn_page_size(void);
 
-/* Number of positions already cached (the position the next step writes). */
-int pn_state_set_pos(pn_state *s, int32_t pos);
+/* Number of positions already cached (the position the next step writes).
+ * Moving pos leaves the cache as it is.  On a pooled state, the positions the
+ * next step reads get pages (zeroed, enqueued on `stream`) where they have
+ * none; PN_ERANGE if the pool runs out, or if that window reaches positions
+ * whose pages went back to the pool (see pn_state_new_pooled). */
+int pn_state_set_pos(pn_state *s, int32_t pos, void *stream);
 int32_t pn_state_pos(const pn_state *s);
 int32_t pn_state_max_ctx(const pn_state *s);
 
@@ -174,6 +182,56 @@ int32_t pn_state_max_ctx(const pn_state *s);
 int pn_state_check(pn_state *s, void *stream, int32_t *flags_out);
 
 void pn_state_free(pn_state *s);
+
+/* ---- shared page pool ------------------------------------------------------
+ *
+ * States of a continuously batched decode (sequences join and leave the batch
+ * between steps: "Serve Layer Architecture", section "Batched Decode", "D2 -
+ * continuous batching"; "Engine Architecture", section "Continuous-Batch VLM
+ * Decoder": a finished sequence's state is recycled for the next) can draw
+ * their K/V pages from one pool instead of each reserving max_ctx positions.
+ * A pooled state takes a page (page_size positions of every layer's K and V)
+ * when a step, a prefill, pn_state_set_kv or pn_state_set_pos first needs one,
+ * zeroes it, and gives every page back on pn_state_reset and pn_state_free
+ * (the pages' reset: "Core Engine API", section "State lifecycle").  With a
+ * sliding window, the pages wholly before the window of the state's next step
+ * go back to the pool after each step, so a windowed sequence holds at most
+ * about window / page_size + 2 pages however long it runs.  Results are those
+ * of private states, bit for bit.  The pool's page bookkeeping is host-side:
+ * all states of a pool must be driven from one thread and on one stream (a
+ * page returned by one state may be zeroed for another by the next call).
+ * When the pool runs out, the step, prefill chunk, set_kv or set_pos fails
+ * with PN_ERANGE before anything is enqueued for it and every state is as
+ * before that call (a prefill keeps the chunks it has already done: pos
+ * tells how far it got). */
+
+/* Bytes of device memory a pool of n_pages pages needs; 0 if n_pages < 1 or
+ * one layer's K pages would reach 2 GiB. */
+size_t pn_pool_bytes(const pn_model *m, int32_t n_pages);
+
+/* Create a pool of n_pages pages in `dev_buf` (>= pn_pool_bytes, 256-byte
+ * aligned).  Nothing is enqueued: pages are zeroed when a state takes them. */
+int pn_pool_new(pn_model *m, int32_t n_pages, void *dev_buf, size_t bytes, pn_pool **out);
+
+/* Pages not held by any state; -1 for NULL. */
+int32_t pn_pool_free_pages(const pn_pool *p);
+
+/* Release the pool's host handle; if states of the pool are alive, the handle
+ * goes with the last of them (the device buffer stays the caller's and must
+ * outlive every state of the pool). */
+void pn_pool_free(pn_pool *p);
+
+/* Bytes of device memory a pooled state of capacity max_ctx positions needs
+ * (page table and attention split scratch; its K/V live in the pool). */
+size_t pn_state_bytes_pooled(const pn_model *m, int32_t max_ctx);
+
+/* Create a state (pos = 0, no pages) whose K/V pages come from `pool` in
+ * `dev_buf` (>= pn_state_bytes_pooled, 256-byte aligned).  max_ctx bounds pos
+ * as for pn_state_new; pn_state_set_page_table is not available (the pool
+ * assigns pages).  Errors: PN_EINVAL (NULL, pool of another model or already
+ * freed), PN_ERANGE (buffer too small). */
+int pn_state_new_pooled(pn_model *m, pn_pool *pool, int32_t max_ctx, void *dev_buf, size_t bytes,
+                        void *stream, pn_state **out);
 
 /* One decode step of one sequence: embed token_dev[0], append its k and v at
  * pos, attend over the window ending at pos, run the FFN, and write the
@@ -201,7 +259,8 @@ int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int3
  * (the pages' chunked prefill: "Serve Layer Architecture", section "Batched
  * Decode", "L2 - chunked prefill"), so every weight is read once per chunk
  * instead of once per token.  Errors: PN_EINVAL (NULL pointer, n < 1, state
- * of another model), PN_ERANGE (pos + n > max_ctx). */
+ * of another model), PN_ERANGE (pos + n > max_ctx; a pooled state's pool ran
+ * out). */
 int pn_prefill(pn_model *m, pn_state *s, const int32_t *tokens_dev, int32_t n, float *logits_dev,
                int32_t *argmax_dev, void *stream);
 

@@ -113,6 +113,26 @@ def test_init_rejects_bad_buffers_without_device_work():
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KERNEL, 3) == C.PN_EINVAL
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_KERNEL, 2) == 0
         assert L.pn_profile_begin(h, 99) == C.PN_EINVAL
+        # shared page pool: sizing, creation and argument checks enqueue nothing
+        page = L.pn_pool_bytes(h, 1)
+        assert page > 0 and L.pn_pool_bytes(h, 10) == 10 * page
+        assert L.pn_pool_bytes(h, 0) == 0 and L.pn_pool_bytes(None, 4) == 0
+        assert L.pn_pool_bytes(h, 1 << 30) == 0  # one layer's K pages past 2 GiB
+        pool = ctypes.c_void_p()
+        assert L.pn_pool_new(h, 10, ctypes.c_void_p(1 << 24), 10 * page - 1, ctypes.byref(pool)) == C.PN_ERANGE
+        assert L.pn_pool_new(h, 10, ctypes.c_void_p((1 << 24) + 64), 10 * page, ctypes.byref(pool)) == C.PN_EINVAL
+        assert L.pn_pool_new(h, 0, ctypes.c_void_p(1 << 24), 10 * page, ctypes.byref(pool)) == C.PN_EINVAL
+        assert L.pn_pool_new(h, 10, ctypes.c_void_p(1 << 24), 10 * page, ctypes.byref(pool)) == 0
+        try:
+            assert L.pn_pool_free_pages(pool) == 10 and L.pn_pool_free_pages(None) == -1
+            sb = L.pn_state_bytes_pooled(h, 132)
+            assert 0 < sb < L.pn_state_bytes(h, 132)
+            assert L.pn_state_bytes_pooled(h, 2_000_000_000) > 0  # K/V live in the pool
+            assert L.pn_state_new_pooled(h, None, 64, ctypes.c_void_p(1 << 21), sb, None, ctypes.byref(st)) == C.PN_EINVAL
+            assert L.pn_state_new_pooled(h, pool, 132, ctypes.c_void_p(1 << 21), sb - 1, None,
+                                         ctypes.byref(st)) == C.PN_ERANGE
+        finally:
+            L.pn_pool_free(pool)
         # sampling: every argument is checked on the host before anything is enqueued
         sp = (C.pn_sampling_params * 2)()
         for i in range(2):

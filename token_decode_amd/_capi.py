@@ -76,7 +76,13 @@ def lib():
             "pn_state_set_page_table": (ctypes.c_int, [vp, P(i32), i32, vp]),
             "pn_state_pages": (i32, [vp]),
             "pn_page_size": (i32, []),
-            "pn_state_set_pos": (ctypes.c_int, [vp, i32]),
+            "pn_state_set_pos": (ctypes.c_int, [vp, i32, vp]),
+            "pn_pool_bytes": (sz, [vp, i32]),
+            "pn_pool_new": (ctypes.c_int, [vp, i32, vp, sz, P(vp)]),
+            "pn_pool_free_pages": (i32, [vp]),
+            "pn_pool_free": (None, [vp]),
+            "pn_state_bytes_pooled": (sz, [vp, i32]),
+            "pn_state_new_pooled": (ctypes.c_int, [vp, vp, i32, vp, sz, vp, P(vp)]),
             "pn_state_pos": (i32, [vp]),
             "pn_state_max_ctx": (i32, [vp]),
             "pn_state_check": (ctypes.c_int, [vp, vp, P(i32)]),
@@ -104,6 +110,8 @@ EXPORTS = ["pn_config_default", "pn_config_check", "pn_model_bytes", "pn_model_c
            "pn_state_bytes", "pn_state_new", "pn_state_reset", "pn_state_set_kv",
            "pn_state_set_page_table", "pn_state_pages", "pn_page_size", "pn_state_set_pos",
            "pn_state_pos", "pn_state_max_ctx", "pn_state_check", "pn_state_free",
+           "pn_pool_bytes", "pn_pool_new", "pn_pool_free_pages", "pn_pool_free", "pn_state_bytes_pooled",
+           "pn_state_new_pooled",
            "pn_forward_step", "pn_forward_batch", "pn_prefill", "pn_sample", "pn_model_set_option", "pn_profile_begin",
            "pn_profile_end", "pn_profile_replay", "pn_last_error"]
 

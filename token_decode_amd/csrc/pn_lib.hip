@@ -112,12 +112,29 @@ struct pn_model {
     size_t replay_kv = 0, replay_pt = 0;
 };
 
+// A page pool shared by states: K pages then V pages, each [layer][page][Hk][kPage][D].
+struct pn_pool {
+    pn_model *m;
+    char *base;
+    size_t bytes;
+    int n_pages;
+    size_t layer_bytes, kpool, vpool;
+    std::vector<int> free_pages;  // a stack of free page ids
+    int users = 0;                // states created on the pool and not yet freed
+    bool closed = false;          // pn_pool_free called: delete with the last state
+};
+
 struct pn_state {
     pn_model *m;
     char *base;
     size_t bytes;
     int max_ctx, n_pages, pos, s_cap;
+    // K/V pages: the state's own pools (offsets from base), or a shared pool's
+    // (offsets from pool->base)
     size_t kpool, vpool, layer_bytes, pt, part, err;
+    pn_pool *pool = nullptr;
+    std::vector<int> phys;  // pooled: physical page of each logical page, -1 = none
+    int kept_from = 0;      // pooled: logical pages below this were returned to the pool
 };
 
 namespace {
@@ -343,14 +360,19 @@ size_t layout_state(pn_state *s) {
     const pn_model *m = s->m;
     s->n_pages = cdiv(s->max_ctx, kPage);
     const int es = dtype_size(m->kvt);
-    s->layer_bytes = (size_t)s->n_pages * m->Hk * kPage * m->D * es;
+    s->layer_bytes = s->pool ? s->pool->layer_bytes : (size_t)s->n_pages * m->Hk * kPage * m->D * es;
     int keys = s->max_ctx;
     if (m->cfg.sliding_window > 0) keys = std::min(keys, m->cfg.sliding_window);
     // splits start on page boundaries, so a window may touch one more chunk
     s->s_cap = std::min(cdiv(keys + kPage - 1, kAttnChunk), kMaxSplits);
     Bump bp;
-    s->kpool = bp.take(s->layer_bytes * m->cfg.n_layer);
-    s->vpool = bp.take(s->layer_bytes * m->cfg.n_layer);
+    if (s->pool) {
+        s->kpool = s->pool->kpool;
+        s->vpool = s->pool->vpool;
+    } else {
+        s->kpool = bp.take(s->layer_bytes * m->cfg.n_layer);
+        s->vpool = bp.take(s->layer_bytes * m->cfg.n_layer);
+    }
     s->pt = bp.take((size_t)s->n_pages * 4);
     s->part = bp.take((size_t)m->Hk * s->s_cap * m->G * (m->D + 4) * 4);
     s->err = bp.take(4);
@@ -358,6 +380,96 @@ size_t layout_state(pn_state *s) {
 }
 
 hipStream_t S(void *stream) { return reinterpret_cast<hipStream_t>(stream); }
+
+// One layer's K (or V) pages of a state.
+char *kv_layer(const pn_state *s, int layer, bool v) {
+    char *b = s->pool ? s->pool->base : s->base;
+    return b + (v ? s->vpool : s->kpool) + (size_t)layer * s->layer_bytes;
+}
+
+int launched(const char *what, const Plan *p = nullptr);
+
+// Zero the pages of a set (all layers, K and V) and write their page-table
+// entries; every page of the set comes from one pool.
+void flush_pages(const pn_pool *pool, PageSet &ps, hipStream_t st) {
+    if (ps.n > 0) {
+        const pn_model *m = pool->m;
+        const long long words = (long long)(pool->layer_bytes / pool->n_pages / 16);
+        const dim3 grid((unsigned)std::min<long long>(cdiv(words, 256), 64), ps.n, 2 * m->cfg.n_layer);
+        hipLaunchKernelGGL(k_zero_pages, grid, dim3(256), 0, st, pool->base + pool->kpool, pool->base + pool->vpool,
+                           pool->layer_bytes, words, ps);
+        hipLaunchKernelGGL(k_set_pages, dim3(1), dim3(kPageSetMax), 0, st, ps);
+    }
+    ps.n = 0;
+}
+
+// Pooled states: a page of the pool for every logical page of positions [p0[b],
+// p1[b]) of each state that has none, all or nothing: on running out, the
+// pages this call took go back (their page-table entries are never read: a
+// logical page is read only after a call gave it a page).  New pages hold
+// zeros, as a private cache does where nothing was written.
+int ensure_pages(pn_state *const *st, int n, const int *p0, const int *p1, hipStream_t s) {
+    PageSet ps{};
+    const pn_pool *cur = nullptr;
+    std::vector<std::pair<pn_state *, int>> taken;
+    for (int b = 0; b < n; ++b) {
+        pn_state *x = st[b];
+        if (!x->pool || p1[b] <= p0[b]) continue;
+        if (x->pool != cur) flush_pages(cur, ps, s);
+        cur = x->pool;
+        for (int lp = p0[b] / kPage; lp <= (p1[b] - 1) / kPage; ++lp) {
+            if (x->phys[lp] >= 0) continue;
+            if (x->pool->free_pages.empty()) {
+                flush_pages(cur, ps, s);
+                for (auto &t : taken) {
+                    t.first->pool->free_pages.push_back(t.first->phys[t.second]);
+                    t.first->phys[t.second] = -1;
+                }
+                return fail(PN_ERANGE, "page pool exhausted (%d pages)", x->pool->n_pages);
+            }
+            const int pg = x->pool->free_pages.back();
+            x->pool->free_pages.pop_back();
+            x->phys[lp] = pg;
+            taken.push_back({x, lp});
+            ps.pt[ps.n] = (int *)(x->base + x->pt);
+            ps.idx[ps.n] = lp;
+            ps.val[ps.n] = pg;
+            if (++ps.n == kPageSetMax) flush_pages(cur, ps, s);
+        }
+    }
+    flush_pages(cur, ps, s);
+    return launched("page assignment", nullptr);
+}
+
+// First position the window of a step at pos reads (0 without a window).
+int window_lo(const pn_model *m, int pos) {
+    const int W = m->cfg.sliding_window;
+    return W > 0 ? std::max(0, pos - W + 1) : 0;
+}
+
+// Pooled states with a window: return the pages wholly before the window of
+// the state's next step.
+void recycle_pages(pn_state *x) {
+    if (!x->pool || x->m->cfg.sliding_window <= 0) return;
+    const int lo = window_lo(x->m, x->pos);
+    for (int lp = x->kept_from; lp < lo / kPage; ++lp)
+        if (x->phys[lp] >= 0) {
+            x->pool->free_pages.push_back(x->phys[lp]);
+            x->phys[lp] = -1;
+        }
+    x->kept_from = std::max(x->kept_from, lo / kPage);
+}
+
+// Pooled states: every page back to the pool.
+void give_back_all(pn_state *x) {
+    if (!x->pool) return;
+    for (int &pg : x->phys)
+        if (pg >= 0) {
+            x->pool->free_pages.push_back(pg);
+            pg = -1;
+        }
+    x->kept_from = 0;
+}
 
 void fill32(void *p, size_t words, uint32_t v, hipStream_t s) {
     if (!words) return;
@@ -435,7 +547,7 @@ void record_gemm(pn_model *m, int cls, int kind, const GemmArgs &g, const Plan &
 }
 
 // the launch just enqueued, checked at once so that a failure names its kernel
-int launched(const char *what, const Plan *p = nullptr) {
+int launched(const char *what, const Plan *p) {
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return PN_OK;
     if (p)
@@ -531,16 +643,15 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     // keys per split (PN_OPT_ATTN_KEYS_PER_SPLIT), else from sharing about
     // kAttnTargetGroups work-groups among the slots in proportion to their
     // pages; it is at most the slot's pages and its scratch capacity.
-    auto window_lo = [&](int pos) { return c.sliding_window > 0 ? std::max(0, pos - c.sliding_window + 1) : 0; };
     long long np_sum = 0;
     for (int b = 0; b < n; ++b) {
         const int pos = posof(b);
-        np_sum += cdiv(pos + 1 - window_lo(pos) / kPage * kPage, kPage);
+        np_sum += cdiv(pos + 1 - window_lo(m, pos) / kPage * kPage, kPage);
     }
     int nsplit_max = 1;
     for (int b = 0; b < n; ++b) {
         const int pos = posof(b);
-        const int lo = window_lo(pos);
+        const int lo = window_lo(m, pos);
         aa.pos[b] = pos;
         aa.lo[b] = lo;
         aa.origin[b] = lo / kPage * kPage;
@@ -595,8 +706,8 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.gain = (const float *)(mb + L.attn_norm);
             g.q_out = (float *)(mb + m->q);
             for (int b = 0; b < n; ++b) {
-                g.kvk[b] = st[b]->base + st[b]->kpool + (size_t)l * st[b]->layer_bytes;
-                g.kvv[b] = st[b]->base + st[b]->vpool + (size_t)l * st[b]->layer_bytes;
+                g.kvk[b] = kv_layer(st[b], l, false);
+                g.kvv[b] = kv_layer(st[b], l, true);
             }
             Timed tm(m, PN_K_QKV, s);
             launch_gemm(GK_QKV, wt, at, g, p_qkv, s);
@@ -606,8 +717,8 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         // ---- attention (+ split combine)
         {
             for (int b = 0; b < n; ++b) {
-                aa.kvk[b] = st[b]->base + st[b]->kpool + (size_t)l * st[b]->layer_bytes;
-                aa.kvv[b] = st[b]->base + st[b]->vpool + (size_t)l * st[b]->layer_bytes;
+                aa.kvk[b] = kv_layer(st[b], l, false);
+                aa.kvv[b] = kv_layer(st[b], l, true);
             }
             aa.kind = m->attn_kind == 1 ? 0 : 1;
             Timed tm(m, PN_K_ATTN, s);
@@ -778,6 +889,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     if (e != hipSuccess) return fail(PN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     if (row_pos) st[0]->pos += n;
     else for (int b = 0; b < n; ++b) st[b]->pos += 1;
+    for (int b = 0; b < n; ++b) recycle_pages(st[b]);
     return PN_OK;
 }
 
@@ -958,8 +1070,12 @@ int pn_state_reset(pn_state *s, void *stream) {
     g_err.clear();
     if (!s) return fail(PN_EINVAL, "state is NULL");
     hipStream_t st = S(stream);
-    fill32(s->base + s->kpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
-    fill32(s->base + s->vpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
+    if (s->pool) {
+        give_back_all(s);  // new pages are zeroed when taken
+    } else {
+        fill32(s->base + s->kpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
+        fill32(s->base + s->vpool, s->layer_bytes * s->m->cfg.n_layer / 4, 0u, st);
+    }
     fill32(s->base + s->err, 1, 0u, st);
     s->pos = 0;
     hipError_t e = hipGetLastError();
@@ -1000,6 +1116,95 @@ int pn_state_new(pn_model *m, int32_t max_ctx, void *dev_buf, size_t bytes, void
     return PN_OK;
 }
 
+// Bytes of one page (all positions and KV heads of one layer's K or V pool).
+size_t pool_page_bytes(const pn_model *m) { return (size_t)m->Hk * kPage * m->D * dtype_size(m->kvt); }
+
+size_t pn_pool_bytes(const pn_model *m, int32_t n_pages) {
+    if (!m || n_pages < 1) return 0;
+    const size_t layer = pool_page_bytes(m) * n_pages;
+    if (layer >= kMaxLayerBytes) return 0;
+    return 2 * layer * m->cfg.n_layer;
+}
+
+int pn_pool_new(pn_model *m, int32_t n_pages, void *dev_buf, size_t bytes, pn_pool **out) {
+    g_err.clear();
+    if (!out) return fail(PN_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!m || !dev_buf) return fail(PN_EINVAL, "model or device buffer is NULL");
+    if (((uintptr_t)dev_buf & 255) != 0) return fail(PN_EINVAL, "device buffer must be 256-byte aligned");
+    if (n_pages < 1) return fail(PN_EINVAL, "n_pages must be >= 1");
+    const size_t need = pn_pool_bytes(m, n_pages);
+    if (need == 0) return fail(PN_ERANGE, "%d pages: one layer's K pool would reach 2 GiB", n_pages);
+    if (bytes < need) return fail(PN_ERANGE, "pool buffer too small: %zu < %zu", bytes, need);
+    pn_pool *p = new pn_pool{};
+    p->m = m;
+    p->base = (char *)dev_buf;
+    p->bytes = bytes;
+    p->n_pages = n_pages;
+    p->layer_bytes = pool_page_bytes(m) * n_pages;
+    p->kpool = 0;
+    p->vpool = p->layer_bytes * m->cfg.n_layer;
+    p->free_pages.resize(n_pages);
+    for (int i = 0; i < n_pages; ++i) p->free_pages[i] = n_pages - 1 - i;  // page 0 is taken first
+    *out = p;
+    return PN_OK;
+}
+
+void pn_pool_free(pn_pool *p) {
+    if (!p) return;
+    p->closed = true;
+    if (p->users == 0) delete p;
+}
+
+int32_t pn_pool_free_pages(const pn_pool *p) { return p ? (int32_t)p->free_pages.size() : -1; }
+
+size_t pn_state_bytes_pooled(const pn_model *m, int32_t max_ctx) {
+    if (!m) return 0;
+    if (max_ctx == 0) max_ctx = m->cfg.n_ctx;
+    if (max_ctx < 1) return 0;
+    pn_pool dummy{};
+    pn_state s{};
+    s.m = const_cast<pn_model *>(m);
+    s.max_ctx = max_ctx;
+    s.pool = &dummy;
+    return layout_state(&s);
+}
+
+int pn_state_new_pooled(pn_model *m, pn_pool *pool, int32_t max_ctx, void *dev_buf, size_t bytes, void *stream,
+                        pn_state **out) {
+    g_err.clear();
+    if (!out) return fail(PN_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!m || !pool || !dev_buf) return fail(PN_EINVAL, "model, pool or device buffer is NULL");
+    if (pool->m != m) return fail(PN_EINVAL, "pool belongs to another model");
+    if (pool->closed) return fail(PN_EINVAL, "pool was freed");
+    if (((uintptr_t)dev_buf & 255) != 0) return fail(PN_EINVAL, "device buffer must be 256-byte aligned");
+    if (max_ctx == 0) max_ctx = m->cfg.n_ctx;
+    if (max_ctx < 1) return fail(PN_EINVAL, "max_ctx must be >= 1");
+    pn_state *s = new pn_state{};
+    s->m = m;
+    s->max_ctx = max_ctx;
+    s->pool = pool;
+    const size_t need = layout_state(s);
+    if (bytes < need) {
+        delete s;
+        return fail(PN_ERANGE, "state buffer too small: %zu < %zu", bytes, need);
+    }
+    s->base = (char *)dev_buf;
+    s->bytes = bytes;
+    s->phys.assign(s->n_pages, -1);
+    // entries without a page are never read; 0 keeps every entry inside the pool
+    fill32(s->base + s->pt, s->n_pages, 0u, S(stream));
+    pool->users += 1;
+    int rc = pn_state_reset(s, stream);
+    if (rc) {
+        pn_state_free(s);
+        return rc;
+    }
+    *out = s;
+    return PN_OK;
+}
+
 int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const void *k, const void *v,
                     void *stream) {
     g_err.clear();
@@ -1008,8 +1213,14 @@ int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const v
     if (layer < 0 || layer >= m->cfg.n_layer) return fail(PN_EINVAL, "layer %d out of range", layer);
     if (n < 0 || pos0 < 0 || (long long)pos0 + n > s->max_ctx) return fail(PN_ERANGE, "positions out of range");
     if (n == 0) return PN_OK;
-    char *kp = s->base + s->kpool + (size_t)layer * s->layer_bytes;
-    char *vp = s->base + s->vpool + (size_t)layer * s->layer_bytes;
+    if (s->pool) {
+        if (pos0 < s->kept_from * kPage)
+            return fail(PN_ERANGE, "positions below %d went back to the page pool", s->kept_from * kPage);
+        const int p1 = pos0 + n;
+        if (int rc = ensure_pages(&s, 1, &pos0, &p1, S(stream))) return rc;
+    }
+    char *kp = kv_layer(s, layer, false);
+    char *vp = kv_layer(s, layer, true);
     long long total = (long long)n * m->Hk * m->D;
     dim3 grid(cdiv(total, 256));
     if (m->kvt == PN_BF16)
@@ -1026,6 +1237,7 @@ int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const v
 int pn_state_set_page_table(pn_state *s, const int32_t *pages, int32_t n, void *stream) {
     g_err.clear();
     if (!s || !pages) return fail(PN_EINVAL, "NULL argument");
+    if (s->pool) return fail(PN_EUNSUPPORTED, "a pooled state's pages come from its pool");
     if (n != s->n_pages) return fail(PN_EINVAL, "page table must have %d entries", s->n_pages);
     std::vector<char> seen(n, 0);
     for (int i = 0; i < n; ++i) {
@@ -1041,10 +1253,18 @@ int pn_state_set_page_table(pn_state *s, const int32_t *pages, int32_t n, void *
 int32_t pn_state_pages(const pn_state *s) { return s ? s->n_pages : 0; }
 int32_t pn_page_size(void) { return kPage; }
 
-int pn_state_set_pos(pn_state *s, int32_t pos) {
+int pn_state_set_pos(pn_state *s, int32_t pos, void *stream) {
     g_err.clear();
     if (!s) return fail(PN_EINVAL, "state is NULL");
     if (pos < 0 || pos > s->max_ctx) return fail(PN_ERANGE, "pos %d out of range", pos);
+    if (s->pool) {
+        // the next step reads the window [lo, pos]: its pages below pos must exist
+        const int lo = window_lo(s->m, pos);
+        if (lo / kPage < s->kept_from)
+            return fail(PN_ERANGE, "pos %d reads positions below %d, which went back to the page pool", pos,
+                        s->kept_from * kPage);
+        if (int rc = ensure_pages(&s, 1, &lo, &pos, S(stream))) return rc;
+    }
     s->pos = pos;
     return PN_OK;
 }
@@ -1067,6 +1287,10 @@ int pn_state_check(pn_state *s, void *stream, int32_t *flags_out) {
 void pn_state_free(pn_state *s) {
     if (!s) return;
     for (auto &r : s->m->last) r.clear();  // recorded launches may point into this state
+    if (pn_pool *p = s->pool) {
+        give_back_all(s);
+        if (--p->users == 0 && p->closed) delete p;
+    }
     delete s;
 }
 
@@ -1083,6 +1307,12 @@ int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int3
         for (int j = 0; j < i; ++j)
             if (states[j] == states[i]) return fail(PN_EINVAL, "state %d appears twice", i);
     }
+    int p0[kMaxSlots], p1[kMaxSlots];
+    for (int i = 0; i < n; ++i) {
+        p0[i] = states[i]->pos;
+        p1[i] = states[i]->pos + 1;
+    }
+    if (int rc = ensure_pages(states, n, p0, p1, S(stream))) return rc;
     return forward_impl(m, states, n, tokens_dev, logits_dev, argmax_dev, S(stream));
 }
 
@@ -1100,6 +1330,8 @@ int pn_prefill(pn_model *m, pn_state *s, const int32_t *tokens_dev, int32_t n, f
     int rp[kMaxSlots];
     for (int t0 = 0; t0 < n; t0 += chunk) {
         const int c = std::min(chunk, n - t0);
+        const int p1 = s->pos + c;
+        if (int rc = ensure_pages(&s, 1, &s->pos, &p1, S(stream))) return rc;
         for (int b = 0; b < c; ++b) rp[b] = s->pos + b;
         if (int rc = forward_impl(m, rows.data(), c, tokens_dev + t0, logits_dev ? logits_dev + (size_t)t0 * m->V : nullptr,
                                   argmax_dev ? argmax_dev + t0 : nullptr, S(stream), rp))

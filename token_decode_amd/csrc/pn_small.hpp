@@ -309,6 +309,29 @@ __global__ void __launch_bounds__(256) k_copy_bytes(uint8_t *dst, const uint8_t 
         dst[i] = src[i];
 }
 
+// Page-table writes of pooled states: entry idx[i] of table pt[i] = val[i].
+constexpr int kPageSetMax = 64;
+struct PageSet {
+    int *pt[kPageSetMax];
+    int idx[kPageSetMax], val[kPageSetMax];
+    int n;
+};
+__global__ void __launch_bounds__(kPageSetMax) k_set_pages(PageSet p) {
+    const int i = threadIdx.x;
+    if (i < p.n) p.pt[i][p.idx[i]] = p.val[i];
+}
+
+// Zero pages of a shared pool before they join a state: page val[y] of every
+// layer's K (z even) and V (z odd) pools, 16 bytes per thread.
+__global__ void __launch_bounds__(256) k_zero_pages(char *kbase, char *vbase, size_t layer_bytes,
+                                                     long long page_words, PageSet p) {
+    const int layer = blockIdx.z >> 1;
+    char *pool = ((blockIdx.z & 1) ? vbase : kbase) + (size_t)layer * layer_bytes;
+    uint4 *pg = reinterpret_cast<uint4 *>(pool) + (long long)p.val[blockIdx.y] * page_words;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < page_words; i += (long long)gridDim.x * 256)
+        pg[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // Scatter K and V of positions pos0..pos0+n-1 ([n][Hk][D]) into the pages of one
 // layer (each head's block of a page laid out as kv_k_off / kv_v_off say).
 template <int ES>

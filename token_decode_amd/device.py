@@ -116,27 +116,63 @@ class DeviceModel:
         return ms.value, n.value
 
 
-class DeviceState:
-    """A decode state (paged KV cache + position) in a torch-allocated device buffer."""
+class DevicePool:
+    """A shared pool of K/V pages for pooled states, in a torch-allocated device buffer."""
 
-    def __init__(self, model: DeviceModel, max_ctx: int, stream=None, device="cuda"):
+    def __init__(self, model: DeviceModel, n_pages: int, device="cuda"):
         L = C.lib()
         self.model = model
-        nbytes = L.pn_state_bytes(model.h, max_ctx)
+        nbytes = L.pn_pool_bytes(model.h, n_pages)
         if nbytes == 0:
-            raise C.PNError(C.PN_EINVAL, "invalid state capacity %d" % max_ctx)
+            raise C.PNError(C.PN_ERANGE, "invalid pool size %d pages" % n_pages)
         self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         h = ctypes.c_void_p()
-        C.check(L.pn_state_new(model.h, max_ctx, ctypes.c_void_p(_aligned(self.buf)), nbytes,
-                               _stream_ptr(stream), ctypes.byref(h)))
+        C.check(L.pn_pool_new(model.h, n_pages, ctypes.c_void_p(_aligned(self.buf)), nbytes, ctypes.byref(h)))
         self.h = h
         self._L = L
+
+    @property
+    def free_pages(self):
+        return self._L.pn_pool_free_pages(self.h)
 
     def __del__(self):
         h, L = getattr(self, "h", None), getattr(self, "_L", None)
         if h is not None and h.value and L is not None:
-            L.pn_state_free(h)
+            L.pn_pool_free(h)
             self.h = None
+
+
+class DeviceState:
+    """A decode state (paged KV cache + position) in a torch-allocated device
+    buffer; with `pool`, its K/V pages come from that shared pool."""
+
+    def __init__(self, model: DeviceModel, max_ctx: int, stream=None, device="cuda", pool: DevicePool = None):
+        L = C.lib()
+        self.model = model
+        self.pool = pool  # the pool outlives its states
+        nbytes = L.pn_state_bytes_pooled(model.h, max_ctx) if pool else L.pn_state_bytes(model.h, max_ctx)
+        if nbytes == 0:
+            raise C.PNError(C.PN_EINVAL, "invalid state capacity %d" % max_ctx)
+        self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        if pool:
+            C.check(L.pn_state_new_pooled(model.h, pool.h, max_ctx, ctypes.c_void_p(_aligned(self.buf)), nbytes,
+                                          _stream_ptr(stream), ctypes.byref(h)))
+        else:
+            C.check(L.pn_state_new(model.h, max_ctx, ctypes.c_void_p(_aligned(self.buf)), nbytes,
+                                   _stream_ptr(stream), ctypes.byref(h)))
+        self.h = h
+        self._L = L
+
+    def free(self):
+        """Release the state now (a pooled state's pages go back to its pool)."""
+        h, L = getattr(self, "h", None), getattr(self, "_L", None)
+        if h is not None and h.value and L is not None:
+            L.pn_state_free(h)
+        self.h = None
+
+    def __del__(self):
+        self.free()
 
     @property
     def pos(self):
@@ -144,7 +180,10 @@ class DeviceState:
 
     @pos.setter
     def pos(self, p):
-        C.check(C.lib().pn_state_set_pos(self.h, int(p)))
+        self.set_pos(p)
+
+    def set_pos(self, p, stream=None):
+        C.check(C.lib().pn_state_set_pos(self.h, int(p), _stream_ptr(stream)))
 
     @property
     def n_pages(self):
