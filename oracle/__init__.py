@@ -33,6 +33,7 @@ class Config(ctypes.Structure):
         ("n_expert_used", ctypes.c_int32), ("sliding_window", ctypes.c_int32),
         ("rope_theta", ctypes.c_double), ("rms_norm_eps", ctypes.c_double),
         ("w_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+        ("rope_neox", ctypes.c_int32),
     ]
 
 
@@ -55,6 +56,8 @@ def lib():
         L.orc_rmsnorm.restype = None
         L.orc_rope.argtypes = [vp, i32, i32, dbl]
         L.orc_rope.restype = None
+        L.orc_rope_neox.argtypes = [vp, i32, i32, dbl]
+        L.orc_rope_neox.restype = None
         L.orc_attend.argtypes = [vp, vp, vp, i32, i32, vp]
         L.orc_attend.restype = None
         L.orc_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
@@ -113,6 +116,13 @@ def rope(u, pos, theta):
     return u
 
 
+def rope_neox(u, pos, theta):
+    """Half-split (NeoX) RoPE of one head vector u [d] at position pos."""
+    u = _f64(u).copy()
+    lib().orc_rope_neox(_ptr(u), u.size, pos, theta)
+    return u
+
+
 def attend(q, K, V):
     q, K, V = _f64(q), _f64(K), _f64(V)
     o = np.empty(q.size)
@@ -158,7 +168,7 @@ def config_of(wl) -> Config:
     return Config(wl.n_layer, wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim, wl.n_ff,
                   wl.n_vocab, wl.n_expert, wl.n_expert_used, wl.sliding_window,
                   float(wl.rope_theta), float(wl.rms_norm_eps), wl.w_dtype, wl.kv_dtype,
-                  wl.act_dtype)
+                  wl.act_dtype, int(wl.rope_neox))
 
 
 class Model:
@@ -185,6 +195,8 @@ class Model:
                 tab[b + 2 + i] = _ptr(L[name])
                 tab[b + 6 + i] = _ptr(L["s_" + name[1:]])
             tab[b + 10] = _ptr(L["w_router"])
+            for i, name in enumerate(("b_q", "b_k", "b_v")):
+                tab[b + 11 + i] = _ptr(L.get(name))
             for e in range(len(L["w_gate"])):
                 eb = b + 16 + 6 * e
                 tab[eb + 0] = _ptr(L["w_gate"][e])

@@ -26,10 +26,14 @@
  *   - greedy decoding = argmax of the logits (Engine Architecture, section
  *     "Sampling", temperature 0);
  *   - quantised weights dequantised inside the mat-vec, norms kept in F32
- *     (Engine Architecture, section "Weight Loading Modes").
+ *     (Engine Architecture, section "Weight Loading Modes");
+ *   - the variants that share the Llama forward through config flags:
+ *     attention biases (Qwen2) and, from Phi-3, the NeoX half-split RoPE
+ *     (Engine Architecture, section "Architecture Detection").
  * Where the pages are silent the plain Llama reading is taken: RMSNorm with
  * eps inside the root; RoPE on adjacent pairs (2i, 2i+1) with
- * w_i = theta^(-2i/d), applied to q and k only, k cached after rotation;
+ * w_i = theta^(-2i/d) (NeoX: on the pairs (i, i + d/2), same w_i), applied to
+ * q and k only, after the biases, k cached after rotation;
  * query head h reads kv head floor(h / (n_head / n_kv_head)); scores scaled by
  * 1/sqrt(d); the window holds the keys t with pos - W < t <= pos; SwiGLU FFN
  * down(silu(gate x) * up x); MoE softmax router, top-k with ties to the lower
@@ -63,6 +67,7 @@ typedef struct {
     int32_t n_expert, n_expert_used, sliding_window;
     double rope_theta, rms_norm_eps;
     int32_t w_dtype, kv_dtype, act_dtype;
+    int32_t rope_neox; /* 1: rotate the half-split pairs (i, i + d/2) */
 } orc_config;
 
 /* Weight table (array of pointers, all host memory, matrices row-major [out][in]):
@@ -72,11 +77,12 @@ typedef struct {
  *   +0 attn_norm  +1 ffn_norm  +2 wq [H*d][E]  +3 wk [Hk*d][E]  +4 wv [Hk*d][E]
  *   +5 wo [E][H*d]  +6..+9 row scales of q, k, v, o (int8 only)
  *   +10 router [n_expert][E] (fp32 when w_dtype is fp32, else bf16)
+ *   +11..+13 q, k, v biases [H*d], [Hk*d], [Hk*d] fp32, or NULL (no bias)
  *   +16 + 6e: gate [F][E], up [F][E], down [E][F], then their row scales.  */
 int orc_layer_stride(const orc_config *c) { return 16 + 6 * (c->n_expert > 0 ? c->n_expert : 1); }
 
 enum { T_EMBD = 0, T_OUT_NORM = 1, T_OUT = 2, T_S_OUT = 3, T_LAYER0 = 4 };
-enum { L_ATTN_NORM = 0, L_FFN_NORM, L_WQ, L_WK, L_WV, L_WO, L_SQ, L_SK, L_SV, L_SO, L_ROUTER };
+enum { L_ATTN_NORM = 0, L_FFN_NORM, L_WQ, L_WK, L_WV, L_WO, L_SQ, L_SK, L_SV, L_SO, L_ROUTER, L_BQ, L_BK, L_BV };
 
 /* ------------------------------------------------------------------ rounding */
 
@@ -150,6 +156,21 @@ void orc_rope(double *u, int d, int pos, double theta) {
         double a = u[2 * i], b = u[2 * i + 1];
         u[2 * i] = a * c - b * s;
         u[2 * i + 1] = a * s + b * c;
+    }
+}
+
+/* NeoX form: rotate pairs (u[i], u[i + d/2]) of one head vector by
+ * pos * theta^(-2i/d) (the half-split RoPE that "Engine Architecture",
+ * section "Architecture Detection", names for Phi-3) */
+void orc_rope_neox(double *u, int d, int pos, double theta) {
+    int h = d / 2;
+    for (int i = 0; i < h; ++i) {
+        double w = pow(theta, -2.0 * (double)i / (double)d);
+        double phi = (double)pos * w;
+        double c = cos(phi), s = sin(phi);
+        double a = u[i], b = u[i + h];
+        u[i] = a * c - b * s;
+        u[i + h] = a * s + b * c;
     }
 }
 
@@ -372,7 +393,15 @@ static double ffn(const orc_config *c, const void *const *tab, int lb, double *x
     return gap;
 }
 
-/* q, k, v of one token at position pos: round_act(RMSNorm(x)*g), projections, RoPE */
+/* y[r] += b[r] when the bias exists */
+static void add_bias(double *y, const void *b, int n) {
+    if (!b) return;
+    for (int r = 0; r < n; ++r) y[r] += (double)((const float *)b)[r];
+}
+
+/* q, k, v of one token at position pos: round_act(RMSNorm(x)*g), projections,
+ * biases (Qwen2's attention biases: "Engine Architecture", section
+ * "Architecture Detection"), RoPE */
 static void qkv(const orc_config *c, const void *const *tab, int lb, const double *x, int pos,
                 scratch *s) {
     int E = c->n_embd, d = c->head_dim, H = c->n_head, Hk = c->n_kv_head;
@@ -381,8 +410,12 @@ static void qkv(const orc_config *c, const void *const *tab, int lb, const doubl
     matvec(T(tab, lb + L_WQ), wdt(c), (const float *)T(tab, lb + L_SQ), H * d, E, s->xn, s->q);
     matvec(T(tab, lb + L_WK), wdt(c), (const float *)T(tab, lb + L_SK), Hk * d, E, s->xn, s->k);
     matvec(T(tab, lb + L_WV), wdt(c), (const float *)T(tab, lb + L_SV), Hk * d, E, s->xn, s->v);
-    for (int h = 0; h < H; ++h) orc_rope(s->q + (size_t)h * d, d, pos, c->rope_theta);
-    for (int j = 0; j < Hk; ++j) orc_rope(s->k + (size_t)j * d, d, pos, c->rope_theta);
+    add_bias(s->q, T(tab, lb + L_BQ), H * d);
+    add_bias(s->k, T(tab, lb + L_BK), Hk * d);
+    add_bias(s->v, T(tab, lb + L_BV), Hk * d);
+    void (*rot)(double *, int, int, double) = c->rope_neox ? orc_rope_neox : orc_rope;
+    for (int h = 0; h < H; ++h) rot(s->q + (size_t)h * d, d, pos, c->rope_theta);
+    for (int j = 0; j < Hk; ++j) rot(s->k + (size_t)j * d, d, pos, c->rope_theta);
 }
 
 /* x += W_o * round_act(o) */

@@ -38,8 +38,10 @@ TID_POSITIONS = (1 << 20) + 1
 TID_KV = 1 << 21
 
 J_ATTN_NORM, J_WQ, J_WK, J_WV, J_WO, J_FFN_NORM, J_ROUTER = 0, 1, 2, 3, 4, 5, 6
+J_BQ, J_BK, J_BV = 40, 41, 42
 W_STD = 0.02
 GAIN_STD = 0.1
+BIAS_STD = 0.5
 
 
 def build(force: bool = False) -> str:
@@ -142,6 +144,8 @@ class Workload:
     w_dtype: int = F32
     kv_dtype: int = F32
     act_dtype: int = F32
+    rope_neox: bool = False      # half-split RoPE pairs (i, i + d/2)
+    qkv_bias: bool = False       # q, k, v projections carry fp32 biases
     seed: int = 1
     slots: int = 1
     steps: int = 8
@@ -240,6 +244,9 @@ def make_layer(wl: Workload, l: int, threads=None) -> dict:
         m, s = _matrix(wl, wl.tid_layer(l, j), rows, cols, threads)
         out[name] = m
         out["s_" + name[1:]] = s
+    for name, j, rows in (("b_q", J_BQ, H * d), ("b_k", J_BK, Hk * d), ("b_v", J_BV, Hk * d)):
+        out[name] = (normal(wl.seed, wl.tid_layer(l, j), rows, 0.0, BIAS_STD, F32, threads=threads)
+                     if wl.qkv_bias else None)
     gates, ups, downs, sg, su, sd = [], [], [], [], [], []
     for e in range(wl.n_experts_stored):
         m, s = _matrix(wl, wl.tid_expert(l, e, 0), F, E, threads)

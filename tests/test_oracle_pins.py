@@ -65,6 +65,38 @@ def test_rope_matches_complex_rotation(d, theta):
                                    rtol=0, atol=1e-12)
 
 
+def _rope_half_split_complex(u, pos, theta):
+    """NeoX RoPE as a complex product: z_i = u_i + 1j * u_{i+d/2} (numpy complex)."""
+    d = u.size
+    h = d // 2
+    freqs = theta ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    z = (u[:h] + 1j * u[h:]) * np.exp(1j * pos * freqs)
+    return np.concatenate([z.real, z.imag])
+
+
+@pytest.mark.parametrize("d,theta", [(32, 1e4), (128, 1e6), (64, 1e4)])
+def test_rope_neox_matches_half_split_complex_rotation(d, theta):
+    for pos in (0, 1, 9, 4096, 30001):
+        u = rng.standard_normal(d)
+        # the angle pos * w carries pos * ulp(w) of difference between the two ways of computing w
+        np.testing.assert_allclose(oracle.rope_neox(u, pos, theta), _rope_half_split_complex(u, pos, theta),
+                                   rtol=0, atol=2e-11)
+
+
+def test_rope_neox_pairs_and_relative_position():
+    d, h = 64, 32
+    u = rng.standard_normal(d)
+    np.testing.assert_array_equal(oracle.rope_neox(u, 0, 1e4), u)
+    r = oracle.rope_neox(u, 777, 1e4)
+    np.testing.assert_allclose(r[:h] ** 2 + r[h:] ** 2, u[:h] ** 2 + u[h:] ** 2, rtol=1e-12)
+    assert not np.allclose(r, oracle.rope(u, 777, 1e4))  # not the adjacent-pair form
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n, delta in [(5, 2, 100), (300, 17, 4000)]:
+        a = oracle.rope_neox(q, m, 1e4) @ oracle.rope_neox(k, n, 1e4)
+        b = oracle.rope_neox(q, m + delta, 1e4) @ oracle.rope_neox(k, n + delta, 1e4)
+        assert abs(a - b) < 1e-9
+
+
 def test_rope_identity_at_zero_and_pair_norms():
     d = 64
     u = rng.standard_normal(d)
@@ -243,8 +275,16 @@ def _torch_forward(wl, W, tokens):
     rot = torch.polar(torch.ones(n, d // 2, dtype=torch.float64), pos[:, None] * freqs[None])
 
     def rope(t):  # t [n, heads, d]
+        if wl.rope_neox:  # half-split pairs (i, i + d/2): rotate_half form
+            c, s_ = rot.real[:, None, :].repeat(1, 1, 2), rot.imag[:, None, :].repeat(1, 1, 2)
+            half = torch.cat([-t[..., d // 2:], t[..., :d // 2]], dim=-1)
+            return t * c + half * s_
         z = torch.view_as_complex(t.reshape(n, t.shape[1], d // 2, 2).contiguous())
         return torch.view_as_real(z * rot[:, None, :]).reshape(t.shape)
+
+    def bias(name):
+        b = L.get(name)
+        return 0.0 if b is None else torch.tensor(b.astype(np.float64))
 
     tpos = torch.arange(n)
     mask = tpos[None, :] <= tpos[:, None]
@@ -253,9 +293,9 @@ def _torch_forward(wl, W, tokens):
     for L in W["layers"]:
         g = torch.tensor(L["attn_norm"].astype(np.float64))
         xn = act(F.rms_norm(x, (E,), weight=g, eps=wl.rms_norm_eps))
-        q = rope((xn @ mat(L["wq"], L["s_q"]).T).reshape(n, H, d))
-        k = kvr(rope((xn @ mat(L["wk"], L["s_k"]).T).reshape(n, Hk, d)))
-        v = kvr((xn @ mat(L["wv"], L["s_v"]).T).reshape(n, Hk, d))
+        q = rope((xn @ mat(L["wq"], L["s_q"]).T + bias("b_q")).reshape(n, H, d))
+        k = kvr(rope((xn @ mat(L["wk"], L["s_k"]).T + bias("b_k")).reshape(n, Hk, d)))
+        v = kvr((xn @ mat(L["wv"], L["s_v"]).T + bias("b_v")).reshape(n, Hk, d))
         o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
                                            v.transpose(0, 1)[None], attn_mask=mask[None, None],
                                            enable_gqa=True)[0].transpose(0, 1).reshape(n, H * d)
@@ -290,6 +330,12 @@ SMALL = [
     synth.tiny_fp32().with_(name="small-int8", w_dtype=synth.I8, kv_dtype=synth.BF16,
                             act_dtype=synth.BF16, seed=12, n_head=4, n_kv_head=4, head_dim=64),
     synth.tiny_fp32().with_(name="small-moe", n_expert=4, n_expert_used=2, seed=13, n_ff=96),
+    synth.tiny_fp32().with_(name="small-neox-bias-f32", rope_neox=True, qkv_bias=True, seed=14),
+    synth.tiny_fp32().with_(name="small-neox-bias-bf16-window", rope_neox=True, qkv_bias=True, w_dtype=synth.BF16,
+                            kv_dtype=synth.BF16, act_dtype=synth.BF16, sliding_window=4, seed=15),
+    synth.tiny_fp32().with_(name="small-bias-int8", qkv_bias=True, w_dtype=synth.I8, kv_dtype=synth.BF16,
+                            act_dtype=synth.BF16, seed=16),
+    synth.tiny_fp32().with_(name="small-neox-moe", rope_neox=True, n_expert=4, n_expert_used=2, seed=17, n_ff=96),
 ]
 
 
