@@ -68,7 +68,14 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2 } pn_dtype;
  *            residual stream, q, softmax and all accumulators stay fp32.
  *            PN_I8 weights need act_dtype PN_BF16.
  *  max_batch largest n accepted by pn_forward_batch (1..16; with act_dtype
- *            PN_F32 and bf16/int8 weights, 1..5). */
+ *            PN_F32 and bf16/int8 weights, 1..5).
+ *  rope_neox, qkv_bias  the variants that share the Llama forward through
+ *            config flags ("Engine Architecture", section "Architecture
+ *            Detection"): attention biases (Qwen2), added to q, k and v before
+ *            RoPE; the NeoX RoPE of Phi-3, which rotates (i, i + d/2) instead
+ *            of (2i, 2i+1) with the same angles.  0 (default) or 1.  A fused
+ *            QKV or gate+up checkpoint needs no flag: pass pointers into it
+ *            (wk = wq + H*d rows, w_up = w_gate + F rows). */
 typedef struct pn_config {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab;
     int32_t n_ctx;          /* default state capacity when pn_state_* is given max_ctx 0 */
@@ -78,6 +85,8 @@ typedef struct pn_config {
     int32_t max_batch;
     float rope_theta, rms_norm_eps;
     int32_t w_dtype, kv_dtype, act_dtype; /* pn_dtype values */
+    int32_t rope_neox; /* 1: RoPE rotates the half-split pairs (i, i + head_dim/2) */
+    int32_t qkv_bias;  /* 1: the q, k, v projections add fp32 biases (b_q, b_k, b_v) */
 } pn_config;
 
 /* Device pointers of one layer's weights, logical row-major [out][in].  The
@@ -90,6 +99,7 @@ typedef struct pn_layer_weights {
     const void *w_gate, *w_up, *w_down;  /* [X][F][E], [X][F][E], [X][E][F] */
     const void *w_router;                /* [n_expert][E]; NULL for dense */
     const float *s_q, *s_k, *s_v, *s_o, *s_gate, *s_up, *s_down;
+    const float *b_q, *b_k, *b_v;        /* [H*d], [Hk*d], [Hk*d]; required iff qkv_bias */
 } pn_layer_weights;
 
 typedef struct pn_weights {

@@ -33,7 +33,8 @@ def device_config(wl, max_batch=1):
                           wl.n_vocab, n_expert=wl.n_expert, n_expert_used=wl.n_expert_used,
                           sliding_window=wl.sliding_window, max_batch=max_batch,
                           rope_theta=wl.rope_theta, rms_norm_eps=wl.rms_norm_eps,
-                          w_dtype=wl.w_dtype, kv_dtype=wl.kv_dtype, act_dtype=wl.act_dtype)
+                          w_dtype=wl.w_dtype, kv_dtype=wl.kv_dtype, act_dtype=wl.act_dtype,
+                          rope_neox=wl.rope_neox, qkv_bias=wl.qkv_bias)
 
 
 def compare_step(wl, g_logits, o_logits, g_id, o_id, what="", tol=None):

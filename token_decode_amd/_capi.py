@@ -24,13 +24,14 @@ class pn_config(ctypes.Structure):
                 ("head_dim", i32), ("n_ff", i32), ("n_vocab", i32), ("n_ctx", i32),
                 ("n_expert", i32), ("n_expert_used", i32), ("sliding_window", i32),
                 ("max_batch", i32), ("rope_theta", ctypes.c_float), ("rms_norm_eps", ctypes.c_float),
-                ("w_dtype", i32), ("kv_dtype", i32), ("act_dtype", i32)]
+                ("w_dtype", i32), ("kv_dtype", i32), ("act_dtype", i32), ("rope_neox", i32),
+                ("qkv_bias", i32)]
 
 
 class pn_layer_weights(ctypes.Structure):
     _fields_ = [(n, vp) for n in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo", "w_gate", "w_up",
                                    "w_down", "w_router", "s_q", "s_k", "s_v", "s_o", "s_gate",
-                                   "s_up", "s_down")]
+                                   "s_up", "s_down", "b_q", "b_k", "b_v")]
 
 
 class pn_sampling_params(ctypes.Structure):

@@ -196,6 +196,7 @@ struct GemmArgs {
     long long out_plane;    // elements per output plane
     int ld_out;
     float *q_out;           // QKV: q [slot][Hq*D]
+    const float *bias;      // QKV: biases [N] in packed row order, or null
     int Hq, Hk, D;
     int kv_es;              // QKV: bytes per cached element (2 = bf16, 4 = fp32)
     const float2 *rope;     // QKV: (cos, sin) per slot and rotation index [slot][D/2]
@@ -572,9 +573,9 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     // epilogue inputs of one block, loaded early by the threads that use them
     // (row r of slot b: the old x for the residual, the (cos, sin) for RoPE,
     // the int8 row scales)
-    struct EpIn { float x, s0, s1; float2 cs; int page; };
+    struct EpIn { float x, s0, s1, b0, b1; float2 cs; int page; };
     auto epi_load = [&](int blk) -> EpIn {
-        EpIn e{0.f, 1.f, 1.f, make_float2(1.f, 0.f), 0};
+        EpIn e{0.f, 1.f, 1.f, 0.f, 0.f, make_float2(1.f, 0.f), 0};
         if constexpr (EPI == EPI_RESID) {
             if (tid < nb * 16) {
                 const int b = tid >> 4, r = blk * 16 + (tid & 15);
@@ -588,6 +589,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 if (r0 < g.N) {
                     e.cs = g.rope[(long long)b * (g.D / 2) + ((r0 % g.D) >> 1)];
                     if constexpr (WT == WT_I8) { e.s0 = g.sc[r0]; e.s1 = g.sc[r0 + 1]; }
+                    if (g.bias) { e.b0 = g.bias[r0]; e.b1 = g.bias[r0 + 1]; }
                 }
             }
         } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN) {
@@ -866,6 +868,10 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 if (r0 < g.N) {
                     float y0 = Y(0, b, n0) * epc.s0;
                     float y1 = Y(0, b, n0 + 1) * epc.s1;
+                    if (g.bias) {
+                        y0 += epc.b0;
+                        y1 += epc.b1;
+                    }
                     const int pos = g.pos[b];
                     if (r0 < hd) {
                         rope_pair(y0, y1, epc.cs);

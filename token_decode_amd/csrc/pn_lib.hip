@@ -59,6 +59,7 @@ struct Mat {  // one packed matrix (or a stack of experts' matrices)
 
 struct LayerOff {
     size_t attn_norm, ffn_norm, router;
+    size_t bqkv;  // q, k, v biases [Nqkv] fp32 in packed row order (0: none)
     Mat qkv, o, gate, up, down;
 };
 
@@ -250,6 +251,7 @@ int check_config_n(const pn_config *c) {
     if (c->w_dtype == PN_I8 && c->act_dtype != PN_BF16)
         return fail(PN_EUNSUPPORTED, "int8 weights need bf16 activations");
     if (c->max_batch < 1 || c->max_batch > kMaxSlots) return fail(PN_EINVAL, "max_batch must be in [1, 16]");
+    if ((c->rope_neox & ~1) != 0 || (c->qkv_bias & ~1) != 0) return fail(PN_EINVAL, "rope_neox and qkv_bias must be 0 or 1");
     const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
@@ -303,6 +305,7 @@ size_t layout_model(pn_model *m) {
         L.attn_norm = bp.take((size_t)m->E * 4);
         L.ffn_norm = bp.take((size_t)m->E * 4);
         L.router = c.n_expert > 0 ? bp.take((size_t)c.n_expert * m->E * es_aux) : 0;
+        L.bqkv = c.qkv_bias ? bp.take((size_t)m->Nqkv * 4) : 0;
         L.qkv = make_mat(m->Nqkv, m->E, wt);
         L.o = make_mat(m->E, m->H * m->D, wt);
         L.gate = make_mat(m->F, m->E, wt);
@@ -484,18 +487,27 @@ void copy_bytes(void *dst, const void *src, size_t n, hipStream_t s) {
                        (long long)n);
 }
 
+// Pack a row-major [N][K] matrix into tiles; with neox_d > 0 the rows of each
+// head block of neox_d rows are reordered into rotation pairs (see neox_src).
 void pack(const void *src, int N, int K, int wt, const Mat &mt, int tile_row0, uint8_t *dst_base,
-          hipStream_t s) {
+          hipStream_t s, int neox_d = 0) {
     const int nt = cdiv(N, 16);
     uint8_t *dst = dst_base + (size_t)tile_row0 * mt.KT * 1024;
     long long lanes = (long long)nt * mt.KT * 64;
     int blocks = cdiv(lanes, 256);
+    const uint8_t *sp = (const uint8_t *)src;
     if (wt == PN_F32)
-        hipLaunchKernelGGL(k_pack<4>, dim3(blocks), dim3(256), 0, s, (const uint8_t *)src, N, K, mt.KT, nt, dst);
+        hipLaunchKernelGGL(k_pack<4>, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, neox_d);
     else if (wt == PN_BF16)
-        hipLaunchKernelGGL(k_pack<2>, dim3(blocks), dim3(256), 0, s, (const uint8_t *)src, N, K, mt.KT, nt, dst);
+        hipLaunchKernelGGL(k_pack<2>, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, neox_d);
     else
-        hipLaunchKernelGGL(k_pack<1>, dim3(blocks), dim3(256), 0, s, (const uint8_t *)src, N, K, mt.KT, nt, dst);
+        hipLaunchKernelGGL(k_pack<1>, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, neox_d);
+}
+
+// dst[r] = src[neox_src(r, neox_d)] for n fp32 values (row scales, biases).
+void copy_rows_f32(void *dst, const float *src, int n, int neox_d, hipStream_t s) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_copy_rows_f32, dim3(cdiv(n, 256)), dim3(256), 0, s, (float *)dst, src, n, neox_d);
 }
 
 // ---------------------------------------------------------------- launch dispatch
@@ -705,6 +717,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.x = x;
             g.gain = (const float *)(mb + L.attn_norm);
             g.q_out = (float *)(mb + m->q);
+            g.bias = L.bqkv ? (const float *)(mb + L.bqkv) : nullptr;
             for (int b = 0; b < n; ++b) {
                 g.kvk[b] = kv_layer(st[b], l, false);
                 g.kvv[b] = kv_layer(st[b], l, true);
@@ -981,6 +994,7 @@ int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *W, v
     if (cfg->n_expert > 0 && !W->w_router) return fail(PN_EINVAL, "missing router in layer %d", layer);
     if (i8 && (!W->s_q || !W->s_k || !W->s_v || !W->s_o || !W->s_gate || !W->s_up || !W->s_down))
         return fail(PN_EINVAL, "missing int8 scales in layer %d", layer);
+    if (cfg->qkv_bias && (!W->b_q || !W->b_k || !W->b_v)) return fail(PN_EINVAL, "missing q/k/v bias in layer %d", layer);
     hipStream_t s = S(stream);
     char *mb = m->base;
     const int wt = m->wt, es_aux = wt == PN_F32 ? 4 : 2, esw = dtype_size(wt);
@@ -991,15 +1005,24 @@ int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *W, v
     if (cfg->n_expert > 0) copy_bytes(mb + L.router, W->w_router, (size_t)cfg->n_expert * E * es_aux, s);
     // q, k and v blocks are tile aligned because head_dim is a multiple of 16
     uint8_t *qkv = (uint8_t *)(mb + L.qkv.off);
-    pack(W->wq, m->H * m->D, E, wt, L.qkv, 0, qkv, s);
-    pack(W->wk, m->Hk * m->D, E, wt, L.qkv, m->H * m->D / 16, qkv, s);
+    // NeoX RoPE: q and k rows are packed in rotation-pair order, so the
+    // epilogue's adjacent-pair rotation is the half-split one
+    const int nx = cfg->rope_neox ? m->D : 0;
+    pack(W->wq, m->H * m->D, E, wt, L.qkv, 0, qkv, s, nx);
+    pack(W->wk, m->Hk * m->D, E, wt, L.qkv, m->H * m->D / 16, qkv, s, nx);
     pack(W->wv, m->Hk * m->D, E, wt, L.qkv, (m->H + m->Hk) * m->D / 16, qkv, s);
+    if (cfg->qkv_bias) {
+        char *bq = mb + L.bqkv;
+        copy_rows_f32(bq, W->b_q, m->H * m->D, nx, s);
+        copy_rows_f32(bq + (size_t)m->H * m->D * 4, W->b_k, m->Hk * m->D, nx, s);
+        copy_rows_f32(bq + (size_t)(m->H + m->Hk) * m->D * 4, W->b_v, m->Hk * m->D, 0, s);
+    }
     pack(W->wo, E, HD, wt, L.o, 0, (uint8_t *)(mb + L.o.off), s);
     if (i8) {
         char *sq = mb + L.qkv.soff;
         fill32(sq, (size_t)L.qkv.n_tiles * 16, 0u, s);
-        copy_bytes(sq, W->s_q, (size_t)m->H * m->D * 4, s);
-        copy_bytes(sq + (size_t)m->H * m->D * 4, W->s_k, (size_t)m->Hk * m->D * 4, s);
+        copy_rows_f32(sq, W->s_q, m->H * m->D, nx, s);
+        copy_rows_f32(sq + (size_t)m->H * m->D * 4, W->s_k, m->Hk * m->D, nx, s);
         copy_bytes(sq + (size_t)(m->H + m->Hk) * m->D * 4, W->s_v, (size_t)m->Hk * m->D * 4, s);
         fill32(mb + L.o.soff, (size_t)L.o.n_tiles * 16, 0u, s);
         copy_bytes(mb + L.o.soff, W->s_o, (size_t)E * 4, s);
@@ -1223,12 +1246,13 @@ int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const v
     char *vp = kv_layer(s, layer, true);
     long long total = (long long)n * m->Hk * m->D;
     dim3 grid(cdiv(total, 256));
+    const int nx = m->cfg.rope_neox ? m->D : 0;  // k is cached in rotation-pair order
     if (m->kvt == PN_BF16)
         hipLaunchKernelGGL(k_set_kv<2>, grid, dim3(256), 0, S(stream), kp, vp, (const int *)(s->base + s->pt),
-                           (const char *)k, (const char *)v, pos0, n, m->Hk, m->D);
+                           (const char *)k, (const char *)v, pos0, n, m->Hk, m->D, nx);
     else
         hipLaunchKernelGGL(k_set_kv<4>, grid, dim3(256), 0, S(stream), kp, vp, (const int *)(s->base + s->pt),
-                           (const char *)k, (const char *)v, pos0, n, m->Hk, m->D);
+                           (const char *)k, (const char *)v, pos0, n, m->Hk, m->D, nx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PN_EHIP, "set_kv failed: %s", hipGetErrorString(e));
     return PN_OK;

@@ -260,11 +260,21 @@ __global__ void __launch_bounds__(256) k_moe_combine(float *x, const float *y, c
     if ((threadIdx.x & 15) == 0 && r < E) ssp[(long long)b * ssp_ld + (r >> 4)] = sq;
 }
 
+// Source row of stored row r when each head's d rows are put in rotation-pair
+// order for the NeoX RoPE: stored rows 2i, 2i+1 of a head are its rows i and
+// i + d/2, which the half-split RoPE rotates together (d = 0: no reordering).
+// q.k is a sum over dims, so q and k in this order give the same scores.
+__host__ __device__ inline int neox_src(int r, int d) {
+    if (d <= 0) return r;
+    const int h = r % d;
+    return r - h + (h >> 1) + (h & 1) * (d >> 1);
+}
+
 // Re-lay a row-major matrix [N][K] (element size ES) into 1 KiB tiles.
 // Int8 codes are stored biased (u = q + 128); padding is the code of 0.
 template <int ES>
 __global__ void __launch_bounds__(256) k_pack(const uint8_t *src, int N, int K, int KT, int n_tiles,
-                                               uint8_t *dst) {
+                                               uint8_t *dst, int neox_d) {
     constexpr int EPL = 16 / ES;  // elements per lane chunk
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long total = (long long)n_tiles * KT * 64;
@@ -281,7 +291,7 @@ __global__ void __launch_bounds__(256) k_pack(const uint8_t *src, int N, int K, 
         const bool in = row < N && k < K;
 #pragma unroll
         for (int bb = 0; bb < ES; ++bb) {
-            uint8_t v = in ? src[((long long)row * K + k) * ES + bb] : 0;
+            uint8_t v = in ? src[((long long)neox_src(row, neox_d) * K + k) * ES + bb] : 0;
             if (ES == 1) v = (uint8_t)(v ^ 0x80u);
             out[e * ES + bb] = v;
         }
@@ -292,6 +302,11 @@ __global__ void __launch_bounds__(256) k_pack(const uint8_t *src, int N, int K, 
         o[q] = (uint32_t)out[4 * q] | ((uint32_t)out[4 * q + 1] << 8) | ((uint32_t)out[4 * q + 2] << 16) |
                ((uint32_t)out[4 * q + 3] << 24);
     reinterpret_cast<u32x4 *>(dst)[i] = o;
+}
+
+__global__ void __launch_bounds__(256) k_copy_rows_f32(float *dst, const float *src, int n, int neox_d) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r < n) dst[r] = src[neox_src(r, neox_d)];
 }
 
 __global__ void __launch_bounds__(256) k_fill32(uint32_t *p, long long n, uint32_t v) {
@@ -336,7 +351,7 @@ __global__ void __launch_bounds__(256) k_zero_pages(char *kbase, char *vbase, si
 // layer (each head's block of a page laid out as kv_k_off / kv_v_off say).
 template <int ES>
 __global__ void __launch_bounds__(256) k_set_kv(char *kpool, char *vpool, const int *pt, const char *k,
-                                                 const char *v, int pos0, int n, int Hk, int D) {
+                                                 const char *v, int pos0, int n, int Hk, int D, int neox_d) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long total = (long long)n * Hk * D;
     if (i >= total) return;
@@ -347,11 +362,12 @@ __global__ void __launch_bounds__(256) k_set_kv(char *kpool, char *vpool, const 
     const long long hb = ((long long)pt[p / kPage] * Hk + j) * kPage * D;
     const long long koff = hb + kv_k_off(ES == 2, p % kPage, d, D);
     const long long voff = hb + kv_v_off(ES == 2, p % kPage, d, D);
+    const long long ki = i - d + neox_src(d, neox_d);  // cached dim d holds source dim neox_src(d)
     if constexpr (ES == 2) {
-        reinterpret_cast<uint16_t *>(kpool)[koff] = reinterpret_cast<const uint16_t *>(k)[i];
+        reinterpret_cast<uint16_t *>(kpool)[koff] = reinterpret_cast<const uint16_t *>(k)[ki];
         reinterpret_cast<uint16_t *>(vpool)[voff] = reinterpret_cast<const uint16_t *>(v)[i];
     } else {
-        reinterpret_cast<float *>(kpool)[koff] = reinterpret_cast<const float *>(k)[i];
+        reinterpret_cast<float *>(kpool)[koff] = reinterpret_cast<const float *>(k)[ki];
         reinterpret_cast<float *>(vpool)[voff] = reinterpret_cast<const float *>(v)[i];
     }
 }

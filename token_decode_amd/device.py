@@ -34,14 +34,16 @@ def upload(arr, device="cuda"):
 
 def make_config(n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab, *, n_ctx=2048,
                 n_expert=0, n_expert_used=0, sliding_window=0, max_batch=1, rope_theta=10000.0,
-                rms_norm_eps=1e-5, w_dtype=C.PN_BF16, kv_dtype=C.PN_BF16, act_dtype=C.PN_F32):
+                rms_norm_eps=1e-5, w_dtype=C.PN_BF16, kv_dtype=C.PN_BF16, act_dtype=C.PN_F32,
+                rope_neox=False, qkv_bias=False):
     cfg = C.pn_config()
     C.lib().pn_config_default(ctypes.byref(cfg))
     for k, v in dict(n_layer=n_layer, n_embd=n_embd, n_head=n_head, n_kv_head=n_kv_head,
                      head_dim=head_dim, n_ff=n_ff, n_vocab=n_vocab, n_ctx=n_ctx, n_expert=n_expert,
                      n_expert_used=n_expert_used, sliding_window=sliding_window,
                      max_batch=max_batch, rope_theta=rope_theta, rms_norm_eps=rms_norm_eps,
-                     w_dtype=w_dtype, kv_dtype=kv_dtype, act_dtype=act_dtype).items():
+                     w_dtype=w_dtype, kv_dtype=kv_dtype, act_dtype=act_dtype,
+                     rope_neox=int(rope_neox), qkv_bias=int(qkv_bias)).items():
         setattr(cfg, k, v)
     return cfg
 
@@ -57,7 +59,10 @@ class DeviceModel:
     `weights` uses the key names of pn_layer_weights / pn_weights: tok_embd,
     out_norm, w_out, s_out and `layers`, a list of dicts with attn_norm,
     ffn_norm, wq, wk, wv, wo, w_gate, w_up, w_down (lists over experts),
-    w_router and the int8 scales s_q, s_k, s_v, s_o, s_gate, s_up, s_down.
+    w_router, the int8 scales s_q, s_k, s_v, s_o, s_gate, s_up, s_down and
+    the biases b_q, b_k, b_v.  A fused checkpoint may give `wqkv` ([q; k; v]
+    rows) instead of wq, wk, wv and, for a dense FFN, `w_gate_up` ([gate; up]
+    rows) instead of w_gate, w_up: the library is handed pointers into it.
     """
 
     def __init__(self, cfg, weights, stream=None, device="cuda"):
@@ -82,11 +87,26 @@ class DeviceModel:
         del g
         for l, W in enumerate(weights["layers"]):
             t = {k: upload(W[k], device) for k in ("attn_norm", "ffn_norm", "wq", "wk", "wv", "wo",
-                                                   "s_q", "s_k", "s_v", "s_o", "w_router")}
+                                                   "s_q", "s_k", "s_v", "s_o", "w_router",
+                                                   "b_q", "b_k", "b_v") if W.get(k) is not None}
             for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
                 v = W.get(k)
                 t[k] = None if (v is None or v[0] is None) else upload(np.stack(v), device)
-            lw = C.pn_layer_weights(**{k: _ptr(t.get(k)) for k, _ in C.pn_layer_weights._fields_})
+            ptrs = {k: _ptr(t.get(k)) for k, _ in C.pn_layer_weights._fields_}
+            # fused checkpoints: pointers into one device copy of [q; k; v] / [gate; up]
+            if W.get("wqkv") is not None:
+                t["wqkv"] = upload(W["wqkv"], device)
+                row = t["wqkv"].element_size() * cfg.n_embd
+                base = t["wqkv"].data_ptr()
+                hq, hk = cfg.n_head * cfg.head_dim, cfg.n_kv_head * cfg.head_dim
+                ptrs["wq"], ptrs["wk"] = ctypes.c_void_p(base), ctypes.c_void_p(base + hq * row)
+                ptrs["wv"] = ctypes.c_void_p(base + (hq + hk) * row)
+            if W.get("w_gate_up") is not None:  # dense FFN: [2F][E]
+                t["w_gate_up"] = upload(W["w_gate_up"], device)
+                base = t["w_gate_up"].data_ptr()
+                ptrs["w_gate"] = ctypes.c_void_p(base)
+                ptrs["w_up"] = ctypes.c_void_p(base + cfg.n_ff * cfg.n_embd * t["w_gate_up"].element_size())
+            lw = C.pn_layer_weights(**ptrs)
             C.check(L.pn_model_load_layer(h, l, ctypes.byref(lw), sp))
             s.synchronize()
             del t
