@@ -58,6 +58,10 @@ def lib():
         L.orc_rope.restype = None
         L.orc_rope_neox.argtypes = [vp, i32, i32, dbl]
         L.orc_rope_neox.restype = None
+        L.orc_half_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_half_to_double.restype = dbl
+        L.orc_matvec.argtypes = [vp, i32, vp, i32, i32, vp, vp]
+        L.orc_matvec.restype = None
         L.orc_attend.argtypes = [vp, vp, vp, i32, i32, vp]
         L.orc_attend.restype = None
         L.orc_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
@@ -114,6 +118,20 @@ def rope(u, pos, theta):
     u = _f64(u).copy()
     lib().orc_rope(_ptr(u), u.size, pos, theta)
     return u
+
+
+def half_to_double(bits):
+    return lib().orc_half_to_double(int(bits))
+
+
+def matvec(W, dt, s, rows, cols, x):
+    """y = W x through the oracle's mat-vec (W in storage type dt; s: int8 row scales)."""
+    W = np.ascontiguousarray(W)
+    x = _f64(x)
+    y = np.empty(rows)
+    sp = None if s is None else np.ascontiguousarray(s, dtype=np.float32)
+    lib().orc_matvec(_ptr(W), dt, _ptr(sp), rows, cols, _ptr(x), _ptr(y))
+    return y
 
 
 def rope_neox(u, pos, theta):

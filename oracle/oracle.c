@@ -40,8 +40,9 @@
  * index, weights renormalised over the chosen experts; untied LM head behind
  * a final RMSNorm.
  *
- * Precision.  Every stored value (fp32, bf16, or int8 times an fp32 row
- * scale) is widened to double on read and all arithmetic is double.  The
+ * Precision.  Every stored value (fp32, bf16, int8 times an fp32 row scale,
+ * or a Q8_0 code times its block's fp16 scale) is widened to double on read
+ * and all arithmetic is double.  The
  * values that the decode step stores in a narrower type are rounded at the
  * same points: the inputs of every mat-vec (normed x, attention output,
  * FFN hidden, final normed x) to the activation type, and the appended k, v
@@ -60,7 +61,11 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_Q8_0 = 3 };
+
+/* Q8_0 block-quantised rows (GGUF-style): each row is cols/32 blocks of
+ * 34 bytes, an fp16 scale d followed by 32 int8 codes q; weight = d * q. */
+enum { Q8_BLOCK = 32, Q8_BLOCK_BYTES = 34 };
 
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab;
@@ -114,6 +119,23 @@ static double bf16_value(uint16_t h) {
     return (double)f;
 }
 
+/* IEEE binary16 bits -> double (normal, subnormal, zero, inf, NaN) */
+double orc_half_to_double(uint16_t h) {
+    int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);                    /* subnormal or zero */
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + m), e - 25);               /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* weight (r, c) of a Q8_0 matrix with `cols` columns, dequantised: d * q */
+static double q8_weight(const void *W, int cols, int r, int c) {
+    const uint8_t *blk = (const uint8_t *)W + ((size_t)r * (size_t)(cols / Q8_BLOCK) + (size_t)(c / Q8_BLOCK)) * Q8_BLOCK_BYTES;
+    uint16_t dbits = (uint16_t)(blk[0] | (blk[1] << 8));
+    return orc_half_to_double(dbits) * (double)(int8_t)blk[2 + c % Q8_BLOCK];
+}
+
 /* element i of a stored tensor, widened to double (int8: the raw code) */
 static double rd(const void *p, int dt, size_t i) {
     switch (dt) {
@@ -127,16 +149,29 @@ static double rd(const void *p, int dt, size_t i) {
 
 static int g_threads = 1;
 
-/* y[r] = sum_c W[r][c] * x[c]; int8 rows are scaled by s[r] after the sum */
+/* y[r] = sum_c W[r][c] * x[c]; int8 rows are scaled by s[r] after the sum;
+ * Q8_0 weights are dequantised (d * q) before the product ("Weight Loading
+ * Modes": dequantisation per block inside the mat-vec) */
 static void matvec(const void *W, int dt, const float *s, int rows, int cols, const double *x,
                    double *y) {
 #pragma omp parallel for num_threads(g_threads) schedule(static) if (g_threads > 1)
     for (int r = 0; r < rows; ++r) {
         double acc = 0.0;
         size_t base = (size_t)r * (size_t)cols;
-        for (int c = 0; c < cols; ++c) acc += rd(W, dt, base + (size_t)c) * x[c];
+        if (dt == ORC_Q8_0)
+            for (int c = 0; c < cols; ++c) acc += q8_weight(W, cols, r, c) * x[c];
+        else
+            for (int c = 0; c < cols; ++c) acc += rd(W, dt, base + (size_t)c) * x[c];
         y[r] = (dt == ORC_I8) ? (double)s[r] * acc : acc;
     }
+}
+
+/* the mat-vec above, exported for the tests (one thread) */
+void orc_matvec(const void *W, int dt, const float *s, int rows, int cols, const double *x, double *y) {
+    int t = g_threads;
+    g_threads = 1;
+    matvec(W, dt, s, rows, cols, x, y);
+    g_threads = t;
 }
 
 /* y = x * (mean(x^2) + eps)^(-1/2) * g */

@@ -29,7 +29,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libsynth.so")
 _SRC = os.path.join(_HERE, "synth.c")
 
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, Q8_0 = 0, 1, 2, 3
+Q8_BLOCK, Q8_BLOCK_BYTES = 32, 34
 DTYPE_NAMES = {F32: "f32", BF16: "bf16", I8: "i8"}
 
 TID_EMBD = 0
@@ -220,10 +221,29 @@ class Workload:
         return k.reshape(shp), v.reshape(shp)
 
 
+def q8_0_blocks(w: np.ndarray) -> np.ndarray:
+    """Quantise fp32 rows [rows][cols] (cols a multiple of 32) into Q8_0 blocks as
+    a checkpoint would store them: per block of 32, d = max|w| / 127 as fp16,
+    codes round(w / d); 34 bytes per block (d little-endian, then the codes)."""
+    rows, cols = w.shape
+    b = w.reshape(rows, cols // Q8_BLOCK, Q8_BLOCK).astype(np.float64)
+    d = (np.abs(b).max(axis=2) / 127.0).astype(np.float16)
+    df = d.astype(np.float64)[..., None]
+    q = np.where(df > 0, np.rint(b / np.where(df > 0, df, 1.0)), 0.0)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    out = np.empty((rows, cols // Q8_BLOCK, Q8_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = d.view(np.uint8).reshape(rows, cols // Q8_BLOCK, 2)
+    out[:, :, 2:] = q.view(np.uint8)
+    return out.reshape(rows, cols // Q8_BLOCK * Q8_BLOCK_BYTES)
+
+
 def _matrix(wl: Workload, tid: int, rows: int, cols: int, threads=None):
     if wl.w_dtype == I8:
         q, s = int8_rows(wl.seed, tid, rows, cols, W_STD, threads)
         return q, s
+    if wl.w_dtype == Q8_0:
+        w = normal(wl.seed, tid, rows * cols, 0.0, W_STD, F32, threads=threads)
+        return q8_0_blocks(w.reshape(rows, cols)), None
     m = normal(wl.seed, tid, rows * cols, 0.0, W_STD, wl.w_dtype, threads=threads)
     return m.reshape(rows, cols), None
 

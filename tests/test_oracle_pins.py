@@ -243,6 +243,52 @@ def test_round_bf16_matches_torch():
     np.testing.assert_array_equal(mine, ref)
 
 
+# ----------------------------------------------------------------------------- Q8_0 weights
+
+def test_half_to_double_matches_numpy_float16():
+    bits = np.concatenate([np.arange(0, 0x7C00, 37), [0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF]]).astype(np.uint16)
+    bits = np.concatenate([bits, bits | 0x8000])
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(b) for b in bits])
+    np.testing.assert_array_equal(got, want)
+    assert oracle.half_to_double(0x7C00) == np.inf and np.isnan(oracle.half_to_double(0x7E00))
+
+
+def _q8_block(d, codes):
+    return np.concatenate([np.array([d], np.float16).view(np.uint8),
+                           np.asarray(codes, np.int8).view(np.uint8)])
+
+
+def test_q8_0_matvec_closed_form():
+    # two rows of two blocks: d = 0.5 and 2^-20 (an fp16 subnormal scale); then -0.25 and 3
+    c = np.arange(-16, 16)
+    W = np.stack([np.concatenate([_q8_block(0.5, c), _q8_block(2.0 ** -20, c[::-1])]),
+                  np.concatenate([_q8_block(-0.25, np.full(32, 127)), _q8_block(3.0, np.full(32, -128))])])
+    x = np.concatenate([np.ones(32), np.full(32, 2.0)])
+    y = oracle.matvec(W, synth.Q8_0, None, 2, 64, x)
+    want0 = 0.5 * c.sum() + 2.0 * 2.0 ** -20 * c[::-1].sum()
+    want1 = -0.25 * 127 * 32 + 2.0 * 3.0 * (-128) * 32
+    np.testing.assert_array_equal(y, [want0, want1])
+    # one-hot x reads single weights: d * q at block b, index i
+    for col in (0, 31, 32, 47, 63):
+        e = np.zeros(64)
+        e[col] = 1.0
+        d = (0.5, 2.0 ** -20)[col // 32]
+        q = (c, c[::-1])[col // 32][col % 32]
+        assert oracle.matvec(W, synth.Q8_0, None, 2, 64, e)[0] == d * q
+
+
+def test_q8_0_matvec_matches_numpy_dequantisation():
+    w = rng.standard_normal((24, 160)).astype(np.float32) * 0.05
+    blocks = synth.q8_0_blocks(w)
+    b = blocks.reshape(24, 5, 34)
+    deq = (b[:, :, 0:2].copy().view(np.float16).astype(np.float64)
+           * b[:, :, 2:].copy().view(np.int8).astype(np.float64)).reshape(24, 160)
+    assert np.abs(deq - w).max() <= np.abs(w).max() / 127  # a faithful quantisation of w
+    x = rng.standard_normal(160)
+    np.testing.assert_allclose(oracle.matvec(blocks, synth.Q8_0, None, 24, 160, x), deq @ x, rtol=1e-13)
+
+
 # ----------------------------------------------------------------------------- whole model
 
 def _torch_forward(wl, W, tokens):
@@ -250,6 +296,11 @@ def _torch_forward(wl, W, tokens):
     E, H, Hk, d = wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim
 
     def mat(m, s=None):
+        if m.dtype == np.uint8:  # Q8_0 blocks: fp16 scale, 32 int8 codes
+            b = m.reshape(m.shape[0], -1, 34)
+            d = b[:, :, 0:2].copy().view(np.float16).astype(np.float64)
+            q = b[:, :, 2:].copy().view(np.int8).astype(np.float64)
+            return torch.tensor((d * q).reshape(m.shape[0], -1))
         if m.dtype == np.uint16:
             a = torch.tensor(synth.bf16_to_f32(m).astype(np.float64))
         elif m.dtype == np.int8:
@@ -336,6 +387,11 @@ SMALL = [
     synth.tiny_fp32().with_(name="small-bias-int8", qkv_bias=True, w_dtype=synth.I8, kv_dtype=synth.BF16,
                             act_dtype=synth.BF16, seed=16),
     synth.tiny_fp32().with_(name="small-neox-moe", rope_neox=True, n_expert=4, n_expert_used=2, seed=17, n_ff=96),
+    synth.tiny_fp32().with_(name="small-q8_0", w_dtype=synth.Q8_0, kv_dtype=synth.BF16, act_dtype=synth.BF16,
+                            seed=18, n_ff=672),
+    synth.tiny_fp32().with_(name="small-q8_0-moe-neox-bias", w_dtype=synth.Q8_0, kv_dtype=synth.F32,
+                            act_dtype=synth.BF16, n_expert=4, n_expert_used=2, n_ff=96, rope_neox=True,
+                            qkv_bias=True, seed=19),
 ]
 
 
