@@ -49,7 +49,7 @@ enum {
     PN_EHIP = -4          /* HIP runtime failure */
 };
 
-typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2 } pn_dtype;
+typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3 } pn_dtype;
 
 /* Model dimensions and storage types.  Field names and defaults follow the
  * pages' config keys ("Engine Architecture", section "Config Parsing"):
@@ -59,9 +59,14 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2 } pn_dtype;
  * top-k MoE FFN ("Engine Architecture", section "Architecture Detection":
  * Mixtral is llama with an expert count > 0).
  *
- *  w_dtype   matrices: PN_F32, PN_BF16, or PN_I8 (symmetric int8 with one fp32
- *            scale per output row).  The token embedding and the MoE router are
- *            fp32 when w_dtype is PN_F32 and bf16 otherwise; norm gains are fp32.
+ *  w_dtype   matrices: PN_F32, PN_BF16, PN_I8 (symmetric int8 with one fp32
+ *            scale per output row), or PN_Q8_0 (GGUF-style block quantisation:
+ *            each row is K/32 blocks of 34 bytes, an fp16 scale d then 32 int8
+ *            codes q, weight = d*q, dequantised inside the mat-vec: "Engine
+ *            Architecture", section "Weight Loading Modes"; needs act_dtype
+ *            PN_BF16 and n_embd, n_ff multiples of 32).  The token embedding
+ *            and the MoE router are fp32 when w_dtype is PN_F32 and bf16
+ *            otherwise; norm gains are fp32.
  *  kv_dtype  cached K and V: PN_F32 or PN_BF16 (k is cached after RoPE).
  *  act_dtype type that every mat-vec input (normed x, attention output, FFN
  *            hidden, final normed x) is rounded to: PN_F32 or PN_BF16.  The
@@ -89,9 +94,9 @@ typedef struct pn_config {
     int32_t qkv_bias;  /* 1: the q, k, v projections add fp32 biases (b_q, b_k, b_v) */
 } pn_config;
 
-/* Device pointers of one layer's weights, logical row-major [out][in].  The
- * expert matrices are stacked: X = max(1, n_expert) blocks of gate/up [F][E]
- * and down [E][F].  Scales (s_*) are required iff w_dtype == PN_I8 (one fp32
+/* Device pointers of one layer's weights, logical row-major [out][in] (PN_Q8_0:
+ * each row its K/32 blocks).  The expert matrices are stacked: X = max(1,
+ * n_expert) blocks of gate/up [F][E] and down [E][F].  Scales (s_*) are required iff w_dtype == PN_I8 (one fp32
  * per output row, stacked like the matrices), else ignored. */
 typedef struct pn_layer_weights {
     const float *attn_norm, *ffn_norm;   /* [E] */

@@ -68,6 +68,8 @@ def lib():
         L.synth_normal.restype = None
         L.synth_int8_rows.argtypes = [u64, u64, u64, u64, dbl, vp, vp, ctypes.c_int]
         L.synth_int8_rows.restype = None
+        L.synth_q8_0_rows.argtypes = [u64, u64, u64, u64, dbl, vp, ctypes.c_int]
+        L.synth_q8_0_rows.restype = None
         L.synth_uniform_int.argtypes = [u64, u64, u64, i64, i64, vp]
         L.synth_uniform_int.restype = None
         L.synth_distinct_int.argtypes = [u64, u64, u64, i64, i64, vp]
@@ -101,6 +103,14 @@ def int8_rows(seed, tid, rows, cols, std=W_STD, threads=None):
     lib().synth_int8_rows(seed, tid, rows, cols, std, q.ctypes.data, s.ctypes.data,
                           threads or default_threads())
     return q, s
+
+
+def q8_0_rows(seed, tid, rows, cols, std=W_STD, threads=None):
+    """Q8_0 rows quantised from an fp32 N(0, std) draw: uint8 [rows][cols / 32 * 34]."""
+    assert cols % Q8_BLOCK == 0
+    out = np.empty((rows, cols // Q8_BLOCK * Q8_BLOCK_BYTES), dtype=np.uint8)
+    lib().synth_q8_0_rows(seed, tid, rows, cols, std, out.ctypes.data, threads or default_threads())
+    return out
 
 
 def uniform_int(seed, tid, n, lo, hi):
@@ -242,8 +252,7 @@ def _matrix(wl: Workload, tid: int, rows: int, cols: int, threads=None):
         q, s = int8_rows(wl.seed, tid, rows, cols, W_STD, threads)
         return q, s
     if wl.w_dtype == Q8_0:
-        w = normal(wl.seed, tid, rows * cols, 0.0, W_STD, F32, threads=threads)
-        return q8_0_blocks(w.reshape(rows, cols)), None
+        return q8_0_rows(wl.seed, tid, rows, cols, W_STD, threads), None
     m = normal(wl.seed, tid, rows * cols, 0.0, W_STD, wl.w_dtype, threads=threads)
     return m.reshape(rows, cols), None
 
@@ -345,10 +354,16 @@ def mixtral_8x7b_slots() -> Workload:
                     slots=16, pos_range=(512, 4096), steps=64)
 
 
+def llama3_8b_q8_0() -> Workload:
+    """Llama-3-8B shape, Q8_0 block-quantised weights, bf16 activations and KV; KV from 2048."""
+    return llama3_8b_bf16().with_(name="llama3-8b-q8_0", w_dtype=Q8_0, act_dtype=BF16, seed=6)
+
+
 WORKLOADS = {
     "tiny-fp32": tiny_fp32,
     "llama3-8b-bf16": llama3_8b_bf16,
     "llama3-8b-int8": llama3_8b_int8,
     "mistral-7b-8slots": mistral_7b_slots,
     "mixtral-8x7b-16slots": mixtral_8x7b_slots,
+    "llama3-8b-q8_0": llama3_8b_q8_0,
 }

@@ -194,14 +194,20 @@ static void int8_rows_range(void *p, uint64_t lo, uint64_t hi) {
     free(row);
 }
 
+static void parallel_rows(range_fn fn, void *ctx, uint64_t rows, int nthreads);
+
 void synth_int8_rows(uint64_t seed, uint64_t tid, uint64_t rows, uint64_t cols, double std,
                      int8_t *q, float *scale, int nthreads) {
     int8_ctx c = {stream_key(seed), tid, cols, std, q, scale};
-    /* rows are independent; partition rows (not elements) */
+    parallel_rows(int8_rows_range, &c, rows, nthreads);
+}
+
+/* rows are independent; partition rows (not elements) */
+static void parallel_rows(range_fn fn, void *ctx, uint64_t rows, int nthreads) {
     if (nthreads < 1) nthreads = 1;
     if ((uint64_t)nthreads > rows) nthreads = (int)rows;
     if (nthreads <= 1) {
-        int8_rows_range(&c, 0, rows);
+        fn(ctx, 0, rows);
         return;
     }
     pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
@@ -212,8 +218,8 @@ void synth_int8_rows(uint64_t seed, uint64_t tid, uint64_t rows, uint64_t cols, 
         uint64_t lo = (uint64_t)t * chunk, hi = lo + chunk;
         if (lo >= rows) break;
         if (hi > rows) hi = rows;
-        jobs[t].fn = int8_rows_range;
-        jobs[t].ctx = &c;
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
         jobs[t].lo = lo;
         jobs[t].hi = hi;
         if (pthread_create(&th[t], NULL, job_main, &jobs[t]) != 0) {
@@ -262,3 +268,70 @@ int synth_distinct_int(uint64_t seed, uint64_t tid, uint64_t n, int64_t lo, int6
 
 /* raw 64-bit draw, exposed for tests of the stream definition */
 uint64_t synth_draw_u64(uint64_t seed, uint64_t ctr) { return draw_u64(stream_key(seed), ctr); }
+
+/* ---- Q8_0 block-quantised rows ---------------------------------------------
+ * A checkpoint's Q8_0 rows, made from an fp32 N(0, std) draw: per block of 32,
+ * d = max|w| / 127 stored as fp16 (round to nearest even), codes
+ * round(w / d) clipped to [-127, 127]; 34 bytes per block (d little-endian,
+ * then the codes). */
+
+/* fp16 bits of a finite v >= 0, round to nearest even */
+static uint16_t half_bits_rne(double v) {
+    if (v == 0.0) return 0;
+    int e;
+    double m = frexp(v, &e); /* v = m * 2^e, m in [0.5, 1) */
+    int E = e - 1 + 15;      /* biased exponent of 1.xxx * 2^(e-1) */
+    if (E >= 1) {
+        double r = nearbyint(ldexp(m, 11)); /* 11 significant bits */
+        if (r == 2048.0) {
+            r = 1024.0;
+            E += 1;
+        }
+        if (E >= 31) return 0x7C00;
+        return (uint16_t)((E << 10) | ((int)r - 1024));
+    }
+    return (uint16_t)nearbyint(ldexp(v, 24)); /* subnormal (1024 is the smallest normal) */
+}
+
+static double half_bits_value(uint16_t h) {
+    int e = (h >> 10) & 31, m = h & 1023;
+    return e == 0 ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
+}
+
+typedef struct {
+    uint64_t key, tid, cols;
+    double std;
+    uint8_t *out;
+} q8_ctx;
+
+static void q8_rows_range(void *p, uint64_t lo, uint64_t hi) {
+    q8_ctx *c = (q8_ctx *)p;
+    const uint64_t nb = c->cols / 32;
+    for (uint64_t r = lo; r < hi; ++r) {
+        for (uint64_t b = 0; b < nb; ++b) {
+            float w[32];
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                w[i] = (float)(c->std * normal_at(c->key, c->tid, r * c->cols + b * 32 + (uint64_t)i));
+                if (fabs((double)w[i]) > amax) amax = fabs((double)w[i]);
+            }
+            uint16_t dh = half_bits_rne(amax / 127.0);
+            double d = half_bits_value(dh);
+            uint8_t *blk = c->out + (r * nb + b) * 34;
+            blk[0] = (uint8_t)(dh & 0xFF);
+            blk[1] = (uint8_t)(dh >> 8);
+            for (int i = 0; i < 32; ++i) {
+                double t = d > 0.0 ? nearbyint((double)w[i] / d) : 0.0;
+                if (t > 127.0) t = 127.0;
+                if (t < -127.0) t = -127.0;
+                blk[2 + i] = (uint8_t)(int8_t)t;
+            }
+        }
+    }
+}
+
+void synth_q8_0_rows(uint64_t seed, uint64_t tid, uint64_t rows, uint64_t cols, double std, uint8_t *out,
+                     int nthreads) {
+    q8_ctx c = {stream_key(seed), tid, cols, std, out};
+    parallel_rows(q8_rows_range, &c, rows, nthreads);
+}

@@ -72,6 +72,12 @@ def test_llama3_8b_int8_full():
     _single(synth.llama3_8b_int8(), tol=FLOOR_TOL)
 
 
+def test_llama3_8b_q8_0_four_layers():
+    """Q8_0 block-quantised weights, bf16 activations and KV, batch 1 from position 2048, 4 layers
+    at full width (K = 4096 and 14336: every Q8_0 GEMM at its real shape)."""
+    _single(synth.llama3_8b_q8_0().with_(name="llama3-8b-q8_0-4layers", n_layer=4))
+
+
 def test_mistral_7b_8slots_four_layers():
     """Mistral-7B width, window 4096, 8 slots at distinct positions in [1024, 16384], 4 layers."""
     _batch(synth.mistral_7b_slots().with_(name="mistral-7b-8slots-4layers", n_layer=4))

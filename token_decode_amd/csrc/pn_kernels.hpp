@@ -49,7 +49,9 @@ __host__ __device__ constexpr long long kv_v_off(bool tiled, int key, int d, int
                  : (long long)d * kPage + key;
 }
 
-enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2 };
+// WT_Q8: Q8_0 block-quantised weights (per row, blocks of 32 along K with one
+// fp16 scale each and int8 codes)
+enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2, WT_Q8 = 3 };
 enum AType { AT_F32 = 0, AT_BF16 = 1 };
 enum Pro { PRO_NORM = 0, PRO_LOAD = 1, PRO_CONV = 2 };  // CONV: A = round_act(fp32 rows), no norm
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_MOE_SWIGLU = 4,
@@ -65,8 +67,15 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __host__ __device__ constexpr int tile_k(int wt) { return wt == WT_F32 ? 16 : (wt == WT_BF16 ? 32 : 64); }
+// int8 and Q8_0 weights are widened to f16 and meet f16 activations
+__host__ __device__ constexpr bool f16_a(int wt) { return wt == WT_I8 || wt == WT_Q8; }
 // A-fragment bytes per (k-group, row) per tile
-__host__ __device__ constexpr int frag_bytes(int wt) { return wt == WT_I8 ? 32 : 16; }
+__host__ __device__ constexpr int frag_bytes(int wt) { return f16_a(wt) ? 32 : 16; }
+// Q8_0 tiles (16 rows x 64 k, two 32-wide blocks per row) order each row's k
+// so that MFMA step j of a tile covers exactly block j: element e of k-group g
+// (the g-th 16 of the tile's 64 positions) is k = 32 (e / 8) + 8 g + e % 8.
+// q8_pos gives the position of k; A-ready rows of a Q8_0 GEMM use the same order.
+__host__ __device__ constexpr int q8_pos(int k) { return ((k & 31) >> 3) * 16 + ((k >> 5) << 3) + (k & 7); }
 
 // ---------------------------------------------------------------- small helpers
 
@@ -137,6 +146,7 @@ enum { ERR_TOKEN = 1, ERR_NAN = 2 };
 //   bf16 weights, fp32 act: 3 planes of bf16 pieces (sum = the fp32 value)
 //   bf16 weights, bf16 act: 1 plane of bf16
 //   int8 weights (bf16 act): 1 plane of f16
+//   Q8_0 weights (bf16 act): 1 plane of f16, each tile's 64 k in q8_pos order
 //   fp32 weights:           1 plane of fp32 (bf16-rounded when act is bf16)
 // Plane p of row r starts at element p*plane + r*ld; rows are zero-padded to
 // a whole number of k tiles.
@@ -148,7 +158,9 @@ struct AReady {
         if constexpr (AT == AT_BF16) v = bf16_round(v);
         if constexpr (WT == WT_F32) {
             reinterpret_cast<float *>(base)[idx] = v;
-        } else if constexpr (WT == WT_I8) {
+        } else if constexpr (f16_a(WT)) {
+            // (rows and planes hold whole tiles, so idx % 64 is the k within the tile)
+            if constexpr (WT == WT_Q8) idx = (idx & ~63LL) | q8_pos((int)(idx & 63));
             reinterpret_cast<_Float16 *>(base)[idx] = (_Float16)v;
         } else if constexpr (PIECES == 1) {
             reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)bf16_rne_bits(v);
@@ -212,7 +224,8 @@ struct GemmArgs {
 // One weight tile times one A fragment.  a0 (and a1 for int8) hold this lane's
 // A values: 4 fp32, 8 bf16 or 16 f16 of row (lane & 15).
 template <int WT>
-__device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32x4 &a0, const u32x4 &a1) {
+__device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32x4 &a0, const u32x4 &a1,
+                                          uint32_t sv) {
     if constexpr (WT == WT_BF16) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
                                                       __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
@@ -236,10 +249,24 @@ __device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32
             if (i < 2) { b0[2 * i] = ulo; b0[2 * i + 1] = uhi; }
             else { b1[2 * (i - 2)] = ulo; b1[2 * (i - 2) + 1] = uhi; }
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0),
-                                                     __builtin_bit_cast(f16x8, b0), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1),
-                                                     __builtin_bit_cast(f16x8, b1), acc, 0, 0, 0);
+        if constexpr (WT == WT_Q8) {
+            // one step per 32-wide block, each scaled by the block's fp16 scale of
+            // this lane's weight row (the output column the lane holds)
+            const f16x2 d = __builtin_bit_cast(f16x2, sv);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0),
+                                                                    __builtin_bit_cast(f16x8, b0), z, 0, 0, 0);
+            const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1),
+                                                                    __builtin_bit_cast(f16x8, b1), z, 0, 0, 0);
+            const float d0 = (float)d[0], d1 = (float)d[1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(d1, t1[i], fmaf(d0, t0[i], acc[i]));
+        } else {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0),
+                                                         __builtin_bit_cast(f16x8, b0), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1),
+                                                         __builtin_bit_cast(f16x8, b1), acc, 0, 0, 0);
+        }
     }
 }
 
@@ -279,6 +306,20 @@ __device__ __forceinline__ void issue_w(u32x4 (&wr)[NTW][KU], const uint8_t *con
     }
 }
 
+// Q8_0: the block scales of the same tiles, one 32-bit word (two fp16) per
+// lane: its weight row's two blocks (scale tiles of 64 bytes, [row][block]).
+template <int NTW, int KU>
+__device__ __forceinline__ void issue_s(uint32_t (&sr)[NTW][KU], const uint8_t *const (&sbase)[NTW], int t_at,
+                                        int last) {
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+        const int t = min(t_at + i, last);
+#pragma unroll
+        for (int mt = 0; mt < NTW; ++mt)
+            sr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sbase[mt] + (long long)t * 64));
+    }
+}
+
 // Issue the direct A-fragment loads of one round (A-ready input not staged in
 // LDS), with the same clamping.  `arow` is a valid address on every lane; rows
 // past `rows` read row 0 and use zeros.
@@ -292,7 +333,7 @@ __device__ __forceinline__ void issue_a(u32x4 (&ar0)[KU], u32x4 (&ar1)[KU], cons
         const uint8_t *p = arow + (long long)t * TK * AReady<WT, AT>::ES;
         const u32x4 v0 = *reinterpret_cast<const u32x4 *>(p);
         ar0[i] = alive ? v0 : u32x4{0, 0, 0, 0};
-        if constexpr (WT == WT_I8) {
+        if constexpr (f16_a(WT)) {
             const u32x4 v1 = *reinterpret_cast<const u32x4 *>(p + 16);
             ar1[i] = alive ? v1 : u32x4{0, 0, 0, 0};
         }
@@ -302,9 +343,9 @@ __device__ __forceinline__ void issue_a(u32x4 (&ar0)[KU], u32x4 (&ar1)[KU], cons
 // MFMA over one round: tiles t_at..t_at+n-1 with A from LDS fragments or registers.
 template <int WT, int NTW, int KU, bool ALDS>
 __device__ __forceinline__ void compute_round(f32x4 (&acc)[NTW], const u32x4 (&wr)[NTW][KU],
-                                              const u32x4 (&ar0)[KU], const u32x4 (&ar1)[KU],
-                                              const uint8_t *sa, int rows, int am, int ag, bool alive,
-                                              const bool (&wlive)[NTW], int t_loc, int n) {
+                                              const uint32_t (&sr)[NTW][KU], const u32x4 (&ar0)[KU],
+                                              const u32x4 (&ar1)[KU], const uint8_t *sa, int rows, int am,
+                                              int ag, bool alive, const bool (&wlive)[NTW], int t_loc, int n) {
     constexpr int FB = frag_bytes(WT);
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
@@ -313,15 +354,15 @@ __device__ __forceinline__ void compute_round(f32x4 (&acc)[NTW], const u32x4 (&w
             if constexpr (ALDS) {
                 const uint8_t *af = sa + (((t_loc + i) * 4 + ag) * rows + am) * FB;
                 a0 = alive ? *reinterpret_cast<const u32x4 *>(af) : u32x4{0, 0, 0, 0};
-                if constexpr (WT == WT_I8)
+                if constexpr (f16_a(WT))
                     a1 = alive ? *reinterpret_cast<const u32x4 *>(af + 16) : u32x4{0, 0, 0, 0};
             } else {
                 a0 = ar0[i];
-                if constexpr (WT == WT_I8) a1 = ar1[i];
+                if constexpr (f16_a(WT)) a1 = ar1[i];
             }
 #pragma unroll
             for (int mt = 0; mt < NTW; ++mt)
-                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], a0, a1);
+                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], a0, a1, sr[mt][i]);
         }
     }
 }
@@ -341,8 +382,10 @@ __device__ __forceinline__ void put_a8(uint8_t *sa, int rows, int nb, int b, int
             *reinterpret_cast<f32x4 *>(sa + ((kt * 4 + gq) * rows + b) * FB) =
                 f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
         }
-    } else if constexpr (WT == WT_I8) {
-        const int gq = kin / EPG, el = kin % EPG;
+    } else if constexpr (f16_a(WT)) {
+        // k0..k0+7 are 8 consecutive positions in both orders (int8: k; Q8_0: q8_pos)
+        const int pos = WT == WT_Q8 ? q8_pos(kin) : kin;
+        const int gq = pos / EPG, el = pos % EPG;
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -566,7 +609,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
             const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
                                  ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
             st0[c] = *reinterpret_cast<const u32x4 *>(src);  // (rows past A are never stored)
-            if constexpr (WT == WT_I8) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
+            if constexpr (f16_a(WT)) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
         }
     }
 
@@ -622,13 +665,22 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
 #pragma unroll
     for (int mt = 0; mt < NTW; ++mt)
         mbase[mt] = ((PAIR && mt == 1) ? g.w2 : g.w) + (long long)ex * g.ew_stride + lane * 16;
+    // Q8_0 scale tiles (64 bytes per weight tile): this lane's row, both blocks
+    const uint8_t *sbase0[NTW];
+#pragma unroll
+    for (int mt = 0; mt < NTW; ++mt)
+        sbase0[mt] = reinterpret_cast<const uint8_t *>((PAIR && mt == 1) ? g.sc2 : g.sc) +
+                     (long long)ex * g.es_stride * 4 + am * 4;
+    const uint8_t *sbase[NTW];
     auto block_ptrs = [&](int blk, const uint8_t *(&wbase)[NTW], bool (&wlive)[NTW]) {
 #pragma unroll
         for (int mt = 0; mt < NTW; ++mt) {
             const int nt = PAIR ? blk : blk * NTW + mt;
             wlive[mt] = nt < g.n_tiles;
             // a dead tile (past the matrix) re-reads the block's first tile
-            wbase[mt] = mbase[mt] + ((long long)(wlive[mt] ? nt : (PAIR ? blk : blk * NTW)) * g.KT) * 1024;
+            const long long t0 = (long long)(wlive[mt] ? nt : (PAIR ? blk : blk * NTW)) * g.KT;
+            wbase[mt] = mbase[mt] + t0 * 1024;
+            if constexpr (WT == WT_Q8) sbase[mt] = sbase0[mt] + t0 * 64;
         }
     };
     const uint8_t *arow = nullptr;
@@ -646,7 +698,16 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     const uint8_t *wbase[NTW];
     bool wlive[NTW];
     block_ptrs(blk0, wbase, wlive);
+    uint32_t sca[NTW][KU], scb[NTW][KU];  // Q8_0 block scales of the rounds in wa, wb
+#pragma unroll
+    for (int mt = 0; mt < NTW; ++mt)
+#pragma unroll
+        for (int i = 0; i < KU; ++i) sca[mt][i] = scb[mt][i] = 0u;
     auto issue_first = [&]() {
+        if constexpr (WT == WT_Q8) {
+            issue_s<NTW, KU>(sca, sbase, wt0, last);
+            issue_s<NTW, KU>(scb, sbase, wt0 + KU, last);
+        }
         issue_w<NTW, KU>(wa, wbase, wt0, last);
         if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, wt0, last);
         issue_w<NTW, KU>(wb, wbase, wt0 + KU, last);
@@ -771,7 +832,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 const int f = wt0 * 4 + j;
                 uint8_t *dst = sa + (f * rows + m) * FB;
                 *reinterpret_cast<u32x4 *>(dst) = st0[c];
-                if constexpr (WT == WT_I8) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
+                if constexpr (f16_a(WT)) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
             }
         } else {
             const int chunksA = g.KT * 4;  // fragments per A row
@@ -783,7 +844,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                     if (m >= rows) continue;
                     uint8_t *dst = sa + (f * rows + m) * FB;
                     *reinterpret_cast<u32x4 *>(dst) = st0[c];
-                    if constexpr (WT == WT_I8) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
+                    if constexpr (f16_a(WT)) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
                 }
             };
             stage_a(0);  // from the phase-1 registers
@@ -798,7 +859,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                     const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
                                          ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
                     st0[c] = *reinterpret_cast<const u32x4 *>(src);
-                    if constexpr (WT == WT_I8) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
+                    if constexpr (f16_a(WT)) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
                 }
                 stage_a(base);
             }
@@ -815,16 +876,18 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         for (int mt = 0; mt < NTW; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int r = 0; r < rounds; r += 2) {
             const int ta = wt0 + r * KU;
-            compute_round<WT, NTW, KU, ALDS>(acc, wa, aa0, aa1, sa, rows, am, ag, alive, wlive, ta,
+            compute_round<WT, NTW, KU, ALDS>(acc, wa, sca, aa0, aa1, sa, rows, am, ag, alive, wlive, ta,
                                              min(KU, wt1 - ta));
             if (r + 2 < rounds) {
+                if constexpr (WT == WT_Q8) issue_s<NTW, KU>(sca, sbase, ta + 2 * KU, last);
                 issue_w<NTW, KU>(wa, wbase, ta + 2 * KU, last);
                 if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, ta + 2 * KU, last);
             }
             if (r + 1 < rounds) {
-                compute_round<WT, NTW, KU, ALDS>(acc, wb, ab0, ab1, sa, rows, am, ag, alive, wlive, ta + KU,
+                compute_round<WT, NTW, KU, ALDS>(acc, wb, scb, ab0, ab1, sa, rows, am, ag, alive, wlive, ta + KU,
                                                  min(KU, wt1 - ta - KU));
                 if (r + 3 < rounds) {
+                    if constexpr (WT == WT_Q8) issue_s<NTW, KU>(scb, sbase, ta + 3 * KU, last);
                     issue_w<NTW, KU>(wb, wbase, ta + 3 * KU, last);
                     if constexpr (!ALDS) issue_a<WT, AT, KU>(ab0, ab1, arow, alive, ta + 3 * KU, last);
                 }

@@ -54,7 +54,8 @@ struct Mat {  // one packed matrix (or a stack of experts' matrices)
     int N = 0, K = 0, n_tiles = 0, KT = 0;
     size_t bytes1 = 0;  // bytes of one packed matrix
     size_t off = 0;     // offset of the packed tiles
-    size_t soff = 0;    // offset of row scales (int8 only)
+    size_t soff = 0;    // offset of the scales: int8 row scales, Q8_0 block-scale tiles
+    size_t sbytes1 = 0; // bytes of one matrix's scales (0: none)
 };
 
 struct LayerOff {
@@ -170,11 +171,13 @@ struct OccKey {
 // more waves on a compute unit (a large A in LDS may leave room for one
 // work-group only).
 template <typename OccFn>
+// nw_cap: the most waves per work-group (Q8_0 kernels keep to 8: with 16 waves'
+// 128-register budget their block-scale registers spill)
 Plan make_plan(int kind, int nblk, int gz, int KT, int rows, int fb, int nw, OccFn occ_of, bool auto_nw = true,
-               int slots_in = 1) {
+               int slots_in = 1, int nw_cap = 16) {
     auto plan_for = [&](int want) {
         Plan p;
-        p.nw = want;
+        p.nw = std::min(want, nw_cap);
         p.gz = gz;
         p.nblk = nblk;
         const bool norm = norm_kind(kind);
@@ -199,7 +202,7 @@ Plan make_plan(int kind, int nblk, int gz, int KT, int rows, int fb, int nw, Occ
         return std::make_pair(p, p.nw * std::min<long long>(wpc, cdiv((long long)p.gx * gz, kCUs)));
     };
     auto best = plan_for(nw);
-    if (auto_nw && nw != 16) {
+    if (auto_nw && nw != 16 && nw_cap >= 16) {
         // 16-wave groups also stage four input rows per prologue batch (against one
         // with 8 waves): with several slots they win ties
         auto alt = plan_for(16);
@@ -245,7 +248,11 @@ int check_config_n(const pn_config *c) {
     if (c->n_ctx < 0) return fail(PN_EINVAL, "n_ctx must be >= 0");
     if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(PN_EINVAL, "rope_theta must be > 0");
     if (!(c->rms_norm_eps >= 0.f) || !std::isfinite(c->rms_norm_eps)) return fail(PN_EINVAL, "rms_norm_eps must be >= 0");
-    if (c->w_dtype < PN_F32 || c->w_dtype > PN_I8) return fail(PN_EINVAL, "bad w_dtype");
+    if (c->w_dtype < PN_F32 || c->w_dtype > PN_Q8_0) return fail(PN_EINVAL, "bad w_dtype");
+    if (c->w_dtype == PN_Q8_0 && c->act_dtype != PN_BF16)
+        return fail(PN_EUNSUPPORTED, "Q8_0 weights need bf16 activations");
+    if (c->w_dtype == PN_Q8_0 && (c->n_embd % 32 != 0 || c->n_ff % 32 != 0))
+        return fail(PN_EINVAL, "Q8_0 rows are whole 32-weight blocks: n_embd and n_ff must be multiples of 32");
     if (c->kv_dtype != PN_F32 && c->kv_dtype != PN_BF16) return fail(PN_EINVAL, "kv_dtype must be F32 or BF16");
     if (c->act_dtype != PN_F32 && c->act_dtype != PN_BF16) return fail(PN_EINVAL, "act_dtype must be F32 or BF16");
     if (c->w_dtype == PN_I8 && c->act_dtype != PN_BF16)
@@ -269,7 +276,13 @@ Mat make_mat(int N, int K, int wt) {
     m.n_tiles = cdiv(N, 16);
     m.KT = cdiv(K, tile_k(wt));
     m.bytes1 = (size_t)m.n_tiles * m.KT * 1024;
+    m.sbytes1 = wt == PN_I8 ? (size_t)m.n_tiles * 16 * 4 : wt == PN_Q8_0 ? (size_t)m.n_tiles * m.KT * 64 : 0;
     return m;
+}
+
+// Bytes of one source row of K weights in the caller's format.
+size_t src_row_bytes(int wt, int K) {
+    return wt == PN_Q8_0 ? (size_t)K / 32 * 34 : (size_t)K * dtype_size(wt);
 }
 
 
@@ -298,7 +311,7 @@ size_t layout_model(pn_model *m) {
     m->out_norm = bp.take((size_t)m->E * 4);
     m->out = make_mat(m->V, m->E, wt);
     m->out.off = bp.take(m->out.bytes1);
-    if (i8) m->out.soff = bp.take((size_t)m->out.n_tiles * 16 * 4);
+    if (m->out.sbytes1) m->out.soff = bp.take(m->out.sbytes1);
     m->L.assign(c.n_layer, LayerOff{});
     for (int l = 0; l < c.n_layer; ++l) {
         LayerOff &L = m->L[l];
@@ -313,11 +326,11 @@ size_t layout_model(pn_model *m) {
         L.down = make_mat(m->E, m->F, wt);
         for (Mat *mt : {&L.qkv, &L.o}) {
             mt->off = bp.take(mt->bytes1);
-            if (i8) mt->soff = bp.take((size_t)mt->n_tiles * 16 * 4);
+            if (mt->sbytes1) mt->soff = bp.take(mt->sbytes1);
         }
         for (Mat *mt : {&L.gate, &L.up, &L.down}) {
             mt->off = bp.take(mt->bytes1 * m->X);
-            if (i8) mt->soff = bp.take((size_t)mt->n_tiles * 16 * 4 * m->X);
+            if (mt->sbytes1) mt->soff = bp.take(mt->sbytes1 * m->X);
         }
     }
     // scratch
@@ -487,16 +500,20 @@ void copy_bytes(void *dst, const void *src, size_t n, hipStream_t s) {
                        (long long)n);
 }
 
-// Pack a row-major [N][K] matrix into tiles; with neox_d > 0 the rows of each
-// head block of neox_d rows are reordered into rotation pairs (see neox_src).
+// Pack a row-major [N][K] matrix into tiles (Q8_0: also its block scales into
+// the scale tiles at sdst_base); with neox_d > 0 the rows of each head block of
+// neox_d rows are reordered into rotation pairs (see neox_src).
 void pack(const void *src, int N, int K, int wt, const Mat &mt, int tile_row0, uint8_t *dst_base,
-          hipStream_t s, int neox_d = 0) {
+          uint8_t *sdst_base, hipStream_t s, int neox_d = 0) {
     const int nt = cdiv(N, 16);
     uint8_t *dst = dst_base + (size_t)tile_row0 * mt.KT * 1024;
     long long lanes = (long long)nt * mt.KT * 64;
     int blocks = cdiv(lanes, 256);
     const uint8_t *sp = (const uint8_t *)src;
-    if (wt == PN_F32)
+    if (wt == PN_Q8_0) {
+        uint8_t *sdst = sdst_base + (size_t)tile_row0 * mt.KT * 64;
+        hipLaunchKernelGGL(k_pack_q8, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, sdst, neox_d);
+    } else if (wt == PN_F32)
         hipLaunchKernelGGL(k_pack<4>, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, neox_d);
     else if (wt == PN_BF16)
         hipLaunchKernelGGL(k_pack<2>, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, neox_d);
@@ -518,7 +535,8 @@ void gemm_entry(int kind, int wt, int at, int nw, int amode, const GemmArgs &g, 
     else if (wt == PN_BF16) launch_gemm_bf16_bf16(kind, nw, amode, g, grid, lds, s, occ);
     else if (wt == PN_F32 && at == PN_F32) launch_gemm_f32_f32(kind, nw, amode, g, grid, lds, s, occ);
     else if (wt == PN_F32) launch_gemm_f32_bf16(kind, nw, amode, g, grid, lds, s, occ);
-    else launch_gemm_i8_bf16(kind, nw, amode, g, grid, lds, s, occ);
+    else if (wt == PN_I8) launch_gemm_i8_bf16(kind, nw, amode, g, grid, lds, s, occ);
+    else launch_gemm_q8_bf16(kind, nw, amode, g, grid, lds, s, occ);
 }
 
 int pro_of(int kind) {
@@ -694,13 +712,16 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         m->occ[key] = n;
         return n;
     };
-    const Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of, !m->nw_set, n);
-    const Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of, !m->nw_set, n);
+    const int cap = wt == PN_Q8_0 ? 8 : 16;
+    const Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of, !m->nw_set, n,
+                                 cap);
+    const Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of, !m->nw_set, n, cap);
     const Plan p_gu = make_plan(moe ? GK_MOE_SWIGLU : GK_SWIGLU, L0.gate.n_tiles, gz, L0.gate.KT, rows, fb,
-                                m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of, !m->nw_set, n);
+                                m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of, !m->nw_set, n, cap);
     const Plan p_dn = make_plan(moe ? GK_MOE_DOWN : GK_RESID, L0.down.n_tiles, gz, L0.down.KT, rows, fb,
-                                moe ? m->nw[GK_MOE_DOWN] : m->nw_down, occ_of, !m->nw_set);
-    const Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of, !m->nw_set, n);
+                                moe ? m->nw[GK_MOE_DOWN] : m->nw_down, occ_of, !m->nw_set, 1, cap);
+    const Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of,
+                                !m->nw_set, n, cap);
     // (plans for the other kinds take one row block per tile)
 
     for (int l = 0; l < c.n_layer; ++l) {
@@ -827,7 +848,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.sc = (const float *)(mb + L.gate.soff);
                 g.sc2 = (const float *)(mb + L.up.soff);
                 g.ew_stride = (long long)L.gate.bytes1;
-                g.es_stride = (long long)L.gate.n_tiles * 16;
+                g.es_stride = (long long)(L.gate.sbytes1 / 4);
                 g.N = F;
                 g.n_tiles = L.gate.n_tiles;
                 g.KT = L.gate.KT;
@@ -849,7 +870,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 g.w = (const uint8_t *)(mb + L.down.off);
                 g.sc = (const float *)(mb + L.down.soff);
                 g.ew_stride = (long long)L.down.bytes1;
-                g.es_stride = (long long)L.down.n_tiles * 16;
+                g.es_stride = (long long)(L.down.sbytes1 / 4);
                 g.N = E;
                 g.n_tiles = L.down.n_tiles;
                 g.KT = L.down.KT;
@@ -969,7 +990,7 @@ int pn_model_load_globals(pn_model *m, const void *tok_embd, const float *out_no
     const int es_aux = m->wt == PN_F32 ? 4 : 2;
     copy_bytes(mb + m->embd, tok_embd, (size_t)m->V * m->E * es_aux, s);
     copy_bytes(mb + m->out_norm, out_norm, (size_t)m->E * 4, s);
-    pack(w_out, m->V, m->E, m->wt, m->out, 0, (uint8_t *)(mb + m->out.off), s);
+    pack(w_out, m->V, m->E, m->wt, m->out, 0, (uint8_t *)(mb + m->out.off), (uint8_t *)(mb + m->out.soff), s);
     if (i8) {
         fill32(mb + m->out.soff, (size_t)m->out.n_tiles * 16, 0u, s);
         copy_bytes(mb + m->out.soff, s_out, (size_t)m->V * 4, s);
@@ -997,7 +1018,7 @@ int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *W, v
     if (cfg->qkv_bias && (!W->b_q || !W->b_k || !W->b_v)) return fail(PN_EINVAL, "missing q/k/v bias in layer %d", layer);
     hipStream_t s = S(stream);
     char *mb = m->base;
-    const int wt = m->wt, es_aux = wt == PN_F32 ? 4 : 2, esw = dtype_size(wt);
+    const int wt = m->wt, es_aux = wt == PN_F32 ? 4 : 2;
     const int E = m->E, HD = m->H * m->D, F = m->F, X = m->X;
     const LayerOff &L = m->L[layer];
     copy_bytes(mb + L.attn_norm, W->attn_norm, (size_t)E * 4, s);
@@ -1008,16 +1029,17 @@ int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *W, v
     // NeoX RoPE: q and k rows are packed in rotation-pair order, so the
     // epilogue's adjacent-pair rotation is the half-split one
     const int nx = cfg->rope_neox ? m->D : 0;
-    pack(W->wq, m->H * m->D, E, wt, L.qkv, 0, qkv, s, nx);
-    pack(W->wk, m->Hk * m->D, E, wt, L.qkv, m->H * m->D / 16, qkv, s, nx);
-    pack(W->wv, m->Hk * m->D, E, wt, L.qkv, (m->H + m->Hk) * m->D / 16, qkv, s);
+    uint8_t *qkv_s = (uint8_t *)(mb + L.qkv.soff);
+    pack(W->wq, m->H * m->D, E, wt, L.qkv, 0, qkv, qkv_s, s, nx);
+    pack(W->wk, m->Hk * m->D, E, wt, L.qkv, m->H * m->D / 16, qkv, qkv_s, s, nx);
+    pack(W->wv, m->Hk * m->D, E, wt, L.qkv, (m->H + m->Hk) * m->D / 16, qkv, qkv_s, s);
     if (cfg->qkv_bias) {
         char *bq = mb + L.bqkv;
         copy_rows_f32(bq, W->b_q, m->H * m->D, nx, s);
         copy_rows_f32(bq + (size_t)m->H * m->D * 4, W->b_k, m->Hk * m->D, nx, s);
         copy_rows_f32(bq + (size_t)(m->H + m->Hk) * m->D * 4, W->b_v, m->Hk * m->D, 0, s);
     }
-    pack(W->wo, E, HD, wt, L.o, 0, (uint8_t *)(mb + L.o.off), s);
+    pack(W->wo, E, HD, wt, L.o, 0, (uint8_t *)(mb + L.o.off), (uint8_t *)(mb + L.o.soff), s);
     if (i8) {
         char *sq = mb + L.qkv.soff;
         fill32(sq, (size_t)L.qkv.n_tiles * 16, 0u, s);
@@ -1028,12 +1050,15 @@ int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *W, v
         copy_bytes(mb + L.o.soff, W->s_o, (size_t)E * 4, s);
     }
     for (int e = 0; e < X; ++e) {
-        const char *g = (const char *)W->w_gate + (size_t)e * F * E * esw;
-        const char *u = (const char *)W->w_up + (size_t)e * F * E * esw;
-        const char *d = (const char *)W->w_down + (size_t)e * E * F * esw;
-        pack(g, F, E, wt, L.gate, 0, (uint8_t *)(mb + L.gate.off + e * L.gate.bytes1), s);
-        pack(u, F, E, wt, L.up, 0, (uint8_t *)(mb + L.up.off + e * L.up.bytes1), s);
-        pack(d, E, F, wt, L.down, 0, (uint8_t *)(mb + L.down.off + e * L.down.bytes1), s);
+        const char *g = (const char *)W->w_gate + (size_t)e * F * src_row_bytes(wt, E);
+        const char *u = (const char *)W->w_up + (size_t)e * F * src_row_bytes(wt, E);
+        const char *d = (const char *)W->w_down + (size_t)e * E * src_row_bytes(wt, F);
+        pack(g, F, E, wt, L.gate, 0, (uint8_t *)(mb + L.gate.off + e * L.gate.bytes1),
+             (uint8_t *)(mb + L.gate.soff + e * L.gate.sbytes1), s);
+        pack(u, F, E, wt, L.up, 0, (uint8_t *)(mb + L.up.off + e * L.up.bytes1),
+             (uint8_t *)(mb + L.up.soff + e * L.up.sbytes1), s);
+        pack(d, E, F, wt, L.down, 0, (uint8_t *)(mb + L.down.off + e * L.down.bytes1),
+             (uint8_t *)(mb + L.down.soff + e * L.down.sbytes1), s);
         if (i8) {
             const size_t gs = (size_t)L.gate.n_tiles * 16 * 4, ds = (size_t)L.down.n_tiles * 16 * 4;
             fill32(mb + L.gate.soff + e * gs, gs / 4, 0u, s);

@@ -304,6 +304,47 @@ __global__ void __launch_bounds__(256) k_pack(const uint8_t *src, int N, int K, 
     reinterpret_cast<u32x4 *>(dst)[i] = o;
 }
 
+// Q8_0 rows (per 32-weight block: fp16 scale, 32 int8 codes; K a multiple of
+// 32) into 1 KiB tiles of biased codes (u = q + 128) whose 16 bytes per lane
+// follow q8_pos, and 64-byte scale tiles holding each row's two block scales.
+// Blocks past K read as code 0 with scale 0.
+__global__ void __launch_bounds__(256) k_pack_q8(const uint8_t *src, int N, int K, int KT, int n_tiles,
+                                                  uint8_t *dst, uint8_t *sdst, int neox_d) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)n_tiles * KT * 64;
+    if (i >= total) return;
+    const int lane = (int)(i & 63);
+    const long long tileid = i >> 6;
+    const int nt = (int)(tileid / KT), kt = (int)(tileid % KT);
+    const int row = nt * 16 + (lane & 15), g = lane >> 4;
+    const int nblk = K / 32;
+    const uint8_t *srow = src + (long long)(row < N ? neox_src(row, neox_d) : 0) * nblk * 34;
+    uint8_t out[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int k = kt * 64 + 32 * (e >> 3) + 8 * g + (e & 7);
+        const int blk = k >> 5;
+        const uint8_t q = (row < N && blk < nblk) ? srow[blk * 34 + 2 + (k & 31)] : 0;
+        out[e] = (uint8_t)(q ^ 0x80u);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)out[4 * q] | ((uint32_t)out[4 * q + 1] << 8) | ((uint32_t)out[4 * q + 2] << 16) |
+               ((uint32_t)out[4 * q + 3] << 24);
+    reinterpret_cast<u32x4 *>(dst)[i] = o;
+    if (g == 0) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int blk = 2 * kt + j;
+            const uint32_t d = (row < N && blk < nblk) ? (uint32_t)srow[blk * 34] | ((uint32_t)srow[blk * 34 + 1] << 8) : 0u;
+            w |= d << (16 * j);
+        }
+        reinterpret_cast<uint32_t *>(sdst)[tileid * 16 + (lane & 15)] = w;
+    }
+}
+
 __global__ void __launch_bounds__(256) k_copy_rows_f32(float *dst, const float *src, int n, int neox_d) {
     const int r = blockIdx.x * 256 + threadIdx.x;
     if (r < n) dst[r] = src[neox_src(r, neox_d)];
