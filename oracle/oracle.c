@@ -41,7 +41,7 @@
  * a final RMSNorm.
  *
  * Precision.  Every stored value (fp32, bf16, int8 times an fp32 row scale,
- * or a Q8_0 code times its block's fp16 scale) is widened to double on read
+ * or a Q8_0 / Q4_0 code times its block's fp16 scale) is widened to double on read
  * and all arithmetic is double.  The
  * values that the decode step stores in a narrower type are rounded at the
  * same points: the inputs of every mat-vec (normed x, attention output,
@@ -61,11 +61,17 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_Q8_0 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_Q8_0 = 3, ORC_Q4_0 = 4 };
 
 /* Q8_0 block-quantised rows (GGUF-style): each row is cols/32 blocks of
  * 34 bytes, an fp16 scale d followed by 32 int8 codes q; weight = d * q. */
 enum { Q8_BLOCK = 32, Q8_BLOCK_BYTES = 34 };
+
+/* Q4_0 block-quantised rows (GGUF-style): each row is cols/32 blocks of
+ * 18 bytes, an fp16 scale d followed by 16 bytes of 4-bit codes: byte i holds
+ * code i in its low nibble and code i + 16 in its high nibble; weight =
+ * d * (code - 8). */
+enum { Q4_BLOCK_BYTES = 18 };
 
 typedef struct {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab;
@@ -136,6 +142,15 @@ static double q8_weight(const void *W, int cols, int r, int c) {
     return orc_half_to_double(dbits) * (double)(int8_t)blk[2 + c % Q8_BLOCK];
 }
 
+/* weight (r, c) of a Q4_0 matrix with `cols` columns, dequantised: d * (code - 8) */
+static double q4_weight(const void *W, int cols, int r, int c) {
+    const uint8_t *blk = (const uint8_t *)W + ((size_t)r * (size_t)(cols / Q8_BLOCK) + (size_t)(c / Q8_BLOCK)) * Q4_BLOCK_BYTES;
+    uint16_t dbits = (uint16_t)(blk[0] | (blk[1] << 8));
+    int i = c % Q8_BLOCK;
+    int code = i < 16 ? (blk[2 + i] & 15) : (blk[2 + i - 16] >> 4);
+    return orc_half_to_double(dbits) * (double)(code - 8);
+}
+
 /* element i of a stored tensor, widened to double (int8: the raw code) */
 static double rd(const void *p, int dt, size_t i) {
     switch (dt) {
@@ -150,7 +165,7 @@ static double rd(const void *p, int dt, size_t i) {
 static int g_threads = 1;
 
 /* y[r] = sum_c W[r][c] * x[c]; int8 rows are scaled by s[r] after the sum;
- * Q8_0 weights are dequantised (d * q) before the product ("Weight Loading
+ * Q8_0 and Q4_0 weights are dequantised (d * q, d * (code - 8)) before the product ("Weight Loading
  * Modes": dequantisation per block inside the mat-vec) */
 static void matvec(const void *W, int dt, const float *s, int rows, int cols, const double *x,
                    double *y) {
@@ -160,6 +175,8 @@ static void matvec(const void *W, int dt, const float *s, int rows, int cols, co
         size_t base = (size_t)r * (size_t)cols;
         if (dt == ORC_Q8_0)
             for (int c = 0; c < cols; ++c) acc += q8_weight(W, cols, r, c) * x[c];
+        else if (dt == ORC_Q4_0)
+            for (int c = 0; c < cols; ++c) acc += q4_weight(W, cols, r, c) * x[c];
         else
             for (int c = 0; c < cols; ++c) acc += rd(W, dt, base + (size_t)c) * x[c];
         y[r] = (dt == ORC_I8) ? (double)s[r] * acc : acc;

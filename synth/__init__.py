@@ -29,8 +29,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libsynth.so")
 _SRC = os.path.join(_HERE, "synth.c")
 
-F32, BF16, I8, Q8_0 = 0, 1, 2, 3
-Q8_BLOCK, Q8_BLOCK_BYTES = 32, 34
+F32, BF16, I8, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+Q8_BLOCK, Q8_BLOCK_BYTES, Q4_BLOCK_BYTES = 32, 34, 18
 DTYPE_NAMES = {F32: "f32", BF16: "bf16", I8: "i8"}
 
 TID_EMBD = 0
@@ -70,6 +70,8 @@ def lib():
         L.synth_int8_rows.restype = None
         L.synth_q8_0_rows.argtypes = [u64, u64, u64, u64, dbl, vp, ctypes.c_int]
         L.synth_q8_0_rows.restype = None
+        L.synth_q4_0_rows.argtypes = [u64, u64, u64, u64, dbl, vp, ctypes.c_int]
+        L.synth_q4_0_rows.restype = None
         L.synth_uniform_int.argtypes = [u64, u64, u64, i64, i64, vp]
         L.synth_uniform_int.restype = None
         L.synth_distinct_int.argtypes = [u64, u64, u64, i64, i64, vp]
@@ -110,6 +112,14 @@ def q8_0_rows(seed, tid, rows, cols, std=W_STD, threads=None):
     assert cols % Q8_BLOCK == 0
     out = np.empty((rows, cols // Q8_BLOCK * Q8_BLOCK_BYTES), dtype=np.uint8)
     lib().synth_q8_0_rows(seed, tid, rows, cols, std, out.ctypes.data, threads or default_threads())
+    return out
+
+
+def q4_0_rows(seed, tid, rows, cols, std=W_STD, threads=None):
+    """Q4_0 rows quantised from an fp32 N(0, std) draw: uint8 [rows][cols / 32 * 18]."""
+    assert cols % Q8_BLOCK == 0
+    out = np.empty((rows, cols // Q8_BLOCK * Q4_BLOCK_BYTES), dtype=np.uint8)
+    lib().synth_q4_0_rows(seed, tid, rows, cols, std, out.ctypes.data, threads or default_threads())
     return out
 
 
@@ -253,6 +263,8 @@ def _matrix(wl: Workload, tid: int, rows: int, cols: int, threads=None):
         return q, s
     if wl.w_dtype == Q8_0:
         return q8_0_rows(wl.seed, tid, rows, cols, W_STD, threads), None
+    if wl.w_dtype == Q4_0:
+        return q4_0_rows(wl.seed, tid, rows, cols, W_STD, threads), None
     m = normal(wl.seed, tid, rows * cols, 0.0, W_STD, wl.w_dtype, threads=threads)
     return m.reshape(rows, cols), None
 
@@ -359,6 +371,11 @@ def llama3_8b_q8_0() -> Workload:
     return llama3_8b_bf16().with_(name="llama3-8b-q8_0", w_dtype=Q8_0, act_dtype=BF16, seed=6)
 
 
+def llama3_8b_q4_0() -> Workload:
+    """Llama-3-8B shape, Q4_0 block-quantised weights, bf16 activations and KV; KV from 2048."""
+    return llama3_8b_bf16().with_(name="llama3-8b-q4_0", w_dtype=Q4_0, act_dtype=BF16, seed=7)
+
+
 WORKLOADS = {
     "tiny-fp32": tiny_fp32,
     "llama3-8b-bf16": llama3_8b_bf16,
@@ -366,4 +383,5 @@ WORKLOADS = {
     "mistral-7b-8slots": mistral_7b_slots,
     "mixtral-8x7b-16slots": mixtral_8x7b_slots,
     "llama3-8b-q8_0": llama3_8b_q8_0,
+    "llama3-8b-q4_0": llama3_8b_q4_0,
 }

@@ -335,3 +335,55 @@ void synth_q8_0_rows(uint64_t seed, uint64_t tid, uint64_t rows, uint64_t cols, 
     q8_ctx c = {stream_key(seed), tid, cols, std, out};
     parallel_rows(q8_rows_range, &c, rows, nthreads);
 }
+
+/* ---- Q4_0 block-quantised rows ---------------------------------------------
+ * Per block of 32 from an fp32 N(0, std) draw: m = the value of largest
+ * magnitude, d = m / -8 as fp16, codes round(w / d) + 8 clipped to [0, 15];
+ * 18 bytes per block: d, then byte i = code i | code (i + 16) << 4. */
+
+static double half_bits_signed_value(uint16_t h) {
+    double v = half_bits_value((uint16_t)(h & 0x7FFF));
+    return (h & 0x8000) ? -v : v;
+}
+
+typedef struct {
+    uint64_t key, tid, cols;
+    double std;
+    uint8_t *out;
+} q4_ctx;
+
+static void q4_rows_range(void *p, uint64_t lo, uint64_t hi) {
+    q4_ctx *c = (q4_ctx *)p;
+    const uint64_t nb = c->cols / 32;
+    for (uint64_t r = lo; r < hi; ++r) {
+        for (uint64_t b = 0; b < nb; ++b) {
+            float w[32];
+            double m = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                w[i] = (float)(c->std * normal_at(c->key, c->tid, r * c->cols + b * 32 + (uint64_t)i));
+                if (fabs((double)w[i]) > fabs(m)) m = (double)w[i];
+            }
+            const double dv = m / -8.0;
+            uint16_t dh = half_bits_rne(fabs(dv));
+            if (dv < 0) dh |= 0x8000;
+            const double d = half_bits_signed_value(dh);
+            uint8_t *blk = c->out + (r * nb + b) * 18;
+            blk[0] = (uint8_t)(dh & 0xFF);
+            blk[1] = (uint8_t)(dh >> 8);
+            int code[32];
+            for (int i = 0; i < 32; ++i) {
+                double t = d != 0.0 ? nearbyint((double)w[i] / d) + 8.0 : 8.0;
+                if (t > 15.0) t = 15.0;
+                if (t < 0.0) t = 0.0;
+                code[i] = (int)t;
+            }
+            for (int i = 0; i < 16; ++i) blk[2 + i] = (uint8_t)(code[i] | (code[i + 16] << 4));
+        }
+    }
+}
+
+void synth_q4_0_rows(uint64_t seed, uint64_t tid, uint64_t rows, uint64_t cols, double std, uint8_t *out,
+                     int nthreads) {
+    q4_ctx c = {stream_key(seed), tid, cols, std, out};
+    parallel_rows(q4_rows_range, &c, rows, nthreads);
+}

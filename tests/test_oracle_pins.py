@@ -289,6 +289,40 @@ def test_q8_0_matvec_matches_numpy_dequantisation():
     np.testing.assert_allclose(oracle.matvec(blocks, synth.Q8_0, None, 24, 160, x), deq @ x, rtol=1e-13)
 
 
+def _q4_block(d, codes):
+    codes = np.asarray(codes, np.uint8)
+    return np.concatenate([np.array([d], np.float16).view(np.uint8), codes[:16] | (codes[16:] << 4)])
+
+
+def test_q4_0_matvec_closed_form():
+    c = np.arange(32) % 16  # codes 0..15, 0..15: weights d * (-8..7)
+    W = np.stack([np.concatenate([_q4_block(0.5, c), _q4_block(-2.0 ** -18, c[::-1])])])
+    x = np.concatenate([np.ones(32), np.full(32, 3.0)])
+    y = oracle.matvec(W, synth.Q4_0, None, 1, 64, x)
+    want = 0.5 * (c - 8).sum() + 3.0 * -(2.0 ** -18) * (c[::-1] - 8).sum()
+    np.testing.assert_array_equal(y, [want])
+    for col in (0, 5, 15, 16, 31, 32, 48, 63):  # low nibbles hold codes 0..15, high ones 16..31
+        e = np.zeros(64)
+        e[col] = 1.0
+        d = (0.5, -(2.0 ** -18))[col // 32]
+        code = (c, c[::-1])[col // 32][col % 32]
+        assert oracle.matvec(W, synth.Q4_0, None, 1, 64, e)[0] == d * (int(code) - 8)
+
+
+def test_q4_0_rows_are_a_faithful_quantisation():
+    q = synth.q4_0_rows(3, 9, 24, 160)
+    b = q.reshape(24, 5, 18)
+    d = b[:, :, 0:2].copy().view(np.float16).astype(np.float64)
+    codes = np.concatenate([b[:, :, 2:] & 15, b[:, :, 2:] >> 4], axis=2).astype(np.float64)
+    deq = (d * (codes - 8)).reshape(24, 160)
+    w = synth.normal(3, 9, 24 * 160, 0.0, synth.W_STD, synth.F32).reshape(24, 160).astype(np.float64)
+    amax = np.abs(w.reshape(24, 5, 32)).max(axis=2)
+    # half a step (d = amax / 8) everywhere, a whole step where +8 steps clip to code 15
+    assert np.all(np.abs(deq - w).reshape(24, 5, 32).max(axis=2) <= amax / 8 * 1.01)
+    x = rng.standard_normal(160)
+    np.testing.assert_allclose(oracle.matvec(q, synth.Q4_0, None, 24, 160, x), deq @ x, rtol=1e-13)
+
+
 # ----------------------------------------------------------------------------- whole model
 
 def _torch_forward(wl, W, tokens):
@@ -296,11 +330,16 @@ def _torch_forward(wl, W, tokens):
     E, H, Hk, d = wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim
 
     def mat(m, s=None):
-        if m.dtype == np.uint8:  # Q8_0 blocks: fp16 scale, 32 int8 codes
+        if m.dtype == np.uint8 and wl.w_dtype == synth.Q8_0:  # fp16 scale, 32 int8 codes
             b = m.reshape(m.shape[0], -1, 34)
             d = b[:, :, 0:2].copy().view(np.float16).astype(np.float64)
             q = b[:, :, 2:].copy().view(np.int8).astype(np.float64)
             return torch.tensor((d * q).reshape(m.shape[0], -1))
+        if m.dtype == np.uint8:  # Q4_0: fp16 scale, codes 0..15 in nibbles (i low, i + 16 high)
+            b = m.reshape(m.shape[0], -1, 18)
+            d = b[:, :, 0:2].copy().view(np.float16).astype(np.float64)
+            codes = np.concatenate([b[:, :, 2:] & 15, b[:, :, 2:] >> 4], axis=2).astype(np.float64)
+            return torch.tensor((d * (codes - 8)).reshape(m.shape[0], -1))
         if m.dtype == np.uint16:
             a = torch.tensor(synth.bf16_to_f32(m).astype(np.float64))
         elif m.dtype == np.int8:
@@ -392,6 +431,10 @@ SMALL = [
     synth.tiny_fp32().with_(name="small-q8_0-moe-neox-bias", w_dtype=synth.Q8_0, kv_dtype=synth.F32,
                             act_dtype=synth.BF16, n_expert=4, n_expert_used=2, n_ff=96, rope_neox=True,
                             qkv_bias=True, seed=19),
+    synth.tiny_fp32().with_(name="small-q4_0", w_dtype=synth.Q4_0, kv_dtype=synth.BF16, act_dtype=synth.BF16,
+                            seed=20, n_ff=672),
+    synth.tiny_fp32().with_(name="small-q4_0-moe-window", w_dtype=synth.Q4_0, kv_dtype=synth.BF16,
+                            act_dtype=synth.BF16, n_expert=4, n_expert_used=2, n_ff=96, sliding_window=5, seed=21),
 ]
 
 
