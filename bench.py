@@ -46,7 +46,8 @@ def algorithmic_bytes(wl, positions):
     cache-resident) are not counted.  Dense models only."""
     E, H, Hk, d, F, V, L = (wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim, wl.n_ff,
                             wl.n_vocab, wl.n_layer)
-    sw = {0: 4, 1: 2, 2: 1, 3: 34 / 32}[wl.w_dtype]  # Q8_0: 34 bytes per 32 weights (codes + fp16 scale)
+    # Q8_0 / Q4_0: 34 / 18 bytes per 32 weights (codes + fp16 scale)
+    sw = {0: 4, 1: 2, 2: 1, 3: 34 / 32, 4: 18 / 32}[wl.w_dtype]
     skv = 4 if wl.kv_dtype == 0 else 2
     se = 4 if wl.w_dtype == 0 else 2
     per_layer_w = (H * d * E + 2 * Hk * d * E + E * H * d + 3 * E * F) * sw
@@ -64,7 +65,7 @@ def algorithmic_bytes(wl, positions):
 def gemm_bytes(wl, kind):
     """Algorithmic bytes of one launch of a GEMM kernel class (weights + scales)."""
     E, H, Hk, d, F, V = wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim, wl.n_ff, wl.n_vocab
-    sw = {0: 4, 1: 2, 2: 1, 3: 34 / 32}[wl.w_dtype]
+    sw = {0: 4, 1: 2, 2: 1, 3: 34 / 32, 4: 18 / 32}[wl.w_dtype]
     sc = 4 if wl.w_dtype == 2 else 0
     rows, cols = {"qkv": ((H + 2 * Hk) * d, E), "o": (E, H * d), "gateup": (2 * F, E),
                   "down": (E, F), "lmhead": (V, E)}[kind]
@@ -219,7 +220,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {0: "f32", 1: "bf16", 2: "int8", 3: "q8_0"}[wl.w_dtype] + "-weights/" +
+        "dtype": {0: "f32", 1: "bf16", 2: "int8", 3: "q8_0", 4: "q4_0"}[wl.w_dtype] + "-weights/" +
                  {0: "f32", 1: "bf16"}[wl.act_dtype] + "-act",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) cached K/V)",
         "config": {"workload": wl.name, "n_layer": wl.n_layer, "n_embd": wl.n_embd,

@@ -49,7 +49,7 @@ enum {
     PN_EHIP = -4          /* HIP runtime failure */
 };
 
-typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3 } pn_dtype;
+typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3, PN_Q4_0 = 4 } pn_dtype;
 
 /* Model dimensions and storage types.  Field names and defaults follow the
  * pages' config keys ("Engine Architecture", section "Config Parsing"):
@@ -60,11 +60,14 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3 } pn_dtype;
  * Mixtral is llama with an expert count > 0).
  *
  *  w_dtype   matrices: PN_F32, PN_BF16, PN_I8 (symmetric int8 with one fp32
- *            scale per output row), or PN_Q8_0 (GGUF-style block quantisation:
- *            each row is K/32 blocks of 34 bytes, an fp16 scale d then 32 int8
- *            codes q, weight = d*q, dequantised inside the mat-vec: "Engine
- *            Architecture", section "Weight Loading Modes"; needs act_dtype
- *            PN_BF16 and n_embd, n_ff multiples of 32).  The token embedding
+ *            scale per output row), or a GGUF-style block quantisation,
+ *            dequantised inside the mat-vec ("Engine Architecture", section
+ *            "Weight Loading Modes"): each row is K/32 blocks, PN_Q8_0 blocks
+ *            of 34 bytes (an fp16 scale d, then 32 int8 codes q; weight d*q),
+ *            PN_Q4_0 blocks of 18 bytes (an fp16 scale d, then 16 bytes whose
+ *            byte i holds code i in its low nibble and code i+16 in its high
+ *            one; weight d*(code-8)).  Block formats need act_dtype PN_BF16
+ *            and n_embd, n_ff multiples of 32.  The token embedding
  *            and the MoE router are fp32 when w_dtype is PN_F32 and bf16
  *            otherwise; norm gains are fp32.
  *  kv_dtype  cached K and V: PN_F32 or PN_BF16 (k is cached after RoPE).

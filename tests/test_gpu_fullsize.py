@@ -78,6 +78,11 @@ def test_llama3_8b_q8_0_four_layers():
     _single(synth.llama3_8b_q8_0().with_(name="llama3-8b-q8_0-4layers", n_layer=4))
 
 
+def test_llama3_8b_q4_0_four_layers():
+    """The same with Q4_0 weights (4-bit codes, 512-byte tiles)."""
+    _single(synth.llama3_8b_q4_0().with_(name="llama3-8b-q4_0-4layers", n_layer=4))
+
+
 def test_mistral_7b_8slots_four_layers():
     """Mistral-7B width, window 4096, 8 slots at distinct positions in [1024, 16384], 4 layers."""
     _batch(synth.mistral_7b_slots().with_(name="mistral-7b-8slots-4layers", n_layer=4))

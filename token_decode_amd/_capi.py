@@ -6,7 +6,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpn.so")
 
 PN_OK, PN_EINVAL, PN_ERANGE, PN_EUNSUPPORTED, PN_EHIP = 0, -1, -2, -3, -4
-PN_F32, PN_BF16, PN_I8, PN_Q8_0 = 0, 1, 2, 3
+PN_F32, PN_BF16, PN_I8, PN_Q8_0, PN_Q4_0 = 0, 1, 2, 3, 4
 (PN_K_EMBED, PN_K_QKV, PN_K_ATTN, PN_K_O, PN_K_GATEUP, PN_K_DOWN, PN_K_LMHEAD, PN_K_ARGMAX,
  PN_K_ROUTER, PN_K_MOE_GATEUP, PN_K_MOE_DOWN, PN_K_MOE_COMBINE, PN_K_COUNT) = range(13)
 PN_OPT_ATTN_KEYS_PER_SPLIT = 1

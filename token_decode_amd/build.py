@@ -30,6 +30,7 @@ GEMM_UNITS = [  # (weight type, activation type, entry point)
     (1, 1, "launch_gemm_bf16_bf16"),
     (2, 1, "launch_gemm_i8_bf16"),
     (3, 1, "launch_gemm_q8_bf16"),
+    (4, 1, "launch_gemm_q4_bf16"),
 ]
 
 

@@ -49,9 +49,9 @@ __host__ __device__ constexpr long long kv_v_off(bool tiled, int key, int d, int
                  : (long long)d * kPage + key;
 }
 
-// WT_Q8: Q8_0 block-quantised weights (per row, blocks of 32 along K with one
-// fp16 scale each and int8 codes)
-enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2, WT_Q8 = 3 };
+// WT_Q8 / WT_Q4: Q8_0 / Q4_0 block-quantised weights (per row, blocks of 32
+// along K with one fp16 scale each, and int8 / 4-bit codes)
+enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2, WT_Q8 = 3, WT_Q4 = 4 };
 enum AType { AT_F32 = 0, AT_BF16 = 1 };
 enum Pro { PRO_NORM = 0, PRO_LOAD = 1, PRO_CONV = 2 };  // CONV: A = round_act(fp32 rows), no norm
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_MOE_SWIGLU = 4,
@@ -67,14 +67,19 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __host__ __device__ constexpr int tile_k(int wt) { return wt == WT_F32 ? 16 : (wt == WT_BF16 ? 32 : 64); }
-// int8 and Q8_0 weights are widened to f16 and meet f16 activations
-__host__ __device__ constexpr bool f16_a(int wt) { return wt == WT_I8 || wt == WT_Q8; }
+// int8 and block-quantised weights are widened to f16 and meet f16 activations
+__host__ __device__ constexpr bool f16_a(int wt) { return wt == WT_I8 || wt == WT_Q8 || wt == WT_Q4; }
+// block-quantised weights: one fp16 scale per 32 weights of a row
+__host__ __device__ constexpr bool blockq(int wt) { return wt == WT_Q8 || wt == WT_Q4; }
+// bytes of one packed 16-row weight tile (Q4_0: 64 k of 4-bit codes)
+__host__ __device__ constexpr int tile_bytes(int wt) { return wt == WT_Q4 ? 512 : 1024; }
 // A-fragment bytes per (k-group, row) per tile
 __host__ __device__ constexpr int frag_bytes(int wt) { return f16_a(wt) ? 32 : 16; }
-// Q8_0 tiles (16 rows x 64 k, two 32-wide blocks per row) order each row's k
-// so that MFMA step j of a tile covers exactly block j: element e of k-group g
-// (the g-th 16 of the tile's 64 positions) is k = 32 (e / 8) + 8 g + e % 8.
-// q8_pos gives the position of k; A-ready rows of a Q8_0 GEMM use the same order.
+// Block-quantised tiles (16 rows x 64 k, two 32-wide blocks per row) order each
+// row's k so that MFMA step j of a tile covers exactly block j: element e of
+// k-group g (the g-th 16 of the tile's 64 positions) is k = 32 (e / 8) + 8 g +
+// e % 8.  q8_pos gives the position of k; A-ready rows of a Q8_0 or Q4_0 GEMM
+// use the same order.
 __host__ __device__ constexpr int q8_pos(int k) { return ((k & 31) >> 3) * 16 + ((k >> 5) << 3) + (k & 7); }
 
 // ---------------------------------------------------------------- small helpers
@@ -146,7 +151,7 @@ enum { ERR_TOKEN = 1, ERR_NAN = 2 };
 //   bf16 weights, fp32 act: 3 planes of bf16 pieces (sum = the fp32 value)
 //   bf16 weights, bf16 act: 1 plane of bf16
 //   int8 weights (bf16 act): 1 plane of f16
-//   Q8_0 weights (bf16 act): 1 plane of f16, each tile's 64 k in q8_pos order
+//   Q8_0 / Q4_0 weights (bf16 act): 1 plane of f16, each tile's 64 k in q8_pos order
 //   fp32 weights:           1 plane of fp32 (bf16-rounded when act is bf16)
 // Plane p of row r starts at element p*plane + r*ld; rows are zero-padded to
 // a whole number of k tiles.
@@ -160,7 +165,7 @@ struct AReady {
             reinterpret_cast<float *>(base)[idx] = v;
         } else if constexpr (f16_a(WT)) {
             // (rows and planes hold whole tiles, so idx % 64 is the k within the tile)
-            if constexpr (WT == WT_Q8) idx = (idx & ~63LL) | q8_pos((int)(idx & 63));
+            if constexpr (blockq(WT)) idx = (idx & ~63LL) | q8_pos((int)(idx & 63));
             reinterpret_cast<_Float16 *>(base)[idx] = (_Float16)v;
         } else if constexpr (PIECES == 1) {
             reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)bf16_rne_bits(v);
@@ -237,19 +242,33 @@ __device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bw[2], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bw[3], acc, 0, 0, 0);
     } else {
-        const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
         u32x4 b0, b1;
+        if constexpr (WT == WT_Q4) {
+            // 8 codes per word (elements 0..7 in wv[0], 8..15 in wv[1]); pair j of
+            // a word sits at bits 4j and 16 + 4j, so one mask gives both halves:
+            // code c -> f16 (1024 + c), minus 1032 leaves c - 8 exactly
+            const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // byte u -> f16 (1024 + u); minus 1152 leaves the signed code exactly
-            const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04010400u);
-            const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04030402u);
-            const uint32_t ulo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
-            const uint32_t uhi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
-            if (i < 2) { b0[2 * i] = ulo; b0[2 * i + 1] = uhi; }
-            else { b1[2 * (i - 2)] = ulo; b1[2 * (i - 2) + 1] = uhi; }
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = ((wv[0] >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+                const uint32_t hi = ((wv[1] >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+                b0[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
+                b1[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
+            }
+        } else {
+            const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // byte u -> f16 (1024 + u); minus 1152 leaves the signed code exactly
+                const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04010400u);
+                const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04030402u);
+                const uint32_t ulo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
+                const uint32_t uhi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
+                if (i < 2) { b0[2 * i] = ulo; b0[2 * i + 1] = uhi; }
+                else { b1[2 * (i - 2)] = ulo; b1[2 * (i - 2) + 1] = uhi; }
+            }
         }
-        if constexpr (WT == WT_Q8) {
+        if constexpr (blockq(WT)) {
             // one step per 32-wide block, each scaled by the block's fp16 scale of
             // this lane's weight row (the output column the lane holds)
             const f16x2 d = __builtin_bit_cast(f16x2, sv);
@@ -294,15 +313,21 @@ __device__ __forceinline__ void rope_pair(float &y0, float &y1, float2 cs) {
 // Issue the weight loads of one round: KU tiles of each matrix, always the
 // same number of loads (tiles past `last` re-read tile `last`), so the
 // compiler can wait for exactly the rounds it needs.
-template <int NTW, int KU>
+template <int WT, int NTW, int KU>
 __device__ __forceinline__ void issue_w(u32x4 (&wr)[NTW][KU], const uint8_t *const (&wbase)[NTW], int t_at,
                                         int last) {
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
         const int t = min(t_at + i, last);
 #pragma unroll
-        for (int mt = 0; mt < NTW; ++mt)
-            wr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wbase[mt] + (long long)t * 1024));
+        for (int mt = 0; mt < NTW; ++mt) {
+            if constexpr (WT == WT_Q4) {  // 8 bytes per lane
+                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(wbase[mt] + (long long)t * 512));
+                wr[mt][i] = u32x4{v[0], v[1], 0u, 0u};
+            } else {
+                wr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wbase[mt] + (long long)t * 1024));
+            }
+        }
     }
 }
 
@@ -384,7 +409,7 @@ __device__ __forceinline__ void put_a8(uint8_t *sa, int rows, int nb, int b, int
         }
     } else if constexpr (f16_a(WT)) {
         // k0..k0+7 are 8 consecutive positions in both orders (int8: k; Q8_0: q8_pos)
-        const int pos = WT == WT_Q8 ? q8_pos(kin) : kin;
+        const int pos = blockq(WT) ? q8_pos(kin) : kin;
         const int gq = pos / EPG, el = pos % EPG;
         u32x4 o;
 #pragma unroll
@@ -664,7 +689,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     const uint8_t *mbase[NTW];
 #pragma unroll
     for (int mt = 0; mt < NTW; ++mt)
-        mbase[mt] = ((PAIR && mt == 1) ? g.w2 : g.w) + (long long)ex * g.ew_stride + lane * 16;
+        mbase[mt] = ((PAIR && mt == 1) ? g.w2 : g.w) + (long long)ex * g.ew_stride + lane * (tile_bytes(WT) / 64);
     // Q8_0 scale tiles (64 bytes per weight tile): this lane's row, both blocks
     const uint8_t *sbase0[NTW];
 #pragma unroll
@@ -679,8 +704,8 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
             wlive[mt] = nt < g.n_tiles;
             // a dead tile (past the matrix) re-reads the block's first tile
             const long long t0 = (long long)(wlive[mt] ? nt : (PAIR ? blk : blk * NTW)) * g.KT;
-            wbase[mt] = mbase[mt] + t0 * 1024;
-            if constexpr (WT == WT_Q8) sbase[mt] = sbase0[mt] + t0 * 64;
+            wbase[mt] = mbase[mt] + t0 * tile_bytes(WT);
+            if constexpr (blockq(WT)) sbase[mt] = sbase0[mt] + t0 * 64;
         }
     };
     const uint8_t *arow = nullptr;
@@ -704,13 +729,13 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < KU; ++i) sca[mt][i] = scb[mt][i] = 0u;
     auto issue_first = [&]() {
-        if constexpr (WT == WT_Q8) {
+        if constexpr (blockq(WT)) {
             issue_s<NTW, KU>(sca, sbase, wt0, last);
             issue_s<NTW, KU>(scb, sbase, wt0 + KU, last);
         }
-        issue_w<NTW, KU>(wa, wbase, wt0, last);
+        issue_w<WT, NTW, KU>(wa, wbase, wt0, last);
         if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, wt0, last);
-        issue_w<NTW, KU>(wb, wbase, wt0 + KU, last);
+        issue_w<WT, NTW, KU>(wb, wbase, wt0 + KU, last);
         if constexpr (!ALDS) issue_a<WT, AT, KU>(ab0, ab1, arow, alive, wt0 + KU, last);
     };
     issue_first();
@@ -879,16 +904,16 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
             compute_round<WT, NTW, KU, ALDS>(acc, wa, sca, aa0, aa1, sa, rows, am, ag, alive, wlive, ta,
                                              min(KU, wt1 - ta));
             if (r + 2 < rounds) {
-                if constexpr (WT == WT_Q8) issue_s<NTW, KU>(sca, sbase, ta + 2 * KU, last);
-                issue_w<NTW, KU>(wa, wbase, ta + 2 * KU, last);
+                if constexpr (blockq(WT)) issue_s<NTW, KU>(sca, sbase, ta + 2 * KU, last);
+                issue_w<WT, NTW, KU>(wa, wbase, ta + 2 * KU, last);
                 if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, ta + 2 * KU, last);
             }
             if (r + 1 < rounds) {
                 compute_round<WT, NTW, KU, ALDS>(acc, wb, scb, ab0, ab1, sa, rows, am, ag, alive, wlive, ta + KU,
                                                  min(KU, wt1 - ta - KU));
                 if (r + 3 < rounds) {
-                    if constexpr (WT == WT_Q8) issue_s<NTW, KU>(scb, sbase, ta + 3 * KU, last);
-                    issue_w<NTW, KU>(wb, wbase, ta + 3 * KU, last);
+                    if constexpr (blockq(WT)) issue_s<NTW, KU>(scb, sbase, ta + 3 * KU, last);
+                    issue_w<WT, NTW, KU>(wb, wbase, ta + 3 * KU, last);
                     if constexpr (!ALDS) issue_a<WT, AT, KU>(ab0, ab1, arow, alive, ta + 3 * KU, last);
                 }
             }

@@ -40,6 +40,8 @@ void launch_gemm_i8_bf16(int kind, int nw, int amode, const GemmArgs &g, dim3 gr
                          int *occ);
 void launch_gemm_q8_bf16(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
                          int *occ);
+void launch_gemm_q4_bf16(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
+                         int *occ);
 
 // Defined once per (head_dim, KV type) in pn_attn.hip: attention with G query
 // heads per KV head, and the split combine when `combine`.

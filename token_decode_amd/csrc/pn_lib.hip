@@ -171,8 +171,8 @@ struct OccKey {
 // more waves on a compute unit (a large A in LDS may leave room for one
 // work-group only).
 template <typename OccFn>
-// nw_cap: the most waves per work-group (Q8_0 kernels keep to 8: with 16 waves'
-// 128-register budget their block-scale registers spill)
+// nw_cap: the most waves per work-group (block-quantised kernels keep to 8: with
+// 16 waves' 128-register budget their block-scale registers spill)
 Plan make_plan(int kind, int nblk, int gz, int KT, int rows, int fb, int nw, OccFn occ_of, bool auto_nw = true,
                int slots_in = 1, int nw_cap = 16) {
     auto plan_for = [&](int want) {
@@ -248,11 +248,12 @@ int check_config_n(const pn_config *c) {
     if (c->n_ctx < 0) return fail(PN_EINVAL, "n_ctx must be >= 0");
     if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(PN_EINVAL, "rope_theta must be > 0");
     if (!(c->rms_norm_eps >= 0.f) || !std::isfinite(c->rms_norm_eps)) return fail(PN_EINVAL, "rms_norm_eps must be >= 0");
-    if (c->w_dtype < PN_F32 || c->w_dtype > PN_Q8_0) return fail(PN_EINVAL, "bad w_dtype");
-    if (c->w_dtype == PN_Q8_0 && c->act_dtype != PN_BF16)
-        return fail(PN_EUNSUPPORTED, "Q8_0 weights need bf16 activations");
-    if (c->w_dtype == PN_Q8_0 && (c->n_embd % 32 != 0 || c->n_ff % 32 != 0))
-        return fail(PN_EINVAL, "Q8_0 rows are whole 32-weight blocks: n_embd and n_ff must be multiples of 32");
+    if (c->w_dtype < PN_F32 || c->w_dtype > PN_Q4_0) return fail(PN_EINVAL, "bad w_dtype");
+    const bool bq = c->w_dtype == PN_Q8_0 || c->w_dtype == PN_Q4_0;
+    if (bq && c->act_dtype != PN_BF16)
+        return fail(PN_EUNSUPPORTED, "block-quantised weights need bf16 activations");
+    if (bq && (c->n_embd % 32 != 0 || c->n_ff % 32 != 0))
+        return fail(PN_EINVAL, "block-quantised rows are whole 32-weight blocks: n_embd and n_ff must be multiples of 32");
     if (c->kv_dtype != PN_F32 && c->kv_dtype != PN_BF16) return fail(PN_EINVAL, "kv_dtype must be F32 or BF16");
     if (c->act_dtype != PN_F32 && c->act_dtype != PN_BF16) return fail(PN_EINVAL, "act_dtype must be F32 or BF16");
     if (c->w_dtype == PN_I8 && c->act_dtype != PN_BF16)
@@ -275,14 +276,14 @@ Mat make_mat(int N, int K, int wt) {
     m.K = K;
     m.n_tiles = cdiv(N, 16);
     m.KT = cdiv(K, tile_k(wt));
-    m.bytes1 = (size_t)m.n_tiles * m.KT * 1024;
-    m.sbytes1 = wt == PN_I8 ? (size_t)m.n_tiles * 16 * 4 : wt == PN_Q8_0 ? (size_t)m.n_tiles * m.KT * 64 : 0;
+    m.bytes1 = (size_t)m.n_tiles * m.KT * tile_bytes(wt);
+    m.sbytes1 = wt == PN_I8 ? (size_t)m.n_tiles * 16 * 4 : blockq(wt) ? (size_t)m.n_tiles * m.KT * 64 : 0;
     return m;
 }
 
 // Bytes of one source row of K weights in the caller's format.
 size_t src_row_bytes(int wt, int K) {
-    return wt == PN_Q8_0 ? (size_t)K / 32 * 34 : (size_t)K * dtype_size(wt);
+    return wt == PN_Q8_0 ? (size_t)K / 32 * 34 : wt == PN_Q4_0 ? (size_t)K / 32 * 18 : (size_t)K * dtype_size(wt);
 }
 
 
@@ -506,13 +507,16 @@ void copy_bytes(void *dst, const void *src, size_t n, hipStream_t s) {
 void pack(const void *src, int N, int K, int wt, const Mat &mt, int tile_row0, uint8_t *dst_base,
           uint8_t *sdst_base, hipStream_t s, int neox_d = 0) {
     const int nt = cdiv(N, 16);
-    uint8_t *dst = dst_base + (size_t)tile_row0 * mt.KT * 1024;
+    uint8_t *dst = dst_base + (size_t)tile_row0 * mt.KT * tile_bytes(wt);
     long long lanes = (long long)nt * mt.KT * 64;
     int blocks = cdiv(lanes, 256);
     const uint8_t *sp = (const uint8_t *)src;
-    if (wt == PN_Q8_0) {
+    if (blockq(wt)) {
         uint8_t *sdst = sdst_base + (size_t)tile_row0 * mt.KT * 64;
-        hipLaunchKernelGGL(k_pack_q8, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, sdst, neox_d);
+        if (wt == PN_Q8_0)
+            hipLaunchKernelGGL(k_pack_q8, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, sdst, neox_d);
+        else
+            hipLaunchKernelGGL(k_pack_q4, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, sdst, neox_d);
     } else if (wt == PN_F32)
         hipLaunchKernelGGL(k_pack<4>, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, neox_d);
     else if (wt == PN_BF16)
@@ -536,7 +540,8 @@ void gemm_entry(int kind, int wt, int at, int nw, int amode, const GemmArgs &g, 
     else if (wt == PN_F32 && at == PN_F32) launch_gemm_f32_f32(kind, nw, amode, g, grid, lds, s, occ);
     else if (wt == PN_F32) launch_gemm_f32_bf16(kind, nw, amode, g, grid, lds, s, occ);
     else if (wt == PN_I8) launch_gemm_i8_bf16(kind, nw, amode, g, grid, lds, s, occ);
-    else launch_gemm_q8_bf16(kind, nw, amode, g, grid, lds, s, occ);
+    else if (wt == PN_Q8_0) launch_gemm_q8_bf16(kind, nw, amode, g, grid, lds, s, occ);
+    else launch_gemm_q4_bf16(kind, nw, amode, g, grid, lds, s, occ);
 }
 
 int pro_of(int kind) {
@@ -712,7 +717,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         m->occ[key] = n;
         return n;
     };
-    const int cap = wt == PN_Q8_0 ? 8 : 16;
+    const int cap = blockq(wt) ? 8 : 16;
     const Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of, !m->nw_set, n,
                                  cap);
     const Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of, !m->nw_set, n, cap);

@@ -345,6 +345,48 @@ __global__ void __launch_bounds__(256) k_pack_q8(const uint8_t *src, int N, int 
     }
 }
 
+// Q4_0 rows (per 32-weight block: fp16 scale, 16 bytes whose byte i holds code
+// i in its low nibble and code i + 16 in its high one; K a multiple of 32) into
+// 512-byte tiles, 8 bytes per lane: the lane's 16 elements in q8_pos order, as
+// two words of 8 codes, pair j of a word at bits 4j and 16 + 4j (the layout
+// the GEMM widens with one mask per pair); scale tiles as for Q8_0.  Blocks
+// past K read as code 8 (weight 0) with scale 0.
+__global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int K, int KT, int n_tiles,
+                                                  uint8_t *dst, uint8_t *sdst, int neox_d) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)n_tiles * KT * 64;
+    if (i >= total) return;
+    const int lane = (int)(i & 63);
+    const long long tileid = i >> 6;
+    const int nt = (int)(tileid / KT), kt = (int)(tileid % KT);
+    const int row = nt * 16 + (lane & 15), g = lane >> 4;
+    const int nblk = K / 32;
+    const uint8_t *srow = src + (long long)(row < N ? neox_src(row, neox_d) : 0) * nblk * 18;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int k = kt * 64 + 32 * (e >> 3) + 8 * g + (e & 7);
+        const int blk = k >> 5, kb = k & 31;
+        uint32_t code = 8u;
+        if (row < N && blk < nblk) {
+            const uint8_t byte = srow[blk * 18 + 2 + (kb & 15)];
+            code = kb < 16 ? (byte & 15u) : (uint32_t)(byte >> 4);
+        }
+        w[e >> 3] |= code << (4 * ((e & 7) >> 1) + 16 * (e & 1));
+    }
+    reinterpret_cast<u32x2 *>(dst)[i] = u32x2{w[0], w[1]};
+    if (g == 0) {
+        uint32_t sw = 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int blk = 2 * kt + j;
+            const uint32_t d = (row < N && blk < nblk) ? (uint32_t)srow[blk * 18] | ((uint32_t)srow[blk * 18 + 1] << 8) : 0u;
+            sw |= d << (16 * j);
+        }
+        reinterpret_cast<uint32_t *>(sdst)[tileid * 16 + (lane & 15)] = sw;
+    }
+}
+
 __global__ void __launch_bounds__(256) k_copy_rows_f32(float *dst, const float *src, int n, int neox_d) {
     const int r = blockIdx.x * 256 + threadIdx.x;
     if (r < n) dst[r] = src[neox_src(r, neox_d)];
