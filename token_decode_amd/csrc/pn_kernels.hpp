@@ -66,21 +66,31 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-__host__ __device__ constexpr int tile_k(int wt) { return wt == WT_F32 ? 16 : (wt == WT_BF16 ? 32 : 64); }
+__host__ __device__ constexpr int tile_k(int wt) {
+    return wt == WT_F32 ? 16 : (wt == WT_BF16 ? 32 : (wt == WT_Q4 ? 128 : 64));
+}
 // int8 and block-quantised weights are widened to f16 and meet f16 activations
 __host__ __device__ constexpr bool f16_a(int wt) { return wt == WT_I8 || wt == WT_Q8 || wt == WT_Q4; }
 // block-quantised weights: one fp16 scale per 32 weights of a row
 __host__ __device__ constexpr bool blockq(int wt) { return wt == WT_Q8 || wt == WT_Q4; }
-// bytes of one packed 16-row weight tile (Q4_0: 64 k of 4-bit codes)
-__host__ __device__ constexpr int tile_bytes(int wt) { return wt == WT_Q4 ? 512 : 1024; }
-// A-fragment bytes per (k-group, row) per tile
-__host__ __device__ constexpr int frag_bytes(int wt) { return f16_a(wt) ? 32 : 16; }
-// Block-quantised tiles (16 rows x 64 k, two 32-wide blocks per row) order each
-// row's k so that MFMA step j of a tile covers exactly block j: element e of
-// k-group g (the g-th 16 of the tile's 64 positions) is k = 32 (e / 8) + 8 g +
-// e % 8.  q8_pos gives the position of k; A-ready rows of a Q8_0 or Q4_0 GEMM
-// use the same order.
-__host__ __device__ constexpr int q8_pos(int k) { return ((k & 31) >> 3) * 16 + ((k >> 5) << 3) + (k & 7); }
+// the scale words of one block-quantised tile per lane: its row's fp16 block
+// scales (two for Q8_0, four for Q4_0)
+template <int WT>
+using SReg = typename std::conditional<WT == WT_Q4, u32x2, uint32_t>::type;
+// A-fragment bytes per (k-group, row) per tile: a quarter of a tile row's k
+__host__ __device__ constexpr int frag_bytes(int wt) { return wt == WT_Q4 ? 64 : (f16_a(wt) ? 32 : 16); }
+// 16-byte vectors per A fragment, and 32-wide blocks per tile row (block formats)
+__host__ __device__ constexpr int frag_vecs(int wt) { return frag_bytes(wt) / 16; }
+__host__ __device__ constexpr int tile_blocks(int wt) { return tile_k(wt) / 32; }
+// Block-quantised tiles (16 rows x 64 k for Q8_0, x 128 k for Q4_0: two or four
+// 32-wide blocks per row) order each row's k so that MFMA step j of a tile
+// covers exactly block j: element e of k-group g (the g-th quarter of the
+// tile's positions, 8 per block) is k = 32 (e / 8) + 8 g + e % 8.  blk_pos
+// gives the position of k in its tile; A-ready rows of these GEMMs use the
+// same order.
+__host__ __device__ constexpr int blk_pos(int nblk, int k) {
+    return ((k & 31) >> 3) * (8 * nblk) + ((k >> 5) << 3) + (k & 7);
+}
 
 // ---------------------------------------------------------------- small helpers
 
@@ -151,7 +161,7 @@ enum { ERR_TOKEN = 1, ERR_NAN = 2 };
 //   bf16 weights, fp32 act: 3 planes of bf16 pieces (sum = the fp32 value)
 //   bf16 weights, bf16 act: 1 plane of bf16
 //   int8 weights (bf16 act): 1 plane of f16
-//   Q8_0 / Q4_0 weights (bf16 act): 1 plane of f16, each tile's 64 k in q8_pos order
+//   Q8_0 / Q4_0 weights (bf16 act): 1 plane of f16, each tile's k in blk_pos order
 //   fp32 weights:           1 plane of fp32 (bf16-rounded when act is bf16)
 // Plane p of row r starts at element p*plane + r*ld; rows are zero-padded to
 // a whole number of k tiles.
@@ -164,8 +174,11 @@ struct AReady {
         if constexpr (WT == WT_F32) {
             reinterpret_cast<float *>(base)[idx] = v;
         } else if constexpr (f16_a(WT)) {
-            // (rows and planes hold whole tiles, so idx % 64 is the k within the tile)
-            if constexpr (blockq(WT)) idx = (idx & ~63LL) | q8_pos((int)(idx & 63));
+            // (rows and planes hold whole tiles, so idx % TK is the k within the tile)
+            if constexpr (blockq(WT)) {
+                constexpr int TK = tile_k(WT);
+                idx = (idx & ~(long long)(TK - 1)) | blk_pos(tile_blocks(WT), (int)(idx & (TK - 1)));
+            }
             reinterpret_cast<_Float16 *>(base)[idx] = (_Float16)v;
         } else if constexpr (PIECES == 1) {
             reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)bf16_rne_bits(v);
@@ -226,35 +239,42 @@ struct GemmArgs {
     const int *pt[kMaxSlots];
 };
 
-// One weight tile times one A fragment.  a0 (and a1 for int8) hold this lane's
-// A values: 4 fp32, 8 bf16 or 16 f16 of row (lane & 15).
+// fp16 halves of a 32-bit word as floats
+__device__ __forceinline__ float half_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)); }
+
+// One weight tile times one A fragment.  a holds this lane's A values of the
+// tile: 4 fp32, 8 bf16, or 16 / 32 f16 of row (lane & 15).
 template <int WT>
-__device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32x4 &a0, const u32x4 &a1,
-                                          uint32_t sv) {
+__device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32x4 (&a)[frag_vecs(WT)],
+                                          SReg<WT> sv) {
     if constexpr (WT == WT_BF16) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[0]),
                                                       __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
     } else if constexpr (WT == WT_F32) {
-        const f32x4 av = __builtin_bit_cast(f32x4, a0);
+        const f32x4 av = __builtin_bit_cast(f32x4, a[0]);
         const f32x4 bw = __builtin_bit_cast(f32x4, wv);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bw[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bw[1], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bw[2], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bw[3], acc, 0, 0, 0);
     } else {
-        u32x4 b0, b1;
+        constexpr int NS = frag_vecs(WT);  // f16 MFMA steps per tile (one per block for block formats)
+        u32x4 b[NS];
         if constexpr (WT == WT_Q4) {
-            // 8 codes per word (elements 0..7 in wv[0], 8..15 in wv[1]); pair j of
-            // a word sits at bits 4j and 16 + 4j, so one mask gives both halves:
-            // code c -> f16 (1024 + c), minus 1032 leaves c - 8 exactly
+            // word j holds the 8 codes of step j; pair p of a word sits at bits 4p
+            // and 16 + 4p, so one mask gives both halves: code c -> f16 (1024 + c),
+            // minus 1032 leaves c - 8 exactly
             const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = ((wv[0] >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-                const uint32_t hi = ((wv[1] >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-                b0[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
-                b1[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
-            }
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t h = ((wv[j] >> (4 * q)) & 0x000F000Fu) | 0x64006400u;
+                    b[j][q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) - off);
+                }
         } else {
             const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
@@ -262,29 +282,42 @@ __device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32
                 // byte u -> f16 (1024 + u); minus 1152 leaves the signed code exactly
                 const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04010400u);
                 const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wv[i], 0x04030402u);
-                const uint32_t ulo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
-                const uint32_t uhi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
-                if (i < 2) { b0[2 * i] = ulo; b0[2 * i + 1] = uhi; }
-                else { b1[2 * (i - 2)] = ulo; b1[2 * (i - 2) + 1] = uhi; }
+                b[i >> 1][2 * (i & 1)] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
+                b[i >> 1][2 * (i & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
             }
         }
         if constexpr (blockq(WT)) {
-            // one step per 32-wide block, each scaled by the block's fp16 scale of
-            // this lane's weight row (the output column the lane holds)
-            const f16x2 d = __builtin_bit_cast(f16x2, sv);
+            // one step per 32-wide block from zero, scaled by the block's fp16
+            // scale of this lane's weight row (the output column the lane holds)
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0),
-                                                                    __builtin_bit_cast(f16x8, b0), z, 0, 0, 0);
-            const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1),
-                                                                    __builtin_bit_cast(f16x8, b1), z, 0, 0, 0);
-            const float d0 = (float)d[0], d1 = (float)d[1];
+            f32x4 t[NS];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = fmaf(d1, t1[i], fmaf(d0, t0[i], acc[i]));
+            for (int j = 0; j < NS; ++j)
+                t[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[j]),
+                                                              __builtin_bit_cast(f16x8, b[j]), z, 0, 0, 0);
+            // the scales are taken out of their words by shifts and masks: a bit
+            // cast of the second word of a two-word vector to f16x2 was compiled
+            // here from the first word for both (every block read blocks 0, 1's scales)
+            float d[NS];
+            if constexpr (NS == 2) {
+                d[0] = half_lo(sv);
+                d[1] = half_hi(sv);
+            } else {
+                const uint32_t w0 = sv[0], w1 = sv[1];
+                d[0] = half_lo(w0);
+                d[1] = half_hi(w0);
+                d[2] = half_lo(w1);
+                d[3] = half_hi(w1);
+            }
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[j], t[j][i], acc[i]);
         } else {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0),
-                                                         __builtin_bit_cast(f16x8, b0), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1),
-                                                         __builtin_bit_cast(f16x8, b1), acc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[j]),
+                                                             __builtin_bit_cast(f16x8, b[j]), acc, 0, 0, 0);
         }
     }
 }
@@ -320,28 +353,24 @@ __device__ __forceinline__ void issue_w(u32x4 (&wr)[NTW][KU], const uint8_t *con
     for (int i = 0; i < KU; ++i) {
         const int t = min(t_at + i, last);
 #pragma unroll
-        for (int mt = 0; mt < NTW; ++mt) {
-            if constexpr (WT == WT_Q4) {  // 8 bytes per lane
-                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(wbase[mt] + (long long)t * 512));
-                wr[mt][i] = u32x4{v[0], v[1], 0u, 0u};
-            } else {
-                wr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wbase[mt] + (long long)t * 1024));
-            }
-        }
+        for (int mt = 0; mt < NTW; ++mt)
+            wr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wbase[mt] + (long long)t * 1024));
     }
 }
 
-// Q8_0: the block scales of the same tiles, one 32-bit word (two fp16) per
-// lane: its weight row's two blocks (scale tiles of 64 bytes, [row][block]).
-template <int NTW, int KU>
-__device__ __forceinline__ void issue_s(uint32_t (&sr)[NTW][KU], const uint8_t *const (&sbase)[NTW], int t_at,
+// Block formats: the scales of the same tiles, one word (Q8_0) or two (Q4_0)
+// per lane: its weight row's block scales (scale tiles of 4 bytes per block
+// and row, [row][block]).
+template <int WT, int NTW, int KU>
+__device__ __forceinline__ void issue_s(SReg<WT> (&sr)[NTW][KU], const uint8_t *const (&sbase)[NTW], int t_at,
                                         int last) {
+    constexpr int SB = 16 * 2 * tile_blocks(WT);  // bytes of one scale tile
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
         const int t = min(t_at + i, last);
 #pragma unroll
         for (int mt = 0; mt < NTW; ++mt)
-            sr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sbase[mt] + (long long)t * 64));
+            sr[mt][i] = __builtin_nontemporal_load(reinterpret_cast<const SReg<WT> *>(sbase[mt] + (long long)t * SB));
     }
 }
 
@@ -349,45 +378,45 @@ __device__ __forceinline__ void issue_s(uint32_t (&sr)[NTW][KU], const uint8_t *
 // LDS), with the same clamping.  `arow` is a valid address on every lane; rows
 // past `rows` read row 0 and use zeros.
 template <int WT, int AT, int KU>
-__device__ __forceinline__ void issue_a(u32x4 (&ar0)[KU], u32x4 (&ar1)[KU], const uint8_t *arow, bool alive,
+__device__ __forceinline__ void issue_a(u32x4 (&ar)[KU][frag_vecs(WT)], const uint8_t *arow, bool alive,
                                         int t_at, int last) {
     constexpr int TK = tile_k(WT);
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
         const int t = min(t_at + i, last);
         const uint8_t *p = arow + (long long)t * TK * AReady<WT, AT>::ES;
-        const u32x4 v0 = *reinterpret_cast<const u32x4 *>(p);
-        ar0[i] = alive ? v0 : u32x4{0, 0, 0, 0};
-        if constexpr (f16_a(WT)) {
-            const u32x4 v1 = *reinterpret_cast<const u32x4 *>(p + 16);
-            ar1[i] = alive ? v1 : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int v = 0; v < frag_vecs(WT); ++v) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(p + 16 * v);
+            ar[i][v] = alive ? x : u32x4{0, 0, 0, 0};
         }
     }
 }
 
 // MFMA over one round: tiles t_at..t_at+n-1 with A from LDS fragments or registers.
+// With A in LDS the round is branch-free: lanes past the A rows and tiles past
+// n read zero fragments (at zoff), which add nothing; so the compiler can
+// overlap one tile's matrix-core steps with the next tile's arithmetic.
 template <int WT, int NTW, int KU, bool ALDS>
 __device__ __forceinline__ void compute_round(f32x4 (&acc)[NTW], const u32x4 (&wr)[NTW][KU],
-                                              const uint32_t (&sr)[NTW][KU], const u32x4 (&ar0)[KU],
-                                              const u32x4 (&ar1)[KU], const uint8_t *sa, int rows, int am,
-                                              int ag, bool alive, const bool (&wlive)[NTW], int t_loc, int n) {
-    constexpr int FB = frag_bytes(WT);
+                                              const SReg<WT> (&sr)[NTW][KU], const u32x4 (&ar)[KU][frag_vecs(WT)],
+                                              const uint8_t *sa, int zoff, int rows, int am, int ag, bool alive,
+                                              const bool (&wlive)[NTW], int t_loc, int n) {
+    constexpr int FB = frag_bytes(WT), AV = frag_vecs(WT);
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
-        if (i < n) {
-            u32x4 a0, a1 = u32x4{0, 0, 0, 0};
-            if constexpr (ALDS) {
-                const uint8_t *af = sa + (((t_loc + i) * 4 + ag) * rows + am) * FB;
-                a0 = alive ? *reinterpret_cast<const u32x4 *>(af) : u32x4{0, 0, 0, 0};
-                if constexpr (f16_a(WT))
-                    a1 = alive ? *reinterpret_cast<const u32x4 *>(af + 16) : u32x4{0, 0, 0, 0};
-            } else {
-                a0 = ar0[i];
-                if constexpr (f16_a(WT)) a1 = ar1[i];
-            }
+        if constexpr (ALDS) {
+            const uint8_t *af = (alive && i < n) ? sa + (((t_loc + i) * 4 + ag) * rows + am) * FB : sa + zoff;
+            u32x4 a[AV];
+#pragma unroll
+            for (int v = 0; v < AV; ++v) a[v] = *reinterpret_cast<const u32x4 *>(af + 16 * v);
 #pragma unroll
             for (int mt = 0; mt < NTW; ++mt)
-                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], a0, a1, sr[mt][i]);
+                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], a, sr[mt][i]);
+        } else if (i < n) {
+#pragma unroll
+            for (int mt = 0; mt < NTW; ++mt)
+                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], ar[i], sr[mt][i]);
         }
     }
 }
@@ -408,8 +437,8 @@ __device__ __forceinline__ void put_a8(uint8_t *sa, int rows, int nb, int b, int
                 f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
         }
     } else if constexpr (f16_a(WT)) {
-        // k0..k0+7 are 8 consecutive positions in both orders (int8: k; Q8_0: q8_pos)
-        const int pos = blockq(WT) ? q8_pos(kin) : kin;
+        // k0..k0+7 are 8 consecutive positions in both orders (int8: k; block formats: blk_pos)
+        const int pos = blockq(WT) ? blk_pos(tile_blocks(WT), kin) : kin;
         const int gq = pos / EPG, el = pos % EPG;
         u32x4 o;
 #pragma unroll
@@ -541,9 +570,15 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     const int rows = nb * PIECES;
     const int am = lane & 15, ag = lane >> 4;
     const bool alive = am < rows;
-    uint8_t *sa = smem;  // A fragments [kt][k-group][row][FB bytes]
-    const int abytes = ALDS ? (g.KT * 4 * rows * FB + 255) & ~255 : 0;
+    uint8_t *sa = smem;  // A fragments [kt][k-group][row][FB bytes], then 256 zero bytes
+    const int zoff = ALDS ? (g.KT * 4 * rows * FB + 255) & ~255 : 0;
+    const int abytes = ALDS ? zoff + 256 : 0;
     float *red = reinterpret_cast<float *>(smem + abytes);  // [wave][mt][m][n]
+    // The zero block: lanes past the A rows, and tiles past the end of a round,
+    // read their A fragments here, so a round has no branches.  Every wave
+    // writes it before its own reads (a wave's LDS operations run in order; all
+    // writers write zeros).
+    if (ALDS && lane < 16) *reinterpret_cast<u32x4 *>(sa + zoff + lane * 16) = u32x4{0, 0, 0, 0};
     float *C = red + NW * NTW * 256;                          // [mt][m][n]
 
     // ---- phase 1: the prologue's loads, all issued before any weight load and
@@ -567,7 +602,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     constexpr bool wl = WL;
     float xv[CH][8], gv[CH][8];
     float ssv[SPW][8];
-    u32x4 st0[CHA], st1[CHA];
+    u32x4 st[CHA][frag_vecs(WT)];
     if constexpr (XPRO) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
@@ -633,8 +668,9 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
             const long long r = MOE ? s_ent[b] : b;
             const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
                                  ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
-            st0[c] = *reinterpret_cast<const u32x4 *>(src);  // (rows past A are never stored)
-            if constexpr (f16_a(WT)) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
+#pragma unroll
+            for (int v = 0; v < frag_vecs(WT); ++v)  // (rows past A are never stored)
+                st[c][v] = *reinterpret_cast<const u32x4 *>(src + 16 * v);
         }
     }
 
@@ -689,13 +725,15 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     const uint8_t *mbase[NTW];
 #pragma unroll
     for (int mt = 0; mt < NTW; ++mt)
-        mbase[mt] = ((PAIR && mt == 1) ? g.w2 : g.w) + (long long)ex * g.ew_stride + lane * (tile_bytes(WT) / 64);
-    // Q8_0 scale tiles (64 bytes per weight tile): this lane's row, both blocks
+        mbase[mt] = ((PAIR && mt == 1) ? g.w2 : g.w) + (long long)ex * g.ew_stride + lane * 16;
+    // block formats: scale tiles (2 bytes per block and row) after each weight
+    // tile's scales; this lane reads its row's
+    constexpr int SB = 16 * 2 * tile_blocks(WT);
     const uint8_t *sbase0[NTW];
 #pragma unroll
     for (int mt = 0; mt < NTW; ++mt)
         sbase0[mt] = reinterpret_cast<const uint8_t *>((PAIR && mt == 1) ? g.sc2 : g.sc) +
-                     (long long)ex * g.es_stride * 4 + am * 4;
+                     (long long)ex * g.es_stride * 4 + am * (SB / 16);
     const uint8_t *sbase[NTW];
     auto block_ptrs = [&](int blk, const uint8_t *(&wbase)[NTW], bool (&wlive)[NTW]) {
 #pragma unroll
@@ -704,8 +742,8 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
             wlive[mt] = nt < g.n_tiles;
             // a dead tile (past the matrix) re-reads the block's first tile
             const long long t0 = (long long)(wlive[mt] ? nt : (PAIR ? blk : blk * NTW)) * g.KT;
-            wbase[mt] = mbase[mt] + t0 * tile_bytes(WT);
-            if constexpr (blockq(WT)) sbase[mt] = sbase0[mt] + t0 * 64;
+            wbase[mt] = mbase[mt] + t0 * 1024;
+            if constexpr (blockq(WT)) sbase[mt] = sbase0[mt] + t0 * SB;
         }
     };
     const uint8_t *arow = nullptr;
@@ -719,24 +757,24 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         arow = reinterpret_cast<const uint8_t *>(g.a) + (sp * g.a_plane + r * g.lda + ag * (TK / 4)) * ES;
     }
     u32x4 wa[NTW][KU], wb[NTW][KU];
-    u32x4 aa0[KU], aa1[KU], ab0[KU], ab1[KU];
+    u32x4 aa[KU][frag_vecs(WT)], ab[KU][frag_vecs(WT)];
     const uint8_t *wbase[NTW];
     bool wlive[NTW];
     block_ptrs(blk0, wbase, wlive);
-    uint32_t sca[NTW][KU], scb[NTW][KU];  // Q8_0 block scales of the rounds in wa, wb
+    SReg<WT> sca[NTW][KU], scb[NTW][KU];  // block scales of the rounds in wa, wb
 #pragma unroll
     for (int mt = 0; mt < NTW; ++mt)
 #pragma unroll
-        for (int i = 0; i < KU; ++i) sca[mt][i] = scb[mt][i] = 0u;
+        for (int i = 0; i < KU; ++i) sca[mt][i] = scb[mt][i] = SReg<WT>{};
     auto issue_first = [&]() {
         if constexpr (blockq(WT)) {
-            issue_s<NTW, KU>(sca, sbase, wt0, last);
-            issue_s<NTW, KU>(scb, sbase, wt0 + KU, last);
+            issue_s<WT, NTW, KU>(sca, sbase, wt0, last);
+            issue_s<WT, NTW, KU>(scb, sbase, wt0 + KU, last);
         }
         issue_w<WT, NTW, KU>(wa, wbase, wt0, last);
-        if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, wt0, last);
+        if constexpr (!ALDS) issue_a<WT, AT, KU>(aa, arow, alive, wt0, last);
         issue_w<WT, NTW, KU>(wb, wbase, wt0 + KU, last);
-        if constexpr (!ALDS) issue_a<WT, AT, KU>(ab0, ab1, arow, alive, wt0 + KU, last);
+        if constexpr (!ALDS) issue_a<WT, AT, KU>(ab, arow, alive, wt0 + KU, last);
     };
     issue_first();
 
@@ -856,8 +894,8 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 if (m >= rows || j >= nfw) continue;
                 const int f = wt0 * 4 + j;
                 uint8_t *dst = sa + (f * rows + m) * FB;
-                *reinterpret_cast<u32x4 *>(dst) = st0[c];
-                if constexpr (f16_a(WT)) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
+#pragma unroll
+                for (int v = 0; v < frag_vecs(WT); ++v) *reinterpret_cast<u32x4 *>(dst + 16 * v) = st[c][v];
             }
         } else {
             const int chunksA = g.KT * 4;  // fragments per A row
@@ -868,8 +906,8 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                     const int m = idx / chunksA, f = idx - m * chunksA;
                     if (m >= rows) continue;
                     uint8_t *dst = sa + (f * rows + m) * FB;
-                    *reinterpret_cast<u32x4 *>(dst) = st0[c];
-                    if constexpr (f16_a(WT)) *reinterpret_cast<u32x4 *>(dst + 16) = st1[c];
+#pragma unroll
+                    for (int v = 0; v < frag_vecs(WT); ++v) *reinterpret_cast<u32x4 *>(dst + 16 * v) = st[c][v];
                 }
             };
             stage_a(0);  // from the phase-1 registers
@@ -883,8 +921,8 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                     const long long r = MOE ? s_ent[b] : b;
                     const uint8_t *src = reinterpret_cast<const uint8_t *>(g.a) +
                                          ((long long)s * g.a_plane + r * g.lda + (long long)(in ? f : 0) * (TK / 4)) * ES;
-                    st0[c] = *reinterpret_cast<const u32x4 *>(src);
-                    if constexpr (f16_a(WT)) st1[c] = *reinterpret_cast<const u32x4 *>(src + 16);
+#pragma unroll
+                    for (int v = 0; v < frag_vecs(WT); ++v) st[c][v] = *reinterpret_cast<const u32x4 *>(src + 16 * v);
                 }
                 stage_a(base);
             }
@@ -901,20 +939,20 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         for (int mt = 0; mt < NTW; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int r = 0; r < rounds; r += 2) {
             const int ta = wt0 + r * KU;
-            compute_round<WT, NTW, KU, ALDS>(acc, wa, sca, aa0, aa1, sa, rows, am, ag, alive, wlive, ta,
+            compute_round<WT, NTW, KU, ALDS>(acc, wa, sca, aa, sa, zoff, rows, am, ag, alive, wlive, ta,
                                              min(KU, wt1 - ta));
             if (r + 2 < rounds) {
-                if constexpr (blockq(WT)) issue_s<NTW, KU>(sca, sbase, ta + 2 * KU, last);
+                if constexpr (blockq(WT)) issue_s<WT, NTW, KU>(sca, sbase, ta + 2 * KU, last);
                 issue_w<WT, NTW, KU>(wa, wbase, ta + 2 * KU, last);
-                if constexpr (!ALDS) issue_a<WT, AT, KU>(aa0, aa1, arow, alive, ta + 2 * KU, last);
+                if constexpr (!ALDS) issue_a<WT, AT, KU>(aa, arow, alive, ta + 2 * KU, last);
             }
             if (r + 1 < rounds) {
-                compute_round<WT, NTW, KU, ALDS>(acc, wb, scb, ab0, ab1, sa, rows, am, ag, alive, wlive, ta + KU,
+                compute_round<WT, NTW, KU, ALDS>(acc, wb, scb, ab, sa, zoff, rows, am, ag, alive, wlive, ta + KU,
                                                  min(KU, wt1 - ta - KU));
                 if (r + 3 < rounds) {
-                    if constexpr (blockq(WT)) issue_s<NTW, KU>(scb, sbase, ta + 3 * KU, last);
+                    if constexpr (blockq(WT)) issue_s<WT, NTW, KU>(scb, sbase, ta + 3 * KU, last);
                     issue_w<WT, NTW, KU>(wb, wbase, ta + 3 * KU, last);
-                    if constexpr (!ALDS) issue_a<WT, AT, KU>(ab0, ab1, arow, alive, ta + 3 * KU, last);
+                    if constexpr (!ALDS) issue_a<WT, AT, KU>(ab, arow, alive, ta + 3 * KU, last);
                 }
             }
         }

@@ -143,10 +143,11 @@ namespace {
 
 int dtype_size(int dt) { return dt == PN_F32 ? 4 : (dt == PN_BF16 ? 2 : 1); }
 
-// LDS of one GEMM launch with nw waves: the A fragments of every k tile (when
-// A is staged in LDS), the waves' partial tiles and the summed tile.
+// LDS of one GEMM launch with nw waves: the A fragments of every k tile and a
+// 256-byte zero block (when A is staged in LDS), the waves' partial tiles and
+// the summed tile.
 size_t lds_of(bool a_in_lds, int KT, int rows, int ntw, int fb, int nw) {
-    size_t a = a_in_lds ? (((size_t)KT * 4 * rows * fb + 255) & ~(size_t)255) : 0;
+    size_t a = a_in_lds ? (((size_t)KT * 4 * rows * fb + 255) & ~(size_t)255) + 256 : 0;  // + zero block
     return a + (size_t)nw * ntw * 1024 + (size_t)ntw * 1024;
 }
 
@@ -182,8 +183,9 @@ Plan make_plan(int kind, int nblk, int gz, int KT, int rows, int fb, int nw, Occ
         p.nblk = nblk;
         const bool norm = norm_kind(kind);
         p.a_lds = !norm && (size_t)KT * 4 * rows * fb <= kALdsMax;
-        // direct A fragments need the larger register budget (int8 needs twice the fragment registers)
-        if (!norm && !p.a_lds) p.nw = fb == 32 ? 4 : std::min(want, 8);
+        // direct A fragments need the larger register budget (f16 fragments take two or four
+        // times the registers)
+        if (!norm && !p.a_lds) p.nw = fb >= 32 ? 4 : std::min(want, 8);
         p.lds = lds_of(norm || p.a_lds, KT, rows, ntw_of(kind), fb, p.nw);
         while (p.lds > kMaxLds && p.nw > 4) {  // many A rows: fewer waves leave room for them
             p.nw /= 2;
@@ -276,8 +278,10 @@ Mat make_mat(int N, int K, int wt) {
     m.K = K;
     m.n_tiles = cdiv(N, 16);
     m.KT = cdiv(K, tile_k(wt));
-    m.bytes1 = (size_t)m.n_tiles * m.KT * tile_bytes(wt);
-    m.sbytes1 = wt == PN_I8 ? (size_t)m.n_tiles * 16 * 4 : blockq(wt) ? (size_t)m.n_tiles * m.KT * 64 : 0;
+    m.bytes1 = (size_t)m.n_tiles * m.KT * 1024;
+    // int8: a row scale per row; block formats: a 2-byte scale per block and row
+    m.sbytes1 = wt == PN_I8 ? (size_t)m.n_tiles * 16 * 4
+                : blockq(wt) ? (size_t)m.n_tiles * m.KT * 16 * 2 * tile_blocks(wt) : 0;
     return m;
 }
 
@@ -507,12 +511,12 @@ void copy_bytes(void *dst, const void *src, size_t n, hipStream_t s) {
 void pack(const void *src, int N, int K, int wt, const Mat &mt, int tile_row0, uint8_t *dst_base,
           uint8_t *sdst_base, hipStream_t s, int neox_d = 0) {
     const int nt = cdiv(N, 16);
-    uint8_t *dst = dst_base + (size_t)tile_row0 * mt.KT * tile_bytes(wt);
+    uint8_t *dst = dst_base + (size_t)tile_row0 * mt.KT * 1024;
     long long lanes = (long long)nt * mt.KT * 64;
     int blocks = cdiv(lanes, 256);
     const uint8_t *sp = (const uint8_t *)src;
     if (blockq(wt)) {
-        uint8_t *sdst = sdst_base + (size_t)tile_row0 * mt.KT * 64;
+        uint8_t *sdst = sdst_base + (size_t)tile_row0 * mt.KT * 16 * 2 * tile_blocks(wt);
         if (wt == PN_Q8_0)
             hipLaunchKernelGGL(k_pack_q8, dim3(blocks), dim3(256), 0, s, sp, N, K, mt.KT, nt, dst, sdst, neox_d);
         else

@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(256) k_pack(const uint8_t *src, int N, int K, 
 
 // Q8_0 rows (per 32-weight block: fp16 scale, 32 int8 codes; K a multiple of
 // 32) into 1 KiB tiles of biased codes (u = q + 128) whose 16 bytes per lane
-// follow q8_pos, and 64-byte scale tiles holding each row's two block scales.
+// follow blk_pos, and 64-byte scale tiles holding each row's two block scales.
 // Blocks past K read as code 0 with scale 0.
 __global__ void __launch_bounds__(256) k_pack_q8(const uint8_t *src, int N, int K, int KT, int n_tiles,
                                                   uint8_t *dst, uint8_t *sdst, int neox_d) {
@@ -347,10 +347,11 @@ __global__ void __launch_bounds__(256) k_pack_q8(const uint8_t *src, int N, int 
 
 // Q4_0 rows (per 32-weight block: fp16 scale, 16 bytes whose byte i holds code
 // i in its low nibble and code i + 16 in its high one; K a multiple of 32) into
-// 512-byte tiles, 8 bytes per lane: the lane's 16 elements in q8_pos order, as
-// two words of 8 codes, pair j of a word at bits 4j and 16 + 4j (the layout
-// the GEMM widens with one mask per pair); scale tiles as for Q8_0.  Blocks
-// past K read as code 8 (weight 0) with scale 0.
+// 1 KiB tiles of 16 rows x 128 k, 16 bytes per lane: word j holds the 8 codes
+// of the lane's elements 8j..8j+7 (blk_pos order: block j of the tile), pair p
+// of a word at bits 4p and 16 + 4p (the layout the GEMM widens with one mask
+// per pair); and 128-byte scale tiles holding each row's four block scales.
+// Blocks past K read as code 8 (weight 0) with scale 0.
 __global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int K, int KT, int n_tiles,
                                                   uint8_t *dst, uint8_t *sdst, int neox_d) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -362,11 +363,11 @@ __global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int 
     const int row = nt * 16 + (lane & 15), g = lane >> 4;
     const int nblk = K / 32;
     const uint8_t *srow = src + (long long)(row < N ? neox_src(row, neox_d) : 0) * nblk * 18;
-    uint32_t w[2] = {0u, 0u};
+    u32x4 w = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int k = kt * 64 + 32 * (e >> 3) + 8 * g + (e & 7);
-        const int blk = k >> 5, kb = k & 31;
+    for (int e = 0; e < 32; ++e) {
+        const int blk = 4 * kt + (e >> 3);
+        const int kb = 8 * g + (e & 7);  // k within the block
         uint32_t code = 8u;
         if (row < N && blk < nblk) {
             const uint8_t byte = srow[blk * 18 + 2 + (kb & 15)];
@@ -374,16 +375,16 @@ __global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int 
         }
         w[e >> 3] |= code << (4 * ((e & 7) >> 1) + 16 * (e & 1));
     }
-    reinterpret_cast<u32x2 *>(dst)[i] = u32x2{w[0], w[1]};
+    reinterpret_cast<u32x4 *>(dst)[i] = w;
     if (g == 0) {
-        uint32_t sw = 0;
+        uint32_t sw[2] = {0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int blk = 2 * kt + j;
+        for (int j = 0; j < 4; ++j) {
+            const int blk = 4 * kt + j;
             const uint32_t d = (row < N && blk < nblk) ? (uint32_t)srow[blk * 18] | ((uint32_t)srow[blk * 18 + 1] << 8) : 0u;
-            sw |= d << (16 * j);
+            sw[j >> 1] |= d << (16 * (j & 1));
         }
-        reinterpret_cast<uint32_t *>(sdst)[tileid * 16 + (lane & 15)] = sw;
+        reinterpret_cast<u32x2 *>(sdst)[tileid * 16 + (lane & 15)] = u32x2{sw[0], sw[1]};
     }
 }
 
