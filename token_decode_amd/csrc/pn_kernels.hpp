@@ -264,17 +264,21 @@ __device__ __forceinline__ void mfma_tile(f32x4 &acc, const u32x4 &wv, const u32
         constexpr int NS = frag_vecs(WT);  // f16 MFMA steps per tile (one per block for block formats)
         u32x4 b[NS];
         if constexpr (WT == WT_Q4) {
-            // word j holds the 8 codes of step j; pair p of a word sits at bits 4p
-            // and 16 + 4p, so one mask gives both halves: code c -> f16 (1024 + c),
-            // minus 1032 leaves c - 8 exactly
+            // word j holds the 8 codes of step j: codes 0..3 in the low nibbles of
+            // its bytes, 4..7 in the high ones.  Two masks give a byte per code, a
+            // byte permute pairs them into f16 (1024 + c), minus 1032 leaves c - 8
+            // exactly
             const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = wv[j] & 0x0F0F0F0Fu, hi = (wv[j] >> 4) & 0x0F0F0F0Fu;
+                const uint32_t p[4] = {__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u),
+                                       __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u),
+                                       __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u),
+                                       __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t h = ((wv[j] >> (4 * q)) & 0x000F000Fu) | 0x64006400u;
-                    b[j][q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) - off);
-                }
+                for (int q = 0; q < 4; ++q) b[j][q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p[q]) - off);
+            }
         } else {
             const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll

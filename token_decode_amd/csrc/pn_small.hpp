@@ -348,9 +348,10 @@ __global__ void __launch_bounds__(256) k_pack_q8(const uint8_t *src, int N, int 
 // Q4_0 rows (per 32-weight block: fp16 scale, 16 bytes whose byte i holds code
 // i in its low nibble and code i + 16 in its high one; K a multiple of 32) into
 // 1 KiB tiles of 16 rows x 128 k, 16 bytes per lane: word j holds the 8 codes
-// of the lane's elements 8j..8j+7 (blk_pos order: block j of the tile), pair p
-// of a word at bits 4p and 16 + 4p (the layout the GEMM widens with one mask
-// per pair); and 128-byte scale tiles holding each row's four block scales.
+// of the lane's elements 8j..8j+7 (blk_pos order: block j of the tile), codes
+// 0..3 in the low nibbles of its bytes and 4..7 in the high ones (the layout
+// the GEMM widens with two masks and byte permutes); and 128-byte scale tiles
+// holding each row's four block scales.
 // Blocks past K read as code 8 (weight 0) with scale 0.
 __global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int K, int KT, int n_tiles,
                                                   uint8_t *dst, uint8_t *sdst, int neox_d) {
@@ -373,7 +374,8 @@ __global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int 
             const uint8_t byte = srow[blk * 18 + 2 + (kb & 15)];
             code = kb < 16 ? (byte & 15u) : (uint32_t)(byte >> 4);
         }
-        w[e >> 3] |= code << (4 * ((e & 7) >> 1) + 16 * (e & 1));
+        const int ee = e & 7;  // codes 0..3 of a word in its bytes' low nibbles, 4..7 in the high ones
+        w[e >> 3] |= code << (ee < 4 ? 8 * ee : 8 * (ee - 4) + 4);
     }
     reinterpret_cast<u32x4 *>(dst)[i] = w;
     if (g == 0) {
