@@ -60,6 +60,8 @@ def lib():
         L.orc_rope_neox.restype = None
         L.orc_half_to_double.argtypes = [ctypes.c_uint16]
         L.orc_half_to_double.restype = dbl
+        L.orc_q4_kv_round.argtypes = [vp, i32, vp]
+        L.orc_q4_kv_round.restype = None
         L.orc_matvec.argtypes = [vp, i32, vp, i32, i32, vp, vp]
         L.orc_matvec.restype = None
         L.orc_attend.argtypes = [vp, vp, vp, i32, i32, vp]
@@ -122,6 +124,14 @@ def rope(u, pos, theta):
 
 def half_to_double(bits):
     return lib().orc_half_to_double(int(bits))
+
+
+def q4_kv_round(u):
+    """A head vector as a Q4 KV cache stores it (blocks of 32 dims)."""
+    u = _f64(u).copy()
+    out = np.empty_like(u)
+    lib().orc_q4_kv_round(_ptr(u), u.size, _ptr(out))
+    return out
 
 
 def matvec(W, dt, s, rows, cols, x):

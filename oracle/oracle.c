@@ -27,6 +27,9 @@
  *     "Sampling", temperature 0);
  *   - quantised weights dequantised inside the mat-vec, norms kept in F32
  *     (Engine Architecture, section "Weight Loading Modes");
+ *   - a Q4 KV cache (Serve Layer Architecture, section "Environment
+ *     Variables": the admission math counts a Q4-quantised KV cache): k and v
+ *     kept as 32-dim Q4_0-style blocks (orc_q4_kv_round gives the reading);
  *   - the variants that share the Llama forward through config flags:
  *     attention biases (Qwen2) and, from Phi-3, the NeoX half-split RoPE
  *     (Engine Architecture, section "Architecture Detection").
@@ -327,7 +330,63 @@ typedef struct {
     void **k, **v; /* per layer [Hk][max_ctx][d] in kv dtype */
 } orc_state;
 
+/* bytes per cached element: a Q4_0 cache is kept here as its exact dequantised fp32 values */
 static size_t kv_elem(const orc_config *c) { return c->kv_dtype == ORC_BF16 ? 2 : 4; }
+static int kv_store_dt(const orc_config *c) { return c->kv_dtype == ORC_Q4_0 ? ORC_F32 : c->kv_dtype; }
+
+/* fp16 bits of a finite float, round to nearest even (magnitudes past 65504 give inf) */
+static uint16_t half_rne(float f) {
+    uint16_t sign = (uint16_t)(signbit(f) ? 0x8000 : 0);
+    double a = fabs((double)f);
+    if (a == 0.0) return sign;
+    int e;
+    double m = frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+    int E = e - 1 + 15;
+    if (E >= 1) {
+        double r = nearbyint(ldexp(m, 11));
+        if (r == 2048.0) { r = 1024.0; E += 1; }
+        if (E >= 31) return (uint16_t)(sign | 0x7C00);
+        return (uint16_t)(sign | (E << 10) | ((int)r - 1024));
+    }
+    return (uint16_t)(sign | (uint16_t)nearbyint(ldexp(a, 24)));
+}
+
+/* A Q4 KV cache stores each head vector in blocks of 32 dims, Q4_0-style: an
+ * fp16 scale d and 4-bit codes, value d * (code - 8).  The pages only name the
+ * Q4 KV cache; the rule taken here: m = the element of largest magnitude (the
+ * first on ties), d = fp16(m / -8), code = clamp(rint(x / d) + 8, 0, 15) (all
+ * codes 8 when d is 0).  Every decision is taken on fp32 values with fp32
+ * division, as the GPU takes it.  out[i] receives the stored value. */
+void orc_q4_kv_round(const double *u, int d, double *out) {
+    for (int b = 0; b + 32 <= d; b += 32) {
+        float f[32];
+        int im = 0;
+        for (int i = 0; i < 32; ++i) {
+            f[i] = (float)u[b + i];
+            if (fabsf(f[i]) > fabsf(f[im])) im = i;
+        }
+        float dv = f[im] / -8.0f;
+        float dd = (float)orc_half_to_double(half_rne(dv));
+        for (int i = 0; i < 32; ++i) {
+            int code = 8;
+            if (dd != 0.0f) {
+                volatile float q = f[i] / dd; /* fp32 quotient, correctly rounded */
+                float r = nearbyintf(q) + 8.0f;
+                code = r < 0.0f ? 0 : (r > 15.0f ? 15 : (int)r);
+            }
+            out[b + i] = (double)dd * (double)(code - 8);
+        }
+    }
+}
+
+/* a head vector [d] as the cache stores it */
+static void kv_round_head(const orc_config *c, const double *u, int d, double *out) {
+    if (c->kv_dtype == ORC_Q4_0) {
+        orc_q4_kv_round(u, d, out);
+        return;
+    }
+    for (int i = 0; i < d; ++i) out[i] = round_to(u[i], c->kv_dtype);
+}
 
 orc_state *orc_state_new(const orc_config *c, int max_ctx) {
     orc_state *s = (orc_state *)calloc(1, sizeof(orc_state));
@@ -358,15 +417,27 @@ void orc_state_free(orc_state *s) {
 void orc_state_set_pos(orc_state *s, int pos) { s->pos = pos; }
 int orc_state_pos(const orc_state *s) { return s->pos; }
 
-/* copy stored K/V of positions pos0..pos0+n-1, given as [n][Hk][d] in kv dtype */
+/* copy stored K/V of positions pos0..pos0+n-1, given as [n][Hk][d] in kv dtype
+ * (a Q4 cache takes fp32 vectors and stores them as an append would) */
 int orc_state_set_kv(orc_state *s, int layer, int pos0, int n, const void *k, const void *v) {
     const orc_config *c = &s->cfg;
     if (layer < 0 || layer >= c->n_layer || pos0 < 0 || pos0 + n > s->max_ctx) return -2;
     size_t es = kv_elem(c), d = (size_t)c->head_dim;
+    double u[128], r[128];
     for (int t = 0; t < n; ++t)
         for (int j = 0; j < c->n_kv_head; ++j) {
             size_t src = ((size_t)t * c->n_kv_head + j) * d * es;
             size_t dst = ((size_t)j * s->max_ctx + (size_t)(pos0 + t)) * d * es;
+            if (c->kv_dtype == ORC_Q4_0) {
+                for (int w = 0; w < 2; ++w) {
+                    const float *in = (const float *)((const char *)(w ? v : k) + src);
+                    float *o = (float *)((char *)(w ? s->v[layer] : s->k[layer]) + dst);
+                    for (size_t i = 0; i < d; ++i) u[i] = (double)in[i];
+                    orc_q4_kv_round(u, (int)d, r);
+                    for (size_t i = 0; i < d; ++i) o[i] = (float)r[i];
+                }
+                continue;
+            }
             memcpy((char *)s->k[layer] + dst, (const char *)k + src, d * es);
             memcpy((char *)s->v[layer] + dst, (const char *)v + src, d * es);
         }
@@ -517,20 +588,24 @@ int orc_step(const orc_config *c, const void *const *tab, orc_state *st, int tok
     for (int l = 0; l < c->n_layer; ++l) {
         int lb = T_LAYER0 + l * orc_layer_stride(c);
         qkv(c, tab, lb, x, p, &s);
-        for (int j = 0; j < Hk; ++j)
+        for (int j = 0; j < Hk; ++j) {
+            double rk[128], rv[128];
+            kv_round_head(c, s.k + (size_t)j * d, d, rk);
+            kv_round_head(c, s.v + (size_t)j * d, d, rv);
             for (int i = 0; i < d; ++i) {
                 size_t at = ((size_t)j * st->max_ctx + (size_t)p) * d + (size_t)i;
-                store_kv(st->k[l], c->kv_dtype, at, s.k[(size_t)j * d + i]);
-                store_kv(st->v[l], c->kv_dtype, at, s.v[(size_t)j * d + i]);
+                store_kv(st->k[l], kv_store_dt(c), at, rk[i]);
+                store_kv(st->v[l], kv_store_dt(c), at, rv[i]);
             }
+        }
         /* the window's cached keys and values, widened to double, [Hk][n][d] */
         for (int j = 0; j < Hk; ++j)
             for (int t = 0; t < n; ++t)
                 for (int i = 0; i < d; ++i) {
                     size_t src = ((size_t)j * st->max_ctx + (size_t)(t0 + t)) * d + (size_t)i;
                     size_t dst = ((size_t)j * n + (size_t)t) * d + (size_t)i;
-                    K[dst] = rd(st->k[l], c->kv_dtype, src);
-                    V[dst] = rd(st->v[l], c->kv_dtype, src);
+                    K[dst] = rd(st->k[l], kv_store_dt(c), src);
+                    V[dst] = rd(st->v[l], kv_store_dt(c), src);
                 }
         /* keys are the window only, so position p sits at index n-1 and W is not re-applied */
         orc_attention(s.q, K, V, H, Hk, d, n, n - 1, 0, s.o);
@@ -571,11 +646,10 @@ int orc_full_recompute(const orc_config *c, const void *const *tab, const int32_
         for (int t = 0; t < n; ++t) {
             qkv(c, tab, lb, X + (size_t)t * E, t, &s);
             memcpy(Q + (size_t)t * H * d, s.q, sizeof(double) * (size_t)H * d);
-            for (int j = 0; j < Hk; ++j)
-                for (int i = 0; i < d; ++i) {
-                    K[((size_t)j * n + t) * d + i] = round_to(s.k[(size_t)j * d + i], c->kv_dtype);
-                    V[((size_t)j * n + t) * d + i] = round_to(s.v[(size_t)j * d + i], c->kv_dtype);
-                }
+            for (int j = 0; j < Hk; ++j) {
+                kv_round_head(c, s.k + (size_t)j * d, d, K + ((size_t)j * n + t) * d);
+                kv_round_head(c, s.v + (size_t)j * d, d, V + ((size_t)j * n + t) * d);
+            }
         }
         for (int t = 0; t < n; ++t) {
             orc_attention(Q + (size_t)t * H * d, K, V, H, Hk, d, n, t, c->sliding_window, s.o);

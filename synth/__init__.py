@@ -231,12 +231,12 @@ class Workload:
         return 0
 
     def kv_prefill(self, slot: int, l: int, p0: int, n: int, threads=None):
-        """Cached K and V of positions p0..p0+n-1: arrays [n][n_kv_head][head_dim] in kv dtype."""
+        """Cached K and V of positions p0..p0+n-1: arrays [n][n_kv_head][head_dim] in kv dtype
+        (fp32 for a Q4 cache, whose set_kv quantises as an append does)."""
         per = self.n_kv_head * self.head_dim
-        k = normal(self.seed, self.tid_kv(slot, l, 0), n * per, 0.0, 1.0, self.kv_dtype,
-                   start=p0 * per, threads=threads)
-        v = normal(self.seed, self.tid_kv(slot, l, 1), n * per, 0.0, 1.0, self.kv_dtype,
-                   start=p0 * per, threads=threads)
+        dt = F32 if self.kv_dtype == Q4_0 else self.kv_dtype
+        k = normal(self.seed, self.tid_kv(slot, l, 0), n * per, 0.0, 1.0, dt, start=p0 * per, threads=threads)
+        v = normal(self.seed, self.tid_kv(slot, l, 1), n * per, 0.0, 1.0, dt, start=p0 * per, threads=threads)
         shp = (n, self.n_kv_head, self.head_dim)
         return k.reshape(shp), v.reshape(shp)
 

@@ -323,6 +323,43 @@ def test_q4_0_rows_are_a_faithful_quantisation():
     np.testing.assert_allclose(oracle.matvec(q, synth.Q4_0, None, 24, 160, x), deq @ x, rtol=1e-13)
 
 
+# ----------------------------------------------------------------------------- Q4 KV cache
+
+def test_q4_kv_round_worked_examples():
+    z = [0.0] * 24
+    # m = -4: d = 0.5; 0.25 / 0.5 = 0.5 rounds to even (0), 0.75 / 0.5 = 1.5 to 2, -0.5 to -0
+    got = oracle.q4_kv_round(np.array([-4, 1, 2, 3.5, 0, 0.25, 0.75, -0.25] + z))
+    np.testing.assert_array_equal(got[:8], [-4, 1, 2, 3.5, 0, 0, 1, 0])
+    # m = +4: d = -0.5; -4 would be code 16 and clips to 15: -0.5 * 7 = -3.5
+    got = oracle.q4_kv_round(np.array([4, -4, 1] + [0.0] * 29))
+    np.testing.assert_array_equal(got[:3], [4, -3.5, 1])
+    # equal magnitudes: the first is m (3 -> d = -0.375, so -3 clips to -2.625)
+    got = oracle.q4_kv_round(np.array([3, -3] + [0.0] * 30))
+    np.testing.assert_array_equal(got[:2], [3, -2.625])
+    # d is an fp16: m = 1 + 2^-12 gives d = -0.125 exactly, so m itself comes back as 1
+    got = oracle.q4_kv_round(np.array([1 + 2.0 ** -12] + [0.0] * 31))
+    assert got[0] == 1.0
+    # an all-zero block stays zero; blocks are independent
+    got = oracle.q4_kv_round(np.array([0.0] * 32 + [8.0] + [0.0] * 31))
+    np.testing.assert_array_equal(got[:32], 0.0)
+    assert got[32] == 8.0
+
+
+def test_q4_kv_round_values_are_scaled_codes():
+    for trial in range(20):
+        u = rng.standard_normal(128) * (10.0 ** rng.uniform(-3, 2))
+        got = oracle.q4_kv_round(u)
+        for b in range(4):
+            blk, g = u[32 * b: 32 * b + 32], got[32 * b: 32 * b + 32]
+            m = blk[np.argmax(np.abs(blk.astype(np.float32)))]
+            d = float(np.float16(np.float32(m) / np.float32(-8.0)))
+            codes = g / d + 8
+            np.testing.assert_array_equal(codes, np.rint(codes))
+            assert codes.min() >= 0 and codes.max() <= 15
+            ok = codes != 15  # away from the clipped end every value is within half a step
+            assert np.all(np.abs(g - blk)[ok] <= abs(d) / 2 * (1 + 1e-6))
+
+
 # ----------------------------------------------------------------------------- whole model
 
 def _torch_forward(wl, W, tokens):
@@ -356,6 +393,13 @@ def _torch_forward(wl, W, tokens):
     def kvr(t):
         if wl.kv_dtype == synth.BF16:
             return t.to(torch.bfloat16).to(torch.float64)
+        if wl.kv_dtype == synth.Q4_0:  # per head vector, blocks of 32: fp16 scale, 4-bit codes
+            f = t.to(torch.float32).numpy().reshape(-1, 32)
+            m = f[np.arange(len(f)), np.argmax(np.abs(f), axis=1)]
+            dd = (m / np.float32(-8.0)).astype(np.float16).astype(np.float32)[:, None]
+            with np.errstate(divide="ignore", invalid="ignore"):
+                c = np.where(dd != 0, np.clip(np.rint(f / np.where(dd != 0, dd, 1)) + 8, 0, 15), 8)
+            return torch.tensor((dd.astype(np.float64) * (c - 8)).reshape(t.shape))
         return t.to(torch.float32).to(torch.float64)
 
     n = len(tokens)
@@ -433,6 +477,9 @@ SMALL = [
                             qkv_bias=True, seed=19),
     synth.tiny_fp32().with_(name="small-q4_0", w_dtype=synth.Q4_0, kv_dtype=synth.BF16, act_dtype=synth.BF16,
                             seed=20, n_ff=672),
+    synth.tiny_fp32().with_(name="small-q4kv-window", kv_dtype=synth.Q4_0, sliding_window=5, seed=22),
+    synth.tiny_fp32().with_(name="small-q4kv-bf16-moe", w_dtype=synth.BF16, kv_dtype=synth.Q4_0,
+                            act_dtype=synth.BF16, n_expert=4, n_expert_used=2, n_ff=96, seed=23),
     synth.tiny_fp32().with_(name="small-q4_0-moe-window", w_dtype=synth.Q4_0, kv_dtype=synth.BF16,
                             act_dtype=synth.BF16, n_expert=4, n_expert_used=2, n_ff=96, sliding_window=5, seed=21),
 ]
