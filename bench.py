@@ -48,7 +48,7 @@ def algorithmic_bytes(wl, positions):
                             wl.n_vocab, wl.n_layer)
     # Q8_0 / Q4_0: 34 / 18 bytes per 32 weights (codes + fp16 scale)
     sw = {0: 4, 1: 2, 2: 1, 3: 34 / 32, 4: 18 / 32}[wl.w_dtype]
-    skv = 4 if wl.kv_dtype == 0 else 2
+    skv = {0: 4, 1: 2, 4: 9 / 16}[wl.kv_dtype]  # Q4 cache: codes and a 2-byte scale per 32 dims
     se = 4 if wl.w_dtype == 0 else 2
     per_layer_w = (H * d * E + 2 * Hk * d * E + E * H * d + 3 * E * F) * sw
     rows_layer = H * d + 2 * Hk * d + E + 2 * F + E

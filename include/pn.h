@@ -70,7 +70,14 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3, PN_Q4_0 = 4 } pn
  *            and n_embd, n_ff multiples of 32.  The token embedding
  *            and the MoE router are fp32 when w_dtype is PN_F32 and bf16
  *            otherwise; norm gains are fp32.
- *  kv_dtype  cached K and V: PN_F32 or PN_BF16 (k is cached after RoPE).
+ *  kv_dtype  cached K and V: PN_F32, PN_BF16, or PN_Q4_0 (k is cached after
+ *            RoPE).  A Q4 cache (the pages' serve layer counts a Q4-quantised
+ *            KV cache: "Serve Layer Architecture", section "Environment
+ *            Variables") keeps each head vector of k and v as 32-dim blocks of
+ *            an fp16 scale d and 4-bit codes, value d*(code-8), set when the
+ *            token is appended: m = the element of largest magnitude (the first
+ *            on ties), d = fp16(m/-8), code = clamp(rint(x/d)+8, 0, 15), in
+ *            fp32; 9*head_dim/16 bytes per cached vector.  Not with rope_neox.
  *  act_dtype type that every mat-vec input (normed x, attention output, FFN
  *            hidden, final normed x) is rounded to: PN_F32 or PN_BF16.  The
  *            residual stream, q, softmax and all accumulators stay fp32.
@@ -171,7 +178,7 @@ int pn_state_reset(pn_state *s, void *stream);
 
 /* Write cached K and V of positions pos0..pos0+n-1 of one layer from device
  * arrays k_dev, v_dev laid out [n][n_kv_head][head_dim] in kv_dtype (k after
- * RoPE).  Used to resume or to prefill a cache.  Does not change pos.  A
+ * RoPE; fp32 for a PN_Q4_0 cache, quantised as an append quantises).  Used to resume or to prefill a cache.  Does not change pos.  A
  * pooled state takes pages for those positions (PN_ERANGE if the pool runs
  * out or if pos0 lies below pages that went back to the pool). */
 int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const void *k_dev,

@@ -34,7 +34,7 @@ GEMM_UNITS = [  # (weight type, activation type, entry point)
 ]
 
 
-ATTN_UNITS = [(d, kv) for d in (32, 64, 128) for kv in (0, 1)]
+ATTN_UNITS = [(d, kv) for d in (32, 64, 128) for kv in (0, 1, 2)]  # kv: fp32, bf16, Q4
 
 
 def _units():

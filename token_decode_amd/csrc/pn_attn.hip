@@ -1,6 +1,6 @@
 // pn_attn.hip - split-K flash-decode attention and its split merge for one
 // (head_dim, KV type) pair.  Compiled once per pair with -DPN_D=<32|64|128>
-// -DPN_KV=<0|1> -DPN_NAME=<entry>.
+// -DPN_KV=<0|1|2> (fp32, bf16, Q4) -DPN_NAME=<entry>.
 #include "pn_launch.hpp"
 
 namespace pn {
@@ -8,7 +8,7 @@ namespace {
 
 template <int G>
 void go(const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
-    // an fp32 cache goes to the vector units; a bf16 one where a.kind says
+    // fp32 and Q4 caches go to the vector units; a bf16 one where a.kind says
     if (PN_KV == 1 && a.kind == 1) hipLaunchKernelGGL((k_attn_mfma<PN_D, G>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_attn<PN_D, PN_KV, G>), grid, dim3(256), 0, s, a);
     if (merge) hipLaunchKernelGGL((k_attn_merge<PN_D, G>), dim3(a.Hq, grid.z), dim3(256), 0, s, a);

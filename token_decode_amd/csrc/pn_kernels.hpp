@@ -227,6 +227,8 @@ struct GemmArgs {
     int ld_out;
     float *q_out;           // QKV: q [slot][Hq*D]
     const float *bias;      // QKV: biases [N] in packed row order, or null
+    float *kv_new;          // QKV with a Q4 cache: the new k, v rows [slot][2][Hk][D] fp32 (then
+                            // quantised into the pages by k_kv_q4); null: append to the cache here
     int Hq, Hk, D;
     int kv_es;              // QKV: bytes per cached element (2 = bf16, 4 = fp32)
     const float2 *rope;     // QKV: (cos, sin) per slot and rotation index [slot][D/2]
@@ -1016,7 +1018,11 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                         const long long hb = ((long long)epc.page * g.Hk + j) * kPage * g.D;
                         const int t = pos % kPage;
                         const bool tiled = g.kv_es == 2;
-                        if (isk) {
+                        if (g.kv_new) {
+                            float *kn = g.kv_new + (((long long)b * 2 + (isk ? 0 : 1)) * g.Hk + j) * g.D + dd;
+                            kn[0] = y0;
+                            kn[1] = y1;
+                        } else if (isk) {
                             // dd, dd + 1 are adjacent in both K layouts
                             const long long off = hb + kv_k_off(tiled, t, dd, g.D);
                             if (tiled) {
@@ -1176,13 +1182,62 @@ __device__ __forceinline__ float wave_max_q(float v) {
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Q4 KV cache: per page and KV head, the 64 keys' codes [key][D/2 bytes] (dims
+// 2i, 2i+1 in the low and high nibbles of byte i), then their block scales
+// [key][D/32] fp16; a block is 32 dims, value = d * (code - 8).
+__host__ __device__ constexpr int q4kv_key_bytes(int D) { return D / 2 + D / 16; }
+
+// Quantise one head vector src[D] into a key's codes and scales (one wave; lane l
+// < D/2 takes dims 2l, 2l+1, 16 lanes a block).  Per block: m = the element of
+// largest magnitude (the lowest index on ties), d = fp16(m / -8), code =
+// clamp(rint(x / d) + 8, 0, 15), all codes 8 when d is 0; fp32 throughout.
+__device__ __forceinline__ void q4kv_store(const float *src, uint8_t *codes, uint16_t *scales, int D, int lane) {
+    const bool on = lane < D / 2;
+    const float v0 = on ? src[2 * lane] : 0.f, v1 = on ? src[2 * lane + 1] : 0.f;
+    float m = fabsf(v1) > fabsf(v0) ? v1 : v0;
+    int mi = fabsf(v1) > fabsf(v0) ? 2 * lane + 1 : 2 * lane;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        const float om = __shfl_xor(m, o, 64);
+        const int oi = __shfl_xor(mi, o, 64);
+        if (fabsf(om) > fabsf(m) || (fabsf(om) == fabsf(m) && oi < mi)) {
+            m = om;
+            mi = oi;
+        }
+    }
+    const _Float16 dh = (_Float16)(m / -8.0f);
+    const float dd = (float)dh;
+    uint32_t c0 = 8u, c1 = 8u;
+    if (dd != 0.f) {
+        c0 = (uint32_t)fminf(fmaxf(rintf(v0 / dd) + 8.f, 0.f), 15.f);
+        c1 = (uint32_t)fminf(fmaxf(rintf(v1 / dd) + 8.f, 0.f), 15.f);
+    }
+    if (on) {
+        codes[lane] = (uint8_t)(c0 | (c1 << 4));
+        if ((lane & 15) == 0) scales[lane / 16] = __builtin_bit_cast(uint16_t, dh);
+    }
+}
+
+// the new rows of a Q4 KV cache and where they go
+struct KvQ4Args {
+    const float *src;  // [row][2][Hk][D]: k then v
+    char *kvk[kMaxSlots];
+    char *kvv[kMaxSlots];
+    const int *pt[kMaxSlots];
+    int pos[kMaxSlots];
+    int Hk, D;
+};
+
 template <int D, int KV>
 struct AttnShape {
-    static constexpr int ES = KV == 1 ? 2 : 4;       // bytes per cached element
+    // KV: 0 fp32, 1 bf16, 2 Q4 (values widened to fp32 as they are loaded)
+    static constexpr int ES = KV == 1 ? 2 : 4;       // bytes per cached (or widened) element
     static constexpr int VE = D >= 64 ? D / 64 : 1;  // value elements per lane
     static constexpr int VL = D / VE;                // lanes holding values
-    static constexpr int NKL = D * ES / 64;          // 16-byte K loads per lane
-    static constexpr int KVEC = 16 / ES;             // K elements per load
+    // 16-byte K registers per lane (Q4: the codes of the lane's quarter of the
+    // dims, then the block scale)
+    static constexpr int NKL = KV == 2 ? 2 : D * ES / 64;
+    static constexpr int KVEC = 16 / ES;             // K elements per load (fp32 / bf16)
     typedef typename std::conditional<VE * ES == 2, uint16_t,
             typename std::conditional<VE * ES == 4, uint32_t, unsigned long long>::type>::type vword;
     // double-buffer a chunk's rows when both copies fit the register budget
@@ -1204,7 +1259,36 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int p
     const int tq = min(max(k0 + kq, lo), kl);
     const int dl = (lane < S::VL ? lane : 0) * S::VE;
     uint32_t col[S::VE][16];
-    if constexpr (KV == 1) {
+    if constexpr (KV == 2) {
+        // Q4 block of the head (q4kv_*): codes [key][D/2] then scales [key][D/32]
+        const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.kvk[b]) + ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(D);
+        const uint8_t *krow = kb + (tq % kPage) * (D / 2) + dq * (D / 8);  // the lane's quarter: D/8 bytes
+        if constexpr (D == 128) {
+            kr[0] = *reinterpret_cast<const u32x4 *>(krow);
+        } else if constexpr (D == 64) {
+            const u32x2 t = *reinterpret_cast<const u32x2 *>(krow);
+            kr[0] = u32x4{t[0], t[1], 0u, 0u};
+        } else {
+            kr[0] = u32x4{*reinterpret_cast<const uint32_t *>(krow), 0u, 0u, 0u};
+        }
+        const uint16_t *ks = reinterpret_cast<const uint16_t *>(kb + kPage * (D / 2)) + (tq % kPage) * (D / 32) +
+                             dq * (D / 4) / 32;
+        kr[1] = u32x4{(uint32_t)*ks, 0u, 0u, 0u};
+        // values: each of the lane's dims for the 16 keys, widened to fp32 here
+        const uint8_t *vb = reinterpret_cast<const uint8_t *>(a.kvv[b]) + ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(D);
+        const uint16_t *vs = reinterpret_cast<const uint16_t *>(vb + kPage * (D / 2));
+        const int key0 = k0 % kPage;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const uint32_t byte = vb[(key0 + u) * (D / 2) + dl / 2];
+            const float sc = half_lo(vs[(key0 + u) * (D / 32) + dl / 32]);
+#pragma unroll
+            for (int e = 0; e < S::VE; ++e) {
+                const int code = (int)(((dl + e) & 1) ? byte >> 4 : byte & 15u);
+                col[e][u] = __float_as_uint(sc * (float)(code - 8));
+            }
+        }
+    } else if constexpr (KV == 1) {
         // tiled (kv_k_off / kv_v_off): piece dq + 4c of key row tq % 16 is 16 bytes of
         // the group's 1 KiB step c; the 4 keys 4q..4q+3 of a dim are 8 contiguous bytes
         const uint8_t *gk = reinterpret_cast<const uint8_t *>(a.kvk[b]) + (hb + (long long)(k0 % kPage) * D) * 2;
@@ -1265,23 +1349,41 @@ __device__ __forceinline__ void attn_chunk(const float (*qs)[D], float (*pw)[16]
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
+    if constexpr (KV == 2) {
+        // Q4: the lane's D/4 dims from 4-bit codes (dim 2i in the low nibble of
+        // byte i, 2i + 1 in the high one), times the block scale
+        constexpr int QD = D / 4;
+        const float dsc = half_lo(kr[1][0]);
+        float t[G];
 #pragma unroll
-    for (int c = 0; c < S::NKL; ++c) {
-        float kf[S::KVEC];
-        if constexpr (KV == 1) {
+        for (int g = 0; g < G; ++g) t[g] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kf[2 * e] = __uint_as_float(kr[c][e] << 16);
-                kf[2 * e + 1] = __uint_as_float(kr[c][e] & 0xFFFF0000u);
-            }
-        } else {
+        for (int i = 0; i < QD; ++i) {
+            const float kf = (float)((int)((kr[0][i / 8] >> (4 * (i % 8))) & 15u) - 8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) kf[e] = __uint_as_float(kr[c][e]);
+            for (int g = 0; g < G; ++g) t[g] = fmaf(qs[g][dq * QD + i], kf, t[g]);
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) sc[g] = t[g] * dsc;
+    } else {
 #pragma unroll
-            for (int e = 0; e < S::KVEC; ++e) sc[g] = fmaf(qs[g][(4 * c + dq) * S::KVEC + e], kf[e], sc[g]);
+        for (int c = 0; c < S::NKL; ++c) {
+            float kf[S::KVEC];
+            if constexpr (KV == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kf[2 * e] = __uint_as_float(kr[c][e] << 16);
+                    kf[2 * e + 1] = __uint_as_float(kr[c][e] & 0xFFFF0000u);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kf[e] = __uint_as_float(kr[c][e]);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < S::KVEC; ++e) sc[g] = fmaf(qs[g][(4 * c + dq) * S::KVEC + e], kf[e], sc[g]);
+        }
     }
     const int key = k0 + kq;
     const bool valid = key >= lo && key < ke;

@@ -53,10 +53,18 @@ PN_ATTN_DECL(launch_attn_64_0)
 PN_ATTN_DECL(launch_attn_64_1)
 PN_ATTN_DECL(launch_attn_128_0)
 PN_ATTN_DECL(launch_attn_128_1)
+PN_ATTN_DECL(launch_attn_32_2)
+PN_ATTN_DECL(launch_attn_64_2)
+PN_ATTN_DECL(launch_attn_128_2)
 #undef PN_ATTN_DECL
 
+// kvt: the pn_dtype of the cache (PN_F32 0, PN_BF16 1, PN_Q4_0 4 -> instantiation 2)
 inline void launch_attn(int D, int kvt, int G, const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
-    if (kvt == 1) {
+    if (kvt == 4) {
+        if (D == 32) launch_attn_32_2(G, a, grid, merge, s);
+        else if (D == 64) launch_attn_64_2(G, a, grid, merge, s);
+        else launch_attn_128_2(G, a, grid, merge, s);
+    } else if (kvt == 1) {
         if (D == 32) launch_attn_32_1(G, a, grid, merge, s);
         else if (D == 64) launch_attn_64_1(G, a, grid, merge, s);
         else launch_attn_128_1(G, a, grid, merge, s);

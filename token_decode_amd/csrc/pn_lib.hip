@@ -85,6 +85,7 @@ struct pn_model {
     size_t x, q, o, h, y, route_ids, route_w, am_val, am_idx;
     size_t samp_keys = 0, samp_hist = 0;  // pn_sample scratch
     size_t attn_part = 0, attn_part_row = 0;  // pn_prefill: per-row attention split scratch
+    size_t kv_new = 0;                        // Q4 KV cache: the step's new k, v rows [row][2][Hk][D] fp32
     size_t o_bytes = 0, h_bytes = 0, am_count = 0;
     int a_es = 2;                      // bytes per A-ready element
     long long h_plane = 0;
@@ -142,6 +143,11 @@ struct pn_state {
 namespace {
 
 int dtype_size(int dt) { return dt == PN_F32 ? 4 : (dt == PN_BF16 ? 2 : 1); }
+
+// bytes of one cached key (or value) of one KV head
+size_t kv_key_bytes(const pn_model *m) {
+    return m->kvt == PN_Q4_0 ? (size_t)q4kv_key_bytes(m->D) : (size_t)m->D * dtype_size(m->kvt);
+}
 
 // LDS of one GEMM launch with nw waves: the A fragments of every k tile and a
 // 256-byte zero block (when A is staged in LDS), the waves' partial tiles and
@@ -256,12 +262,15 @@ int check_config_n(const pn_config *c) {
         return fail(PN_EUNSUPPORTED, "block-quantised weights need bf16 activations");
     if (bq && (c->n_embd % 32 != 0 || c->n_ff % 32 != 0))
         return fail(PN_EINVAL, "block-quantised rows are whole 32-weight blocks: n_embd and n_ff must be multiples of 32");
-    if (c->kv_dtype != PN_F32 && c->kv_dtype != PN_BF16) return fail(PN_EINVAL, "kv_dtype must be F32 or BF16");
+    if (c->kv_dtype != PN_F32 && c->kv_dtype != PN_BF16 && c->kv_dtype != PN_Q4_0)
+        return fail(PN_EINVAL, "kv_dtype must be F32, BF16 or Q4_0");
     if (c->act_dtype != PN_F32 && c->act_dtype != PN_BF16) return fail(PN_EINVAL, "act_dtype must be F32 or BF16");
     if (c->w_dtype == PN_I8 && c->act_dtype != PN_BF16)
         return fail(PN_EUNSUPPORTED, "int8 weights need bf16 activations");
     if (c->max_batch < 1 || c->max_batch > kMaxSlots) return fail(PN_EINVAL, "max_batch must be in [1, 16]");
     if ((c->rope_neox & ~1) != 0 || (c->qkv_bias & ~1) != 0) return fail(PN_EINVAL, "rope_neox and qkv_bias must be 0 or 1");
+    if (c->rope_neox && c->kv_dtype == PN_Q4_0)
+        return fail(PN_EUNSUPPORTED, "a Q4 KV cache quantises k in natural dim order: no NeoX RoPE");
     const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
@@ -363,10 +372,11 @@ size_t layout_model(pn_model *m) {
     m->samp_keys = bp.take((size_t)MB * m->V * 4);
     m->attn_part_row = (size_t)m->Hk * kMaxSplits * m->G * (m->D + 4) * 4;
     m->attn_part = bp.take((size_t)MB * m->attn_part_row);
+    m->kv_new = c.kv_dtype == PN_Q4_0 ? bp.take((size_t)MB * 2 * m->Hk * m->D * 4) : 0;
     m->samp_hist = bp.take((size_t)MB * kSampleBlocks * kSampleBins * 4);
     // pn_profile_replay: a QKV replay appends its k, v rows here (page 0 of a
     // one-entry page table) instead of into a state's cache
-    m->replay_kv = bp.take((size_t)2 * MB * m->Hk * kPage * m->D * dtype_size(m->kvt));
+    m->replay_kv = bp.take((size_t)2 * MB * m->Hk * kPage * kv_key_bytes(m));
     m->replay_pt = bp.take(256);
     return bp.off;
 }
@@ -380,8 +390,7 @@ constexpr size_t kMaxLayerBytes = (size_t)1 << 31;
 size_t layout_state(pn_state *s) {
     const pn_model *m = s->m;
     s->n_pages = cdiv(s->max_ctx, kPage);
-    const int es = dtype_size(m->kvt);
-    s->layer_bytes = s->pool ? s->pool->layer_bytes : (size_t)s->n_pages * m->Hk * kPage * m->D * es;
+    s->layer_bytes = s->pool ? s->pool->layer_bytes : (size_t)s->n_pages * m->Hk * kPage * kv_key_bytes(m);
     int keys = s->max_ctx;
     if (m->cfg.sliding_window > 0) keys = std::min(keys, m->cfg.sliding_window);
     // splits start on page boundaries, so a window may touch one more chunk
@@ -574,7 +583,7 @@ void record_gemm(pn_model *m, int cls, int kind, const GemmArgs &g, const Plan &
     r.g = g;
     r.p = p;
     if (kind == GK_QKV) {  // keep a replay away from the states' caches
-        const size_t slot = (size_t)m->Hk * kPage * m->D * dtype_size(m->kvt);
+        const size_t slot = (size_t)m->Hk * kPage * kv_key_bytes(m);
         for (int b = 0; b < g.B; ++b) {
             r.g.kvk[b] = m->base + m->replay_kv + (size_t)(2 * b) * slot;
             r.g.kvv[b] = m->base + m->replay_kv + (size_t)(2 * b + 1) * slot;
@@ -748,6 +757,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.gain = (const float *)(mb + L.attn_norm);
             g.q_out = (float *)(mb + m->q);
             g.bias = L.bqkv ? (const float *)(mb + L.bqkv) : nullptr;
+            g.kv_new = m->kv_new ? (float *)(mb + m->kv_new) : nullptr;
             for (int b = 0; b < n; ++b) {
                 g.kvk[b] = kv_layer(st[b], l, false);
                 g.kvv[b] = kv_layer(st[b], l, true);
@@ -756,6 +766,20 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             launch_gemm(GK_QKV, wt, at, g, p_qkv, s);
             if (int rc = launched("QKV projection", &p_qkv)) return rc;
             record_gemm(m, PN_K_QKV, GK_QKV, g, p_qkv);
+            if (m->kv_new) {  // Q4 cache: quantise the new rows into the pages
+                KvQ4Args q{};
+                q.src = g.kv_new;
+                q.Hk = m->Hk;
+                q.D = m->D;
+                for (int b = 0; b < n; ++b) {
+                    q.kvk[b] = g.kvk[b];
+                    q.kvv[b] = g.kvv[b];
+                    q.pt[b] = g.pt[b];
+                    q.pos[b] = g.pos[b];
+                }
+                hipLaunchKernelGGL(k_kv_q4_append, dim3(n, m->Hk, 2), dim3(64), 0, s, q);
+                if (int rc = launched("Q4 KV append")) return rc;
+            }
         }
         // ---- attention (+ split combine)
         {
@@ -1174,7 +1198,7 @@ int pn_state_new(pn_model *m, int32_t max_ctx, void *dev_buf, size_t bytes, void
 }
 
 // Bytes of one page (all positions and KV heads of one layer's K or V pool).
-size_t pool_page_bytes(const pn_model *m) { return (size_t)m->Hk * kPage * m->D * dtype_size(m->kvt); }
+size_t pool_page_bytes(const pn_model *m) { return (size_t)m->Hk * kPage * kv_key_bytes(m); }
 
 size_t pn_pool_bytes(const pn_model *m, int32_t n_pages) {
     if (!m || n_pages < 1) return 0;
@@ -1281,7 +1305,10 @@ int pn_state_set_kv(pn_state *s, int32_t layer, int32_t pos0, int32_t n, const v
     long long total = (long long)n * m->Hk * m->D;
     dim3 grid(cdiv(total, 256));
     const int nx = m->cfg.rope_neox ? m->D : 0;  // k is cached in rotation-pair order
-    if (m->kvt == PN_BF16)
+    if (m->kvt == PN_Q4_0)
+        hipLaunchKernelGGL(k_kv_q4_set, dim3(n, m->Hk, 2), dim3(64), 0, S(stream), kp, vp, (const int *)(s->base + s->pt),
+                           (const float *)k, (const float *)v, pos0, m->Hk, m->D);
+    else if (m->kvt == PN_BF16)
         hipLaunchKernelGGL(k_set_kv<2>, grid, dim3(256), 0, S(stream), kp, vp, (const int *)(s->base + s->pt),
                            (const char *)k, (const char *)v, pos0, n, m->Hk, m->D, nx);
     else

@@ -390,6 +390,32 @@ __global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int 
     }
 }
 
+// Q4 KV cache: quantise the step's new k and v rows (kv_new of the QKV
+// epilogue) into the pages, one wave per (row, KV head, k or v).
+__global__ void __launch_bounds__(64) k_kv_q4_append(KvQ4Args a) {
+    const int b = blockIdx.x, j = blockIdx.y, w = blockIdx.z, lane = threadIdx.x;
+    const int pos = a.pos[b];
+    const int pg = a.pt[b][pos / kPage];
+    uint8_t *base = reinterpret_cast<uint8_t *>(w ? a.kvv[b] : a.kvk[b]) +
+                    ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(a.D);
+    const int key = pos % kPage;
+    q4kv_store(a.src + (((long long)b * 2 + w) * a.Hk + j) * a.D, base + key * (a.D / 2),
+               reinterpret_cast<uint16_t *>(base + kPage * (a.D / 2)) + key * (a.D / 32), a.D, lane);
+}
+
+// Q4 KV cache: positions pos0..pos0+n-1 of one layer from fp32 rows k, v
+// [n][Hk][D], quantised as an append quantises them.
+__global__ void __launch_bounds__(64) k_kv_q4_set(char *kpool, char *vpool, const int *pt, const float *k,
+                                                   const float *v, int pos0, int Hk, int D) {
+    const int t = blockIdx.x, j = blockIdx.y, w = blockIdx.z, lane = threadIdx.x;
+    const int pos = pos0 + t;
+    uint8_t *base = reinterpret_cast<uint8_t *>(w ? vpool : kpool) +
+                    ((long long)pt[pos / kPage] * Hk + j) * kPage * q4kv_key_bytes(D);
+    const int key = pos % kPage;
+    q4kv_store((w ? v : k) + ((long long)t * Hk + j) * D, base + key * (D / 2),
+               reinterpret_cast<uint16_t *>(base + kPage * (D / 2)) + key * (D / 32), D, lane);
+}
+
 __global__ void __launch_bounds__(256) k_copy_rows_f32(float *dst, const float *src, int n, int neox_d) {
     const int r = blockIdx.x * 256 + threadIdx.x;
     if (r < n) dst[r] = src[neox_src(r, neox_d)];
