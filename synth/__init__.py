@@ -376,6 +376,12 @@ def llama3_8b_q4_0() -> Workload:
     return llama3_8b_bf16().with_(name="llama3-8b-q4_0", w_dtype=Q4_0, act_dtype=BF16, seed=7)
 
 
+def llama3_8b_kv_long(kv_dtype: int) -> Workload:
+    """Llama-3-8B shape, Q4_0 weights, batch 1 from position 32768, with a bf16 or Q4 KV cache."""
+    return llama3_8b_q4_0().with_(name="llama3-8b-q4_0-kv%s-32k" % ("q4" if kv_dtype == Q4_0 else "bf16"),
+                                  kv_dtype=kv_dtype, prefill=32768)
+
+
 WORKLOADS = {
     "tiny-fp32": tiny_fp32,
     "llama3-8b-bf16": llama3_8b_bf16,
@@ -384,4 +390,6 @@ WORKLOADS = {
     "mixtral-8x7b-16slots": mixtral_8x7b_slots,
     "llama3-8b-q8_0": llama3_8b_q8_0,
     "llama3-8b-q4_0": llama3_8b_q4_0,
+    "llama3-8b-q4_0-kvbf16-32k": lambda: llama3_8b_kv_long(BF16),
+    "llama3-8b-q4_0-kvq4-32k": lambda: llama3_8b_kv_long(Q4_0),
 }

@@ -1182,16 +1182,20 @@ __device__ __forceinline__ float wave_max_q(float v) {
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Q4 KV cache: per page and KV head, the 64 keys' codes [key][D/2 bytes] (dims
-// 2i, 2i+1 in the low and high nibbles of byte i), then their block scales
-// [key][D/32] fp16; a block is 32 dims, value = d * (code - 8).
+// Q4 KV cache: per page and KV head, the 64 keys' codes (dims 2i, 2i+1 in the
+// low and high nibbles of byte i) and their block scales (fp16; a block is 32
+// dims, value = d * (code - 8)).  K by key rows: codes [key][D/2], then scales
+// [key][D/32].  V by columns, so a lane reads one byte column of 16 keys at
+// once: codes [D/2][key], then scales [D/32][key].  Each key owns its bytes.
 __host__ __device__ constexpr int q4kv_key_bytes(int D) { return D / 2 + D / 16; }
 
 // Quantise one head vector src[D] into a key's codes and scales (one wave; lane l
-// < D/2 takes dims 2l, 2l+1, 16 lanes a block).  Per block: m = the element of
-// largest magnitude (the lowest index on ties), d = fp16(m / -8), code =
-// clamp(rint(x / d) + 8, 0, 15), all codes 8 when d is 0; fp32 throughout.
-__device__ __forceinline__ void q4kv_store(const float *src, uint8_t *codes, uint16_t *scales, int D, int lane) {
+// < D/2 takes dims 2l, 2l+1, 16 lanes a block); byte l goes to codes[l * cs],
+// block scale b to scales[b * ss].  Per block: m = the element of largest
+// magnitude (the lowest index on ties), d = fp16(m / -8), code = clamp(rint(x /
+// d) + 8, 0, 15), all codes 8 when d is 0; fp32 throughout.
+__device__ __forceinline__ void q4kv_store(const float *src, uint8_t *codes, int cs, uint16_t *scales, int ss, int D,
+                                           int lane) {
     const bool on = lane < D / 2;
     const float v0 = on ? src[2 * lane] : 0.f, v1 = on ? src[2 * lane + 1] : 0.f;
     float m = fabsf(v1) > fabsf(v0) ? v1 : v0;
@@ -1213,8 +1217,8 @@ __device__ __forceinline__ void q4kv_store(const float *src, uint8_t *codes, uin
         c1 = (uint32_t)fminf(fmaxf(rintf(v1 / dd) + 8.f, 0.f), 15.f);
     }
     if (on) {
-        codes[lane] = (uint8_t)(c0 | (c1 << 4));
-        if ((lane & 15) == 0) scales[lane / 16] = __builtin_bit_cast(uint16_t, dh);
+        codes[lane * cs] = (uint8_t)(c0 | (c1 << 4));
+        if ((lane & 15) == 0) scales[(lane / 16) * ss] = __builtin_bit_cast(uint16_t, dh);
     }
 }
 
@@ -1274,14 +1278,18 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int p
         const uint16_t *ks = reinterpret_cast<const uint16_t *>(kb + kPage * (D / 2)) + (tq % kPage) * (D / 32) +
                              dq * (D / 4) / 32;
         kr[1] = u32x4{(uint32_t)*ks, 0u, 0u, 0u};
-        // values: each of the lane's dims for the 16 keys, widened to fp32 here
+        // values: the lane's byte column for the 16 keys (one 16-byte load) and
+        // their scales of its block (32 bytes), widened to fp32 here
         const uint8_t *vb = reinterpret_cast<const uint8_t *>(a.kvv[b]) + ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(D);
-        const uint16_t *vs = reinterpret_cast<const uint16_t *>(vb + kPage * (D / 2));
         const int key0 = k0 % kPage;
+        const u32x4 cw = *reinterpret_cast<const u32x4 *>(vb + (dl / 2) * kPage + key0);
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb + kPage * (D / 2) + ((dl / 32) * kPage + key0) * 2);
+        const u32x4 s0 = vs[0], s1 = vs[1];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const uint32_t byte = vb[(key0 + u) * (D / 2) + dl / 2];
-            const float sc = half_lo(vs[(key0 + u) * (D / 32) + dl / 32]);
+            const uint32_t byte = (cw[u / 4] >> (8 * (u % 4))) & 0xFFu;
+            const uint32_t sw = u < 8 ? s0[(u % 8) / 2] : s1[(u % 8) / 2];
+            const float sc = (u & 1) ? half_hi(sw) : half_lo(sw);
 #pragma unroll
             for (int e = 0; e < S::VE; ++e) {
                 const int code = (int)(((dl + e) & 1) ? byte >> 4 : byte & 15u);

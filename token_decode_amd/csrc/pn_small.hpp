@@ -390,6 +390,14 @@ __global__ void __launch_bounds__(256) k_pack_q4(const uint8_t *src, int N, int 
     }
 }
 
+// Store one k (w = 0: key rows) or v (w = 1: columns) head vector of a Q4 cache
+// at key `key` of its page block `base` (layout as q4kv_key_bytes says).
+__device__ __forceinline__ void q4kv_put(const float *src, uint8_t *base, int key, int w, int D, int lane) {
+    uint16_t *sc = reinterpret_cast<uint16_t *>(base + kPage * (D / 2));
+    if (w == 0) q4kv_store(src, base + key * (D / 2), 1, sc + key * (D / 32), 1, D, lane);
+    else q4kv_store(src, base + key, kPage, sc + key, kPage, D, lane);
+}
+
 // Q4 KV cache: quantise the step's new k and v rows (kv_new of the QKV
 // epilogue) into the pages, one wave per (row, KV head, k or v).
 __global__ void __launch_bounds__(64) k_kv_q4_append(KvQ4Args a) {
@@ -398,9 +406,7 @@ __global__ void __launch_bounds__(64) k_kv_q4_append(KvQ4Args a) {
     const int pg = a.pt[b][pos / kPage];
     uint8_t *base = reinterpret_cast<uint8_t *>(w ? a.kvv[b] : a.kvk[b]) +
                     ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(a.D);
-    const int key = pos % kPage;
-    q4kv_store(a.src + (((long long)b * 2 + w) * a.Hk + j) * a.D, base + key * (a.D / 2),
-               reinterpret_cast<uint16_t *>(base + kPage * (a.D / 2)) + key * (a.D / 32), a.D, lane);
+    q4kv_put(a.src + (((long long)b * 2 + w) * a.Hk + j) * a.D, base, pos % kPage, w, a.D, lane);
 }
 
 // Q4 KV cache: positions pos0..pos0+n-1 of one layer from fp32 rows k, v
@@ -411,9 +417,7 @@ __global__ void __launch_bounds__(64) k_kv_q4_set(char *kpool, char *vpool, cons
     const int pos = pos0 + t;
     uint8_t *base = reinterpret_cast<uint8_t *>(w ? vpool : kpool) +
                     ((long long)pt[pos / kPage] * Hk + j) * kPage * q4kv_key_bytes(D);
-    const int key = pos % kPage;
-    q4kv_store((w ? v : k) + ((long long)t * Hk + j) * D, base + key * (D / 2),
-               reinterpret_cast<uint16_t *>(base + kPage * (D / 2)) + key * (D / 32), D, lane);
+    q4kv_put((w ? v : k) + ((long long)t * Hk + j) * D, base, pos % kPage, w, D, lane);
 }
 
 __global__ void __launch_bounds__(256) k_copy_rows_f32(float *dst, const float *src, int n, int neox_d) {
