@@ -47,6 +47,14 @@ def good_cfg(**kw):
     return dv.make_config(**base)
 
 
+def test_flag_fields_are_zero_or_one():
+    cfg = good_cfg()
+    cfg.rope_neox = 2
+    assert C.lib().pn_config_check(ctypes.byref(cfg)) == C.PN_EINVAL
+    cfg.rope_neox, cfg.qkv_bias = 0, -1
+    assert C.lib().pn_config_check(ctypes.byref(cfg)) == C.PN_EINVAL
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(n_head=6, n_kv_head=4), C.PN_EINVAL),
     (dict(head_dim=48), C.PN_EUNSUPPORTED),
@@ -60,6 +68,12 @@ def good_cfg(**kw):
     (dict(sliding_window=-1), C.PN_EINVAL),
     (dict(rope_theta=0.0), C.PN_EINVAL),
     (dict(n_embd=252), C.PN_EUNSUPPORTED),
+    (dict(w_dtype=C.PN_Q8_0, act_dtype=C.PN_F32), C.PN_EUNSUPPORTED),
+    (dict(w_dtype=C.PN_Q4_0, act_dtype=C.PN_BF16, n_ff=680), C.PN_EINVAL),  # rows of whole 32-blocks
+    (dict(w_dtype=C.PN_Q4_0, act_dtype=C.PN_BF16, n_embd=264), C.PN_EINVAL),
+    (dict(w_dtype=5), C.PN_EINVAL),
+    (dict(kv_dtype=C.PN_Q8_0), C.PN_EINVAL),
+    (dict(kv_dtype=C.PN_Q4_0, rope_neox=True), C.PN_EUNSUPPORTED),
 ])
 def test_bad_configs_rejected(kw, code):
     cfg = good_cfg(**kw)
@@ -73,10 +87,39 @@ def test_good_configs_and_sizes():
     for kw in (dict(), dict(w_dtype=C.PN_BF16, kv_dtype=C.PN_BF16, act_dtype=C.PN_F32, max_batch=5),
                dict(w_dtype=C.PN_I8, kv_dtype=C.PN_BF16, act_dtype=C.PN_BF16, max_batch=16),
                dict(n_expert=8, n_expert_used=2, w_dtype=C.PN_BF16, act_dtype=C.PN_BF16),
-               dict(n_kv_head=0)):
+               dict(n_kv_head=0),
+               dict(w_dtype=C.PN_Q8_0, act_dtype=C.PN_BF16, n_ff=672),
+               dict(w_dtype=C.PN_Q4_0, act_dtype=C.PN_BF16, n_ff=672, kv_dtype=C.PN_Q4_0),
+               dict(rope_neox=True, qkv_bias=True)):
         cfg = good_cfg(**kw)
         assert L.pn_config_check(ctypes.byref(cfg)) == 0, L.pn_last_error()
         assert L.pn_model_bytes(ctypes.byref(cfg)) > 0
+
+
+def test_block_formats_and_q4_cache_sizes():
+    """Llama-3-8B shape: Q8_0 / Q4_0 packed weights take 34 / 18 bytes per 32 weights (codes
+    plus fp16 scales); a Q4 KV cache takes 9/16 byte per element, 9/32 of a bf16 one."""
+    L = C.lib()
+    shape = dict(n_layer=32, n_embd=4096, n_head=32, n_kv_head=8, head_dim=128, n_ff=14336, n_vocab=128256,
+                 act_dtype=C.PN_BF16)
+    params = 32 * (4096 * 6144 + 4096 * 4096 + 3 * 4096 * 14336) + 128256 * 4096
+    embd = 128256 * 4096 * 2
+    for wt, per32 in ((C.PN_Q8_0, 34), (C.PN_Q4_0, 18)):
+        n = L.pn_model_bytes(ctypes.byref(good_cfg(w_dtype=wt, kv_dtype=C.PN_BF16, **shape)))
+        assert params * per32 / 32 + embd <= n < (params * per32 / 32 + embd) * 1.01
+    sizes = {}
+    for kvt in (C.PN_BF16, C.PN_Q4_0):
+        cfg = good_cfg(w_dtype=C.PN_Q4_0, kv_dtype=kvt, **shape)
+        need = L.pn_model_bytes(ctypes.byref(cfg))
+        h = ctypes.c_void_p()
+        assert L.pn_model_init(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), need, ctypes.byref(h)) == 0
+        try:
+            sizes[kvt] = (L.pn_state_bytes(h, 32768), L.pn_pool_bytes(h, 1))
+        finally:
+            L.pn_model_free(h)
+    kv_bf16 = 2 * 32 * 32768 * 8 * 128 * 2
+    assert sizes[C.PN_BF16][1] * 9 == sizes[C.PN_Q4_0][1] * 32  # a page: 9/32 of the bf16 bytes
+    assert sizes[C.PN_BF16][0] - sizes[C.PN_Q4_0][0] == kv_bf16 * 23 // 32
 
 
 def test_model_bytes_cover_packed_weights():

@@ -8,7 +8,7 @@ cached value by a quantisation step; the logits are held to the 2e-2 bound of
 the low-precision workloads.  Cases cover the three head sizes (one lane's
 quarter of a key is a whole block, half a block or a quarter), a window,
 batched slots, MoE, chunked prefill, the fp32 rows of set_kv, and a shared page
-pool (whose pages are 9/16 of a bf16 page)."""
+pool (whose pages are 9/32 of a bf16 page)."""
 import numpy as np
 import pytest
 
