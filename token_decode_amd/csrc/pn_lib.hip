@@ -83,7 +83,8 @@ struct pn_model {
     Mat out;
     // scratch
     size_t x, q, o, h, y, route_ids, route_w, am_val, am_idx;
-    size_t samp_keys = 0, samp_hist = 0;  // pn_sample scratch
+    size_t samp_keys = 0, samp_hist = 0, samp_cnt = 0, samp_cand = 0;  // pn_sample scratch
+    bool samp_dirty = false;  // a pn_sample call stopped before k_sample_pick cleared its histogram
     size_t attn_part = 0, attn_part_row = 0;  // pn_prefill: per-row attention split scratch
     size_t kv_new = 0;                        // Q4 KV cache: the step's new k, v rows [row][2][Hk][D] fp32
     size_t o_bytes = 0, h_bytes = 0, am_count = 0;
@@ -373,7 +374,9 @@ size_t layout_model(pn_model *m) {
     m->attn_part_row = (size_t)m->Hk * kMaxSplits * m->G * (m->D + 4) * 4;
     m->attn_part = bp.take((size_t)MB * m->attn_part_row);
     m->kv_new = c.kv_dtype == PN_Q4_0 ? bp.take((size_t)MB * 2 * m->Hk * m->D * 4) : 0;
-    m->samp_hist = bp.take((size_t)MB * kSampleBlocks * kSampleBins * 4);
+    m->samp_hist = bp.take((size_t)MB * kSampleBins * 4);
+    m->samp_cnt = bp.take((size_t)MB * 2 * 4);
+    m->samp_cand = bp.take((size_t)MB * kSampleCap * 8);
     // pn_profile_replay: a QKV replay appends its k, v rows here (page 0 of a
     // one-entry page table) instead of into a state's cache
     m->replay_kv = bp.take((size_t)2 * MB * m->Hk * kPage * kv_key_bytes(m));
@@ -1032,6 +1035,8 @@ int pn_model_load_globals(pn_model *m, const void *tok_embd, const float *out_no
     fill32(mb + m->o, m->o_bytes / 4, 0u, s);
     fill32(mb + m->h, m->h_bytes / 4, 0u, s);
     fill32(mb + m->replay_pt, 64, 0u, s);
+    fill32(mb + m->samp_hist, (size_t)m->cfg.max_batch * kSampleBins, 0u, s);
+    fill32(mb + m->samp_cnt, (size_t)m->cfg.max_batch * 2, 0u, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PN_EHIP, "weight packing failed: %s", hipGetErrorString(e));
     return PN_OK;
@@ -1442,6 +1447,8 @@ int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling
     a.ids = ids_dev;
     a.keys = (unsigned *)(m->base + m->samp_keys);
     a.hist = (unsigned *)(m->base + m->samp_hist);
+    a.cnt = (unsigned *)(m->base + m->samp_cnt);
+    a.cand = (unsigned long long *)(m->base + m->samp_cand);
     for (int b = 0; b < n; ++b) {
         const pn_sampling_params &p = params[b];
         if (std::isnan(p.temperature)) return fail(PN_EINVAL, "row %d: temperature is NaN", b);
@@ -1459,8 +1466,14 @@ int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling
         a.top_k[b] = p.top_k;
     }
     hipStream_t st = S(stream);
-    hipLaunchKernelGGL(k_sample_keys, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
-    if (int rc = launched("sampling keys")) return rc;
+    // the histogram and the gather counters start each call at zero: the
+    // previous call's k_sample_pick cleared them, unless that call stopped early
+    if (m->samp_dirty) {
+        fill32(m->base + m->samp_hist, (size_t)m->cfg.max_batch * kSampleBins, 0u, st);
+        fill32(m->base + m->samp_cnt, (size_t)m->cfg.max_batch * 2, 0u, st);
+        if (int rc = launched("sampling scratch clear")) return rc;
+        m->samp_dirty = false;
+    }
     // the candidate buffer is dynamic LDS; with the kernel's static LDS the
     // total passes 64 KiB, which needs the attribute (the two within 160 KiB)
     static bool lds_set = false;
@@ -1471,8 +1484,14 @@ int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling
         if (e != hipSuccess) return fail(PN_EHIP, "sampling LDS attribute: %s", hipGetErrorString(e));
         lds_set = true;
     }
+    m->samp_dirty = true;
+    hipLaunchKernelGGL(k_sample_keys, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
+    if (int rc = launched("sampling keys")) return rc;
+    hipLaunchKernelGGL(k_sample_gather, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
+    if (int rc = launched("sampling gather")) return rc;
     hipLaunchKernelGGL(k_sample_pick, dim3(n), dim3(kSamplePick), lds, st, a);
     if (int rc = launched("sampling pick")) return rc;
+    m->samp_dirty = false;
     return PN_OK;
 }
 
