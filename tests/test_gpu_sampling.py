@@ -176,3 +176,58 @@ def test_sampled_decode_loop():
     log("  sampled trajectory %s..., near ties %d" % (hist[:12], near))
     assert near <= 1
     assert st.pos == n
+
+
+def test_vocab_past_one_pass():
+    """A vocabulary of 262147 tokens: each key / gather work-group loops over
+    more than one pass of its share, and the last share is ragged."""
+    from token_decode_amd import device as dv
+    Vb = 262147
+    wl = synth.Workload("sampler-wide", n_layer=1, n_embd=64, n_head=2, n_kv_head=1, head_dim=32, n_ff=64,
+                        n_vocab=Vb, rope_theta=10000.0, w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                        act_dtype=synth.BF16, seed=72)
+    dm = dv.DeviceModel(device_config(wl, max_batch=3), synth.make_weights(wl))
+    rng = np.random.default_rng(9)
+    rows = [(rng.standard_normal(Vb) * s).astype(np.float32) for s in (1.0, 2.0, 4.0)]
+    rows[2][Vb - 1] = 40.0  # the last token (in the ragged tail) dominates this row
+    params = [dict(temperature=0.8, top_k=40, top_p=0.95, repeat_penalty=1.1),
+              dict(temperature=1.0, top_k=4096, top_p=1.0), dict(temperature=0.0)]
+    recent = rng.integers(0, Vb, size=(3, 64)).astype(np.int32)
+    us = [0.3, 0.9, 0.5]
+    got = run(dm, rows, params, us, recent)
+    for b in range(3):
+        check(rows[b], params[b], us[b], int(got[b]), recent[b])
+    assert got[2] == Vb - 1
+
+
+def test_graph_replays(model):
+    """pn_sample captured in a HIP graph and replayed with new logits and draws
+    in the captured buffers: every replay matches the reference sampler and the
+    eager call (the histogram scratch is cleared by a kernel, so replays start
+    from zero without a memset)."""
+    import torch
+    from token_decode_amd import device as dv
+    rng = np.random.default_rng(10)
+    params = [dict(temperature=0.9, top_k=50, top_p=0.9), dict(temperature=1.2, top_k=1000, top_p=0.97)]
+    n = len(params)
+    lg = torch.zeros(n, V, dtype=torch.float32, device="cuda")
+    u = torch.zeros(n, dtype=torch.float32, device="cuda")
+    ids = torch.zeros(n, dtype=torch.int32, device="cuda")
+    dv.sample(model, lg, params, u, ids)  # eager warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dv.sample(model, lg, params, u, ids)
+    for rep in range(4):
+        rows = [(rng.standard_normal(V) * (1.0 + rep)).astype(np.float32) for _ in range(n)]
+        us = [float(x) for x in rng.random(n)]
+        lg.copy_(torch.from_numpy(np.stack(rows)))
+        u.copy_(torch.tensor(us, dtype=torch.float32))
+        g.replay()
+        torch.cuda.synchronize()
+        got = ids.cpu().numpy().copy()
+        eager = run(model, rows, params, us)  # eager work between the replays
+        np.testing.assert_array_equal(got, eager)
+        for b in range(n):
+            check(rows[b], params[b], us[b], int(got[b]))
+    log("  4 graph replays of pn_sample: equal to the eager calls and to the reference sampler")
