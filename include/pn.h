@@ -90,7 +90,14 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3, PN_Q4_0 = 4 } pn
  *            RoPE; the NeoX RoPE of Phi-3, which rotates (i, i + d/2) instead
  *            of (2i, 2i+1) with the same angles.  0 (default) or 1.  A fused
  *            QKV or gate+up checkpoint needs no flag: pass pointers into it
- *            (wk = wq + H*d rows, w_up = w_gate + F rows). */
+ *            (wk = wq + H*d rows, w_up = w_gate + F rows).
+ *  prefill_chunk  rows per pn_prefill chunk on the wide path, 1..256, or 0
+ *            (chunks of max_batch through the decode kernels).  The wide path
+ *            takes each chunk through every projection as one matrix product
+ *            on the matrix cores, so a weight is read once per chunk; it needs
+ *            w_dtype PN_BF16, no experts and kv_dtype PN_F32 or PN_BF16
+ *            (PN_EUNSUPPORTED otherwise), and adds its row buffers to
+ *            pn_model_bytes. */
 typedef struct pn_config {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab;
     int32_t n_ctx;          /* default state capacity when pn_state_* is given max_ctx 0 */
@@ -102,6 +109,8 @@ typedef struct pn_config {
     int32_t w_dtype, kv_dtype, act_dtype; /* pn_dtype values */
     int32_t rope_neox; /* 1: RoPE rotates the half-split pairs (i, i + head_dim/2) */
     int32_t qkv_bias;  /* 1: the q, k, v projections add fp32 biases (b_q, b_k, b_v) */
+    int32_t prefill_chunk; /* 0: pn_prefill goes in chunks of max_batch; 1..256: in chunks
+                              of this many rows through the wide prefill path (below) */
 } pn_config;
 
 /* Device pointers of one layer's weights, logical row-major [out][in] (PN_Q8_0:
@@ -279,11 +288,13 @@ int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int3
  * "Generation Loop": prefill runs the forward for each prompt token), up to
  * fp32 summation order: row t of logits_dev [n][n_vocab] and argmax_dev [n]
  * (either may be NULL) are the logits and greedy id after token t, and the
- * cache holds every token's K/V.  The tokens go in chunks of max_batch, each
- * chunk one batched step whose rows are consecutive positions of the state
- * (the pages' chunked prefill: "Serve Layer Architecture", section "Batched
- * Decode", "L2 - chunked prefill"), so every weight is read once per chunk
- * instead of once per token.  Errors: PN_EINVAL (NULL pointer, n < 1, state
+ * cache holds every token's K/V.  The tokens go in chunks (the pages' chunked
+ * prefill: "Serve Layer Architecture", section "Batched Decode", "L2 - chunked
+ * prefill"), so every weight is read once per chunk instead of once per token:
+ * with prefill_chunk 0, chunks of max_batch, each one batched step whose rows
+ * are consecutive positions of the state; otherwise chunks of prefill_chunk
+ * rows on the wide path, whose fp32 sums run in another order (split K).  With
+ * both outputs NULL the wide path skips the LM head.  Errors: PN_EINVAL (NULL pointer, n < 1, state
  * of another model), PN_ERANGE (pos + n > max_ctx; a pooled state's pool ran
  * out). */
 int pn_prefill(pn_model *m, pn_state *s, const int32_t *tokens_dev, int32_t n, float *logits_dev,

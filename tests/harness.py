@@ -27,14 +27,14 @@ def log(msg):
     print(msg, flush=True)
 
 
-def device_config(wl, max_batch=1):
+def device_config(wl, max_batch=1, prefill_chunk=0):
     from token_decode_amd import device as dv
     return dv.make_config(wl.n_layer, wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim, wl.n_ff,
                           wl.n_vocab, n_expert=wl.n_expert, n_expert_used=wl.n_expert_used,
                           sliding_window=wl.sliding_window, max_batch=max_batch,
                           rope_theta=wl.rope_theta, rms_norm_eps=wl.rms_norm_eps,
                           w_dtype=wl.w_dtype, kv_dtype=wl.kv_dtype, act_dtype=wl.act_dtype,
-                          rope_neox=wl.rope_neox, qkv_bias=wl.qkv_bias)
+                          rope_neox=wl.rope_neox, qkv_bias=wl.qkv_bias, prefill_chunk=prefill_chunk)
 
 
 def compare_step(wl, g_logits, o_logits, g_id, o_id, what="", tol=None):
@@ -57,13 +57,13 @@ def compare_step(wl, g_logits, o_logits, g_id, o_id, what="", tol=None):
 class Pair:
     """A device model and the oracle over the same seeded weights."""
 
-    def __init__(self, wl, max_batch=1, weights=None):
+    def __init__(self, wl, max_batch=1, weights=None, prefill_chunk=0):
         from token_decode_amd import device as dv
         t = time.time()
         self.wl = wl
         self.W = weights if weights is not None else synth.make_weights(wl)
         self.om = oracle.Model(wl, self.W)
-        self.cfg = device_config(wl, max_batch)
+        self.cfg = device_config(wl, max_batch, prefill_chunk)
         self.dm = dv.DeviceModel(self.cfg, self.W)
         log("  [%s] weights ready in %.1fs" % (wl.name, time.time() - t))
 

@@ -74,6 +74,11 @@ def test_flag_fields_are_zero_or_one():
     (dict(w_dtype=5), C.PN_EINVAL),
     (dict(kv_dtype=C.PN_Q8_0), C.PN_EINVAL),
     (dict(kv_dtype=C.PN_Q4_0, rope_neox=True), C.PN_EUNSUPPORTED),
+    (dict(prefill_chunk=-1), C.PN_EINVAL),
+    (dict(prefill_chunk=257), C.PN_EINVAL),
+    (dict(prefill_chunk=64, w_dtype=C.PN_I8, act_dtype=C.PN_BF16), C.PN_EUNSUPPORTED),
+    (dict(prefill_chunk=64, n_expert=8, n_expert_used=2), C.PN_EUNSUPPORTED),
+    (dict(prefill_chunk=64, kv_dtype=C.PN_Q4_0), C.PN_EUNSUPPORTED),
 ])
 def test_bad_configs_rejected(kw, code):
     cfg = good_cfg(**kw)
@@ -90,7 +95,8 @@ def test_good_configs_and_sizes():
                dict(n_kv_head=0),
                dict(w_dtype=C.PN_Q8_0, act_dtype=C.PN_BF16, n_ff=672),
                dict(w_dtype=C.PN_Q4_0, act_dtype=C.PN_BF16, n_ff=672, kv_dtype=C.PN_Q4_0),
-               dict(rope_neox=True, qkv_bias=True)):
+               dict(rope_neox=True, qkv_bias=True),
+               dict(prefill_chunk=256, w_dtype=C.PN_BF16, act_dtype=C.PN_F32, kv_dtype=C.PN_F32)):
         cfg = good_cfg(**kw)
         assert L.pn_config_check(ctypes.byref(cfg)) == 0, L.pn_last_error()
         assert L.pn_model_bytes(ctypes.byref(cfg)) > 0
@@ -207,3 +213,13 @@ def test_package_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(C, "_lib", None)
     with pytest.raises(ImportError):
         C.lib()
+
+
+def test_wide_prefill_buffers_in_model_bytes():
+    """The wide path's row buffers are part of pn_model_bytes: larger chunks take more."""
+    L = C.lib()
+    sizes = []
+    for chunk in (0, 32, 128):
+        cfg = good_cfg(prefill_chunk=chunk, w_dtype=C.PN_BF16, act_dtype=C.PN_F32)
+        sizes.append(L.pn_model_bytes(ctypes.byref(cfg)))
+    assert 0 < sizes[0] < sizes[1] < sizes[2]

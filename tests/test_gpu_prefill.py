@@ -95,3 +95,79 @@ def test_prefill_range_error():
         dv.prefill(p.dm, ds, torch.zeros(6, dtype=torch.int32, device="cuda"))
     assert e.value.code == C.PN_ERANGE
     assert ds.pos == 15
+
+
+# ---- the wide path (prefill_chunk > 0): each chunk through every projection
+# as one matrix product, K split over work-groups, fp32 partial sums added in
+# split order
+
+def test_wide_fp32_activations_three_chunks():
+    """fp32 activations (three bf16 pieces per value), chunks of 64 rows:
+    64 + 64 + 22 prompt tokens from position 0, then decode on the cache."""
+    wl = ragged("wide-actf32", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.F32, seed=84)
+    p = Pair(wl, max_batch=1, prefill_chunk=64)
+    prompt = list(synth.uniform_int(wl.seed, 95, 150, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 0, prompt, 3)
+    log("  wide, fp32 activations, 150 tokens in chunks of 64: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_wide_window_bias_neox_on_existing_cache():
+    """bf16 activations, fp32 cache, q/k/v biases, NeoX RoPE and a 40-token
+    window narrower than the 48-row chunks, from a cache written up to 200."""
+    wl = ragged("wide-bf16-window", w_dtype=synth.BF16, kv_dtype=synth.F32, act_dtype=synth.BF16,
+                sliding_window=40, rope_neox=True, qkv_bias=True, seed=85)
+    p = Pair(wl, max_batch=2, prefill_chunk=48)
+    prompt = list(synth.uniform_int(wl.seed, 96, 100, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 200, prompt, 3)
+    log("  wide, window 40, bias + NeoX, 100 tokens from 200: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_wide_outputs_optional_and_pooled():
+    """A pooled, windowed state: the prompt in chunks of 32 with only the
+    argmax asked for, then with no output (the LM head is skipped), then
+    decode steps that read every appended K/V; the pooled twin of a private
+    state prefilled the decode-kernel way gives the same decode logits to
+    within the wide path's summation order."""
+    import numpy as np
+    import torch
+    from token_decode_amd import device as dv
+    wl = ragged("wide-pooled", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.BF16,
+                sliding_window=70, seed=86)
+    p = Pair(wl, max_batch=1, prefill_chunk=32)
+    pool = dv.DevicePool(p.dm, 6)
+    ds = dv.DeviceState(p.dm, 600, pool=pool)
+    os_ = p.om.new_state(600)
+    prompt = [int(t) for t in synth.uniform_int(wl.seed, 97, 140, 0, wl.n_vocab - 1)]
+    am = torch.empty(90, dtype=torch.int32, device="cuda")
+    dv.prefill(p.dm, ds, torch.tensor(prompt[:90], dtype=torch.int32, device="cuda"), None, am)
+    got = am.cpu().numpy()
+    for t in range(90):
+        ol, oa = os_.step(prompt[t])
+        top2 = np.sort(ol)[-2:]
+        assert got[t] == oa or top2[1] - top2[0] < 1e-2 * np.abs(ol).max(), (t, got[t], oa)
+    dv.prefill(p.dm, ds, torch.tensor(prompt[90:], dtype=torch.int32, device="cuda"))
+    for t in prompt[90:]:
+        ol, oa = os_.step(t)
+    assert ds.pos == 140 and pool.free_pages >= 0
+    tok = torch.tensor([oa], dtype=torch.int32, device="cuda")
+    lg = torch.empty(wl.n_vocab, dtype=torch.float32, device="cuda")
+    a1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    worst = 0.0
+    for i in range(4):
+        dv.forward_step(p.dm, ds, tok, lg, a1)
+        ol, oa = os_.step(int(tok.item()))
+        from harness import compare_step
+        rel, _ = compare_step(wl, lg.cpu().numpy(), ol, int(a1.item()), oa, "decode step %d:" % i)
+        worst = max(worst, rel)
+        tok.fill_(oa)
+    log("  wide, pooled window 70, argmax-only then no output: decode after worst rel L2 %.2e" % worst)
+
+
+def test_wide_llama3_shape():
+    """Llama-3-8B layer shape (2 layers, full 128256 vocabulary): 40 prompt
+    tokens in chunks of 32 (32 + 8 rows) after a 100-token cache."""
+    wl = synth.WORKLOADS["llama3-8b-bf16"]().with_(name="wide-llama3-2l", n_layer=2, seed=87)
+    p = Pair(wl, max_batch=1, prefill_chunk=32)
+    prompt = list(synth.uniform_int(wl.seed, 98, 40, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 100, prompt, 1)
+    log("  wide, Llama-3-8B shape, 40 tokens from 100: worst rel L2 %.2e, near %d" % (worst, near))

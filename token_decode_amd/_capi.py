@@ -25,7 +25,7 @@ class pn_config(ctypes.Structure):
                 ("n_expert", i32), ("n_expert_used", i32), ("sliding_window", i32),
                 ("max_batch", i32), ("rope_theta", ctypes.c_float), ("rms_norm_eps", ctypes.c_float),
                 ("w_dtype", i32), ("kv_dtype", i32), ("act_dtype", i32), ("rope_neox", i32),
-                ("qkv_bias", i32)]
+                ("qkv_bias", i32), ("prefill_chunk", i32)]
 
 
 class pn_layer_weights(ctypes.Structure):

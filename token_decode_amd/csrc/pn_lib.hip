@@ -21,6 +21,7 @@
 #include "pn_launch.hpp"
 #include "pn_small.hpp"
 #include "pn_sample.hpp"
+#include "pn_wide.hpp"
 
 using namespace pn;
 
@@ -87,6 +88,12 @@ struct pn_model {
     bool samp_dirty = false;  // a pn_sample call stopped before k_sample_pick cleared its histogram
     size_t attn_part = 0, attn_part_row = 0;  // pn_prefill: per-row attention split scratch
     size_t kv_new = 0;                        // Q4 KV cache: the step's new k, v rows [row][2][Hk][D] fp32
+    // wide prefill (prefill_chunk > 0): one chunk's rows.  x [C][E], A planes
+    // [pieces][C][wlda] bf16, GEMM split outputs (wy_cap floats), q and the
+    // attention output [C][H*D]
+    size_t wx = 0, wa = 0, wy = 0, wq = 0, wo = 0;
+    long long wa_plane = 0, wy_cap = 0;
+    int wlda = 0;
     size_t o_bytes = 0, h_bytes = 0, am_count = 0;
     int a_es = 2;                      // bytes per A-ready element
     long long h_plane = 0;
@@ -272,6 +279,10 @@ int check_config_n(const pn_config *c) {
     if ((c->rope_neox & ~1) != 0 || (c->qkv_bias & ~1) != 0) return fail(PN_EINVAL, "rope_neox and qkv_bias must be 0 or 1");
     if (c->rope_neox && c->kv_dtype == PN_Q4_0)
         return fail(PN_EUNSUPPORTED, "a Q4 KV cache quantises k in natural dim order: no NeoX RoPE");
+    if (c->prefill_chunk < 0 || c->prefill_chunk > kWideRows)
+        return fail(PN_EINVAL, "prefill_chunk must be in [0, %d]", kWideRows);
+    if (c->prefill_chunk > 0 && (c->w_dtype != PN_BF16 || c->n_expert > 0 || c->kv_dtype == PN_Q4_0))
+        return fail(PN_EUNSUPPORTED, "the wide prefill path needs bf16 weights, no experts and an fp32 or bf16 cache");
     const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
@@ -372,7 +383,21 @@ size_t layout_model(pn_model *m) {
     m->am_idx = bp.take(m->am_count * 4);
     m->samp_keys = bp.take((size_t)MB * m->V * 4);
     m->attn_part_row = (size_t)m->Hk * kMaxSplits * m->G * (m->D + 4) * 4;
-    m->attn_part = bp.take((size_t)MB * m->attn_part_row);
+    const int C = c.prefill_chunk;
+    // (wide prefill runs its attention 16 rows at a time, each with its own split scratch)
+    m->attn_part = bp.take((size_t)std::max(MB, C > 0 ? kMaxSlots : 0) * m->attn_part_row);
+    if (C > 0) {
+        m->wlda = cdiv(std::max(m->E, std::max(HD, m->F)), 32) * 32;
+        m->wa_plane = (long long)C * m->wlda;
+        m->wx = bp.take((size_t)C * m->E * 4);
+        m->wa = bp.take((size_t)m->pieces * m->wa_plane * 2);
+        m->wq = bp.take((size_t)C * HD * 4);
+        m->wo = bp.take((size_t)C * HD * 4);
+        const long long qo = (long long)cdiv(std::max(m->Nqkv, m->E), 16) * 16;
+        m->wy_cap = std::max((long long)kWideSplitMax * C * qo,
+                             std::max(2LL * 2 * C * cdiv(m->F, 16) * 16, (long long)C * cdiv(m->V, 16) * 16));
+        m->wy = bp.take((size_t)m->wy_cap * 4);
+    }
     m->kv_new = c.kv_dtype == PN_Q4_0 ? bp.take((size_t)MB * 2 * m->Hk * m->D * 4) : 0;
     m->samp_hist = bp.take((size_t)MB * kSampleBins * 4);
     m->samp_cnt = bp.take((size_t)MB * 2 * 4);
@@ -634,9 +659,50 @@ struct Timed {
 // prefill (row_pos given), every row to the one state st[0] at row_pos[b]:
 // the rows then share the state's cache and page table, and their attention
 // splits use the model's per-row scratch.
+// Attention geometry of n rows (row b: state st[b] at position pos[b]).
+// Splits: a row's window, from its start rounded down to a page, is np pages;
+// split s of nsplit takes pages [s*np/nsplit, (s+1)*np/nsplit), so a row's
+// splits differ by at most one page.  nsplit comes from the caller's keys per
+// split (PN_OPT_ATTN_KEYS_PER_SPLIT), else from sharing about
+// kAttnTargetGroups work-groups among the rows in proportion to their pages;
+// it is at most the row's pages and its scratch capacity.  With rows, the
+// split scratch is the model's per-row buffer (prefill rows share a state);
+// otherwise each state's own.  Sets everything but q, o and the K/V pools;
+// returns the largest nsplit.
+int attn_setup(const pn_model *m, pn_state *const *st, int n, const int *pos, bool rows, AttnArgs &aa) {
+    aa.Hq = m->H;
+    aa.Hk = m->Hk;
+    aa.scale = (float)(1.4426950408889634 / std::sqrt((double)m->D));  // log2(e) / sqrt(D)
+    long long np_sum = 0;
+    for (int b = 0; b < n; ++b) np_sum += cdiv(pos[b] + 1 - window_lo(m, pos[b]) / kPage * kPage, kPage);
+    int nsplit_max = 1;
+    for (int b = 0; b < n; ++b) {
+        const int lo = window_lo(m, pos[b]);
+        aa.pos[b] = pos[b];
+        aa.lo[b] = lo;
+        aa.origin[b] = lo / kPage * kPage;
+        const int np = cdiv(pos[b] + 1 - aa.origin[b], kPage);
+        long long ns = m->attn_kps > 0 ? cdiv(np, m->attn_kps / kPage)
+                                       : (long long)kAttnTargetGroups * np / ((long long)m->Hk * np_sum);
+        const int cap = rows ? kMaxSplits : st[b]->s_cap;
+        ns = std::min<long long>(std::max<long long>(ns, 1), std::min(np, std::min(cap, kMaxSplits)));
+        aa.np[b] = np;
+        aa.nsplit[b] = (int)ns;
+        aa.s_cap[b] = cap;
+        nsplit_max = std::max(nsplit_max, aa.nsplit[b]);
+        aa.pt[b] = (const int *)(st[b]->base + st[b]->pt);
+        aa.part[b] = rows ? (float *)(m->base + m->attn_part + (size_t)b * m->attn_part_row)
+                          : (float *)(st[b]->base + st[b]->part);
+        aa.kv_bytes[b] = (unsigned)st[b]->layer_bytes;
+    }
+    return nsplit_max;
+}
+
 int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, float *logits, int32_t *amax,
                  hipStream_t s, const int *row_pos = nullptr) {
     auto posof = [&](int b) { return row_pos ? row_pos[b] : st[b]->pos; };
+    int pos_of_rows[kMaxSlots];
+    for (int b = 0; b < n; ++b) pos_of_rows[b] = posof(b);
     const pn_config &c = m->cfg;
     char *mb = m->base;
     for (auto &r : m->last) r.clear();
@@ -683,43 +749,9 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
 
     // attention geometry per slot
     AttnArgs aa{};
+    const int nsplit_max = attn_setup(m, st, n, pos_of_rows, row_pos != nullptr, aa);
     aa.q = (const float *)(mb + m->q);
     aa.o = (float *)(mb + m->o);
-    aa.Hq = m->H;
-    aa.Hk = m->Hk;
-    aa.scale = (float)(1.4426950408889634 / std::sqrt((double)m->D));  // log2(e) / sqrt(D)
-    // Splits.  A slot's window, from its start rounded down to a page, is np
-    // pages; split s of nsplit takes pages [s*np/nsplit, (s+1)*np/nsplit), so a
-    // slot's splits differ by at most one page.  nsplit comes from the caller's
-    // keys per split (PN_OPT_ATTN_KEYS_PER_SPLIT), else from sharing about
-    // kAttnTargetGroups work-groups among the slots in proportion to their
-    // pages; it is at most the slot's pages and its scratch capacity.
-    long long np_sum = 0;
-    for (int b = 0; b < n; ++b) {
-        const int pos = posof(b);
-        np_sum += cdiv(pos + 1 - window_lo(m, pos) / kPage * kPage, kPage);
-    }
-    int nsplit_max = 1;
-    for (int b = 0; b < n; ++b) {
-        const int pos = posof(b);
-        const int lo = window_lo(m, pos);
-        aa.pos[b] = pos;
-        aa.lo[b] = lo;
-        aa.origin[b] = lo / kPage * kPage;
-        const int np = cdiv(pos + 1 - aa.origin[b], kPage);
-        long long ns = m->attn_kps > 0 ? cdiv(np, m->attn_kps / kPage)
-                                       : (long long)kAttnTargetGroups * np / ((long long)m->Hk * np_sum);
-        const int cap = row_pos ? kMaxSplits : st[b]->s_cap;
-        ns = std::min<long long>(std::max<long long>(ns, 1), std::min(np, std::min(cap, kMaxSplits)));
-        aa.np[b] = np;
-        aa.nsplit[b] = (int)ns;
-        aa.s_cap[b] = cap;
-        nsplit_max = std::max(nsplit_max, aa.nsplit[b]);
-        aa.pt[b] = (const int *)(st[b]->base + st[b]->pt);
-        aa.part[b] = row_pos ? (float *)(m->base + m->attn_part + (size_t)b * m->attn_part_row)
-                             : (float *)(st[b]->base + st[b]->part);
-        aa.kv_bytes[b] = (unsigned)st[b]->layer_bytes;
-    }
 
     const LayerOff &L0 = m->L[0];
     const int gz = moe ? m->X : 1;
@@ -960,6 +992,163 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     if (row_pos) st[0]->pos += n;
     else for (int b = 0; b < n; ++b) st[b]->pos += 1;
     for (int b = 0; b < n; ++b) recycle_pages(st[b]);
+    return PN_OK;
+}
+
+// ---- wide prefill: the rows of one chunk through each projection at once
+
+// Splits over K of one wide GEMM: doubled while the grid gives under two
+// work-groups per compute unit, every split keeps at least 8 k tiles and the
+// outputs fit the split buffer.
+int wide_splits(long long groups, int KT, long long floats_per_split, long long cap) {
+    int ks = 1;
+    while (ks < kWideSplitMax && groups * ks < 2 * kCUs && KT / (2 * ks) >= 8 && 2 * ks * floats_per_split <= cap)
+        ks *= 2;
+    return ks;
+}
+
+// Y = A * W^T for R rows of the A planes: nz matrices (1, or 2 for gate and
+// up) with outputs y[z] [split][R][ldy]; returns the number of splits used.
+int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_t *w1, float *y0, float *y1, int nz,
+              int R, int N, int ldy, bool split_ok, hipStream_t s) {
+    static_assert(tile_k(WT_BF16) == 32, "bf16 tiles hold 32 k");
+    const long long groups = (long long)cdiv(R, 128) * cdiv(mat.n_tiles, 8) * nz;
+    const long long per = (long long)R * ldy;
+    const int ks = split_ok ? wide_splits(groups, mat.KT, per * nz, m->wy_cap) : 1;
+    WGemmArgs g{};
+    g.w[0] = w0;
+    g.w[1] = w1 ? w1 : w0;
+    g.y[0] = y0;
+    g.y[1] = y1 ? y1 : y0;
+    g.y_split = per;
+    g.a = (const uint16_t *)(m->base + m->wa);
+    g.a_plane = m->wa_plane;
+    g.lda = m->wlda;
+    g.R = R;
+    g.N = N;
+    g.n_tiles = mat.n_tiles;
+    g.KT = mat.KT;
+    g.ldy = ldy;
+    g.nsplit = ks;
+    const dim3 grid(cdiv(R, 128), cdiv(mat.n_tiles, 8), nz * ks);
+    if (m->pieces == 3) hipLaunchKernelGGL(k_wgemm<3>, grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL(k_wgemm<1>, grid, dim3(256), 0, s, g);
+    return ks;
+}
+
+// One chunk of R rows of state st at positions st->pos .. st->pos + R - 1
+// (pages already present).  Same result as R decode steps up to fp32
+// summation order.
+int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *logits, int32_t *amax, hipStream_t s) {
+    const pn_config &c = m->cfg;
+    char *mb = m->base;
+    const int E = m->E, HD = m->H * m->D, F = m->F, p0 = st->pos;
+    const bool bf = m->at == PN_BF16;
+    float *x = (float *)(mb + m->wx), *y = (float *)(mb + m->wy);
+    float *q = (float *)(mb + m->wq), *o = (float *)(mb + m->wo);
+    uint16_t *a = (uint16_t *)(mb + m->wa);
+    int *err = (int *)(st->base + st->err);
+    const float eps = c.rms_norm_eps;
+    auto norm = [&](const float *gain) {
+        if (bf) hipLaunchKernelGGL(k_w_norm<AT_BF16>, dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane, m->wlda);
+        else hipLaunchKernelGGL(k_w_norm<AT_F32>, dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane, m->wlda);
+    };
+    hipLaunchKernelGGL(k_w_embed, dim3(R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E, m->V, err);
+    for (int l = 0; l < c.n_layer; ++l) {
+        const LayerOff &L = m->L[l];
+        char *kvk = kv_layer(st, l, false), *kvv = kv_layer(st, l, true);
+        // ---- QKV, bias, RoPE, K/V append
+        norm((const float *)(mb + L.attn_norm));
+        {
+            const int ld = L.qkv.n_tiles * 16;
+            const int ks = wide_gemm(m, L.qkv, (const uint8_t *)(mb + L.qkv.off), nullptr, y, nullptr, 1, R, ld, ld,
+                                     true, s);
+            WQkvArgs w{};
+            w.y = y;
+            w.split = (long long)R * ld;
+            w.nsplit = ks;
+            w.ldy = ld;
+            w.p0 = p0;
+            w.Hq = m->H;
+            w.Hk = m->Hk;
+            w.D = m->D;
+            w.kv_es = dtype_size(m->kvt);
+            w.bias = L.bqkv ? (const float *)(mb + L.bqkv) : nullptr;
+            w.omega = (const double *)(mb + m->omega);
+            w.q = q;
+            w.kvk = kvk;
+            w.kvv = kvv;
+            w.pt = (const int *)(st->base + st->pt);
+            hipLaunchKernelGGL(k_w_qkv, dim3(R), dim3(256), 0, s, w);
+            if (int rc = launched("wide QKV")) return rc;
+        }
+        // ---- attention, kMaxSlots rows per launch (each row sees keys up to its own position)
+        for (int r0 = 0; r0 < R; r0 += kMaxSlots) {
+            const int n = std::min(kMaxSlots, R - r0);
+            pn_state *sts[kMaxSlots];
+            int pos[kMaxSlots];
+            for (int b = 0; b < n; ++b) {
+                sts[b] = st;
+                pos[b] = p0 + r0 + b;
+            }
+            AttnArgs aa{};
+            const int nsm = attn_setup(m, sts, n, pos, true, aa);
+            aa.q = q + (size_t)r0 * HD;
+            aa.o = o + (size_t)r0 * HD;
+            for (int b = 0; b < n; ++b) {
+                aa.kvk[b] = kvk;
+                aa.kvv[b] = kvv;
+            }
+            aa.kind = m->attn_kind == 1 ? 0 : 1;
+            launch_attn(m->D, m->kvt, m->G, aa, dim3(nsm, m->Hk, n), nsm > 1, s);
+            if (int rc = launched("wide attention")) return rc;
+        }
+        // ---- O + residual
+        if (bf) hipLaunchKernelGGL(k_w_conv<AT_BF16>, dim3(R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+        else hipLaunchKernelGGL(k_w_conv<AT_F32>, dim3(R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+        {
+            const int ld = L.o.n_tiles * 16;
+            const int ks = wide_gemm(m, L.o, (const uint8_t *)(mb + L.o.off), nullptr, y, nullptr, 1, R, ld, ld, true, s);
+            hipLaunchKernelGGL(k_w_resid, dim3(R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
+            if (int rc = launched("wide O")) return rc;
+        }
+        // ---- gate/up, SwiGLU, down + residual
+        norm((const float *)(mb + L.ffn_norm));
+        {
+            const int ld = L.gate.n_tiles * 16;
+            float *yu = y + m->wy_cap / 2;  // (2 matrices x at most 2 splits of R x ld fit each half)
+            const bool fits = 2LL * 2 * R * ld <= m->wy_cap;
+            const int ks = wide_gemm(m, L.gate, (const uint8_t *)(mb + L.gate.off), (const uint8_t *)(mb + L.up.off),
+                                     y, yu, 2, R, ld, ld, fits, s);
+            if (bf)
+                hipLaunchKernelGGL(k_w_swiglu<AT_BF16>, dim3(R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
+                                   m->wa_plane, m->wlda);
+            else
+                hipLaunchKernelGGL(k_w_swiglu<AT_F32>, dim3(R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
+                                   m->wa_plane, m->wlda);
+            if (int rc = launched("wide gate/up")) return rc;
+        }
+        {
+            const int ld = L.down.n_tiles * 16;
+            const int ks = wide_gemm(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, y, nullptr, 1, R, ld, ld,
+                                     true, s);
+            hipLaunchKernelGGL(k_w_resid, dim3(R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
+            if (int rc = launched("wide down")) return rc;
+        }
+    }
+    // ---- final norm, LM head, argmax (only when an output is asked for)
+    if (logits || amax) {
+        norm((const float *)(mb + m->out_norm));
+        float *lg = logits ? logits : y;
+        const int ld = logits ? m->V : m->out.n_tiles * 16;
+        wide_gemm(m, m->out, (const uint8_t *)(mb + m->out.off), nullptr, lg, nullptr, 1, R, m->V, ld, false, s);
+        if (amax) hipLaunchKernelGGL(k_w_argmax, dim3(R), dim3(256), 0, s, lg, (long long)ld, m->V, amax, err);
+        if (int rc = launched("wide LM head")) return rc;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    st->pos += R;
+    recycle_pages(st);
     return PN_OK;
 }
 
@@ -1414,6 +1603,17 @@ int pn_prefill(pn_model *m, pn_state *s, const int32_t *tokens_dev, int32_t n, f
     if (n < 1) return fail(PN_EINVAL, "n = %d must be >= 1", n);
     if (s->pos < 0 || (long long)s->pos + n > s->max_ctx)
         return fail(PN_ERANGE, "positions %d..%lld exceed max_ctx %d", s->pos, (long long)s->pos + n - 1, s->max_ctx);
+    if (m->cfg.prefill_chunk > 0) {  // the wide path
+        for (int t0 = 0; t0 < n; t0 += m->cfg.prefill_chunk) {
+            const int c = std::min(m->cfg.prefill_chunk, n - t0);
+            const int p1 = s->pos + c;
+            if (int rc = ensure_pages(&s, 1, &s->pos, &p1, S(stream))) return rc;
+            if (int rc = prefill_wide(m, s, tokens_dev + t0, c, logits_dev ? logits_dev + (size_t)t0 * m->V : nullptr,
+                                      argmax_dev ? argmax_dev + t0 : nullptr, S(stream)))
+                return rc;
+        }
+        return PN_OK;
+    }
     // chunks of max_batch tokens, each one batched step over consecutive positions
     const int chunk = m->cfg.max_batch;
     std::vector<pn_state *> rows(chunk, s);

@@ -1,0 +1,299 @@
+// pn_wide.hpp - prefill of many prompt rows of one sequence at once ("Engine
+// Architecture", chunked prefill: the prompt's positions go through each layer
+// together, so every weight is read once per chunk).  Included only by
+// pn_lib.hip.
+//
+// The decode GEMM takes at most 16 rows, so a chunk there re-reads every
+// weight each 16 tokens.  Here a chunk of up to kWideRows rows goes through
+// each projection as one matrix product on the matrix cores (k_wgemm), with
+// the steps around it as plain row kernels: RMSNorm into MFMA-ready planes,
+// RoPE + K/V append, SwiGLU, the residual add and the per-row argmax.  Dense
+// models with bf16 weights and an fp32 or bf16 cache take this path.
+#pragma once
+#include "pn_kernels.hpp"
+
+namespace pn {
+
+constexpr int kWideRows = 256;   // most rows of one wide chunk
+constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
+
+// Y_s[r][n] = sum over k in split s of A[r][k] * W[n][k], for the P planes of
+// A (the bf16 pieces whose sum is the fp32 input, or one bf16 plane).
+//   W: packed bf16 tiles [n_tiles][KT][1 KiB]; tile = 16 rows x 32 k, lane l
+//      holds row l & 15, k 8*(l >> 4) .. +7 (the 16x16x32 operand layout).
+//   A: planes [P][rows][lda] bf16, lda >= KT*32, zero from K up to lda.
+//   Y: split s, matrix z at y[z] + s * y_split, [r][ldy] fp32; rows < R and
+//      n < N are written.
+// grid: x = 128-row group of A, y = 128-row group of W (8 tiles), z =
+// matrix * nsplit + split; 256 threads.  Wave w computes weight tiles
+// 4*(w & 1) .. +3 against row tiles 4*(w >> 1) .. +3 of the group (16
+// accumulators); each k step loads its 4 weight fragments and 4*P row
+// fragments, the next step's loads in flight while this step's 16*P matrix
+// steps run.  Tiles past n_tiles and rows past R load clamped (in bounds)
+// and are not stored.
+struct WGemmArgs {
+    const uint8_t *w[2];
+    float *y[2];
+    long long y_split;  // floats between the splits' outputs
+    const uint16_t *a;
+    long long a_plane;  // elements between the planes of A
+    int lda, R, N, n_tiles, KT, ldy, nsplit;
+};
+
+template <int P>
+__global__ void __launch_bounds__(256) k_wgemm(WGemmArgs g) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int z = blockIdx.z / g.nsplit, s = blockIdx.z % g.nsplit;
+    const int kt0 = (int)((long long)s * g.KT / g.nsplit), kt1 = (int)((long long)(s + 1) * g.KT / g.nsplit);
+    const int wt0 = blockIdx.y * 8 + 4 * (wv & 1);  // first weight tile of the wave
+    const int rt0 = blockIdx.x * 8 + 4 * (wv >> 1);  // first row tile of the wave
+    if (wt0 >= g.n_tiles || rt0 * 16 >= g.R) return;  // (no barriers below)
+    const uint8_t *wp[4];
+    const uint16_t *ap[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wp[i] = g.w[z] + (long long)min(wt0 + i, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
+        const int r = min((rt0 + i) * 16 + (lane & 15), g.R - 1);
+        ap[i] = g.a + (long long)r * g.lda + 8 * (lane >> 4);
+    }
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 wa[4], wb[4], aa[4][P], ab[4][P];
+    auto load = [&](int kt, u32x4 (&wr)[4], u32x4 (&ar)[4][P]) {
+        kt = min(kt, kt1 - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp[i] + (long long)kt * 1024));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                ar[j][p] = *reinterpret_cast<const u32x4 *>(ap[j] + p * g.a_plane + (long long)kt * 32);
+    };
+    auto step = [&](const u32x4 (&wr)[4], const u32x4 (&ar)[4][P]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[i]),
+                                                                        __builtin_bit_cast(bf16x8, ar[j][p]),
+                                                                        acc[i][j], 0, 0, 0);
+    };
+    if (kt0 < kt1) {
+        load(kt0, wa, aa);
+        for (int kt = kt0; kt < kt1; kt += 2) {
+            load(kt + 1, wb, ab);
+            step(wa, aa);
+            load(kt + 2, wa, aa);
+            if (kt + 1 < kt1) step(wb, ab);
+        }
+    }
+    // lane l holds rows 4*(l >> 4) .. +3 of weight tile i (outputs n) for A row (l & 15) of row tile j
+    float *y = g.y[z] + (long long)s * g.y_split;
+    const bool vec = (g.ldy & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (rt0 + j) * 16 + (lane & 15);
+        if (r >= g.R) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n0 = (wt0 + i) * 16 + 4 * (lane >> 4);
+            float *yp = y + (long long)r * g.ldy + n0;
+            if (vec && n0 + 3 < g.N) {
+                *reinterpret_cast<f32x4 *>(yp) = acc[i][j];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n0 + e < g.N) yp[e] = acc[i][j][e];
+            }
+        }
+    }
+}
+
+// The sum over the nsplit partial outputs (in split order) of element idx.
+__device__ __forceinline__ float wide_sum(const float *y, long long split, int nsplit, long long idx) {
+    float v = y[idx];
+    for (int s = 1; s < nsplit; ++s) v += y[(long long)s * split + idx];
+    return v;
+}
+
+// x[r] = tok_embd[token[r]] (bf16 table); a bad id uses row 0 and sets a flag.
+// grid: rows; 256 threads.
+__global__ void __launch_bounds__(256) k_w_embed(const uint16_t *embd, const int *tokens, float *x, int E, int V,
+                                                  int *err) {
+    const int r = blockIdx.x;
+    int tok = tokens[r];
+    if (tok < 0 || tok >= V) {
+        if (threadIdx.x == 0) atomicOr(err, ERR_TOKEN);
+        tok = 0;
+    }
+    const uint16_t *src = embd + (long long)tok * E;
+    for (int k = threadIdx.x; k < E; k += 256) x[(long long)r * E + k] = __uint_as_float((uint32_t)src[k] << 16);
+}
+
+// Row r of A = round_act(RMSNorm(x[r]) * gain) as MFMA planes (AReady
+// layout of bf16 weights), zero from K to lda.  grid: rows; 256 threads.
+template <int AT>
+__global__ void __launch_bounds__(256) k_w_norm(const float *x, int K, const float *gain, float eps, uint16_t *a,
+                                                 long long a_plane, int lda) {
+    __shared__ float red[4];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const float *xr = x + (long long)r * K;
+    float ss = 0.f;
+    for (int k = tid; k < K; k += 256) ss += xr[k] * xr[k];
+    ss = block_sum<4>(ss, red);
+    const float ri = 1.0f / sqrtf(ss / (float)K + eps);
+    for (int k = tid; k < lda; k += 256) {
+        const float v = k < K ? (xr[k] * ri) * gain[k] : 0.f;
+        AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, v);
+    }
+}
+
+// Row r of A = round_act(src[r]) (fp32 rows of ld K), zero from K to lda.
+template <int AT>
+__global__ void __launch_bounds__(256) k_w_conv(const float *src, int K, uint16_t *a, long long a_plane, int lda) {
+    const int r = blockIdx.x;
+    for (int k = threadIdx.x; k < lda; k += 256)
+        AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, k < K ? src[(long long)r * K + k] : 0.f);
+}
+
+// h = silu(gate) * up from the split outputs of the gate / up products, as the
+// down projection's A planes (zero from F to lda).
+template <int AT>
+__global__ void __launch_bounds__(256) k_w_swiglu(const float *yg, const float *yu, long long split, int nsplit,
+                                                   int ldy, int F, uint16_t *a, long long a_plane, int lda) {
+    const int r = blockIdx.x;
+    for (int k = threadIdx.x; k < lda; k += 256) {
+        float h = 0.f;
+        if (k < F) {
+            const long long i = (long long)r * ldy + k;
+            const float gt = wide_sum(yg, split, nsplit, i);
+            const float up = wide_sum(yu, split, nsplit, i);
+            h = (gt / (1.0f + expf(-gt))) * up;
+        }
+        AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, h);
+    }
+}
+
+// x[r] += y[r] (summed over the splits).
+__global__ void __launch_bounds__(256) k_w_resid(float *x, const float *y, long long split, int nsplit, int ldy,
+                                                  int E) {
+    const int r = blockIdx.x;
+    for (int k = threadIdx.x; k < E; k += 256)
+        x[(long long)r * E + k] += wide_sum(y, split, nsplit, (long long)r * ldy + k);
+}
+
+struct WQkvArgs {
+    const float *y;     // split outputs [r][ldy], rows in packed order (q, k, v)
+    long long split;
+    int nsplit, ldy;
+    int p0;             // position of row 0
+    int Hq, Hk, D, kv_es;
+    const float *bias;  // packed order, or null
+    const double *omega;
+    float *q;           // [r][Hq*D]
+    char *kvk, *kvv;    // this layer's K, V pages
+    const int *pt;
+};
+
+// Per row r at position p0 + r and adjacent pair (2i, 2i+1) of the QKV rows:
+// bias, RoPE on q and k by the angle (p0 + r) * omega_(pair in head), whose
+// sine and cosine are taken in fp64 and rounded to fp32, then q into q[r] and
+// k, v into the cache (layouts as kv_k_off / kv_v_off).  grid: rows; 256 threads.
+__global__ void __launch_bounds__(256) k_w_qkv(WQkvArgs g) {
+    const int r = blockIdx.x, pos = g.p0 + r;
+    const int hd = g.Hq * g.D, kd = g.Hk * g.D;
+    const int page = g.pt[pos / kPage], t = pos % kPage;
+    const bool tiled = g.kv_es == 2;
+    for (int i = threadIdx.x; i < (hd + 2 * kd) / 2; i += 256) {
+        const int r0 = 2 * i;
+        const long long yi = (long long)r * g.ldy + r0;
+        float y0 = wide_sum(g.y, g.split, g.nsplit, yi), y1 = wide_sum(g.y, g.split, g.nsplit, yi + 1);
+        if (g.bias) {
+            y0 += g.bias[r0];
+            y1 += g.bias[r0 + 1];
+        }
+        const bool isv = r0 >= hd + kd;
+        if (!isv) {
+            const double phi = (double)pos * g.omega[(r0 % g.D) >> 1];
+            double sn, cs;
+            sincos(phi, &sn, &cs);
+            rope_pair(y0, y1, make_float2((float)cs, (float)sn));
+        }
+        if (r0 < hd) {
+            g.q[(long long)r * hd + r0] = y0;
+            g.q[(long long)r * hd + r0 + 1] = y1;
+            continue;
+        }
+        const int rr = isv ? r0 - hd - kd : r0 - hd;
+        const int j = rr / g.D, dd = rr % g.D;
+        const long long hb = ((long long)page * g.Hk + j) * kPage * g.D;
+        if (!isv) {
+            const long long off = hb + kv_k_off(tiled, t, dd, g.D);  // dd, dd + 1 adjacent
+            if (tiled) {
+                *reinterpret_cast<uint32_t *>(g.kvk + off * 2) = bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
+            } else {
+                reinterpret_cast<float *>(g.kvk)[off] = y0;
+                reinterpret_cast<float *>(g.kvk)[off + 1] = y1;
+            }
+        } else {
+            const long long o0 = hb + kv_v_off(tiled, t, dd, g.D), o1 = hb + kv_v_off(tiled, t, dd + 1, g.D);
+            if (tiled) {
+                reinterpret_cast<uint16_t *>(g.kvv)[o0] = (uint16_t)bf16_rne_bits(y0);
+                reinterpret_cast<uint16_t *>(g.kvv)[o1] = (uint16_t)bf16_rne_bits(y1);
+            } else {
+                reinterpret_cast<float *>(g.kvv)[o0] = y0;
+                reinterpret_cast<float *>(g.kvv)[o1] = y1;
+            }
+        }
+    }
+}
+
+// out[r] = the index of the largest logit of row r (the lowest on ties; NaN
+// logits are skipped and set the NaN flag; -1 when every logit is NaN).
+// grid: rows; 256 threads.
+__global__ void __launch_bounds__(256) k_w_argmax(const float *logits, long long ld, int N, int *out, int *err) {
+    __shared__ float sv[256];
+    __shared__ int si[256];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const float *lr = logits + (long long)r * ld;
+    float best = 0.f;
+    int bi = -1;
+    bool nan = false;
+    for (int n = tid; n < N; n += 256) {  // increasing n: a later equal value never wins
+        const float v = lr[n];
+        if (v != v) {
+            nan = true;
+            continue;
+        }
+        if (bi < 0 || v > best) {
+            best = v;
+            bi = n;
+        }
+    }
+    if (nan) atomicOr(err, ERR_NAN);
+    sv[tid] = best;
+    si[tid] = bi;
+    lds_barrier();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) {
+            const float v = sv[tid + o];
+            const int i = si[tid + o];
+            if (i >= 0 && (si[tid] < 0 || v > sv[tid] || (v == sv[tid] && i < si[tid]))) {
+                sv[tid] = v;
+                si[tid] = i;
+            }
+        }
+        lds_barrier();
+    }
+    if (tid == 0) out[r] = si[0];
+}
+
+}  // namespace pn

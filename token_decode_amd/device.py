@@ -35,7 +35,7 @@ def upload(arr, device="cuda"):
 def make_config(n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab, *, n_ctx=2048,
                 n_expert=0, n_expert_used=0, sliding_window=0, max_batch=1, rope_theta=10000.0,
                 rms_norm_eps=1e-5, w_dtype=C.PN_BF16, kv_dtype=C.PN_BF16, act_dtype=C.PN_F32,
-                rope_neox=False, qkv_bias=False):
+                rope_neox=False, qkv_bias=False, prefill_chunk=0):
     cfg = C.pn_config()
     C.lib().pn_config_default(ctypes.byref(cfg))
     for k, v in dict(n_layer=n_layer, n_embd=n_embd, n_head=n_head, n_kv_head=n_kv_head,
@@ -43,7 +43,8 @@ def make_config(n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab, *, 
                      n_expert_used=n_expert_used, sliding_window=sliding_window,
                      max_batch=max_batch, rope_theta=rope_theta, rms_norm_eps=rms_norm_eps,
                      w_dtype=w_dtype, kv_dtype=kv_dtype, act_dtype=act_dtype,
-                     rope_neox=int(rope_neox), qkv_bias=int(qkv_bias)).items():
+                     rope_neox=int(rope_neox), qkv_bias=int(qkv_bias),
+                     prefill_chunk=prefill_chunk).items():
         setattr(cfg, k, v)
     return cfg
 
