@@ -86,13 +86,19 @@ __global__ void __launch_bounds__(256) k_wgemm(WGemmArgs g) {
                                                                         __builtin_bit_cast(bf16x8, ar[j][p]),
                                                                         acc[i][j], 0, 0, 0);
     };
+    // (the scheduling barriers keep each step's loads issued ahead of the
+    // previous step's matrix-core work instead of sunk next to their use)
     if (kt0 < kt1) {
         load(kt0, wa, aa);
         for (int kt = kt0; kt < kt1; kt += 2) {
             load(kt + 1, wb, ab);
+            __builtin_amdgcn_sched_barrier(0);
             step(wa, aa);
+            __builtin_amdgcn_sched_barrier(0);
             load(kt + 2, wa, aa);
+            __builtin_amdgcn_sched_barrier(0);
             if (kt + 1 < kt1) step(wb, ab);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // lane l holds rows 4*(l >> 4) .. +3 of weight tile i (outputs n) for A row (l & 15) of row tile j
@@ -117,11 +123,16 @@ __global__ void __launch_bounds__(256) k_wgemm(WGemmArgs g) {
     }
 }
 
-// The sum over the nsplit partial outputs (in split order) of element idx.
+// The sum over the nsplit partial outputs (in split order) of element idx;
+// all loads are issued before the adds (splits past nsplit add +0).
 __device__ __forceinline__ float wide_sum(const float *y, long long split, int nsplit, long long idx) {
-    float v = y[idx];
-    for (int s = 1; s < nsplit; ++s) v += y[(long long)s * split + idx];
-    return v;
+    float v[kWideSplitMax];
+#pragma unroll
+    for (int s = 0; s < kWideSplitMax; ++s) v[s] = s < nsplit ? y[(long long)s * split + idx] : 0.f;
+    float t = v[0];
+#pragma unroll
+    for (int s = 1; s < kWideSplitMax; ++s) t += v[s];
+    return t;
 }
 
 // x[r] = tok_embd[token[r]] (bf16 table); a bad id uses row 0 and sets a flag.
