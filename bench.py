@@ -12,8 +12,9 @@ replays of the timed steps' launches; HBM traffic from the committed counter
 summary while the GEMM sources are unchanged) and the fp64 CPU oracle timed
 on a bounded sample of the same workload.
 
-The line also reports the time of one on-device sampling call (pn_sample) over
-the step's logits, outside the timed steps.
+The line also reports, outside the timed steps, the time of one on-device
+sampling call (pn_sample) over the step's logits and the throughput of a
+512-token prompt prefilled on the wide path (pn_prefill in chunks of 256 rows).
 
 --calibrate-copy runs only a 1 GiB device copy, the reference for scaling the
 HBM byte counters; --print-source-hash prints the hash the counter summary is
@@ -33,6 +34,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+
+# chunked prefill, timed next to the decode step: rows per wide chunk and prompt length
+PREFILL_CHUNK = 256
+PREFILL_TOKENS = 512
+
+
+def wide_ok(wl):
+    """Whether the workload can take the wide prefill path (bf16 weights, dense, fp32 or bf16 cache)."""
+    import synth
+    return wl.w_dtype == synth.BF16 and wl.n_expert == 0 and wl.kv_dtype in (synth.F32, synth.BF16)
 
 
 def log(msg):
@@ -115,7 +127,8 @@ def main():
                          wl.n_vocab, n_expert=wl.n_expert, n_expert_used=wl.n_expert_used,
                          sliding_window=wl.sliding_window, max_batch=wl.slots,
                          rope_theta=wl.rope_theta, rms_norm_eps=wl.rms_norm_eps,
-                         w_dtype=wl.w_dtype, kv_dtype=wl.kv_dtype, act_dtype=wl.act_dtype)
+                         w_dtype=wl.w_dtype, kv_dtype=wl.kv_dtype, act_dtype=wl.act_dtype,
+                         prefill_chunk=PREFILL_CHUNK if wide_ok(wl) else 0)
     t0 = time.time()
     model = dv.DeviceModel(cfg, W)
     log("model packed in %.1fs (%.2f GB)" % (time.time() - t0, model.nbytes / 1e9))
@@ -195,6 +208,33 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     sample_us = round(1e3 * e0.elapsed_time(e1) / 64, 2)
+    # chunked prefill on the wide path (pn_prefill), for the record: a
+    # 512-token prompt from position 0 into a fresh state, greedy ids only
+    prefill = None
+    if wide_ok(wl):
+        n_p = PREFILL_TOKENS
+        pst = dv.DeviceState(model, n_p + 8)
+        ptok = torch.from_numpy(synth.uniform_int(wl.seed, 99, n_p, 0, wl.n_vocab - 1).astype("int32")).cuda()
+        pam = torch.empty(n_p, dtype=torch.int32, device="cuda")
+        runs = []
+        for i in range(3):
+            pst.pos = 0
+            e0.record(stream)
+            dv.prefill(model, pst, ptok, None, pam, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                runs.append(e0.elapsed_time(e1))
+        p_ms = sum(runs) / len(runs)
+        pieces = 3 if wl.act_dtype == synth.F32 else 1
+        mm = wl.n_layer * (wl.n_embd * (wl.n_head + 2 * wl.n_kv_head) * wl.head_dim +
+                           wl.n_head * wl.head_dim * wl.n_embd + 3 * wl.n_embd * wl.n_ff) + wl.n_vocab * wl.n_embd
+        prefill = {"tokens_per_s": round(n_p / p_ms * 1e3, 1), "tokens": n_p, "chunk": PREFILL_CHUNK,
+                   "ms": round(p_ms, 3),
+                   "matrix_core_tflops": round(2.0 * mm * n_p * pieces / (p_ms * 1e-3) / 1e12, 1),
+                   "bf16_pieces_per_input": pieces}
+        pst.free()
+        log("prefill: %d tokens in %.2f ms = %.0f tokens/s" % (n_p, p_ms, n_p / p_ms * 1e3))
     dom = "gateup"
     dom_bytes = gemm_bytes(wl, dom)
     dom_us = per_kernel[dom]["avg_us"]
@@ -236,6 +276,7 @@ def main():
         "kernels": per_kernel,
         "sampling": {"us_per_call": sample_us, "rows": B, "vocab": wl.n_vocab,
                      "params": "temperature 0.8, top_k 40, top_p 0.95, repeat_penalty 1.1 over 64 recent tokens"},
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -1140,7 +1140,52 @@ struct AttnArgs {
     float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max (base 2), sum, 2 pad, unnormalised output
     unsigned kv_bytes[kMaxSlots];  // bytes of one layer's K (and of its V) pool
     int kind;                // bf16 cache: 0 = vector units (k_attn), 1 = matrix cores (k_attn_mfma)
+    // rows > 0: the grid's slots are `rows` prefill rows of one state, row b at
+    // position p0 + b; the per-slot entries 0 hold that state's pages, page
+    // table and split capacity; window, lo, origin, np come from the position
+    // (window 0 = none), nsplit = min(ns_rows, np), and row b's split scratch
+    // starts part_row floats after row b - 1's
+    int rows, p0, window, ns_rows;
+    long long part_row;
 };
+
+// One slot's (or prefill row's) attention geometry.
+struct AttnRow {
+    int pos, lo, origin, np, nsplit, s_cap;
+    const char *kvk, *kvv;
+    const int *pt;
+    float *part;
+    unsigned kv_bytes;
+};
+__device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, int b) {
+    AttnRow r;
+    if (a.rows > 0) {
+        r.pos = a.p0 + b;
+        r.lo = a.window > 0 ? max(0, r.pos - a.window + 1) : 0;
+        r.origin = r.lo / kPage * kPage;
+        r.np = (r.pos + 1 - r.origin + kPage - 1) / kPage;
+        r.nsplit = min(a.ns_rows, r.np);
+        r.s_cap = a.s_cap[0];
+        r.kvk = a.kvk[0];
+        r.kvv = a.kvv[0];
+        r.pt = a.pt[0];
+        r.part = a.part[0] + (long long)b * a.part_row;
+        r.kv_bytes = a.kv_bytes[0];
+    } else {
+        r.pos = a.pos[b];
+        r.lo = a.lo[b];
+        r.origin = a.origin[b];
+        r.np = a.np[b];
+        r.nsplit = a.nsplit[b];
+        r.s_cap = a.s_cap[b];
+        r.kvk = a.kvk[b];
+        r.kvv = a.kvv[b];
+        r.pt = a.pt[b];
+        r.part = a.part[b];
+        r.kv_bytes = a.kv_bytes[b];
+    }
+    return r;
+}
 
 // Split-K flash decode for G query heads per KV head.  Decode attention
 // moves few bytes per work-group, and one compute unit only pulls a small
@@ -1255,7 +1300,7 @@ struct AttnShape {
 // cache, four 8-byte pieces for a bf16 one), and keys outside [lo, kl] read
 // zeros (their weights are 0, and 0 * NaN would not be).
 template <int D, int KV>
-__device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int pg, int k0, int lo, int kl, int kq,
+__device__ __forceinline__ void attn_load(const AttnArgs &a, const AttnRow &R, int j, int pg, int k0, int lo, int kl, int kq,
                                           int dq, int lane, u32x4 (&kr)[AttnShape<D, KV>::NKL],
                                           typename AttnShape<D, KV>::vword (&vr)[16]) {
     typedef AttnShape<D, KV> S;
@@ -1265,7 +1310,7 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int p
     uint32_t col[S::VE][16];
     if constexpr (KV == 2) {
         // Q4 block of the head (q4kv_*): codes [key][D/2] then scales [key][D/32]
-        const uint8_t *kb = reinterpret_cast<const uint8_t *>(a.kvk[b]) + ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(D);
+        const uint8_t *kb = reinterpret_cast<const uint8_t *>(R.kvk) + ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(D);
         const uint8_t *krow = kb + (tq % kPage) * (D / 2) + dq * (D / 8);  // the lane's quarter: D/8 bytes
         if constexpr (D == 128) {
             kr[0] = *reinterpret_cast<const u32x4 *>(krow);
@@ -1280,7 +1325,7 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int p
         kr[1] = u32x4{(uint32_t)*ks, 0u, 0u, 0u};
         // values: the lane's byte column for the 16 keys (one 16-byte load) and
         // their scales of its block (32 bytes), widened to fp32 here
-        const uint8_t *vb = reinterpret_cast<const uint8_t *>(a.kvv[b]) + ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(D);
+        const uint8_t *vb = reinterpret_cast<const uint8_t *>(R.kvv) + ((long long)pg * a.Hk + j) * kPage * q4kv_key_bytes(D);
         const int key0 = k0 % kPage;
         const u32x4 cw = *reinterpret_cast<const u32x4 *>(vb + (dl / 2) * kPage + key0);
         const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb + kPage * (D / 2) + ((dl / 32) * kPage + key0) * 2);
@@ -1299,11 +1344,11 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int p
     } else if constexpr (KV == 1) {
         // tiled (kv_k_off / kv_v_off): piece dq + 4c of key row tq % 16 is 16 bytes of
         // the group's 1 KiB step c; the 4 keys 4q..4q+3 of a dim are 8 contiguous bytes
-        const uint8_t *gk = reinterpret_cast<const uint8_t *>(a.kvk[b]) + (hb + (long long)(k0 % kPage) * D) * 2;
+        const uint8_t *gk = reinterpret_cast<const uint8_t *>(R.kvk) + (hb + (long long)(k0 % kPage) * D) * 2;
 #pragma unroll
         for (int c = 0; c < S::NKL; ++c)
             kr[c] = *reinterpret_cast<const u32x4 *>(gk + c * 1024 + (dq * 16 + tq % 16) * 16);
-        const uint8_t *gv = reinterpret_cast<const uint8_t *>(a.kvv[b]) + (hb + (long long)(k0 % kPage) * D) * 2;
+        const uint8_t *gv = reinterpret_cast<const uint8_t *>(R.kvv) + (hb + (long long)(k0 % kPage) * D) * 2;
 #pragma unroll
         for (int e = 0; e < S::VE; ++e) {
             const int d = dl + e;
@@ -1318,14 +1363,14 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, int b, int j, int p
         }
     } else {
         // rows for K, columns for V
-        const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.kvk[b] + (hb + (long long)(tq % kPage) * D + dq * S::KVEC) * S::ES);
+        const u32x4 *kp = reinterpret_cast<const u32x4 *>(R.kvk + (hb + (long long)(tq % kPage) * D + dq * S::KVEC) * S::ES);
 #pragma unroll
         for (int c = 0; c < S::NKL; ++c) kr[c] = kp[4 * c];
         constexpr int NV = 16 * S::ES / 16;  // 16-byte loads per column run
 #pragma unroll
         for (int e = 0; e < S::VE; ++e) {
             const u32x4 *vp = reinterpret_cast<const u32x4 *>(
-                a.kvv[b] + (hb + (long long)(dl + e) * kPage + k0 % kPage) * S::ES);
+                R.kvv + (hb + (long long)(dl + e) * kPage + k0 % kPage) * S::ES);
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
                 const u32x4 t = vp[c];
@@ -1448,13 +1493,14 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     typedef AttnShape<D, KV> S;
     constexpr int NWV = kAttnWaves;
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    if (s >= a.nsplit[b]) return;
+    const AttnRow R = attn_row(a, b);
+    if (s >= R.nsplit) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lo = a.lo[b];
-    const int np = a.np[b], ns_b = a.nsplit[b];
-    const int kb = a.origin[b] + (int)((long long)s * np / ns_b) * kPage;
-    const int ke = min(a.origin[b] + (int)((long long)(s + 1) * np / ns_b) * kPage, a.pos[b] + 1);
+    const int lo = R.lo;
+    const int np = R.np, ns_b = R.nsplit;
+    const int kb = R.origin + (int)((long long)s * np / ns_b) * kPage;
+    const int ke = min(R.origin + (int)((long long)(s + 1) * np / ns_b) * kPage, R.pos + 1);
     const int kl = ke - 1;
 
     __shared__ __align__(16) float qs[G][D];
@@ -1466,7 +1512,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     // the split's pages, one chunk (= page) per lane, looked up once; chunk ci
     // past the split's last reads the last one (its loads are clamped there)
     const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
-    const int *ptb = a.pt[b] + kb / kPage;
+    const int *ptb = R.pt + kb / kPage;
     const int vpg = ptb[min(lane, nch - 1)];
     auto page_of = [&](int ci) -> int {
         ci = min(ci, nch - 1);
@@ -1474,7 +1520,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     };
     u32x4 kc[S::NKL], kn[S::NKL];
     typename S::vword vc[16], vn[16];
-    attn_load<D, KV>(a, b, j, page_of(0), kb + w * 16, lo, kl, kq, dq, lane, kc, vc);
+    attn_load<D, KV>(a, R, j, page_of(0), kb + w * 16, lo, kl, kq, dq, lane, kc, vc);
     {
         const f32x4 *q4 = reinterpret_cast<const f32x4 *>(a.q + (long long)b * a.Hq * D + (long long)(j * G) * D);
         for (int i = tid; i < G * D / 4; i += 256) {
@@ -1503,9 +1549,9 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
             const int k0 = c0 + w * 16;
             if constexpr (S::PREF) {
                 // next chunk in flight (clamped into the split past its end)
-                attn_load<D, KV>(a, b, j, page_of(ci + 1), k0 + kAttnChunk, lo, kl, kq, dq, lane, kn, vn);
+                attn_load<D, KV>(a, R, j, page_of(ci + 1), k0 + kAttnChunk, lo, kl, kq, dq, lane, kn, vn);
             } else if (c0 != kb) {
-                attn_load<D, KV>(a, b, j, page_of(ci), k0, lo, kl, kq, dq, lane, kc, vc);
+                attn_load<D, KV>(a, R, j, page_of(ci), k0, lo, kl, kq, dq, lane, kc, vc);
             }
             if (k0 + 15 >= lo && k0 < ke) attn_chunk<D, KV, G>(qs, pws[w], kc, vc, k0, lo, ke, kq, dq, m, l, acc);
             if constexpr (S::PREF) {
@@ -1528,7 +1574,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
             for (int e = 0; e < S::VE; ++e) wacc[w][g][lane * S::VE + e] = acc[g][e];
     lds_barrier();
 
-    const int ns = a.nsplit[b];
+    const int ns = R.nsplit;
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, d = idx % D;
         float M = wm[0][g];
@@ -1544,7 +1590,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
         if (ns == 1) {
             a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A / L;
         } else {
-            float *pp = a.part[b] + (((long long)j * a.s_cap[b] + s) * G + g) * (D + 4);
+            float *pp = R.part + (((long long)j * R.s_cap + s) * G + g) * (D + 4);
             if (d == 0) { pp[0] = M; pp[1] = L; }
             pp[4 + d] = A;
         }
@@ -1588,14 +1634,15 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     constexpr int KS = D / 32;  // 16x16x32 steps over d
     constexpr int DT = D / 16;  // 16-row output tiles over d
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    if (s >= a.nsplit[b]) return;
+    const AttnRow R = attn_row(a, b);
+    if (s >= R.nsplit) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
-    const int lo = a.lo[b];
-    const int np = a.np[b], ns_b = a.nsplit[b];
-    const int kb = a.origin[b] + (int)((long long)s * np / ns_b) * kPage;
-    const int ke = min(a.origin[b] + (int)((long long)(s + 1) * np / ns_b) * kPage, a.pos[b] + 1);
+    const int lo = R.lo;
+    const int np = R.np, ns_b = R.nsplit;
+    const int kb = R.origin + (int)((long long)s * np / ns_b) * kPage;
+    const int ke = min(R.origin + (int)((long long)(s + 1) * np / ns_b) * kPage, R.pos + 1);
     const int kl = ke - 1;
 
     __shared__ __align__(16) u32x4 qsh[3][KS][64];  // B operands of the query pieces, by lane
@@ -1604,7 +1651,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
 
     // the split's pages, one chunk (= page) per lane, looked up once
     const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
-    const int *ptb = a.pt[b] + kb / kPage;
+    const int *ptb = R.pt + kb / kPage;
     const int vpg = ptb[min(lane, nch - 1)];
     auto page_of = [&](int ci) -> int {
         ci = min(ci, nch - 1);
@@ -1614,9 +1661,9 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     // without a memory access, which is how chunks past the split are loaded
     constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) access
     const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(a.kvk[b]), (short)0, (int)a.kv_bytes[b], kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(R.kvk), (short)0, (int)R.kv_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(a.kvv[b]), (short)0, (int)a.kv_bytes[b], kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(R.kvv), (short)0, (int)R.kv_bytes, kRsrcWord3);
     auto load = [&](int ci, u32x4 (&kr)[KS], u32x2 (&vr)[DT]) {
         // the wave's 16-key group of the page's head block (16 * D elements of K and of V)
         const unsigned gb = (unsigned)((((long long)page_of(ci) * a.Hk + j) * kPage + w * 16) * D * 2);
@@ -1752,7 +1799,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
             for (int i = 0; i < 4; ++i) wacc[w][r16][dt * 16 + 4 * q4 + i] = acc[dt][i];
     lds_barrier();
 
-    const int ns = a.nsplit[b];
+    const int ns = R.nsplit;
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, d = idx % D;
         float M = wm[0][g];
@@ -1768,7 +1815,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
         if (ns == 1) {
             a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A / L;
         } else {
-            float *pp = a.part[b] + (((long long)j * a.s_cap[b] + s) * G + g) * (D + 4);
+            float *pp = R.part + (((long long)j * R.s_cap + s) * G + g) * (D + 4);
             if (d == 0) { pp[0] = M; pp[1] = L; }
             pp[4 + d] = A;
         }
@@ -1783,7 +1830,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
 // wave sums its splits' weighted outputs, and the four partial sums are added
 // in wave order.  Slots with one split were finished by k_attn.
 template <int D, int G, int NB>
-__device__ __forceinline__ void attn_merge_body(const AttnArgs &a, int h, int b, int ns) {
+__device__ __forceinline__ void attn_merge_body(const AttnArgs &a, const AttnRow &R, int h, int b, int ns) {
     constexpr int VE = D >= 64 ? D / 64 : 1;
     constexpr int VL = D / VE;
     constexpr int NWV = 4;
@@ -1791,7 +1838,7 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs &a, int h, int b,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = h / G, g = h % G;
     const long long stride = (long long)G * (D + 4);  // floats between consecutive splits
-    const float *base = a.part[b] + ((long long)j * a.s_cap[b] * G + g) * (D + 4);
+    const float *base = R.part + ((long long)j * R.s_cap * G + g) * (D + 4);
 
     __shared__ float fs[kMaxSplits];
     __shared__ float red[NWV][2];
@@ -1849,13 +1896,14 @@ __device__ __forceinline__ void attn_merge_body(const AttnArgs &a, int h, int b,
 template <int D, int G>
 __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
     const int h = blockIdx.x, b = blockIdx.y;
-    const int ns = a.nsplit[b];
+    const AttnRow R = attn_row(a, b);
+    const int ns = R.nsplit;
     if (ns <= 1) return;
     // per-wave split count, rounded up to one of three batch depths (block-uniform)
     const int nbw = (ns + 3) / 4;
-    if (nbw <= 4) attn_merge_body<D, G, 4>(a, h, b, ns);
-    else if (nbw <= 16) attn_merge_body<D, G, 16>(a, h, b, ns);
-    else attn_merge_body<D, G, kMaxSplits / 4>(a, h, b, ns);
+    if (nbw <= 4) attn_merge_body<D, G, 4>(a, R, h, b, ns);
+    else if (nbw <= 16) attn_merge_body<D, G, 16>(a, R, h, b, ns);
+    else attn_merge_body<D, G, kMaxSplits / 4>(a, R, h, b, ns);
 }
 
 }  // namespace pn

@@ -1000,6 +1000,11 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
 // Splits over K of one wide GEMM: doubled while the grid gives under two
 // work-groups per compute unit, every split keeps at least 8 k tiles and the
 // outputs fit the split buffer.
+// Attention splits per row on the wide path (the rows already give many work-groups).
+constexpr int kWideAttnSplits = 8;
+static_assert((long long)kWideRows * kWideAttnSplits <= (long long)kMaxSlots * kMaxSplits,
+              "the rows' split scratch fits the per-row attention buffer");
+
 int wide_splits(long long groups, int KT, long long floats_per_split, long long cap) {
     int ks = 1;
     while (ks < kWideSplitMax && groups * ks < 2 * kCUs && KT / (2 * ks) >= 8 && 2 * ks * floats_per_split <= cap)
@@ -1030,7 +1035,9 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
     g.KT = mat.KT;
     g.ldy = ldy;
     g.nsplit = ks;
-    const dim3 grid(cdiv(R, 128), cdiv(mat.n_tiles, 8), nz * ks);
+    g.nzs = nz * ks;
+    g.gx = cdiv(R, 128);
+    const dim3 grid((unsigned)(g.gx * cdiv(mat.n_tiles, 8) * g.nzs));
     if (m->pieces == 3) hipLaunchKernelGGL(k_wgemm<3>, grid, dim3(256), 0, s, g);
     else hipLaunchKernelGGL(k_wgemm<1>, grid, dim3(256), 0, s, g);
     return ks;
@@ -1082,25 +1089,22 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             hipLaunchKernelGGL(k_w_qkv, dim3(R), dim3(256), 0, s, w);
             if (int rc = launched("wide QKV")) return rc;
         }
-        // ---- attention, kMaxSlots rows per launch (each row sees keys up to its own position)
-        for (int r0 = 0; r0 < R; r0 += kMaxSlots) {
-            const int n = std::min(kMaxSlots, R - r0);
-            pn_state *sts[kMaxSlots];
-            int pos[kMaxSlots];
-            for (int b = 0; b < n; ++b) {
-                sts[b] = st;
-                pos[b] = p0 + r0 + b;
-            }
+        // ---- attention: one launch over the chunk's rows (each row sees keys up to its own position)
+        {
             AttnArgs aa{};
-            const int nsm = attn_setup(m, sts, n, pos, true, aa);
-            aa.q = q + (size_t)r0 * HD;
-            aa.o = o + (size_t)r0 * HD;
-            for (int b = 0; b < n; ++b) {
-                aa.kvk[b] = kvk;
-                aa.kvv[b] = kvv;
-            }
+            attn_setup(m, &st, 1, &p0, true, aa);  // scale, and slot 0's pages, table and scratch
+            aa.q = q;
+            aa.o = o;
+            aa.kvk[0] = kvk;
+            aa.kvv[0] = kvv;
+            aa.rows = R;
+            aa.p0 = p0;
+            aa.window = c.sliding_window;
+            aa.ns_rows = (int)std::max(1LL, std::min((long long)kWideAttnSplits, 1024LL / ((long long)R * m->Hk)));
+            aa.s_cap[0] = kWideAttnSplits;
+            aa.part_row = (long long)m->Hk * kWideAttnSplits * m->G * (m->D + 4);
             aa.kind = m->attn_kind == 1 ? 0 : 1;
-            launch_attn(m->D, m->kvt, m->G, aa, dim3(nsm, m->Hk, n), nsm > 1, s);
+            launch_attn(m->D, m->kvt, m->G, aa, dim3(aa.ns_rows, m->Hk, R), aa.ns_rows > 1, s);
             if (int rc = launched("wide attention")) return rc;
         }
         // ---- O + residual

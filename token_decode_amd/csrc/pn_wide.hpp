@@ -24,8 +24,11 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 //   A: planes [P][rows][lda] bf16, lda >= KT*32, zero from K up to lda.
 //   Y: split s, matrix z at y[z] + s * y_split, [r][ldy] fp32; rows < R and
 //      n < N are written.
-// grid: x = 128-row group of A, y = 128-row group of W (8 tiles), z =
-// matrix * nsplit + split; 256 threads.  Wave w computes weight tiles
+// grid: one dimension, work-group id = (W group * A groups + A group) * nzs +
+// zs, with zs = matrix * nsplit + split varying fastest: work-groups are
+// dealt to the XCDs in id order, so with 8 (or 4) values of zs each XCD's L2
+// holds the A slice of one split instead of all of A; a W group is 8 tiles
+// (128 rows), an A group 128 rows; 256 threads.  Wave w computes weight tiles
 // 4*(w & 1) .. +3 against row tiles 4*(w >> 1) .. +3 of the group (16
 // accumulators); each k step loads its 4 weight fragments and 4*P row
 // fragments, the next step's loads in flight while this step's 16*P matrix
@@ -38,16 +41,19 @@ struct WGemmArgs {
     const uint16_t *a;
     long long a_plane;  // elements between the planes of A
     int lda, R, N, n_tiles, KT, ldy, nsplit;
+    int nzs, gx;  // matrices * nsplit; A groups
 };
 
 template <int P>
 __global__ void __launch_bounds__(256) k_wgemm(WGemmArgs g) {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int z = blockIdx.z / g.nsplit, s = blockIdx.z % g.nsplit;
+    const int id = blockIdx.x, zs = id % g.nzs, rest = id / g.nzs;
+    const int gxi = rest % g.gx, gyi = rest / g.gx;
+    const int z = zs / g.nsplit, s = zs % g.nsplit;
     const int kt0 = (int)((long long)s * g.KT / g.nsplit), kt1 = (int)((long long)(s + 1) * g.KT / g.nsplit);
-    const int wt0 = blockIdx.y * 8 + 4 * (wv & 1);  // first weight tile of the wave
-    const int rt0 = blockIdx.x * 8 + 4 * (wv >> 1);  // first row tile of the wave
+    const int wt0 = gyi * 8 + 4 * (wv & 1);  // first weight tile of the wave
+    const int rt0 = gxi * 8 + 4 * (wv >> 1);  // first row tile of the wave
     if (wt0 >= g.n_tiles || rt0 * 16 >= g.R) return;  // (no barriers below)
     const uint8_t *wp[4];
     const uint16_t *ap[4];

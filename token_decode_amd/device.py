@@ -243,7 +243,8 @@ def forward_batch(model, states, tokens_dev, logits_dev=None, argmax_dev=None, s
 
 
 def prefill(model, state, tokens_dev, logits_dev=None, argmax_dev=None, stream=None):
-    """Feed tokens_dev [n] to the state at consecutive positions (chunks of max_batch)."""
+    """Feed tokens_dev [n] to the state at consecutive positions (chunks of max_batch, or of
+    prefill_chunk rows on the wide path)."""
     C.check(C.lib().pn_prefill(model.h, state.h, _ptr(tokens_dev), int(tokens_dev.numel()), _ptr(logits_dev),
                                _ptr(argmax_dev), _stream_ptr(stream)))
 
