@@ -1086,7 +1086,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             w.kvk = kvk;
             w.kvv = kvv;
             w.pt = (const int *)(st->base + st->pt);
-            hipLaunchKernelGGL(k_w_qkv, dim3(R), dim3(256), 0, s, w);
+            hipLaunchKernelGGL(k_w_qkv, dim3(cdiv(m->Nqkv / 2, 256), R), dim3(256), 0, s, w);
             if (int rc = launched("wide QKV")) return rc;
         }
         // ---- attention: one launch over the chunk's rows (each row sees keys up to its own position)
@@ -1108,12 +1108,12 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             if (int rc = launched("wide attention")) return rc;
         }
         // ---- O + residual
-        if (bf) hipLaunchKernelGGL(k_w_conv<AT_BF16>, dim3(R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
-        else hipLaunchKernelGGL(k_w_conv<AT_F32>, dim3(R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+        if (bf) hipLaunchKernelGGL(k_w_conv<AT_BF16>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+        else hipLaunchKernelGGL(k_w_conv<AT_F32>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
         {
             const int ld = L.o.n_tiles * 16;
             const int ks = wide_gemm(m, L.o, (const uint8_t *)(mb + L.o.off), nullptr, y, nullptr, 1, R, ld, ld, true, s);
-            hipLaunchKernelGGL(k_w_resid, dim3(R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
+            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
             if (int rc = launched("wide O")) return rc;
         }
         // ---- gate/up, SwiGLU, down + residual
@@ -1125,10 +1125,10 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             const int ks = wide_gemm(m, L.gate, (const uint8_t *)(mb + L.gate.off), (const uint8_t *)(mb + L.up.off),
                                      y, yu, 2, R, ld, ld, fits, s);
             if (bf)
-                hipLaunchKernelGGL(k_w_swiglu<AT_BF16>, dim3(R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
+                hipLaunchKernelGGL(k_w_swiglu<AT_BF16>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
                                    m->wa_plane, m->wlda);
             else
-                hipLaunchKernelGGL(k_w_swiglu<AT_F32>, dim3(R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
+                hipLaunchKernelGGL(k_w_swiglu<AT_F32>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
                                    m->wa_plane, m->wlda);
             if (int rc = launched("wide gate/up")) return rc;
         }
@@ -1136,7 +1136,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             const int ld = L.down.n_tiles * 16;
             const int ks = wide_gemm(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, y, nullptr, 1, R, ld, ld,
                                      true, s);
-            hipLaunchKernelGGL(k_w_resid, dim3(R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
+            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
             if (int rc = launched("wide down")) return rc;
         }
     }

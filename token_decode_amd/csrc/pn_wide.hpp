@@ -155,56 +155,99 @@ __global__ void __launch_bounds__(256) k_w_embed(const uint16_t *embd, const int
     for (int k = threadIdx.x; k < E; k += 256) x[(long long)r * E + k] = __uint_as_float((uint32_t)src[k] << 16);
 }
 
-// Row r of A = round_act(RMSNorm(x[r]) * gain) as MFMA planes (AReady
-// layout of bf16 weights), zero from K to lda.  grid: rows; 256 threads.
+// Row kernels: grid (column blocks, rows) with 256 threads and four
+// consecutive columns per thread (one pass, every load issued up front),
+// except the norm, which reduces its row first.
+
+// Columns c .. c+3 of row r of A as MFMA planes (AReady layout of bf16
+// weights: three bf16 pieces of an fp32 value, or its bf16 rounding).
 template <int AT>
-__global__ void __launch_bounds__(256) k_w_norm(const float *x, int K, const float *gain, float eps, uint16_t *a,
-                                                 long long a_plane, int lda) {
+__device__ __forceinline__ void wide_put4(uint16_t *a, long long plane, long long idx, const float (&v)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) AReady<WT_BF16, AT>::store(a, plane, idx + e, v[e]);
+}
+
+// Row r of A = round_act(RMSNorm(x[r]) * gain), zero from K to lda.  grid:
+// rows; 256 threads; the row is read in batches of 8 loads per thread.
+template <int AT>
+__global__ void __launch_bounds__(256) k_w_norm(const float *__restrict__ x, int K, const float *__restrict__ gain,
+                                                 float eps, uint16_t *__restrict__ a, long long a_plane, int lda) {
     __shared__ float red[4];
     const int r = blockIdx.x, tid = threadIdx.x;
     const float *xr = x + (long long)r * K;
     float ss = 0.f;
-    for (int k = tid; k < K; k += 256) ss += xr[k] * xr[k];
+    for (int k0 = 0; k0 < K; k0 += 256 * 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = k0 + tid + 256 * u;
+            v[u] = k < K ? xr[k] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ss += v[u] * v[u];
+    }
     ss = block_sum<4>(ss, red);
     const float ri = 1.0f / sqrtf(ss / (float)K + eps);
-    for (int k = tid; k < lda; k += 256) {
-        const float v = k < K ? (xr[k] * ri) * gain[k] : 0.f;
-        AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, v);
+    for (int k0 = 0; k0 < lda; k0 += 256 * 8) {
+        float v[8], gv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = k0 + tid + 256 * u;
+            v[u] = k < K ? xr[k] : 0.f;
+            gv[u] = k < K ? gain[k] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = k0 + tid + 256 * u;
+            if (k < lda) AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, (v[u] * ri) * gv[u]);
+        }
     }
 }
 
 // Row r of A = round_act(src[r]) (fp32 rows of ld K), zero from K to lda.
+// grid: (cdiv(lda, 1024), rows).
 template <int AT>
-__global__ void __launch_bounds__(256) k_w_conv(const float *src, int K, uint16_t *a, long long a_plane, int lda) {
-    const int r = blockIdx.x;
-    for (int k = threadIdx.x; k < lda; k += 256)
-        AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, k < K ? src[(long long)r * K + k] : 0.f);
+__global__ void __launch_bounds__(256) k_w_conv(const float *__restrict__ src, int K, uint16_t *__restrict__ a,
+                                                 long long a_plane, int lda) {
+    const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= lda) return;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = c + e < K ? src[(long long)r * K + c + e] : 0.f;
+    wide_put4<AT>(a, a_plane, (long long)r * lda + c, v);
 }
 
 // h = silu(gate) * up from the split outputs of the gate / up products, as the
-// down projection's A planes (zero from F to lda).
+// down projection's A planes (zero from F to lda).  grid: (cdiv(lda, 1024), rows).
 template <int AT>
-__global__ void __launch_bounds__(256) k_w_swiglu(const float *yg, const float *yu, long long split, int nsplit,
-                                                   int ldy, int F, uint16_t *a, long long a_plane, int lda) {
-    const int r = blockIdx.x;
-    for (int k = threadIdx.x; k < lda; k += 256) {
-        float h = 0.f;
-        if (k < F) {
-            const long long i = (long long)r * ldy + k;
-            const float gt = wide_sum(yg, split, nsplit, i);
-            const float up = wide_sum(yu, split, nsplit, i);
-            h = (gt / (1.0f + expf(-gt))) * up;
-        }
-        AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, h);
+__global__ void __launch_bounds__(256) k_w_swiglu(const float *__restrict__ yg, const float *__restrict__ yu,
+                                                   long long split, int nsplit, int ldy, int F,
+                                                   uint16_t *__restrict__ a, long long a_plane, int lda) {
+    const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= lda) return;
+    float gt[4], up[4], h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const long long i = (long long)r * ldy + min(c + e, F - 1);
+        gt[e] = wide_sum(yg, split, nsplit, i);
+        up[e] = wide_sum(yu, split, nsplit, i);
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = c + e < F ? (gt[e] / (1.0f + expf(-gt[e]))) * up[e] : 0.f;
+    wide_put4<AT>(a, a_plane, (long long)r * lda + c, h);
 }
 
-// x[r] += y[r] (summed over the splits).
-__global__ void __launch_bounds__(256) k_w_resid(float *x, const float *y, long long split, int nsplit, int ldy,
-                                                  int E) {
-    const int r = blockIdx.x;
-    for (int k = threadIdx.x; k < E; k += 256)
-        x[(long long)r * E + k] += wide_sum(y, split, nsplit, (long long)r * ldy + k);
+// x[r] += y[r] (summed over the splits).  grid: (cdiv(E, 1024), rows).
+__global__ void __launch_bounds__(256) k_w_resid(float *__restrict__ x, const float *__restrict__ y, long long split,
+                                                  int nsplit, int ldy, int E) {
+    const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= E) return;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = wide_sum(y, split, nsplit, (long long)r * ldy + min(c + e, E - 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (c + e < E) x[(long long)r * E + c + e] += v[e];
 }
 
 struct WQkvArgs {
@@ -223,13 +266,15 @@ struct WQkvArgs {
 // Per row r at position p0 + r and adjacent pair (2i, 2i+1) of the QKV rows:
 // bias, RoPE on q and k by the angle (p0 + r) * omega_(pair in head), whose
 // sine and cosine are taken in fp64 and rounded to fp32, then q into q[r] and
-// k, v into the cache (layouts as kv_k_off / kv_v_off).  grid: rows; 256 threads.
+// k, v into the cache (layouts as kv_k_off / kv_v_off).  grid: (cdiv(pairs,
+// 256), rows); 256 threads, a pair each.
 __global__ void __launch_bounds__(256) k_w_qkv(WQkvArgs g) {
-    const int r = blockIdx.x, pos = g.p0 + r;
+    const int r = blockIdx.y, pos = g.p0 + r;
     const int hd = g.Hq * g.D, kd = g.Hk * g.D;
     const int page = g.pt[pos / kPage], t = pos % kPage;
     const bool tiled = g.kv_es == 2;
-    for (int i = threadIdx.x; i < (hd + 2 * kd) / 2; i += 256) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < (hd + 2 * kd) / 2) {
         const int r0 = 2 * i;
         const long long yi = (long long)r * g.ldy + r0;
         float y0 = wide_sum(g.y, g.split, g.nsplit, yi), y1 = wide_sum(g.y, g.split, g.nsplit, yi + 1);
@@ -247,7 +292,7 @@ __global__ void __launch_bounds__(256) k_w_qkv(WQkvArgs g) {
         if (r0 < hd) {
             g.q[(long long)r * hd + r0] = y0;
             g.q[(long long)r * hd + r0 + 1] = y1;
-            continue;
+            return;
         }
         const int rr = isv ? r0 - hd - kd : r0 - hd;
         const int j = rr / g.D, dd = rr % g.D;
