@@ -1038,9 +1038,25 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
     g.nzs = nz * ks;
     g.gx = cdiv(R, 128);
     const dim3 grid((unsigned)(g.gx * cdiv(mat.n_tiles, 8) * g.nzs));
-    if (m->pieces == 3) hipLaunchKernelGGL(k_wgemm<3>, grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL(k_wgemm<1>, grid, dim3(256), 0, s, g);
+    const int pi = m->pieces == 3 ? 1 : 0;
+    const size_t lds = (size_t)wgemm_lds(m->pieces);  // (attribute set by wide_lds_attr)
+    if (pi) hipLaunchKernelGGL(k_wgemm<3>, grid, dim3(256), lds, s, g);
+    else hipLaunchKernelGGL(k_wgemm<1>, grid, dim3(256), lds, s, g);
     return ks;
+}
+
+// The wide GEMMs' LDS ring is dynamic and passes 64 KiB: raise the limit
+// once per kernel.
+int wide_lds_attr() {
+    static bool done = false;
+    if (done) return PN_OK;
+    for (int p : {1, 3}) {
+        const void *fn = p == 3 ? reinterpret_cast<const void *>(&k_wgemm<3>) : reinterpret_cast<const void *>(&k_wgemm<1>);
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, wgemm_lds(p));
+        if (e != hipSuccess) return fail(PN_EHIP, "wide GEMM LDS attribute: %s", hipGetErrorString(e));
+    }
+    done = true;
+    return PN_OK;
 }
 
 // One chunk of R rows of state st at positions st->pos .. st->pos + R - 1
@@ -1060,6 +1076,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         if (bf) hipLaunchKernelGGL(k_w_norm<AT_BF16>, dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane, m->wlda);
         else hipLaunchKernelGGL(k_w_norm<AT_F32>, dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane, m->wlda);
     };
+    if (int rc = wide_lds_attr()) return rc;
     hipLaunchKernelGGL(k_w_embed, dim3(R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E, m->V, err);
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerOff &L = m->L[l];

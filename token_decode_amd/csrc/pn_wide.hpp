@@ -30,10 +30,11 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 // holds the A slice of one split instead of all of A; a W group is 8 tiles
 // (128 rows), an A group 128 rows; 256 threads.  Wave w computes weight tiles
 // 4*(w & 1) .. +3 against row tiles 4*(w >> 1) .. +3 of the group (16
-// accumulators); each k step loads its 4 weight fragments and 4*P row
-// fragments, the next step's loads in flight while this step's 16*P matrix
-// steps run.  Tiles past n_tiles and rows past R load clamped (in bounds)
-// and are not stored.
+// accumulators).  A k step's 8 weight and 8*P row fragments (1 KiB each)
+// go from memory straight into a ring of LDS stages (each wave loads a quarter
+// of them); S - 1 steps are in flight while the work-group computes one, at
+// one barrier per step, so the loads in flight take no registers.  Tiles past
+// n_tiles and rows past R load clamped (in bounds) and are not stored.
 struct WGemmArgs {
     const uint8_t *w[2];
     float *y[2];
@@ -44,69 +45,108 @@ struct WGemmArgs {
     int nzs, gx;  // matrices * nsplit; A groups
 };
 
+// Stages of the LDS ring: fp32 activations (three planes) take 32 KiB per k
+// step, bf16 ones 16 KiB; either way 128 KiB in all.
+__host__ __device__ constexpr int wgemm_stages(int P) { return P == 3 ? 4 : 8; }
+__host__ __device__ constexpr int wgemm_frags(int P) { return 8 + 8 * P; }  // 1 KiB fragments per k step
+__host__ __device__ constexpr int wgemm_lds(int P) { return wgemm_stages(P) * wgemm_frags(P) * 1024; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS (lane i's at dst +
+// 16*i), and the wait for all but the newest n of this wave's loads and for
+// its LDS reads, then the work-group barrier.  Their bodies exist only in the
+// device pass (the host compiler has neither the instruction nor the asm).
+__device__ __forceinline__ void lds_dma16(const void *src, lds_void *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+#endif
+}
+__device__ __forceinline__ void wait_vm_all() {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
 template <int P>
-__global__ void __launch_bounds__(256) k_wgemm(WGemmArgs g) {
+__global__ void __launch_bounds__(256, 1) k_wgemm(WGemmArgs g) {
+    constexpr int S = wgemm_stages(P), FR = wgemm_frags(P), LPW = FR / 4;
+    extern __shared__ __align__(16) uint8_t ring[];  // [S][FR][1 KiB]: W tiles 0..7, then A [row tile][plane]
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int id = blockIdx.x, zs = id % g.nzs, rest = id / g.nzs;
     const int gxi = rest % g.gx, gyi = rest / g.gx;
     const int z = zs / g.nsplit, s = zs % g.nsplit;
     const int kt0 = (int)((long long)s * g.KT / g.nsplit), kt1 = (int)((long long)(s + 1) * g.KT / g.nsplit);
-    const int wt0 = gyi * 8 + 4 * (wv & 1);  // first weight tile of the wave
-    const int rt0 = gxi * 8 + 4 * (wv >> 1);  // first row tile of the wave
-    if (wt0 >= g.n_tiles || rt0 * 16 >= g.R) return;  // (no barriers below)
-    const uint8_t *wp[4];
-    const uint16_t *ap[4];
+    const int wt0 = gyi * 8 + 4 * (wv & 1);  // first weight tile the wave computes
+    const int rt0 = gxi * 8 + 4 * (wv >> 1);  // first row tile the wave computes
+    // The wave loads fragments wv*LPW .. +LPW-1 of every stage: a W tile
+    // (clamped to the matrix) or a (row tile, plane) of A (rows clamped to R).
+    const uint8_t *src[LPW];
+    int stride[LPW];  // bytes per k step
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wp[i] = g.w[z] + (long long)min(wt0 + i, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
-        const int r = min((rt0 + i) * 16 + (lane & 15), g.R - 1);
-        ap[i] = g.a + (long long)r * g.lda + 8 * (lane >> 4);
+    for (int q = 0; q < LPW; ++q) {
+        const int f = wv * LPW + q;
+        if (f < 8) {
+            src[q] = g.w[z] + (long long)min(gyi * 8 + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
+            stride[q] = 1024;
+        } else {
+            const int rt = (f - 8) / P, p = (f - 8) % P;
+            const int r = min((gxi * 8 + rt) * 16 + (lane & 15), g.R - 1);
+            src[q] = reinterpret_cast<const uint8_t *>(g.a + p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4));
+            stride[q] = 64;
+        }
     }
+    auto issue = [&](int kt, int slot) {  // every call issues LPW loads (k steps past the split re-read the last)
+        kt = min(kt, kt1 - 1);
+#pragma unroll
+        for (int q = 0; q < LPW; ++q)
+            lds_dma16(src[q] + (long long)kt * stride[q], (lds_void *)(ring + (slot * FR + wv * LPW + q) * 1024));
+    };
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 wa[4], wb[4], aa[4][P], ab[4][P];
-    auto load = [&](int kt, u32x4 (&wr)[4], u32x4 (&ar)[4][P]) {
-        kt = min(kt, kt1 - 1);
+    // (every split has at least one k step)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp[i] + (long long)kt * 1024));
+    for (int st = 0; st < S - 1; ++st) issue(kt0 + st, st);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int slot = (kt - kt0) % S;
+        // this wave's loads of step kt have landed (S - 2 later steps may be
+        // in flight) and its reads of the previous step are done; then every
+        // wave's: the barrier
+        wait_vm_barrier<(S - 2) * LPW>();
+        u32x4 wf[4], af[4][P];
+        const uint8_t *base = ring + slot * FR * 1024 + lane * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4 *>(base + (4 * (wv & 1) + i) * 1024);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int p = 0; p < P; ++p)
-                ar[j][p] = *reinterpret_cast<const u32x4 *>(ap[j] + p * g.a_plane + (long long)kt * 32);
-    };
-    auto step = [&](const u32x4 (&wr)[4], const u32x4 (&ar)[4][P]) {
+                af[j][p] = *reinterpret_cast<const u32x4 *>(base + (8 + (4 * (wv >> 1) + j) * P + p) * 1024);
+        // the slot of step kt - 1: every wave has read it (it passed the barrier)
+        issue(kt + S - 1, (kt - kt0 + S - 1) % S);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int p = 0; p < P; ++p)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[i]),
-                                                                        __builtin_bit_cast(bf16x8, ar[j][p]),
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[i]),
+                                                                        __builtin_bit_cast(bf16x8, af[j][p]),
                                                                         acc[i][j], 0, 0, 0);
-    };
-    // (the scheduling barriers keep each step's loads issued ahead of the
-    // previous step's matrix-core work instead of sunk next to their use)
-    if (kt0 < kt1) {
-        load(kt0, wa, aa);
-        for (int kt = kt0; kt < kt1; kt += 2) {
-            load(kt + 1, wb, ab);
-            __builtin_amdgcn_sched_barrier(0);
-            step(wa, aa);
-            __builtin_amdgcn_sched_barrier(0);
-            load(kt + 2, wa, aa);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < kt1) step(wb, ab);
-            __builtin_amdgcn_sched_barrier(0);
-        }
     }
+    wait_vm_all();  // the clamped tail loads land before the work-group ends
+    if (wt0 >= g.n_tiles) return;
     // lane l holds rows 4*(l >> 4) .. +3 of weight tile i (outputs n) for A row (l & 15) of row tile j
     float *y = g.y[z] + (long long)s * g.y_split;
     const bool vec = (g.ldy & 3) == 0;
