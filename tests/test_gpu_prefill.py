@@ -171,3 +171,51 @@ def test_wide_llama3_shape():
     prompt = list(synth.uniform_int(wl.seed, 98, 40, 0, wl.n_vocab - 1))
     worst, near = run_prefill(p, 100, prompt, 1)
     log("  wide, Llama-3-8B shape, 40 tokens from 100: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_wide_one_row_then_full_chunk():
+    """Chunks of 256 rows: a 1-row prefill (one row tile, clamped loads), then
+    300 tokens (a full 256-row chunk over two row groups, then 44 rows)."""
+    wl = ragged("wide-256", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.F32, seed=88)
+    p = Pair(wl, max_batch=1, prefill_chunk=256)
+    prompt = list(synth.uniform_int(wl.seed, 99, 301, 0, wl.n_vocab - 1))
+    import torch
+    from token_decode_amd import device as dv
+    ds, os_ = p.states(0, 0, 400)
+    worst = 0.0
+    for part in (prompt[:1], prompt[1:]):
+        toks = torch.tensor(part, dtype=torch.int32, device="cuda")
+        lg = torch.empty(len(part), wl.n_vocab, dtype=torch.float32, device="cuda")
+        am = torch.empty(len(part), dtype=torch.int32, device="cuda")
+        dv.prefill(p.dm, ds, toks, lg, am)
+        g, ga = lg.cpu().numpy(), am.cpu().numpy()
+        for t, tok in enumerate(part):
+            ol, oa = os_.step(int(tok))
+            from harness import compare_step
+            rel, _ = compare_step(wl, g[t], ol, int(ga[t]), oa, "row %d:" % t)
+            worst = max(worst, rel)
+    assert ds.pos == 301
+    log("  wide, 1 row then 256 + 44 rows: worst rel L2 %.2e" % worst)
+
+
+def test_wide_bad_token_sets_the_flag():
+    """An id outside the vocabulary reads row 0 of the embedding and sets the
+    state's token flag, as on the decode path; the flag clears on reading."""
+    import torch
+    from token_decode_amd import device as dv
+    wl = ragged("wide-badtok", w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.BF16, seed=89)
+    p = Pair(wl, max_batch=1, prefill_chunk=32)
+    ds = dv.DeviceState(p.dm, 100)
+    toks = torch.tensor([3, 5, wl.n_vocab, 7], dtype=torch.int32, device="cuda")
+    am = torch.empty(4, dtype=torch.int32, device="cuda")
+    lg = torch.empty(4, wl.n_vocab, dtype=torch.float32, device="cuda")
+    dv.prefill(p.dm, ds, toks, lg, am)
+    assert ds.check_flags() & 1
+    assert ds.check_flags() == 0
+    assert ds.pos == 4
+    # the same chunk with token 0 in its place gives the same logits bit for bit
+    d0 = dv.DeviceState(p.dm, 100)
+    lg0 = torch.empty(4, wl.n_vocab, dtype=torch.float32, device="cuda")
+    dv.prefill(p.dm, d0, torch.tensor([3, 5, 0, 7], dtype=torch.int32, device="cuda"), lg0, None)
+    assert d0.check_flags() == 0
+    assert lg.cpu().numpy().tobytes() == lg0.cpu().numpy().tobytes()
