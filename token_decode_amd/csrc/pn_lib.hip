@@ -1040,8 +1040,8 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
     const dim3 grid((unsigned)(g.gx * cdiv(mat.n_tiles, 8) * g.nzs));
     const int pi = m->pieces == 3 ? 1 : 0;
     const size_t lds = (size_t)wgemm_lds(m->pieces);  // (attribute set by wide_lds_attr)
-    if (pi) hipLaunchKernelGGL(k_wgemm<3>, grid, dim3(256), lds, s, g);
-    else hipLaunchKernelGGL(k_wgemm<1>, grid, dim3(256), lds, s, g);
+    if (pi) hipLaunchKernelGGL(k_wgemm<3>, grid, dim3(512), lds, s, g);
+    else hipLaunchKernelGGL(k_wgemm<1>, grid, dim3(512), lds, s, g);
     return ks;
 }
 

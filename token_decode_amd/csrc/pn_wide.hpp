@@ -28,10 +28,11 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 // zs, with zs = matrix * nsplit + split varying fastest: work-groups are
 // dealt to the XCDs in id order, so with 8 (or 4) values of zs each XCD's L2
 // holds the A slice of one split instead of all of A; a W group is 8 tiles
-// (128 rows), an A group 128 rows; 256 threads.  Wave w computes weight tiles
-// 4*(w & 1) .. +3 against row tiles 4*(w >> 1) .. +3 of the group (16
+// (128 rows), an A group 128 rows; 512 threads (two waves per SIMD: one
+// computes while the other waits on LDS).  Wave w computes weight tiles
+// 4*(w & 1) .. +3 against row tiles 2*(w >> 1), +1 of the group (8
 // accumulators).  A k step's 8 weight and 8*P row fragments (1 KiB each)
-// go from memory straight into a ring of LDS stages (each wave loads a quarter
+// go from memory straight into a ring of LDS stages (each wave loads an eighth
 // of them); S - 1 steps are in flight while the work-group computes one, at
 // one barrier per step, so the loads in flight take no registers.  Tiles past
 // n_tiles and rows past R load clamped (in bounds) and are not stored.
@@ -75,8 +76,8 @@ __device__ __forceinline__ void wait_vm_all() {
 }
 
 template <int P>
-__global__ void __launch_bounds__(256, 1) k_wgemm(WGemmArgs g) {
-    constexpr int S = wgemm_stages(P), FR = wgemm_frags(P), LPW = FR / 4;
+__global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
+    constexpr int S = wgemm_stages(P), FR = wgemm_frags(P), LPW = FR / 8;
     extern __shared__ __align__(16) uint8_t ring[];  // [S][FR][1 KiB]: W tiles 0..7, then A [row tile][plane]
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(256, 1) k_wgemm(WGemmArgs g) {
     const int z = zs / g.nsplit, s = zs % g.nsplit;
     const int kt0 = (int)((long long)s * g.KT / g.nsplit), kt1 = (int)((long long)(s + 1) * g.KT / g.nsplit);
     const int wt0 = gyi * 8 + 4 * (wv & 1);  // first weight tile the wave computes
-    const int rt0 = gxi * 8 + 4 * (wv >> 1);  // first row tile the wave computes
+    const int rt0 = gxi * 8 + 2 * (wv >> 1);  // first row tile the wave computes
     // The wave loads fragments wv*LPW .. +LPW-1 of every stage: a W tile
     // (clamped to the matrix) or a (row tile, plane) of A (rows clamped to R).
     const uint8_t *src[LPW];
@@ -109,11 +110,11 @@ __global__ void __launch_bounds__(256, 1) k_wgemm(WGemmArgs g) {
         for (int q = 0; q < LPW; ++q)
             lds_dma16(src[q] + (long long)kt * stride[q], (lds_void *)(ring + (slot * FR + wv * LPW + q) * 1024));
     };
-    f32x4 acc[4][4];
+    f32x4 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // (every split has at least one k step)
 #pragma unroll
@@ -124,21 +125,21 @@ __global__ void __launch_bounds__(256, 1) k_wgemm(WGemmArgs g) {
         // in flight) and its reads of the previous step are done; then every
         // wave's: the barrier
         wait_vm_barrier<(S - 2) * LPW>();
-        u32x4 wf[4], af[4][P];
+        u32x4 wf[4], af[2][P];
         const uint8_t *base = ring + slot * FR * 1024 + lane * 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4 *>(base + (4 * (wv & 1) + i) * 1024);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int p = 0; p < P; ++p)
-                af[j][p] = *reinterpret_cast<const u32x4 *>(base + (8 + (4 * (wv >> 1) + j) * P + p) * 1024);
+                af[j][p] = *reinterpret_cast<const u32x4 *>(base + (8 + (2 * (wv >> 1) + j) * P + p) * 1024);
         // the slot of step kt - 1: every wave has read it (it passed the barrier)
         issue(kt + S - 1, (kt - kt0 + S - 1) % S);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int p = 0; p < P; ++p)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[i]),
@@ -151,7 +152,7 @@ __global__ void __launch_bounds__(256, 1) k_wgemm(WGemmArgs g) {
     float *y = g.y[z] + (long long)s * g.y_split;
     const bool vec = (g.ldy & 3) == 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
         const int r = (rt0 + j) * 16 + (lane & 15);
         if (r >= g.R) continue;
 #pragma unroll
