@@ -219,3 +219,24 @@ def test_wide_bad_token_sets_the_flag():
     dv.prefill(p.dm, d0, torch.tensor([3, 5, 0, 7], dtype=torch.int32, device="cuda"), lg0, None)
     assert d0.check_flags() == 0
     assert lg.cpu().numpy().tobytes() == lg0.cpu().numpy().tobytes()
+
+
+def test_wide_int8_weights():
+    """INT8 weights (per-row scales, f16 matrix-core steps over the widened
+    codes, the scale applied to each output row) with bf16 activations, chunks
+    of 64 over 150 tokens from a cache written up to 40."""
+    wl = ragged("wide-int8", w_dtype=synth.I8, kv_dtype=synth.BF16, act_dtype=synth.BF16, seed=90)
+    p = Pair(wl, max_batch=1, prefill_chunk=64)
+    prompt = list(synth.uniform_int(wl.seed, 100, 150, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 40, prompt, 2)
+    log("  wide, int8 weights, 150 tokens from 40: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_wide_int8_llama3_shape():
+    """Llama-3-8B layer shape with INT8 weights (2 layers, full vocabulary),
+    32 prompt tokens in one chunk after a 60-token cache."""
+    wl = synth.WORKLOADS["llama3-8b-int8"]().with_(name="wide-llama3-int8-2l", n_layer=2, seed=91)
+    p = Pair(wl, max_batch=1, prefill_chunk=32)
+    prompt = list(synth.uniform_int(wl.seed, 101, 32, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 60, prompt, 1)
+    log("  wide, Llama-3-8B int8, 32 tokens from 60: worst rel L2 %.2e, near %d" % (worst, near))

@@ -281,8 +281,9 @@ int check_config_n(const pn_config *c) {
         return fail(PN_EUNSUPPORTED, "a Q4 KV cache quantises k in natural dim order: no NeoX RoPE");
     if (c->prefill_chunk < 0 || c->prefill_chunk > kWideRows)
         return fail(PN_EINVAL, "prefill_chunk must be in [0, %d]", kWideRows);
-    if (c->prefill_chunk > 0 && (c->w_dtype != PN_BF16 || c->n_expert > 0 || c->kv_dtype == PN_Q4_0))
-        return fail(PN_EUNSUPPORTED, "the wide prefill path needs bf16 weights, no experts and an fp32 or bf16 cache");
+    if (c->prefill_chunk > 0 && ((c->w_dtype != PN_BF16 && c->w_dtype != PN_I8) || c->n_expert > 0 ||
+                                 c->kv_dtype == PN_Q4_0))
+        return fail(PN_EUNSUPPORTED, "the wide prefill path needs bf16 or int8 weights, no experts and an fp32 or bf16 cache");
     const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
@@ -387,7 +388,7 @@ size_t layout_model(pn_model *m) {
     // (wide prefill runs its attention 16 rows at a time, each with its own split scratch)
     m->attn_part = bp.take((size_t)std::max(MB, C > 0 ? kMaxSlots : 0) * m->attn_part_row);
     if (C > 0) {
-        m->wlda = cdiv(std::max(m->E, std::max(HD, m->F)), 32) * 32;
+        m->wlda = cdiv(std::max(m->E, std::max(HD, m->F)), tile_k(wt)) * tile_k(wt);
         m->wa_plane = (long long)C * m->wlda;
         m->wx = bp.take((size_t)C * m->E * 4);
         m->wa = bp.take((size_t)m->pieces * m->wa_plane * 2);
@@ -1014,15 +1015,27 @@ int wide_splits(long long groups, int KT, long long floats_per_split, long long 
 
 // Y = A * W^T for R rows of the A planes: nz matrices (1, or 2 for gate and
 // up) with outputs y[z] [split][R][ldy]; returns the number of splits used.
-int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_t *w1, float *y0, float *y1, int nz,
-              int R, int N, int ldy, bool split_ok, hipStream_t s) {
-    static_assert(tile_k(WT_BF16) == 32, "bf16 tiles hold 32 k");
+// The wide GEMM kernel of the model's weight and activation types: 0 = bf16
+// weights with bf16 rows, 1 = bf16 weights with fp32 rows (three pieces), 2 =
+// int8 weights (f16 rows).
+int wide_variant(const pn_model *m) { return m->wt == PN_I8 ? 2 : (m->pieces == 3 ? 1 : 0); }
+const void *wide_kernel(int v) {
+    return v == 2 ? reinterpret_cast<const void *>(&k_wgemm<WT_I8, 1>)
+                  : v == 1 ? reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 3>)
+                           : reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 1>);
+}
+int wide_lds(int v) { return v == 2 ? wgemm_lds(WT_I8, 1) : v == 1 ? wgemm_lds(WT_BF16, 3) : wgemm_lds(WT_BF16, 1); }
+
+int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_t *w1, const float *s0,
+              const float *s1, float *y0, float *y1, int nz, int R, int N, int ldy, bool split_ok, hipStream_t s) {
     const long long groups = (long long)cdiv(R, 128) * cdiv(mat.n_tiles, 8) * nz;
     const long long per = (long long)R * ldy;
     const int ks = split_ok ? wide_splits(groups, mat.KT, per * nz, m->wy_cap) : 1;
     WGemmArgs g{};
     g.w[0] = w0;
     g.w[1] = w1 ? w1 : w0;
+    g.sc[0] = s0;
+    g.sc[1] = s1 ? s1 : s0;
     g.y[0] = y0;
     g.y[1] = y1 ? y1 : y0;
     g.y_split = per;
@@ -1038,10 +1051,11 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
     g.nzs = nz * ks;
     g.gx = cdiv(R, 128);
     const dim3 grid((unsigned)(g.gx * cdiv(mat.n_tiles, 8) * g.nzs));
-    const int pi = m->pieces == 3 ? 1 : 0;
-    const size_t lds = (size_t)wgemm_lds(m->pieces);  // (attribute set by wide_lds_attr)
-    if (pi) hipLaunchKernelGGL(k_wgemm<3>, grid, dim3(512), lds, s, g);
-    else hipLaunchKernelGGL(k_wgemm<1>, grid, dim3(512), lds, s, g);
+    const int v = wide_variant(m);
+    const size_t lds = (size_t)wide_lds(v);  // (attribute set by wide_lds_attr)
+    if (v == 2) hipLaunchKernelGGL((k_wgemm<WT_I8, 1>), grid, dim3(512), lds, s, g);
+    else if (v == 1) hipLaunchKernelGGL((k_wgemm<WT_BF16, 3>), grid, dim3(512), lds, s, g);
+    else hipLaunchKernelGGL((k_wgemm<WT_BF16, 1>), grid, dim3(512), lds, s, g);
     return ks;
 }
 
@@ -1050,9 +1064,8 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
 int wide_lds_attr() {
     static bool done = false;
     if (done) return PN_OK;
-    for (int p : {1, 3}) {
-        const void *fn = p == 3 ? reinterpret_cast<const void *>(&k_wgemm<3>) : reinterpret_cast<const void *>(&k_wgemm<1>);
-        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, wgemm_lds(p));
+    for (int v = 0; v < 3; ++v) {
+        const hipError_t e = hipFuncSetAttribute(wide_kernel(v), hipFuncAttributeMaxDynamicSharedMemorySize, wide_lds(v));
         if (e != hipSuccess) return fail(PN_EHIP, "wide GEMM LDS attribute: %s", hipGetErrorString(e));
     }
     done = true;
@@ -1072,10 +1085,20 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
     uint16_t *a = (uint16_t *)(mb + m->wa);
     int *err = (int *)(st->base + st->err);
     const float eps = c.rms_norm_eps;
+    const int var = wide_variant(m);
+    const bool i8 = var == 2;
     auto norm = [&](const float *gain) {
-        if (bf) hipLaunchKernelGGL(k_w_norm<AT_BF16>, dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane, m->wlda);
-        else hipLaunchKernelGGL(k_w_norm<AT_F32>, dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane, m->wlda);
+        if (i8)
+            hipLaunchKernelGGL((k_w_norm<WT_I8, AT_BF16>), dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane,
+                               m->wlda);
+        else if (bf)
+            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_BF16>), dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane,
+                               m->wlda);
+        else
+            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_F32>), dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane,
+                               m->wlda);
     };
+    auto scales = [&](const Mat &mt) { return i8 ? (const float *)(mb + mt.soff) : nullptr; };
     if (int rc = wide_lds_attr()) return rc;
     hipLaunchKernelGGL(k_w_embed, dim3(R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E, m->V, err);
     for (int l = 0; l < c.n_layer; ++l) {
@@ -1085,7 +1108,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         norm((const float *)(mb + L.attn_norm));
         {
             const int ld = L.qkv.n_tiles * 16;
-            const int ks = wide_gemm(m, L.qkv, (const uint8_t *)(mb + L.qkv.off), nullptr, y, nullptr, 1, R, ld, ld,
+            const int ks = wide_gemm(m, L.qkv, (const uint8_t *)(mb + L.qkv.off), nullptr, scales(L.qkv), nullptr, y, nullptr, 1, R, ld, ld,
                                      true, s);
             WQkvArgs w{};
             w.y = y;
@@ -1125,11 +1148,15 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             if (int rc = launched("wide attention")) return rc;
         }
         // ---- O + residual
-        if (bf) hipLaunchKernelGGL(k_w_conv<AT_BF16>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
-        else hipLaunchKernelGGL(k_w_conv<AT_F32>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+        {
+            const dim3 gc(cdiv(m->wlda, 1024), R);
+            if (i8) hipLaunchKernelGGL((k_w_conv<WT_I8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+            else if (bf) hipLaunchKernelGGL((k_w_conv<WT_BF16, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+            else hipLaunchKernelGGL((k_w_conv<WT_BF16, AT_F32>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+        }
         {
             const int ld = L.o.n_tiles * 16;
-            const int ks = wide_gemm(m, L.o, (const uint8_t *)(mb + L.o.off), nullptr, y, nullptr, 1, R, ld, ld, true, s);
+            const int ks = wide_gemm(m, L.o, (const uint8_t *)(mb + L.o.off), nullptr, scales(L.o), nullptr, y, nullptr, 1, R, ld, ld, true, s);
             hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
             if (int rc = launched("wide O")) return rc;
         }
@@ -1140,18 +1167,23 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             float *yu = y + m->wy_cap / 2;  // (2 matrices x at most 2 splits of R x ld fit each half)
             const bool fits = 2LL * 2 * R * ld <= m->wy_cap;
             const int ks = wide_gemm(m, L.gate, (const uint8_t *)(mb + L.gate.off), (const uint8_t *)(mb + L.up.off),
-                                     y, yu, 2, R, ld, ld, fits, s);
-            if (bf)
-                hipLaunchKernelGGL(k_w_swiglu<AT_BF16>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
+                                     scales(L.gate), scales(L.up), y, yu, 2, R, ld, ld, fits, s);
+            const dim3 gs(cdiv(m->wlda, 1024), R);
+            const long long sp = (long long)R * ld;
+            if (i8)
+                hipLaunchKernelGGL((k_w_swiglu<WT_I8, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a, m->wa_plane,
+                                   m->wlda);
+            else if (bf)
+                hipLaunchKernelGGL((k_w_swiglu<WT_BF16, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a,
                                    m->wa_plane, m->wlda);
             else
-                hipLaunchKernelGGL(k_w_swiglu<AT_F32>, dim3(cdiv(m->wlda, 1024), R), dim3(256), 0, s, y, yu, (long long)R * ld, ks, ld, F, a,
+                hipLaunchKernelGGL((k_w_swiglu<WT_BF16, AT_F32>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a,
                                    m->wa_plane, m->wlda);
             if (int rc = launched("wide gate/up")) return rc;
         }
         {
             const int ld = L.down.n_tiles * 16;
-            const int ks = wide_gemm(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, y, nullptr, 1, R, ld, ld,
+            const int ks = wide_gemm(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, scales(L.down), nullptr, y, nullptr, 1, R, ld, ld,
                                      true, s);
             hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
             if (int rc = launched("wide down")) return rc;
@@ -1162,7 +1194,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         norm((const float *)(mb + m->out_norm));
         float *lg = logits ? logits : y;
         const int ld = logits ? m->V : m->out.n_tiles * 16;
-        wide_gemm(m, m->out, (const uint8_t *)(mb + m->out.off), nullptr, lg, nullptr, 1, R, m->V, ld, false, s);
+        wide_gemm(m, m->out, (const uint8_t *)(mb + m->out.off), nullptr, scales(m->out), nullptr, lg, nullptr, 1, R, m->V, ld, false, s);
         if (amax) hipLaunchKernelGGL(k_w_argmax, dim3(R), dim3(256), 0, s, lg, (long long)ld, m->V, amax, err);
         if (int rc = launched("wide LM head")) return rc;
     }

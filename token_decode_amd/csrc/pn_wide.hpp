@@ -38,6 +38,7 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 // n_tiles and rows past R load clamped (in bounds) and are not stored.
 struct WGemmArgs {
     const uint8_t *w[2];
+    const float *sc[2];  // int8 weights: the rows' scales (padded to tiles), else null
     float *y[2];
     long long y_split;  // floats between the splits' outputs
     const uint16_t *a;
@@ -46,11 +47,14 @@ struct WGemmArgs {
     int nzs, gx;  // matrices * nsplit; A groups
 };
 
+// Row fragments per row tile and k step: the P bf16 planes, or for int8
+// weights (64-wide tiles, f16 rows) the two 32-wide halves of the step.
+__host__ __device__ constexpr int wgemm_na(int WT, int P) { return WT == WT_I8 ? 2 : P; }
 // Stages of the LDS ring: fp32 activations (three planes) take 32 KiB per k
-// step, bf16 ones 16 KiB; either way 128 KiB in all.
-__host__ __device__ constexpr int wgemm_stages(int P) { return P == 3 ? 4 : 8; }
-__host__ __device__ constexpr int wgemm_frags(int P) { return 8 + 8 * P; }  // 1 KiB fragments per k step
-__host__ __device__ constexpr int wgemm_lds(int P) { return wgemm_stages(P) * wgemm_frags(P) * 1024; }
+// step, bf16 ones 16 KiB, int8 weights 24 KiB; 120-128 KiB in all.
+__host__ __device__ constexpr int wgemm_stages(int WT, int P) { return WT == WT_I8 ? 5 : (P == 3 ? 4 : 8); }
+__host__ __device__ constexpr int wgemm_frags(int WT, int P) { return 8 + 8 * wgemm_na(WT, P); }  // 1 KiB each
+__host__ __device__ constexpr int wgemm_lds(int WT, int P) { return wgemm_stages(WT, P) * wgemm_frags(WT, P) * 1024; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -75,9 +79,10 @@ __device__ __forceinline__ void wait_vm_all() {
 #endif
 }
 
-template <int P>
+template <int WT, int P>
 __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
-    constexpr int S = wgemm_stages(P), FR = wgemm_frags(P), LPW = FR / 8;
+    constexpr int NA = wgemm_na(WT, P), TK = tile_k(WT);
+    constexpr int S = wgemm_stages(WT, P), FR = wgemm_frags(WT, P), LPW = FR / 8;
     extern __shared__ __align__(16) uint8_t ring[];  // [S][FR][1 KiB]: W tiles 0..7, then A [row tile][plane]
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -98,10 +103,13 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
             src[q] = g.w[z] + (long long)min(gyi * 8 + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
             stride[q] = 1024;
         } else {
-            const int rt = (f - 8) / P, p = (f - 8) % P;
+            // bf16: plane p, k 8*(l >> 4) of the step; int8: half p, k 16*(l >> 4) + 8p
+            const int rt = (f - 8) / NA, p = (f - 8) % NA;
             const int r = min((gxi * 8 + rt) * 16 + (lane & 15), g.R - 1);
-            src[q] = reinterpret_cast<const uint8_t *>(g.a + p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4));
-            stride[q] = 64;
+            const long long e = WT == WT_I8 ? (long long)r * g.lda + 16 * (lane >> 4) + 8 * p
+                                            : p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4);
+            src[q] = reinterpret_cast<const uint8_t *>(g.a + e);
+            stride[q] = TK * 2;
         }
     }
     auto issue = [&](int kt, int slot) {  // every call issues LPW loads (k steps past the split re-read the last)
@@ -125,26 +133,49 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
         // in flight) and its reads of the previous step are done; then every
         // wave's: the barrier
         wait_vm_barrier<(S - 2) * LPW>();
-        u32x4 wf[4], af[2][P];
+        u32x4 wf[4], af[2][NA];
         const uint8_t *base = ring + slot * FR * 1024 + lane * 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4 *>(base + (4 * (wv & 1) + i) * 1024);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-                af[j][p] = *reinterpret_cast<const u32x4 *>(base + (8 + (2 * (wv >> 1) + j) * P + p) * 1024);
+            for (int p = 0; p < NA; ++p)
+                af[j][p] = *reinterpret_cast<const u32x4 *>(base + (8 + (2 * (wv >> 1) + j) * NA + p) * 1024);
         // the slot of step kt - 1: every wave has read it (it passed the barrier)
         issue(kt + S - 1, (kt - kt0 + S - 1) % S);
+        if constexpr (WT == WT_I8) {
+            // biased codes u = q + 128 -> f16 (1024 + u) by a byte permute; minus 1152 leaves q
+            const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                u32x4 b[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04010400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04030402u);
+                    b[c >> 1][2 * (c & 1)] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
+                    b[c >> 1][2 * (c & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
+                }
 #pragma unroll
-                for (int p = 0; p < P; ++p)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[i]),
-                                                                        __builtin_bit_cast(bf16x8, af[j][p]),
-                                                                        acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, b[h]),
+                                                                           __builtin_bit_cast(f16x8, af[j][h]),
+                                                                           acc[i][j], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[i]),
+                                                                            __builtin_bit_cast(bf16x8, af[j][p]),
+                                                                            acc[i][j], 0, 0, 0);
+        }
     }
     wait_vm_all();  // the clamped tail loads land before the work-group ends
     if (wt0 >= g.n_tiles) return;
@@ -159,12 +190,16 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
         for (int i = 0; i < 4; ++i) {
             const int n0 = (wt0 + i) * 16 + 4 * (lane >> 4);
             float *yp = y + (long long)r * g.ldy + n0;
+            f32x4 v = acc[i][j];
+            if constexpr (WT == WT_I8) {  // the rows' scales (a table padded to whole tiles)
+                if (wt0 + i < g.n_tiles) v = v * *reinterpret_cast<const f32x4 *>(g.sc[z] + n0);
+            }
             if (vec && n0 + 3 < g.N) {
-                *reinterpret_cast<f32x4 *>(yp) = acc[i][j];
+                *reinterpret_cast<f32x4 *>(yp) = v;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (n0 + e < g.N) yp[e] = acc[i][j][e];
+                    if (n0 + e < g.N) yp[e] = v[e];
             }
         }
     }
@@ -202,15 +237,16 @@ __global__ void __launch_bounds__(256) k_w_embed(const uint16_t *embd, const int
 
 // Columns c .. c+3 of row r of A as MFMA planes (AReady layout of bf16
 // weights: three bf16 pieces of an fp32 value, or its bf16 rounding).
-template <int AT>
+template <int WT, int AT>
 __device__ __forceinline__ void wide_put4(uint16_t *a, long long plane, long long idx, const float (&v)[4]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) AReady<WT_BF16, AT>::store(a, plane, idx + e, v[e]);
+    for (int e = 0; e < 4; ++e) AReady<WT, AT>::store(a, plane, idx + e, v[e]);
 }
 
 // Row r of A = round_act(RMSNorm(x[r]) * gain), zero from K to lda.  grid:
 // rows; 256 threads; the row is read in batches of 8 loads per thread.
-template <int AT>
+// (WT, AT: the layout of AReady - bf16 pieces or planes, or f16 rows for int8 weights.)
+template <int WT, int AT>
 __global__ void __launch_bounds__(256) k_w_norm(const float *__restrict__ x, int K, const float *__restrict__ gain,
                                                  float eps, uint16_t *__restrict__ a, long long a_plane, int lda) {
     __shared__ float red[4];
@@ -240,14 +276,14 @@ __global__ void __launch_bounds__(256) k_w_norm(const float *__restrict__ x, int
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int k = k0 + tid + 256 * u;
-            if (k < lda) AReady<WT_BF16, AT>::store(a, a_plane, (long long)r * lda + k, (v[u] * ri) * gv[u]);
+            if (k < lda) AReady<WT, AT>::store(a, a_plane, (long long)r * lda + k, (v[u] * ri) * gv[u]);
         }
     }
 }
 
 // Row r of A = round_act(src[r]) (fp32 rows of ld K), zero from K to lda.
 // grid: (cdiv(lda, 1024), rows).
-template <int AT>
+template <int WT, int AT>
 __global__ void __launch_bounds__(256) k_w_conv(const float *__restrict__ src, int K, uint16_t *__restrict__ a,
                                                  long long a_plane, int lda) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -255,12 +291,12 @@ __global__ void __launch_bounds__(256) k_w_conv(const float *__restrict__ src, i
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = c + e < K ? src[(long long)r * K + c + e] : 0.f;
-    wide_put4<AT>(a, a_plane, (long long)r * lda + c, v);
+    wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, v);
 }
 
 // h = silu(gate) * up from the split outputs of the gate / up products, as the
 // down projection's A planes (zero from F to lda).  grid: (cdiv(lda, 1024), rows).
-template <int AT>
+template <int WT, int AT>
 __global__ void __launch_bounds__(256) k_w_swiglu(const float *__restrict__ yg, const float *__restrict__ yu,
                                                    long long split, int nsplit, int ldy, int F,
                                                    uint16_t *__restrict__ a, long long a_plane, int lda) {
@@ -275,7 +311,7 @@ __global__ void __launch_bounds__(256) k_w_swiglu(const float *__restrict__ yg, 
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = c + e < F ? (gt[e] / (1.0f + expf(-gt[e]))) * up[e] : 0.f;
-    wide_put4<AT>(a, a_plane, (long long)r * lda + c, h);
+    wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, h);
 }
 
 // x[r] += y[r] (summed over the splits).  grid: (cdiv(E, 1024), rows).
