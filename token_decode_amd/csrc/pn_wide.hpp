@@ -8,7 +8,7 @@
 // each projection as one matrix product on the matrix cores (k_wgemm), with
 // the steps around it as plain row kernels: RMSNorm into MFMA-ready planes,
 // RoPE + K/V append, SwiGLU, the residual add and the per-row argmax.  Dense
-// models with bf16 weights and an fp32 or bf16 cache take this path.
+// models with bf16 or int8 weights and an fp32 or bf16 cache take this path.
 #pragma once
 #include "pn_kernels.hpp"
 
@@ -18,10 +18,13 @@ constexpr int kWideRows = 256;   // most rows of one wide chunk
 constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 
 // Y_s[r][n] = sum over k in split s of A[r][k] * W[n][k], for the P planes of
-// A (the bf16 pieces whose sum is the fp32 input, or one bf16 plane).
-//   W: packed bf16 tiles [n_tiles][KT][1 KiB]; tile = 16 rows x 32 k, lane l
-//      holds row l & 15, k 8*(l >> 4) .. +7 (the 16x16x32 operand layout).
-//   A: planes [P][rows][lda] bf16, lda >= KT*32, zero from K up to lda.
+// A (the bf16 pieces whose sum is the fp32 input, or one bf16 plane); int8
+// weights: times the row scale sc[n].
+//   W: packed tiles [n_tiles][KT][1 KiB]; bf16: 16 rows x 32 k, lane l holds
+//      row l & 15, k 8*(l >> 4) .. +7 (the 16x16x32 operand layout); int8:
+//      16 rows x 64 k of biased codes, lane l row l & 15, k 16*(l >> 4) .. +15.
+//   A: planes [P][rows][lda] bf16 (int8 weights: one plane of f16), lda >=
+//      KT * tile width, zero from K up to lda.
 //   Y: split s, matrix z at y[z] + s * y_split, [r][ldy] fp32; rows < R and
 //      n < N are written.
 // grid: one dimension, work-group id = (W group * A groups + A group) * nzs +
@@ -31,7 +34,7 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 // (128 rows), an A group 128 rows; 512 threads (two waves per SIMD: one
 // computes while the other waits on LDS).  Wave w computes weight tiles
 // 4*(w & 1) .. +3 against row tiles 2*(w >> 1), +1 of the group (8
-// accumulators).  A k step's 8 weight and 8*P row fragments (1 KiB each)
+// accumulators).  A k step's 8 weight and 8*NA row fragments (1 KiB each)
 // go from memory straight into a ring of LDS stages (each wave loads an eighth
 // of them); S - 1 steps are in flight while the work-group computes one, at
 // one barrier per step, so the loads in flight take no registers.  Tiles past
