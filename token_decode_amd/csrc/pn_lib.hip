@@ -91,7 +91,7 @@ struct pn_model {
     // wide prefill (prefill_chunk > 0): one chunk's rows.  x [C][E], A planes
     // [pieces][C][wlda] bf16, GEMM split outputs (wy_cap floats), q and the
     // attention output [C][H*D]
-    size_t wx = 0, wa = 0, wy = 0, wq = 0, wo = 0;
+    size_t wx = 0, wa = 0, wy = 0, wq = 0, wo = 0, wss = 0;
     long long wa_plane = 0, wy_cap = 0;
     int wlda = 0;
     size_t o_bytes = 0, h_bytes = 0, am_count = 0;
@@ -281,6 +281,8 @@ int check_config_n(const pn_config *c) {
         return fail(PN_EUNSUPPORTED, "a Q4 KV cache quantises k in natural dim order: no NeoX RoPE");
     if (c->prefill_chunk < 0 || c->prefill_chunk > kWideRows)
         return fail(PN_EINVAL, "prefill_chunk must be in [0, %d]", kWideRows);
+    if (c->prefill_chunk > 0 && c->n_embd > 1024 * kWideSsq)
+        return fail(PN_EUNSUPPORTED, "the wide prefill path takes n_embd up to %d", 1024 * kWideSsq);
     if (c->prefill_chunk > 0 && ((c->w_dtype != PN_BF16 && c->w_dtype != PN_I8) || c->n_expert > 0 ||
                                  c->kv_dtype == PN_Q4_0))
         return fail(PN_EUNSUPPORTED, "the wide prefill path needs bf16 or int8 weights, no experts and an fp32 or bf16 cache");
@@ -391,6 +393,7 @@ size_t layout_model(pn_model *m) {
         m->wlda = cdiv(std::max(m->E, std::max(HD, m->F)), tile_k(wt)) * tile_k(wt);
         m->wa_plane = (long long)C * m->wlda;
         m->wx = bp.take((size_t)C * m->E * 4);
+        m->wss = bp.take((size_t)C * kWideSsq * 4);
         m->wa = bp.take((size_t)m->pieces * m->wa_plane * 2);
         m->wq = bp.take((size_t)C * HD * 4);
         m->wo = bp.take((size_t)C * HD * 4);
@@ -1087,20 +1090,23 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
     const float eps = c.rms_norm_eps;
     const int var = wide_variant(m);
     const bool i8 = var == 2;
+    float *ssq = (float *)(mb + m->wss);
     auto norm = [&](const float *gain) {
+        const dim3 gn(cdiv(m->wlda, 1024), R);
         if (i8)
-            hipLaunchKernelGGL((k_w_norm<WT_I8, AT_BF16>), dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane,
+            hipLaunchKernelGGL((k_w_norm<WT_I8, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
                                m->wlda);
         else if (bf)
-            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_BF16>), dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane,
+            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
                                m->wlda);
         else
-            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_F32>), dim3(R), dim3(256), 0, s, x, E, gain, eps, a, m->wa_plane,
+            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_F32>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
                                m->wlda);
     };
     auto scales = [&](const Mat &mt) { return i8 ? (const float *)(mb + mt.soff) : nullptr; };
     if (int rc = wide_lds_attr()) return rc;
-    hipLaunchKernelGGL(k_w_embed, dim3(R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E, m->V, err);
+    hipLaunchKernelGGL(k_w_embed, dim3(cdiv(E, 1024), R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E,
+                       m->V, err, ssq);
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerOff &L = m->L[l];
         char *kvk = kv_layer(st, l, false), *kvv = kv_layer(st, l, true);
@@ -1157,7 +1163,8 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         {
             const int ld = L.o.n_tiles * 16;
             const int ks = wide_gemm(m, L.o, (const uint8_t *)(mb + L.o.off), nullptr, scales(L.o), nullptr, y, nullptr, 1, R, ld, ld, true, s);
-            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
+            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E,
+                               ssq);
             if (int rc = launched("wide O")) return rc;
         }
         // ---- gate/up, SwiGLU, down + residual
@@ -1185,7 +1192,8 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             const int ld = L.down.n_tiles * 16;
             const int ks = wide_gemm(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, scales(L.down), nullptr, y, nullptr, 1, R, ld, ld,
                                      true, s);
-            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E);
+            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E,
+                               ssq);
             if (int rc = launched("wide down")) return rc;
         }
     }

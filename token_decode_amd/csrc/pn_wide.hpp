@@ -220,18 +220,41 @@ __device__ __forceinline__ float wide_sum(const float *y, long long split, int n
     return t;
 }
 
+// Sums of squares of x per row and 1024-column block, [row][kWideSsq]: written
+// by the kernels that write x, read by the norm in block order.
+constexpr int kWideSsq = 8;  // blocks per row (E <= 8192)
+
+// The sum over the work-group (256 threads) of one value per thread, in a
+// fixed order: within each wave, then the four waves' sums in wave order.
+__device__ __forceinline__ float wide_block_sum(float v) {
+    __shared__ float red[4];
+    return block_sum<4>(v, red);
+}
+
 // x[r] = tok_embd[token[r]] (bf16 table); a bad id uses row 0 and sets a flag.
-// grid: rows; 256 threads.
-__global__ void __launch_bounds__(256) k_w_embed(const uint16_t *embd, const int *tokens, float *x, int E, int V,
-                                                  int *err) {
-    const int r = blockIdx.x;
+// Also the row's block sums of squares.  grid: (cdiv(E, 1024), rows); 256
+// threads, four columns each.
+__global__ void __launch_bounds__(256) k_w_embed(const uint16_t *__restrict__ embd, const int *__restrict__ tokens,
+                                                  float *__restrict__ x, int E, int V, int *err,
+                                                  float *__restrict__ ssq) {
+    const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
     int tok = tokens[r];
     if (tok < 0 || tok >= V) {
-        if (threadIdx.x == 0) atomicOr(err, ERR_TOKEN);
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err, ERR_TOKEN);
         tok = 0;
     }
     const uint16_t *src = embd + (long long)tok * E;
-    for (int k = threadIdx.x; k < E; k += 256) x[(long long)r * E + k] = __uint_as_float((uint32_t)src[k] << 16);
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (c + e < E) {
+            const float v = __uint_as_float((uint32_t)src[c + e] << 16);
+            x[(long long)r * E + c + e] = v;
+            sq += v * v;
+        }
+    }
+    sq = wide_block_sum(sq);
+    if (threadIdx.x == 0) ssq[r * kWideSsq + blockIdx.x] = sq;
 }
 
 // Row kernels: grid (column blocks, rows) with 256 threads and four
@@ -246,42 +269,24 @@ __device__ __forceinline__ void wide_put4(uint16_t *a, long long plane, long lon
     for (int e = 0; e < 4; ++e) AReady<WT, AT>::store(a, plane, idx + e, v[e]);
 }
 
-// Row r of A = round_act(RMSNorm(x[r]) * gain), zero from K to lda.  grid:
-// rows; 256 threads; the row is read in batches of 8 loads per thread.
-// (WT, AT: the layout of AReady - bf16 pieces or planes, or f16 rows for int8 weights.)
+// Row r of A = round_act(RMSNorm(x[r]) * gain), zero from K to lda, the
+// row's sum of squares added from its block sums in block order.  grid:
+// (cdiv(lda, 1024), rows).  (WT, AT: the layout of AReady - bf16 pieces or
+// planes, or f16 rows for int8 weights.)
 template <int WT, int AT>
 __global__ void __launch_bounds__(256) k_w_norm(const float *__restrict__ x, int K, const float *__restrict__ gain,
-                                                 float eps, uint16_t *__restrict__ a, long long a_plane, int lda) {
-    __shared__ float red[4];
-    const int r = blockIdx.x, tid = threadIdx.x;
-    const float *xr = x + (long long)r * K;
+                                                 float eps, const float *__restrict__ ssq, uint16_t *__restrict__ a,
+                                                 long long a_plane, int lda) {
+    const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= lda) return;
+    const int nb = (K + 1023) / 1024;
     float ss = 0.f;
-    for (int k0 = 0; k0 < K; k0 += 256 * 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int k = k0 + tid + 256 * u;
-            v[u] = k < K ? xr[k] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ss += v[u] * v[u];
-    }
-    ss = block_sum<4>(ss, red);
+    for (int i = 0; i < nb; ++i) ss += ssq[r * kWideSsq + i];
     const float ri = 1.0f / sqrtf(ss / (float)K + eps);
-    for (int k0 = 0; k0 < lda; k0 += 256 * 8) {
-        float v[8], gv[8];
+    float v[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int k = k0 + tid + 256 * u;
-            v[u] = k < K ? xr[k] : 0.f;
-            gv[u] = k < K ? gain[k] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int k = k0 + tid + 256 * u;
-            if (k < lda) AReady<WT, AT>::store(a, a_plane, (long long)r * lda + k, (v[u] * ri) * gv[u]);
-        }
-    }
+    for (int e = 0; e < 4; ++e) v[e] = c + e < K ? (x[(long long)r * K + c + e] * ri) * gain[c + e] : 0.f;
+    wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, v);
 }
 
 // Row r of A = round_act(src[r]) (fp32 rows of ld K), zero from K to lda.
@@ -317,17 +322,27 @@ __global__ void __launch_bounds__(256) k_w_swiglu(const float *__restrict__ yg, 
     wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, h);
 }
 
-// x[r] += y[r] (summed over the splits).  grid: (cdiv(E, 1024), rows).
+// x[r] += y[r] (summed over the splits), and the new row's block sums of
+// squares.  grid: (cdiv(E, 1024), rows).
 __global__ void __launch_bounds__(256) k_w_resid(float *__restrict__ x, const float *__restrict__ y, long long split,
-                                                  int nsplit, int ldy, int E) {
+                                                  int nsplit, int ldy, int E, float *__restrict__ ssq) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (c >= E) return;
-    float v[4];
+    float sq = 0.f;
+    if (c < E) {
+        float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = wide_sum(y, split, nsplit, (long long)r * ldy + min(c + e, E - 1));
+        for (int e = 0; e < 4; ++e) v[e] = wide_sum(y, split, nsplit, (long long)r * ldy + min(c + e, E - 1));
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (c + e < E) x[(long long)r * E + c + e] += v[e];
+        for (int e = 0; e < 4; ++e) {
+            if (c + e < E) {
+                const float xn = x[(long long)r * E + c + e] + v[e];
+                x[(long long)r * E + c + e] = xn;
+                sq += xn * xn;
+            }
+        }
+    }
+    sq = wide_block_sum(sq);  // (every thread takes part: no early return above)
+    if (threadIdx.x == 0) ssq[r * kWideSsq + blockIdx.x] = sq;
 }
 
 struct WQkvArgs {
