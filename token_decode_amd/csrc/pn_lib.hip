@@ -1001,19 +1001,30 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
 
 // ---- wide prefill: the rows of one chunk through each projection at once
 
-// Splits over K of one wide GEMM: doubled while the grid gives under two
-// work-groups per compute unit, every split keeps at least 8 k tiles and the
-// outputs fit the split buffer.
 // Attention splits per row on the wide path (the rows already give many work-groups).
 constexpr int kWideAttnSplits = 8;
 static_assert((long long)kWideRows * kWideAttnSplits <= (long long)kMaxSlots * kMaxSplits,
               "the rows' split scratch fits the per-row attention buffer");
 
+// Splits over K of one wide GEMM.  The kernel runs one work-group per compute
+// unit (its LDS ring), so the grid should fill whole rounds of kCUs: the
+// fewest splits (1, 2, 4, 8) that give at least one round at 95% or better
+// of whole rounds, else the best such fraction; every split keeps at least 8
+// k tiles and the outputs fit the split buffer.
 int wide_splits(long long groups, int KT, long long floats_per_split, long long cap) {
-    int ks = 1;
-    while (ks < kWideSplitMax && groups * ks < 2 * kCUs && KT / (2 * ks) >= 8 && 2 * ks * floats_per_split <= cap)
-        ks *= 2;
-    return ks;
+    int best = 1;
+    double best_f = -1.0;
+    for (int ks = 1; ks <= kWideSplitMax; ks *= 2) {
+        if (ks > 1 && (KT / ks < 8 || ks * floats_per_split > cap)) break;
+        const long long n = groups * ks;
+        const double f = (double)n / (double)(cdiv(n, (long long)kCUs) * kCUs);
+        if (n >= kCUs && f >= 0.95) return ks;
+        if (f > best_f + 1e-9) {
+            best_f = f;
+            best = ks;
+        }
+    }
+    return best;
 }
 
 // Y = A * W^T for R rows of the A planes: nz matrices (1, or 2 for gate and
