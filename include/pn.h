@@ -378,6 +378,23 @@ int pn_profile_end(pn_model *m, void *stream, double *total_ms, int64_t *launche
  * created, or a state of the recorded step was freed since). */
 int pn_profile_replay(pn_model *m, int32_t kernel, int32_t reps, void *stream);
 
+/* Routing record of an MoE model, for measurement (the bytes of a step's
+ * expert FFN are those of the experts its rows chose).  With log_dev non-NULL,
+ * decode call i (pn_forward_step or pn_forward_batch, counted from this call)
+ * writes the experts each layer chose for each row into
+ * log_dev[i % n_steps][n_layer][max_batch][n_expert_used] (int32, device,
+ * caller-owned; rows past the call's n are not written), in the router kernel
+ * itself (no extra launch).  NULL turns it off.  Errors: PN_EINVAL (NULL
+ * model, a dense model, n_steps < 1). */
+int pn_model_route_log(pn_model *m, int32_t *log_dev, int32_t n_steps);
+
+/* Streaming read ceiling, for measurement: read `bytes` (a positive multiple
+ * of 16) of device memory at src_dev (16-byte aligned) with 16-byte loads
+ * spread over every compute unit, and xor them into *sink_dev (one device
+ * word, caller-owned).  Its achieved bandwidth is the measured read ceiling
+ * that the decode kernels' HBM rates are set against.  Errors: PN_EINVAL. */
+int pn_stream_read(const void *src_dev, size_t bytes, uint32_t *sink_dev, void *stream);
+
 /* Message of the last failure on this thread ("" if none). */
 const char *pn_last_error(void);
 

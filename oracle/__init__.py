@@ -86,6 +86,14 @@ def lib():
         L.orc_state_set_kv.restype = i32
         L.orc_step.argtypes = [P(Config), vp, vp, i32, vp, i32, vp, vp]
         L.orc_step.restype = i32
+        L.orc_step_ex.argtypes = [P(Config), vp, vp, i32, vp, i32, vp, vp, vp, ctypes.c_uint64]
+        L.orc_step_ex.restype = i32
+        L.orc_round_store.argtypes = [dbl, i32]
+        L.orc_round_store.restype = dbl
+        L.orc_set_perturbation.argtypes = [dbl, ctypes.c_uint64]
+        L.orc_set_perturbation.restype = None
+        L.orc_moe_route_swapped.argtypes = [vp, i32, i32, vp, vp]
+        L.orc_moe_route_swapped.restype = dbl
         L.orc_full_recompute.argtypes = [P(Config), vp, vp, i32, vp, i32]
         L.orc_full_recompute.restype = i32
         L.orc_max_threads.argtypes = []
@@ -185,6 +193,26 @@ def argmax(logits):
     return lib().orc_argmax(_ptr(logits), logits.size)
 
 
+def round_store(v, dt):
+    """v as the oracle stores a value of type dt (fp32, or bf16 through fp32)."""
+    return lib().orc_round_store(float(v), int(dt))
+
+
+def set_perturbation(eps, seed=1):
+    """Sensitivity probe: multiply every value about to be stored as bf16 by
+    (1 + eps*u), u uniform in [-1, 1); eps = 0 turns it off."""
+    lib().orc_set_perturbation(float(eps), int(seed))
+
+
+def moe_route_swapped(r, k):
+    """Top-k routing with the (k+1)-th expert in the k-th one's place."""
+    r = _f64(r)
+    ids = np.zeros(k, dtype=np.int32)
+    w = np.zeros(k)
+    gap = lib().orc_moe_route_swapped(_ptr(r), r.size, k, _ptr(ids), _ptr(w))
+    return ids, w, gap
+
+
 def round_bf16(v):
     return lib().orc_round_bf16(float(v))
 
@@ -274,18 +302,25 @@ class State:
         if rc != 0:
             raise ValueError("set_kv out of range")
 
-    def step(self, token, threads=1, want_route=False):
-        """One decode step. Returns (logits float64 [V], argmax id[, route ids, route gap])."""
+    def step(self, token, threads=1, want_route=False, swap_mask=0, want_gaps=False):
+        """One decode step. Returns (logits float64 [V], argmax id[, route ids, route gap]
+        [, per-layer router gaps]).  Bit l of swap_mask routes layer l to the
+        (k+1)-th expert in place of the k-th."""
         wl = self.model.wl
         logits = np.empty(wl.n_vocab)
         ids = None
         gap = ctypes.c_double(0.0)
+        gaps = np.zeros(wl.n_layer) if want_gaps else None
         if want_route:
             ids = np.zeros((wl.n_layer, max(1, wl.n_expert_used)), dtype=np.int32)
-        am = lib().orc_step(ctypes.byref(self.model.cfg), self.model.tab, self.h, int(token),
-                            _ptr(logits), threads, _ptr(ids), ctypes.byref(gap))
+        am = lib().orc_step_ex(ctypes.byref(self.model.cfg), self.model.tab, self.h, int(token),
+                               _ptr(logits), threads, _ptr(ids), _ptr(gaps), ctypes.byref(gap),
+                               int(swap_mask))
         if am < -1:
             raise ValueError("oracle step failed (%d)" % am)
+        out = (logits, am)
         if want_route:
-            return logits, am, ids, gap.value
-        return logits, am
+            out = out + (ids, gap.value)
+        if want_gaps:
+            out = out + (gaps,)
+        return out

@@ -108,11 +108,41 @@ double orc_round_bf16(double v) {
     return ldexp(nearbyint(ldexp(m, 8)), e - 8);
 }
 
-/* v stored in type dt: fp32, or the bf16 code of its fp32 value */
+/* Sensitivity probe, for the tests only (off unless a test sets it): with
+ * eps > 0 every value about to be stored as bf16 is first multiplied by
+ * (1 + eps * u), u uniform in [-1, 1) from a SplitMix64 counter (Steele, Lea
+ * and Flood, "Fast splittable pseudorandom number generators", 2014).  It
+ * measures how far the logits move when every bf16 rounding sees an input off
+ * by a relative eps, as a GPU's fp32 arithmetic may be. */
+static double g_pert_eps = 0.0;
+static uint64_t g_pert_ctr = 0;
+
+void orc_set_perturbation(double eps, uint64_t seed) {
+    g_pert_eps = eps;
+    g_pert_ctr = seed;
+}
+
+static double perturb(double v) {
+    uint64_t z = (g_pert_ctr += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    double u = (double)(z >> 11) * 0x1.0p-52 - 1.0;
+    return v * (1.0 + g_pert_eps * u);
+}
+
+/* v stored in type dt: fp32, or the bf16 code of its fp32 value (the decision
+ * is taken in fp32, the precision the GPU decides in: fp64 -> fp32 -> bf16) */
 static double round_to(double v, int dt) {
-    if (dt == ORC_BF16) return orc_round_bf16((double)(float)v);
+    if (dt == ORC_BF16) {
+        if (g_pert_eps != 0.0) v = perturb(v);
+        return orc_round_bf16((double)(float)v);
+    }
     return (double)(float)v;
 }
+
+/* the storage rounding above, exported for the tests */
+double orc_round_store(double v, int dt) { return round_to(v, dt); }
 
 static uint16_t bf16_bits(double v) {
     float f = (float)orc_round_bf16((double)(float)v);
@@ -275,9 +305,11 @@ double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 /* Top-k routing of one token: ids by descending router logit compared in fp32
  * (ties -> lower index); weights = softmax over all experts, renormalised over
  * the chosen ones (equal to a softmax over the chosen logits). Returns the
- * fp32 gap between the k-th and (k+1)-th logits (inf if k == n). */
-double orc_moe_route(const double *r, int n, int k, int32_t *ids, double *w) {
-    int used[64] = {0};
+ * fp32 gap between the k-th and (k+1)-th logits (inf if k == n).  With `swap`
+ * (and k < n) the (k+1)-th expert takes the k-th one's place: the other valid
+ * choice when those two logits are a near tie that fp32 cannot order. */
+static double route(const double *r, int n, int k, int swap, int32_t *ids, double *w) {
+    char *used = (char *)calloc((size_t)n, 1);
     for (int a = 0; a < k; ++a) {
         int best = -1;
         float bv = 0.0f;
@@ -289,6 +321,16 @@ double orc_moe_route(const double *r, int n, int k, int32_t *ids, double *w) {
         used[best] = 1;
         ids[a] = best;
     }
+    double gap = INFINITY;
+    if (k < n) {
+        float kth = (float)r[ids[k - 1]], next = -INFINITY;
+        int inext = -1;
+        for (int e = 0; e < n; ++e)
+            if (!used[e] && (inext < 0 || (float)r[e] > next)) { next = (float)r[e]; inext = e; }
+        gap = (double)kth - (double)next;
+        if (swap) ids[k - 1] = inext;
+    }
+    free(used);
     double mx = -INFINITY;
     for (int e = 0; e < n; ++e) if (r[e] > mx) mx = r[e];
     double den = 0.0;
@@ -299,14 +341,15 @@ double orc_moe_route(const double *r, int n, int k, int32_t *ids, double *w) {
         sel += w[a];
     }
     for (int a = 0; a < k; ++a) w[a] /= sel;
-    double gap = INFINITY;
-    if (k < n) {
-        float kth = (float)r[ids[k - 1]], next = -INFINITY;
-        for (int e = 0; e < n; ++e)
-            if (!used[e] && (float)r[e] > next) next = (float)r[e];
-        gap = (double)kth - (double)next;
-    }
     return gap;
+}
+
+double orc_moe_route(const double *r, int n, int k, int32_t *ids, double *w) {
+    return route(r, n, k, 0, ids, w);
+}
+
+double orc_moe_route_swapped(const double *r, int n, int k, int32_t *ids, double *w) {
+    return route(r, n, k, 1, ids, w);
 }
 
 /* index of the largest logit compared in fp32, lowest index among equal maxima;
@@ -423,7 +466,7 @@ int orc_state_set_kv(orc_state *s, int layer, int pos0, int n, const void *k, co
     const orc_config *c = &s->cfg;
     if (layer < 0 || layer >= c->n_layer || pos0 < 0 || pos0 + n > s->max_ctx) return -2;
     size_t es = kv_elem(c), d = (size_t)c->head_dim;
-    double u[128], r[128];
+    double *u = (double *)malloc(sizeof(double) * d), *r = (double *)malloc(sizeof(double) * d);
     for (int t = 0; t < n; ++t)
         for (int j = 0; j < c->n_kv_head; ++j) {
             size_t src = ((size_t)t * c->n_kv_head + j) * d * es;
@@ -441,6 +484,8 @@ int orc_state_set_kv(orc_state *s, int layer, int pos0, int n, const void *k, co
             memcpy((char *)s->k[layer] + dst, (const char *)k + src, d * es);
             memcpy((char *)s->v[layer] + dst, (const char *)v + src, d * es);
         }
+    free(u);
+    free(r);
     return 0;
 }
 
@@ -485,19 +530,20 @@ static int wdt(const orc_config *c) { return c->w_dtype; }
 static int aux_dt(const orc_config *c) { return c->w_dtype == ORC_F32 ? ORC_F32 : ORC_BF16; }
 
 /* the FFN of one token: x += FFN(round_act(RMSNorm(x) * g_ffn)); returns the
- * router's fp32 k-th/(k+1)-th gap for MoE layers, +inf otherwise */
+ * router's fp32 k-th/(k+1)-th gap for MoE layers, +inf otherwise; `swap`
+ * routes to the (k+1)-th expert in place of the k-th (see route) */
 static double ffn(const orc_config *c, const void *const *tab, int lb, double *x, scratch *s,
-                  int32_t *ids_out) {
+                  int32_t *ids_out, int swap) {
     int E = c->n_embd, F = c->n_ff;
     orc_rmsnorm(x, (const float *)T(tab, lb + L_FFN_NORM), E, c->rms_norm_eps, s->xn);
     for (int i = 0; i < E; ++i) s->xn[i] = round_to(s->xn[i], c->act_dtype);
     int n_used = c->n_expert > 0 ? c->n_expert_used : 1;
-    int32_t ids[64];
-    double w[64];
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)n_used);
+    double *w = (double *)malloc(sizeof(double) * (size_t)n_used);
     double gap = INFINITY;
     if (c->n_expert > 0) {
         matvec(T(tab, lb + L_ROUTER), aux_dt(c), NULL, c->n_expert, E, s->xn, s->r);
-        gap = orc_moe_route(s->r, c->n_expert, n_used, ids, w);
+        gap = route(s->r, c->n_expert, n_used, swap, ids, w);
     } else {
         ids[0] = 0;
         w[0] = 1.0;
@@ -513,6 +559,8 @@ static double ffn(const orc_config *c, const void *const *tab, int lb, double *x
         if (ids_out) ids_out[a] = ids[a];
     }
     for (int i = 0; i < E; ++i) x[i] += s->acc[i];
+    free(ids);
+    free(w);
     return gap;
 }
 
@@ -567,18 +615,24 @@ static void embed(const orc_config *c, const void *const *tab, int token, double
 
 /* One decode step: append the token's k, v at state->pos, attend, write the
  * logits [V] and return the greedy id (or a negative error).  `route_ids`
- * (optional, [n_layer][n_expert_used]) receives the experts each layer chose
- * and `route_gap` (optional) the smallest router k-th/(k+1)-th fp32 gap. */
-int orc_step(const orc_config *c, const void *const *tab, orc_state *st, int token,
-             double *logits, int nthreads, int32_t *route_ids, double *route_gap) {
+ * (optional, [n_layer][n_expert_used]) receives the experts each layer chose,
+ * `layer_gaps` (optional, [n_layer]) each layer's router k-th/(k+1)-th fp32
+ * gap (+inf for dense layers), and `route_gap` (optional) the smallest of
+ * them.  Bit l of `swap_mask` makes layer l (< 64) route to the (k+1)-th
+ * expert in place of the k-th: the other branch of a routing near tie. */
+int orc_step_ex(const orc_config *c, const void *const *tab, orc_state *st, int token,
+                double *logits, int nthreads, int32_t *route_ids, double *layer_gaps,
+                double *route_gap, uint64_t swap_mask) {
     int E = c->n_embd, d = c->head_dim, H = c->n_head, Hk = c->n_kv_head;
     int p = st->pos;
     if (token < 0 || token >= c->n_vocab) return -3;
     if (p < 0 || p >= st->max_ctx) return -2;
+    if (c->head_dim < 2 || c->head_dim % 2 || c->n_head % c->n_kv_head) return -4;
     g_threads = nthreads > 0 ? nthreads : 1;
     scratch s;
     scratch_new(c, &s);
     double *x = malloc(sizeof(double) * E);
+    double *rk = malloc(sizeof(double) * d), *rv = malloc(sizeof(double) * d);
     int t0 = (c->sliding_window > 0 && p - c->sliding_window + 1 > 0) ? p - c->sliding_window + 1 : 0;
     int n = p - t0 + 1;
     double *K = malloc(sizeof(double) * (size_t)Hk * n * d);
@@ -589,7 +643,6 @@ int orc_step(const orc_config *c, const void *const *tab, orc_state *st, int tok
         int lb = T_LAYER0 + l * orc_layer_stride(c);
         qkv(c, tab, lb, x, p, &s);
         for (int j = 0; j < Hk; ++j) {
-            double rk[128], rv[128];
             kv_round_head(c, s.k + (size_t)j * d, d, rk);
             kv_round_head(c, s.v + (size_t)j * d, d, rv);
             for (int i = 0; i < d; ++i) {
@@ -612,7 +665,9 @@ int orc_step(const orc_config *c, const void *const *tab, orc_state *st, int tok
         attn_out(c, tab, lb, x, &s);
         double gl = ffn(c, tab, lb, x, &s,
                         route_ids ? route_ids + (size_t)l * (c->n_expert > 0 ? c->n_expert_used : 1)
-                                  : NULL);
+                                  : NULL,
+                        l < 64 && ((swap_mask >> l) & 1));
+        if (layer_gaps) layer_gaps[l] = gl;
         if (gl < gap) gap = gl;
     }
     head(c, tab, x, logits, &s);
@@ -620,9 +675,16 @@ int orc_step(const orc_config *c, const void *const *tab, orc_state *st, int tok
     if (route_gap) *route_gap = gap;
     free(K);
     free(V);
+    free(rk);
+    free(rv);
     free(x);
     scratch_free(&s);
     return orc_argmax(logits, c->n_vocab);
+}
+
+int orc_step(const orc_config *c, const void *const *tab, orc_state *st, int token,
+             double *logits, int nthreads, int32_t *route_ids, double *route_gap) {
+    return orc_step_ex(c, tab, st, token, logits, nthreads, route_ids, NULL, route_gap, 0);
 }
 
 /* Causal forward over tokens[0..n-1] from scratch (no cache carried between
@@ -654,7 +716,7 @@ int orc_full_recompute(const orc_config *c, const void *const *tab, const int32_
         for (int t = 0; t < n; ++t) {
             orc_attention(Q + (size_t)t * H * d, K, V, H, Hk, d, n, t, c->sliding_window, s.o);
             attn_out(c, tab, lb, X + (size_t)t * E, &s);
-            ffn(c, tab, lb, X + (size_t)t * E, &s, NULL);
+            ffn(c, tab, lb, X + (size_t)t * E, &s, NULL, 0);
         }
     }
     head(c, tab, X + (size_t)(n - 1) * E, logits, &s);

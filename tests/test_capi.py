@@ -224,3 +224,50 @@ def test_wide_prefill_buffers_in_model_bytes():
         cfg = good_cfg(prefill_chunk=chunk, w_dtype=C.PN_BF16, act_dtype=C.PN_F32)
         sizes.append(L.pn_model_bytes(ctypes.byref(cfg)))
     assert 0 < sizes[0] < sizes[1] < sizes[2]
+
+
+def test_model_create_checks_every_layer_before_any_device_work():
+    """pn_model_create validates the pointers of every layer before it enqueues
+    anything: a NULL in the last layer fails with PN_EINVAL and names that layer.
+    (On this host there is no device, so any enqueue would fail as PN_EHIP.)"""
+    L = C.lib()
+    cfg = good_cfg(n_layer=4)
+    need = L.pn_model_bytes(ctypes.byref(cfg))
+    fake = ctypes.c_void_p(1 << 20)
+    layers = (C.pn_layer_weights * 4)()
+    for l in range(4):
+        for name, _ in C.pn_layer_weights._fields_:
+            if name in ("w_router", "s_q", "s_k", "s_v", "s_o", "s_gate", "s_up", "s_down", "b_q", "b_k", "b_v"):
+                continue
+            setattr(layers[l], name, fake.value)
+    layers[3].wo = None
+    w = C.pn_weights(fake.value, fake.value, fake.value, None, layers)
+    h = ctypes.c_void_p()
+    assert L.pn_model_create(ctypes.byref(cfg), ctypes.byref(w), fake, need, None, ctypes.byref(h)) == C.PN_EINVAL
+    assert b"layer 3" in L.pn_last_error()
+    assert not h.value
+    w.w_out = None
+    assert L.pn_model_create(ctypes.byref(cfg), ctypes.byref(w), fake, need, None, ctypes.byref(h)) == C.PN_EINVAL
+    assert b"global" in L.pn_last_error()
+
+
+def test_route_log_and_stream_read_arguments():
+    L = C.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    for kw, ok in ((dict(), False), (dict(n_expert=4, n_expert_used=2), True)):
+        cfg = good_cfg(**kw)
+        need = L.pn_model_bytes(ctypes.byref(cfg))
+        h = ctypes.c_void_p()
+        assert L.pn_model_init(ctypes.byref(cfg), fake, need, ctypes.byref(h)) == 0
+        try:
+            rc = L.pn_model_route_log(h, ctypes.c_void_p(1 << 22), 4)
+            assert rc == (0 if ok else C.PN_EINVAL)
+            if ok:
+                assert L.pn_model_route_log(h, ctypes.c_void_p(1 << 22), 0) == C.PN_EINVAL
+                assert L.pn_model_route_log(h, None, 0) == 0  # off
+        finally:
+            L.pn_model_free(h)
+    assert L.pn_model_route_log(None, None, 0) == C.PN_EINVAL
+    assert L.pn_stream_read(None, 1024, fake, None) == C.PN_EINVAL
+    assert L.pn_stream_read(fake, 1000, fake, None) == C.PN_EINVAL
+    assert L.pn_stream_read(ctypes.c_void_p((1 << 20) + 4), 1024, fake, None) == C.PN_EINVAL

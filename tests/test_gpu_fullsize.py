@@ -7,20 +7,20 @@ oracle (the GPU fed the oracle's tokens), comparing every step's logits and
 greedy ids.
 
 Tolerance.  Logits of bf16 / INT8 models must be within relative L2 2e-2 of
-the oracle.  With bf16 activations, though, every mat-vec input is rounded to
-bf16, and the GPU's fp32 arithmetic lands a few fp32 ulps away from the
-oracle's fp64 values before those roundings, which flips a few of them.  A
-32-layer model of these random weights amplifies such flips: in the oracle
-alone, a relative perturbation of 1e-7 before each bf16 rounding moves the
-logits by 0.8% and one of 1e-6 by 2%.  So the full 32-layer bf16-activation
-workloads are checked against that floor (FLOOR_TOL), and the same widths and
-contexts with 4 layers, where the floor is about 0.4%, against 2e-2.  The
-fp32-activation workload (Llama-3-8B bf16) meets 2e-2 by four orders of
-magnitude.
+the oracle (fp32 ones within 1e-4), at every depth.  With bf16 activations
+every mat-vec input is rounded to bf16, and the GPU's fp32 arithmetic lands a
+few fp32 ulps from the oracle's fp64 values before those roundings, which
+flips a few of them; 32 layers of these random weights carry each flip to the
+logits (tests/test_oracle_state_pins.py measures how far: in the oracle
+alone, a relative perturbation of 1e-7 before every bf16 rounding moves the
+Llama-3-8B INT8 logits by 0.8%).
 
-The Mixtral-shaped cases keep the full width, all 8 experts and 16 slots but
-one and four layers, so that the oracle's host copy of the weights stays
-small; their kernels run at their full per-layer shapes.
+The Mixtral-shaped cases keep the full width, all 8 experts and 16 slots.
+Past the first layer the router sees activations that carry that rounding
+noise, so where the oracle's k-th and (k+1)-th expert logits are closer than
+ROUTE_TOL either choice is a valid result at fp32 precision: the oracle then
+also runs the branch with those experts swapped, and the GPU must match one
+branch by the same parity rule (harness.moe_step_branches).
 """
 import time
 
@@ -32,8 +32,7 @@ from harness import Pair, log, run_batch, run_single
 
 pytestmark = pytest.mark.gpu
 
-FLOOR_TOL = 3e-2  # 32 layers, bf16 activations: the rounding-flip floor (see above)
-ROUTE_TOL = 2e-2  # MoE past layer 1: router top-k gaps below this are near ties (8x the noise)
+ROUTE_TOL = 1e-2  # MoE: router k-th/(k+1)-th gaps below this also admit the swapped branch
 
 
 def _timed(label, fn):
@@ -68,8 +67,8 @@ def test_llama3_8b_int8_four_layers():
 
 
 def test_llama3_8b_int8_full():
-    """The same with all 32 layers, against the bf16 rounding-flip floor."""
-    _single(synth.llama3_8b_int8(), tol=FLOOR_TOL)
+    """The same with all 32 layers."""
+    _single(synth.llama3_8b_int8())
 
 
 def test_llama3_8b_q8_0_four_layers():
@@ -89,8 +88,8 @@ def test_mistral_7b_8slots_four_layers():
 
 
 def test_mistral_7b_8slots_full():
-    """The same with all 32 layers, against the bf16 rounding-flip floor."""
-    _batch(synth.mistral_7b_slots(), tol=FLOOR_TOL)
+    """The same with all 32 layers."""
+    _batch(synth.mistral_7b_slots())
 
 
 def test_mixtral_8x7b_16slots_one_layer():
@@ -99,16 +98,23 @@ def test_mixtral_8x7b_16slots_one_layer():
     _batch(synth.mixtral_8x7b_slots().with_(name="mixtral-8x7b-16slots-1layer", n_layer=1))
 
 
-def test_mixtral_8x7b_16slots_four_layers():
-    """The same with 4 layers.  Past the first layer the router sees activations
-    carrying the bf16 rounding noise of the layers before it (router logits off by
-    ~1e-3), so a slot-step whose oracle top-k gap is below ROUTE_TOL is a routing
-    near tie and is only checked for finite logits; at least 3/4 of the
-    slot-steps must be compared."""
+def _moe(wl, steps=2):
     stats = {}
-    wl = synth.mixtral_8x7b_slots().with_(name="mixtral-8x7b-16slots-4layers", n_layer=4)
     p = _timed("setup", lambda: Pair(wl, max_batch=wl.slots))
     starts = [int(s) for s in wl.start_positions()]
-    worst, near = _timed("steps", lambda: run_batch(p, starts, 2, route_tol=ROUTE_TOL, stats=stats))
-    log("  %s: worst rel L2 %.2e, near ties %d, %s" % (wl.name, worst, near, stats))
-    assert stats.get("compared", 0) >= 3 * (stats.get("compared", 0) + stats.get("exempt", 0)) // 4
+    worst, near = _timed("steps", lambda: run_batch(p, starts, steps, route_tol=ROUTE_TOL, stats=stats))
+    log("  %s: worst rel L2 %.2e, near ties %d, slot-steps matched on the oracle's routing %d, on a "
+        "swapped branch %d" % (wl.name, worst, near, stats.get("base", 0), stats.get("swapped", 0)))
+    assert stats.get("base", 0) + stats.get("swapped", 0) == steps * len(starts)
+
+
+def test_mixtral_8x7b_16slots_four_layers():
+    """The same with 4 layers: every slot-step compared, on the oracle's routing
+    or, at a routing near tie, on the branch the GPU's router took."""
+    _moe(synth.mixtral_8x7b_slots().with_(name="mixtral-8x7b-16slots-4layers", n_layer=4))
+
+
+def test_mixtral_8x7b_16slots_full():
+    """All 32 layers (93 GB of bf16 weights on the device and in the oracle's
+    host memory), 16 slots, 2 steps, routing near ties checked branch by branch."""
+    _moe(synth.mixtral_8x7b_slots())

@@ -362,8 +362,11 @@ def test_q4_kv_round_values_are_scaled_codes():
 
 # ----------------------------------------------------------------------------- whole model
 
-def _torch_forward(wl, W, tokens):
-    """The same model built from torch library routines (float64), full causal recompute."""
+def _torch_forward(wl, W, tokens, kv_out=None):
+    """The same model built from torch library routines (float64), full causal recompute.
+    With `kv_out` (a list), each layer appends (k, v): every position's cached k
+    (after RoPE) and v, [n][Hk][d], in the form a cache of the workload's KV type
+    is written with (fp32 values, bf16 bits, or fp32 values before Q4 blocks)."""
     E, H, Hk, d = wl.n_embd, wl.n_head, wl.n_kv_head, wl.head_dim
 
     def mat(m, s=None):
@@ -428,8 +431,15 @@ def _torch_forward(wl, W, tokens):
         g = torch.tensor(L["attn_norm"].astype(np.float64))
         xn = act(F.rms_norm(x, (E,), weight=g, eps=wl.rms_norm_eps))
         q = rope((xn @ mat(L["wq"], L["s_q"]).T + bias("b_q")).reshape(n, H, d))
-        k = kvr(rope((xn @ mat(L["wk"], L["s_k"]).T + bias("b_k")).reshape(n, Hk, d)))
-        v = kvr((xn @ mat(L["wv"], L["s_v"]).T + bias("b_v")).reshape(n, Hk, d))
+        k_raw = rope((xn @ mat(L["wk"], L["s_k"]).T + bias("b_k")).reshape(n, Hk, d))
+        v_raw = (xn @ mat(L["wv"], L["s_v"]).T + bias("b_v")).reshape(n, Hk, d)
+        k, v = kvr(k_raw), kvr(v_raw)
+        if kv_out is not None:
+            if wl.kv_dtype == synth.BF16:
+                kv_out.append(tuple(t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+                                    for t in (k_raw, v_raw)))
+            else:
+                kv_out.append(tuple(t.to(torch.float32).numpy().copy() for t in (k_raw, v_raw)))
         o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
                                            v.transpose(0, 1)[None], attn_mask=mask[None, None],
                                            enable_gqa=True)[0].transpose(0, 1).reshape(n, H * d)

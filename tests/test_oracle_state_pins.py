@@ -1,0 +1,206 @@
+"""Pins of the oracle's state input and of its storage-rounding reading.
+
+Every parity case that resumes from a cache (the full-size workloads, the
+700-position ragged cases, prefill from an existing cache) writes K/V into the
+oracle's state with set_kv and moves its position with set_pos, so these are
+pinned against an independent composition: the cached k (after RoPE) and v of
+a prefix, computed by torch float64 library routines ("Core Engine API",
+sections "pn_state struct" and "State lifecycle": a state is the KV cache of
+the tokens before pos, plus pos), written in two set_kv calls (the second at
+pos0 > 0), then one oracle step must give the logits of the whole sequence.
+A slip in the [n][Hk][d] layout, in pos0, in set_pos, or in which rows a Q4
+cache quantises fails here.
+
+The perturbation experiment at the end measures how far the logits of a
+32-layer bf16-activation model move when every value is off by a relative
+eps before its bf16 rounding: the sensitivity that sets how close a GPU's
+fp32 arithmetic can come to the fp64 oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from test_oracle_pins import _torch_forward
+
+RESUME = [
+    # fp32 cache, 4 query heads per KV head
+    synth.tiny_fp32().with_(name="resume-f32", seed=31),
+    # bf16 cache and activations, window 5: only the window's positions are written
+    synth.tiny_fp32().with_(name="resume-bf16-window", w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                            act_dtype=synth.BF16, sliding_window=5, seed=32),
+    # Q4 cache (fp32 rows in, quantised by set_kv) with a window of 6
+    synth.tiny_fp32().with_(name="resume-q4kv-window", kv_dtype=synth.Q4_0, sliding_window=6, seed=33),
+    # int8 weights, bf16 cache, d = 64, 8 query heads per KV head
+    synth.tiny_fp32().with_(name="resume-int8-g8", w_dtype=synth.I8, kv_dtype=synth.BF16,
+                            act_dtype=synth.BF16, n_head=8, n_kv_head=1, head_dim=64, seed=34),
+    # NeoX RoPE and biases, bf16, window 4
+    synth.tiny_fp32().with_(name="resume-neox-bias-window", rope_neox=True, qkv_bias=True,
+                            w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=synth.BF16,
+                            sliding_window=4, seed=35),
+    # MoE with a Q4 cache
+    synth.tiny_fp32().with_(name="resume-moe-q4kv", kv_dtype=synth.Q4_0, n_expert=4, n_expert_used=2,
+                            n_ff=96, seed=36),
+]
+
+
+@pytest.mark.parametrize("wl", RESUME, ids=lambda w: w.name)
+def test_set_kv_set_pos_resume_equals_full_forward(wl):
+    W = synth.make_weights(wl)
+    m = oracle.Model(wl, W)
+    n = 13
+    tokens = [int(t) for t in synth.uniform_int(wl.seed, 98, n, 0, wl.n_vocab - 1)]
+    kv = []
+    ref = _torch_forward(wl, W, tokens, kv_out=kv)
+    p = n - 1  # the step's position: positions 0..p-1 come from the composition
+    lo = max(0, p - wl.sliding_window + 1) if wl.sliding_window > 0 else 0
+    mid = lo + (p - lo) // 2
+    assert 0 < mid < p
+    st = m.new_state(n + 3)
+    for l, (k, v) in enumerate(kv):
+        # two calls, the second at pos0 = mid > 0; positions below lo stay zero,
+        # so a window read past its start would change the result
+        st.set_kv(l, lo, k[lo:mid], v[lo:mid])
+        st.set_kv(l, mid, k[mid:p], v[mid:p])
+    st.pos = p
+    assert st.pos == p
+    logits, am = st.step(tokens[p])
+    rel = np.linalg.norm(logits - ref) / np.linalg.norm(ref)
+    assert rel < 1e-12, rel
+    assert am == int(np.argmax(ref.astype(np.float32)))
+    assert st.pos == p + 1
+
+
+def test_set_pos_rewind_rewrites_position():
+    """set_pos back to p and a step there overwrite position p's cache rows
+    (the step writes before it attends), so a rewound step equals the first."""
+    wl = synth.tiny_fp32().with_(name="rewind", seed=37)
+    m = oracle.Model(wl, synth.make_weights(wl))
+    st = m.new_state(8)
+    for t in (5, 6, 7):
+        st.step(t)
+    l1, a1 = st.step(9)
+    st.step(10)
+    st.pos = 3
+    l2, a2 = st.step(9)
+    np.testing.assert_array_equal(l1, l2)
+    assert a1 == a2 and st.pos == 4
+
+
+def test_set_kv_rejects_out_of_range():
+    wl = synth.tiny_fp32().with_(n_layer=1)
+    m = oracle.Model(wl, synth.make_weights(wl))
+    st = m.new_state(4)
+    k = np.zeros((2, wl.n_kv_head, wl.head_dim), dtype=np.float32)
+    with pytest.raises(ValueError):
+        st.set_kv(0, 3, k, k)  # positions 3, 4: past max_ctx
+    with pytest.raises(ValueError):
+        st.set_kv(1, 0, k, k)  # no layer 1
+
+
+# ----------------------------------------------------------------------------- storage rounding
+
+def _bf16_via_f32(v):
+    """Independent fp64 -> fp32 -> bf16 (round to nearest even on the fp32 bits)."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16 << 16
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def test_storage_rounding_goes_through_fp32():
+    """A value stored as bf16 is rounded to fp32 first, then to its bf16 code: the
+    decision is taken in the precision the GPU decides in.  Worked example:
+    v = 1 + 2^-8 + 2^-30 lies just above the midpoint of the bf16 neighbours 1
+    and 1 + 2^-7, so direct rounding gives 1 + 2^-7; its fp32 value is the
+    midpoint 1 + 2^-8 itself, which rounds to the even neighbour 1."""
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert oracle.round_bf16(v) == 1.0 + 2.0 ** -7          # direct fp64 -> bf16
+    assert oracle.round_store(v, synth.BF16) == 1.0           # fp64 -> fp32 -> bf16
+    assert oracle.round_store(-v, synth.BF16) == -1.0
+    # just below a midpoint, both agree
+    w = 1.0 + 2.0 ** -8 - 2.0 ** -30
+    assert oracle.round_store(w, synth.BF16) == oracle.round_bf16(w) == 1.0
+    # torch's float64 -> bfloat16 conversion takes the same path, so the torch
+    # composition that pins the whole model pins this reading too
+    assert torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).item() == 1.0
+    # fp32 storage: plain fp32 rounding
+    assert oracle.round_store(1.0 + 2.0 ** -30, synth.F32) == 1.0
+
+
+def test_storage_rounding_matches_independent_form():
+    r = np.random.default_rng(77)
+    vals = np.concatenate([r.standard_normal(4000) * 10.0 ** r.integers(-6, 6, 4000),
+                           # values a hair above and below bf16 midpoints
+                           (1 + (2 * r.integers(0, 128, 500) + 1) * 2.0 ** -8) * (1 + 2.0 ** -29),
+                           (1 + (2 * r.integers(0, 128, 500) + 1) * 2.0 ** -8) * (1 - 2.0 ** -29)])
+    got = np.array([oracle.round_store(v, synth.BF16) for v in vals])
+    np.testing.assert_array_equal(got, _bf16_via_f32(vals))
+    direct = np.array([oracle.round_bf16(v) for v in vals])
+    assert np.sum(direct != got) > 100  # the two readings really differ on such inputs
+
+
+# ----------------------------------------------------------------------------- perturbation
+
+def _perturbation_spread(wl, eps_list, steps=2, p0=64, threads=None):
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
+    W = synth.make_weights(wl)
+    om = oracle.Model(wl, W)
+
+    def run(eps):
+        oracle.set_perturbation(eps, seed=12345)
+        try:
+            st = om.new_state(p0 + steps + 1)
+            for l in range(wl.n_layer):
+                k, v = wl.kv_prefill(0, l, 0, p0)
+                st.set_kv(l, 0, k, v)
+            st.pos = p0
+            tok = int(wl.first_tokens(1)[0])
+            out = []
+            for _ in range(steps):
+                lg, _ = st.step(tok, threads=threads)
+                out.append(lg)
+                tok = int(synth.uniform_int(wl.seed, 97, 1, 0, wl.n_vocab - 1)[0])  # fixed inputs
+            return out
+        finally:
+            oracle.set_perturbation(0.0)
+
+    base = run(0.0)
+    again = run(0.0)
+    for a, b in zip(base, again):
+        np.testing.assert_array_equal(a, b)
+    spread = {}
+    for eps in eps_list:
+        pert = run(eps)
+        spread[eps] = max(float(np.linalg.norm(a - b) / np.linalg.norm(b)) for a, b in zip(pert, base))
+        print("  %s: eps %.0e before every bf16 rounding -> logits rel L2 %.3e" % (wl.name, eps, spread[eps]),
+              flush=True)
+    return spread
+
+
+def test_bf16_rounding_sensitivity_32_layers():
+    """32 layers, bf16 activations and cache, int8 weights, at a quarter of the
+    Llama-3-8B width (the full width runs with TD_FULL_PERTURB=1).  A relative
+    perturbation far below one bf16 ulp (2^-8) before each rounding flips a few
+    of them, and 32 layers of random weights carry each flip to the logits."""
+    wl = synth.llama3_8b_int8().with_(name="perturb-32l-e1024", n_embd=1024, n_head=8, n_kv_head=2,
+                                      n_ff=3584, n_vocab=32000, seed=41)
+    spread = _perturbation_spread(wl, (1e-8, 1e-7, 1e-6))
+    # 1e-8 (a sixth of an fp32 ulp) rarely moves a value across an fp32 rounding
+    # boundary, let alone a bf16 one; 1e-7 (one to two fp32 ulps) flips a few
+    # bf16 roundings, and the logits move by about 1%: once a few roundings
+    # flip, the spread is set by the depth and width, not by eps
+    assert spread[1e-8] <= spread[1e-7]
+    assert spread[1e-7] > 5e-3
+    assert spread[1e-6] < 0.2  # still a perturbation, not noise
+
+
+@pytest.mark.skipif(os.environ.get("TD_FULL_PERTURB") != "1",
+                    reason="full-width run (about 5 minutes on 8 cores): set TD_FULL_PERTURB=1")
+def test_bf16_rounding_sensitivity_llama3_8b_int8():
+    """The experiment at the Llama-3-8B INT8 workload's full shape (32 layers)."""
+    wl = synth.llama3_8b_int8().with_(name="perturb-llama3-8b-int8")
+    _perturbation_spread(wl, (1e-8, 3e-8, 1e-7, 3e-7, 1e-6), steps=1, p0=256)

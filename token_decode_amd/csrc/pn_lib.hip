@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "pn.h"
+#include "pn_host.hpp"
 #include "pn_launch.hpp"
 #include "pn_small.hpp"
 #include "pn_sample.hpp"
@@ -84,6 +85,11 @@ struct pn_model {
     Mat out;
     // scratch
     size_t x, q, o, h, y, route_ids, route_w, am_val, am_idx;
+    // routing record (pn_model_route_log): step i writes its experts to
+    // route_log[(i % route_log_steps)][layer][slot][k]
+    int *route_log = nullptr;
+    int route_log_steps = 0;
+    long long route_log_step = 0;
     size_t samp_keys = 0, samp_hist = 0, samp_cnt = 0, samp_cand = 0;  // pn_sample scratch
     bool samp_dirty = false;  // a pn_sample call stopped before k_sample_pick cleared its histogram
     size_t attn_part = 0, attn_part_row = 0;  // pn_prefill: per-row attention split scratch
@@ -896,6 +902,9 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         } else {
             int *rid = (int *)(mb + m->route_ids);
             float *rw = (float *)(mb + m->route_w);
+            int *rlog = (m->route_log && !row_pos) ? m->route_log + ((m->route_log_step % m->route_log_steps) * c.n_layer + l) *
+                                                           (long long)c.max_batch * m->n_used
+                                     : nullptr;
             {
                 Timed tm(m, PN_K_ROUTER, s);
                 const size_t sh = (size_t)E * 4;
@@ -903,14 +912,14 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                 const float *gn = (const float *)(mb + L.ffn_norm);
                 if (wt == PN_F32) {
                     if (at == PN_F32)
-                        hipLaunchKernelGGL((k_router<0, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
+                        hipLaunchKernelGGL((k_router<0, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw, rlog);
                     else
-                        hipLaunchKernelGGL((k_router<0, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
+                        hipLaunchKernelGGL((k_router<0, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw, rlog);
                 } else {
                     if (at == PN_F32)
-                        hipLaunchKernelGGL((k_router<1, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
+                        hipLaunchKernelGGL((k_router<1, AT_F32>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw, rlog);
                     else
-                        hipLaunchKernelGGL((k_router<1, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw);
+                        hipLaunchKernelGGL((k_router<1, AT_BF16>), dim3(n), dim3(256), sh, s, (const float *)x, gn, wr, E, c.n_expert, m->n_used, c.rms_norm_eps, (const float *)(mb + m->ssp), m->ssp_ld, m->ssp_ld, rid, rw, rlog);
                 }
             }
             {
@@ -993,6 +1002,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    if (moe && m->route_log && !row_pos) ++m->route_log_step;
     if (row_pos) st[0]->pos += n;
     else for (int b = 0; b < n; ++b) st[b]->pos += 1;
     for (int b = 0; b < n; ++b) recycle_pages(st[b]);
@@ -1276,12 +1286,140 @@ int pn_model_init(const pn_config *cfg, void *dev_buf, size_t bytes, pn_model **
     return PN_OK;
 }
 
+}  // extern "C"
+
+namespace pn {
+
+// The sampler's host side, shared by pn_sample (scratch in the model buffer)
+// and pn_sample_noalloc (scratch in a file-scope device array).
+// Host checks of the sampling parameters of n rows over a vocabulary of V, into a.
+namespace {
+
+int sample_args(int n, int V, const pn_sampling_params *params, const int32_t *recent_dev, int n_recent,
+                const float *logits_dev, const float *u_dev, int32_t *ids_dev, SampleArgs &a) {
+    if (n_recent < 0 || n_recent > kSampleMaxRecent)
+        return fail(PN_EINVAL, "n_recent = %d outside [0, %d]", n_recent, kSampleMaxRecent);
+    if (n_recent > 0 && !recent_dev) return fail(PN_EINVAL, "recent_dev is NULL");
+    a.logits = logits_dev;
+    a.V = V;
+    a.n_recent = n_recent;
+    a.recent = recent_dev;
+    a.u = u_dev;
+    a.ids = ids_dev;
+    for (int b = 0; b < n; ++b) {
+        const pn_sampling_params &p = params[b];
+        if (std::isnan(p.temperature)) return fail(PN_EINVAL, "row %d: temperature is NaN", b);
+        if (p.temperature > 0.f) {
+            if (!std::isfinite(p.temperature)) return fail(PN_EINVAL, "row %d: temperature must be finite", b);
+            if (p.top_k < 1 || p.top_k > kSampleMaxK)
+                return fail(PN_EUNSUPPORTED, "row %d: top_k = %d outside [1, %d]", b, p.top_k, kSampleMaxK);
+            if (!(p.repeat_penalty > 0.f) || !std::isfinite(p.repeat_penalty))
+                return fail(PN_EINVAL, "row %d: repeat_penalty must be finite and > 0", b);
+            if (std::isnan(p.top_p)) return fail(PN_EINVAL, "row %d: top_p is NaN", b);
+        }
+        a.temp[b] = p.temperature;
+        a.rp[b] = p.repeat_penalty;
+        a.top_p[b] = p.top_p;
+        a.top_k[b] = p.top_k;
+    }
+    return PN_OK;
+}
+
+// The sampler's three kernels over n rows.  The histogram and the gather
+// counters (rows_cap rows of them) start each call at zero: the previous call's
+// k_sample_pick cleared them, unless that call stopped early (`dirty`), and
+// then a fill kernel clears them first (a kernel, not a memset, so that the
+// call may be captured in a graph).
+int sample_run(const SampleArgs &a, int n, int rows_cap, bool &dirty, hipStream_t st) {
+    if (dirty) {
+        fill32(a.hist, (size_t)rows_cap * kSampleBins, 0u, st);
+        fill32(a.cnt, (size_t)rows_cap * 2, 0u, st);
+        if (int rc = launched("sampling scratch clear")) return rc;
+        dirty = false;
+    }
+    // the candidate buffer is dynamic LDS; with the kernel's static LDS the
+    // total passes 64 KiB, which needs the attribute (the two within 160 KiB)
+    static bool lds_set = false;
+    const size_t lds = (size_t)kSampleCap * 8;
+    if (!lds_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_sample_pick),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return fail(PN_EHIP, "sampling LDS attribute: %s", hipGetErrorString(e));
+        lds_set = true;
+    }
+    dirty = true;
+    hipLaunchKernelGGL(k_sample_keys, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
+    if (int rc = launched("sampling keys")) return rc;
+    hipLaunchKernelGGL(k_sample_gather, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
+    if (int rc = launched("sampling gather")) return rc;
+    hipLaunchKernelGGL(k_sample_pick, dim3(n), dim3(kSamplePick), lds, st, a);
+    if (int rc = launched("sampling pick")) return rc;
+    dirty = false;
+    return PN_OK;
+}
+
+}  // namespace
+
+int host_sample(const float *logits_dev, int n, int V, const pn_sampling_params *params, const int32_t *recent_dev,
+                int n_recent, const float *u_dev, int32_t *ids_dev, const SampleScratchPtrs &sp, int rows_cap,
+                bool &dirty, hipStream_t st) {
+    SampleArgs a{};
+    if (int rc = sample_args(n, V, params, recent_dev, n_recent, logits_dev, u_dev, ids_dev, a)) return rc;
+    a.keys = sp.keys;
+    a.hist = sp.hist;
+    a.cnt = sp.cnt;
+    a.cand = sp.cand;
+    return sample_run(a, n, rows_cap, dirty, st);
+}
+
+int host_fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+void host_clear_error() { g_err.clear(); }
+
+}  // namespace pn
+
+namespace {
+
+// the pointer checks of the load calls, shared with pn_model_create, which
+// runs them over every layer before it enqueues anything
+int check_globals(const pn_config *cfg, const void *tok_embd, const float *out_norm, const void *w_out,
+                  const float *s_out) {
+    const bool i8 = cfg->w_dtype == PN_I8;
+    if (!tok_embd || !out_norm || !w_out || (i8 && !s_out)) return fail(PN_EINVAL, "missing global weight pointer");
+    return PN_OK;
+}
+
+int check_layer(const pn_config *cfg, int32_t layer, const pn_layer_weights *W) {
+    if (!W) return fail(PN_EINVAL, "NULL argument");
+    if (layer < 0 || layer >= cfg->n_layer) return fail(PN_EINVAL, "layer %d out of range", layer);
+    const bool i8 = cfg->w_dtype == PN_I8;
+    if (!W->attn_norm || !W->ffn_norm || !W->wq || !W->wk || !W->wv || !W->wo || !W->w_gate || !W->w_up || !W->w_down)
+        return fail(PN_EINVAL, "missing weight pointer in layer %d", layer);
+    if (cfg->n_expert > 0 && !W->w_router) return fail(PN_EINVAL, "missing router in layer %d", layer);
+    if (i8 && (!W->s_q || !W->s_k || !W->s_v || !W->s_o || !W->s_gate || !W->s_up || !W->s_down))
+        return fail(PN_EINVAL, "missing int8 scales in layer %d", layer);
+    if (cfg->qkv_bias && (!W->b_q || !W->b_k || !W->b_v)) return fail(PN_EINVAL, "missing q/k/v bias in layer %d", layer);
+    return PN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int pn_model_load_globals(pn_model *m, const void *tok_embd, const float *out_norm, const void *w_out,
                           const float *s_out, void *stream) {
     g_err.clear();
     if (!m) return fail(PN_EINVAL, "model is NULL");
     const bool i8 = m->wt == PN_I8;
-    if (!tok_embd || !out_norm || !w_out || (i8 && !s_out)) return fail(PN_EINVAL, "missing global weight pointer");
+    if (int rc = check_globals(&m->cfg, tok_embd, out_norm, w_out, s_out)) return rc;
     hipStream_t s = S(stream);
     char *mb = m->base;
     const int es_aux = m->wt == PN_F32 ? 4 : 2;
@@ -1307,14 +1445,8 @@ int pn_model_load_layer(pn_model *m, int32_t layer, const pn_layer_weights *W, v
     g_err.clear();
     if (!m || !W) return fail(PN_EINVAL, "NULL argument");
     const pn_config *cfg = &m->cfg;
-    if (layer < 0 || layer >= cfg->n_layer) return fail(PN_EINVAL, "layer %d out of range", layer);
+    if (int rc = check_layer(cfg, layer, W)) return rc;
     const bool i8 = m->wt == PN_I8;
-    if (!W->attn_norm || !W->ffn_norm || !W->wq || !W->wk || !W->wv || !W->wo || !W->w_gate || !W->w_up || !W->w_down)
-        return fail(PN_EINVAL, "missing weight pointer in layer %d", layer);
-    if (cfg->n_expert > 0 && !W->w_router) return fail(PN_EINVAL, "missing router in layer %d", layer);
-    if (i8 && (!W->s_q || !W->s_k || !W->s_v || !W->s_o || !W->s_gate || !W->s_up || !W->s_down))
-        return fail(PN_EINVAL, "missing int8 scales in layer %d", layer);
-    if (cfg->qkv_bias && (!W->b_q || !W->b_k || !W->b_v)) return fail(PN_EINVAL, "missing q/k/v bias in layer %d", layer);
     hipStream_t s = S(stream);
     char *mb = m->base;
     const int wt = m->wt, es_aux = wt == PN_F32 ? 4 : 2;
@@ -1381,6 +1513,11 @@ int pn_model_create(const pn_config *cfg, const pn_weights *w, void *dev_buf, si
     int rc = check_config(cfg);
     if (rc) return rc;
     if (!w || !w->layers) return fail(PN_EINVAL, "weights are NULL");
+    // every pointer of every layer is checked before anything is enqueued
+    const pn_config n = normalized(*cfg);
+    if ((rc = check_globals(&n, w->tok_embd, w->out_norm, w->w_out, w->s_out))) return rc;
+    for (int l = 0; l < n.n_layer; ++l)
+        if ((rc = check_layer(&n, l, &w->layers[l]))) return rc;
     pn_model *m = nullptr;
     rc = pn_model_init(cfg, dev_buf, bytes, &m);
     if (rc) return rc;
@@ -1707,64 +1844,10 @@ int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling
     g_err.clear();
     if (!m || !logits_dev || !params || !u_dev || !ids_dev) return fail(PN_EINVAL, "NULL argument");
     if (n < 1 || n > m->cfg.max_batch) return fail(PN_EINVAL, "n = %d outside [1, max_batch = %d]", n, m->cfg.max_batch);
-    if (n_recent < 0 || n_recent > kSampleMaxRecent)
-        return fail(PN_EINVAL, "n_recent = %d outside [0, %d]", n_recent, kSampleMaxRecent);
-    if (n_recent > 0 && !recent_dev) return fail(PN_EINVAL, "recent_dev is NULL");
-    SampleArgs a{};
-    a.logits = logits_dev;
-    a.V = m->V;
-    a.n_recent = n_recent;
-    a.recent = recent_dev;
-    a.u = u_dev;
-    a.ids = ids_dev;
-    a.keys = (unsigned *)(m->base + m->samp_keys);
-    a.hist = (unsigned *)(m->base + m->samp_hist);
-    a.cnt = (unsigned *)(m->base + m->samp_cnt);
-    a.cand = (unsigned long long *)(m->base + m->samp_cand);
-    for (int b = 0; b < n; ++b) {
-        const pn_sampling_params &p = params[b];
-        if (std::isnan(p.temperature)) return fail(PN_EINVAL, "row %d: temperature is NaN", b);
-        if (p.temperature > 0.f) {
-            if (!std::isfinite(p.temperature)) return fail(PN_EINVAL, "row %d: temperature must be finite", b);
-            if (p.top_k < 1 || p.top_k > kSampleMaxK)
-                return fail(PN_EUNSUPPORTED, "row %d: top_k = %d outside [1, %d]", b, p.top_k, kSampleMaxK);
-            if (!(p.repeat_penalty > 0.f) || !std::isfinite(p.repeat_penalty))
-                return fail(PN_EINVAL, "row %d: repeat_penalty must be finite and > 0", b);
-            if (std::isnan(p.top_p)) return fail(PN_EINVAL, "row %d: top_p is NaN", b);
-        }
-        a.temp[b] = p.temperature;
-        a.rp[b] = p.repeat_penalty;
-        a.top_p[b] = p.top_p;
-        a.top_k[b] = p.top_k;
-    }
-    hipStream_t st = S(stream);
-    // the histogram and the gather counters start each call at zero: the
-    // previous call's k_sample_pick cleared them, unless that call stopped early
-    if (m->samp_dirty) {
-        fill32(m->base + m->samp_hist, (size_t)m->cfg.max_batch * kSampleBins, 0u, st);
-        fill32(m->base + m->samp_cnt, (size_t)m->cfg.max_batch * 2, 0u, st);
-        if (int rc = launched("sampling scratch clear")) return rc;
-        m->samp_dirty = false;
-    }
-    // the candidate buffer is dynamic LDS; with the kernel's static LDS the
-    // total passes 64 KiB, which needs the attribute (the two within 160 KiB)
-    static bool lds_set = false;
-    const size_t lds = (size_t)kSampleCap * 8;
-    if (!lds_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_sample_pick),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return fail(PN_EHIP, "sampling LDS attribute: %s", hipGetErrorString(e));
-        lds_set = true;
-    }
-    m->samp_dirty = true;
-    hipLaunchKernelGGL(k_sample_keys, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
-    if (int rc = launched("sampling keys")) return rc;
-    hipLaunchKernelGGL(k_sample_gather, dim3(kSampleBlocks, n), dim3(256), 0, st, a);
-    if (int rc = launched("sampling gather")) return rc;
-    hipLaunchKernelGGL(k_sample_pick, dim3(n), dim3(kSamplePick), lds, st, a);
-    if (int rc = launched("sampling pick")) return rc;
-    m->samp_dirty = false;
-    return PN_OK;
+    SampleScratchPtrs sp{(unsigned *)(m->base + m->samp_keys), (unsigned *)(m->base + m->samp_hist),
+                         (unsigned *)(m->base + m->samp_cnt), (unsigned long long *)(m->base + m->samp_cand)};
+    return host_sample(logits_dev, n, m->V, params, recent_dev, n_recent, u_dev, ids_dev, sp, m->cfg.max_batch,
+                       m->samp_dirty, S(stream));
 }
 
 int pn_forward_step(pn_model *m, pn_state *s, const int32_t *token_dev, float *logits_dev, int32_t *argmax_dev,
@@ -1847,6 +1930,30 @@ int pn_profile_end(pn_model *m, void *stream, double *total_ms, int64_t *launche
     *launches = (int64_t)(m->ev_used / 2);
     m->ev_used = 0;
     return PN_OK;
+}
+
+int pn_model_route_log(pn_model *m, int32_t *log_dev, int32_t n_steps) {
+    g_err.clear();
+    if (!m) return fail(PN_EINVAL, "model is NULL");
+    if (m->cfg.n_expert == 0) return fail(PN_EINVAL, "a dense model has no routing to record");
+    if (log_dev && n_steps < 1) return fail(PN_EINVAL, "n_steps must be >= 1");
+    m->route_log = log_dev;
+    m->route_log_steps = log_dev ? n_steps : 0;
+    m->route_log_step = 0;
+    return PN_OK;
+}
+
+int pn_stream_read(const void *src_dev, size_t bytes, uint32_t *sink_dev, void *stream) {
+    g_err.clear();
+    if (!src_dev || !sink_dev) return fail(PN_EINVAL, "NULL argument");
+    if (bytes == 0 || bytes % 16 != 0) return fail(PN_EINVAL, "bytes must be a positive multiple of 16");
+    if (((uintptr_t)src_dev & 15) != 0) return fail(PN_EINVAL, "src_dev must be 16-byte aligned");
+    // eight work-groups of 256 threads per compute unit keep enough loads in flight
+    const long long n16 = (long long)(bytes / 16);
+    const int groups = (int)std::min<long long>(kCUs * 8, cdiv(n16, 256LL));
+    hipLaunchKernelGGL(k_stream_read, dim3(groups), dim3(256), 0, S(stream), (const u32x4 *)src_dev, n16,
+                       (unsigned *)sink_dev);
+    return launched("stream read");
 }
 
 const char *pn_last_error(void) { return g_err.c_str(); }

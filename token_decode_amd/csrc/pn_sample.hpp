@@ -25,15 +25,12 @@
 // a few, a bitonic network in LDS for many) and applies top-p and the draw
 // with an fp64 prefix sum.
 #pragma once
+#include "pn_host.hpp"
 #include "pn_kernels.hpp"
 
 namespace pn {
 
-constexpr int kSampleMaxK = 4096;       // largest top_k
-constexpr int kSampleCap = 8192;        // candidates held in LDS
-constexpr int kSampleBins = 4096;       // histogram bins per level (12 key bits)
 constexpr int kSampleBlocks = 64;       // key and gather work-groups per row
-constexpr int kSampleMaxRecent = 1024;  // tokens of a row's recent window
 constexpr int kSampleTab = 2048;        // recent-token hash table slots
 constexpr int kSamplePick = 1024;       // threads of k_sample_pick
 constexpr int kSampleU = 16;            // key loads a thread of k_sample_pick keeps in flight

@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(256) k_argmax(const float *val, const int *idx
 template <int RT, int AT>
 __global__ void __launch_bounds__(256) k_router(const float *x, const float *gain, const void *wr, int E,
                                                  int n_expert, int k_used, float eps, const float *ssp, int ssp_ld,
-                                                 int ssp_n, int *ids, float *wts) {
+                                                 int ssp_n, int *ids, float *wts, int *ids_log) {
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     extern __shared__ float xs[];  // [E]
     __shared__ float red4[4];
@@ -240,6 +240,7 @@ __global__ void __launch_bounds__(256) k_router(const float *x, const float *gai
         for (int a2 = 0; a2 < k_used; ++a2) {
             ids[b * k_used + a2] = sel[a2];
             wts[b * k_used + a2] = pe[a2] / den;
+            if (ids_log) ids_log[b * k_used + a2] = sel[a2];  // the caller's routing record
         }
     }
 }
@@ -428,6 +429,29 @@ __global__ void __launch_bounds__(256) k_copy_rows_f32(float *dst, const float *
 __global__ void __launch_bounds__(256) k_fill32(uint32_t *p, long long n, uint32_t v) {
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
         p[i] = v;
+}
+
+// A plain streaming read of n16 16-byte words (nontemporal loads, four in
+// flight per thread), folded into one xor per work-group so that no load is
+// dead: the measured read ceiling of HBM that the decode kernels are held to.
+__global__ void __launch_bounds__(256) k_stream_read(const u32x4 *src, long long n16, unsigned *sink) {
+    const long long stride = (long long)gridDim.x * 256;
+    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    unsigned acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
 }
 
 __global__ void __launch_bounds__(256) k_iota(int *p, int n) {
