@@ -331,6 +331,20 @@ typedef struct pn_sampling_params {
 int pn_sample(pn_model *m, const float *logits_dev, int32_t n, const pn_sampling_params *params,
               const int32_t *recent_dev, int32_t n_recent, const float *u_dev, int32_t *ids_dev, void *stream);
 
+/* Sampling for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same sampler as pn_sample, with no model.  Its scratch is a file-scope
+ * device array of fixed size (about 17 MB, held on each GPU the library runs
+ * on until the process ends), so it needs no buffer from the caller; rows and
+ * vocabulary are bounded by that array: 1 <= n <= 16, 1 <= n_vocab <= 262144
+ * (PN_EINVAL beyond).  The call allocates nothing.  All calls on one GPU share
+ * its array: calls that overlap on one GPU (other streams, other threads)
+ * race, so order them.  Arguments, outputs and other errors as pn_sample,
+ * with n_vocab giving the row length of logits_dev. */
+int pn_sample_noalloc(const float *logits_dev, int32_t n, int32_t n_vocab, const pn_sampling_params *params,
+                      const int32_t *recent_dev, int32_t n_recent, const float *u_dev, int32_t *ids_dev,
+                      void *stream);
+
 /* ---- tuning and measurement ------------------------------------------------ */
 
 /* Kernel classes, for timing. */

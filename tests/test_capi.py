@@ -271,3 +271,18 @@ def test_route_log_and_stream_read_arguments():
     assert L.pn_stream_read(None, 1024, fake, None) == C.PN_EINVAL
     assert L.pn_stream_read(fake, 1000, fake, None) == C.PN_EINVAL
     assert L.pn_stream_read(ctypes.c_void_p((1 << 20) + 4), 1024, fake, None) == C.PN_EINVAL
+
+
+def test_sample_noalloc_rejects_sizes_past_its_array():
+    """pn_sample_noalloc's bounds are checked on the host, before any device work."""
+    L = C.lib()
+    sp = (C.pn_sampling_params * 1)()
+    sp[0].temperature, sp[0].repeat_penalty, sp[0].top_k, sp[0].top_p = 1.0, 1.0, 40, 0.9
+    d = ctypes.c_void_p(1 << 22)
+    assert L.pn_sample_noalloc(d, 0, 1000, sp, None, 0, d, d, None) == C.PN_EINVAL
+    assert L.pn_sample_noalloc(d, 17, 1000, sp, None, 0, d, d, None) == C.PN_EINVAL
+    assert L.pn_sample_noalloc(d, 1, 0, sp, None, 0, d, d, None) == C.PN_EINVAL
+    assert L.pn_sample_noalloc(d, 1, 262145, sp, None, 0, d, d, None) == C.PN_EINVAL
+    assert L.pn_sample_noalloc(None, 1, 1000, sp, None, 0, d, d, None) == C.PN_EINVAL
+    assert L.pn_sample_noalloc(d, 1, 262145, sp, None, 0, d, d, None) == C.PN_EINVAL
+    assert b"262144" in L.pn_last_error()

@@ -38,7 +38,7 @@ ATTN_UNITS = [(d, kv) for d in (32, 64, 128) for kv in (0, 1, 2)]  # kv: fp32, b
 
 
 def _units():
-    units = [("pn_lib.o", "pn_lib.hip", [])]
+    units = [("pn_lib.o", "pn_lib.hip", []), ("pn_noalloc.o", "pn_noalloc.hip", [])]
     for d, kv in ATTN_UNITS:
         units.append(("attn_%d_%d.o" % (d, kv), "pn_attn.hip",
                       ["-DPN_D=%d" % d, "-DPN_KV=%d" % kv, "-DPN_NAME=launch_attn_%d_%d" % (d, kv)]))
