@@ -402,6 +402,17 @@ int pn_profile_replay(pn_model *m, int32_t kernel, int32_t reps, void *stream);
  * model, a dense model, n_steps < 1). */
 int pn_model_route_log(pn_model *m, int32_t *log_dev, int32_t n_steps);
 
+/* Residual trace, for checking a deep model one layer at a time (each layer is
+ * a function of its input residual, the cache and the position, so a
+ * reference can recompute any layer from the device's own input).  With
+ * trace_dev non-NULL, each later decode call (pn_forward_step,
+ * pn_forward_batch) copies the fp32 residual stream x of its rows as it enters
+ * each layer, and as it leaves the last one, into
+ * trace_dev[n_layer + 1][max_batch][n_embd] (device, caller-owned; rows past
+ * the call's n are not written): one device-to-device copy per layer on the
+ * call's stream.  NULL turns it off.  Errors: PN_EINVAL (NULL model). */
+int pn_model_trace(pn_model *m, float *trace_dev);
+
 /* Streaming read ceiling, for measurement: read `bytes` (a positive multiple
  * of 16) of device memory at src_dev (16-byte aligned) with 16-byte loads
  * spread over every compute unit, and xor them into *sink_dev (one device

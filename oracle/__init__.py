@@ -88,6 +88,12 @@ def lib():
         L.orc_step.restype = i32
         L.orc_step_ex.argtypes = [P(Config), vp, vp, i32, vp, i32, vp, vp, vp, ctypes.c_uint64]
         L.orc_step_ex.restype = i32
+        L.orc_embed.argtypes = [P(Config), vp, i32, vp]
+        L.orc_embed.restype = i32
+        L.orc_layer.argtypes = [P(Config), vp, vp, i32, i32, vp, vp, i32, i32, vp]
+        L.orc_layer.restype = dbl
+        L.orc_head.argtypes = [P(Config), vp, vp, vp, i32]
+        L.orc_head.restype = i32
         L.orc_round_store.argtypes = [dbl, i32]
         L.orc_round_store.restype = dbl
         L.orc_set_perturbation.argtypes = [dbl, ctypes.c_uint64]
@@ -266,6 +272,20 @@ class Model:
     def new_state(self, max_ctx):
         return State(self, max_ctx)
 
+    def embed(self, token):
+        """The token's embedding row (fp64 [E])."""
+        x = np.empty(self.wl.n_embd)
+        if lib().orc_embed(ctypes.byref(self.cfg), self.tab, int(token), _ptr(x)) != 0:
+            raise ValueError("token out of range")
+        return x
+
+    def head(self, x, threads=1):
+        """Logits (fp64 [V]) and greedy id of a final residual x [E]."""
+        x = _f64(x)
+        logits = np.empty(self.wl.n_vocab)
+        am = lib().orc_head(ctypes.byref(self.cfg), self.tab, _ptr(x), _ptr(logits), threads)
+        return logits, am
+
     def full_recompute(self, tokens, threads=1):
         tokens = np.ascontiguousarray(tokens, dtype=np.int32)
         logits = np.empty(self.wl.n_vocab)
@@ -301,6 +321,19 @@ class State:
         rc = lib().orc_state_set_kv(self.h, layer, pos0, k.shape[0], _ptr(k), _ptr(v))
         if rc != 0:
             raise ValueError("set_kv out of range")
+
+    def layer(self, l, pos, x, threads=1, swap=False, want_route=False):
+        """Layer l applied to x [E] at position pos: the output residual (fp64 [E]),
+        with the layer's k, v appended to this state's cache at pos (pos not
+        moved); with want_route also the chosen experts and the router gap."""
+        x = _f64(x)
+        out = np.empty_like(x)
+        ids = np.zeros(max(1, self.model.wl.n_expert_used), dtype=np.int32)
+        gap = lib().orc_layer(ctypes.byref(self.model.cfg), self.model.tab, self.h, int(l), int(pos), _ptr(x),
+                              _ptr(out), threads, int(bool(swap)), _ptr(ids))
+        if gap < -1e300:
+            raise ValueError("bad layer or position")
+        return (out, ids, gap) if want_route else out
 
     def step(self, token, threads=1, want_route=False, swap_mask=0, want_gaps=False):
         """One decode step. Returns (logits float64 [V], argmax id[, route ids, route gap]

@@ -613,6 +613,56 @@ static void embed(const orc_config *c, const void *const *tab, int token, double
 
 /* ------------------------------------------------------------------ decode step */
 
+/* Layer l of one token at position p: x += attention(...) + FFN(...), with
+ * the token's k, v appended to the state's cache at p (state->pos is not
+ * moved).  Returns the router's fp32 k-th/(k+1)-th gap (+inf for dense);
+ * `ids` (optional, [n_expert_used]) receives the chosen experts and `swap`
+ * routes to the (k+1)-th expert in place of the k-th. */
+static double layer_step(const orc_config *c, const void *const *tab, orc_state *st, int l, int p, double *x,
+                         scratch *s, int32_t *ids, int swap) {
+    int d = c->head_dim, H = c->n_head, Hk = c->n_kv_head;
+    int lb = T_LAYER0 + l * orc_layer_stride(c);
+    int t0 = (c->sliding_window > 0 && p - c->sliding_window + 1 > 0) ? p - c->sliding_window + 1 : 0;
+    int n = p - t0 + 1;
+    double *K = malloc(sizeof(double) * (size_t)Hk * n * d);
+    double *V = malloc(sizeof(double) * (size_t)Hk * n * d);
+    double *rk = malloc(sizeof(double) * d), *rv = malloc(sizeof(double) * d);
+    qkv(c, tab, lb, x, p, s);
+    for (int j = 0; j < Hk; ++j) {
+        kv_round_head(c, s->k + (size_t)j * d, d, rk);
+        kv_round_head(c, s->v + (size_t)j * d, d, rv);
+        for (int i = 0; i < d; ++i) {
+            size_t at = ((size_t)j * st->max_ctx + (size_t)p) * d + (size_t)i;
+            store_kv(st->k[l], kv_store_dt(c), at, rk[i]);
+            store_kv(st->v[l], kv_store_dt(c), at, rv[i]);
+        }
+    }
+    /* the window's cached keys and values, widened to double, [Hk][n][d] */
+    for (int j = 0; j < Hk; ++j)
+        for (int t = 0; t < n; ++t)
+            for (int i = 0; i < d; ++i) {
+                size_t src = ((size_t)j * st->max_ctx + (size_t)(t0 + t)) * d + (size_t)i;
+                size_t dst = ((size_t)j * n + (size_t)t) * d + (size_t)i;
+                K[dst] = rd(st->k[l], kv_store_dt(c), src);
+                V[dst] = rd(st->v[l], kv_store_dt(c), src);
+            }
+    /* keys are the window only, so position p sits at index n-1 and W is not re-applied */
+    orc_attention(s->q, K, V, H, Hk, d, n, n - 1, 0, s->o);
+    attn_out(c, tab, lb, x, s);
+    double gap = ffn(c, tab, lb, x, s, ids, swap);
+    free(K);
+    free(V);
+    free(rk);
+    free(rv);
+    return gap;
+}
+
+static int check_step_args(const orc_config *c, const orc_state *st, int p) {
+    if (p < 0 || p >= st->max_ctx) return -2;
+    if (c->head_dim < 2 || c->head_dim % 2 || c->n_head % c->n_kv_head) return -4;
+    return 0;
+}
+
 /* One decode step: append the token's k, v at state->pos, attend, write the
  * logits [V] and return the greedy id (or a negative error).  `route_ids`
  * (optional, [n_layer][n_expert_used]) receives the experts each layer chose,
@@ -623,61 +673,61 @@ static void embed(const orc_config *c, const void *const *tab, int token, double
 int orc_step_ex(const orc_config *c, const void *const *tab, orc_state *st, int token,
                 double *logits, int nthreads, int32_t *route_ids, double *layer_gaps,
                 double *route_gap, uint64_t swap_mask) {
-    int E = c->n_embd, d = c->head_dim, H = c->n_head, Hk = c->n_kv_head;
     int p = st->pos;
     if (token < 0 || token >= c->n_vocab) return -3;
-    if (p < 0 || p >= st->max_ctx) return -2;
-    if (c->head_dim < 2 || c->head_dim % 2 || c->n_head % c->n_kv_head) return -4;
+    if (check_step_args(c, st, p)) return check_step_args(c, st, p);
     g_threads = nthreads > 0 ? nthreads : 1;
     scratch s;
     scratch_new(c, &s);
-    double *x = malloc(sizeof(double) * E);
-    double *rk = malloc(sizeof(double) * d), *rv = malloc(sizeof(double) * d);
-    int t0 = (c->sliding_window > 0 && p - c->sliding_window + 1 > 0) ? p - c->sliding_window + 1 : 0;
-    int n = p - t0 + 1;
-    double *K = malloc(sizeof(double) * (size_t)Hk * n * d);
-    double *V = malloc(sizeof(double) * (size_t)Hk * n * d);
+    double *x = malloc(sizeof(double) * c->n_embd);
     double gap = INFINITY;
     embed(c, tab, token, x);
     for (int l = 0; l < c->n_layer; ++l) {
-        int lb = T_LAYER0 + l * orc_layer_stride(c);
-        qkv(c, tab, lb, x, p, &s);
-        for (int j = 0; j < Hk; ++j) {
-            kv_round_head(c, s.k + (size_t)j * d, d, rk);
-            kv_round_head(c, s.v + (size_t)j * d, d, rv);
-            for (int i = 0; i < d; ++i) {
-                size_t at = ((size_t)j * st->max_ctx + (size_t)p) * d + (size_t)i;
-                store_kv(st->k[l], kv_store_dt(c), at, rk[i]);
-                store_kv(st->v[l], kv_store_dt(c), at, rv[i]);
-            }
-        }
-        /* the window's cached keys and values, widened to double, [Hk][n][d] */
-        for (int j = 0; j < Hk; ++j)
-            for (int t = 0; t < n; ++t)
-                for (int i = 0; i < d; ++i) {
-                    size_t src = ((size_t)j * st->max_ctx + (size_t)(t0 + t)) * d + (size_t)i;
-                    size_t dst = ((size_t)j * n + (size_t)t) * d + (size_t)i;
-                    K[dst] = rd(st->k[l], kv_store_dt(c), src);
-                    V[dst] = rd(st->v[l], kv_store_dt(c), src);
-                }
-        /* keys are the window only, so position p sits at index n-1 and W is not re-applied */
-        orc_attention(s.q, K, V, H, Hk, d, n, n - 1, 0, s.o);
-        attn_out(c, tab, lb, x, &s);
-        double gl = ffn(c, tab, lb, x, &s,
-                        route_ids ? route_ids + (size_t)l * (c->n_expert > 0 ? c->n_expert_used : 1)
-                                  : NULL,
-                        l < 64 && ((swap_mask >> l) & 1));
+        double gl = layer_step(c, tab, st, l, p, x, &s,
+                               route_ids ? route_ids + (size_t)l * (c->n_expert > 0 ? c->n_expert_used : 1) : NULL,
+                               l < 64 && ((swap_mask >> l) & 1));
         if (layer_gaps) layer_gaps[l] = gl;
         if (gl < gap) gap = gl;
     }
     head(c, tab, x, logits, &s);
     st->pos = p + 1;
     if (route_gap) *route_gap = gap;
-    free(K);
-    free(V);
-    free(rk);
-    free(rv);
     free(x);
+    scratch_free(&s);
+    return orc_argmax(logits, c->n_vocab);
+}
+
+/* The step's parts, for checking a deep model one layer at a time from
+ * inputs given by the caller (a layer is a function of its input x, the
+ * cache and the position).  orc_embed: x_out [E] = the token's embedding row.
+ * orc_layer: x_out = layer l applied to x_in at position pos (the layer's k,
+ * v appended to the state's cache at pos; pos not moved); returns the router
+ * gap as layer_step, or a value < -1e300 on a bad argument.  orc_head: the
+ * logits [V] of x_in (final RMSNorm, LM head) and the greedy id.  Running
+ * orc_embed, every orc_layer and orc_head in turn is orc_step. */
+int orc_embed(const orc_config *c, const void *const *tab, int token, double *x_out) {
+    if (token < 0 || token >= c->n_vocab) return -3;
+    embed(c, tab, token, x_out);
+    return 0;
+}
+
+double orc_layer(const orc_config *c, const void *const *tab, orc_state *st, int l, int pos, const double *x_in,
+                 double *x_out, int nthreads, int swap, int32_t *ids) {
+    if (l < 0 || l >= c->n_layer || check_step_args(c, st, pos)) return -INFINITY;
+    g_threads = nthreads > 0 ? nthreads : 1;
+    scratch s;
+    scratch_new(c, &s);
+    memcpy(x_out, x_in, sizeof(double) * (size_t)c->n_embd);
+    double gap = layer_step(c, tab, st, l, pos, x_out, &s, ids, swap);
+    scratch_free(&s);
+    return gap;
+}
+
+int orc_head(const orc_config *c, const void *const *tab, const double *x_in, double *logits, int nthreads) {
+    g_threads = nthreads > 0 ? nthreads : 1;
+    scratch s;
+    scratch_new(c, &s);
+    head(c, tab, x_in, logits, &s);
     scratch_free(&s);
     return orc_argmax(logits, c->n_vocab);
 }

@@ -204,3 +204,27 @@ def test_bf16_rounding_sensitivity_llama3_8b_int8():
     """The experiment at the Llama-3-8B INT8 workload's full shape (32 layers)."""
     wl = synth.llama3_8b_int8().with_(name="perturb-llama3-8b-int8")
     _perturbation_spread(wl, (1e-8, 3e-8, 1e-7, 3e-7, 1e-6), steps=1, p0=256)
+
+
+# ----------------------------------------------------------------------------- the step in parts
+
+@pytest.mark.parametrize("wl", [RESUME[0], RESUME[1], RESUME[5]], ids=lambda w: w.name)
+def test_step_in_parts_equals_step(wl):
+    """embed, then every layer, then the head, each from the previous output,
+    is the step itself bit for bit (the parts checked one by one against a
+    device's own layer inputs must be the pinned step)."""
+    W = synth.make_weights(wl)
+    m = oracle.Model(wl, W)
+    toks = [int(t) for t in synth.uniform_int(wl.seed, 96, 6, 0, wl.n_vocab - 1)]
+    a, b = m.new_state(8), m.new_state(8)
+    for p, t in enumerate(toks):
+        la, ia = a.step(t)
+        x = m.embed(t)
+        for l in range(wl.n_layer):
+            x = b.layer(l, p, x)
+        lb, ib = m.head(x)
+        b.pos = p + 1
+        np.testing.assert_array_equal(la, lb)
+        assert ia == ib
+    with pytest.raises(ValueError):
+        b.layer(wl.n_layer, 0, x)

@@ -98,6 +98,7 @@ def lib():
             "pn_profile_replay": (ctypes.c_int, [vp, i32, i32, vp]),
             "pn_sample_noalloc": (ctypes.c_int, [vp, i32, i32, P(pn_sampling_params), vp, i32, vp, vp, vp]),
             "pn_model_route_log": (ctypes.c_int, [vp, vp, i32]),
+            "pn_model_trace": (ctypes.c_int, [vp, vp]),
             "pn_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
             "pn_last_error": (ctypes.c_char_p, []),
         }
@@ -117,7 +118,7 @@ EXPORTS = ["pn_config_default", "pn_config_check", "pn_model_bytes", "pn_model_c
            "pn_pool_bytes", "pn_pool_new", "pn_pool_free_pages", "pn_pool_free", "pn_state_bytes_pooled",
            "pn_state_new_pooled",
            "pn_forward_step", "pn_forward_batch", "pn_prefill", "pn_sample", "pn_sample_noalloc", "pn_model_set_option", "pn_profile_begin",
-           "pn_profile_end", "pn_profile_replay", "pn_model_route_log", "pn_stream_read", "pn_last_error"]
+           "pn_profile_end", "pn_profile_replay", "pn_model_route_log", "pn_model_trace", "pn_stream_read", "pn_last_error"]
 
 
 def check(rc):

@@ -90,6 +90,9 @@ struct pn_model {
     int *route_log = nullptr;
     int route_log_steps = 0;
     long long route_log_step = 0;
+    // residual trace (pn_model_trace): x entering each layer and leaving the last,
+    // [n_layer + 1][max_batch][n_embd] fp32
+    float *trace = nullptr;
     size_t samp_keys = 0, samp_hist = 0, samp_cnt = 0, samp_cand = 0;  // pn_sample scratch
     bool samp_dirty = false;  // a pn_sample call stopped before k_sample_pick cleared its histogram
     size_t attn_part = 0, attn_part_row = 0;  // pn_prefill: per-row attention split scratch
@@ -757,6 +760,15 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                                rope, omega, m->D, ssp, m->ssp_ld);
     }
 
+    // the residual trace: x as it enters layer l (and, at n_layer, as it leaves the last)
+    auto trace_x = [&](int l) -> int {
+        if (!m->trace || row_pos) return PN_OK;
+        const hipError_t e = hipMemcpyAsync(m->trace + (size_t)l * c.max_batch * E, x, (size_t)n * E * 4,
+                                            hipMemcpyDeviceToDevice, s);
+        return e == hipSuccess ? PN_OK : fail(PN_EHIP, "residual trace copy: %s", hipGetErrorString(e));
+    };
+    if (int rc = trace_x(0)) return rc;
+
     // attention geometry per slot
     AttnArgs aa{};
     const int nsplit_max = attn_setup(m, st, n, pos_of_rows, row_pos != nullptr, aa);
@@ -975,6 +987,7 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
                                    (float *)(mb + m->ssp), m->ssp_ld);
             }
         }
+        if (int rc = trace_x(l + 1)) return rc;
     }
     // ---- final norm + LM head + argmax
     {
@@ -1943,14 +1956,21 @@ int pn_model_route_log(pn_model *m, int32_t *log_dev, int32_t n_steps) {
     return PN_OK;
 }
 
+int pn_model_trace(pn_model *m, float *trace_dev) {
+    g_err.clear();
+    if (!m) return fail(PN_EINVAL, "model is NULL");
+    m->trace = trace_dev;
+    return PN_OK;
+}
+
 int pn_stream_read(const void *src_dev, size_t bytes, uint32_t *sink_dev, void *stream) {
     g_err.clear();
     if (!src_dev || !sink_dev) return fail(PN_EINVAL, "NULL argument");
     if (bytes == 0 || bytes % 16 != 0) return fail(PN_EINVAL, "bytes must be a positive multiple of 16");
     if (((uintptr_t)src_dev & 15) != 0) return fail(PN_EINVAL, "src_dev must be 16-byte aligned");
-    // eight work-groups of 256 threads per compute unit keep enough loads in flight
+    // eight work-groups of 256 threads per compute unit, eight loads in flight per thread
     const long long n16 = (long long)(bytes / 16);
-    const int groups = (int)std::min<long long>(kCUs * 8, cdiv(n16, 256LL));
+    const int groups = (int)std::min<long long>(kCUs * 8, cdiv(n16, 256LL * 8));
     hipLaunchKernelGGL(k_stream_read, dim3(groups), dim3(256), 0, S(stream), (const u32x4 *)src_dev, n16,
                        (unsigned *)sink_dev);
     return launched("stream read");

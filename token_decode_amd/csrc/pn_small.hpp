@@ -431,23 +431,24 @@ __global__ void __launch_bounds__(256) k_fill32(uint32_t *p, long long n, uint32
         p[i] = v;
 }
 
-// A plain streaming read of n16 16-byte words (nontemporal loads, four in
-// flight per thread), folded into one xor per work-group so that no load is
-// dead: the measured read ceiling of HBM that the decode kernels are held to.
+// A plain streaming read of n16 16-byte words, folded into one xor per wave
+// so that no load is dead: the measured read ceiling of HBM that the decode
+// kernels are held to.  Each pass a work-group reads 256 * 8 consecutive
+// words (32 KiB, eight nontemporal loads in flight per thread), then strides
+// by the grid.
 __global__ void __launch_bounds__(256) k_stream_read(const u32x4 *src, long long n16, unsigned *sink) {
-    const long long stride = (long long)gridDim.x * 256;
-    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    constexpr int U = 8;
+    const long long stride = (long long)gridDim.x * 256 * U;
     unsigned acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        u32x4 v[4];
+    for (long long base = (long long)blockIdx.x * 256 * U + threadIdx.x; base < n16; base += stride) {
+        u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+        for (int u = 0; u < U; ++u) {
+            const long long i = base + (long long)u * 256;
+            v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
+        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
-    }
-    for (; i < n16; i += stride) {
-        const u32x4 v = __builtin_nontemporal_load(src + i);
-        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+        for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
