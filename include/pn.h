@@ -415,8 +415,9 @@ int pn_model_trace(pn_model *m, float *trace_dev);
 
 /* Streaming read ceiling, for measurement: read `bytes` (a positive multiple
  * of 16) of device memory at src_dev (16-byte aligned) with 16-byte loads
- * spread over every compute unit, and xor them into *sink_dev (one device
- * word, caller-owned).  Its achieved bandwidth is the measured read ceiling
+ * spread over every compute unit (their xor reaches *sink_dev, one device
+ * word, caller-owned, only in the rare case that it equals a fixed constant:
+ * the sink keeps the loads live and is not a checksum).  Its achieved bandwidth is the measured read ceiling
  * that the decode kernels' HBM rates are set against.  Errors: PN_EINVAL. */
 int pn_stream_read(const void *src_dev, size_t bytes, uint32_t *sink_dev, void *stream);
 

@@ -228,3 +228,28 @@ def test_step_in_parts_equals_step(wl):
         assert ia == ib
     with pytest.raises(ValueError):
         b.layer(wl.n_layer, 0, x)
+
+
+# ----------------------------------------------------------------------------- routing branches
+
+def test_routing_branch_check_finds_a_planted_swap():
+    """The MoE parity harness, on the host: a "device" row planted from the
+    oracle's branch with layer 1's k-th and (k+1)-th experts swapped is matched
+    to that branch (with every layer treated as a near tie), the oracle state
+    is left in it, and a row that matches no branch is rejected."""
+    import harness
+    wl = synth.tiny_fp32().with_(name="branch", n_expert=4, n_expert_used=2, n_ff=96, seed=38)
+    m = oracle.Model(wl, synth.make_weights(wl))
+    a = m.new_state(4)
+    base, _ = m.new_state(4).step(7)
+    planted, pid = a.step(7, swap_mask=0b10)
+    assert np.linalg.norm(planted - base) > 1e-3 * np.linalg.norm(base)  # the swap matters
+    b = m.new_state(4)
+    rel, near, mask, oid = harness.moe_step_branches(wl, b, 7, planted, pid, route_tol=1e9, threads=1, tol=1e-12)
+    assert mask == 0b10 and oid == pid and rel < 1e-12 and b.pos == 1
+    la, _ = a.step(3)
+    lb, _ = b.step(3)
+    np.testing.assert_array_equal(la, lb)
+    c = m.new_state(4)
+    with pytest.raises(AssertionError):
+        harness.moe_step_branches(wl, c, 7, planted * 1.1, pid, route_tol=1e9, threads=1, tol=1e-12)

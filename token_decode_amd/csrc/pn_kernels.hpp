@@ -37,15 +37,17 @@ constexpr int kMaxG = 8;       // query heads per KV head
 // that each load instruction of a wave reads one contiguous run:
 //   K: [key / 16][dim / 32][((dim % 32) / 8) * 16 + key % 16][dim % 8]
 //      (a 16x16x32 A fragment per 16 keys and 32 dims, 1 KiB),
-//   V: [key / 16][dim / 16][((key % 16) / 4) * 16 + dim % 16][key % 4]
-//      (a 16x16x16 A fragment per 16 keys and 16 dims, 512 B).
+//   V: [key / 16][dim / 32][((key % 16) / 4) * 16 + dim % 16][(dim % 32) / 16][key % 4]
+//      (the 16x16x16 A fragments of 16 keys for dims d..d+15 and d+16..d+31,
+//      interleaved per lane, so one 16-byte load per lane reads both: 1 KiB).
 // Offsets are in elements from the start of the head's block.
 __host__ __device__ constexpr long long kv_k_off(bool tiled, int key, int d, int D) {
     return tiled ? ((long long)((key / 16) * (D / 32) + d / 32) * 64 + ((d % 32) / 8) * 16 + key % 16) * 8 + d % 8
                  : (long long)key * D + d;
 }
 __host__ __device__ constexpr long long kv_v_off(bool tiled, int key, int d, int D) {
-    return tiled ? ((long long)((key / 16) * (D / 16) + d / 16) * 64 + ((key % 16) / 4) * 16 + d % 16) * 4 + key % 4
+    return tiled ? ((long long)((key / 16) * (D / 32) + d / 32) * 64 + ((key % 16) / 4) * 16 + d % 16) * 8 +
+                       ((d % 32) / 16) * 4 + key % 4
                  : (long long)d * kPage + key;
 }
 
@@ -1344,6 +1346,7 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, const AttnRow &R, i
     } else if constexpr (KV == 1) {
         // tiled (kv_k_off / kv_v_off): piece dq + 4c of key row tq % 16 is 16 bytes of
         // the group's 1 KiB step c; the 4 keys 4q..4q+3 of a dim are 8 contiguous bytes
+        // (next to the same keys of dim + 16 or dim - 16)
         const uint8_t *gk = reinterpret_cast<const uint8_t *>(R.kvk) + (hb + (long long)(k0 % kPage) * D) * 2;
 #pragma unroll
         for (int c = 0; c < S::NKL; ++c)
@@ -1354,7 +1357,8 @@ __device__ __forceinline__ void attn_load(const AttnArgs &a, const AttnRow &R, i
             const int d = dl + e;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const u32x2 t = *reinterpret_cast<const u32x2 *>(gv + (((d / 16) * 64 + q * 16 + d % 16) * 4) * 2);
+                const u32x2 t = *reinterpret_cast<const u32x2 *>(
+                    gv + (((d / 32) * 64 + q * 16 + d % 16) * 8 + ((d % 32) / 16) * 4) * 2);
                 col[e][4 * q] = t[0] & 0xFFFFu;
                 col[e][4 * q + 1] = t[0] >> 16;
                 col[e][4 * q + 2] = t[1] & 0xFFFFu;
@@ -1619,8 +1623,8 @@ __device__ __forceinline__ void bf16_pieces(float x, uint32_t &b0, uint32_t &b1,
 // 16x16x16 step over keys, so the softmax stays in the lane and the weights
 // (again three bf16 pieces) feed
 //   O^T[d][g] += sum_key V^T[d][key] * P^T[key][g]
-// with V fragments (stored in operand order too, see kv_v_off: 512 B per
-// load) as the A operand; keys of a fragment outside the window are zeroed
+// with V fragments (stored in operand order too, see kv_v_off: two fragments
+// per 16-byte lane load, 1 KiB per load) as the A operand; keys of a fragment outside the window are zeroed
 // (their weight is 0, and 0 * NaN is not) and rows of K outside it are masked
 // after the scores.  The output tile's column is again the lane's head, the one whose
 // running max the lane keeps (its running sum covers the lane's own keys and
@@ -1658,7 +1662,11 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
         return ci < 64 ? __builtin_amdgcn_readlane(vpg, ci) : ptb[ci];
     };
     // buffer loads over the layer's pools: an offset past the pool reads zeros
-    // without a memory access, which is how chunks past the split are loaded
+    // without a memory access, which is how chunks past the split are loaded.
+    // Their base offset is 2^31: a layer's pool is smaller (the host refuses
+    // 2 GiB), and adding the fragment steps (under 8 KiB) keeps every such
+    // offset past the pool without wrapping round to the pool's start.
+    constexpr unsigned kPast = 0x80000000u;
     constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) access
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(R.kvk), (short)0, (int)R.kv_bytes, kRsrcWord3);
@@ -1667,12 +1675,17 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     auto load = [&](int ci, u32x4 (&kr)[KS], u32x2 (&vr)[DT]) {
         // the wave's 16-key group of the page's head block (16 * D elements of K and of V)
         const unsigned gb = (unsigned)((((long long)page_of(ci) * a.Hk + j) * kPage + w * 16) * D * 2);
-        const unsigned ko = ci < nch ? gb + lane * 16 : 0xFFFFFFF0u;
-        const unsigned vo = ci < nch ? gb + lane * 8 : 0xFFFFFFF0u;
+        const unsigned ko = ci < nch ? gb + lane * 16 : kPast;
+        const unsigned vo = ci < nch ? gb + lane * 16 : kPast;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kr[ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(ko + ks * 1024), 0, 0);
+        // one 16-byte load per lane holds its fragments of output tiles 2p and 2p + 1
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vr[dt] = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(vo + dt * 512), 0, 0);
+        for (int dp = 0; dp < DT / 2; ++dp) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(vo + dp * 1024), 0, 0);
+            vr[2 * dp] = u32x2{t[0], t[1]};
+            vr[2 * dp + 1] = u32x2{t[2], t[3]};
+        }
     };
     u32x4 k0r[KS], k1r[KS], k2r[KS];
     u32x2 v0r[DT], v1r[DT], v2r[DT];

@@ -431,11 +431,12 @@ __global__ void __launch_bounds__(256) k_fill32(uint32_t *p, long long n, uint32
         p[i] = v;
 }
 
-// A plain streaming read of n16 16-byte words, folded into one xor per wave
-// so that no load is dead: the measured read ceiling of HBM that the decode
-// kernels are held to.  Each pass a work-group reads 256 * 8 consecutive
-// words (32 KiB, eight nontemporal loads in flight per thread), then strides
-// by the grid.
+// A plain streaming read of n16 16-byte words: the measured read ceiling of
+// HBM that the decode kernels are held to.  Each pass a work-group reads 256 *
+// 8 consecutive words (32 KiB, eight nontemporal loads in flight per thread),
+// then strides by the grid.  The words are folded into one xor per wave that
+// is written only when it equals an arbitrary constant (almost never), so no
+// load is dead and the waves do not serialise on one atomic.
 __global__ void __launch_bounds__(256) k_stream_read(const u32x4 *src, long long n16, unsigned *sink) {
     constexpr int U = 8;
     const long long stride = (long long)gridDim.x * 256 * U;
@@ -452,7 +453,7 @@ __global__ void __launch_bounds__(256) k_stream_read(const u32x4 *src, long long
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
-    if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+    if ((threadIdx.x & 63) == 0 && acc == 0x9E3779B9u) atomicXor(sink, acc);
 }
 
 __global__ void __launch_bounds__(256) k_iota(int *p, int n) {
