@@ -51,6 +51,12 @@ __host__ __device__ constexpr long long kv_v_off(bool tiled, int key, int d, int
                  : (long long)d * kPage + key;
 }
 
+// Elements between dim d and d + 1 (d even) of one key in the V layout.
+__host__ __device__ constexpr int kv_v_dim_step(bool tiled) { return tiled ? 8 : kPage; }
+static_assert(kv_v_off(true, 5, 7, 64) == kv_v_off(true, 5, 6, 64) + kv_v_dim_step(true), "dim step (tiled)");
+static_assert(kv_v_off(false, 5, 7, 64) == kv_v_off(false, 5, 6, 64) + kv_v_dim_step(false), "dim step");
+static_assert(kv_v_off(true, 17, 31, 128) == kv_v_off(true, 17, 30, 128) + kv_v_dim_step(true), "dim step (tiled)");
+
 // WT_Q8 / WT_Q4: Q8_0 / Q4_0 block-quantised weights (per row, blocks of 32
 // along K with one fp16 scale each, and int8 / 4-bit codes)
 enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2, WT_Q8 = 3, WT_Q4 = 4 };
@@ -1035,8 +1041,9 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                                 reinterpret_cast<float *>(g.kvk[b])[off + 1] = y1;
                             }
                         } else {
+                            // dd is even: dd + 1 sits one dim further in either layout
                             const long long o0 = hb + kv_v_off(tiled, t, dd, g.D);
-                            const long long o1 = hb + kv_v_off(tiled, t, dd + 1, g.D);
+                            const long long o1 = o0 + kv_v_dim_step(tiled);
                             if (tiled) {
                                 reinterpret_cast<uint16_t *>(g.kvv[b])[o0] = (uint16_t)bf16_rne_bits(y0);
                                 reinterpret_cast<uint16_t *>(g.kvv[b])[o1] = (uint16_t)bf16_rne_bits(y1);

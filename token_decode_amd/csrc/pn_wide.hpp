@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(256) k_w_qkv(WQkvArgs g) {
                 reinterpret_cast<float *>(g.kvk)[off + 1] = y1;
             }
         } else {
-            const long long o0 = hb + kv_v_off(tiled, t, dd, g.D), o1 = hb + kv_v_off(tiled, t, dd + 1, g.D);
+            const long long o0 = hb + kv_v_off(tiled, t, dd, g.D), o1 = o0 + kv_v_dim_step(tiled);  // dd even
             if (tiled) {
                 reinterpret_cast<uint16_t *>(g.kvv)[o0] = (uint16_t)bf16_rne_bits(y0);
                 reinterpret_cast<uint16_t *>(g.kvv)[o1] = (uint16_t)bf16_rne_bits(y1);
