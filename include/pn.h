@@ -29,7 +29,10 @@
  *  - Return value: 0 on success, else a negative PN_E* code; every failure
  *    sets a message readable through pn_last_error() (thread-local).  All
  *    argument checks happen on the host before anything is enqueued, so a
- *    failed call leaves the device untouched.
+ *    failed call leaves the device untouched.  One exception: a multi-chunk
+ *    pn_prefill into a pooled state whose pool runs out in a later chunk
+ *    returns PN_ERANGE after the earlier chunks were enqueued (their tokens
+ *    are in the cache and pos counts them; see pn_prefill).
  */
 #ifndef PN_H
 #define PN_H
@@ -81,7 +84,13 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3, PN_Q4_0 = 4 } pn
  *  act_dtype type that every mat-vec input (normed x, attention output, FFN
  *            hidden, final normed x) is rounded to: PN_F32 or PN_BF16.  The
  *            residual stream, q, softmax and all accumulators stay fp32.
- *            PN_I8 weights need act_dtype PN_BF16.
+ *            PN_I8 weights need act_dtype PN_BF16.  With int8 and block
+ *            (Q8_0, Q4_0) weights the bf16 activations enter the f16 matrix
+ *            cores as f16, exactly for magnitudes 2^-17 .. 65504: larger ones
+ *            become inf (the step's logits then show it) and smaller ones keep
+ *            fewer bits (below 2^-25 they are 0).  Normed inputs stay far inside
+ *            (|x| <= sqrt(n_embd) * max|gain|); the FFN hidden values do for any
+ *            weights that keep |silu(gate) * up| under 65504.
  *  max_batch largest n accepted by pn_forward_batch (1..16; with act_dtype
  *            PN_F32 and bf16/int8 weights, 1..5).
  *  rope_neox, qkv_bias  the variants that share the Llama forward through
@@ -295,8 +304,9 @@ int pn_forward_batch(pn_model *m, pn_state *const *states, int32_t n, const int3
  * are consecutive positions of the state; otherwise chunks of prefill_chunk
  * rows on the wide path, whose fp32 sums run in another order (split K).  With
  * both outputs NULL the wide path skips the LM head.  Errors: PN_EINVAL (NULL pointer, n < 1, state
- * of another model), PN_ERANGE (pos + n > max_ctx; a pooled state's pool ran
- * out). */
+ * of another model), PN_ERANGE (pos + n > max_ctx, checked before anything is
+ * enqueued; a pooled state's pool ran out: checked per chunk, so the chunks
+ * before the one that found the pool empty stay done and pos counts them). */
 int pn_prefill(pn_model *m, pn_state *s, const int32_t *tokens_dev, int32_t n, float *logits_dev,
                int32_t *argmax_dev, void *stream);
 
