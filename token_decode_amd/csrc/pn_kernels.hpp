@@ -1148,6 +1148,7 @@ struct AttnArgs {
     const int *pt[kMaxSlots];
     float *part[kMaxSlots];  // [Hk][s_cap][G][D+4]: running max (base 2), sum, 2 pad, unnormalised output
     unsigned kv_bytes[kMaxSlots];  // bytes of one layer's K (and of its V) pool
+    int pt_ident[kMaxSlots];       // 1: the slot's page table is the identity (logical page = physical)
     int kind;                // bf16 cache: 0 = vector units (k_attn), 1 = matrix cores (k_attn_mfma)
     // rows > 0: the grid's slots are `rows` prefill rows of one state, row b at
     // position p0 + b; the per-slot entries 0 hold that state's pages, page
@@ -1165,6 +1166,7 @@ struct AttnRow {
     const int *pt;
     float *part;
     unsigned kv_bytes;
+    int pt_ident;
 };
 __device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, int b) {
     AttnRow r;
@@ -1180,6 +1182,7 @@ __device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, int b) {
         r.pt = a.pt[0];
         r.part = a.part[0] + (long long)b * a.part_row;
         r.kv_bytes = a.kv_bytes[0];
+        r.pt_ident = a.pt_ident[0];
     } else {
         r.pos = a.pos[b];
         r.lo = a.lo[b];
@@ -1192,6 +1195,7 @@ __device__ __forceinline__ AttnRow attn_row(const AttnArgs &a, int b) {
         r.pt = a.pt[b];
         r.part = a.part[b];
         r.kv_bytes = a.kv_bytes[b];
+        r.pt_ident = a.pt_ident[b];
     }
     return r;
 }
@@ -1523,10 +1527,12 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     // the split's pages, one chunk (= page) per lane, looked up once; chunk ci
     // past the split's last reads the last one (its loads are clamped there)
     const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
+    // (an identity table needs no load: the K/V loads can go out at once)
     const int *ptb = R.pt + kb / kPage;
-    const int vpg = ptb[min(lane, nch - 1)];
+    const int vpg = R.pt_ident ? kb / kPage + min(lane, nch - 1) : ptb[min(lane, nch - 1)];
     auto page_of = [&](int ci) -> int {
         ci = min(ci, nch - 1);
+        if (R.pt_ident) return kb / kPage + ci;
         return ci < 64 ? __builtin_amdgcn_readlane(vpg, ci) : ptb[ci];
     };
     u32x4 kc[S::NKL], kn[S::NKL];
@@ -1662,10 +1668,12 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
 
     // the split's pages, one chunk (= page) per lane, looked up once
     const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
+    // (an identity table needs no load: the K/V loads can go out at once)
     const int *ptb = R.pt + kb / kPage;
-    const int vpg = ptb[min(lane, nch - 1)];
+    const int vpg = R.pt_ident ? kb / kPage + min(lane, nch - 1) : ptb[min(lane, nch - 1)];
     auto page_of = [&](int ci) -> int {
         ci = min(ci, nch - 1);
+        if (R.pt_ident) return kb / kPage + ci;
         return ci < 64 ? __builtin_amdgcn_readlane(vpg, ci) : ptb[ci];
     };
     // buffer loads over the layer's pools: an offset past the pool reads zeros

@@ -154,6 +154,7 @@ struct pn_state {
     size_t kpool, vpool, layer_bytes, pt, part, err;
     pn_pool *pool = nullptr;
     std::vector<int> phys;  // pooled: physical page of each logical page, -1 = none
+    bool pt_identity = true;  // private state whose page table is the identity
     int kept_from = 0;      // pooled: logical pages below this were returned to the pool
 };
 
@@ -707,6 +708,7 @@ int attn_setup(const pn_model *m, pn_state *const *st, int n, const int *pos, bo
         aa.part[b] = rows ? (float *)(m->base + m->attn_part + (size_t)b * m->attn_part_row)
                           : (float *)(st[b]->base + st[b]->part);
         aa.kv_bytes[b] = (unsigned)st[b]->layer_bytes;
+        aa.pt_ident[b] = (!st[b]->pool && st[b]->pt_identity) ? 1 : 0;
     }
     return nsplit_max;
 }
@@ -1748,6 +1750,9 @@ int pn_state_set_page_table(pn_state *s, const int32_t *pages, int32_t n, void *
     hipError_t e = hipMemcpyAsync(s->base + s->pt, pages, (size_t)n * 4, hipMemcpyHostToDevice, S(stream));
     if (e == hipSuccess) e = hipStreamSynchronize(S(stream));
     if (e != hipSuccess) return fail(PN_EHIP, "page table copy failed: %s", hipGetErrorString(e));
+    bool ident = true;
+    for (int i = 0; i < n && ident; ++i) ident = pages[i] == i;
+    s->pt_identity = ident;  // attention computes page ids for an identity table instead of loading them
     return PN_OK;
 }
 
