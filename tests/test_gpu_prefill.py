@@ -249,3 +249,14 @@ def test_wide_int8_llama3_shape():
     prompt = list(synth.uniform_int(wl.seed, 101, 32, 0, wl.n_vocab - 1))
     worst, near = run_prefill(p, 60, prompt, 1)
     log("  wide, Llama-3-8B int8, 32 tokens from 60: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_wide_mistral_shape_full_chunk():
+    """Mistral-7B layer shape (2 layers, bf16 activations, window 4096): a full
+    256-row chunk, then 44 rows.  At 256 rows the gate/up and LM-head products
+    run in work-groups of 16 weight tiles, the narrower rest in groups of 8."""
+    wl = synth.mistral_7b_slots().with_(name="wide-mistral-2l", n_layer=2, slots=1, seed=92)
+    p = Pair(wl, max_batch=1, prefill_chunk=256)
+    prompt = list(synth.uniform_int(wl.seed, 102, 300, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 0, prompt, 1)
+    log("  wide, Mistral-7B shape, 300 tokens in chunks of 256: worst rel L2 %.2e, near %d" % (worst, near))

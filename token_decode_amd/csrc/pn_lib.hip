@@ -1058,18 +1058,42 @@ int wide_splits(long long groups, int KT, long long floats_per_split, long long 
 // weights with bf16 rows, 1 = bf16 weights with fp32 rows (three pieces), 2 =
 // int8 weights (f16 rows).
 int wide_variant(const pn_model *m) { return m->wt == PN_I8 ? 2 : (m->pieces == 3 ? 1 : 0); }
-const void *wide_kernel(int v) {
-    return v == 2 ? reinterpret_cast<const void *>(&k_wgemm<WT_I8, 1>)
-                  : v == 1 ? reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 3>)
-                           : reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 1>);
+// The kernel of variant v with work-groups of wgw weight tiles (8 or 16).
+const void *wide_kernel(int v, int wgw) {
+    if (wgw == 16)
+        return v == 2 ? reinterpret_cast<const void *>(&k_wgemm<WT_I8, 1, 16>)
+               : v == 1 ? reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 3, 16>)
+                        : reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 1, 16>);
+    return v == 2 ? reinterpret_cast<const void *>(&k_wgemm<WT_I8, 1, 8>)
+           : v == 1 ? reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 3, 8>)
+                    : reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 1, 8>);
 }
-int wide_lds(int v) { return v == 2 ? wgemm_lds(WT_I8, 1) : v == 1 ? wgemm_lds(WT_BF16, 3) : wgemm_lds(WT_BF16, 1); }
+int wide_lds(int v, int wgw) {
+    const int w = wgw == 16 ? 16 : 8;
+    return v == 2 ? (w == 16 ? wgemm_lds(WT_I8, 1, 16) : wgemm_lds(WT_I8, 1, 8))
+           : v == 1 ? (w == 16 ? wgemm_lds(WT_BF16, 3, 16) : wgemm_lds(WT_BF16, 3, 8))
+                    : (w == 16 ? wgemm_lds(WT_BF16, 1, 16) : wgemm_lds(WT_BF16, 1, 8));
+}
 
 int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_t *w1, const float *s0,
               const float *s1, float *y0, float *y1, int nz, int R, int N, int ldy, bool split_ok, hipStream_t s) {
-    const long long groups = (long long)cdiv(R, 128) * cdiv(mat.n_tiles, 8) * nz;
+    // Groups of 8 or 16 weight tiles, each with the K split wide_splits picks
+    // for it: the wider group reads a third fewer LDS bytes per output, taken
+    // here as 0.8 of the time per tile; the width with the fewer rounds of
+    // work per compute unit wins (ties: 8).
     const long long per = (long long)R * ldy;
-    const int ks = split_ok ? wide_splits(groups, mat.KT, per * nz, m->wy_cap) : 1;
+    int wgw = 8, ks = 1;
+    double best = 0.0;
+    for (int w : {8, 16}) {
+        const long long groups = (long long)cdiv(R, 128) * cdiv(mat.n_tiles, w) * nz;
+        const int k = split_ok ? wide_splits(groups, mat.KT, per * nz, m->wy_cap) : 1;
+        const double cost = (double)cdiv(groups * k, kCUs) * (w / 8) / k * (w == 16 ? 0.8 : 1.0);
+        if (w == 8 || cost < best - 1e-9) {
+            best = cost;
+            wgw = w;
+            ks = k;
+        }
+    }
     WGemmArgs g{};
     g.w[0] = w0;
     g.w[1] = w1 ? w1 : w0;
@@ -1089,12 +1113,18 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
     g.nsplit = ks;
     g.nzs = nz * ks;
     g.gx = cdiv(R, 128);
-    const dim3 grid((unsigned)(g.gx * cdiv(mat.n_tiles, 8) * g.nzs));
+    const dim3 grid((unsigned)(g.gx * cdiv(mat.n_tiles, wgw) * g.nzs));
     const int v = wide_variant(m);
-    const size_t lds = (size_t)wide_lds(v);  // (attribute set by wide_lds_attr)
-    if (v == 2) hipLaunchKernelGGL((k_wgemm<WT_I8, 1>), grid, dim3(512), lds, s, g);
-    else if (v == 1) hipLaunchKernelGGL((k_wgemm<WT_BF16, 3>), grid, dim3(512), lds, s, g);
-    else hipLaunchKernelGGL((k_wgemm<WT_BF16, 1>), grid, dim3(512), lds, s, g);
+    const size_t lds = (size_t)wide_lds(v, wgw);  // (attribute set by wide_lds_attr)
+    if (wgw == 16) {
+        if (v == 2) hipLaunchKernelGGL((k_wgemm<WT_I8, 1, 16>), grid, dim3(512), lds, s, g);
+        else if (v == 1) hipLaunchKernelGGL((k_wgemm<WT_BF16, 3, 16>), grid, dim3(512), lds, s, g);
+        else hipLaunchKernelGGL((k_wgemm<WT_BF16, 1, 16>), grid, dim3(512), lds, s, g);
+    } else {
+        if (v == 2) hipLaunchKernelGGL((k_wgemm<WT_I8, 1, 8>), grid, dim3(512), lds, s, g);
+        else if (v == 1) hipLaunchKernelGGL((k_wgemm<WT_BF16, 3, 8>), grid, dim3(512), lds, s, g);
+        else hipLaunchKernelGGL((k_wgemm<WT_BF16, 1, 8>), grid, dim3(512), lds, s, g);
+    }
     return ks;
 }
 
@@ -1103,10 +1133,12 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
 int wide_lds_attr() {
     static bool done = false;
     if (done) return PN_OK;
-    for (int v = 0; v < 3; ++v) {
-        const hipError_t e = hipFuncSetAttribute(wide_kernel(v), hipFuncAttributeMaxDynamicSharedMemorySize, wide_lds(v));
-        if (e != hipSuccess) return fail(PN_EHIP, "wide GEMM LDS attribute: %s", hipGetErrorString(e));
-    }
+    for (int v = 0; v < 3; ++v)
+        for (int wgw : {8, 16}) {
+            const hipError_t e = hipFuncSetAttribute(wide_kernel(v, wgw), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     wide_lds(v, wgw));
+            if (e != hipSuccess) return fail(PN_EHIP, "wide GEMM LDS attribute: %s", hipGetErrorString(e));
+        }
     done = true;
     return PN_OK;
 }

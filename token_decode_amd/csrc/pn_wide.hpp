@@ -30,11 +30,13 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 // grid: one dimension, work-group id = (W group * A groups + A group) * nzs +
 // zs, with zs = matrix * nsplit + split varying fastest: work-groups are
 // dealt to the XCDs in id order, so with 8 (or 4) values of zs each XCD's L2
-// holds the A slice of one split instead of all of A; a W group is 8 tiles
-// (128 rows), an A group 128 rows; 512 threads (two waves per SIMD: one
-// computes while the other waits on LDS).  Wave w computes weight tiles
-// 4*(w & 1) .. +3 against row tiles 2*(w >> 1), +1 of the group (8
-// accumulators).  A k step's 8 weight and 8*NA row fragments (1 KiB each)
+// holds the A slice of one split instead of all of A; a W group is WGW tiles
+// (8 or 16: 128 or 256 rows), an A group 128 rows; 512 threads (two waves per
+// SIMD: one computes while the other waits on LDS).  Wave w computes weight
+// tiles (WGW/2)*(w & 1) .. +WGW/2-1 against row tiles 2*(w >> 1), +1 of the
+// group (WGW accumulators): the wider group reads a third fewer LDS bytes per
+// output, for products with rows enough to fill the chip without splitting K.
+// A k step's WGW weight and 8*NA row fragments (1 KiB each)
 // go from memory straight into a ring of LDS stages (each wave loads an eighth
 // of them); S - 1 steps are in flight while the work-group computes one, at
 // one barrier per step, so the loads in flight take no registers.  Tiles past
@@ -53,11 +55,16 @@ struct WGemmArgs {
 // Row fragments per row tile and k step: the P bf16 planes, or for int8
 // weights (64-wide tiles, f16 rows) the two 32-wide halves of the step.
 __host__ __device__ constexpr int wgemm_na(int WT, int P) { return WT == WT_I8 ? 2 : P; }
-// Stages of the LDS ring: fp32 activations (three planes) take 32 KiB per k
-// step, bf16 ones 16 KiB, int8 weights 24 KiB; 120-128 KiB in all.
-__host__ __device__ constexpr int wgemm_stages(int WT, int P) { return WT == WT_I8 ? 5 : (P == 3 ? 4 : 8); }
-__host__ __device__ constexpr int wgemm_frags(int WT, int P) { return 8 + 8 * wgemm_na(WT, P); }  // 1 KiB each
-__host__ __device__ constexpr int wgemm_lds(int WT, int P) { return wgemm_stages(WT, P) * wgemm_frags(WT, P) * 1024; }
+// Fragments (1 KiB each) of one k step of a work-group that owns WGW weight
+// tiles and 8 row tiles: the weight tiles, then every row tile's NA fragments.
+__host__ __device__ constexpr int wgemm_frags(int WT, int P, int WGW) { return WGW + 8 * wgemm_na(WT, P); }
+// Stages of the LDS ring: as many k steps as fit 128 KiB (at most 8).
+__host__ __device__ constexpr int wgemm_stages(int WT, int P, int WGW) {
+    return 128 / wgemm_frags(WT, P, WGW) < 8 ? 128 / wgemm_frags(WT, P, WGW) : 8;
+}
+__host__ __device__ constexpr int wgemm_lds(int WT, int P, int WGW) {
+    return wgemm_stages(WT, P, WGW) * wgemm_frags(WT, P, WGW) * 1024;
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -82,18 +89,20 @@ __device__ __forceinline__ void wait_vm_all() {
 #endif
 }
 
-template <int WT, int P>
+template <int WT, int P, int WGW>
 __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     constexpr int NA = wgemm_na(WT, P), TK = tile_k(WT);
-    constexpr int S = wgemm_stages(WT, P), FR = wgemm_frags(WT, P), LPW = FR / 8;
-    extern __shared__ __align__(16) uint8_t ring[];  // [S][FR][1 KiB]: W tiles 0..7, then A [row tile][plane]
+    constexpr int S = wgemm_stages(WT, P, WGW), FR = wgemm_frags(WT, P, WGW), LPW = FR / 8;
+    constexpr int WWT = WGW / 2;  // weight tiles per wave
+    static_assert(FR % 8 == 0 && S >= 3, "eight waves share a step's loads; three stages at least");
+    extern __shared__ __align__(16) uint8_t ring[];  // [S][FR][1 KiB]: W tiles 0..WGW-1, then A [row tile][plane]
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int id = blockIdx.x, zs = id % g.nzs, rest = id / g.nzs;
     const int gxi = rest % g.gx, gyi = rest / g.gx;
     const int z = zs / g.nsplit, s = zs % g.nsplit;
     const int kt0 = (int)((long long)s * g.KT / g.nsplit), kt1 = (int)((long long)(s + 1) * g.KT / g.nsplit);
-    const int wt0 = gyi * 8 + 4 * (wv & 1);  // first weight tile the wave computes
+    const int wt0 = gyi * WGW + WWT * (wv & 1);  // first weight tile the wave computes
     const int rt0 = gxi * 8 + 2 * (wv >> 1);  // first row tile the wave computes
     // The wave loads fragments wv*LPW .. +LPW-1 of every stage: a W tile
     // (clamped to the matrix) or a (row tile, plane) of A (rows clamped to R).
@@ -102,12 +111,12 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
         const int f = wv * LPW + q;
-        if (f < 8) {
-            src[q] = g.w[z] + (long long)min(gyi * 8 + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
+        if (f < WGW) {
+            src[q] = g.w[z] + (long long)min(gyi * WGW + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
             stride[q] = 1024;
         } else {
             // bf16: plane p, k 8*(l >> 4) of the step; int8: half p, k 16*(l >> 4) + 8p
-            const int rt = (f - 8) / NA, p = (f - 8) % NA;
+            const int rt = (f - WGW) / NA, p = (f - WGW) % NA;
             const int r = min((gxi * 8 + rt) * 16 + (lane & 15), g.R - 1);
             const long long e = WT == WT_I8 ? (long long)r * g.lda + 16 * (lane >> 4) + 8 * p
                                             : p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4);
@@ -121,9 +130,9 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
         for (int q = 0; q < LPW; ++q)
             lds_dma16(src[q] + (long long)kt * stride[q], (lds_void *)(ring + (slot * FR + wv * LPW + q) * 1024));
     };
-    f32x4 acc[4][2];
+    f32x4 acc[WWT][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WWT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -136,22 +145,22 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
         // in flight) and its reads of the previous step are done; then every
         // wave's: the barrier
         wait_vm_barrier<(S - 2) * LPW>();
-        u32x4 wf[4], af[2][NA];
+        u32x4 wf[WWT], af[2][NA];
         const uint8_t *base = ring + slot * FR * 1024 + lane * 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4 *>(base + (4 * (wv & 1) + i) * 1024);
+        for (int i = 0; i < WWT; ++i) wf[i] = *reinterpret_cast<const u32x4 *>(base + (WWT * (wv & 1) + i) * 1024);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int p = 0; p < NA; ++p)
-                af[j][p] = *reinterpret_cast<const u32x4 *>(base + (8 + (2 * (wv >> 1) + j) * NA + p) * 1024);
+                af[j][p] = *reinterpret_cast<const u32x4 *>(base + (WGW + (2 * (wv >> 1) + j) * NA + p) * 1024);
         // the slot of step kt - 1: every wave has read it (it passed the barrier)
         issue(kt + S - 1, (kt - kt0 + S - 1) % S);
         if constexpr (WT == WT_I8) {
             // biased codes u = q + 128 -> f16 (1024 + u) by a byte permute; minus 1152 leaves q
             const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < WWT; ++i) {
                 u32x4 b[2];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -170,7 +179,7 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < WWT; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -190,7 +199,7 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
         const int r = (rt0 + j) * 16 + (lane & 15);
         if (r >= g.R) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < WWT; ++i) {
             const int n0 = (wt0 + i) * 16 + 4 * (lane >> 4);
             float *yp = y + (long long)r * g.ldy + n0;
             f32x4 v = acc[i][j];
