@@ -2,7 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
-#include "pn_kernels.hpp"
+#include "pn_attn.hpp"
 
 namespace pn {
 

@@ -2,7 +2,7 @@
 // MoE router and combine) and the one-time set-up kernels (weight packing,
 // fills, K/V scatter).  Included only by pn_lib.hip.
 #pragma once
-#include "pn_kernels.hpp"
+#include "pn_attn.hpp"
 
 namespace pn {
 
