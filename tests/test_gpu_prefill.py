@@ -5,7 +5,7 @@ import pytest
 
 import synth
 
-from harness import Pair, compare_step, log
+from harness import Pair, compare_step, log, oracle_threads
 
 pytestmark = pytest.mark.gpu
 
@@ -29,8 +29,11 @@ def run_prefill(p, start, prompt, n_decode, tol=None):
     assert ds.pos == start + len(prompt)
     g, ga = logits.cpu().numpy(), am.cpu().numpy()
     worst, near, nxt = 0.0, 0, None
+    th = oracle_threads()
     for t, tok in enumerate(prompt):
-        ol, oa = os_.step(int(tok))
+        ol, oa = os_.step(int(tok), th)
+        if t % 32 == 31:
+            log("    (oracle at prompt row %d)" % t)
         rel, nt = compare_step(wl, g[t], ol, int(ga[t]), oa, "prompt row %d:" % t, tol)
         worst, near, nxt = max(worst, rel), near + int(nt), oa
     # decode on from the prefilled cache
@@ -39,7 +42,7 @@ def run_prefill(p, start, prompt, n_decode, tol=None):
     a1 = torch.empty(1, dtype=torch.int32, device="cuda")
     for i in range(n_decode):
         dv.forward_step(p.dm, ds, tok, lg1, a1)
-        ol, oa = os_.step(int(tok.item()))
+        ol, oa = os_.step(int(tok.item()), th)
         rel, nt = compare_step(wl, lg1.cpu().numpy(), ol, int(a1.item()), oa, "decode step %d:" % i, tol)
         worst, near = max(worst, rel), near + int(nt)
         tok.fill_(oa)
@@ -251,10 +254,36 @@ def test_wide_int8_llama3_shape():
     log("  wide, Llama-3-8B int8, 32 tokens from 60: worst rel L2 %.2e, near %d" % (worst, near))
 
 
+def test_wide_q8_0_weights():
+    """Q8_0 weights (an fp16 scale per 32-weight block: each block's matrix-core
+    step from zero, scaled and added in fp32) with bf16 activations, chunks of
+    64 over 150 tokens from a cache written up to 40; n_embd 224 leaves the
+    last 64-wide k tile half past K.  The small products run in work-groups of
+    8 weight tiles."""
+    wl = ragged("wide-q8_0", w_dtype=synth.Q8_0, kv_dtype=synth.BF16, act_dtype=synth.BF16, n_embd=224,
+                n_ff=320, seed=93)
+    p = Pair(wl, max_batch=1, prefill_chunk=64)
+    prompt = list(synth.uniform_int(wl.seed, 103, 150, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 40, prompt, 2)
+    log("  wide, Q8_0 weights, 150 tokens from 40: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_wide_q8_0_llama3_shape():
+    """Llama-3-8B layer shape with Q8_0 weights (2 layers, full vocabulary):
+    40 prompt tokens in chunks of 32 after a 30-token cache.  At 32 rows QKV,
+    gate/up and the LM head run in work-groups of 16 weight tiles, O and down
+    in groups of 8, all but the LM head with K split over work-groups."""
+    wl = synth.WORKLOADS["llama3-8b-q8_0"]().with_(name="wide-llama3-q8_0-2l", n_layer=2, seed=94)
+    p = Pair(wl, max_batch=1, prefill_chunk=32)
+    prompt = list(synth.uniform_int(wl.seed, 104, 40, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 30, prompt, 1)
+    log("  wide, Llama-3-8B Q8_0, 40 tokens from 30: worst rel L2 %.2e, near %d" % (worst, near))
+
+
 def test_wide_mistral_shape_full_chunk():
     """Mistral-7B layer shape (2 layers, bf16 activations, window 4096): a full
-    256-row chunk, then 44 rows.  At 256 rows the gate/up and LM-head products
-    run in work-groups of 16 weight tiles, the narrower rest in groups of 8."""
+    256-row chunk, then 44 rows.  At 256 rows every product but QKV runs in
+    work-groups of 16 weight tiles (QKV in groups of 8, K split 8 ways)."""
     wl = synth.mistral_7b_slots().with_(name="wide-mistral-2l", n_layer=2, slots=1, seed=92)
     p = Pair(wl, max_batch=1, prefill_chunk=256)
     prompt = list(synth.uniform_int(wl.seed, 102, 300, 0, wl.n_vocab - 1))

@@ -293,9 +293,10 @@ int check_config_n(const pn_config *c) {
         return fail(PN_EINVAL, "prefill_chunk must be in [0, %d]", kWideRows);
     if (c->prefill_chunk > 0 && c->n_embd > 1024 * kWideSsq)
         return fail(PN_EUNSUPPORTED, "the wide prefill path takes n_embd up to %d", 1024 * kWideSsq);
-    if (c->prefill_chunk > 0 && ((c->w_dtype != PN_BF16 && c->w_dtype != PN_I8) || c->n_expert > 0 ||
-                                 c->kv_dtype == PN_Q4_0))
-        return fail(PN_EUNSUPPORTED, "the wide prefill path needs bf16 or int8 weights, no experts and an fp32 or bf16 cache");
+    if (c->prefill_chunk > 0 && ((c->w_dtype != PN_BF16 && c->w_dtype != PN_I8 && c->w_dtype != PN_Q8_0) ||
+                                 c->n_expert > 0 || c->kv_dtype == PN_Q4_0))
+        return fail(PN_EUNSUPPORTED,
+                    "the wide prefill path needs bf16, int8 or Q8_0 weights, no experts and an fp32 or bf16 cache");
     const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
@@ -1056,23 +1057,34 @@ int wide_splits(long long groups, int KT, long long floats_per_split, long long 
 // up) with outputs y[z] [split][R][ldy]; returns the number of splits used.
 // The wide GEMM kernel of the model's weight and activation types: 0 = bf16
 // weights with bf16 rows, 1 = bf16 weights with fp32 rows (three pieces), 2 =
-// int8 weights (f16 rows).
-int wide_variant(const pn_model *m) { return m->wt == PN_I8 ? 2 : (m->pieces == 3 ? 1 : 0); }
-// The kernel of variant v with work-groups of wgw weight tiles (8 or 16).
+// int8 weights, 3 = Q8_0 weights (both with f16 rows).
+int wide_variant(const pn_model *m) {
+    return m->wt == PN_Q8_0 ? 3 : (m->wt == PN_I8 ? 2 : (m->pieces == 3 ? 1 : 0));
+}
+// fn(WT, P, WGW) (as integral constants) for variant v with work-groups of wgw
+// weight tiles (8 or 16).
+template <typename Fn>
+auto with_wide(int v, int wgw, Fn fn) {
+    auto go = [&](auto wt, auto p) {
+        return wgw == 16 ? fn(wt, p, std::integral_constant<int, 16>{}) : fn(wt, p, std::integral_constant<int, 8>{});
+    };
+    using I = std::integral_constant<int, 1>;
+    switch (v) {
+        case 3: return go(std::integral_constant<int, WT_Q8>{}, I{});
+        case 2: return go(std::integral_constant<int, WT_I8>{}, I{});
+        case 1: return go(std::integral_constant<int, WT_BF16>{}, std::integral_constant<int, 3>{});
+        default: return go(std::integral_constant<int, WT_BF16>{}, I{});
+    }
+}
 const void *wide_kernel(int v, int wgw) {
-    if (wgw == 16)
-        return v == 2 ? reinterpret_cast<const void *>(&k_wgemm<WT_I8, 1, 16>)
-               : v == 1 ? reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 3, 16>)
-                        : reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 1, 16>);
-    return v == 2 ? reinterpret_cast<const void *>(&k_wgemm<WT_I8, 1, 8>)
-           : v == 1 ? reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 3, 8>)
-                    : reinterpret_cast<const void *>(&k_wgemm<WT_BF16, 1, 8>);
+    return with_wide(v, wgw, [](auto wt, auto p, auto w) {
+        return reinterpret_cast<const void *>(&k_wgemm<decltype(wt)::value, decltype(p)::value, decltype(w)::value>);
+    });
 }
 int wide_lds(int v, int wgw) {
-    const int w = wgw == 16 ? 16 : 8;
-    return v == 2 ? (w == 16 ? wgemm_lds(WT_I8, 1, 16) : wgemm_lds(WT_I8, 1, 8))
-           : v == 1 ? (w == 16 ? wgemm_lds(WT_BF16, 3, 16) : wgemm_lds(WT_BF16, 3, 8))
-                    : (w == 16 ? wgemm_lds(WT_BF16, 1, 16) : wgemm_lds(WT_BF16, 1, 8));
+    return with_wide(v, wgw, [](auto wt, auto p, auto w) {
+        return wgemm_lds(decltype(wt)::value, decltype(p)::value, decltype(w)::value);
+    });
 }
 
 int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_t *w1, const float *s0,
@@ -1116,15 +1128,11 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
     const dim3 grid((unsigned)(g.gx * cdiv(mat.n_tiles, wgw) * g.nzs));
     const int v = wide_variant(m);
     const size_t lds = (size_t)wide_lds(v, wgw);  // (attribute set by wide_lds_attr)
-    if (wgw == 16) {
-        if (v == 2) hipLaunchKernelGGL((k_wgemm<WT_I8, 1, 16>), grid, dim3(512), lds, s, g);
-        else if (v == 1) hipLaunchKernelGGL((k_wgemm<WT_BF16, 3, 16>), grid, dim3(512), lds, s, g);
-        else hipLaunchKernelGGL((k_wgemm<WT_BF16, 1, 16>), grid, dim3(512), lds, s, g);
-    } else {
-        if (v == 2) hipLaunchKernelGGL((k_wgemm<WT_I8, 1, 8>), grid, dim3(512), lds, s, g);
-        else if (v == 1) hipLaunchKernelGGL((k_wgemm<WT_BF16, 3, 8>), grid, dim3(512), lds, s, g);
-        else hipLaunchKernelGGL((k_wgemm<WT_BF16, 1, 8>), grid, dim3(512), lds, s, g);
-    }
+    with_wide(v, wgw, [&](auto wt, auto p, auto w) {
+        hipLaunchKernelGGL((k_wgemm<decltype(wt)::value, decltype(p)::value, decltype(w)::value>), grid, dim3(512),
+                           lds, s, g);
+        return 0;
+    });
     return ks;
 }
 
@@ -1133,7 +1141,7 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
 int wide_lds_attr() {
     static bool done = false;
     if (done) return PN_OK;
-    for (int v = 0; v < 3; ++v)
+    for (int v = 0; v < 4; ++v)
         for (int wgw : {8, 16}) {
             const hipError_t e = hipFuncSetAttribute(wide_kernel(v, wgw), hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      wide_lds(v, wgw));
@@ -1157,11 +1165,14 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
     int *err = (int *)(st->base + st->err);
     const float eps = c.rms_norm_eps;
     const int var = wide_variant(m);
-    const bool i8 = var == 2;
+    const bool i8 = var == 2, q8 = var == 3;
     float *ssq = (float *)(mb + m->wss);
     auto norm = [&](const float *gain) {
         const dim3 gn(cdiv(m->wlda, 1024), R);
-        if (i8)
+        if (q8)
+            hipLaunchKernelGGL((k_w_norm<WT_Q8, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
+                               m->wlda);
+        else if (i8)
             hipLaunchKernelGGL((k_w_norm<WT_I8, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
                                m->wlda);
         else if (bf)
@@ -1171,7 +1182,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_F32>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
                                m->wlda);
     };
-    auto scales = [&](const Mat &mt) { return i8 ? (const float *)(mb + mt.soff) : nullptr; };
+    auto scales = [&](const Mat &mt) { return (i8 || q8) ? (const float *)(mb + mt.soff) : nullptr; };
     if (int rc = wide_lds_attr()) return rc;
     hipLaunchKernelGGL(k_w_embed, dim3(cdiv(E, 1024), R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E,
                        m->V, err, ssq);
@@ -1224,7 +1235,8 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         // ---- O + residual
         {
             const dim3 gc(cdiv(m->wlda, 1024), R);
-            if (i8) hipLaunchKernelGGL((k_w_conv<WT_I8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+            if (q8) hipLaunchKernelGGL((k_w_conv<WT_Q8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+            else if (i8) hipLaunchKernelGGL((k_w_conv<WT_I8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
             else if (bf) hipLaunchKernelGGL((k_w_conv<WT_BF16, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
             else hipLaunchKernelGGL((k_w_conv<WT_BF16, AT_F32>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
         }
@@ -1245,7 +1257,10 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
                                      scales(L.gate), scales(L.up), y, yu, 2, R, ld, ld, fits, s);
             const dim3 gs(cdiv(m->wlda, 1024), R);
             const long long sp = (long long)R * ld;
-            if (i8)
+            if (q8)
+                hipLaunchKernelGGL((k_w_swiglu<WT_Q8, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a, m->wa_plane,
+                                   m->wlda);
+            else if (i8)
                 hipLaunchKernelGGL((k_w_swiglu<WT_I8, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a, m->wa_plane,
                                    m->wlda);
             else if (bf)

@@ -8,7 +8,8 @@
 // each projection as one matrix product on the matrix cores (k_wgemm), with
 // the steps around it as plain row kernels: RMSNorm into MFMA-ready planes,
 // RoPE + K/V append, SwiGLU, the residual add and the per-row argmax.  Dense
-// models with bf16 or int8 weights and an fp32 or bf16 cache take this path.
+// models with bf16, int8 or Q8_0 weights and an fp32 or bf16 cache take this
+// path.
 #pragma once
 #include "pn_kernels.hpp"
 
@@ -19,12 +20,16 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 
 // Y_s[r][n] = sum over k in split s of A[r][k] * W[n][k], for the P planes of
 // A (the bf16 pieces whose sum is the fp32 input, or one bf16 plane); int8
-// weights: times the row scale sc[n].
+// weights: times the row scale sc[n]; Q8_0 weights: each 32-wide block's
+// product times that block's scale of row n.
 //   W: packed tiles [n_tiles][KT][1 KiB]; bf16: 16 rows x 32 k, lane l holds
 //      row l & 15, k 8*(l >> 4) .. +7 (the 16x16x32 operand layout); int8:
-//      16 rows x 64 k of biased codes, lane l row l & 15, k 16*(l >> 4) .. +15.
-//   A: planes [P][rows][lda] bf16 (int8 weights: one plane of f16), lda >=
-//      KT * tile width, zero from K up to lda.
+//      16 rows x 64 k of biased codes, lane l row l & 15, k 16*(l >> 4) .. +15;
+//      Q8_0: the same, with each lane's first 8 codes in block 0 of the tile
+//      and its last 8 in block 1 (blk_pos order), and the scale tiles
+//      [n_tiles][KT][16 rows][2 blocks] fp16 at sc.
+//   A: planes [P][rows][lda] bf16 (int8 and Q8_0 weights: one plane of f16,
+//      Q8_0 in blk_pos order), lda >= KT * tile width, zero from K up to lda.
 //   Y: split s, matrix z at y[z] + s * y_split, [r][ldy] fp32; rows < R and
 //      n < N are written.
 // grid: one dimension, work-group id = (W group * A groups + A group) * nzs +
@@ -43,7 +48,7 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 // n_tiles and rows past R load clamped (in bounds) and are not stored.
 struct WGemmArgs {
     const uint8_t *w[2];
-    const float *sc[2];  // int8 weights: the rows' scales (padded to tiles), else null
+    const float *sc[2];  // int8 weights: the rows' scales (padded to tiles); Q8_0: the scale tiles; else null
     float *y[2];
     long long y_split;  // floats between the splits' outputs
     const uint16_t *a;
@@ -52,18 +57,28 @@ struct WGemmArgs {
     int nzs, gx;  // matrices * nsplit; A groups
 };
 
-// Row fragments per row tile and k step: the P bf16 planes, or for int8
-// weights (64-wide tiles, f16 rows) the two 32-wide halves of the step.
-__host__ __device__ constexpr int wgemm_na(int WT, int P) { return WT == WT_I8 ? 2 : P; }
+// Row fragments per row tile and k step: the P bf16 planes, or for int8 and
+// Q8_0 weights (64-wide tiles, f16 rows) the two 32-wide halves of the step.
+__host__ __device__ constexpr int wgemm_na(int WT, int P) { return (WT == WT_I8 || WT == WT_Q8) ? 2 : P; }
+// Q8_0: bytes of block scales per stage, after its fragments: each of the 8
+// waves loads 256 (a dword per lane), 4 weight tiles' 64-byte scale tiles;
+// the first WGW * 64 are the work-group's (waves past them load copies).
+__host__ __device__ constexpr int wgemm_scb(int WT) { return WT == WT_Q8 ? 2048 : 0; }
 // Fragments (1 KiB each) of one k step of a work-group that owns WGW weight
 // tiles and 8 row tiles: the weight tiles, then every row tile's NA fragments.
 __host__ __device__ constexpr int wgemm_frags(int WT, int P, int WGW) { return WGW + 8 * wgemm_na(WT, P); }
-// Stages of the LDS ring: as many k steps as fit 128 KiB (at most 8).
+// Bytes of one stage of the LDS ring, and the stages: as many k steps as fit
+// 128 KiB (Q8_0, whose stages also hold scales: 144 KiB), at most 8.
+__host__ __device__ constexpr int wgemm_stage_bytes(int WT, int P, int WGW) {
+    return wgemm_frags(WT, P, WGW) * 1024 + wgemm_scb(WT);
+}
 __host__ __device__ constexpr int wgemm_stages(int WT, int P, int WGW) {
-    return 128 / wgemm_frags(WT, P, WGW) < 8 ? 128 / wgemm_frags(WT, P, WGW) : 8;
+    return (WT == WT_Q8 ? 144 : 128) * 1024 / wgemm_stage_bytes(WT, P, WGW) < 8
+               ? (WT == WT_Q8 ? 144 : 128) * 1024 / wgemm_stage_bytes(WT, P, WGW)
+               : 8;
 }
 __host__ __device__ constexpr int wgemm_lds(int WT, int P, int WGW) {
-    return wgemm_stages(WT, P, WGW) * wgemm_frags(WT, P, WGW) * 1024;
+    return wgemm_stages(WT, P, WGW) * wgemm_stage_bytes(WT, P, WGW);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -75,6 +90,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void lds_dma16(const void *src, lds_void *dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
+}
+// The same with 4 bytes per lane (lane i's at dst + 4*i).
+__device__ __forceinline__ void lds_dma4(const void *src, lds_void *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 #endif
 }
 template <int N>
@@ -94,8 +115,13 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     constexpr int NA = wgemm_na(WT, P), TK = tile_k(WT);
     constexpr int S = wgemm_stages(WT, P, WGW), FR = wgemm_frags(WT, P, WGW), LPW = FR / 8;
     constexpr int WWT = WGW / 2;  // weight tiles per wave
+    constexpr bool BQ = WT == WT_Q8;
+    constexpr int SB = wgemm_stage_bytes(WT, P, WGW);
+    constexpr int LPS = LPW + (BQ ? 1 : 0);  // loads per wave per k step
     static_assert(FR % 8 == 0 && S >= 3, "eight waves share a step's loads; three stages at least");
-    extern __shared__ __align__(16) uint8_t ring[];  // [S][FR][1 KiB]: W tiles 0..WGW-1, then A [row tile][plane]
+    static_assert(!BQ || WGW * 64 <= wgemm_scb(WT), "the scale area holds the work-group's scale tiles");
+    // [S][SB]: W tiles 0..WGW-1, then A [row tile][plane] (1 KiB each), then (Q8_0) the scales
+    extern __shared__ __align__(16) uint8_t ring[];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int id = blockIdx.x, zs = id % g.nzs, rest = id / g.nzs;
@@ -115,20 +141,28 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
             src[q] = g.w[z] + (long long)min(gyi * WGW + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
             stride[q] = 1024;
         } else {
-            // bf16: plane p, k 8*(l >> 4) of the step; int8: half p, k 16*(l >> 4) + 8p
+            // bf16: plane p, k 8*(l >> 4) of the step; int8, Q8_0: half p, positions 16*(l >> 4) + 8p
             const int rt = (f - WGW) / NA, p = (f - WGW) % NA;
             const int r = min((gxi * 8 + rt) * 16 + (lane & 15), g.R - 1);
-            const long long e = WT == WT_I8 ? (long long)r * g.lda + 16 * (lane >> 4) + 8 * p
-                                            : p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4);
+            const long long e = (WT == WT_I8 || BQ) ? (long long)r * g.lda + 16 * (lane >> 4) + 8 * p
+                                                    : p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4);
             src[q] = reinterpret_cast<const uint8_t *>(g.a + e);
             stride[q] = TK * 2;
         }
     }
-    auto issue = [&](int kt, int slot) {  // every call issues LPW loads (k steps past the split re-read the last)
+    // Q8_0: this lane's dword of the stage's scales: byte 256*wv + 4*lane is
+    // row (lane & 15) of local weight tile (4*wv + lane / 16) mod WGW (clamped to the matrix)
+    const uint8_t *ssrc = nullptr;
+    if constexpr (BQ) {
+        const int t = min(gyi * WGW + (4 * wv + lane / 16) % WGW, g.n_tiles - 1);
+        ssrc = reinterpret_cast<const uint8_t *>(g.sc[z]) + (long long)t * g.KT * 64 + (lane & 15) * 4;
+    }
+    auto issue = [&](int kt, int slot) {  // every call issues LPS loads (k steps past the split re-read the last)
         kt = min(kt, kt1 - 1);
 #pragma unroll
         for (int q = 0; q < LPW; ++q)
-            lds_dma16(src[q] + (long long)kt * stride[q], (lds_void *)(ring + (slot * FR + wv * LPW + q) * 1024));
+            lds_dma16(src[q] + (long long)kt * stride[q], (lds_void *)(ring + slot * SB + (wv * LPW + q) * 1024));
+        if constexpr (BQ) lds_dma4(ssrc + (long long)kt * 64, (lds_void *)(ring + slot * SB + FR * 1024 + wv * 256));
     };
     f32x4 acc[WWT][2];
 #pragma unroll
@@ -144,9 +178,9 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
         // this wave's loads of step kt have landed (S - 2 later steps may be
         // in flight) and its reads of the previous step are done; then every
         // wave's: the barrier
-        wait_vm_barrier<(S - 2) * LPW>();
+        wait_vm_barrier<(S - 2) * LPS>();
         u32x4 wf[WWT], af[2][NA];
-        const uint8_t *base = ring + slot * FR * 1024 + lane * 16;
+        const uint8_t *base = ring + slot * SB + lane * 16;
 #pragma unroll
         for (int i = 0; i < WWT; ++i) wf[i] = *reinterpret_cast<const u32x4 *>(base + (WWT * (wv & 1) + i) * 1024);
 #pragma unroll
@@ -156,7 +190,36 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
                 af[j][p] = *reinterpret_cast<const u32x4 *>(base + (WGW + (2 * (wv >> 1) + j) * NA + p) * 1024);
         // the slot of step kt - 1: every wave has read it (it passed the barrier)
         issue(kt + S - 1, (kt - kt0 + S - 1) % S);
-        if constexpr (WT == WT_I8) {
+        if constexpr (BQ) {
+            // the codes widened as for int8; per block h a matrix-core step from
+            // zero with the rows as the A operand (so the lane holds weight row
+            // l & 15, whose block scales it reads), scaled and added in fp32
+            const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const uint8_t *sbase = ring + slot * SB + FR * 1024 + (lane & 15) * 4;
+#pragma unroll
+            for (int i = 0; i < WWT; ++i) {
+                const uint32_t sw = *reinterpret_cast<const uint32_t *>(sbase + (WWT * (wv & 1) + i) * 64);
+                const float d0 = half_lo(sw), d1 = half_hi(sw);
+                u32x4 b[2];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04010400u);
+                    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04030402u);
+                    b[c >> 1][2 * (c & 1)] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
+                    b[c >> 1][2 * (c & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[j][0]),
+                                                                            __builtin_bit_cast(f16x8, b[0]), zero, 0, 0, 0);
+                    const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[j][1]),
+                                                                            __builtin_bit_cast(f16x8, b[1]), zero, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(d1, t1[e], fmaf(d0, t0[e], acc[i][j][e]));
+                }
+            }
+        } else if constexpr (WT == WT_I8) {
             // biased codes u = q + 128 -> f16 (1024 + u) by a byte permute; minus 1152 leaves q
             const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
@@ -191,8 +254,23 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     }
     wait_vm_all();  // the clamped tail loads land before the work-group ends
     if (wt0 >= g.n_tiles) return;
-    // lane l holds rows 4*(l >> 4) .. +3 of weight tile i (outputs n) for A row (l & 15) of row tile j
     float *y = g.y[z] + (long long)s * g.y_split;
+    if constexpr (BQ) {
+        // lane l holds weight row (output n) l & 15 of tile i for A rows 4*(l >> 4) .. +3 of row tile j
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < WWT; ++i) {
+                const int n = (wt0 + i) * 16 + (lane & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = (rt0 + j) * 16 + 4 * (lane >> 4) + e;
+                    if (r < g.R && n < g.N) y[(long long)r * g.ldy + n] = acc[i][j][e];
+                }
+            }
+        return;
+    }
+    // lane l holds rows 4*(l >> 4) .. +3 of weight tile i (outputs n) for A row (l & 15) of row tile j
     const bool vec = (g.ldy & 3) == 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
