@@ -489,55 +489,84 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     }
 }
 
-// The three bf16 pieces of x: x == p0 + p1 + p2 exactly (24 mantissa bits).
-__device__ __forceinline__ void bf16_pieces(float x, uint32_t &b0, uint32_t &b1, uint32_t &b2) {
+// Piece pc (0..2) of x's exact three-piece bf16 split (x == p0 + p1 + p2:
+// 24 mantissa bits), as bits.
+__device__ __forceinline__ uint32_t bf16_piece(float x, int pc) {
     const float p0 = bf16_round(x);
     const float r1 = x - p0;
     const float p1 = bf16_round(r1);
     const float p2 = bf16_round(r1 - p1);
-    b0 = bf16_rne_bits(p0);
-    b1 = bf16_rne_bits(p1);
-    b2 = bf16_rne_bits(p2);
+    return bf16_rne_bits(pc == 0 ? p0 : (pc == 1 ? p1 : p2));  // (already a bf16 value)
+}
+// Piece pc of x and of y packed low, high; zero when !on.
+__device__ __forceinline__ uint32_t bf16_piece2(float x, float y, int pc, bool on) {
+    return on ? (bf16_piece(x, pc) | (bf16_piece(y, pc) << 16)) : 0u;
+}
+// Rotation by N lanes within each row of 16 lanes.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+// The sum of lanes c, c+4, c+8, c+12 of a row of 16, the same value in all
+// four: (v_c + v_c+8) + (v_c+4 + v_c+12), whose adds are commutative.
+__device__ __forceinline__ float sum_stride4(float v) {
+    const float t = v + row_ror<8>(v);
+    return t + row_ror<4>(t);
 }
 
 // The same split-K flash decode as k_attn for a bf16 cache, on the matrix
 // cores.  A wave's 16 keys form one 16x16 score tile per KV head:
-//   S^T[key][g] = sum_d K[key][d] * q[g][d]
+//   S^T[key][c] = sum_d K[key][d] * Q[c][d]
 // with K fragments as the A operand (16x16x32 steps over d; the cache stores
-// them in that order, see kv_k_off, so each load reads 1 KiB) and the scaled fp32
-// query split into three exact bf16 pieces that the same accumulator adds
-// (the products are exact, the sums fp32).  The tile leaves lane l holding
-// head l%16 and keys 4*(l/16)..+3, which is the B-operand layout of a
-// 16x16x16 step over keys, so the softmax stays in the lane and the weights
-// (again three bf16 pieces) feed
-//   O^T[d][g] += sum_key V^T[d][key] * P^T[key][g]
+// them in that order, see kv_k_off, so each load reads 1 KiB) and the scaled
+// fp32 query split into three exact bf16 pieces (the products are exact, the
+// sums fp32).  With G <= 4 the pieces are columns of the tile: column c =
+// 4p + g holds piece p of head g (p = 3 and heads past G are zero), so one
+// step per 32 dims scores all pieces, and a head's score is its four columns
+// added across lanes (sum_stride4, the same value in each).  With more heads
+// the columns are the heads and the same accumulator adds three steps, one
+// per piece.  The tile leaves lane l holding column l%16 and keys
+// 4*(l/16)..+3, which is the B-operand layout of a 16x16x16 step over keys,
+// so the softmax stays in the lane and the weights, again as three bf16
+// pieces (in the columns, or in three steps), feed
+//   O^T[d][c] += sum_key V^T[d][key] * P^T[key][c]
 // with V fragments (stored in operand order too, see kv_v_off: two fragments
-// per 16-byte lane load, 1 KiB per load) as the A operand; keys of a fragment outside the window are zeroed
-// (their weight is 0, and 0 * NaN is not) and rows of K outside it are masked
-// after the scores.  The output tile's column is again the lane's head, the one whose
-// running max the lane keeps (its running sum covers the lane's own keys and
-// is added over the four lanes of a head at the end).  Query heads past G are
-// zero columns.  The query pieces sit in LDS; K and V rotate through three
-// register buffers, so two chunks are in flight while one is scored.
+// per 16-byte lane load, 1 KiB per load) as the A operand; a head's output is
+// again the sum of its piece columns.  Keys of a fragment outside the window
+// are zeroed (their weight is 0, and 0 * NaN is not) and rows of K outside it
+// are masked after the scores.  A lane keeps the running max of its column's
+// head; the max moves only when a chunk's exceeds it by more than 8 (base 2,
+// so every weight stays below 2^8), and the output is rescaled only when it
+// moved for a head that had keys: both sides of the final division use the
+// same max, so this changes rounding only.  The running sum covers the lane's
+// own keys and is added over the four lanes of a column at the end.  The
+// query's loads go out before the first K/V loads, its pieces sit in LDS; K
+// and V rotate through three register buffers, so two chunks are in flight
+// while one is scored.
 template <int D, int G>
 __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     static_assert(G <= 16, "one 16-column tile of query heads");
+    constexpr bool PC = G <= 4;  // pieces in the columns
+    constexpr int NP = PC ? 1 : 3;  // steps per 32 dims and per 16 keys
     constexpr int NWV = kAttnWaves;
     constexpr int KS = D / 32;  // 16x16x32 steps over d
     constexpr int DT = D / 16;  // 16-row output tiles over d
+    constexpr int QU = (KS + NWV - 1) / NWV;  // query steps per wave
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const AttnRow R = attn_row(a, b);
     if (s >= R.nsplit) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
+    // the lane's column: piece pc of head gc (PC), or head r16
+    const int pc = PC ? r16 >> 2 : 0, gc = PC ? r16 & 3 : r16;
+    const bool hc = gc < G && pc < 3;  // the column holds a head (and a piece)
     const int lo = R.lo;
     const int np = R.np, ns_b = R.nsplit;
     const int kb = R.origin + (int)((long long)s * np / ns_b) * kPage;
     const int ke = min(R.origin + (int)((long long)(s + 1) * np / ns_b) * kPage, R.pos + 1);
-    const int kl = ke - 1;
 
-    __shared__ __align__(16) u32x4 qsh[3][KS][64];  // B operands of the query pieces, by lane
+    __shared__ __align__(16) u32x4 qsh[NP][KS][64];  // B operands of the query pieces, by lane
     __shared__ float wm[NWV][16], wl[NWV][16];
     __shared__ float wacc[NWV][G][D];
 
@@ -577,30 +606,37 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
             vr[2 * dp + 1] = u32x2{t[2], t[3]};
         }
     };
+    // the query's loads first (wave w: steps w, w+4, ...; lane l: its column's
+    // head, d = ks*32 + 8*q4..+7), so its pieces are made while K and V load
+    float qx[QU][8];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+        const int ks = min(w + u * NWV, KS - 1);
+        const float *qp = a.q + (long long)b * a.Hq * D + (long long)(j * G + min(gc, G - 1)) * D + ks * 32 + 8 * q4;
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(qp);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(qp + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qx[u][e] = x0[e];
+            qx[u][4 + e] = x1[e];
+        }
+    }
     u32x4 k0r[KS], k1r[KS], k2r[KS];
     u32x2 v0r[DT], v1r[DT], v2r[DT];
     load(0, k0r, v0r);
-    if (nch > 1) load(1, k1r, v1r);  // (split-uniform)
-
-    // the query pieces: wave w fills steps w, w+4, ... (lane l: head r16, d = ks*32 + 8*q4..+7)
-    for (int ks = w; ks < KS; ks += NWV) {
-        const float *qp = a.q + (long long)b * a.Hq * D + (long long)(j * G + min(r16, G - 1)) * D + ks * 32 + 8 * q4;
-        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(qp);
-        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(qp + 4);
-        const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        u32x4 p0, p1, p2;
+    load(1, k1r, v1r);  // (past a one-chunk split: zeros without a memory access; the count of loads stays fixed)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t lo0, lo1, lo2, hi0, hi1, hi2;
-            bf16_pieces(r16 < G ? xv[2 * e] * a.scale : 0.f, lo0, lo1, lo2);
-            bf16_pieces(r16 < G ? xv[2 * e + 1] * a.scale : 0.f, hi0, hi1, hi2);
-            p0[e] = lo0 | (hi0 << 16);
-            p1[e] = lo1 | (hi1 << 16);
-            p2[e] = lo2 | (hi2 << 16);
+    for (int u = 0; u < QU; ++u) {
+        const int ks = w + u * NWV;
+        if (ks >= KS) break;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            u32x4 pq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pq[e] = bf16_piece2(qx[u][2 * e] * a.scale, qx[u][2 * e + 1] * a.scale, PC ? pc : p, hc);
+            qsh[p][ks][lane] = pq;
         }
-        qsh[0][ks][lane] = p0;
-        qsh[1][ks][lane] = p1;
-        qsh[2][ks][lane] = p2;
     }
     lds_barrier();
 
@@ -617,7 +653,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
+            for (int p = 0; p < NP; ++p)
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[ks]),
                                                              __builtin_bit_cast(bf16x8, qsh[p][ks][lane]), sc, 0, 0,
                                                              0);
@@ -628,13 +664,15 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             vin[i] = key0 + i >= lo && key0 + i < ke;
-            sv[i] = vin[i] ? sc[i] : -INFINITY;
+            const float full = PC ? sum_stride4(sc[i]) : sc[i];  // the head's score
+            sv[i] = vin[i] ? full : -INFINITY;
             cm = fmaxf(cm, sv[i]);
         }
         cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-        const float mn = fmaxf(m, cm);
-        const float f = exp2_fast(m - mn);  // 0 on the wave's first chunk
+        const float mn = cm > m + 8.f ? cm : m;
+        const float f = exp2_fast(m - mn);  // 1 where the max stays, 0 on the wave's first chunk
+        const bool rescale = __builtin_amdgcn_ballot_w64(mn != m && m != -INFINITY) != 0;
         float pv[4], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -643,32 +681,32 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
         }
         l = l * f + ps;
         m = mn;
-        u32x2 pb[3];
+        u32x2 pb[NP];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t a0, a1, a2, c0, c1, c2;
-            bf16_pieces(pv[2 * h], a0, a1, a2);
-            bf16_pieces(pv[2 * h + 1], c0, c1, c2);
-            pb[0][h] = a0 | (c0 << 16);
-            pb[1][h] = a1 | (c1 << 16);
-            pb[2][h] = a2 | (c2 << 16);
-        }
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) pb[p][h] = bf16_piece2(pv[2 * h], pv[2 * h + 1], PC ? pc : p, hc);
         // keys outside the window read zeros from V (their weight is 0, and 0 * NaN is not)
-        const bool all_in = vin[0] && vin[1] && vin[2] && vin[3];
+        const bool all_in = __builtin_amdgcn_ballot_w64(!(vin[0] && vin[1] && vin[2] && vin[3])) == 0;
+        u32x2 vm[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            u32x2 v = vr[dt];
-            if (!all_in) {
-                v[0] = (vin[0] ? v[0] & 0xFFFFu : 0u) | (vin[1] ? v[0] & 0xFFFF0000u : 0u);
-                v[1] = (vin[2] ? v[1] & 0xFFFFu : 0u) | (vin[3] ? v[1] & 0xFFFF0000u : 0u);
-            }
-            f32x4 c = acc[dt] * f;
+        for (int dt = 0; dt < DT; ++dt) vm[dt] = vr[dt];
+        if (!all_in) {  // (wave-uniform: a window's edge chunks only)
+            const uint32_t m0 = (vin[0] ? 0xFFFFu : 0u) | (vin[1] ? 0xFFFF0000u : 0u);
+            const uint32_t m1 = (vin[2] ? 0xFFFFu : 0u) | (vin[3] ? 0xFFFF0000u : 0u);
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-                c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v),
-                                                             __builtin_bit_cast(s16x4, pb[p]), c, 0, 0, 0);
-            acc[dt] = c;
+            for (int dt = 0; dt < DT; ++dt) vm[dt] = u32x2{vm[dt][0] & m0, vm[dt][1] & m1};
         }
+        if (rescale) {  // (wave-uniform)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = acc[dt] * f;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vm[dt]),
+                                                                    __builtin_bit_cast(s16x4, pb[p]), acc[dt], 0, 0, 0);
     };
 
     if (nch == 1) {
@@ -686,11 +724,18 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
             chunk(ci + 2, k2r, v2r);
         }
     }
-    // the lane's sum covers its own keys: add the head's four lanes
+    // the lane's sum covers its own keys: add the column's four lanes
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
+    if constexpr (PC) {  // a head's output: its piece columns added (columns 0..G-1 hold them)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[dt][i] = sum_stride4(acc[dt][i]);
+    }
 
-    // merge the waves in wave order (a wave with no keys has m = -inf, l = 0)
+    // merge the waves in wave order (a wave with no keys has m = -inf, l = 0);
+    // columns 0..G-1 are the heads (with PC: piece 0 of each, holding the sums)
     if (q4 == 0) {
         wm[w][r16] = m;
         wl[w][r16] = l;

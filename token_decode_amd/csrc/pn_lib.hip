@@ -424,9 +424,11 @@ size_t layout_model(pn_model *m) {
     return bp.off;
 }
 
-// Automatic split size: aim for about this many attention work-groups per step
-// (two per compute unit: all resident at once, and evenly spread).
-constexpr int kAttnTargetGroups = 512;
+// Automatic split size: about one attention work-group per compute unit, or
+// two when that still leaves every split 8 pages or more (a short split is
+// scored right after its one round trip, so few long ones keep the tail
+// short; many pages want both work-groups of a compute unit streaming).
+long long attn_target_groups(long long pages) { return pages >= 8LL * 2 * kCUs ? 2 * kCUs : kCUs; }
 // The attention addresses a layer's K and V pools with 32-bit buffer offsets.
 constexpr size_t kMaxLayerBytes = (size_t)1 << 31;
 
@@ -679,7 +681,7 @@ struct Timed {
 // split s of nsplit takes pages [s*np/nsplit, (s+1)*np/nsplit), so a row's
 // splits differ by at most one page.  nsplit comes from the caller's keys per
 // split (PN_OPT_ATTN_KEYS_PER_SPLIT), else from sharing about
-// kAttnTargetGroups work-groups among the rows in proportion to their pages;
+// attn_target_groups work-groups among the rows in proportion to their pages;
 // it is at most the row's pages and its scratch capacity.  With rows, the
 // split scratch is the model's per-row buffer (prefill rows share a state);
 // otherwise each state's own.  Sets everything but q, o and the K/V pools;
@@ -698,7 +700,7 @@ int attn_setup(const pn_model *m, pn_state *const *st, int n, const int *pos, bo
         aa.origin[b] = lo / kPage * kPage;
         const int np = cdiv(pos[b] + 1 - aa.origin[b], kPage);
         long long ns = m->attn_kps > 0 ? cdiv(np, m->attn_kps / kPage)
-                                       : (long long)kAttnTargetGroups * np / ((long long)m->Hk * np_sum);
+                                       : attn_target_groups(m->Hk * np_sum) * np / ((long long)m->Hk * np_sum);
         const int cap = rows ? kMaxSplits : st[b]->s_cap;
         ns = std::min<long long>(std::max<long long>(ns, 1), std::min(np, std::min(cap, kMaxSplits)));
         aa.np[b] = np;
