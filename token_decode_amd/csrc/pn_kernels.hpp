@@ -410,7 +410,10 @@ __device__ __forceinline__ void issue_a(u32x4 (&ar)[KU][frag_vecs(WT)], const ui
 // MFMA over one round: tiles t_at..t_at+n-1 with A from LDS fragments or registers.
 // With A in LDS the round is branch-free: lanes past the A rows and tiles past
 // n read zero fragments (at zoff), which add nothing; so the compiler can
-// overlap one tile's matrix-core steps with the next tile's arithmetic.
+// overlap one tile's matrix-core steps with the next tile's arithmetic.  A
+// dead tile (past the matrix) is multiplied too (it re-reads a live tile of
+// its block, and the epilogues store rows below N only), except in the block
+// formats, whose scaled steps take more registers when not branched over.
 template <int WT, int NTW, int KU, bool ALDS>
 __device__ __forceinline__ void compute_round(f32x4 (&acc)[NTW], const u32x4 (&wr)[NTW][KU],
                                               const SReg<WT> (&sr)[NTW][KU], const u32x4 (&ar)[KU][frag_vecs(WT)],
@@ -426,11 +429,11 @@ __device__ __forceinline__ void compute_round(f32x4 (&acc)[NTW], const u32x4 (&w
             for (int v = 0; v < AV; ++v) a[v] = *reinterpret_cast<const u32x4 *>(af + 16 * v);
 #pragma unroll
             for (int mt = 0; mt < NTW; ++mt)
-                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], a, sr[mt][i]);
+                if (!blockq(WT) || wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], a, sr[mt][i]);
         } else if (i < n) {
 #pragma unroll
             for (int mt = 0; mt < NTW; ++mt)
-                if (wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], ar[i], sr[mt][i]);
+                if (!blockq(WT) || wlive[mt]) mfma_tile<WT>(acc[mt], wr[mt][i], ar[i], sr[mt][i]);
         }
     }
 }
@@ -970,8 +973,6 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 }
             }
         }
-        const bool live0 = wlive[0];
-        const bool live1 = NTW > 1 ? wlive[NTW - 1] : false;
         // the next block's first rounds and epilogue inputs go out before this block's epilogue
         EpIn epn = epc;
         if (blk + 1 < blk1) {
@@ -1125,8 +1126,6 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 }
             }
         }
-        (void)live0;
-        (void)live1;
         epc = epn;
         lds_barrier();  // red and C are reused by the next block
     }
