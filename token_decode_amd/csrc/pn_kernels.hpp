@@ -417,13 +417,15 @@ __device__ __forceinline__ void issue_a(u32x4 (&ar)[KU][frag_vecs(WT)], const ui
 template <int WT, int NTW, int KU, bool ALDS>
 __device__ __forceinline__ void compute_round(f32x4 (&acc)[NTW], const u32x4 (&wr)[NTW][KU],
                                               const SReg<WT> (&sr)[NTW][KU], const u32x4 (&ar)[KU][frag_vecs(WT)],
-                                              const uint8_t *sa, int zoff, int rows, int am, int ag, bool alive,
+                                              const uint8_t *sa, int zoff, int a_step, int a_base,
                                               const bool (&wlive)[NTW], int t_loc, int n) {
-    constexpr int FB = frag_bytes(WT), AV = frag_vecs(WT);
+    constexpr int AV = frag_vecs(WT);
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
         if constexpr (ALDS) {
-            const uint8_t *af = (alive && i < n) ? sa + (((t_loc + i) * 4 + ag) * rows + am) * FB : sa + zoff;
+            // this lane's fragment of tile t_loc + i: a_base + t * a_step (a dead lane's
+            // a_step is 0 and its a_base the zero block); tiles past n read the zero block
+            const uint8_t *af = sa + (i < n ? (t_loc + i) * a_step + a_base : zoff);
             u32x4 a[AV];
 #pragma unroll
             for (int v = 0; v < AV; ++v) a[v] = *reinterpret_cast<const u32x4 *>(af + 16 * v);
@@ -561,7 +563,9 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     constexpr int ES = AReady<WT, AT>::ES;
     extern __shared__ __align__(16) uint8_t smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index is uniform: read from lane 0 it lives in a scalar register, so the
+    // k range, round counts and tile addresses derived from it are scalar too)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ex = blockIdx.z;
     // an equal share (+-1) of the expert's blocks per work-group
     const int blk0 = (int)((long long)blockIdx.x * g.nblk / gridDim.x);
@@ -596,6 +600,9 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     // writes it before its own reads (a wave's LDS operations run in order; all
     // writers write zeros).
     if (ALDS && lane < 16) *reinterpret_cast<u32x4 *>(sa + zoff + lane * 16) = u32x4{0, 0, 0, 0};
+    // LDS offset of this lane's A fragment of k tile t: a_base + t * a_step
+    const int a_step = alive ? 4 * rows * FB : 0;
+    const int a_base = alive ? (ag * rows + am) * FB : zoff;
     float *C = red + NW * NTW * 256;                          // [mt][m][n]
 
     // ---- phase 1: the prologue's loads, all issued before any weight load and
@@ -956,7 +963,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         for (int mt = 0; mt < NTW; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int r = 0; r < rounds; r += 2) {
             const int ta = wt0 + r * KU;
-            compute_round<WT, NTW, KU, ALDS>(acc, wa, sca, aa, sa, zoff, rows, am, ag, alive, wlive, ta,
+            compute_round<WT, NTW, KU, ALDS>(acc, wa, sca, aa, sa, zoff, a_step, a_base, wlive, ta,
                                              min(KU, wt1 - ta));
             if (r + 2 < rounds) {
                 if constexpr (blockq(WT)) issue_s<WT, NTW, KU>(sca, sbase, ta + 2 * KU, last);
@@ -964,7 +971,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
                 if constexpr (!ALDS) issue_a<WT, AT, KU>(aa, arow, alive, ta + 2 * KU, last);
             }
             if (r + 1 < rounds) {
-                compute_round<WT, NTW, KU, ALDS>(acc, wb, scb, ab, sa, zoff, rows, am, ag, alive, wlive, ta + KU,
+                compute_round<WT, NTW, KU, ALDS>(acc, wb, scb, ab, sa, zoff, a_step, a_base, wlive, ta + KU,
                                                  min(KU, wt1 - ta - KU));
                 if (r + 3 < rounds) {
                     if constexpr (blockq(WT)) issue_s<WT, NTW, KU>(scb, sbase, ta + 3 * KU, last);
