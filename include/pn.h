@@ -364,8 +364,9 @@ enum {
 };
 
 /* Options (tuning only; results change at most by fp32 rounding):
- *  PN_OPT_ATTN_KEYS_PER_SPLIT  0 = automatic (about 512 attention
- *                              work-groups shared among the slots in
+ *  PN_OPT_ATTN_KEYS_PER_SPLIT  0 = automatic (about 256 attention
+ *                              work-groups, or 512 when each split still
+ *                              gets 8 pages, shared among the slots in
  *                              proportion to their windows), else a multiple
  *                              of 64: a slot's window of P pages of 64 keys is
  *                              cut into ceil(P / (value / 64)) splits that
