@@ -14,6 +14,10 @@
 - pn_model_create (one call, from a pn_weights struct of device pointers)
   builds the same model as pn_model_init + load_globals + load_layer: the
   logits are bitwise equal.
+- Scores that jump by far more than the matrix-core attention's lazy-max
+  threshold (2^8 in the softmax weights) from one page to the next, in one
+  split and across splits, so the running maximum moves and the output is
+  rescaled, against the oracle.
 """
 import ctypes
 
@@ -158,3 +162,42 @@ def test_model_create_equals_init_and_load():
     finally:
         L.pn_model_free(h)
     log("  pn_model_create: 6 steps bitwise equal to the init + load path")
+
+
+def _pow2_scale_bf16(bits, factor):
+    """bf16 bits times a power of two (exact)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kps,act", [(0, synth.F32), (4096, synth.F32), (4096, synth.BF16)])
+def test_attention_running_max_moves(kps, act):
+    """K rows of pages 3..5 scaled by 2^3 and of pages 6..10 by 2^6: each group's
+    scores dwarf the earlier ones', so a wave walking the pages in one split
+    (keys per split 4096) moves its running max twice and rescales its output;
+    with automatic splits (one page each) the merge weighs them instead."""
+    from token_decode_amd import _capi as C
+    wl = small("max-jump-kps%d" % kps, n_head=8, n_kv_head=2, head_dim=128, w_dtype=synth.BF16,
+               kv_dtype=synth.BF16, act_dtype=act, seed=156)
+    p = Pair(wl)
+    if kps:
+        p.dm.set_option(C.PN_OPT_ATTN_KEYS_PER_SPLIT, kps)
+    from token_decode_amd import device as dv
+    pos = 11 * 64 - 5
+    ds = dv.DeviceState(p.dm, pos + 4)
+    os_ = p.om.new_state(pos + 4)
+    for l in range(wl.n_layer):
+        k, v = wl.kv_prefill(0, l, 0, pos)
+        k = k.copy()
+        k[3 * 64:6 * 64] = _pow2_scale_bf16(k[3 * 64:6 * 64], 8.0)
+        k[6 * 64:] = _pow2_scale_bf16(k[6 * 64:], 64.0)
+        ds.set_kv(l, 0, k, v)
+        os_.set_kv(l, 0, k, v)
+    ds.pos = os_.pos = pos
+    token = int(synth.uniform_int(wl.seed, 8, 1, 0, wl.n_vocab - 1)[0])
+    for i in range(3):
+        g, gid = _one_step(p, ds, token)
+        ol, oa = os_.step(token)
+        rel, _ = compare_step(wl, g, ol, gid, oa, "kps %d, pos %d:" % (kps, pos + i))
+        token = oa
+    log("  running max moved between pages (keys per split %s): ok (last rel L2 %.2e)" % (kps or "auto", rel))
