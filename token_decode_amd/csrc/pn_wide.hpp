@@ -307,6 +307,18 @@ __device__ __forceinline__ float wide_sum(const float *y, long long split, int n
     return t;
 }
 
+// The same for elements idx .. idx+3 (16-byte aligned), four per load.
+__device__ __forceinline__ f32x4 wide_sum4(const float *y, long long split, int nsplit, long long idx) {
+    f32x4 v[kWideSplitMax];
+#pragma unroll
+    for (int s = 0; s < kWideSplitMax; ++s)
+        v[s] = s < nsplit ? *reinterpret_cast<const f32x4 *>(y + (long long)s * split + idx) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 t = v[0];
+#pragma unroll
+    for (int s = 1; s < kWideSplitMax; ++s) t += v[s];
+    return t;
+}
+
 // Sums of squares of x per row and 1024-column block, [row][kWideSsq]: written
 // by the kernels that write x, read by the norm in block order.
 constexpr int kWideSsq = 8;  // blocks per row (E <= 8192)
@@ -348,12 +360,43 @@ __global__ void __launch_bounds__(256) k_w_embed(const uint16_t *__restrict__ em
 // consecutive columns per thread (one pass, every load issued up front),
 // except the norm, which reduces its row first.
 
-// Columns c .. c+3 of row r of A as MFMA planes (AReady layout of bf16
-// weights: three bf16 pieces of an fp32 value, or its bf16 rounding).
+// Columns c .. c+3 (c a multiple of 4) of row r of A as MFMA planes, in the
+// AReady layout: three bf16 pieces of an fp32 value, or its bf16 rounding, or
+// f16 for int8 and Q8_0 weights (Q8_0 in blk_pos order, which keeps runs of 8
+// in place).  The four land side by side in every plane: one 8-byte store each.
 template <int WT, int AT>
-__device__ __forceinline__ void wide_put4(uint16_t *a, long long plane, long long idx, const float (&v)[4]) {
+__device__ __forceinline__ void wide_put4(uint16_t *a, long long plane, long long idx, const float (&v0)[4]) {
+    float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) AReady<WT, AT>::store(a, plane, idx + e, v[e]);
+    for (int e = 0; e < 4; ++e) v[e] = AT == AT_BF16 ? bf16_round(v0[e]) : v0[e];
+    long long pos = idx;
+    if constexpr (blockq(WT)) {
+        constexpr int TK = tile_k(WT);
+        pos = (idx & ~(long long)(TK - 1)) | blk_pos(tile_blocks(WT), (int)(idx & (TK - 1)));
+    }
+    if constexpr (f16_a(WT)) {
+        *reinterpret_cast<u32x2 *>(a + pos) =
+            u32x2{__builtin_bit_cast(uint32_t, f16x2{(_Float16)v[0], (_Float16)v[1]}),
+                  __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[2], (_Float16)v[3]})};
+    } else if constexpr (AReady<WT, AT>::PIECES == 1) {
+        *reinterpret_cast<u32x2 *>(a + pos) = u32x2{bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16),
+                                                    bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16)};
+    } else {
+        uint32_t b[3][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = bf16_round(v[e]);
+            const float r1 = v[e] - p0;
+            const float p1 = bf16_round(r1);
+            const float p2 = bf16_round(r1 - p1);
+            b[0][e] = bf16_rne_bits(p0);
+            b[1][e] = bf16_rne_bits(p1);
+            b[2][e] = bf16_rne_bits(p2);
+        }
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            *reinterpret_cast<u32x2 *>(a + p * plane + pos) = u32x2{b[p][0] | (b[p][1] << 16), b[p][2] | (b[p][3] << 16)};
+    }
 }
 
 // Row r of A = round_act(RMSNorm(x[r]) * gain), zero from K to lda, the
@@ -367,12 +410,22 @@ __global__ void __launch_bounds__(256) k_w_norm(const float *__restrict__ x, int
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= lda) return;
     const int nb = (K + 1023) / 1024;
+    // every load first (K is a multiple of 8, so four columns are all in or all out)
+    const bool in = c < K;
+    const int cc = in ? c : 0;
+    const f32x4 xv = *reinterpret_cast<const f32x4 *>(x + (long long)r * K + cc);
+    const f32x4 gv = *reinterpret_cast<const f32x4 *>(gain + cc);
+    float sv[kWideSsq];
+#pragma unroll
+    for (int i = 0; i < kWideSsq; ++i) sv[i] = ssq[r * kWideSsq + min(i, nb - 1)];
     float ss = 0.f;
-    for (int i = 0; i < nb; ++i) ss += ssq[r * kWideSsq + i];
+#pragma unroll
+    for (int i = 0; i < kWideSsq; ++i)
+        if (i < nb) ss += sv[i];
     const float ri = 1.0f / sqrtf(ss / (float)K + eps);
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = c + e < K ? (x[(long long)r * K + c + e] * ri) * gain[c + e] : 0.f;
+    for (int e = 0; e < 4; ++e) v[e] = in ? (xv[e] * ri) * gv[e] : 0.f;
     wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, v);
 }
 
@@ -383,9 +436,12 @@ __global__ void __launch_bounds__(256) k_w_conv(const float *__restrict__ src, i
                                                  long long a_plane, int lda) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= lda) return;
+    // (K = heads x head_dim, a multiple of 32: four columns are all in or all out)
+    const bool in = c < K;
+    const f32x4 sv = *reinterpret_cast<const f32x4 *>(src + (long long)r * K + (in ? c : 0));
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = c + e < K ? src[(long long)r * K + c + e] : 0.f;
+    for (int e = 0; e < 4; ++e) v[e] = in ? sv[e] : 0.f;
     wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, v);
 }
 
@@ -397,13 +453,10 @@ __global__ void __launch_bounds__(256) k_w_swiglu(const float *__restrict__ yg, 
                                                    uint16_t *__restrict__ a, long long a_plane, int lda) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= lda) return;
-    float gt[4], up[4], h[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const long long i = (long long)r * ldy + min(c + e, F - 1);
-        gt[e] = wide_sum(yg, split, nsplit, i);
-        up[e] = wide_sum(yu, split, nsplit, i);
-    }
+    // four columns per load; past F (ldy is F rounded up to 16) the values are not used
+    const long long i = (long long)r * ldy + min(c, ldy - 4);
+    const f32x4 gt = wide_sum4(yg, split, nsplit, i), up = wide_sum4(yu, split, nsplit, i);
+    float h[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = c + e < F ? (gt[e] / (1.0f + expf(-gt[e]))) * up[e] : 0.f;
     wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, h);
@@ -415,18 +468,17 @@ __global__ void __launch_bounds__(256) k_w_resid(float *__restrict__ x, const fl
                                                   int nsplit, int ldy, int E, float *__restrict__ ssq) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
     float sq = 0.f;
-    if (c < E) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = wide_sum(y, split, nsplit, (long long)r * ldy + min(c + e, E - 1));
+    if (c < E) {  // (E a multiple of 8: all four columns in; ldy and the split stride multiples of 16)
+        const f32x4 v = wide_sum4(y, split, nsplit, (long long)r * ldy + c);
+        f32x4 *xp = reinterpret_cast<f32x4 *>(x + (long long)r * E + c);
+        const f32x4 xo = *xp;
+        f32x4 xn;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (c + e < E) {
-                const float xn = x[(long long)r * E + c + e] + v[e];
-                x[(long long)r * E + c + e] = xn;
-                sq += xn * xn;
-            }
+            xn[e] = xo[e] + v[e];
+            sq += xn[e] * xn[e];
         }
+        *xp = xn;
     }
     sq = wide_block_sum(sq);  // (every thread takes part: no early return above)
     if (threadIdx.x == 0) ssq[r * kWideSsq + blockIdx.x] = sq;
