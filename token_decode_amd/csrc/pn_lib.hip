@@ -1169,8 +1169,10 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
     const int var = wide_variant(m);
     const bool i8 = var == 2, q8 = var == 3;
     float *ssq = (float *)(mb + m->wss);
+    // the row kernels write the columns a product over K reads (K rounded up to weight tiles)
+    auto cols = [&](int K) { return (unsigned)cdiv(wide_kp((i8 || q8) ? WT_I8 : WT_BF16, K), 1024); };
     auto norm = [&](const float *gain) {
-        const dim3 gn(cdiv(m->wlda, 1024), R);
+        const dim3 gn(cols(E), R);
         if (q8)
             hipLaunchKernelGGL((k_w_norm<WT_Q8, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
                                m->wlda);
@@ -1236,7 +1238,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         }
         // ---- O + residual
         {
-            const dim3 gc(cdiv(m->wlda, 1024), R);
+            const dim3 gc(cols(HD), R);
             if (q8) hipLaunchKernelGGL((k_w_conv<WT_Q8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
             else if (i8) hipLaunchKernelGGL((k_w_conv<WT_I8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
             else if (bf) hipLaunchKernelGGL((k_w_conv<WT_BF16, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
@@ -1257,7 +1259,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             const bool fits = 2LL * 2 * R * ld <= m->wy_cap;
             const int ks = wide_gemm(m, L.gate, (const uint8_t *)(mb + L.gate.off), (const uint8_t *)(mb + L.up.off),
                                      scales(L.gate), scales(L.up), y, yu, 2, R, ld, ld, fits, s);
-            const dim3 gs(cdiv(m->wlda, 1024), R);
+            const dim3 gs(cols(F), R);
             const long long sp = (long long)R * ld;
             if (q8)
                 hipLaunchKernelGGL((k_w_swiglu<WT_Q8, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a, m->wa_plane,

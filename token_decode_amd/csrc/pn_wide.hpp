@@ -399,16 +399,21 @@ __device__ __forceinline__ void wide_put4(uint16_t *a, long long plane, long lon
     }
 }
 
-// Row r of A = round_act(RMSNorm(x[r]) * gain), zero from K to lda, the
-// row's sum of squares added from its block sums in block order.  grid:
-// (cdiv(lda, 1024), rows).  (WT, AT: the layout of AReady - bf16 pieces or
-// planes, or f16 rows for int8 weights.)
+// The columns of an A row that a product over K reads: K rounded up to whole
+// weight tiles.  The row kernels write those (zeros past K) and leave the
+// rest of the lda-wide row alone: no product with this K reads it.
+__host__ __device__ constexpr int wide_kp(int WT, int K) { return (K + tile_k(WT) - 1) / tile_k(WT) * tile_k(WT); }
+
+// Row r of A = round_act(RMSNorm(x[r]) * gain), zero from K to wide_kp(K),
+// the row's sum of squares added from its block sums in block order.  grid:
+// (cdiv(wide_kp(K), 1024), rows).  (WT, AT: the layout of AReady - bf16
+// pieces or planes, or f16 rows for int8 and Q8_0 weights.)
 template <int WT, int AT>
 __global__ void __launch_bounds__(256) k_w_norm(const float *__restrict__ x, int K, const float *__restrict__ gain,
                                                  float eps, const float *__restrict__ ssq, uint16_t *__restrict__ a,
                                                  long long a_plane, int lda) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (c >= lda) return;
+    if (c >= wide_kp(WT, K)) return;
     const int nb = (K + 1023) / 1024;
     // every load first (K is a multiple of 8, so four columns are all in or all out)
     const bool in = c < K;
@@ -429,13 +434,13 @@ __global__ void __launch_bounds__(256) k_w_norm(const float *__restrict__ x, int
     wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, v);
 }
 
-// Row r of A = round_act(src[r]) (fp32 rows of ld K), zero from K to lda.
-// grid: (cdiv(lda, 1024), rows).
+// Row r of A = round_act(src[r]) (fp32 rows of ld K), zero from K to
+// wide_kp(K).  grid: (cdiv(wide_kp(K), 1024), rows).
 template <int WT, int AT>
 __global__ void __launch_bounds__(256) k_w_conv(const float *__restrict__ src, int K, uint16_t *__restrict__ a,
                                                  long long a_plane, int lda) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (c >= lda) return;
+    if (c >= wide_kp(WT, K)) return;
     // (K = heads x head_dim, a multiple of 32: four columns are all in or all out)
     const bool in = c < K;
     const f32x4 sv = *reinterpret_cast<const f32x4 *>(src + (long long)r * K + (in ? c : 0));
@@ -446,13 +451,14 @@ __global__ void __launch_bounds__(256) k_w_conv(const float *__restrict__ src, i
 }
 
 // h = silu(gate) * up from the split outputs of the gate / up products, as the
-// down projection's A planes (zero from F to lda).  grid: (cdiv(lda, 1024), rows).
+// down projection's A planes (zero from F to wide_kp(F)).  grid:
+// (cdiv(wide_kp(F), 1024), rows).
 template <int WT, int AT>
 __global__ void __launch_bounds__(256) k_w_swiglu(const float *__restrict__ yg, const float *__restrict__ yu,
                                                    long long split, int nsplit, int ldy, int F,
                                                    uint16_t *__restrict__ a, long long a_plane, int lda) {
     const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (c >= lda) return;
+    if (c >= wide_kp(WT, F)) return;
     // four columns per load; past F (ldy is F rounded up to 16) the values are not used
     const long long i = (long long)r * ldy + min(c, ldy - 4);
     const f32x4 gt = wide_sum4(yg, split, nsplit, i), up = wide_sum4(yu, split, nsplit, i);
