@@ -1034,22 +1034,35 @@ constexpr int kWideAttnSplits = 8;
 static_assert((long long)kWideRows * kWideAttnSplits <= (long long)kMaxSlots * kMaxSplits,
               "the rows' split scratch fits the per-row attention buffer");
 
-// Splits over K of one wide GEMM.  The kernel runs one work-group per compute
-// unit (its LDS ring), so the grid should fill whole rounds of kCUs: the
-// fewest splits (1, 2, 4, 8) that give at least one round at 95% or better
-// of whole rounds, else the best such fraction; every split keeps at least 8
-// k tiles and the outputs fit the split buffer.
-int wide_splits(long long groups, int KT, long long floats_per_split, long long cap) {
-    int best = 1;
-    double best_f = -1.0;
-    for (int ks = 1; ks <= kWideSplitMax; ks *= 2) {
-        if (ks > 1 && (KT / ks < 8 || ks * floats_per_split > cap)) break;
-        const long long n = groups * ks;
-        const double f = (double)n / (double)(cdiv(n, (long long)kCUs) * kCUs);
-        if (n >= kCUs && f >= 0.95) return ks;
-        if (f > best_f + 1e-9) {
-            best_f = f;
-            best = ks;
+// The weight-group width (8 or 16 tiles) and the splits over K (1 to 8) of
+// one wide GEMM, from a model of its time fitted to timings of the kernel
+// (8B-model projections at 128 and 256 rows, every width and split count):
+// the kernel runs one work-group per compute unit, so the grid runs in rounds
+// of kCUs work-groups; a round takes its split's k steps times the measured
+// time of one step (by weight type and width) plus about 1 us, and every MB
+// of split outputs adds 0.35 us (written here, read back by the row kernel
+// that follows).  The least modelled time wins (ties: the narrower width,
+// then fewer splits).  Every split keeps at least 8 k tiles, and the outputs
+// fit the split buffer (cap floats).
+struct WidePlan {
+    int wgw, ks;
+};
+WidePlan wide_plan(int v, int R, int n_tiles, int KT, int nz, long long per, bool split_ok, long long cap) {
+    // us per k step of a 16- and an 8-tile group: bf16 rows, fp32 rows as three
+    // bf16 pieces, int8, Q8_0 (the variants of wide_variant)
+    static const double step_us[4][2] = {{0.75, 0.43}, {1.185, 0.865}, {1.30, 0.73}, {1.74, 1.03}};
+    WidePlan best{8, 1};
+    double best_t = -1.0;
+    for (int w : {8, 16}) {
+        for (int ks = 1; ks <= (split_ok ? kWideSplitMax : 1); ++ks) {
+            if (ks > 1 && (KT / ks < 8 || ks * per * nz > cap)) break;
+            const long long groups = (long long)cdiv(R, 128) * cdiv(n_tiles, w) * nz * ks;
+            const double rounds = (double)cdiv(groups, (long long)kCUs);
+            const double t = rounds * (cdiv(KT, ks) * step_us[v][w == 16 ? 0 : 1] + 1.0) + 0.35e-6 * 4.0 * ks * nz * per;
+            if (best_t < 0.0 || t < best_t - 1e-9) {
+                best_t = t;
+                best = {w, ks};
+            }
         }
     }
     return best;
@@ -1091,23 +1104,9 @@ int wide_lds(int v, int wgw) {
 
 int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_t *w1, const float *s0,
               const float *s1, float *y0, float *y1, int nz, int R, int N, int ldy, bool split_ok, hipStream_t s) {
-    // Groups of 8 or 16 weight tiles, each with the K split wide_splits picks
-    // for it: the wider group reads a third fewer LDS bytes per output, taken
-    // here as 0.8 of the time per tile; the width with the fewer rounds of
-    // work per compute unit wins (ties: 8).
     const long long per = (long long)R * ldy;
-    int wgw = 8, ks = 1;
-    double best = 0.0;
-    for (int w : {8, 16}) {
-        const long long groups = (long long)cdiv(R, 128) * cdiv(mat.n_tiles, w) * nz;
-        const int k = split_ok ? wide_splits(groups, mat.KT, per * nz, m->wy_cap) : 1;
-        const double cost = (double)cdiv(groups * k, kCUs) * (w / 8) / k * (w == 16 ? 0.8 : 1.0);
-        if (w == 8 || cost < best - 1e-9) {
-            best = cost;
-            wgw = w;
-            ks = k;
-        }
-    }
+    const WidePlan pl = wide_plan(wide_variant(m), R, mat.n_tiles, mat.KT, nz, per, split_ok, m->wy_cap);
+    const int wgw = pl.wgw, ks = pl.ks;
     WGemmArgs g{};
     g.w[0] = w0;
     g.w[1] = w1 ? w1 : w0;
