@@ -1034,15 +1034,17 @@ constexpr int kWideAttnSplits = 8;
 static_assert((long long)kWideRows * kWideAttnSplits <= (long long)kMaxSlots * kMaxSplits,
               "the rows' split scratch fits the per-row attention buffer");
 
-// The weight-group width (8 or 16 tiles) and the splits over K (1 to 8) of
+// The weight-group width (8, 14 or 16 tiles) and the splits over K (1 to 8) of
 // one wide GEMM, from a model of its time fitted to timings of the kernel
 // (8B-model projections at 128 and 256 rows, every width and split count):
 // the kernel runs one work-group per compute unit, so the grid runs in rounds
 // of kCUs work-groups; a round takes its split's k steps times the measured
 // time of one step (by weight type and width) plus about 1 us, and every MB
 // of split outputs adds 0.35 us (written here, read back by the row kernel
-// that follows).  The least modelled time wins (ties: the narrower width,
-// then fewer splits).  Every split keeps at least 8 k tiles, and the outputs
+// that follows); a 14-tile step takes 0.875 of a 16-tile one (its share of
+// the matrix-core work; 14 tiles fill whole rounds where 16 leave compute
+// units idle, e.g. 896 tiles: 256 work-groups against 224).  The least
+// modelled time wins (ties: the narrower width, then fewer splits).  Every split keeps at least 8 k tiles, and the outputs
 // fit the split buffer (cap floats).
 struct WidePlan {
     int wgw, ks;
@@ -1053,12 +1055,13 @@ WidePlan wide_plan(int v, int R, int n_tiles, int KT, int nz, long long per, boo
     static const double step_us[4][2] = {{0.75, 0.43}, {1.185, 0.865}, {1.30, 0.73}, {1.74, 1.03}};
     WidePlan best{8, 1};
     double best_t = -1.0;
-    for (int w : {8, 16}) {
+    for (int w : {8, 14, 16}) {
+        const double step = w == 8 ? step_us[v][1] : step_us[v][0] * (w == 14 ? 0.875 : 1.0);
         for (int ks = 1; ks <= (split_ok ? kWideSplitMax : 1); ++ks) {
             if (ks > 1 && (KT / ks < 8 || ks * per * nz > cap)) break;
             const long long groups = (long long)cdiv(R, 128) * cdiv(n_tiles, w) * nz * ks;
             const double rounds = (double)cdiv(groups, (long long)kCUs);
-            const double t = rounds * (cdiv(KT, ks) * step_us[v][w == 16 ? 0 : 1] + 1.0) + 0.35e-6 * 4.0 * ks * nz * per;
+            const double t = rounds * (cdiv(KT, ks) * step + 1.0) + 0.35e-6 * 4.0 * ks * nz * per;
             if (best_t < 0.0 || t < best_t - 1e-9) {
                 best_t = t;
                 best = {w, ks};
@@ -1077,11 +1080,13 @@ int wide_variant(const pn_model *m) {
     return m->wt == PN_Q8_0 ? 3 : (m->wt == PN_I8 ? 2 : (m->pieces == 3 ? 1 : 0));
 }
 // fn(WT, P, WGW) (as integral constants) for variant v with work-groups of wgw
-// weight tiles (8 or 16).
+// weight tiles (8, 14 or 16).
 template <typename Fn>
 auto with_wide(int v, int wgw, Fn fn) {
     auto go = [&](auto wt, auto p) {
-        return wgw == 16 ? fn(wt, p, std::integral_constant<int, 16>{}) : fn(wt, p, std::integral_constant<int, 8>{});
+        return wgw == 16   ? fn(wt, p, std::integral_constant<int, 16>{})
+               : wgw == 14 ? fn(wt, p, std::integral_constant<int, 14>{})
+                           : fn(wt, p, std::integral_constant<int, 8>{});
     };
     using I = std::integral_constant<int, 1>;
     switch (v) {
@@ -1143,7 +1148,7 @@ int wide_lds_attr() {
     static bool done = false;
     if (done) return PN_OK;
     for (int v = 0; v < 4; ++v)
-        for (int wgw : {8, 16}) {
+        for (int wgw : {8, 14, 16}) {
             const hipError_t e = hipFuncSetAttribute(wide_kernel(v, wgw), hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      wide_lds(v, wgw));
             if (e != hipSuccess) return fail(PN_EHIP, "wide GEMM LDS attribute: %s", hipGetErrorString(e));

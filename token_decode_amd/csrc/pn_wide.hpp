@@ -36,14 +36,15 @@ constexpr int kWideSplitMax = 8; // most K splits of one wide GEMM
 // zs, with zs = matrix * nsplit + split varying fastest: work-groups are
 // dealt to the XCDs in id order, so with 8 (or 4) values of zs each XCD's L2
 // holds the A slice of one split instead of all of A; a W group is WGW tiles
-// (8 or 16: 128 or 256 rows), an A group 128 rows; 512 threads (two waves per
-// SIMD: one computes while the other waits on LDS).  Wave w computes weight
-// tiles (WGW/2)*(w & 1) .. +WGW/2-1 against row tiles 2*(w >> 1), +1 of the
-// group (WGW accumulators): the wider group reads a third fewer LDS bytes per
-// output, for products with rows enough to fill the chip without splitting K.
-// A k step's WGW weight and 8*NA row fragments (1 KiB each)
-// go from memory straight into a ring of LDS stages (each wave loads an eighth
-// of them); S - 1 steps are in flight while the work-group computes one, at
+// (8, 14 or 16: 128, 224 or 256 rows), an A group 128 rows; 512 threads (two
+// waves per SIMD: one computes while the other waits on LDS).  Wave w
+// computes weight tiles (WGW/2)*(w & 1) .. +WGW/2-1 against row tiles
+// 2*(w >> 1), +1 of the group (WGW accumulators): the wider group reads a
+// third fewer LDS bytes per output, for products with rows enough to fill the
+// chip without splitting K; 14 tiles fill whole rounds of compute units where
+// 16 would not.  A k step's WGW weight and 8*NA row fragments (1 KiB each) go
+// from memory straight into a ring of LDS stages (each wave loads an eighth
+// of them, rounded up); S - 1 steps are in flight while the work-group computes one, at
 // one barrier per step, so the loads in flight take no registers.  Tiles past
 // n_tiles and rows past R load clamped (in bounds) and are not stored.
 struct WGemmArgs {
@@ -67,10 +68,14 @@ __host__ __device__ constexpr int wgemm_scb(int WT) { return WT == WT_Q8 ? 2048 
 // Fragments (1 KiB each) of one k step of a work-group that owns WGW weight
 // tiles and 8 row tiles: the weight tiles, then every row tile's NA fragments.
 __host__ __device__ constexpr int wgemm_frags(int WT, int P, int WGW) { return WGW + 8 * wgemm_na(WT, P); }
+// Loads per wave per k step: the fragments shared over 8 waves, rounded up
+// (with 14 weight tiles the last loads repeat a fragment into a slot nobody
+// reads, so that every wave issues the same number and its waits count right).
+__host__ __device__ constexpr int wgemm_lpw(int WT, int P, int WGW) { return (wgemm_frags(WT, P, WGW) + 7) / 8; }
 // Bytes of one stage of the LDS ring, and the stages: as many k steps as fit
 // 128 KiB (Q8_0, whose stages also hold scales: 144 KiB), at most 8.
 __host__ __device__ constexpr int wgemm_stage_bytes(int WT, int P, int WGW) {
-    return wgemm_frags(WT, P, WGW) * 1024 + wgemm_scb(WT);
+    return 8 * wgemm_lpw(WT, P, WGW) * 1024 + wgemm_scb(WT);
 }
 __host__ __device__ constexpr int wgemm_stages(int WT, int P, int WGW) {
     return (WT == WT_Q8 ? 144 : 128) * 1024 / wgemm_stage_bytes(WT, P, WGW) < 8
@@ -113,12 +118,12 @@ __device__ __forceinline__ void wait_vm_all() {
 template <int WT, int P, int WGW>
 __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     constexpr int NA = wgemm_na(WT, P), TK = tile_k(WT);
-    constexpr int S = wgemm_stages(WT, P, WGW), FR = wgemm_frags(WT, P, WGW), LPW = FR / 8;
+    constexpr int S = wgemm_stages(WT, P, WGW), FR = wgemm_frags(WT, P, WGW), LPW = wgemm_lpw(WT, P, WGW);
     constexpr int WWT = WGW / 2;  // weight tiles per wave
     constexpr bool BQ = WT == WT_Q8;
     constexpr int SB = wgemm_stage_bytes(WT, P, WGW);
     constexpr int LPS = LPW + (BQ ? 1 : 0);  // loads per wave per k step
-    static_assert(FR % 8 == 0 && S >= 3, "eight waves share a step's loads; three stages at least");
+    static_assert(WGW % 2 == 0 && S >= 3, "two waves share a row tile's weight tiles; three stages at least");
     static_assert(!BQ || WGW * 64 <= wgemm_scb(WT), "the scale area holds the work-group's scale tiles");
     // [S][SB]: W tiles 0..WGW-1, then A [row tile][plane] (1 KiB each), then (Q8_0) the scales
     extern __shared__ __align__(16) uint8_t ring[];
@@ -131,12 +136,13 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     const int wt0 = gyi * WGW + WWT * (wv & 1);  // first weight tile the wave computes
     const int rt0 = gxi * 8 + 2 * (wv >> 1);  // first row tile the wave computes
     // The wave loads fragments wv*LPW .. +LPW-1 of every stage: a W tile
-    // (clamped to the matrix) or a (row tile, plane) of A (rows clamped to R).
+    // (clamped to the matrix) or a (row tile, plane) of A (rows clamped to R);
+    // a slot past the FR fragments takes a copy of the last one.
     const uint8_t *src[LPW];
     int stride[LPW];  // bytes per k step
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-        const int f = wv * LPW + q;
+        const int f = min(wv * LPW + q, FR - 1);
         if (f < WGW) {
             src[q] = g.w[z] + (long long)min(gyi * WGW + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
             stride[q] = 1024;
@@ -162,7 +168,7 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
 #pragma unroll
         for (int q = 0; q < LPW; ++q)
             lds_dma16(src[q] + (long long)kt * stride[q], (lds_void *)(ring + slot * SB + (wv * LPW + q) * 1024));
-        if constexpr (BQ) lds_dma4(ssrc + (long long)kt * 64, (lds_void *)(ring + slot * SB + FR * 1024 + wv * 256));
+        if constexpr (BQ) lds_dma4(ssrc + (long long)kt * 64, (lds_void *)(ring + slot * SB + 8 * LPW * 1024 + wv * 256));
     };
     f32x4 acc[WWT][2];
 #pragma unroll
@@ -196,7 +202,7 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
             // l & 15, whose block scales it reads), scaled and added in fp32
             const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t *sbase = ring + slot * SB + FR * 1024 + (lane & 15) * 4;
+            const uint8_t *sbase = ring + slot * SB + 8 * LPW * 1024 + (lane & 15) * 4;
 #pragma unroll
             for (int i = 0; i < WWT; ++i) {
                 const uint32_t sw = *reinterpret_cast<const uint32_t *>(sbase + (WWT * (wv & 1) + i) * 64);
