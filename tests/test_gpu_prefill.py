@@ -270,9 +270,10 @@ def test_wide_q8_0_weights():
 
 def test_wide_q8_0_llama3_shape():
     """Llama-3-8B layer shape with Q8_0 weights (2 layers, full vocabulary):
-    40 prompt tokens in chunks of 32 after a 30-token cache.  At 32 rows QKV,
-    gate/up and the LM head run in work-groups of 16 weight tiles, O and down
-    in groups of 8, all but the LM head with K split over work-groups."""
+    40 prompt tokens in chunks of 32 after a 30-token cache.  At 32 rows the
+    planner runs QKV and gate/up in work-groups of 14 weight tiles (QKV's 384
+    tiles leave the last group ragged), O and down in groups of 8 and the LM
+    head in groups of 16, all but the LM head with K split over work-groups."""
     wl = synth.WORKLOADS["llama3-8b-q8_0"]().with_(name="wide-llama3-q8_0-2l", n_layer=2, seed=94)
     p = Pair(wl, max_batch=1, prefill_chunk=32)
     prompt = list(synth.uniform_int(wl.seed, 104, 40, 0, wl.n_vocab - 1))
@@ -282,8 +283,10 @@ def test_wide_q8_0_llama3_shape():
 
 def test_wide_mistral_shape_full_chunk():
     """Mistral-7B layer shape (2 layers, bf16 activations, window 4096): a full
-    256-row chunk, then 44 rows.  At 256 rows every product but QKV runs in
-    work-groups of 16 weight tiles (QKV in groups of 8, K split 8 ways)."""
+    256-row chunk, then 44 rows.  At 256 rows the planner runs QKV (ragged
+    last group) and gate/up in work-groups of 14 weight tiles, O in groups of
+    8 and down and the LM head in groups of 16; the 44-row tail takes narrower
+    groups with more K splits."""
     wl = synth.mistral_7b_slots().with_(name="wide-mistral-2l", n_layer=2, slots=1, seed=92)
     p = Pair(wl, max_batch=1, prefill_chunk=256)
     prompt = list(synth.uniform_int(wl.seed, 102, 300, 0, wl.n_vocab - 1))
