@@ -1190,6 +1190,23 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_F32>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
                                m->wlda);
     };
+    // x += the split outputs y (ld columns, ks splits), then the next norm's A planes from the new x
+    auto resid_norm = [&](int ld, int ks, const float *gain) {
+        const long long sp = (long long)R * ld;
+        if (q8)
+            hipLaunchKernelGGL((k_w_resid_norm<WT_Q8, AT_BF16>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps, a,
+                               m->wa_plane, m->wlda);
+        else if (i8)
+            hipLaunchKernelGGL((k_w_resid_norm<WT_I8, AT_BF16>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps, a,
+                               m->wa_plane, m->wlda);
+        else if (bf)
+            hipLaunchKernelGGL((k_w_resid_norm<WT_BF16, AT_BF16>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps,
+                               a, m->wa_plane, m->wlda);
+        else
+            hipLaunchKernelGGL((k_w_resid_norm<WT_BF16, AT_F32>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps,
+                               a, m->wa_plane, m->wlda);
+    };
+    const bool outputs = logits || amax;
     auto scales = [&](const Mat &mt) { return (i8 || q8) ? (const float *)(mb + mt.soff) : nullptr; };
     if (int rc = wide_lds_attr()) return rc;
     hipLaunchKernelGGL(k_w_embed, dim3(cdiv(E, 1024), R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E,
@@ -1197,8 +1214,8 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerOff &L = m->L[l];
         char *kvk = kv_layer(st, l, false), *kvv = kv_layer(st, l, true);
-        // ---- QKV, bias, RoPE, K/V append
-        norm((const float *)(mb + L.attn_norm));
+        // ---- QKV, bias, RoPE, K/V append (later layers' attention norm ran with the residual before)
+        if (l == 0) norm((const float *)(mb + L.attn_norm));
         {
             const int ld = L.qkv.n_tiles * 16;
             const int ks = wide_gemm(m, L.qkv, (const uint8_t *)(mb + L.qkv.off), nullptr, scales(L.qkv), nullptr, y, nullptr, 1, R, ld, ld,
@@ -1251,12 +1268,10 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         {
             const int ld = L.o.n_tiles * 16;
             const int ks = wide_gemm(m, L.o, (const uint8_t *)(mb + L.o.off), nullptr, scales(L.o), nullptr, y, nullptr, 1, R, ld, ld, true, s);
-            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E,
-                               ssq);
+            resid_norm(ld, ks, (const float *)(mb + L.ffn_norm));
             if (int rc = launched("wide O")) return rc;
         }
-        // ---- gate/up, SwiGLU, down + residual
-        norm((const float *)(mb + L.ffn_norm));
+        // ---- gate/up, SwiGLU, down + residual (and the next norm)
         {
             const int ld = L.gate.n_tiles * 16;
             float *yu = y + m->wy_cap / 2;  // (2 matrices x at most 2 splits of R x ld fit each half)
@@ -1283,14 +1298,18 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             const int ld = L.down.n_tiles * 16;
             const int ks = wide_gemm(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, scales(L.down), nullptr, y, nullptr, 1, R, ld, ld,
                                      true, s);
-            hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E,
-                               ssq);
+            if (l + 1 < c.n_layer)
+                resid_norm(ld, ks, (const float *)(mb + m->L[l + 1].attn_norm));
+            else if (outputs)
+                resid_norm(ld, ks, (const float *)(mb + m->out_norm));
+            else
+                hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E,
+                                   ssq);
             if (int rc = launched("wide down")) return rc;
         }
     }
-    // ---- final norm, LM head, argmax (only when an output is asked for)
-    if (logits || amax) {
-        norm((const float *)(mb + m->out_norm));
+    // ---- LM head, argmax (only when an output is asked for; its norm ran with the last residual)
+    if (outputs) {
         float *lg = logits ? logits : y;
         const int ld = logits ? m->V : m->out.n_tiles * 16;
         wide_gemm(m, m->out, (const uint8_t *)(mb + m->out.off), nullptr, scales(m->out), nullptr, lg, nullptr, 1, R, m->V, ld, false, s);

@@ -496,6 +496,70 @@ __global__ void __launch_bounds__(256) k_w_resid(float *__restrict__ x, const fl
     if (threadIdx.x == 0) ssq[r * kWideSsq + blockIdx.x] = sq;
 }
 
+// The residual add and the RMSNorm that follows it, in one pass over row r:
+// x[r] += y[r] (summed over the splits), then row r of A = round_act(
+// RMSNorm(x[r]) * gain), zero from E to wide_kp(E).  The sum of squares is
+// formed as k_w_resid and k_w_norm form it (per 1024-column block over its
+// 256 threads: within each wave, then the four waves in order; then the
+// blocks in order), so the result is bitwise that of the two kernels.  grid:
+// rows; 1024 threads: thread t takes columns 4*(t & 255) of blocks t >> 8 and
+// (t >> 8) + 4 (E <= 8192).
+template <int WT, int AT>
+__global__ void __launch_bounds__(1024) k_w_resid_norm(float *__restrict__ x, const float *__restrict__ y,
+                                                        long long split, int nsplit, int ldy, int E,
+                                                        const float *__restrict__ gain, float eps,
+                                                        uint16_t *__restrict__ a, long long a_plane, int lda) {
+    static_assert(kWideSsq == 8, "two blocks of 1024 columns per thread");
+    __shared__ float red[kWideSsq][4];
+    const int r = blockIdx.x, t = threadIdx.x;
+    const int q = t & 255, bw = t >> 8, wv = (t >> 6) & 3;
+    const int nb = (E + 1023) / 1024;
+    // every load first (E a multiple of 8: four columns are all in or all out)
+    f32x4 xo[2], yv[2], gv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = (bw + 4 * h) * 1024 + q * 4;
+        const int cc = c < E ? c : 0;
+        yv[h] = wide_sum4(y, split, nsplit, (long long)r * ldy + cc);
+        xo[h] = *reinterpret_cast<const f32x4 *>(x + (long long)r * E + cc);
+        gv[h] = *reinterpret_cast<const f32x4 *>(gain + cc);
+    }
+    f32x4 xn[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int b = bw + 4 * h, c = b * 1024 + q * 4;
+        float sq = 0.f;
+        if (c < E) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xn[h][e] = xo[h][e] + yv[h][e];
+                sq += xn[h][e] * xn[h][e];
+            }
+            *reinterpret_cast<f32x4 *>(x + (long long)r * E + c) = xn[h];
+        }
+        sq = wave_sum(sq);
+        if ((t & 63) == 0) red[b][wv] = sq;
+    }
+    lds_barrier();
+    float ss = 0.f;
+    for (int b = 0; b < nb; ++b) {
+        float sb = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sb += red[b][w];
+        ss += sb;
+    }
+    const float ri = 1.0f / sqrtf(ss / (float)E + eps);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = (bw + 4 * h) * 1024 + q * 4;
+        if (c >= wide_kp(WT, E)) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = c < E ? (xn[h][e] * ri) * gv[h][e] : 0.f;
+        wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, v);
+    }
+}
+
 struct WQkvArgs {
     const float *y;     // split outputs [r][ldy], rows in packed order (q, k, v)
     long long split;
