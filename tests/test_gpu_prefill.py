@@ -185,6 +185,21 @@ def test_wide_llama3_shape():
     log("  wide, Llama-3-8B shape, 40 tokens from 100: worst rel L2 %.2e, near %d" % (worst, near))
 
 
+def test_wide_tiled_attention_window():
+    """A bf16 cache on the matrix cores with four query heads per KV head: the
+    256-row chunk's attention runs four rows per work-group, each of its 16
+    columns with its own 40-key window (windows that start mid-tile, pages
+    that end mid-tile, 16-key groups that hold none of a column's keys), after
+    a cache written up to 120; the 44-row tail runs one row per work-group."""
+    wl = ragged("wide-tiled-window", n_head=8, n_kv_head=2, w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                act_dtype=synth.F32, sliding_window=40, seed=95)
+    p = Pair(wl, max_batch=1, prefill_chunk=256)
+    prompt = list(synth.uniform_int(wl.seed, 106, 300, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 120, prompt, 2)
+    log("  wide, 4 rows per attention work-group, window 40, 300 tokens from 120: worst rel L2 %.2e, near %d"
+        % (worst, near))
+
+
 def test_wide_one_row_then_full_chunk():
     """Chunks of 256 rows: a 1-row prefill (one row tile, clamped loads), then
     300 tokens (a full 256-row chunk over two row groups, then 44 rows)."""

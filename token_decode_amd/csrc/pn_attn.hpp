@@ -32,6 +32,10 @@ struct AttnArgs {
     // starts part_row floats after row b - 1's
     int rows, p0, window, ns_rows;
     long long part_row;
+    // rows mode, bf16 cache on the matrix cores: tile > 1 puts `tile` (= 16 / G)
+    // consecutive rows in one work-group, their heads in the 16 columns, so
+    // the rows share every K and V load (one split; no merge)
+    int tile;
 };
 
 // One slot's (or prefill row's) attention geometry.
@@ -543,32 +547,51 @@ __device__ __forceinline__ float sum_stride4(float v) {
 // query's loads go out before the first K/V loads, its pieces sit in LDS; K
 // and V rotate through three register buffers, so two chunks are in flight
 // while one is scored.
-template <int D, int G>
+//
+// TR > 1 (prefill rows, TR = 16 / G): the work-group takes TR consecutive rows
+// of the chunk, column c = G*r + g holding head g of row r (pieces in three
+// steps), so the rows share each K and V load.  Every column keeps its own
+// key range [lo, pos] of its row; the pages cover the first row's window
+// start to the last row's position, in one split, and V is zeroed only past
+// that range (inside it every key holds data, masked per column by its zero
+// weight).  A column that meets a 16-key group with none of its keys before it
+// has had any keeps max -inf and sum 0.
+template <int D, int G, int TR = 1>
 __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
-    static_assert(G <= 16, "one 16-column tile of query heads");
-    constexpr bool PC = G <= 4;  // pieces in the columns
+    static_assert(G <= 16 && TR * G <= 16, "one 16-column tile of query heads");
+    constexpr bool PC = G <= 4 && TR == 1;  // pieces in the columns
     constexpr int NP = PC ? 1 : 3;  // steps per 32 dims and per 16 keys
+    constexpr int NC = TR * G;      // columns holding a (row, head)
     constexpr int NWV = kAttnWaves;
     constexpr int KS = D / 32;  // 16x16x32 steps over d
     constexpr int DT = D / 16;  // 16-row output tiles over d
     constexpr int QU = (KS + NWV - 1) / NWV;  // query steps per wave
     const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const AttnRow R = attn_row(a, b);
-    if (s >= R.nsplit) return;
+    // tiled: rows b0 .. b0 + nr - 1 (R: the first row's window start and pages)
+    const int b0 = TR > 1 ? b * TR : b;
+    const int nr = TR > 1 ? min(TR, a.rows - b0) : 1;
+    const AttnRow R = attn_row(a, b0);
+    const int posl = TR > 1 ? a.p0 + b0 + nr - 1 : R.pos;  // the last key of the work-group
+    const int ns_b = TR > 1 ? 1 : R.nsplit;
+    if (s >= ns_b) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
-    // the lane's column: piece pc of head gc (PC), or head r16
-    const int pc = PC ? r16 >> 2 : 0, gc = PC ? r16 & 3 : r16;
-    const bool hc = gc < G && pc < 3;  // the column holds a head (and a piece)
+    // the lane's column: piece pc of head gc (PC), head r16, or (TR > 1) head gc of row cr
+    const int cr = TR > 1 ? r16 / G : 0;
+    const int pc = PC ? r16 >> 2 : 0, gc = PC ? r16 & 3 : (TR > 1 ? r16 % G : r16);
+    const bool hc = gc < G && pc < 3 && cr < nr;  // the column holds a head (and a piece)
     const int lo = R.lo;
-    const int np = R.np, ns_b = R.nsplit;
+    const int np = TR > 1 ? (posl + 1 - R.origin + kPage - 1) / kPage : R.np;
     const int kb = R.origin + (int)((long long)s * np / ns_b) * kPage;
-    const int ke = min(R.origin + (int)((long long)(s + 1) * np / ns_b) * kPage, R.pos + 1);
+    const int ke = min(R.origin + (int)((long long)(s + 1) * np / ns_b) * kPage, posl + 1);
+    // the column's own key range (columns past the rows take the last row's)
+    const int cpos = TR > 1 ? a.p0 + b0 + min(cr, nr - 1) : R.pos;
+    const int clo = TR > 1 ? (a.window > 0 ? max(0, cpos - a.window + 1) : 0) : lo;
 
     __shared__ __align__(16) u32x4 qsh[NP][KS][64];  // B operands of the query pieces, by lane
     __shared__ float wm[NWV][16], wl[NWV][16];
-    __shared__ float wacc[NWV][G][D];
+    __shared__ float wacc[NWV][NC][D];
 
     // the split's pages, one chunk (= page) per lane, looked up once
     const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
@@ -612,7 +635,8 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
         const int ks = min(w + u * NWV, KS - 1);
-        const float *qp = a.q + (long long)b * a.Hq * D + (long long)(j * G + min(gc, G - 1)) * D + ks * 32 + 8 * q4;
+        const int qrow = TR > 1 ? b0 + min(cr, nr - 1) : b;
+        const float *qp = a.q + (long long)qrow * a.Hq * D + (long long)(j * G + min(gc, G - 1)) * D + ks * 32 + 8 * q4;
         const f32x4 x0 = *reinterpret_cast<const f32x4 *>(qp);
         const f32x4 x1 = *reinterpret_cast<const f32x4 *>(qp + 4);
 #pragma unroll
@@ -659,24 +683,26 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
                                                              0);
         const int key0 = k0 + 4 * q4;
         float sv[4];
-        bool vin[4];
+        bool vin[4], cin[4];  // in the work-group's range (V holds data); in the column's
         float cm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             vin[i] = key0 + i >= lo && key0 + i < ke;
+            cin[i] = TR > 1 ? key0 + i >= clo && key0 + i <= cpos : vin[i];
             const float full = PC ? sum_stride4(sc[i]) : sc[i];  // the head's score
-            sv[i] = vin[i] ? full : -INFINITY;
+            sv[i] = cin[i] ? full : -INFINITY;
             cm = fmaxf(cm, sv[i]);
         }
         cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
         const float mn = cm > m + 8.f ? cm : m;
-        const float f = exp2_fast(m - mn);  // 1 where the max stays, 0 on the wave's first chunk
+        // 1 where the max stays, 0 on the wave's first chunk (tiled: 1 while a column has no keys)
+        const float f = (TR > 1 && mn == -INFINITY) ? 1.f : exp2_fast(m - mn);
         const bool rescale = __builtin_amdgcn_ballot_w64(mn != m && m != -INFINITY) != 0;
         float pv[4], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pv[i] = vin[i] ? exp2_fast(sv[i] - mn) : 0.f;
+            pv[i] = cin[i] ? exp2_fast(sv[i] - mn) : 0.f;
             ps += pv[i];
         }
         l = l * f + ps;
@@ -740,16 +766,17 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
         wm[w][r16] = m;
         wl[w][r16] = l;
     }
-    if (r16 < G)
+    if (r16 < NC)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) wacc[w][r16][dt * 16 + 4 * q4 + i] = acc[dt][i];
     lds_barrier();
 
-    const int ns = R.nsplit;
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int g = idx / D, d = idx % D;
+    const int ns = ns_b;
+    for (int idx = tid; idx < NC * D; idx += 256) {
+        const int g = idx / D, d = idx % D;  // (tiled: column g = G * row + head)
+        if (TR > 1 && g / G >= nr) continue;
         float M = wm[0][g];
 #pragma unroll
         for (int x = 1; x < NWV; ++x) M = fmaxf(M, wm[x][g]);
@@ -760,7 +787,9 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
             L += wl[x][g] * f;
             A += wacc[x][g][d] * f;
         }
-        if (ns == 1) {
+        if (TR > 1) {
+            a.o[(long long)(b0 + g / G) * a.Hq * D + (long long)(j * G + g % G) * D + d] = A / L;
+        } else if (ns == 1) {
             a.o[(long long)b * a.Hq * D + (long long)(j * G + g) * D + d] = A / L;
         } else {
             float *pp = R.part + (((long long)j * R.s_cap + s) * G + g) * (D + 4);

@@ -1254,7 +1254,19 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             aa.s_cap[0] = kWideAttnSplits;
             aa.part_row = (long long)m->Hk * kWideAttnSplits * m->G * (m->D + 4);
             aa.kind = m->attn_kind == 1 ? 0 : 1;
-            launch_attn(m->D, m->kvt, m->G, aa, dim3(aa.ns_rows, m->Hk, R), aa.ns_rows > 1, s);
+            // a bf16 cache on the matrix cores takes 16 / G rows per work-group (sharing their K/V
+            // loads, one split) when that still gives 64 work-groups; else a row each, with splits
+            const int G = m->G, tr = 16 / std::max(G, 1);
+            const bool tiled = m->kvt == PN_BF16 && aa.kind == 1 && tr > 1 &&
+                               (G == 1 || G == 2 || G == 3 || G == 4 || G == 6 || G == 8) &&
+                               (long long)cdiv(R, tr) * m->Hk >= 64;
+            if (tiled) {
+                aa.tile = tr;
+                aa.ns_rows = 1;
+                launch_attn(m->D, m->kvt, G, aa, dim3(1, m->Hk, cdiv(R, tr)), false, s);
+            } else {
+                launch_attn(m->D, m->kvt, G, aa, dim3(aa.ns_rows, m->Hk, R), aa.ns_rows > 1, s);
+            }
             if (int rc = launched("wide attention")) return rc;
         }
         // ---- O + residual
