@@ -296,6 +296,30 @@ def test_wide_q8_0_llama3_shape():
     log("  wide, Llama-3-8B Q8_0, 40 tokens from 30: worst rel L2 %.2e, near %d" % (worst, near))
 
 
+def test_wide_q4_0_weights():
+    """Q4_0 weights (4-bit codes in 128-wide tiles, four 32-weight blocks each:
+    every block's matrix-core step from zero, scaled and added in fp32) with
+    bf16 activations, chunks of 64 over 150 tokens from a cache written up to
+    40; n_embd 224 and n_ff 320 leave the last 128-wide k tile partly past K."""
+    wl = ragged("wide-q4_0", w_dtype=synth.Q4_0, kv_dtype=synth.BF16, act_dtype=synth.BF16, n_embd=224,
+                n_ff=320, seed=96)
+    p = Pair(wl, max_batch=1, prefill_chunk=64)
+    prompt = list(synth.uniform_int(wl.seed, 107, 150, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 40, prompt, 2)
+    log("  wide, Q4_0 weights, 150 tokens from 40: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+def test_wide_q4_0_llama3_shape():
+    """Llama-3-8B layer shape with Q4_0 weights (2 layers, full vocabulary): a
+    256-row chunk (14-tile groups for gate/up, the tiled attention) and a
+    44-row tail after a 30-token cache."""
+    wl = synth.WORKLOADS["llama3-8b-q4_0"]().with_(name="wide-llama3-q4_0-2l", n_layer=2, seed=97)
+    p = Pair(wl, max_batch=1, prefill_chunk=256)
+    prompt = list(synth.uniform_int(wl.seed, 108, 300, 0, wl.n_vocab - 1))
+    worst, near = run_prefill(p, 30, prompt, 1)
+    log("  wide, Llama-3-8B Q4_0, 300 tokens from 30: worst rel L2 %.2e, near %d" % (worst, near))
+
+
 def test_wide_mistral_shape_full_chunk():
     """Mistral-7B layer shape (2 layers, bf16 activations, window 4096): a full
     256-row chunk, then 44 rows.  At 256 rows the planner runs QKV (ragged

@@ -293,10 +293,9 @@ int check_config_n(const pn_config *c) {
         return fail(PN_EINVAL, "prefill_chunk must be in [0, %d]", kWideRows);
     if (c->prefill_chunk > 0 && c->n_embd > 1024 * kWideSsq)
         return fail(PN_EUNSUPPORTED, "the wide prefill path takes n_embd up to %d", 1024 * kWideSsq);
-    if (c->prefill_chunk > 0 && ((c->w_dtype != PN_BF16 && c->w_dtype != PN_I8 && c->w_dtype != PN_Q8_0) ||
-                                 c->n_expert > 0 || c->kv_dtype == PN_Q4_0))
+    if (c->prefill_chunk > 0 && (c->w_dtype == PN_F32 || c->n_expert > 0 || c->kv_dtype == PN_Q4_0))
         return fail(PN_EUNSUPPORTED,
-                    "the wide prefill path needs bf16, int8 or Q8_0 weights, no experts and an fp32 or bf16 cache");
+                    "the wide prefill path needs bf16, int8, Q8_0 or Q4_0 weights, no experts and an fp32 or bf16 cache");
     const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
@@ -1051,8 +1050,9 @@ struct WidePlan {
 };
 WidePlan wide_plan(int v, int R, int n_tiles, int KT, int nz, long long per, bool split_ok, long long cap) {
     // us per k step of a 16- and an 8-tile group: bf16 rows, fp32 rows as three
-    // bf16 pieces, int8, Q8_0 (the variants of wide_variant)
-    static const double step_us[4][2] = {{0.75, 0.43}, {1.185, 0.865}, {1.30, 0.73}, {1.74, 1.03}};
+    // bf16 pieces, int8, Q8_0, Q4_0 (the variants of wide_variant; a Q4_0 step is
+    // 128 wide)
+    static const double step_us[5][2] = {{0.75, 0.43}, {1.185, 0.865}, {1.30, 0.73}, {1.74, 1.03}, {3.6, 2.1}};
     WidePlan best{8, 1};
     double best_t = -1.0;
     for (int w : {8, 14, 16}) {
@@ -1077,7 +1077,7 @@ WidePlan wide_plan(int v, int R, int n_tiles, int KT, int nz, long long per, boo
 // weights with bf16 rows, 1 = bf16 weights with fp32 rows (three pieces), 2 =
 // int8 weights, 3 = Q8_0 weights (both with f16 rows).
 int wide_variant(const pn_model *m) {
-    return m->wt == PN_Q8_0 ? 3 : (m->wt == PN_I8 ? 2 : (m->pieces == 3 ? 1 : 0));
+    return m->wt == PN_Q4_0 ? 4 : (m->wt == PN_Q8_0 ? 3 : (m->wt == PN_I8 ? 2 : (m->pieces == 3 ? 1 : 0)));
 }
 // fn(WT, P, WGW) (as integral constants) for variant v with work-groups of wgw
 // weight tiles (8, 14 or 16).
@@ -1090,6 +1090,7 @@ auto with_wide(int v, int wgw, Fn fn) {
     };
     using I = std::integral_constant<int, 1>;
     switch (v) {
+        case 4: return go(std::integral_constant<int, WT_Q4>{}, I{});
         case 3: return go(std::integral_constant<int, WT_Q8>{}, I{});
         case 2: return go(std::integral_constant<int, WT_I8>{}, I{});
         case 1: return go(std::integral_constant<int, WT_BF16>{}, std::integral_constant<int, 3>{});
@@ -1147,7 +1148,7 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
 int wide_lds_attr() {
     static bool done = false;
     if (done) return PN_OK;
-    for (int v = 0; v < 4; ++v)
+    for (int v = 0; v < 5; ++v)
         for (int wgw : {8, 14, 16}) {
             const hipError_t e = hipFuncSetAttribute(wide_kernel(v, wgw), hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      wide_lds(v, wgw));
@@ -1164,50 +1165,43 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
     const pn_config &c = m->cfg;
     char *mb = m->base;
     const int E = m->E, HD = m->H * m->D, F = m->F, p0 = st->pos;
-    const bool bf = m->at == PN_BF16;
     float *x = (float *)(mb + m->wx), *y = (float *)(mb + m->wy);
     float *q = (float *)(mb + m->wq), *o = (float *)(mb + m->wo);
     uint16_t *a = (uint16_t *)(mb + m->wa);
     int *err = (int *)(st->base + st->err);
     const float eps = c.rms_norm_eps;
     const int var = wide_variant(m);
-    const bool i8 = var == 2, q8 = var == 3;
+    const bool bq = var >= 2;  // f16 rows with per-row (int8) or per-block scales
     float *ssq = (float *)(mb + m->wss);
+    // fn(WT, AT) as integral constants: the row kernels' A layout for this model
+    auto rows_as = [&](auto fn) {
+        using B = std::integral_constant<int, AT_BF16>;
+        switch (var) {
+            case 4: fn(std::integral_constant<int, WT_Q4>{}, B{}); break;
+            case 3: fn(std::integral_constant<int, WT_Q8>{}, B{}); break;
+            case 2: fn(std::integral_constant<int, WT_I8>{}, B{}); break;
+            case 1: fn(std::integral_constant<int, WT_BF16>{}, std::integral_constant<int, AT_F32>{}); break;
+            default: fn(std::integral_constant<int, WT_BF16>{}, B{}); break;
+        }
+    };
     // the row kernels write the columns a product over K reads (K rounded up to weight tiles)
-    auto cols = [&](int K) { return (unsigned)cdiv(wide_kp((i8 || q8) ? WT_I8 : WT_BF16, K), 1024); };
+    const int wtk = var == 4 ? WT_Q4 : (bq ? WT_I8 : WT_BF16);
+    auto cols = [&](int K) { return (unsigned)cdiv(wide_kp(wtk, K), 1024); };
     auto norm = [&](const float *gain) {
-        const dim3 gn(cols(E), R);
-        if (q8)
-            hipLaunchKernelGGL((k_w_norm<WT_Q8, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
-                               m->wlda);
-        else if (i8)
-            hipLaunchKernelGGL((k_w_norm<WT_I8, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
-                               m->wlda);
-        else if (bf)
-            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_BF16>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
-                               m->wlda);
-        else
-            hipLaunchKernelGGL((k_w_norm<WT_BF16, AT_F32>), gn, dim3(256), 0, s, x, E, gain, eps, ssq, a, m->wa_plane,
-                               m->wlda);
+        rows_as([&](auto wt, auto at) {
+            hipLaunchKernelGGL((k_w_norm<decltype(wt)::value, decltype(at)::value>), dim3(cols(E), R), dim3(256), 0, s, x,
+                               E, gain, eps, ssq, a, m->wa_plane, m->wlda);
+        });
     };
     // x += the split outputs y (ld columns, ks splits), then the next norm's A planes from the new x
     auto resid_norm = [&](int ld, int ks, const float *gain) {
-        const long long sp = (long long)R * ld;
-        if (q8)
-            hipLaunchKernelGGL((k_w_resid_norm<WT_Q8, AT_BF16>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps, a,
-                               m->wa_plane, m->wlda);
-        else if (i8)
-            hipLaunchKernelGGL((k_w_resid_norm<WT_I8, AT_BF16>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps, a,
-                               m->wa_plane, m->wlda);
-        else if (bf)
-            hipLaunchKernelGGL((k_w_resid_norm<WT_BF16, AT_BF16>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps,
-                               a, m->wa_plane, m->wlda);
-        else
-            hipLaunchKernelGGL((k_w_resid_norm<WT_BF16, AT_F32>), dim3(R), dim3(1024), 0, s, x, y, sp, ks, ld, E, gain, eps,
-                               a, m->wa_plane, m->wlda);
+        rows_as([&](auto wt, auto at) {
+            hipLaunchKernelGGL((k_w_resid_norm<decltype(wt)::value, decltype(at)::value>), dim3(R), dim3(1024), 0, s, x, y,
+                               (long long)R * ld, ks, ld, E, gain, eps, a, m->wa_plane, m->wlda);
+        });
     };
     const bool outputs = logits || amax;
-    auto scales = [&](const Mat &mt) { return (i8 || q8) ? (const float *)(mb + mt.soff) : nullptr; };
+    auto scales = [&](const Mat &mt) { return bq ? (const float *)(mb + mt.soff) : nullptr; };
     if (int rc = wide_lds_attr()) return rc;
     hipLaunchKernelGGL(k_w_embed, dim3(cdiv(E, 1024), R), dim3(256), 0, s, (const uint16_t *)(mb + m->embd), tok, x, E,
                        m->V, err, ssq);
@@ -1271,11 +1265,10 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         }
         // ---- O + residual
         {
-            const dim3 gc(cols(HD), R);
-            if (q8) hipLaunchKernelGGL((k_w_conv<WT_Q8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
-            else if (i8) hipLaunchKernelGGL((k_w_conv<WT_I8, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
-            else if (bf) hipLaunchKernelGGL((k_w_conv<WT_BF16, AT_BF16>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
-            else hipLaunchKernelGGL((k_w_conv<WT_BF16, AT_F32>), gc, dim3(256), 0, s, o, HD, a, m->wa_plane, m->wlda);
+            rows_as([&](auto wt, auto at) {
+                hipLaunchKernelGGL((k_w_conv<decltype(wt)::value, decltype(at)::value>), dim3(cols(HD), R), dim3(256), 0, s,
+                                   o, HD, a, m->wa_plane, m->wlda);
+            });
         }
         {
             const int ld = L.o.n_tiles * 16;
@@ -1290,20 +1283,11 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             const bool fits = 2LL * 2 * R * ld <= m->wy_cap;
             const int ks = wide_gemm(m, L.gate, (const uint8_t *)(mb + L.gate.off), (const uint8_t *)(mb + L.up.off),
                                      scales(L.gate), scales(L.up), y, yu, 2, R, ld, ld, fits, s);
-            const dim3 gs(cols(F), R);
             const long long sp = (long long)R * ld;
-            if (q8)
-                hipLaunchKernelGGL((k_w_swiglu<WT_Q8, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a, m->wa_plane,
-                                   m->wlda);
-            else if (i8)
-                hipLaunchKernelGGL((k_w_swiglu<WT_I8, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a, m->wa_plane,
-                                   m->wlda);
-            else if (bf)
-                hipLaunchKernelGGL((k_w_swiglu<WT_BF16, AT_BF16>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a,
-                                   m->wa_plane, m->wlda);
-            else
-                hipLaunchKernelGGL((k_w_swiglu<WT_BF16, AT_F32>), gs, dim3(256), 0, s, y, yu, sp, ks, ld, F, a,
-                                   m->wa_plane, m->wlda);
+            rows_as([&](auto wt, auto at) {
+                hipLaunchKernelGGL((k_w_swiglu<decltype(wt)::value, decltype(at)::value>), dim3(cols(F), R), dim3(256), 0, s,
+                                   y, yu, sp, ks, ld, F, a, m->wa_plane, m->wlda);
+            });
             if (int rc = launched("wide gate/up")) return rc;
         }
         {

@@ -59,12 +59,18 @@ struct WGemmArgs {
 };
 
 // Row fragments per row tile and k step: the P bf16 planes, or for int8 and
-// Q8_0 weights (64-wide tiles, f16 rows) the two 32-wide halves of the step.
-__host__ __device__ constexpr int wgemm_na(int WT, int P) { return (WT == WT_I8 || WT == WT_Q8) ? 2 : P; }
-// Q8_0: bytes of block scales per stage, after its fragments: each of the 8
-// waves loads 256 (a dword per lane), 4 weight tiles' 64-byte scale tiles;
-// the first WGW * 64 are the work-group's (waves past them load copies).
-__host__ __device__ constexpr int wgemm_scb(int WT) { return WT == WT_Q8 ? 2048 : 0; }
+// block-quantised weights (f16 rows) the 32-wide blocks of the step's tile:
+// two for int8 and Q8_0 (64-wide tiles), four for Q4_0 (128-wide).
+__host__ __device__ constexpr int wgemm_na(int WT, int P) {
+    return WT == WT_Q4 ? 4 : ((WT == WT_I8 || WT == WT_Q8) ? 2 : P);
+}
+// Block formats: bytes of one weight tile's scale tile per k step (16 rows x
+// the tile's blocks x fp16: 64 for Q8_0, 128 for Q4_0), and of block scales
+// per stage, after its fragments: each of the 8 waves loads 256 (a dword per
+// lane: 4 or 2 weight tiles' scale tiles); the first WGW tiles' are the
+// work-group's (waves past them load copies).
+__host__ __device__ constexpr int wgemm_sbt(int WT) { return blockq(WT) ? 32 * tile_blocks(WT) : 0; }
+__host__ __device__ constexpr int wgemm_scb(int WT) { return blockq(WT) ? 2048 : 0; }
 // Fragments (1 KiB each) of one k step of a work-group that owns WGW weight
 // tiles and 8 row tiles: the weight tiles, then every row tile's NA fragments.
 __host__ __device__ constexpr int wgemm_frags(int WT, int P, int WGW) { return WGW + 8 * wgemm_na(WT, P); }
@@ -73,14 +79,14 @@ __host__ __device__ constexpr int wgemm_frags(int WT, int P, int WGW) { return W
 // reads, so that every wave issues the same number and its waits count right).
 __host__ __device__ constexpr int wgemm_lpw(int WT, int P, int WGW) { return (wgemm_frags(WT, P, WGW) + 7) / 8; }
 // Bytes of one stage of the LDS ring, and the stages: as many k steps as fit
-// 128 KiB (Q8_0, whose stages also hold scales: 144 KiB), at most 8.
+// 128 KiB (Q8_0, whose stages also hold scales: 144 KiB; Q4_0, with four row
+// fragments per row tile: 160 KiB), at most 8.
 __host__ __device__ constexpr int wgemm_stage_bytes(int WT, int P, int WGW) {
     return 8 * wgemm_lpw(WT, P, WGW) * 1024 + wgemm_scb(WT);
 }
+__host__ __device__ constexpr int wgemm_budget(int WT) { return (WT == WT_Q4 ? 160 : (WT == WT_Q8 ? 144 : 128)) * 1024; }
 __host__ __device__ constexpr int wgemm_stages(int WT, int P, int WGW) {
-    return (WT == WT_Q8 ? 144 : 128) * 1024 / wgemm_stage_bytes(WT, P, WGW) < 8
-               ? (WT == WT_Q8 ? 144 : 128) * 1024 / wgemm_stage_bytes(WT, P, WGW)
-               : 8;
+    return wgemm_budget(WT) / wgemm_stage_bytes(WT, P, WGW) < 8 ? wgemm_budget(WT) / wgemm_stage_bytes(WT, P, WGW) : 8;
 }
 __host__ __device__ constexpr int wgemm_lds(int WT, int P, int WGW) {
     return wgemm_stages(WT, P, WGW) * wgemm_stage_bytes(WT, P, WGW);
@@ -120,11 +126,13 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     constexpr int NA = wgemm_na(WT, P), TK = tile_k(WT);
     constexpr int S = wgemm_stages(WT, P, WGW), FR = wgemm_frags(WT, P, WGW), LPW = wgemm_lpw(WT, P, WGW);
     constexpr int WWT = WGW / 2;  // weight tiles per wave
-    constexpr bool BQ = WT == WT_Q8;
+    constexpr bool BQ = blockq(WT);
+    constexpr int NB = BQ ? tile_blocks(WT) : 1;  // blocks per tile (block formats)
+    constexpr int SBT = wgemm_sbt(WT);            // bytes of a tile's scales per k step
     constexpr int SB = wgemm_stage_bytes(WT, P, WGW);
     constexpr int LPS = LPW + (BQ ? 1 : 0);  // loads per wave per k step
     static_assert(WGW % 2 == 0 && S >= 3, "two waves share a row tile's weight tiles; three stages at least");
-    static_assert(!BQ || WGW * 64 <= wgemm_scb(WT), "the scale area holds the work-group's scale tiles");
+    static_assert(!BQ || WGW * SBT <= wgemm_scb(WT), "the scale area holds the work-group's scale tiles");
     // [S][SB]: W tiles 0..WGW-1, then A [row tile][plane] (1 KiB each), then (Q8_0) the scales
     extern __shared__ __align__(16) uint8_t ring[];
     const int lane = threadIdx.x & 63;
@@ -147,28 +155,31 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
             src[q] = g.w[z] + (long long)min(gyi * WGW + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
             stride[q] = 1024;
         } else {
-            // bf16: plane p, k 8*(l >> 4) of the step; int8, Q8_0: half p, positions 16*(l >> 4) + 8p
+            // bf16: plane p, k 8*(l >> 4) of the step; int8, Q8_0, Q4_0: block p, positions
+            // (TK / 4)*(l >> 4) + 8p (the blk_pos order of the tile)
             const int rt = (f - WGW) / NA, p = (f - WGW) % NA;
             const int r = min((gxi * 8 + rt) * 16 + (lane & 15), g.R - 1);
-            const long long e = (WT == WT_I8 || BQ) ? (long long)r * g.lda + 16 * (lane >> 4) + 8 * p
+            const long long e = (WT == WT_I8 || BQ) ? (long long)r * g.lda + (TK / 4) * (lane >> 4) + 8 * p
                                                     : p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4);
             src[q] = reinterpret_cast<const uint8_t *>(g.a + e);
             stride[q] = TK * 2;
         }
     }
-    // Q8_0: this lane's dword of the stage's scales: byte 256*wv + 4*lane is
-    // row (lane & 15) of local weight tile (4*wv + lane / 16) mod WGW (clamped to the matrix)
+    // Block formats: this lane's dword of the stage's scales: byte 256*wv + 4*lane
+    // is dword lane % (SBT / 4) of local weight tile ((256 / SBT)*wv + lane / (SBT / 4))
+    // mod WGW (clamped to the matrix); the tile's row r holds bytes 2*NB*r .. +2*NB-1
     const uint8_t *ssrc = nullptr;
     if constexpr (BQ) {
-        const int t = min(gyi * WGW + (4 * wv + lane / 16) % WGW, g.n_tiles - 1);
-        ssrc = reinterpret_cast<const uint8_t *>(g.sc[z]) + (long long)t * g.KT * 64 + (lane & 15) * 4;
+        constexpr int DPT = SBT / 4;  // dwords of one tile's scales
+        const int t = min(gyi * WGW + ((256 / SBT) * wv + lane / DPT) % WGW, g.n_tiles - 1);
+        ssrc = reinterpret_cast<const uint8_t *>(g.sc[z]) + (long long)t * g.KT * SBT + (lane % DPT) * 4;
     }
     auto issue = [&](int kt, int slot) {  // every call issues LPS loads (k steps past the split re-read the last)
         kt = min(kt, kt1 - 1);
 #pragma unroll
         for (int q = 0; q < LPW; ++q)
             lds_dma16(src[q] + (long long)kt * stride[q], (lds_void *)(ring + slot * SB + (wv * LPW + q) * 1024));
-        if constexpr (BQ) lds_dma4(ssrc + (long long)kt * 64, (lds_void *)(ring + slot * SB + 8 * LPW * 1024 + wv * 256));
+        if constexpr (BQ) lds_dma4(ssrc + (long long)kt * SBT, (lds_void *)(ring + slot * SB + 8 * LPW * 1024 + wv * 256));
     };
     f32x4 acc[WWT][2];
 #pragma unroll
@@ -197,32 +208,64 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
         // the slot of step kt - 1: every wave has read it (it passed the barrier)
         issue(kt + S - 1, (kt - kt0 + S - 1) % S);
         if constexpr (BQ) {
-            // the codes widened as for int8; per block h a matrix-core step from
-            // zero with the rows as the A operand (so the lane holds weight row
-            // l & 15, whose block scales it reads), scaled and added in fp32
-            const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+            // the codes widened to f16 (Q8_0 as for int8; Q4_0: the nibbles masked to a
+            // byte each, paired into f16 1024 + c, minus 1032); per block h a
+            // matrix-core step from zero with the rows as the A operand (so the lane
+            // holds weight row l & 15, whose block scales it reads), scaled and added
+            // in fp32 in block order
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t *sbase = ring + slot * SB + 8 * LPW * 1024 + (lane & 15) * 4;
+            const uint8_t *sbase = ring + slot * SB + 8 * LPW * 1024 + (lane & 15) * (2 * NB);
 #pragma unroll
             for (int i = 0; i < WWT; ++i) {
-                const uint32_t sw = *reinterpret_cast<const uint32_t *>(sbase + (WWT * (wv & 1) + i) * 64);
-                const float d0 = half_lo(sw), d1 = half_hi(sw);
-                u32x4 b[2];
+                const uint8_t *sp = sbase + (WWT * (wv & 1) + i) * SBT;
+                float d[NB];
+                u32x4 b[NB];
+                if constexpr (WT == WT_Q4) {
+                    const u32x2 sw = *reinterpret_cast<const u32x2 *>(sp);
+                    const uint32_t w0 = sw[0], w1 = sw[1];
+                    d[0] = half_lo(w0);
+                    d[1] = half_hi(w0);
+                    d[2] = half_lo(w1);
+                    d[3] = half_hi(w1);
+                    const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04010400u);
-                    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04030402u);
-                    b[c >> 1][2 * (c & 1)] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
-                    b[c >> 1][2 * (c & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
+                    for (int h = 0; h < 4; ++h) {
+                        const uint32_t lo = wf[i][h] & 0x0F0F0F0Fu, hi = (wf[i][h] >> 4) & 0x0F0F0F0Fu;
+                        const uint32_t pq[4] = {__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u),
+                                                __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u),
+                                                __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u),
+                                                __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            b[h][c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pq[c]) - off);
+                    }
+                } else {
+                    const uint32_t sw = *reinterpret_cast<const uint32_t *>(sp);
+                    d[0] = half_lo(sw);
+                    d[1] = half_hi(sw);
+                    const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04010400u);
+                        const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, wf[i][c], 0x04030402u);
+                        b[c >> 1][2 * (c & 1)] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - off);
+                        b[c >> 1][2 * (c & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - off);
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[j][0]),
-                                                                            __builtin_bit_cast(f16x8, b[0]), zero, 0, 0, 0);
-                    const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[j][1]),
-                                                                            __builtin_bit_cast(f16x8, b[1]), zero, 0, 0, 0);
+                    f32x4 t[NB];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(d1, t1[e], fmaf(d0, t0[e], acc[i][j][e]));
+                    for (int h = 0; h < NB; ++h)
+                        t[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af[j][h]),
+                                                                      __builtin_bit_cast(f16x8, b[h]), zero, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float v = acc[i][j][e];
+#pragma unroll
+                        for (int h = 0; h < NB; ++h) v = fmaf(d[h], t[h][e], v);
+                        acc[i][j][e] = v;
+                    }
                 }
             }
         } else if constexpr (WT == WT_I8) {
