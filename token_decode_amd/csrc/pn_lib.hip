@@ -1052,7 +1052,7 @@ WidePlan wide_plan(int v, int R, int n_tiles, int KT, int nz, long long per, boo
     // us per k step of a 16- and an 8-tile group: bf16 rows, fp32 rows as three
     // bf16 pieces, int8, Q8_0, Q4_0 (the variants of wide_variant; a Q4_0 step is
     // 128 wide)
-    static const double step_us[5][2] = {{0.75, 0.43}, {1.185, 0.865}, {1.30, 0.73}, {1.74, 1.03}, {3.6, 2.1}};
+    static const double step_us[5][2] = {{0.75, 0.43}, {1.185, 0.865}, {1.30, 0.73}, {1.74, 1.03}, {3.96, 2.04}};
     WidePlan best{8, 1};
     double best_t = -1.0;
     for (int w : {8, 14, 16}) {
