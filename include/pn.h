@@ -104,7 +104,7 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3, PN_Q4_0 = 4 } pn
  *            (chunks of max_batch through the decode kernels).  The wide path
  *            takes each chunk through every projection as one matrix product
  *            on the matrix cores, so a weight is read once per chunk; it needs
- *            w_dtype PN_BF16, PN_I8 or PN_Q8_0, no experts and kv_dtype PN_F32 or PN_BF16
+ *            w_dtype PN_BF16, PN_I8, PN_Q8_0 or PN_Q4_0, no experts and kv_dtype PN_F32 or PN_BF16
  *            (PN_EUNSUPPORTED otherwise), and adds its row buffers to
  *            pn_model_bytes. */
 typedef struct pn_config {
