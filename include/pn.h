@@ -375,11 +375,19 @@ enum {
  *  PN_OPT_ATTN_KERNEL          attention over a bf16 cache: 0 = automatic,
  *                              1 = vector units, 2 = matrix cores (an fp32
  *                              cache always uses the vector units);
+ *  PN_OPT_ATTN_COMBINE         0 = automatic: a batch-1 decode step over a
+ *                              bf16 cache on the matrix cores with at most 4
+ *                              query heads per KV head and a window of at most
+ *                              48 pages of 64 keys takes at most 8 attention
+ *                              splits per head and combines them in the O
+ *                              projection's prologue; 1 = always the separate
+ *                              split-merge launch;
  *  PN_OPT_WAVES_*              waves per work-group (4, 8 or 16) of the QKV,
  *                              O, gate/up, down and LM-head projections. */
 enum {
     PN_OPT_ATTN_KEYS_PER_SPLIT = 1,
     PN_OPT_ATTN_KERNEL = 2,
+    PN_OPT_ATTN_COMBINE = 3,
     PN_OPT_WAVES_QKV = 10, PN_OPT_WAVES_O, PN_OPT_WAVES_GATEUP, PN_OPT_WAVES_DOWN, PN_OPT_WAVES_LMHEAD
 };
 int pn_model_set_option(pn_model *m, int32_t option, int64_t value);

@@ -110,6 +110,28 @@ def test_attention_split_sizes(kps):
         log("  kps %d kv %d: worst rel L2 %.2e near %d" % (kps, kv, worst, near))
 
 
+@pytest.mark.parametrize("start", [40, 200, 700, 2100])
+def test_split_combine_in_o_prologue(start):
+    """Batch 1 over a bf16 cache with at most 4 query heads per KV head takes
+    at most 8 attention splits (8-wave work-groups) and combines them in the O
+    projection's prologue: from one page (one split, whose output the prologue
+    reads as is) to 34 pages (8 splits of 4 or 5 pages), with head_dim 128 and
+    fp32 activations, head_dim 64 and bf16 activations; then with 64 keys per
+    split the 700- and 2100-key windows need more than 8 splits and go through
+    the merge launch instead.  Every step against the oracle."""
+    from token_decode_amd import _capi as C
+    for kps in (0, 64):
+        if kps and start < 700:
+            continue
+        for i, (H, Hk, d, act) in enumerate(((8, 2, 128, synth.F32), (6, 3, 64, synth.BF16))):
+            wl = ragged("combine-%d-%d-kps%d" % (start, d, kps), n_head=H, n_kv_head=Hk, head_dim=d,
+                        w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=act, seed=60 + i)
+            p = Pair(wl)
+            p.dm.set_option(C.PN_OPT_ATTN_KEYS_PER_SPLIT, kps)
+            worst, near, n = run_single(p, start, [5, 6], 2, max_ctx=start + 8)
+            log("  %s: worst rel L2 %.2e near %d" % (wl.name, worst, near))
+
+
 @pytest.mark.parametrize("kind", [1, 2], ids=["vector", "matrix"])
 @pytest.mark.parametrize("kps", [0, 64, 256])
 def test_attention_kernels_bf16_cache(kind, kps):

@@ -10,7 +10,10 @@ template <int G>
 void go(const AttnArgs &a, dim3 grid, bool merge, hipStream_t s) {
     // fp32 and Q4 caches go to the vector units; a bf16 one where a.kind says
     // (prefill rows in tiles of 16 / G when a.tile is set)
+    // (8-wave work-groups for decode with G <= 4, where a.waves asks for them)
     if (PN_KV == 1 && a.kind == 1 && a.tile > 1) hipLaunchKernelGGL((k_attn_mfma<PN_D, G, 16 / G>), grid, dim3(256), 0, s, a);
+    else if (PN_KV == 1 && a.kind == 1 && G <= 4 && a.waves == 8)
+        hipLaunchKernelGGL((k_attn_mfma<PN_D, G, 1, (G <= 4 ? 8 : kAttnWaves)>), grid, dim3(512), 0, s, a);
     else if (PN_KV == 1 && a.kind == 1) hipLaunchKernelGGL((k_attn_mfma<PN_D, G>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_attn<PN_D, PN_KV, G>), grid, dim3(256), 0, s, a);
     if (merge) hipLaunchKernelGGL((k_attn_merge<PN_D, G>), dim3(a.Hq, grid.z), dim3(256), 0, s, a);

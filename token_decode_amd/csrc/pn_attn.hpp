@@ -36,6 +36,9 @@ struct AttnArgs {
     // consecutive rows in one work-group, their heads in the 16 columns, so
     // the rows share every K and V load (one split; no merge)
     int tile;
+    // decode over a bf16 cache on the matrix cores: waves per work-group (4, or
+    // 8 for G <= 4: two pages per chunk)
+    int waves;
 };
 
 // One slot's (or prefill row's) attention geometry.
@@ -556,13 +559,20 @@ __device__ __forceinline__ float sum_stride4(float v) {
 // that range (inside it every key holds data, masked per column by its zero
 // weight).  A column that meets a 16-key group with none of its keys before it
 // has had any keeps max -inf and sum 0.
-template <int D, int G, int TR = 1>
-__global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
+//
+// NWV = 8 (decode, G <= 4): a work-group of 8 waves walks chunks of two
+// pages, wave w taking 16 keys of page w / 4: twice the keys in flight per
+// work-group, for few, long splits (the split combine then runs in the O
+// projection's prologue).
+template <int D, int G, int TR = 1, int NWV = kAttnWaves>
+__global__ void __launch_bounds__(NWV * 64) k_attn_mfma(AttnArgs a) {
     static_assert(G <= 16 && TR * G <= 16, "one 16-column tile of query heads");
+    static_assert(NWV % 4 == 0 && (NWV == kAttnWaves || TR == 1), "whole pages per chunk; tiled rows use 4 waves");
     constexpr bool PC = G <= 4 && TR == 1;  // pieces in the columns
     constexpr int NP = PC ? 1 : 3;  // steps per 32 dims and per 16 keys
     constexpr int NC = TR * G;      // columns holding a (row, head)
-    constexpr int NWV = kAttnWaves;
+    constexpr int CHK = NWV * 16;   // keys per chunk (one 16-key group per wave)
+    constexpr int PPC = NWV / 4;    // pages per chunk
     constexpr int KS = D / 32;  // 16x16x32 steps over d
     constexpr int DT = D / 16;  // 16-row output tiles over d
     constexpr int QU = (KS + NWV - 1) / NWV;  // query steps per wave
@@ -593,15 +603,17 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     __shared__ float wm[NWV][16], wl[NWV][16];
     __shared__ float wacc[NWV][NC][D];
 
-    // the split's pages, one chunk (= page) per lane, looked up once
-    const int nch = (ke - kb + kAttnChunk - 1) / kAttnChunk;
+    // the split's chunks and pages; its pages one per lane, looked up once
+    const int nch = (ke - kb + CHK - 1) / CHK;
+    const int npg = (ke - kb + kPage - 1) / kPage;
     // (an identity table needs no load: the K/V loads can go out at once)
     const int *ptb = R.pt + kb / kPage;
-    const int vpg = R.pt_ident ? kb / kPage + min(lane, nch - 1) : ptb[min(lane, nch - 1)];
-    auto page_of = [&](int ci) -> int {
-        ci = min(ci, nch - 1);
-        if (R.pt_ident) return kb / kPage + ci;
-        return ci < 64 ? __builtin_amdgcn_readlane(vpg, ci) : ptb[ci];
+    const int vpg = R.pt_ident ? kb / kPage + min(lane, npg - 1) : ptb[min(lane, npg - 1)];
+    // page pi of the split (pi is wave-uniform)
+    auto page_of = [&](int pi) -> int {
+        pi = min(pi, npg - 1);
+        if (R.pt_ident) return kb / kPage + pi;
+        return pi < 64 ? __builtin_amdgcn_readlane(vpg, pi) : ptb[pi];
     };
     // buffer loads over the layer's pools: an offset past the pool reads zeros
     // without a memory access, which is how chunks past the split are loaded.
@@ -615,10 +627,11 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(R.kvv), (short)0, (int)R.kv_bytes, kRsrcWord3);
     auto load = [&](int ci, u32x4 (&kr)[KS], u32x2 (&vr)[DT]) {
-        // the wave's 16-key group of the page's head block (16 * D elements of K and of V)
-        const unsigned gb = (unsigned)((((long long)page_of(ci) * a.Hk + j) * kPage + w * 16) * D * 2);
-        const unsigned ko = ci < nch ? gb + lane * 16 : kPast;
-        const unsigned vo = ci < nch ? gb + lane * 16 : kPast;
+        // the wave's 16-key group of its page's head block (16 * D elements of K and of V)
+        const int pi = ci * PPC + w / 4;
+        const unsigned gb = (unsigned)((((long long)page_of(pi) * a.Hk + j) * kPage + (w % 4) * 16) * D * 2);
+        const unsigned ko = pi < npg ? gb + lane * 16 : kPast;
+        const unsigned vo = pi < npg ? gb + lane * 16 : kPast;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kr[ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(ko + ks * 1024), 0, 0);
         // one 16-byte load per lane holds its fragments of output tiles 2p and 2p + 1
@@ -671,7 +684,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
 
     // one wave chunk: keys k0..k0+15 with at least one in [lo, ke) (none past the split)
     auto chunk = [&](int ci, const u32x4 (&kr)[KS], const u32x2 (&vr)[DT]) {
-        const int k0 = kb + ci * kAttnChunk + w * 16;
+        const int k0 = kb + ci * CHK + w * 16;
         if (ci >= nch || k0 + 15 < lo || k0 >= ke) return;
         f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -774,7 +787,7 @@ __global__ void __launch_bounds__(256) k_attn_mfma(AttnArgs a) {
     lds_barrier();
 
     const int ns = ns_b;
-    for (int idx = tid; idx < NC * D; idx += 256) {
+    for (int idx = tid; idx < NC * D; idx += NWV * 64) {
         const int g = idx / D, d = idx % D;  // (tiled: column g = G * row + head)
         if (TR > 1 && g / G >= nr) continue;
         float M = wm[0][g];

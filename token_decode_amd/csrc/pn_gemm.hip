@@ -34,17 +34,21 @@ void go_k(const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
 template <int PRO, int EPI, int NTW, bool PAIR, int NW>
 void go_nw(int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
     constexpr bool MOE = EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN;
-    if constexpr (!MOE) {
-        if (amode == A_LDS_WAVE) {
-            go_k<PRO, EPI, NTW, PAIR, NW, true, true>(g, grid, lds, s, occ);
-            return;
-        }
-    }
-    if constexpr (PRO != PRO_LOAD) {
-        go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
+    if constexpr (PRO == PRO_MERGE) {  // (wave-local only)
+        go_k<PRO, EPI, NTW, PAIR, NW, true, true>(g, grid, lds, s, occ);
     } else {
-        if (amode != A_DIRECT) go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
-        else go_k<PRO, EPI, NTW, PAIR, NW, false, false>(g, grid, lds, s, occ);
+        if constexpr (!MOE) {
+            if (amode == A_LDS_WAVE) {
+                go_k<PRO, EPI, NTW, PAIR, NW, true, true>(g, grid, lds, s, occ);
+                return;
+            }
+        }
+        if constexpr (PRO != PRO_LOAD) {
+            go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
+        } else {
+            if (amode != A_DIRECT) go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
+            else go_k<PRO, EPI, NTW, PAIR, NW, false, false>(g, grid, lds, s, occ);
+        }
     }
 }
 
@@ -66,6 +70,7 @@ void PN_NAME(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t l
         case GK_MOE_SWIGLU: go<PRO_NORM, EPI_MOE_SWIGLU, 2, true>(nw, amode, g, grid, lds, s, occ); break;
         case GK_MOE_DOWN: go<PRO_LOAD, EPI_MOE_DOWN, 1, false>(nw, amode, g, grid, lds, s, occ); break;
         case GK_O: go<PRO_CONV, EPI_RESID, 1, false>(nw, amode, g, grid, lds, s, occ); break;
+        case GK_O_MERGE: go<PRO_MERGE, EPI_RESID, 1, false>(nw, amode, g, grid, lds, s, occ); break;
         default: break;
     }
 }

@@ -61,7 +61,10 @@ static_assert(kv_v_off(true, 17, 31, 128) == kv_v_off(true, 17, 30, 128) + kv_v_
 // along K with one fp16 scale each, and int8 / 4-bit codes)
 enum WType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2, WT_Q8 = 3, WT_Q4 = 4 };
 enum AType { AT_F32 = 0, AT_BF16 = 1 };
-enum Pro { PRO_NORM = 0, PRO_LOAD = 1, PRO_CONV = 2 };  // CONV: A = round_act(fp32 rows), no norm
+enum Pro { PRO_NORM = 0, PRO_LOAD = 1, PRO_CONV = 2, PRO_MERGE = 3 };  // CONV: A = round_act(fp32 rows), no norm
+// MERGE (one slot, wave-local): A = round_act(the attention output), its splits
+// combined in the prologue from their (max, sum, unnormalised output)
+constexpr int kMergeSplits = 8;  // the most attention splits per head the MERGE prologue combines
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_MOE_SWIGLU = 4,
            EPI_MOE_DOWN = 5 };
 
@@ -247,6 +250,10 @@ struct GemmArgs {
     char *kvk[kMaxSlots];   // per slot: K pool of this layer
     char *kvv[kMaxSlots];
     const int *pt[kMaxSlots];
+    // MERGE prologue: slot 0's attention splits, [Hk][s_cap][G][D+4] floats each
+    // (max, sum, 2 pad, unnormalised output); with one split the output is in x
+    const float *part;
+    int nsplit, s_cap;
 };
 
 // fp16 halves of a 32-bit word as floats
@@ -499,6 +506,60 @@ __device__ __forceinline__ void put_a8(uint8_t *sa, int rows, int nb, int b, int
     }
 }
 
+// Write the A values of 4 consecutive k (k0..k0+3, k0 a multiple of 4) of slot
+// b into the LDS fragments: half of put_a8's fragment.
+template <int WT, int AT>
+__device__ __forceinline__ void put_a4(uint8_t *sa, int rows, int nb, int b, int k0, const float (&v)[4]) {
+    constexpr int TK = tile_k(WT);
+    constexpr int FB = frag_bytes(WT);
+    constexpr int EPG = TK / 4;
+    const int kt = k0 / TK, kin = k0 % TK;
+    if constexpr (WT == WT_F32) {
+        *reinterpret_cast<f32x4 *>(sa + ((kt * 4 + kin / EPG) * rows + b) * FB) = f32x4{v[0], v[1], v[2], v[3]};
+    } else if constexpr (f16_a(WT)) {
+        // 4-aligned runs of k are 4 consecutive positions in both orders
+        const int pos = blockq(WT) ? blk_pos(tile_blocks(WT), kin) : kin;
+        const int gq = pos / EPG, el = pos % EPG;
+        u32x2 o;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            o[q] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)v[2 * q], (_Float16)v[2 * q + 1]});
+        *reinterpret_cast<u32x2 *>(sa + ((kt * 4 + gq) * rows + b) * FB + el * 2) = o;
+    } else {
+        const int gq = kin / EPG, el = kin % EPG;
+        uint8_t *dst = sa + ((kt * 4 + gq) * rows + b) * FB + el * 2;
+        if constexpr (AReady<WT, AT>::PIECES == 1) {
+            u32x2 o;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) o[q] = bf16_rne_bits(v[2 * q]) | (bf16_rne_bits(v[2 * q + 1]) << 16);
+            *reinterpret_cast<u32x2 *>(dst) = o;
+        } else {
+            u32x2 o0, o1, o2;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                uint32_t w0[2], w1[2], w2[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float x = v[2 * q + h];
+                    const float p0 = bf16_round(x);
+                    const float r1 = x - p0;
+                    const float p1 = bf16_round(r1);
+                    const float p2 = bf16_round(r1 - p1);
+                    w0[h] = bf16_rne_bits(p0);
+                    w1[h] = bf16_rne_bits(p1);
+                    w2[h] = bf16_rne_bits(p2);
+                }
+                o0[q] = w0[0] | (w0[1] << 16);
+                o1[q] = w1[0] | (w1[1] << 16);
+                o2[q] = w2[0] | (w2[1] << 16);
+            }
+            *reinterpret_cast<u32x2 *>(dst) = o0;
+            *reinterpret_cast<u32x2 *>(dst + nb * FB) = o1;
+            *reinterpret_cast<u32x2 *>(dst + 2 * nb * FB) = o2;
+        }
+    }
+}
+
 // Prologue register budgets of a GEMM variant.  x-prologue: 8-element chunks
 // per thread per batch (its first batch's loads go out before any weight
 // load): for the norm prologue four rows of 4096 with 16 waves, one with 8
@@ -544,7 +605,9 @@ template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALD
 __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     static_assert(PRO == PRO_LOAD || ALDS, "the norm prologue stages A in LDS");
     static_assert(!WL || ALDS, "the wave-local prologue stages A in LDS");
+    static_assert(PRO != PRO_MERGE || (WL && EPI == EPI_RESID), "the split combine runs in the wave-local prologue");
     constexpr bool XPRO = PRO == PRO_NORM || PRO == PRO_CONV;  // A built from fp32 rows in g.x
+    constexpr bool MPRO = PRO == PRO_MERGE;
     constexpr int NT = NW * 64;
     constexpr int TK = tile_k(WT);
     constexpr int FB = frag_bytes(WT);
@@ -698,6 +761,36 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         }
     }
 
+    // The split-combine prologue (one slot): lane l takes the 4 consecutive k
+    // wt0*TK + 4l .. +3 of this wave's slice, dims dd.. of query head h.  It
+    // loads every split's (max, sum) and its 4 unnormalised outputs (split
+    // indices clamped to the last split), or with one split the attention
+    // output itself.
+    constexpr int SMX = MPRO ? kMergeSplits : 1;
+    f32x2 mml[SMX];
+    f32x4 mov[SMX];
+    const int mk0 = wt0 * TK + 4 * lane;
+    const bool mslice = MPRO && 4 * lane < (wt1 - wt0) * TK;  // this lane's 4 k are in the wave's tiles
+    const bool min_ = mslice && mk0 < g.K;                      // ... and below K (the rest of a tile is 0)
+    if constexpr (MPRO) {
+        const int kk = min_ ? mk0 : 0;
+        if (g.nsplit <= 1) {
+            mov[0] = *reinterpret_cast<const f32x4 *>(g.x + kk);
+        } else {
+            const int G = g.Hq / g.Hk;
+            const int h = kk / g.D, dd = kk - h * g.D;
+            const int jh = h / G, gh = h - jh * G;
+            const long long sst = (long long)G * (g.D + 4);  // floats between consecutive splits
+            const float *pb = g.part + ((long long)jh * g.s_cap * G + gh) * (g.D + 4);
+#pragma unroll
+            for (int sx = 0; sx < SMX; ++sx) {
+                const float *ps = pb + min(sx, g.nsplit - 1) * sst;
+                mml[sx] = *reinterpret_cast<const f32x2 *>(ps);
+                mov[sx] = *reinterpret_cast<const f32x4 *>(ps + 4 + dd);
+            }
+        }
+    }
+
     // epilogue inputs of one block, loaded early by the threads that use them
     // (row r of slot b: the old x for the residual, the (cos, sin) for RoPE,
     // the int8 row scales)
@@ -780,25 +873,33 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
         }
         arow = reinterpret_cast<const uint8_t *>(g.a) + (sp * g.a_plane + r * g.lda + ag * (TK / 4)) * ES;
     }
-    u32x4 wa[NTW][KU], wb[NTW][KU];
-    u32x4 aa[KU][frag_vecs(WT)], ab[KU][frag_vecs(WT)];
+    // NR register rounds rotate (NR - 1 in flight while one is multiplied).
+    // Three rounds for the 16-wave groups fit their 128 registers with no spill
+    // but made every such kernel slower (8 slots: QKV 15.2 -> 16.9 us, gate/up
+    // 41.2 -> 43.1 us): the weight stream is not short of loads in flight.
+    constexpr int NR = 2;
+    u32x4 wr[NR][NTW][KU];
+    u32x4 ar[NR][KU][frag_vecs(WT)];
     const uint8_t *wbase[NTW];
     bool wlive[NTW];
     block_ptrs(blk0, wbase, wlive);
-    SReg<WT> sca[NTW][KU], scb[NTW][KU];  // block scales of the rounds in wa, wb
+    SReg<WT> sr[NR][NTW][KU];  // block scales of the rounds in wr
 #pragma unroll
-    for (int mt = 0; mt < NTW; ++mt)
+    for (int q = 0; q < NR; ++q)
 #pragma unroll
-        for (int i = 0; i < KU; ++i) sca[mt][i] = scb[mt][i] = SReg<WT>{};
+        for (int mt = 0; mt < NTW; ++mt)
+#pragma unroll
+            for (int i = 0; i < KU; ++i) sr[q][mt][i] = SReg<WT>{};
     auto issue_first = [&]() {
         if constexpr (blockq(WT)) {
-            issue_s<WT, NTW, KU>(sca, sbase, wt0, last);
-            issue_s<WT, NTW, KU>(scb, sbase, wt0 + KU, last);
+#pragma unroll
+            for (int q = 0; q < NR; ++q) issue_s<WT, NTW, KU>(sr[q], sbase, wt0 + q * KU, last);
         }
-        issue_w<WT, NTW, KU>(wa, wbase, wt0, last);
-        if constexpr (!ALDS) issue_a<WT, AT, KU>(aa, arow, alive, wt0, last);
-        issue_w<WT, NTW, KU>(wb, wbase, wt0 + KU, last);
-        if constexpr (!ALDS) issue_a<WT, AT, KU>(ab, arow, alive, wt0 + KU, last);
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+            issue_w<WT, NTW, KU>(wr[q], wbase, wt0 + q * KU, last);
+            if constexpr (!ALDS) issue_a<WT, AT, KU>(ar[q], arow, alive, wt0 + q * KU, last);
+        }
     };
     issue_first();
 
@@ -909,6 +1010,41 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
             }
             lds_barrier();
         }
+    } else if constexpr (MPRO) {
+        // weights exp2(M_s - M) per split, the head's sum L, and the combined
+        // output sum_s (w_s / L) o_s, in split order; straight into LDS (zeros
+        // past K)
+        if (mslice) {
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+            if (!min_) {
+            } else if (g.nsplit <= 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = mov[0][e];
+            } else {
+                float M = -INFINITY;
+#pragma unroll
+                for (int sx = 0; sx < SMX; ++sx) M = sx < g.nsplit ? fmaxf(M, mml[sx][0]) : M;
+                float f[SMX], L = 0.f;
+#pragma unroll
+                for (int sx = 0; sx < SMX; ++sx) {
+                    f[sx] = sx < g.nsplit ? __builtin_amdgcn_exp2f(mml[sx][0] - M) : 0.f;
+                    L = sx < g.nsplit ? fmaf(f[sx], mml[sx][1], L) : L;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = 0.f;
+#pragma unroll
+                for (int sx = 0; sx < SMX; ++sx) {
+                    const float fw = f[sx] / L;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = sx < g.nsplit ? fmaf(fw, mov[sx][e], v[e]) : v[e];
+                }
+            }
+            if constexpr (AT == AT_BF16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = bf16_round(v[e]);
+            }
+            put_a4<WT, AT>(sa, rows, nb, 0, mk0, v);
+        }
     } else if constexpr (ALDS) {
         if constexpr (wl) {
             // this wave's fragments of every row, straight into LDS
@@ -955,28 +1091,24 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     }
 
     for (int blk = blk0; blk < blk1; ++blk) {
-        // ---- main loop of this block: weight rounds ping-pong between wa and wb.
-        // Every round issues the same loads (clamped past the end), so the
-        // waits are exact and the round after next is always in flight.
+        // ---- main loop of this block: weight rounds rotate through the NR
+        // register buffers.  Every round issues the same loads (clamped past the
+        // end), so the waits are exact and NR - 1 rounds are always in flight.
         f32x4 acc[NTW];
 #pragma unroll
         for (int mt = 0; mt < NTW; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int r = 0; r < rounds; r += 2) {
-            const int ta = wt0 + r * KU;
-            compute_round<WT, NTW, KU, ALDS>(acc, wa, sca, aa, sa, zoff, a_step, a_base, wlive, ta,
-                                             min(KU, wt1 - ta));
-            if (r + 2 < rounds) {
-                if constexpr (blockq(WT)) issue_s<WT, NTW, KU>(sca, sbase, ta + 2 * KU, last);
-                issue_w<WT, NTW, KU>(wa, wbase, ta + 2 * KU, last);
-                if constexpr (!ALDS) issue_a<WT, AT, KU>(aa, arow, alive, ta + 2 * KU, last);
-            }
-            if (r + 1 < rounds) {
-                compute_round<WT, NTW, KU, ALDS>(acc, wb, scb, ab, sa, zoff, a_step, a_base, wlive, ta + KU,
-                                                 min(KU, wt1 - ta - KU));
-                if (r + 3 < rounds) {
-                    if constexpr (blockq(WT)) issue_s<WT, NTW, KU>(scb, sbase, ta + 3 * KU, last);
-                    issue_w<WT, NTW, KU>(wb, wbase, ta + 3 * KU, last);
-                    if constexpr (!ALDS) issue_a<WT, AT, KU>(ab, arow, alive, ta + 3 * KU, last);
+        for (int r = 0; r < rounds; r += NR) {
+#pragma unroll
+            for (int q = 0; q < NR; ++q) {
+                if (r + q < rounds) {
+                    const int ta = wt0 + (r + q) * KU;
+                    compute_round<WT, NTW, KU, ALDS>(acc, wr[q], sr[q], ar[q], sa, zoff, a_step, a_base, wlive, ta,
+                                                     min(KU, wt1 - ta));
+                    if (r + q + NR < rounds) {
+                        if constexpr (blockq(WT)) issue_s<WT, NTW, KU>(sr[q], sbase, ta + NR * KU, last);
+                        issue_w<WT, NTW, KU>(wr[q], wbase, ta + NR * KU, last);
+                        if constexpr (!ALDS) issue_a<WT, AT, KU>(ar[q], arow, alive, ta + NR * KU, last);
+                    }
                 }
             }
         }

@@ -15,7 +15,8 @@ enum GemmKind {
     GK_MOE_SWIGLU = 4, // gathered rows, per-expert gate/up pair
     GK_MOE_DOWN = 5,   // gathered A-ready rows, per-expert down
     GK_O = 6,          // fp32 rows rounded to the activation type, residual epilogue
-    GK_COUNT = 7
+    GK_O_MERGE = 7,    // GK_O for one slot whose attention splits are combined in the prologue
+    GK_COUNT = 8
 };
 
 // Dynamic LDS a launch may use, in bytes: a work-group's 160 KiB less 1 KiB

@@ -109,7 +109,8 @@ struct pn_model {
     int h_ld = 0;
     int attn_kps = 0;   // 0 = automatic
     int attn_kind = 0;  // bf16 cache: 0 = automatic, 1 = vector units, 2 = matrix cores
-    int nw[GK_COUNT] = {8, 8, 8, 8, 8, 8, 16};  // waves per work-group of each GEMM kind
+    int attn_combine = 0;  // split combine: 0 = automatic (O prologue where eligible), 1 = merge launch
+    int nw[GK_COUNT] = {8, 8, 8, 8, 8, 8, 16, 16};  // waves per work-group of each GEMM kind (O_MERGE: O's)
     int nw_down = 16;                       // the down projection (K = n_ff) uses GK_RESID too
     bool nw_set = false;                    // waves chosen by the caller (PN_OPT_WAVES_*): no auto choice
     std::map<std::tuple<int, int, int, size_t>, int> occ;  // resident work-groups per CU of a GEMM variant
@@ -180,7 +181,8 @@ constexpr size_t kALdsMax = 96 * 1024;
 constexpr int kCUs = 256;
 
 bool norm_kind(int kind) {  // A built in LDS from fp32 rows
-    return kind == GK_QKV || kind == GK_SWIGLU || kind == GK_LOGITS || kind == GK_MOE_SWIGLU || kind == GK_O;
+    return kind == GK_QKV || kind == GK_SWIGLU || kind == GK_LOGITS || kind == GK_MOE_SWIGLU || kind == GK_O ||
+           kind == GK_O_MERGE;
 }
 int ntw_of(int kind) { return (kind == GK_SWIGLU || kind == GK_LOGITS || kind == GK_MOE_SWIGLU) ? 2 : 1; }
 
@@ -603,6 +605,7 @@ void gemm_entry(int kind, int wt, int at, int nw, int amode, const GemmArgs &g, 
 
 int pro_of(int kind) {
     if (kind == GK_RESID || kind == GK_MOE_DOWN) return PRO_LOAD;
+    if (kind == GK_O_MERGE) return PRO_MERGE;
     return kind == GK_O ? PRO_CONV : PRO_NORM;
 }
 
@@ -618,6 +621,7 @@ void launch_gemm(int kind, int wt, int at, GemmArgs g, const Plan &p, hipStream_
     int amode = p.a_lds || pro != PRO_LOAD ? A_LDS : A_DIRECT;
     if (!moe && amode == A_LDS && gemm_wave_local_fits(wt, pro, p.nw, g.B, g.B * pieces, g.KT))
         amode = A_LDS_WAVE;
+    if (kind == GK_O_MERGE) amode = A_LDS_WAVE;  // (eligibility checked by merge_in_o)
     gemm_entry(kind, wt, at, p.nw, amode, g, grid, p.lds, s, nullptr);
 }
 
@@ -685,7 +689,8 @@ struct Timed {
 // split scratch is the model's per-row buffer (prefill rows share a state);
 // otherwise each state's own.  Sets everything but q, o and the K/V pools;
 // returns the largest nsplit.
-int attn_setup(const pn_model *m, pn_state *const *st, int n, const int *pos, bool rows, AttnArgs &aa) {
+int attn_setup(const pn_model *m, pn_state *const *st, int n, const int *pos, bool rows, AttnArgs &aa,
+               int ns_cap = 0) {
     aa.Hq = m->H;
     aa.Hk = m->Hk;
     aa.scale = (float)(1.4426950408889634 / std::sqrt((double)m->D));  // log2(e) / sqrt(D)
@@ -699,6 +704,7 @@ int attn_setup(const pn_model *m, pn_state *const *st, int n, const int *pos, bo
         aa.origin[b] = lo / kPage * kPage;
         const int np = cdiv(pos[b] + 1 - aa.origin[b], kPage);
         long long ns = m->attn_kps > 0 ? cdiv(np, m->attn_kps / kPage)
+                       : ns_cap > 0    ? ns_cap
                                        : attn_target_groups(m->Hk * np_sum) * np / ((long long)m->Hk * np_sum);
         const int cap = rows ? kMaxSplits : st[b]->s_cap;
         ns = std::min<long long>(std::max<long long>(ns, 1), std::min(np, std::min(cap, kMaxSplits)));
@@ -713,6 +719,22 @@ int attn_setup(const pn_model *m, pn_state *const *st, int n, const int *pos, bo
         aa.pt_ident[b] = (!st[b]->pool && st[b]->pt_identity) ? 1 : 0;
     }
     return nsplit_max;
+}
+
+// Whether a decode step combines the attention splits in the O projection's
+// prologue instead of a separate merge launch: one slot (not prefill rows), a
+// bf16 cache scored on the matrix cores with G <= 4 query heads per KV head
+// (8-wave attention work-groups, at most kMergeSplits splits), a window of at
+// most kMergePages pages, and an O GEMM whose waves each cover at most 256 k
+// (one 4-element piece per lane).  Measured on Llama-3-8B shapes: at 33 pages
+// (2048 keys) the step is 0.8% faster this way; at 129 pages (8192 keys) 4.5%
+// slower (eight splits of 16 pages take longer than 32 of 4 plus the merge).
+constexpr int kMergePages = 48;
+bool merge_in_o(const pn_model *m, int n, bool rows, int pos, const Plan &p_o, int KT_o) {
+    if (n != 1 || rows || m->kvt != PN_BF16 || m->attn_kind == 1 || m->G > 4 || m->attn_combine == 1) return false;
+    const int lo = window_lo(m, pos);
+    if (cdiv(pos + 1 - lo / kPage * kPage, kPage) > kMergePages) return false;
+    return cdiv(KT_o, p_o.nw) * tile_k(m->wt) <= 256;
 }
 
 int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, float *logits, int32_t *amax,
@@ -773,12 +795,6 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     };
     if (int rc = trace_x(0)) return rc;
 
-    // attention geometry per slot
-    AttnArgs aa{};
-    const int nsplit_max = attn_setup(m, st, n, pos_of_rows, row_pos != nullptr, aa);
-    aa.q = (const float *)(mb + m->q);
-    aa.o = (float *)(mb + m->o);
-
     const LayerOff &L0 = m->L[0];
     const int gz = moe ? m->X : 1;
     auto occ_of = [&](int kind, int nw, bool alds, size_t lds) -> int {
@@ -802,6 +818,16 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     const Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of,
                                 !m->nw_set, n, cap);
     // (plans for the other kinds take one row block per tile)
+
+    // attention geometry per slot; with the split combine in the O prologue, at
+    // most kMergeSplits splits per head (unless the caller's keys per split give more)
+    bool mio = merge_in_o(m, n, row_pos != nullptr, pos_of_rows[0], p_o, L0.o.KT);
+    AttnArgs aa{};
+    const int nsplit_max = attn_setup(m, st, n, pos_of_rows, row_pos != nullptr, aa, mio ? kMergeSplits : 0);
+    if (nsplit_max > kMergeSplits) mio = false;
+    aa.q = (const float *)(mb + m->q);
+    aa.o = (float *)(mb + m->o);
+    aa.waves = mio ? 8 : kAttnWaves;
 
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerOff &L = m->L[l];
@@ -850,12 +876,12 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             }
             aa.kind = m->attn_kind == 1 ? 0 : 1;
             Timed tm(m, PN_K_ATTN, s);
-            launch_attn(m->D, m->kvt, m->G, aa, dim3(nsplit_max, m->Hk, n), nsplit_max > 1, s);
+            launch_attn(m->D, m->kvt, m->G, aa, dim3(nsplit_max, m->Hk, n), nsplit_max > 1 && !mio, s);
             if (int rc = launched("attention")) return rc;
             pn_model::Replay r;
             r.aa = aa;
             r.grid = dim3(nsplit_max, m->Hk, n);
-            r.merge = nsplit_max > 1;
+            r.merge = nsplit_max > 1 && !mio;
             m->last[PN_K_ATTN].push_back(r);
         }
         // ---- O projection + residual
@@ -870,10 +896,14 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
             g.x = (const float *)(mb + m->o);
             g.out_f32 = x;
             g.ld_out = E;
+            g.part = aa.part[0];
+            g.nsplit = aa.nsplit[0];
+            g.s_cap = aa.s_cap[0];
+            const int ko = mio ? GK_O_MERGE : GK_O;
             Timed tm(m, PN_K_O, s);
-            launch_gemm(GK_O, wt, at, g, p_o, s);
+            launch_gemm(ko, wt, at, g, p_o, s);
             if (int rc = launched("O projection", &p_o)) return rc;
-            record_gemm(m, PN_K_O, GK_O, g, p_o);
+            record_gemm(m, PN_K_O, ko, g, p_o);
         }
         // ---- FFN
         if (!moe) {
@@ -1962,6 +1992,11 @@ int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
     if (option == PN_OPT_ATTN_KERNEL) {
         if (value < 0 || value > 2) return fail(PN_EINVAL, "attention kernel must be 0, 1 or 2");
         m->attn_kind = (int)value;
+        return PN_OK;
+    }
+    if (option == PN_OPT_ATTN_COMBINE) {
+        if (value < 0 || value > 1) return fail(PN_EINVAL, "split combine must be 0 or 1");
+        m->attn_combine = (int)value;
         return PN_OK;
     }
     if (option == PN_OPT_ATTN_KEYS_PER_SPLIT) {
