@@ -382,12 +382,19 @@ enum {
  *                              splits per head and combines them in the O
  *                              projection's prologue; 1 = always the separate
  *                              split-merge launch;
+ *  PN_OPT_ATTN_WAVES           decode attention over a bf16 cache on the
+ *                              matrix cores (at most 4 query heads per KV
+ *                              head): waves per work-group, 0 = automatic (8
+ *                              where the splits are combined in the O
+ *                              prologue, else 4), 4 or 8 (ignored where the
+ *                              combine runs in the O prologue);
  *  PN_OPT_WAVES_*              waves per work-group (4, 8 or 16) of the QKV,
  *                              O, gate/up, down and LM-head projections. */
 enum {
     PN_OPT_ATTN_KEYS_PER_SPLIT = 1,
     PN_OPT_ATTN_KERNEL = 2,
     PN_OPT_ATTN_COMBINE = 3,
+    PN_OPT_ATTN_WAVES = 4,
     PN_OPT_WAVES_QKV = 10, PN_OPT_WAVES_O, PN_OPT_WAVES_GATEUP, PN_OPT_WAVES_DOWN, PN_OPT_WAVES_LMHEAD
 };
 int pn_model_set_option(pn_model *m, int32_t option, int64_t value);

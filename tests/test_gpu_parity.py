@@ -118,16 +118,20 @@ def test_split_combine_in_o_prologue(start):
     reads as is) to 34 pages (8 splits of 4 or 5 pages), with head_dim 128 and
     fp32 activations, head_dim 64 and bf16 activations; then with 64 keys per
     split the 700- and 2100-key windows need more than 8 splits and go through
-    the merge launch instead.  Every step against the oracle."""
+    the merge launch instead, and with the combine switched off the 8-wave
+    attention work-groups feed the merge launch.  Every step against the
+    oracle."""
     from token_decode_amd import _capi as C
-    for kps in (0, 64):
-        if kps and start < 700:
+    for kps, combine, waves in ((0, 0, 0), (64, 0, 0), (0, 1, 8)):
+        if (kps or combine) and start < 700:
             continue
         for i, (H, Hk, d, act) in enumerate(((8, 2, 128, synth.F32), (6, 3, 64, synth.BF16))):
-            wl = ragged("combine-%d-%d-kps%d" % (start, d, kps), n_head=H, n_kv_head=Hk, head_dim=d,
-                        w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=act, seed=60 + i)
+            wl = ragged("combine-%d-%d-kps%d-c%d" % (start, d, kps, combine), n_head=H, n_kv_head=Hk,
+                        head_dim=d, w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=act, seed=60 + i)
             p = Pair(wl)
             p.dm.set_option(C.PN_OPT_ATTN_KEYS_PER_SPLIT, kps)
+            p.dm.set_option(C.PN_OPT_ATTN_COMBINE, combine)
+            p.dm.set_option(C.PN_OPT_ATTN_WAVES, waves)
             worst, near, n = run_single(p, start, [5, 6], 2, max_ctx=start + 8)
             log("  %s: worst rel L2 %.2e near %d" % (wl.name, worst, near))
 

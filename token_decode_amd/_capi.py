@@ -12,6 +12,7 @@ PN_F32, PN_BF16, PN_I8, PN_Q8_0, PN_Q4_0 = 0, 1, 2, 3, 4
 PN_OPT_ATTN_KEYS_PER_SPLIT = 1
 PN_OPT_ATTN_KERNEL = 2
 PN_OPT_ATTN_COMBINE = 3
+PN_OPT_ATTN_WAVES = 4
 PN_OPT_WAVES_QKV, PN_OPT_WAVES_O, PN_OPT_WAVES_GATEUP, PN_OPT_WAVES_DOWN, PN_OPT_WAVES_LMHEAD = range(10, 15)
 
 KERNEL_NAMES = ["embed", "qkv", "attn", "o", "gateup", "down", "lmhead", "argmax", "router",

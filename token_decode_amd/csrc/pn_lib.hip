@@ -110,6 +110,7 @@ struct pn_model {
     int attn_kps = 0;   // 0 = automatic
     int attn_kind = 0;  // bf16 cache: 0 = automatic, 1 = vector units, 2 = matrix cores
     int attn_combine = 0;  // split combine: 0 = automatic (O prologue where eligible), 1 = merge launch
+    int attn_waves = 0;    // matrix-core attention work-groups: 0 = automatic, 4 or 8 waves
     int nw[GK_COUNT] = {8, 8, 8, 8, 8, 8, 16, 16};  // waves per work-group of each GEMM kind (O_MERGE: O's)
     int nw_down = 16;                       // the down projection (K = n_ff) uses GK_RESID too
     bool nw_set = false;                    // waves chosen by the caller (PN_OPT_WAVES_*): no auto choice
@@ -827,7 +828,11 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     if (nsplit_max > kMergeSplits) mio = false;
     aa.q = (const float *)(mb + m->q);
     aa.o = (float *)(mb + m->o);
-    aa.waves = mio ? 8 : kAttnWaves;
+    // 8-wave attention work-groups (two pages per chunk) where the split
+    // combine runs in the O prologue (few, long splits).  Elsewhere they
+    // measured slower (8 slots: 30.8 -> 34.3 us per layer; Llama-3-8B INT8 at
+    // 8192 keys: 2.147 -> 2.162 ms per step), so 4 unless the caller asks.
+    aa.waves = mio ? 8 : (m->attn_waves && !row_pos ? m->attn_waves : kAttnWaves);
 
     for (int l = 0; l < c.n_layer; ++l) {
         const LayerOff &L = m->L[l];
@@ -1992,6 +1997,11 @@ int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
     if (option == PN_OPT_ATTN_KERNEL) {
         if (value < 0 || value > 2) return fail(PN_EINVAL, "attention kernel must be 0, 1 or 2");
         m->attn_kind = (int)value;
+        return PN_OK;
+    }
+    if (option == PN_OPT_ATTN_WAVES) {
+        if (value != 0 && value != 4 && value != 8) return fail(PN_EINVAL, "attention waves must be 0, 4 or 8");
+        m->attn_waves = (int)value;
         return PN_OK;
     }
     if (option == PN_OPT_ATTN_COMBINE) {
