@@ -54,10 +54,10 @@ PREFILL_TOKENS = 512
 
 
 def wide_ok(wl):
-    """Whether the workload can take the wide prefill path (bf16, int8, Q8_0 or Q4_0 weights, dense,
-    fp32 or bf16 cache)."""
+    """Whether the workload can take the wide prefill path (bf16, int8, Q8_0 or Q4_0 weights,
+    fp32 or bf16 cache; dense or experts)."""
     import synth
-    return (wl.w_dtype in (synth.BF16, synth.I8, synth.Q8_0, synth.Q4_0) and wl.n_expert == 0 and
+    return (wl.w_dtype in (synth.BF16, synth.I8, synth.Q8_0, synth.Q4_0) and
             wl.kv_dtype in (synth.F32, synth.BF16))
 
 

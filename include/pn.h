@@ -103,9 +103,10 @@ typedef enum { PN_F32 = 0, PN_BF16 = 1, PN_I8 = 2, PN_Q8_0 = 3, PN_Q4_0 = 4 } pn
  *  prefill_chunk  rows per pn_prefill chunk on the wide path, 1..256, or 0
  *            (chunks of max_batch through the decode kernels).  The wide path
  *            takes each chunk through every projection as one matrix product
- *            on the matrix cores, so a weight is read once per chunk; it needs
- *            w_dtype PN_BF16, PN_I8, PN_Q8_0 or PN_Q4_0, no experts and kv_dtype PN_F32 or PN_BF16
- *            (PN_EUNSUPPORTED otherwise), and adds its row buffers to
+ *            on the matrix cores, so a weight is read once per chunk (with
+ *            experts: each expert's once, over the rows routed to it); it needs
+ *            w_dtype PN_BF16, PN_I8, PN_Q8_0 or PN_Q4_0 and kv_dtype PN_F32 or
+ *            PN_BF16 (PN_EUNSUPPORTED otherwise), and adds its row buffers to
  *            pn_model_bytes. */
 typedef struct pn_config {
     int32_t n_layer, n_embd, n_head, n_kv_head, head_dim, n_ff, n_vocab;

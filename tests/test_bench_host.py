@@ -37,4 +37,4 @@ def test_wide_prefill_eligibility():
     assert bench.wide_ok(synth.WORKLOADS["llama3-8b-q8_0"]())
     assert bench.wide_ok(synth.WORKLOADS["llama3-8b-q4_0"]())
     assert not bench.wide_ok(synth.WORKLOADS["llama3-8b-q4_0-kvq4-32k"]())
-    assert not bench.wide_ok(synth.WORKLOADS["mixtral-8x7b-16slots"]())
+    assert bench.wide_ok(synth.WORKLOADS["mixtral-8x7b-16slots"]())

@@ -76,7 +76,7 @@ def test_flag_fields_are_zero_or_one():
     (dict(kv_dtype=C.PN_Q4_0, rope_neox=True), C.PN_EUNSUPPORTED),
     (dict(prefill_chunk=-1), C.PN_EINVAL),
     (dict(prefill_chunk=257), C.PN_EINVAL),
-    (dict(prefill_chunk=64, n_expert=8, n_expert_used=2), C.PN_EUNSUPPORTED),
+    (dict(prefill_chunk=64, n_expert=8, n_expert_used=2), C.PN_EUNSUPPORTED),  # fp32 weights
     (dict(prefill_chunk=64, kv_dtype=C.PN_Q4_0), C.PN_EUNSUPPORTED),
 ])
 def test_bad_configs_rejected(kw, code):
@@ -98,7 +98,9 @@ def test_good_configs_and_sizes():
                dict(prefill_chunk=256, w_dtype=C.PN_BF16, act_dtype=C.PN_F32, kv_dtype=C.PN_F32),
                dict(prefill_chunk=64, w_dtype=C.PN_I8, act_dtype=C.PN_BF16, kv_dtype=C.PN_BF16),
                dict(prefill_chunk=64, w_dtype=C.PN_Q8_0, act_dtype=C.PN_BF16, n_ff=672),
-               dict(prefill_chunk=64, w_dtype=C.PN_Q4_0, act_dtype=C.PN_BF16, n_ff=672)):
+               dict(prefill_chunk=64, w_dtype=C.PN_Q4_0, act_dtype=C.PN_BF16, n_ff=672),
+               dict(prefill_chunk=128, n_expert=8, n_expert_used=2, w_dtype=C.PN_BF16, act_dtype=C.PN_BF16,
+                    kv_dtype=C.PN_BF16)):
         cfg = good_cfg(**kw)
         assert L.pn_config_check(ctypes.byref(cfg)) == 0, L.pn_last_error()
         assert L.pn_model_bytes(ctypes.byref(cfg)) > 0

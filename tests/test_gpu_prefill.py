@@ -331,3 +331,78 @@ def test_wide_mistral_shape_full_chunk():
     prompt = list(synth.uniform_int(wl.seed, 102, 300, 0, wl.n_vocab - 1))
     worst, near = run_prefill(p, 0, prompt, 1)
     log("  wide, Mistral-7B shape, 300 tokens in chunks of 256: worst rel L2 %.2e, near %d" % (worst, near))
+
+
+ROUTE_TOL = 1e-2  # router k-th / (k+1)-th gaps below this admit the swapped branch
+
+
+def run_prefill_moe(p, start, prompt, n_decode):
+    """run_prefill for an MoE model: every row is checked by the routing-branch
+    rule (a routing near tie may take the other expert; the oracle runs both
+    branches and the row must match one), and the oracle continues in the
+    branch the GPU took."""
+    import torch
+    from harness import moe_step_branches
+    from token_decode_amd import device as dv
+    wl = p.wl
+    ds, os_ = p.states(0, start, start + len(prompt) + n_decode + 1)
+    toks = torch.tensor([int(t) for t in prompt], dtype=torch.int32, device="cuda")
+    logits = torch.empty(len(prompt), wl.n_vocab, dtype=torch.float32, device="cuda")
+    am = torch.empty(len(prompt), dtype=torch.int32, device="cuda")
+    dv.prefill(p.dm, ds, toks, logits, am)
+    assert ds.pos == start + len(prompt)
+    g, ga = logits.cpu().numpy(), am.cpu().numpy()
+    worst, near, swaps, nxt = 0.0, 0, 0, None
+    th = oracle_threads()
+    for t, tok in enumerate(prompt):
+        rel, nt, mask, oa = moe_step_branches(wl, os_, int(tok), g[t], int(ga[t]), ROUTE_TOL, th)
+        worst, near, swaps, nxt = max(worst, rel), near + int(nt), swaps + int(mask != 0), oa
+    tok = torch.tensor([nxt], dtype=torch.int32, device="cuda")
+    lg1 = torch.empty(wl.n_vocab, dtype=torch.float32, device="cuda")
+    a1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    for i in range(n_decode):
+        dv.forward_step(p.dm, ds, tok, lg1, a1)
+        rel, nt, mask, oa = moe_step_branches(wl, os_, int(tok.item()), lg1.cpu().numpy(), int(a1.item()),
+                                              ROUTE_TOL, th)
+        worst, near, swaps = max(worst, rel), near + int(nt), swaps + int(mask != 0)
+        tok.fill_(oa)
+    return worst, near, swaps
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.I8], ids=["bf16", "int8"])
+def test_wide_moe_weights(dt):
+    """Experts on the wide path: 4 experts, top-2, a ragged model (n_embd 200,
+    n_ff 300) after a 5-token cache, 70 tokens in chunks of 32 (32 + 32 + 6):
+    every row routed, packed by expert, each expert's gate/up and down over its
+    rows, the weighted sum; every row against the oracle, then decode steps."""
+    wl = ragged("wide-moe-%d" % dt, n_expert=4, n_expert_used=2, w_dtype=dt, kv_dtype=synth.BF16,
+                act_dtype=synth.BF16, seed=110 + dt)
+    p = Pair(wl, max_batch=1, prefill_chunk=32)
+    prompt = list(synth.uniform_int(wl.seed, 111, 70, 0, wl.n_vocab - 1))
+    worst, near, swaps = run_prefill_moe(p, 5, prompt, 2)
+    log("  wide MoE (%d), 70 tokens from 5: worst rel L2 %.2e, near %d, routing swaps %d" % (dt, worst, near, swaps))
+
+
+def test_wide_moe_every_row_to_every_expert():
+    """2 experts, top-2: every row goes to both, so each expert takes all 256
+    rows of a full chunk (two 128-row groups of the grouped product), then a
+    44-row tail; top-1 of 3 experts after it (weights of exactly 1)."""
+    for ne, nu, seed in ((2, 2, 120), (3, 1, 121)):
+        wl = ragged("wide-moe-e%d-k%d" % (ne, nu), n_expert=ne, n_expert_used=nu, w_dtype=synth.BF16,
+                    kv_dtype=synth.BF16, act_dtype=synth.F32, seed=seed)
+        p = Pair(wl, max_batch=1, prefill_chunk=256)
+        prompt = list(synth.uniform_int(wl.seed, 122, 300, 0, wl.n_vocab - 1))
+        worst, near, swaps = run_prefill_moe(p, 0, prompt, 1)
+        log("  wide MoE %d experts top-%d, 300 tokens: worst rel L2 %.2e, near %d, swaps %d"
+            % (ne, nu, worst, near, swaps))
+
+
+def test_wide_moe_mixtral_shape():
+    """Mixtral-8x7B layer shape (2 layers, 8 experts of n_ff 14336, top-2,
+    bf16): 80 tokens in chunks of 64 after a 10-token cache."""
+    wl = synth.mixtral_8x7b_slots().with_(name="wide-mixtral-2l", n_layer=2, slots=1, seed=123)
+    p = Pair(wl, max_batch=1, prefill_chunk=64)
+    prompt = list(synth.uniform_int(wl.seed, 124, 80, 0, wl.n_vocab - 1))
+    worst, near, swaps = run_prefill_moe(p, 10, prompt, 1)
+    log("  wide, Mixtral-8x7B shape, 80 tokens from 10: worst rel L2 %.2e, near %d, swaps %d"
+        % (worst, near, swaps))

@@ -102,6 +102,12 @@ struct pn_model {
     // attention output [C][H*D]
     size_t wx = 0, wa = 0, wy = 0, wq = 0, wo = 0, wss = 0;
     long long wa_plane = 0, wy_cap = 0;
+    // wide prefill of an MoE model: the chunk's routing (ids, weights [C][n_used]),
+    // the entries packed by expert (counts and offsets [64], entry of each packed
+    // row, packed row of each entry), the packed rows' A planes [pieces][C *
+    // n_used][wlda], and the weighted sum of the experts' outputs [C][E]
+    size_t wrid = 0, wrw = 0, wecnt = 0, weoff = 0, went = 0, wpos = 0, wap = 0, wyc = 0;
+    long long wap_plane = 0;
     int wlda = 0;
     size_t o_bytes = 0, h_bytes = 0, am_count = 0;
     int a_es = 2;                      // bytes per A-ready element
@@ -296,9 +302,9 @@ int check_config_n(const pn_config *c) {
         return fail(PN_EINVAL, "prefill_chunk must be in [0, %d]", kWideRows);
     if (c->prefill_chunk > 0 && c->n_embd > 1024 * kWideSsq)
         return fail(PN_EUNSUPPORTED, "the wide prefill path takes n_embd up to %d", 1024 * kWideSsq);
-    if (c->prefill_chunk > 0 && (c->w_dtype == PN_F32 || c->n_expert > 0 || c->kv_dtype == PN_Q4_0))
+    if (c->prefill_chunk > 0 && (c->w_dtype == PN_F32 || c->kv_dtype == PN_Q4_0))
         return fail(PN_EUNSUPPORTED,
-                    "the wide prefill path needs bf16, int8, Q8_0 or Q4_0 weights, no experts and an fp32 or bf16 cache");
+                    "the wide prefill path needs bf16, int8, Q8_0 or Q4_0 weights and an fp32 or bf16 cache");
     const int pieces = (c->w_dtype == PN_BF16 && c->act_dtype == PN_F32) ? 3 : 1;
     if (c->max_batch * pieces > kMaxRows)
         return fail(PN_EUNSUPPORTED, "max_batch %d too large for this dtype combination (max %d)",
@@ -413,6 +419,20 @@ size_t layout_model(pn_model *m) {
         const long long qo = (long long)cdiv(std::max(m->Nqkv, m->E), 16) * 16;
         m->wy_cap = std::max((long long)kWideSplitMax * C * qo,
                              std::max(2LL * 2 * C * cdiv(m->F, 16) * 16, (long long)C * cdiv(m->V, 16) * 16));
+        if (c.n_expert > 0) {
+            const long long ne = (long long)C * m->n_used;  // packed rows
+            // gate and up of every packed row in the two halves; the down outputs with 2 splits
+            m->wy_cap = std::max(m->wy_cap, std::max(2LL * ne * cdiv(m->F, 16) * 16, 2LL * ne * cdiv(m->E, 16) * 16));
+            m->wrid = bp.take((size_t)ne * 4);
+            m->wrw = bp.take((size_t)ne * 4);
+            m->wecnt = bp.take(64 * 4);
+            m->weoff = bp.take(64 * 4);
+            m->went = bp.take((size_t)ne * 4);
+            m->wpos = bp.take((size_t)ne * 4);
+            m->wap_plane = ne * m->wlda;
+            m->wap = bp.take((size_t)m->pieces * m->wap_plane * 2);
+            m->wyc = bp.take((size_t)C * m->E * 4);
+        }
         m->wy = bp.take((size_t)m->wy_cap * 4);
     }
     m->kv_new = c.kv_dtype == PN_Q4_0 ? bp.take((size_t)MB * 2 * m->Hk * m->D * 4) : 0;
@@ -1178,6 +1198,55 @@ int wide_gemm(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_
     return ks;
 }
 
+// The experts' products of one wide MoE FFN: Y = A * W_e^T for every expert
+// e over its packed rows (counts and offsets on the device, from
+// k_w_route_lists; at most R rows each), A the packed planes.  Planned as nz *
+// X matrices of the packed rows' average count; returns the splits used.
+int wide_gemm_experts(const pn_model *m, const Mat &mat, const uint8_t *w0, const uint8_t *w1, const float *s0,
+                      const float *s1, float *y0, float *y1, int nz, int R, int N, int ldy, bool split_ok,
+                      hipStream_t s) {
+    const int X = m->X;
+    const long long ne = (long long)R * m->n_used;
+    const long long per = ne * ldy;  // floats of one split's outputs, per matrix
+    const WidePlan pl = wide_plan(wide_variant(m), (int)cdiv(ne, (long long)X), mat.n_tiles, mat.KT, nz * X,
+                                  cdiv(per, (long long)X), split_ok, m->wy_cap);
+    const int wgw = pl.wgw, ks = pl.ks;
+    char *mb = m->base;
+    WGemmArgs g{};
+    g.w[0] = w0;
+    g.w[1] = w1 ? w1 : w0;
+    g.sc[0] = s0;
+    g.sc[1] = s1 ? s1 : s0;
+    g.y[0] = y0;
+    g.y[1] = y1 ? y1 : y0;
+    g.y_split = per;
+    g.a = (const uint16_t *)(mb + m->wap);
+    g.a_plane = m->wap_plane;
+    g.lda = m->wlda;
+    g.R = R;
+    g.N = N;
+    g.n_tiles = mat.n_tiles;
+    g.KT = mat.KT;
+    g.ldy = ldy;
+    g.nsplit = ks;
+    g.nzs = nz * ks;
+    g.gx = cdiv(R, 128);
+    g.ecnt = (const int *)(mb + m->wecnt);
+    g.eoff = (const int *)(mb + m->weoff);
+    g.ew = (long long)mat.bytes1;
+    g.es = (long long)mat.sbytes1;
+    g.per_e = g.gx * cdiv(mat.n_tiles, wgw) * g.nzs;
+    const dim3 grid((unsigned)((long long)g.per_e * X));
+    const int v = wide_variant(m);
+    const size_t lds = (size_t)wide_lds(v, wgw);
+    with_wide(v, wgw, [&](auto wt, auto p, auto w) {
+        hipLaunchKernelGGL((k_wgemm<decltype(wt)::value, decltype(p)::value, decltype(w)::value>), grid, dim3(512),
+                           lds, s, g);
+        return 0;
+    });
+    return ks;
+}
+
 // The wide GEMMs' LDS ring is dynamic and passes 64 KiB: raise the limit
 // once per kernel.
 int wide_lds_attr() {
@@ -1228,13 +1297,15 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
                                E, gain, eps, ssq, a, m->wa_plane, m->wlda);
         });
     };
-    // x += the split outputs y (ld columns, ks splits), then the next norm's A planes from the new x
-    auto resid_norm = [&](int ld, int ks, const float *gain) {
+    // x += the split outputs yy (ld columns, ks splits), then the next norm's A planes from the new x
+    auto resid_norm_y = [&](const float *yy, int ld, int ks, const float *gain) {
         rows_as([&](auto wt, auto at) {
-            hipLaunchKernelGGL((k_w_resid_norm<decltype(wt)::value, decltype(at)::value>), dim3(R), dim3(1024), 0, s, x, y,
+            hipLaunchKernelGGL((k_w_resid_norm<decltype(wt)::value, decltype(at)::value>), dim3(R), dim3(1024), 0, s, x, yy,
                                (long long)R * ld, ks, ld, E, gain, eps, a, m->wa_plane, m->wlda);
         });
     };
+    auto resid_norm = [&](int ld, int ks, const float *gain) { resid_norm_y(y, ld, ks, gain); };
+    const bool moe = c.n_expert > 0;
     const bool outputs = logits || amax;
     auto scales = [&](const Mat &mt) { return bq ? (const float *)(mb + mt.soff) : nullptr; };
     if (int rc = wide_lds_attr()) return rc;
@@ -1308,8 +1379,77 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
         {
             const int ld = L.o.n_tiles * 16;
             const int ks = wide_gemm(m, L.o, (const uint8_t *)(mb + L.o.off), nullptr, scales(L.o), nullptr, y, nullptr, 1, R, ld, ld, true, s);
-            resid_norm(ld, ks, (const float *)(mb + L.ffn_norm));
+            if (!moe) {
+                resid_norm(ld, ks, (const float *)(mb + L.ffn_norm));
+            } else {
+                // the residual with its block sums of squares (the router's norm reads them), the FFN norm
+                hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E,
+                                   ssq);
+                norm((const float *)(mb + L.ffn_norm));
+            }
             if (int rc = launched("wide O")) return rc;
+        }
+        // the residual after the FFN (outputs yy: ld columns, ks splits), and the next norm
+        auto finish_layer = [&](const float *yy, int ld, int ks) {
+            if (l + 1 < c.n_layer)
+                resid_norm_y(yy, ld, ks, (const float *)(mb + m->L[l + 1].attn_norm));
+            else if (outputs)
+                resid_norm_y(yy, ld, ks, (const float *)(mb + m->out_norm));
+            else
+                hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, yy, (long long)R * ld, ks, ld, E,
+                                   ssq);
+        };
+        if (moe) {
+            // ---- experts: route every row, pack the entries by expert, gather their rows' A
+            // planes, each expert's gate/up and down over its rows, the weighted sum per row
+            const int nu = m->n_used, ne = R * nu;
+            int *rid = (int *)(mb + m->wrid);
+            float *rw = (float *)(mb + m->wrw);
+            {
+                const size_t sh = (size_t)E * 4;
+                const void *wr = mb + L.router;
+                const float *gn = (const float *)(mb + L.ffn_norm);
+                const int nbk = cdiv(E, 1024);
+                if (m->at == PN_F32)
+                    hipLaunchKernelGGL((k_router<1, AT_F32>), dim3(R), dim3(256), sh, s, (const float *)x, gn, wr, E,
+                                       c.n_expert, nu, eps, (const float *)ssq, kWideSsq, nbk, rid, rw, (int *)nullptr);
+                else
+                    hipLaunchKernelGGL((k_router<1, AT_BF16>), dim3(R), dim3(256), sh, s, (const float *)x, gn, wr, E,
+                                       c.n_expert, nu, eps, (const float *)ssq, kWideSsq, nbk, rid, rw, (int *)nullptr);
+                hipLaunchKernelGGL(k_w_route_lists, dim3(1), dim3(256), 0, s, (const int *)rid, ne, c.n_expert,
+                                   (int *)(mb + m->wecnt), (int *)(mb + m->weoff), (int *)(mb + m->went),
+                                   (int *)(mb + m->wpos));
+                const int kp = wide_kp(wtk, E);
+                hipLaunchKernelGGL(k_w_gather, dim3(cdiv(kp, 2048), ne, m->pieces), dim3(256), 0, s, (const uint16_t *)a,
+                                   m->wa_plane, m->wlda, (const int *)(mb + m->went), nu, kp, (uint16_t *)(mb + m->wap),
+                                   m->wap_plane);
+                if (int rc = launched("wide routing")) return rc;
+            }
+            uint16_t *ap = (uint16_t *)(mb + m->wap);
+            {
+                const int ld = L.gate.n_tiles * 16;
+                float *yu = y + m->wy_cap / 2;
+                const int ks = wide_gemm_experts(m, L.gate, (const uint8_t *)(mb + L.gate.off),
+                                                 (const uint8_t *)(mb + L.up.off), scales(L.gate), scales(L.up), y, yu, 2,
+                                                 R, ld, ld, true, s);
+                const long long sp = (long long)ne * ld;
+                rows_as([&](auto wt, auto at) {  // (the gathered planes are free again: the down product's input)
+                    hipLaunchKernelGGL((k_w_swiglu<decltype(wt)::value, decltype(at)::value>), dim3(cols(F), ne), dim3(256), 0,
+                                       s, y, yu, sp, ks, ld, F, ap, m->wap_plane, m->wlda);
+                });
+                if (int rc = launched("wide expert gate/up")) return rc;
+            }
+            {
+                const int ld = L.down.n_tiles * 16;
+                const int ks = wide_gemm_experts(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, scales(L.down),
+                                                 nullptr, y, nullptr, 1, R, E, ld, true, s);
+                float *yc = (float *)(mb + m->wyc);
+                hipLaunchKernelGGL(k_w_moe_combine, dim3(cdiv(E, 1024), R), dim3(256), 0, s, (const float *)y,
+                                   (long long)ne * ld, ks, ld, (const int *)(mb + m->wpos), (const float *)rw, nu, E, yc);
+                finish_layer(yc, E, 1);
+                if (int rc = launched("wide expert down")) return rc;
+            }
+            continue;
         }
         // ---- gate/up, SwiGLU, down + residual (and the next norm)
         {
@@ -1329,13 +1469,7 @@ int prefill_wide(pn_model *m, pn_state *st, const int32_t *tok, int R, float *lo
             const int ld = L.down.n_tiles * 16;
             const int ks = wide_gemm(m, L.down, (const uint8_t *)(mb + L.down.off), nullptr, scales(L.down), nullptr, y, nullptr, 1, R, ld, ld,
                                      true, s);
-            if (l + 1 < c.n_layer)
-                resid_norm(ld, ks, (const float *)(mb + m->L[l + 1].attn_norm));
-            else if (outputs)
-                resid_norm(ld, ks, (const float *)(mb + m->out_norm));
-            else
-                hipLaunchKernelGGL(k_w_resid, dim3(cdiv(E, 1024), R), dim3(256), 0, s, x, y, (long long)R * ld, ks, ld, E,
-                                   ssq);
+            finish_layer(y, ld, ks);
             if (int rc = launched("wide down")) return rc;
         }
     }

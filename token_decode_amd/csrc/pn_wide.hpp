@@ -56,6 +56,14 @@ struct WGemmArgs {
     long long a_plane;  // elements between the planes of A
     int lda, R, N, n_tiles, KT, ldy, nsplit;
     int nzs, gx;  // matrices * nsplit; A groups
+    // Grouped experts (ecnt null: one product over R rows).  Work-groups
+    // [e * per_e, (e + 1) * per_e) are expert e's: its rows are the ecnt[e]
+    // packed rows of A from row eoff[e] (at most R), its outputs the same rows
+    // of y, its matrices start ew bytes per expert after w[z], its scales es
+    // bytes per expert after sc[z].  A group past the expert's rows does no work.
+    const int *ecnt, *eoff;
+    long long ew, es;
+    int per_e;
 };
 
 // Row fragments per row tile and k step: the P bf16 planes, or for int8 and
@@ -137,9 +145,20 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     extern __shared__ __align__(16) uint8_t ring[];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int id = blockIdx.x, zs = id % g.nzs, rest = id / g.nzs;
+    int id = blockIdx.x, R = g.R;
+    long long roff = 0, wofs = 0, sofs = 0;  // grouped: the expert's first row, matrix and scale offsets
+    if (g.ecnt) {
+        const int ex = id / g.per_e;
+        id -= ex * g.per_e;
+        R = g.ecnt[ex];
+        roff = g.eoff[ex];
+        wofs = ex * g.ew;
+        sofs = ex * g.es;
+    }
+    const int zs = id % g.nzs, rest = id / g.nzs;
     const int gxi = rest % g.gx, gyi = rest / g.gx;
     const int z = zs / g.nsplit, s = zs % g.nsplit;
+    if (gxi * 128 >= R) return;  // (grouped: a row group past the expert's rows; uniform)
     const int kt0 = (int)((long long)s * g.KT / g.nsplit), kt1 = (int)((long long)(s + 1) * g.KT / g.nsplit);
     const int wt0 = gyi * WGW + WWT * (wv & 1);  // first weight tile the wave computes
     const int rt0 = gxi * 8 + 2 * (wv >> 1);  // first row tile the wave computes
@@ -152,15 +171,15 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     for (int q = 0; q < LPW; ++q) {
         const int f = min(wv * LPW + q, FR - 1);
         if (f < WGW) {
-            src[q] = g.w[z] + (long long)min(gyi * WGW + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
+            src[q] = g.w[z] + wofs + (long long)min(gyi * WGW + f, g.n_tiles - 1) * g.KT * 1024 + lane * 16;
             stride[q] = 1024;
         } else {
             // bf16: plane p, k 8*(l >> 4) of the step; int8, Q8_0, Q4_0: block p, positions
             // (TK / 4)*(l >> 4) + 8p (the blk_pos order of the tile)
             const int rt = (f - WGW) / NA, p = (f - WGW) % NA;
-            const int r = min((gxi * 8 + rt) * 16 + (lane & 15), g.R - 1);
-            const long long e = (WT == WT_I8 || BQ) ? (long long)r * g.lda + (TK / 4) * (lane >> 4) + 8 * p
-                                                    : p * g.a_plane + (long long)r * g.lda + 8 * (lane >> 4);
+            const long long r = roff + min((gxi * 8 + rt) * 16 + (lane & 15), R - 1);
+            const long long e = (WT == WT_I8 || BQ) ? r * g.lda + (TK / 4) * (lane >> 4) + 8 * p
+                                                    : p * g.a_plane + r * g.lda + 8 * (lane >> 4);
             src[q] = reinterpret_cast<const uint8_t *>(g.a + e);
             stride[q] = TK * 2;
         }
@@ -172,7 +191,7 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     if constexpr (BQ) {
         constexpr int DPT = SBT / 4;  // dwords of one tile's scales
         const int t = min(gyi * WGW + ((256 / SBT) * wv + lane / DPT) % WGW, g.n_tiles - 1);
-        ssrc = reinterpret_cast<const uint8_t *>(g.sc[z]) + (long long)t * g.KT * SBT + (lane % DPT) * 4;
+        ssrc = reinterpret_cast<const uint8_t *>(g.sc[z]) + sofs + (long long)t * g.KT * SBT + (lane % DPT) * 4;
     }
     auto issue = [&](int kt, int slot) {  // every call issues LPS loads (k steps past the split re-read the last)
         kt = min(kt, kt1 - 1);
@@ -303,7 +322,7 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
     }
     wait_vm_all();  // the clamped tail loads land before the work-group ends
     if (wt0 >= g.n_tiles) return;
-    float *y = g.y[z] + (long long)s * g.y_split;
+    float *y = g.y[z] + (long long)s * g.y_split + roff * g.ldy;  // (grouped: the expert's rows)
     if constexpr (BQ) {
         // lane l holds weight row (output n) l & 15 of tile i for A rows 4*(l >> 4) .. +3 of row tile j
 #pragma unroll
@@ -314,7 +333,7 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = (rt0 + j) * 16 + 4 * (lane >> 4) + e;
-                    if (r < g.R && n < g.N) y[(long long)r * g.ldy + n] = acc[i][j][e];
+                    if (r < R && n < g.N) y[(long long)r * g.ldy + n] = acc[i][j][e];
                 }
             }
         return;
@@ -324,14 +343,15 @@ __global__ void __launch_bounds__(512, 1) k_wgemm(WGemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int r = (rt0 + j) * 16 + (lane & 15);
-        if (r >= g.R) continue;
+        if (r >= R) continue;
 #pragma unroll
         for (int i = 0; i < WWT; ++i) {
             const int n0 = (wt0 + i) * 16 + 4 * (lane >> 4);
             float *yp = y + (long long)r * g.ldy + n0;
             f32x4 v = acc[i][j];
             if constexpr (WT == WT_I8) {  // the rows' scales (a table padded to whole tiles)
-                if (wt0 + i < g.n_tiles) v = v * *reinterpret_cast<const f32x4 *>(g.sc[z] + n0);
+                const float *scz = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(g.sc[z]) + sofs);
+                if (wt0 + i < g.n_tiles) v = v * *reinterpret_cast<const f32x4 *>(scz + n0);
             }
             if (vec && n0 + 3 < g.N) {
                 *reinterpret_cast<f32x4 *>(yp) = v;
@@ -601,6 +621,83 @@ __global__ void __launch_bounds__(1024) k_w_resid_norm(float *__restrict__ x, co
         for (int e = 0; e < 4; ++e) v[e] = c < E ? (xn[h][e] * ri) * gv[h][e] : 0.f;
         wide_put4<WT, AT>(a, a_plane, (long long)r * lda + c, v);
     }
+}
+
+// ---- experts on the wide path.  A chunk's R rows each route to n_used
+// experts: entry i = r * n_used + k (ids[i], wts[i] from the router).  The
+// entries are packed by expert, in entry order within each (so the packing is
+// deterministic): expert e's rows are packed rows eoff[e] .. eoff[e] + ecnt[e]
+// - 1, entry i sits at packed row pos[i], and packed row p holds entry ent[p].
+
+// The packing, one work-group of 256 threads: wave w counts the entries of
+// experts w, w + 4, ... 64 at a time with a ballot (ranks in entry order);
+// then the offsets in expert order.  nent <= kWideRows * 8, X <= 64.
+__global__ void __launch_bounds__(256) k_w_route_lists(const int *__restrict__ ids, int nent, int X,
+                                                        int *__restrict__ ecnt, int *__restrict__ eoff,
+                                                        int *__restrict__ ent, int *__restrict__ pos) {
+    __shared__ int cnt[64], off[64];
+    __shared__ int rank[kWideRows * 8];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int e = w; e < X; e += 4) {
+        int base = 0;
+        for (int j0 = 0; j0 < nent; j0 += 64) {
+            const int j = j0 + lane;
+            const bool m = j < nent && ids[j] == e;
+            const unsigned long long bal = __ballot(m);
+            if (m) rank[j] = base + __popcll(bal & ((1ull << lane) - 1ull));
+            base += __popcll(bal);
+        }
+        if (lane == 0) cnt[e] = base;
+    }
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        int o = 0;
+        for (int e = 0; e < X; ++e) {
+            off[e] = o;
+            ecnt[e] = cnt[e];
+            eoff[e] = o;
+            o += cnt[e];
+        }
+    }
+    lds_barrier();
+    for (int j = threadIdx.x; j < nent; j += 256) {
+        const int p = off[ids[j]] + rank[j];
+        pos[j] = p;
+        ent[p] = j;
+    }
+}
+
+// Packed row p of the experts' A planes = row ent[p] / n_used of the chunk's
+// A planes (its first `cols` columns, a multiple of 8).  grid: (cdiv(cols,
+// 2048), packed rows, planes); 256 threads, 8 columns each.
+__global__ void __launch_bounds__(256) k_w_gather(const uint16_t *__restrict__ a, long long a_plane, int lda,
+                                                   const int *__restrict__ ent, int n_used, int cols,
+                                                   uint16_t *__restrict__ ap, long long ap_plane) {
+    const int p = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (c >= cols) return;
+    const long long src = (long long)blockIdx.z * a_plane + (long long)(ent[p] / n_used) * lda + c;
+    const long long dst = (long long)blockIdx.z * ap_plane + (long long)p * lda + c;
+    *reinterpret_cast<u32x4 *>(ap + dst) = *reinterpret_cast<const u32x4 *>(a + src);
+}
+
+// out[r] = sum over k of wts[r][k] * (expert output of entry (r, k), summed over
+// the splits), in k order (as the decode step's combine).  grid: (cdiv(E,
+// 1024), rows); 256 threads, four columns each.
+__global__ void __launch_bounds__(256) k_w_moe_combine(const float *__restrict__ y, long long split, int nsplit,
+                                                        int ldy, const int *__restrict__ pos,
+                                                        const float *__restrict__ wts, int n_used, int E,
+                                                        float *__restrict__ out) {
+    const int r = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= E) return;  // (E a multiple of 8: four columns all in or all out)
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < n_used; ++k) {
+        const int i = r * n_used + k;
+        const f32x4 v = wide_sum4(y, split, nsplit, (long long)pos[i] * ldy + c);
+        const float wk = wts[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] += wk * v[e];
+    }
+    *reinterpret_cast<f32x4 *>(out + (long long)r * E + c) = t;
 }
 
 struct WQkvArgs {
