@@ -384,8 +384,11 @@ def time_prefill(model, wl, stream):
             runs.append(e0.elapsed_time(e1))
     p_ms = sum(runs) / len(runs)
     pieces = 3 if wl.act_dtype == synth.F32 else 1
+    # multiply-adds per token: attention projections, the FFN of each expert a token is routed
+    # to (one for a dense model), the LM head
+    ffn_per_token = 3 * wl.n_embd * wl.n_ff * (wl.n_expert_used if wl.n_expert > 0 else 1)
     mm = wl.n_layer * (wl.n_embd * (wl.n_head + 2 * wl.n_kv_head) * wl.head_dim +
-                       wl.n_head * wl.head_dim * wl.n_embd + 3 * wl.n_embd * wl.n_ff) + wl.n_vocab * wl.n_embd
+                       wl.n_head * wl.head_dim * wl.n_embd + ffn_per_token) + wl.n_vocab * wl.n_embd
     pst.free()
     log("[%s] prefill: %d tokens in %.2f ms = %.0f tokens/s" % (wl.name, n_p, p_ms, n_p / p_ms * 1e3))
     return {"tokens_per_s": round(n_p / p_ms * 1e3, 1), "tokens": n_p, "chunk": PREFILL_CHUNK,
