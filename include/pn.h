@@ -389,6 +389,12 @@ enum {
  *                              where the splits are combined in the O
  *                              prologue, else 4), 4 or 8 (ignored where the
  *                              combine runs in the O prologue);
+ *  PN_OPT_GEMM_PROLOGUE        the O projection's input conversion in a
+ *                              batched step: 0 = automatic (each wave of a
+ *                              16-wave work-group converts its own k range of
+ *                              every slot, up to 8 slots), 1 = the work-group
+ *                              converts it together (the same values either
+ *                              way);
  *  PN_OPT_WAVES_*              waves per work-group (4, 8 or 16) of the QKV,
  *                              O, gate/up, down and LM-head projections. */
 enum {
@@ -396,6 +402,7 @@ enum {
     PN_OPT_ATTN_KERNEL = 2,
     PN_OPT_ATTN_COMBINE = 3,
     PN_OPT_ATTN_WAVES = 4,
+    PN_OPT_GEMM_PROLOGUE = 5,
     PN_OPT_WAVES_QKV = 10, PN_OPT_WAVES_O, PN_OPT_WAVES_GATEUP, PN_OPT_WAVES_DOWN, PN_OPT_WAVES_LMHEAD
 };
 int pn_model_set_option(pn_model *m, int32_t option, int64_t value);

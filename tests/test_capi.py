@@ -171,6 +171,9 @@ def test_init_rejects_bad_buffers_without_device_work():
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_WAVES, 16) == C.PN_EINVAL
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_WAVES, 8) == 0
         assert L.pn_model_set_option(h, C.PN_OPT_ATTN_WAVES, 0) == 0
+        assert L.pn_model_set_option(h, C.PN_OPT_GEMM_PROLOGUE, 2) == C.PN_EINVAL
+        assert L.pn_model_set_option(h, C.PN_OPT_GEMM_PROLOGUE, 1) == 0
+        assert L.pn_model_set_option(h, C.PN_OPT_GEMM_PROLOGUE, 0) == 0
         assert L.pn_profile_begin(h, 99) == C.PN_EINVAL
         # shared page pool: sizing, creation and argument checks enqueue nothing
         page = L.pn_pool_bytes(h, 1)

@@ -186,3 +186,29 @@ def test_device_greedy_feedback():
     hl, hi = _steps_single(p, b, host_toks)
     np.testing.assert_array_equal(np.array(dev_ids), hi)
     assert np.stack(dev_l).tobytes() == hl.tobytes()
+
+
+@pytest.mark.parametrize("act", [synth.BF16, synth.F32], ids=["bf16-act", "f32-act"])
+def test_o_prologue_per_wave_bitwise(act):
+    """The O projection's input conversion done per wave over every slot (the
+    automatic choice for 2 to 8 slots in 16-wave work-groups) gives the same
+    logits, bit for bit, as the work-group converting it together.  bf16
+    weights, 16-wave O groups, 8 slots (5 with fp32 activations, three bf16
+    pieces each), from ragged positions."""
+    from token_decode_amd import _capi as C
+    wl = small("inv-oprologue-" + ("bf16" if act == synth.BF16 else "f32"), n_head=8, n_kv_head=2, head_dim=64,
+               n_embd=512, n_ff=640, w_dtype=synth.BF16, kv_dtype=synth.BF16, act_dtype=act, seed=63)
+    starts = [3, 70, 129, 200, 257, 64, 1, 333][:8 if act == synth.BF16 else 5]
+    n_steps = 3
+    p = Pair(wl, max_batch=len(starts))
+    p.dm.set_option(C.PN_OPT_WAVES_O, 16)
+    toks = synth.uniform_int(wl.seed, 79, n_steps * len(starts), 0, wl.n_vocab - 1).reshape(n_steps, len(starts))
+    max_ctx = max(starts) + n_steps + 1
+    out = []
+    for mode in (0, 1):
+        p.dm.set_option(C.PN_OPT_GEMM_PROLOGUE, mode)
+        dss = [_state(p, i, s, max_ctx) for i, s in enumerate(starts)]
+        out.append(_steps_batch(p, dss, toks))
+    np.testing.assert_array_equal(out[0][1], out[1][1])
+    assert out[0][0].tobytes() == out[1][0].tobytes(), "the per-wave O prologue changed the logits"
+    log("  %s: %d slots, %d steps, per-wave and shared O prologues bit-identical" % (wl.name, len(starts), n_steps))

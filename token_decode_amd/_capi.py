@@ -13,6 +13,7 @@ PN_OPT_ATTN_KEYS_PER_SPLIT = 1
 PN_OPT_ATTN_KERNEL = 2
 PN_OPT_ATTN_COMBINE = 3
 PN_OPT_ATTN_WAVES = 4
+PN_OPT_GEMM_PROLOGUE = 5
 PN_OPT_WAVES_QKV, PN_OPT_WAVES_O, PN_OPT_WAVES_GATEUP, PN_OPT_WAVES_DOWN, PN_OPT_WAVES_LMHEAD = range(10, 15)
 
 KERNEL_NAMES = ["embed", "qkv", "attn", "o", "gateup", "down", "lmhead", "argmax", "router",

@@ -18,7 +18,7 @@ void allow_lds(size_t lds) {
 }
 
 // occ >= 0: report resident work-groups per CU in *occ instead of launching
-template <int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS, bool WL>
+template <int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS, int WL>
 void go_k(const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
     auto *k = &k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS, WL>;
     allow_lds<&k_gemm<PN_WT, PN_AT, PRO, EPI, NTW, PAIR, NW, ALDS, WL>>(lds);
@@ -35,19 +35,26 @@ template <int PRO, int EPI, int NTW, bool PAIR, int NW>
 void go_nw(int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s, int *occ) {
     constexpr bool MOE = EPI == EPI_MOE_SWIGLU || EPI == EPI_MOE_DOWN;
     if constexpr (PRO == PRO_MERGE) {  // (wave-local only)
-        go_k<PRO, EPI, NTW, PAIR, NW, true, true>(g, grid, lds, s, occ);
+        go_k<PRO, EPI, NTW, PAIR, NW, true, 1>(g, grid, lds, s, occ);
     } else {
         if constexpr (!MOE) {
             if (amode == A_LDS_WAVE) {
-                go_k<PRO, EPI, NTW, PAIR, NW, true, true>(g, grid, lds, s, occ);
+                go_k<PRO, EPI, NTW, PAIR, NW, true, 1>(g, grid, lds, s, occ);
+                return;
+            }
+        }
+        // several slots per wave: the conversion prologue of 16-wave groups
+        if constexpr (PRO == PRO_CONV && NW == 16) {
+            if (amode == A_LDS_WAVE_ROWS) {
+                go_k<PRO, EPI, NTW, PAIR, NW, true, 2>(g, grid, lds, s, occ);
                 return;
             }
         }
         if constexpr (PRO != PRO_LOAD) {
-            go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
+            go_k<PRO, EPI, NTW, PAIR, NW, true, 0>(g, grid, lds, s, occ);
         } else {
-            if (amode != A_DIRECT) go_k<PRO, EPI, NTW, PAIR, NW, true, false>(g, grid, lds, s, occ);
-            else go_k<PRO, EPI, NTW, PAIR, NW, false, false>(g, grid, lds, s, occ);
+            if (amode != A_DIRECT) go_k<PRO, EPI, NTW, PAIR, NW, true, 0>(g, grid, lds, s, occ);
+            else go_k<PRO, EPI, NTW, PAIR, NW, false, 0>(g, grid, lds, s, occ);
         }
     }
 }

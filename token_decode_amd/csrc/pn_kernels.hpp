@@ -587,6 +587,23 @@ __host__ __device__ constexpr bool gemm_wave_local_fits(int wt, int pro, int nw,
     return rows * cpr <= gemm_cha(wt, nw);
 }
 
+// The wave-local conversion prologue over several slots (WL = 2: the O
+// projection of a batched step).  Each wave loads its own k tiles of every
+// slot's attention output: 64-lane loads of 8-element chunks run over (slot,
+// chunk) pairs, so with npr chunks per slot and npr dividing 64 a lane keeps
+// one chunk column and takes slot (64 c + lane) / npr in load c.  (The same
+// form for the norm prologue, with every slot's sums of squares and the gains
+// in registers, spilled in the 16-wave gate/up and LM-head kernels and made
+// them slower; it made no difference to QKV.)
+constexpr int kWaveRowsMax = 8;  // slots
+constexpr int kWaveRowsCh = 4;   // chunk loads per lane
+__host__ __device__ constexpr bool gemm_wave_rows_fits(int wt, int pro, int nw, int nb, int KT) {
+    const int per = (KT + nw - 1) / nw;
+    const int npr = per * tile_k(wt) / 8;
+    return pro == PRO_CONV && nb >= 1 && nb <= kWaveRowsMax && npr >= 1 && npr <= 64 && 64 % npr == 0 &&
+           nb * npr <= kWaveRowsCh * 64;
+}
+
 // Skinny GEMM Y[rows][N] = A[rows][K] * W[N][K]^T for rows <= 16, fused with a
 // prologue that supplies A and an epilogue that consumes Y.
 // A row block is NTW weight tiles: with PAIR, tile blk of matrices w and w2
@@ -601,11 +618,15 @@ __host__ __device__ constexpr bool gemm_wave_local_fits(int wt, int pro, int nw,
 // the prologue; weight rounds then ping-pong between two register buffers, and
 // the next block's first rounds are in flight during this block's reduction
 // and epilogue.
-template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS, bool WL>
+// WL: 0 = the work-group's shared prologue, 1 = wave-local for one batch of
+// the prologue registers, 2 = the wave-local conversion prologue over up to
+// kWaveRowsMax slots (gemm_wave_rows_fits).
+template <int WT, int AT, int PRO, int EPI, int NTW, bool PAIR, int NW, bool ALDS, int WL>
 __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     static_assert(PRO == PRO_LOAD || ALDS, "the norm prologue stages A in LDS");
     static_assert(!WL || ALDS, "the wave-local prologue stages A in LDS");
-    static_assert(PRO != PRO_MERGE || (WL && EPI == EPI_RESID), "the split combine runs in the wave-local prologue");
+    static_assert(PRO != PRO_MERGE || (WL == 1 && EPI == EPI_RESID), "the split combine runs in the wave-local prologue");
+    static_assert(WL != 2 || PRO == PRO_CONV, "the several-slot wave-local prologue converts x");
     constexpr bool XPRO = PRO == PRO_NORM || PRO == PRO_CONV;  // A built from fp32 rows in g.x
     constexpr bool MPRO = PRO == PRO_MERGE;
     constexpr int NT = NW * 64;
@@ -620,7 +641,7 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     // go out before any weight load): for the norm prologue four rows of 4096
     // with 16 waves, one with 8 (more would cost the occupancy of 8-wave
     // groups), two with 4
-    constexpr int CH = gemm_ch(NW, PRO);
+    constexpr int CH = WL == 2 ? kWaveRowsCh : gemm_ch(NW, PRO);
     constexpr int CHA = gemm_cha(WT, NW);
     constexpr int SPW = gemm_spw(NW);  // norm prologue: slots whose sums of squares a wave reads
     constexpr int ES = AReady<WT, AT>::ES;
@@ -686,11 +707,31 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
     const int nchw = (wt1 - wt0) * TK / 8;  // 8-element chunks of this wave's tiles, per A row
     const int nfw = (wt1 - wt0) * 4;        // A fragments of this wave's tiles, per A row
     const int cpr = XPRO ? max(1, (per * TK / 8 + 63) / 64) : max(1, (per * 4 + 63) / 64);
-    constexpr bool wl = WL;
+    constexpr bool wl = WL == 1;
+    // WL = 2: chunks per slot (one wave's share, the same for every wave) and
+    // this lane's chunk column
+    const int npr = per * TK / 8;
+    const int jr = WL == 2 ? lane % npr : 0;
     float xv[CH][8], gv[CH][8];
     float ssv[SPW][8];
     u32x4 st[CHA][frag_vecs(WT)];
-    if constexpr (XPRO) {
+    if constexpr (WL == 2) {
+        const int k0 = wt0 * TK + jr * 8;
+        const bool jin = jr < nchw && k0 < g.K;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int b = (c * 64 + lane) / npr;
+            const bool in = jin && b < nb;
+            const f32x4 *xp = reinterpret_cast<const f32x4 *>(g.x + (long long)(in ? b : 0) * g.K + (in ? k0 : 0));
+            // (values of chunks past the rows or K are never used)
+            const f32x4 x0 = xp[0], x1 = xp[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xv[c][e] = x0[e];
+                xv[c][4 + e] = x1[e];
+            }
+        }
+    } else if constexpr (XPRO) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             int b, k0;
@@ -905,7 +946,25 @@ __global__ void __launch_bounds__(NW * 64) k_gemm(GemmArgs g) {
 
 
     // ---- phase 3: the prologue's arithmetic
-    if constexpr (XPRO) {
+    if constexpr (WL == 2) {
+        // this wave's chunks of every slot, straight into LDS
+        const int k0 = wt0 * TK + jr * 8;
+        if (jr < nchw) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int b = (c * 64 + lane) / npr;
+                if (b >= nb) continue;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (k0 + e < g.K) ? xv[c][e] : 0.f;
+                if constexpr (AT == AT_BF16) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = bf16_round(v[e]);
+                }
+                put_a8<WT, AT>(sa, rows, nb, b, k0, v);
+            }
+        }
+    } else if constexpr (XPRO) {
         if constexpr (wl) {
             // this wave's tiles of every slot: norm factors from all the slot's
             // sums of squares (same order as below), then straight into LDS

@@ -26,9 +26,11 @@ constexpr size_t kMaxLds = 159 * 1024;
 // Defined once per (weight type, activation type) in pn_gemm.hip; nw = waves
 // per work-group (4, 8 or 16); amode: A_DIRECT reads an A-ready input straight
 // from memory, A_LDS stages A in LDS, A_LDS_WAVE stages it per wave (the
-// wave-local prologue; not for MoE kinds).  With occ non-null nothing is
-// launched: *occ receives the resident work-groups per CU.
-enum AMode { A_DIRECT = 0, A_LDS = 1, A_LDS_WAVE = 2 };
+// wave-local prologue; not for MoE kinds), A_LDS_WAVE_ROWS per wave over
+// several slots (the conversion prologue, up to kWaveRowsMax slots).
+// With occ non-null nothing is launched: *occ receives the resident
+// work-groups per CU.
+enum AMode { A_DIRECT = 0, A_LDS = 1, A_LDS_WAVE = 2, A_LDS_WAVE_ROWS = 3 };
 void launch_gemm_f32_f32(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,
                          int *occ);
 void launch_gemm_f32_bf16(int kind, int nw, int amode, const GemmArgs &g, dim3 grid, size_t lds, hipStream_t s,

@@ -69,6 +69,7 @@ struct LayerOff {
 struct Plan {
     int gx = 1, gz = 1, nw = 8, nblk = 1, tpw = 1;
     bool a_lds = false;
+    bool wave_rows = true;  // the conversion prologue may run per wave over several slots
     size_t lds = 0;
 };
 
@@ -117,6 +118,7 @@ struct pn_model {
     int attn_kind = 0;  // bf16 cache: 0 = automatic, 1 = vector units, 2 = matrix cores
     int attn_combine = 0;  // split combine: 0 = automatic (O prologue where eligible), 1 = merge launch
     int attn_waves = 0;    // matrix-core attention work-groups: 0 = automatic, 4 or 8 waves
+    int prologue = 0;      // O projection's conversion prologue over several slots: 0 = per wave where it fits, 1 = shared
     int nw[GK_COUNT] = {8, 8, 8, 8, 8, 8, 16, 16};  // waves per work-group of each GEMM kind (O_MERGE: O's)
     int nw_down = 16;                       // the down projection (K = n_ff) uses GK_RESID too
     bool nw_set = false;                    // waves chosen by the caller (PN_OPT_WAVES_*): no auto choice
@@ -642,6 +644,8 @@ void launch_gemm(int kind, int wt, int at, GemmArgs g, const Plan &p, hipStream_
     int amode = p.a_lds || pro != PRO_LOAD ? A_LDS : A_DIRECT;
     if (!moe && amode == A_LDS && gemm_wave_local_fits(wt, pro, p.nw, g.B, g.B * pieces, g.KT))
         amode = A_LDS_WAVE;
+    else if (!moe && amode == A_LDS && p.nw == 16 && p.wave_rows && gemm_wave_rows_fits(wt, pro, p.nw, g.B, g.KT))
+        amode = A_LDS_WAVE_ROWS;
     if (kind == GK_O_MERGE) amode = A_LDS_WAVE;  // (eligibility checked by merge_in_o)
     gemm_entry(kind, wt, at, p.nw, amode, g, grid, p.lds, s, nullptr);
 }
@@ -829,16 +833,17 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
         return n;
     };
     const int cap = blockq(wt) ? 8 : 16;
-    const Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of, !m->nw_set, n,
+    Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of, !m->nw_set, n,
                                  cap);
-    const Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of, !m->nw_set, n, cap);
-    const Plan p_gu = make_plan(moe ? GK_MOE_SWIGLU : GK_SWIGLU, L0.gate.n_tiles, gz, L0.gate.KT, rows, fb,
+    Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of, !m->nw_set, n, cap);
+    Plan p_gu = make_plan(moe ? GK_MOE_SWIGLU : GK_SWIGLU, L0.gate.n_tiles, gz, L0.gate.KT, rows, fb,
                                 m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of, !m->nw_set, n, cap);
-    const Plan p_dn = make_plan(moe ? GK_MOE_DOWN : GK_RESID, L0.down.n_tiles, gz, L0.down.KT, rows, fb,
+    Plan p_dn = make_plan(moe ? GK_MOE_DOWN : GK_RESID, L0.down.n_tiles, gz, L0.down.KT, rows, fb,
                                 moe ? m->nw[GK_MOE_DOWN] : m->nw_down, occ_of, !m->nw_set, 1, cap);
-    const Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of,
+    Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of,
                                 !m->nw_set, n, cap);
     // (plans for the other kinds take one row block per tile)
+    for (Plan *p : {&p_qkv, &p_o, &p_gu, &p_dn, &p_lm}) p->wave_rows = m->prologue == 0;
 
     // attention geometry per slot; with the split combine in the O prologue, at
     // most kMergeSplits splits per head (unless the caller's keys per split give more)
@@ -2136,6 +2141,11 @@ int pn_model_set_option(pn_model *m, int32_t option, int64_t value) {
     if (option == PN_OPT_ATTN_WAVES) {
         if (value != 0 && value != 4 && value != 8) return fail(PN_EINVAL, "attention waves must be 0, 4 or 8");
         m->attn_waves = (int)value;
+        return PN_OK;
+    }
+    if (option == PN_OPT_GEMM_PROLOGUE) {
+        if (value < 0 || value > 1) return fail(PN_EINVAL, "GEMM prologue must be 0 or 1");
+        m->prologue = (int)value;
         return PN_OK;
     }
     if (option == PN_OPT_ATTN_COMBINE) {
