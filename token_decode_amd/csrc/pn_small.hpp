@@ -150,6 +150,44 @@ __global__ void __launch_bounds__(256) k_router(const float *x, const float *gai
     extern __shared__ float xs[];  // [E]
     __shared__ float red4[4];
     __shared__ float r[64];
+    // One load of 8 router weights (k .. k+7 of expert e): a 16-byte vector of
+    // bf16, or two of fp32; zeros past E.
+    struct WRaw { u32x4 v[2]; };
+    auto load_raw = [&](int e, int k) -> WRaw {
+        WRaw q{};
+        if (k < E) {
+            if constexpr (RT == 1) {
+                q.v[0] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(wr) + (long long)e * E + k);
+            } else {
+                const u32x4 *p = reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(wr) + (long long)e * E + k);
+                q.v[0] = p[0];
+                q.v[1] = p[1];
+            }
+        }
+        return q;
+    };
+    auto expand = [&](const WRaw &q, float (&o)[8]) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            if constexpr (RT == 1) {
+                o[2 * h] = __uint_as_float(q.v[0][h] << 16);
+                o[2 * h + 1] = __uint_as_float(q.v[0][h] & 0xFFFF0000u);
+            } else {
+                o[h] = __uint_as_float(q.v[0][h]);
+                o[4 + h] = __uint_as_float(q.v[1][h]);
+            }
+        }
+    };
+    // The weights do not depend on x: the first 4096 inputs of this wave's
+    // first two experts (w and w + 4) are loaded before x, so their round trip
+    // overlaps the norm's.
+    constexpr int KC = 64 * 8 * 8;  // inputs per pass of a wave
+    WRaw pre0[8], pre1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        pre0[u] = w < n_expert ? load_raw(w, (lane + 64 * u) * 8) : WRaw{};
+        pre1[u] = w + 4 < n_expert ? load_raw(w + 4, (lane + 64 * u) * 8) : WRaw{};
+    }
     const float *xr = x + (long long)b * E;
     // this thread's 32 elements of x and gain, and a share of the sums of squares
     constexpr int EPT = 32;
@@ -177,34 +215,17 @@ __global__ void __launch_bounds__(256) k_router(const float *x, const float *gai
             }
         }
     lds_barrier();
-    // expert e on wave e % 4: lanes stride over E in 8-element groups
-    for (int e = w; e < n_expert; e += 4) {
+    // expert e on wave e % 4: lanes stride over E in 8-element groups; the
+    // first pass of the first two takes the weights loaded above
+    auto dot = [&](int e, const WRaw (*pre)[8]) -> float {
         float acc = 0.f;
-        for (int base = 0; base < E; base += 64 * 8 * 8) {
+        for (int base = 0; base < E; base += KC) {
             float wv[8][8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int k = base + (lane + 64 * u) * 8;
-                if (k < E) {
-                    if constexpr (RT == 1) {
-                        const u32x4 q = *reinterpret_cast<const u32x4 *>(
-                            reinterpret_cast<const uint16_t *>(wr) + (long long)e * E + k);
-#pragma unroll
-                        for (int h = 0; h < 4; ++h) {
-                            wv[u][2 * h] = __uint_as_float(q[h] << 16);
-                            wv[u][2 * h + 1] = __uint_as_float(q[h] & 0xFFFF0000u);
-                        }
-                    } else {
-                        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(wr) +
-                                                                           (long long)e * E + k);
-                        const f32x4 q0 = p[0], q1 = p[1];
-#pragma unroll
-                        for (int h = 0; h < 4; ++h) { wv[u][h] = q0[h]; wv[u][4 + h] = q1[h]; }
-                    }
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 8; ++h) wv[u][h] = 0.f;
-                }
+                const WRaw q = (pre && base == 0) ? (*pre)[u] : load_raw(e, k);
+                expand(q, wv[u]);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -214,8 +235,19 @@ __global__ void __launch_bounds__(256) k_router(const float *x, const float *gai
                     for (int h = 0; h < 8; ++h) acc = fmaf(wv[u][h], xs[k + h], acc);
             }
         }
-        acc = wave_sum(acc);
-        if (lane == 0) r[e] = acc;
+        return wave_sum(acc);
+    };
+    if (w < n_expert) {
+        const float a = dot(w, &pre0);
+        if (lane == 0) r[w] = a;
+    }
+    if (w + 4 < n_expert) {
+        const float a = dot(w + 4, &pre1);
+        if (lane == 0) r[w + 4] = a;
+    }
+    for (int e = w + 8; e < n_expert; e += 4) {
+        const float a = dot(e, nullptr);
+        if (lane == 0) r[e] = a;
     }
     lds_barrier();
     if (tid == 0) {
