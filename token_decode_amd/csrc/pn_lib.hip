@@ -834,17 +834,17 @@ int forward_impl(pn_model *m, pn_state *const *st, int n, const int32_t *tok, fl
     };
     const int cap = blockq(wt) ? 8 : 16;
     Plan p_qkv = make_plan(GK_QKV, L0.qkv.n_tiles, 1, L0.qkv.KT, rows, fb, m->nw[GK_QKV], occ_of, !m->nw_set, n,
-                                 cap);
+                           cap);
     Plan p_o = make_plan(GK_O, L0.o.n_tiles, 1, L0.o.KT, rows, fb, m->nw[GK_O], occ_of, !m->nw_set, n, cap);
     Plan p_gu = make_plan(moe ? GK_MOE_SWIGLU : GK_SWIGLU, L0.gate.n_tiles, gz, L0.gate.KT, rows, fb,
-                                m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of, !m->nw_set, n, cap);
+                          m->nw[moe ? GK_MOE_SWIGLU : GK_SWIGLU], occ_of, !m->nw_set, n, cap);
     // dense down with bf16 weights: A fragments straight from memory at any
     // batch (Llama-3-8B shape at batch 1: 21.8 -> 19.9 us against A staged in
     // LDS; int8 weights' f16 fragments are slower that way: 13.2 -> 16.1 us)
     Plan p_dn = make_plan(moe ? GK_MOE_DOWN : GK_RESID, L0.down.n_tiles, gz, L0.down.KT, rows, fb,
                           moe ? m->nw[GK_MOE_DOWN] : m->nw_down, occ_of, !m->nw_set, 1, cap, !moe && wt == PN_BF16);
     Plan p_lm = make_plan(GK_LOGITS, cdiv(m->out.n_tiles, 2), 1, m->out.KT, rows, fb, m->nw[GK_LOGITS], occ_of,
-                                !m->nw_set, n, cap);
+                          !m->nw_set, n, cap);
     // (plans for the other kinds take one row block per tile)
     for (Plan *p : {&p_qkv, &p_o, &p_gu, &p_dn, &p_lm}) p->wave_rows = m->prologue == 0;
 
