@@ -87,6 +87,16 @@ def test_moe_small_batched():
     log("  moe: worst rel L2 %.2e near %d" % (worst, near))
 
 
+def test_moe_many_experts():
+    """Twelve experts, top-3: the router's waves take experts w, w + 4 and w + 8
+    (the last pass loads its weights inside the loop), and routing picks three."""
+    wl = ragged("moe-e12", n_expert=12, n_expert_used=3, w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                act_dtype=synth.BF16, seed=46, n_ff=96)
+    p = Pair(wl, max_batch=4)
+    worst, near = run_batch(p, [3, 90, 257, 400], 3)
+    log("  moe 12 experts: worst rel L2 %.2e near %d" % (worst, near))
+
+
 def test_moe_single_fp32():
     wl = ragged("moe-f32", n_expert=4, n_expert_used=2, w_dtype=synth.F32, kv_dtype=synth.F32,
                 act_dtype=synth.F32, seed=45, n_ff=96)
